@@ -1,0 +1,37 @@
+"""CPU oracle for the weight-only quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library in ``gemm_decode_amd/`` and imports nothing from it.
+
+What it computes (plain, slow, obviously correct; NumPy only):
+
+* ``quant``  -- the quantisers and the canonical packed layouts (W8 per output
+  channel, W8 group-128, W4 asymmetric group-128), step by step.
+* ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
+  chunked along N; sampled-column variants for full-size checks; the
+  comparison statistics with the per-element tolerance.
+
+Passages followed:
+
+* tileInfer README, feature table ("INT8 Weight-Only Quantization") and the
+  "Key Optimizations" list: int8 weights with one scale per output channel, bf16
+  activations; decode multiplies the dequantised weights in registers, prefill
+  dequantises to bf16 on the fly before a GEMM.
+* "Marlin register and launch scheduling benchmark", "Validation and limits":
+  INT4 and INT8 weights with bf16 activations, per-channel and group-128 scales.
+* "Heuristic: Mit han lab Llm awq Kernel Selection Thresholds", code excerpt
+  from awq/quantize/qmodule.py: the token count is numel(x) / x.shape[-1].
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+hand-derived worked examples (``tests/golden/``), closed-form error bounds,
+brute force on tiny inputs and reductions to NumPy library routines.
+"""
+from .quant import (  # noqa: F401
+    FORMATS, GROUP, bf16_bits_to_f32, bf16_rne_bits, dequant, pack, packed_sizes,
+    quantize_w4g128, quantize_w8, unpack_w4g128,
+)
+from .linear import (  # noqa: F401
+    compare, ref_linear, ref_linear_columns, token_count, use_gemv,
+)

@@ -1,0 +1,84 @@
+"""Reference linear y = x . dequant(W)^T and the parity statistics (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The layer is the weight-only quantised linear of the tileInfer README (feature
+table, "INT8 Weight-Only Quantization"; "Key Optimizations"): bf16 activations
+times int8 (or int4, Marlin benchmark page, "Validation and limits") weights
+carrying scales.  Its plain definition, which every GPU kernel (GEMV, split-K,
+GEMM) must reach up to fp32 summation order and the final bf16 rounding:
+
+    y[m, n] = sum_k x[m, k] * Wd[n, k],   Wd = dequant(packed W)   (exact fp32)
+
+evaluated here in fp64 with NumPy's matmul, chunked along N to bound memory.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import quant as _quant
+
+TOL_REL = 1e-2          # |y - y_ref| <= TOL_REL * max(1, |y_ref|) per output element
+GEMV_MAX_TOKENS = 7     # tokens < 8 -> GEMV, >= 8 -> GEMM
+
+
+def token_count(x_shape) -> int:
+    """numel(x) / x.shape[-1], the token count of the awq dispatch excerpt
+    ("Heuristic: Mit han lab Llm awq Kernel Selection Thresholds", code from
+    awq/quantize/qmodule.py)."""
+    n = 1
+    for d in x_shape:
+        n *= int(d)
+    return n // int(x_shape[-1])
+
+
+def use_gemv(M: int) -> bool:
+    """Same page, "The Insight (Rule of Thumb)", Linear Kernel: fewer than 8
+    tokens take the GEMV kernel, 8 or more the GEMM kernel."""
+    return M < GEMV_MAX_TOKENS + 1
+
+
+def _x64(x_bits) -> np.ndarray:
+    return _quant.bf16_bits_to_f32(x_bits).astype(np.float64)
+
+
+def ref_linear(x_bits: np.ndarray, P: dict, chunk: int = 4096) -> np.ndarray:
+    """fp64 y[M, N] for bf16 x[M, K] (uint16 bits) and a canonical packed weight."""
+    x = _x64(x_bits)
+    N = P["N"]
+    y = np.empty((x.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, chunk):
+        rows = np.arange(n0, min(N, n0 + chunk))
+        Wd = _quant.dequant(P, rows).astype(np.float64)
+        y[:, n0:n0 + len(rows)] = x @ Wd.T
+    return y
+
+
+def ref_linear_columns(x_bits: np.ndarray, P: dict, cols) -> np.ndarray:
+    """fp64 y[:, cols] only: the oracle one output channel at a time, for
+    sampled checks at sizes where the full product is too slow on the host."""
+    cols = np.asarray(cols)
+    x = _x64(x_bits)
+    Wd = _quant.dequant(P, cols).astype(np.float64)
+    return x @ Wd.T
+
+
+def compare(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
+    """Per-element check of bf16 results against the fp64 reference.
+
+    Returns max(err/tol), the number of failures and the relative RMS
+    ||y - y_ref|| / ||y_ref|| (the statistic the Marlin benchmark page reports
+    for its fixed-input projection check).
+    """
+    y = _quant.bf16_bits_to_f32(y_bits).astype(np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {y_ref.shape}")
+    err = np.abs(y - y_ref)
+    tol = TOL_REL * np.maximum(1.0, np.abs(y_ref))
+    ratio = err / tol
+    denom = float(np.sqrt(np.sum(y_ref * y_ref)))
+    rel_rms = float(np.sqrt(np.sum((y - y_ref) ** 2)) / denom) if denom > 0 else float(np.sqrt(np.sum(y * y)))
+    return dict(max_ratio=float(ratio.max()) if ratio.size else 0.0,
+                fails=int(np.count_nonzero(ratio > 1.0)),
+                rel_rms=rel_rms, n=int(ratio.size))

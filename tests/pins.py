@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+hand-derived worked example (tests/golden/), a closed-form bound, a brute-force
+computation on tiny inputs written independently of the oracle (Python ints and
+Fractions), or a reduction to a NumPy library routine.  The functions call the
+oracle through its modules (``oracle.quant.X``, ``oracle.linear.X``) so that the
+mutation tests can plant a mistake in the oracle and check that a pin fails.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.linear as OL
+import oracle.quant as OQ
+import synth
+from golden_io import num, read_fixture
+
+
+# ------------------------------------------------------------ independent helpers
+def _f32_fraction(v) -> Fraction:
+    return Fraction(float(np.float32(v)))
+
+
+def _bf16_bits_value(b: int) -> Fraction:
+    """Exact value of a bf16 bit pattern, decoded by hand (normal and zero only)."""
+    sign = -1 if b & 0x8000 else 1
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    if e == 0:
+        return Fraction(sign * m, 2 ** (126 + 7))
+    return sign * Fraction(128 + m, 128) * Fraction(2) ** (e - 127)
+
+
+def _fp16_value(h) -> Fraction:
+    b = int(np.asarray(h, dtype=np.float16).view(np.uint16))
+    sign = -1 if b & 0x8000 else 1
+    e = (b >> 10) & 0x1F
+    m = b & 0x3FF
+    if e == 0:
+        return Fraction(sign * m, 2 ** 24)
+    return sign * Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15)
+
+
+def _decode_w4_codes(P: dict, n: int, k: int) -> int:
+    word = int(P["qweight"][n, k // 8])
+    return (word >> (4 * (k % 8))) & 0xF
+
+
+def _decode_w4_zero(P: dict, n: int, g: int) -> int:
+    word = int(P["zeros"][g, n // 8])
+    return (word >> (4 * (n % 8))) & 0xF
+
+
+def _exact_dequant(P: dict, n: int, k: int) -> Fraction:
+    fmt = P["fmt"]
+    if fmt == "w8pc":
+        return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n]))
+    if fmt == "w8g128":
+        return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n, k // 128]))
+    q = _decode_w4_codes(P, n, k)
+    z = _decode_w4_zero(P, n, k // 128)
+    return (q - z) * _fp16_value(P["scales"][n, k // 128])
+
+
+# ------------------------------------------------------------------ conversions
+def pin_bf16_rounding():
+    """bf16 RNE: hand values, then brute force: the result is the nearer of the
+    two bf16 neighbours of v (ties to the even one)."""
+    f = OQ.bf16_rne_bits
+    hand = {1.0: 0x3F80, 1.0 + 2 ** -8: 0x3F80, 1.0 + 3 * 2 ** -8: 0x3F82,
+            -2.0: 0xC000, 0.0: 0x0000, 1.0 / 127.0: 0x3C01, 2.0 ** -7: 0x3C00,
+            1.0 + 2 ** -8 + 2 ** -20: 0x3F81}
+    for v, b in hand.items():
+        got = int(f(np.array([v], dtype=np.float32))[0])
+        assert got == b, f"bf16({v!r}) = {got:#06x}, expected {b:#06x}"
+    rng = np.random.default_rng(123)
+    vals = (rng.standard_normal(4000) * np.exp(rng.uniform(-20, 20, 4000))).astype(np.float32)
+    bits = f(vals)
+    for v, b in zip(vals[:800], bits[:800]):
+        exact = _f32_fraction(v)
+        u = int(np.float32(v).view(np.uint32))
+        lo, hi = u >> 16, (u >> 16) + 1
+        dlo = abs(_bf16_bits_value(lo) - exact)
+        dhi = abs(_bf16_bits_value(hi) - exact)
+        want = lo if dlo < dhi else hi if dhi < dlo else (lo if lo % 2 == 0 else hi)
+        assert int(b) == want, f"bf16 rounding of {v!r}: {int(b):#x} vs {want:#x}"
+    back = OQ.bf16_bits_to_f32(np.array([0x3F80, 0xC000, 0x3C01], dtype=np.uint16))
+    assert [_f32_fraction(v) for v in back] == [1, -2, Fraction(129, 16384)]
+
+
+# ------------------------------------------------------------------- quantisers
+def pin_golden_w8pc():
+    head, blk = read_fixture("w8pc_worked.txt")
+    K, N = int(head["K"][0]), int(head["N"][0])
+    W = np.array([[float(t) for t in r] for r in blk["W"]], dtype=np.float32)
+    assert W.shape == (N, K)
+    P = OQ.pack("w8pc", W)
+    q = np.array([[int(float(t)) for t in r] for r in blk["q"]])
+    s = np.array([num(r[0]) for r in blk["s_bits"]])
+    assert np.array_equal(P["qweight"].astype(int), q), (P["qweight"], q)
+    assert np.array_equal(P["scales"].astype(int), s), (P["scales"], s)
+    assert P["qweight"].dtype == np.int8 and P["scales"].dtype == np.uint16
+
+
+def _golden_w4_weight():
+    head, _ = read_fixture("w4g128_worked.txt")
+    K = int(head["K"][0])
+    W = np.zeros((8, K), dtype=np.float32)    # N = 8 (zeros pack 8 per word); rows 1..7 zero
+    exp_q = np.zeros((8, K), dtype=int)
+    exp_s, exp_z = [], []
+    for g in range(2):
+        vals = [float(t) for t in head[f"group{g}"]]
+        fill = float(head[f"group{g}_fill"][0])
+        row = np.full(128, fill, dtype=np.float32)
+        row[:len(vals)] = vals
+        W[0, 128 * g:128 * (g + 1)] = row
+        qv = [int(t) for t in head[f"group{g}_q"]]
+        qrow = np.full(128, int(head[f"group{g}_fill_q"][0]))
+        qrow[:len(qv)] = qv
+        exp_q[0, 128 * g:128 * (g + 1)] = qrow
+        exp_s.append(num(head[f"group{g}_s_bits"][0]))
+        exp_z.append(int(head[f"group{g}_z"][0]))
+    return W, exp_q, exp_s, exp_z
+
+
+def pin_golden_w4g128():
+    W, exp_q, exp_s, exp_z = _golden_w4_weight()
+    P = OQ.pack("w4g128", W)
+    for k in range(W.shape[1]):
+        assert _decode_w4_codes(P, 0, k) == exp_q[0, k], f"q[0,{k}]"
+    sbits = P["scales"].view(np.uint16)
+    assert [int(sbits[0, g]) for g in range(2)] == exp_s, sbits[0]
+    assert [_decode_w4_zero(P, 0, g) for g in range(2)] == exp_z
+    # all-zero rows 1..7: scale 0, zero-point 0, codes 0 (every code equals its zero-point)
+    assert not np.any(sbits[1:]) and all(_decode_w4_zero(P, n, g) == 0 for n in range(1, 8) for g in range(2))
+    # dequantised row 0 equals (q - z) * s exactly
+    Wd = OQ.dequant(P)
+    for k in range(0, W.shape[1], 7):
+        assert Fraction(float(Wd[0, k])) == _exact_dequant(P, 0, k)
+    assert not np.any(Wd[1:])
+
+
+def pin_nibble_layout():
+    head, _ = read_fixture("nibble_layout.txt")
+    K, N = 16, 8
+    q = np.zeros((N, K), dtype=np.uint8)
+    q[0, :8] = [int(t) for t in head["codes0"]]
+    q[0, 8:] = [int(t) for t in head["codes1"]]
+    words = OQ._pack_nibbles_rows(q)
+    assert int(words[0, 0]) == num(head["word0"][0]) and int(words[0, 1]) == num(head["word1"][0])
+    z = np.zeros((N, 1), dtype=np.uint8)
+    z[:, 0] = [int(t) for t in head["zeros_col"]]
+    zw = OQ._pack_nibbles_rows(np.ascontiguousarray(z.T))
+    assert zw.shape == (1, 1) and int(zw[0, 0]) == num(head["zeros_word"][0])
+    # the same through pack(): a weight whose group-0 codes come out as 0..7 for n = 0..7
+    # (w = (c - 7)/64 with lo = -7/64, hi = 8/64 in every row) and zero-point 7
+    W = np.zeros((8, 128), dtype=np.float32)
+    W[:, 0], W[:, 1] = -7 / 64, 8 / 64
+    for n in range(8):
+        W[n, 2] = (n - 7) / 64
+    P = OQ.pack("w4g128", W)
+    assert [_decode_w4_codes(P, n, 2) for n in range(8)] == list(range(8))
+    assert int(P["zeros"][0, 0]) == 0x77777777
+    assert OQ.packed_sizes("w4g128", 128, 8) == (P["qweight"].nbytes, P["scales"].nbytes, P["zeros"].nbytes)
+
+
+def pin_w8_roundtrip_bound(seed=7, N=64, K=1024, G=None):
+    """P1: |w - q*s| <= s/2 (+ the fp32 division slack) with the stored scale;
+    the clamp never bites because 127*(1 + 2^-8) < 127.5."""
+    W = synth.weight(seed, K, N)
+    q, sb = OQ.quantize_w8(W, G)
+    s = OQ.bf16_bits_to_f32(sb).astype(np.float64)
+    g = K if G is None else G
+    sfull = np.repeat(s.reshape(N, -1), g, axis=1)
+    err = np.abs(W.astype(np.float64) - q.astype(np.float64) * sfull)
+    bound = sfull / 2 + np.abs(W) * 2.0 ** -23
+    assert np.all(err <= bound), float((err / sfull).max())
+    assert int(np.abs(q.astype(int)).max()) <= 127
+    # the scale is the bf16 rounding of max|w| / 127 (checked exactly)
+    a = np.max(np.abs(W.reshape(N, -1, g)), axis=2)
+    for n in range(0, N, 9):
+        exact = _f32_fraction(a.reshape(N, -1)[n, 0]) / 127
+        got = _bf16_bits_value(int(sb.reshape(N, -1)[n, 0]))
+        assert abs(got - exact) <= exact * Fraction(1, 2 ** 8) * Fraction(1001, 1000)
+
+
+def pin_w4_roundtrip_bound(seed=8, N=64, K=1024):
+    """P2: unclamped codes are within s/2 (+ slack); clamped ones within
+    s/2 + (hi - lo) * 2^-11 (the fp16 rounding of the scale)."""
+    W = synth.weight(seed, K, N, outliers=True)
+    q, s16, z = OQ.quantize_w4g128(W)
+    s = np.repeat(s16.astype(np.float64), 128, axis=1)
+    zf = np.repeat(z.astype(np.float64), 128, axis=1)
+    wd = (q.astype(np.float64) - zf) * s
+    err = np.abs(W.astype(np.float64) - wd)
+    Wg = W.reshape(N, -1, 128).astype(np.float64)
+    rng_ = np.repeat(Wg.max(axis=2) - Wg.min(axis=2), 128, axis=1)
+    assert np.all(err <= s / 2 + rng_ * 2.0 ** -11 + np.abs(W) * 2.0 ** -22)
+    assert q.max() <= 15 and z.max() <= 15
+
+
+def pin_nearest_code_bruteforce():
+    """P3: every unclamped code minimises |w - (c - z) * s| over all codes c."""
+    rng = np.random.default_rng(99)
+    for trial in range(20):
+        W = (rng.standard_normal((2, 128)) * 0.02).astype(np.float32)
+        q, sb = OQ.quantize_w8(W, 128)
+        s = OQ.bf16_bits_to_f32(sb).astype(np.float64)
+        for n in range(2):
+            for k in range(0, 128, 5):
+                w = float(W[n, k])
+                errs = [abs(w - c * s[n, 0]) for c in range(-127, 128)]
+                best = min(errs)
+                assert abs(errs[int(q[n, k]) + 127] - best) <= 1e-12 * max(1.0, abs(w)), (trial, n, k)
+        q4, s16, z = OQ.quantize_w4g128(W)
+        for n in range(2):
+            sv = float(s16[n, 0])
+            span = float(W[n].max()) - float(W[n].min())
+            for k in range(0, 128, 3):
+                w = float(W[n, k])
+                errs = [abs(w - (c - int(z[n, 0])) * sv) for c in range(16)]
+                c0 = int(q4[n, k])
+                if 0 < c0 < 15:
+                    assert abs(errs[c0] - min(errs)) <= 1e-12, (trial, n, k)
+                else:
+                    assert errs[c0] <= sv / 2 + span * 2.0 ** -11 + 1e-12, (trial, n, k)
+
+
+def pin_all_zero():
+    """P4: an all-zero row or group stores scale 0, codes equal to the zero-point,
+    and dequantises to exactly 0."""
+    W = synth.weight(3, 256, 16)
+    W[3, :] = 0
+    W[5, 128:] = 0
+    for fmt in ("w8pc", "w8g128", "w4g128"):
+        P = OQ.pack(fmt, W)
+        Wd = OQ.dequant(P)
+        assert not np.any(Wd[3]), fmt
+        sb = P["scales"].view(np.uint16)
+        if fmt == "w8pc":
+            assert sb[3] == 0 and not np.any(P["qweight"][3])
+        else:
+            assert not np.any(sb[3]) and sb[5, 1] == 0 and sb[5, 0] != 0
+            assert not np.any(Wd[5, 128:])
+        if fmt == "w4g128":
+            for g in range(2):
+                assert _decode_w4_zero(P, 3, g) == 0
+            assert all(_decode_w4_codes(P, 3, k) == _decode_w4_zero(P, 3, k // 128) for k in range(256))
+
+
+# ------------------------------------------------------------------- the linear
+def pin_one_hot_golden():
+    """P5 on the hand-derived W4 example: x = e_k selects (q - z) * s exactly."""
+    W, exp_q, exp_s, exp_z = _golden_w4_weight()
+    P = OQ.pack("w4g128", W)
+    ks = [0, 1, 4, 5, 127, 128, 129, 130, 131, 255]
+    x = synth.one_hot_activation(W.shape[1], ks)
+    y = OL.ref_linear(x, P)
+    for m, k in enumerate(ks):
+        g = k // 128
+        s = _fp16_value(np.array(exp_s[g], dtype=np.uint16).view(np.float16))
+        want = (exp_q[0, k] - exp_z[g]) * s
+        assert Fraction(float(y[m, 0])) == want, (k, y[m, 0], float(want))
+        assert not np.any(y[m, 1:])
+
+
+def pin_one_hot_random(fmt="w8g128", K=512, N=40):
+    W = synth.weight(11, K, N, outliers=fmt == "w4g128")
+    P = OQ.pack(fmt, W)
+    ks = [0, 127, 128, 300, K - 1]
+    y = OL.ref_linear(synth.one_hot_activation(K, ks), P)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            assert Fraction(float(y[m, n])) == _exact_dequant(P, n, k), (fmt, m, n)
+
+
+def pin_identity(fmt="w4g128", K=256, N=24):
+    """P6: x = I gives y = dequant(W)^T exactly."""
+    W = synth.weight(12, K, N, outliers=True)
+    P = OQ.pack(fmt, W)
+    y = OL.ref_linear(synth.identity_activation(K), P)
+    for n in range(N):
+        for k in range(0, K, 17):
+            assert Fraction(float(y[k, n])) == _exact_dequant(P, n, k)
+
+
+def pin_bruteforce(fmt, K, N=11, M=3, seed=5):
+    """P7: a triple loop over exact rationals (codes decoded by hand, bf16 x decoded
+    by hand) agrees with the NumPy path to fp64 rounding; N is not a multiple of
+    the chunk so a dropped tail shows."""
+    W = synth.weight(seed, K, N if fmt != "w4g128" else 16, outliers=fmt == "w4g128")
+    N = W.shape[0]
+    P = OQ.pack(fmt, W)
+    x = synth.activation(seed, K, M)
+    y = OL.ref_linear(x, P, chunk=5)
+    for m in range(M):
+        xv = [_bf16_bits_value(int(b)) for b in x[m]]
+        for n in range(N):
+            exact = sum(xv[k] * _exact_dequant(P, n, k) for k in range(K))
+            err = abs(Fraction(float(y[m, n])) - exact)
+            scale = sum(abs(xv[k] * _exact_dequant(P, n, k)) for k in range(K))
+            assert err <= scale * Fraction(K + 2, 2 ** 53), (fmt, m, n, float(err))
+
+
+def pin_library_factorisation(seed=21):
+    """P8: per channel y = (x @ q^T) * s; group-128 y = sum_g s_g (x_g @ (q-z)_g^T),
+    with plain NumPy fp64 on the codes."""
+    K, N, M = 512, 48, 4
+    x = synth.activation(seed, K, M)
+    xf = OQ.bf16_bits_to_f32(x).astype(np.float64)
+    W = synth.weight(seed, K, N)
+    P = OQ.pack("w8pc", W)
+    want = (xf @ P["qweight"].astype(np.float64).T) * OQ.bf16_bits_to_f32(P["scales"]).astype(np.float64)[None, :]
+    assert np.allclose(OL.ref_linear(x, P), want, rtol=1e-12, atol=1e-12)
+    Wo = synth.weight(seed, K, N, outliers=True)
+    P4 = OQ.pack("w4g128", Wo)
+    q, s16, z = OQ.unpack_w4g128(P4)
+    want = np.zeros((M, N))
+    for g in range(K // 128):
+        d = q[:, 128 * g:128 * (g + 1)].astype(np.float64) - z[:, g:g + 1].astype(np.float64)
+        want += (xf[:, 128 * g:128 * (g + 1)] @ d.T) * s16[:, g].astype(np.float64)[None, :]
+    assert np.allclose(OL.ref_linear(x, P4), want, rtol=1e-12, atol=1e-12)
+    P8 = OQ.pack("w8g128", W)
+    sg = OQ.bf16_bits_to_f32(P8["scales"]).astype(np.float64)
+    want = np.zeros((M, N))
+    for g in range(K // 128):
+        want += (xf[:, 128 * g:128 * (g + 1)] @ P8["qweight"][:, 128 * g:128 * (g + 1)].astype(np.float64).T) * sg[:, g][None, :]
+    assert np.allclose(OL.ref_linear(x, P8), want, rtol=1e-12, atol=1e-12)
+
+
+def pin_invariants():
+    """P9: x = 0 gives y = 0; x * 2^j gives y * 2^j exactly; sampled columns
+    equal the full product; chunking does not change the result."""
+    K, N = 384, 40
+    W = synth.weight(31, K, N, outliers=True)
+    P = OQ.pack("w4g128", W)
+    assert not np.any(OL.ref_linear(np.zeros((2, K), dtype=np.uint16), P))
+    x = synth.activation(31, K, 3)
+    y = OL.ref_linear(x, P)
+    x4 = OQ.bf16_rne_bits(OQ.bf16_bits_to_f32(x) * np.float32(4.0))
+    assert np.array_equal(OL.ref_linear(x4, P), 4.0 * y)
+    cols = [0, 7, 13, 39]
+    assert np.array_equal(OL.ref_linear_columns(x, P, cols), y[:, cols])
+    assert np.array_equal(OL.ref_linear(x, P, chunk=7), y)
+
+
+def pin_compare():
+    """The tolerance rule |y - y_ref| <= 1e-2 * max(1, |y_ref|) on crafted values."""
+    ref = np.array([[0.0, 0.5, 100.0, -3.0]])
+    ok = OQ.bf16_rne_bits(np.array([[0.0078125, 0.5, 100.5, -3.0]], dtype=np.float32))
+    st = OL.compare(ok, ref)
+    assert st["fails"] == 0 and abs(st["max_ratio"] - 0.78125) < 1e-12, st
+    bad = OQ.bf16_rne_bits(np.array([[0.015625, 0.5, 102.0, -3.0]], dtype=np.float32))
+    st = OL.compare(bad, ref)
+    assert st["fails"] == 2, st
+
+
+def pin_dispatch():
+    """Token count numel/shape[-1]; fewer than 8 tokens -> GEMV."""
+    assert OL.token_count((7, 5120)) == 7 and OL.token_count((2, 3, 64)) == 6
+    assert OL.use_gemv(1) and OL.use_gemv(7) and not OL.use_gemv(8) and not OL.use_gemv(2048)
+
+
+ALL_PINS = [
+    pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
+    pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
+    pin_nearest_code_bruteforce, pin_all_zero, pin_one_hot_golden,
+    lambda: pin_one_hot_random("w8pc"), lambda: pin_one_hot_random("w8g128"),
+    lambda: pin_one_hot_random("w4g128"), pin_identity,
+    lambda: pin_bruteforce("w8pc", 48), lambda: pin_bruteforce("w8g128", 128),
+    lambda: pin_bruteforce("w4g128", 128), pin_library_factorisation, pin_invariants,
+    pin_compare, pin_dispatch,
+]
+
+
+def run_all_pins():
+    for p in ALL_PINS:
+        p()
