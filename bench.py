@@ -1,0 +1,314 @@
+"""Benchmark of the weight-only quantized linear on one MI355X.
+
+One step = one decode pass of the W8A16 per-channel projection set at M = 1
+token: wq_linear (-> split-K GEMV) on the four weight shapes (K, N) =
+(5120, 27648) fused gate+up, (13824, 5120) down, (5120, 7168) fused QKV,
+(6144, 5120) out-proj.  Weights are int8 codes with bf16 per-channel scales, x is
+bf16 ~ N(0, 1), y bf16.  Every call reads a different copy of its weight from a
+rotation pool of >= 1.28 GB per shape (five times the 256 MB Infinity Cache), so
+the weights come from HBM, as in the Marlin benchmark page's fixed-input
+projection check (weights rotating over more than five times the cache, each
+captured graph running whole rotations).  The timed steps run as one HIP graph
+replay; split_k is tuned per shape first, as the awq heuristic page describes
+(grid {1..32}, 1000 warm-up + 1000 timed calls).
+
+The headline value is whole-step weight-stream throughput in GB/s of
+algorithmic bytes (packed codes + scales + x + y, each counted once).  The JSON
+line also carries the roofline of the GEMV kernel, the CPU oracle timed on the
+host cores, and (unless --quick) per-shape detail for the other workloads: the
+W8A16 M sweep, W4A16 group-128 GEMV, the split-K stress shapes and the prefill
+GEMM (TFLOP/s against the bf16 MFMA peak).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ROTATE_BYTES = 1.28e9           # >= 5 x 256 MB Infinity Cache
+METRIC = "W8A16/W4A16 GEMV weight GB/s & % HBM peak at M=1; prefill GEMM TFLOP/s"
+DECODE_SHAPES = [(5120, 27648), (13824, 5120), (5120, 7168), (6144, 5120)]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_w8pc_decode_traffic.json")
+
+
+def algorithmic_bytes(fmt: str, K: int, N: int, M: int) -> int:
+    """Packed codes + scales (+ zeros) + x + y, each counted once."""
+    G = K // 128
+    if fmt == "w8pc":
+        w = K * N + 2 * N
+    elif fmt == "w8g128":
+        w = K * N + 2 * N * G
+    else:
+        w = K * N // 2 + 2 * N * G + G * (N // 8) * 4
+    return w + 2 * M * K + 2 * M * N
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Pool:
+    """Rotation pool of identical packed copies of one seeded weight on the GPU."""
+
+    def __init__(self, wq, torch, cfg: int, fmt: str, K: int, N: int, M: int, min_copies: int = 2):
+        import synth
+        self.fmt, self.K, self.N, self.M, self.cfg = fmt, K, N, M, cfg
+        W = synth.weight(cfg, K, N, synth.uses_outliers(fmt))
+        Wd = torch.from_numpy(W).to("cuda")
+        base = wq.quantize(Wd, fmt)
+        del Wd
+        self.W = W
+        n = max(min_copies, int(np.ceil(ROTATE_BYTES / base.nbytes())))
+        self.copies = [base] + [base.clone() for _ in range(n - 1)]
+        xb = synth.activation(cfg, K, M)
+        self.x_bits = xb
+        self.x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16)
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.ws = wq.workspace(wq.wq_workspace_size(base, M))
+        self.i = 0
+
+    def call(self, wq):
+        w = self.copies[self.i]
+        self.i = (self.i + 1) % len(self.copies)
+        wq.wq_linear(w, self.x, self.y, ws=self.ws)
+
+    def bytes_per_call(self) -> int:
+        return algorithmic_bytes(self.fmt, self.K, self.N, self.M)
+
+    def check(self, wq, torch, cols: int = 128) -> dict:
+        """Parity of copy 0 on sampled output channels against the oracle."""
+        import oracle
+        self.i = 0
+        self.call(wq)
+        torch.cuda.synchronize()
+        blocks = np.unique(np.linspace(0, self.N // 8 - 1, cols // 8).astype(int))
+        rows = (blocks[:, None] * 8 + np.arange(8)[None, :]).ravel()
+        P = oracle.pack(self.fmt, self.W[rows])
+        y = self.y.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
+        st = oracle.compare(y, oracle.ref_linear(self.x_bits, P))
+        self.i = 0
+        return st
+
+    def free(self):
+        self.copies = []
+        self.W = None
+
+
+def time_graph(torch, fn, n_calls: int, reps: int = 3):
+    """Capture n_calls of fn() in one HIP graph; return the median replay time (ms)
+    measured with HIP events on the capturing stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(n_calls):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+    del g
+    return float(np.median(times))
+
+
+def device_warmup(torch):
+    """100 bf16 8192 x 8192 products (the awq heuristic page's device warm-up)."""
+    a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    for _ in range(100):
+        torch.mm(a, a)
+    torch.cuda.synchronize()
+
+
+def tune(wq, pool: Pool, warmup: int, iters: int):
+    chosen, lat = wq.wq_tune(pool.copies, pool.x, pool.y, pool.ws, warmup=warmup, iters=iters)
+    return chosen, lat
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """The oracle (dequantise to fp32 + fp64 matmul) on the host cores, over the
+    same four weights at M = 1, repeated until budget_s of CPU work."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    packed = []
+    for K, N in DECODE_SHAPES:
+        W = synth.weight(2, K, N)
+        packed.append((oracle.pack("w8pc", W), synth.activation(2, K, 1), K, N))
+        del W
+    done_bytes, t0, passes = 0, time.perf_counter(), 0
+    while True:
+        for P, x, K, N in packed:
+            oracle.ref_linear(x, P)
+            done_bytes += algorithmic_bytes("w8pc", K, N, 1)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} pass(es) of the oracle's dequantise+fp64 matmul over the 4 decode "
+                      f"weights at M=1 ({dt:.1f} s; elementwise dequant single-threaded, BLAS {threads} threads; "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores)"}
+
+
+def traffic_entry(kernel_src_sha: str):
+    """Measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy kernel), only while the GEMV source is the
+    one the counters were taken with."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if d.get("kernel_src_sha256") != kernel_src_sha:
+        return None
+    return d.get("bytes_per_step_avg_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only (no per-workload detail)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune-iters", type=int, default=1000)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_decode_amd.wq as wq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    device_warmup(torch)
+    log("warm-up done")
+
+    # ---------------- headline: W8A16 per-channel decode projections at M = 1
+    pools = [Pool(wq, torch, 2, "w8pc", K, N, 1) for K, N in DECODE_SHAPES]
+    tuned = {}
+    for p in pools:
+        tuned[(p.K, p.N)] = tune(wq, p, args.tune_iters, args.tune_iters)
+        log(f"tuned w8pc K={p.K} N={p.N} M=1: split_k={tuned[(p.K, p.N)][0]} lat_us={tuned[(p.K, p.N)][1]}")
+    parity = {f"{p.K}x{p.N}": p.check(wq, torch) for p in pools}
+    for k, st in parity.items():
+        if st["fails"]:
+            raise SystemExit(f"parity failure on {k}: {st}")
+
+    def step():
+        for p in pools:
+            p.call(wq)
+
+    bytes_step = sum(p.bytes_per_call() for p in pools)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_graph(torch, step, args.steps, reps=1)
+    ms_per_step = ms / args.steps
+    value = bytes_step / (ms_per_step / 1e3) / 1e9
+    log(f"headline: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s")
+
+    detail = {"decode_w8pc_m1": {}}
+    for p in pools:
+        per = time_graph(torch, lambda p=p: p.call(wq), 2 * len(p.copies)) / (2 * len(p.copies))
+        gbs = p.bytes_per_call() / (per / 1e3) / 1e9
+        detail["decode_w8pc_m1"][f"{p.K}x{p.N}"] = {
+            "us": round(per * 1e3, 3), "GB/s": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "split_k": tuned[(p.K, p.N)][0], "copies": len(p.copies), "parity": parity[f"{p.K}x{p.N}"]}
+    for p in pools:
+        p.free()
+    del pools
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        detail.update(run_detail(wq, torch, args))
+
+    src = open(os.path.join(ROOT, "gemm_decode_amd", "csrc", "wq_gemv.hip"), "rb").read()
+    src_sha = hashlib.sha256(src).hexdigest()
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "W8A16 per-channel decode GEMV, M=1, (K,N) in (5120,27648) (13824,5120) "
+                               "(5120,7168) (6144,5120), int8 codes + bf16 scales, x bf16 N(0,1), "
+                               "W N(0,0.02^2), rotating weight copies",
+                   "M": 1, "shapes": DECODE_SHAPES, "kernel": "gemv_kernel<W8_PC, M=1>"},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_entry(src_sha),
+                     "algorithmic_bytes_per_step": bytes_step, "launches_per_step": 4},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_detail(wq, torch, args) -> dict:
+    """Secondary workloads, each timed as graph replays over its rotation pool."""
+    out = {}
+
+    def measure(cfg, fmt, K, N, M, tune_it=True, check=True):
+        p = Pool(wq, torch, cfg, fmt, K, N, M)
+        rec = {}
+        if tune_it:
+            rec["tuned"], rec["tune_lat_us"] = tune(wq, p, 200, 200)
+        if check:
+            rec["parity"] = p.check(wq, torch)
+        n = 2 * len(p.copies)
+        per = time_graph(torch, lambda: p.call(wq), n) / n
+        gbs = p.bytes_per_call() / (per / 1e3) / 1e9
+        tf = 2.0 * M * K * N / (per / 1e3) / 1e12
+        rec.update({"us": round(per * 1e3, 3), "GB/s": round(gbs, 1),
+                    "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1), "TFLOP/s": round(tf, 2),
+                    "pct_mfma": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)})
+        log(f"cfg{cfg} {fmt} K={K} N={N} M={M}: {rec['us']} us {rec['GB/s']} GB/s {rec['TFLOP/s']} TF/s")
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+        return rec
+
+    out["decode_w8pc_msweep"] = {f"{K}x{N}_M{M}": measure(2, "w8pc", K, N, M)
+                                 for K, N in DECODE_SHAPES for M in (2, 4, 7)}
+    out["decode_w4g128"] = {f"{K}x{N}_M{M}": measure(3, "w4g128", K, N, M)
+                            for K, N in [(5120, 27648), (13824, 5120)] for M in (1, 4)}
+    out["splitk_stress"] = {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
+                            for K, N in [(27648, 5120), (5120, 151936)]
+                            for fmt in ("w8pc", "w8g128", "w4g128")}
+    out["prefill_gemm"] = {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
+                           for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
+                           for M in (8, 64, 512, 2048)}
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,442 @@
+// C ABI entry points: validation, workspace sizing, the GEMV/GEMM dispatch and the
+// split-K / tile tuner with its persisted cache.  Host code only; kernels live in
+// the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cinttypes>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "wq_internal.h"
+
+namespace wq {
+
+int64_t gemv_max_rows();
+
+namespace {
+thread_local std::string g_err;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+struct Key {
+  std::string tag;
+  int fmt;
+  int64_t K, N, M;
+  int kind;
+  bool operator<(const Key& o) const {
+    return std::tie(tag, fmt, K, N, M, kind) < std::tie(o.tag, o.fmt, o.K, o.N, o.M, o.kind);
+  }
+};
+std::mutex g_cache_mu;
+std::map<Key, int> g_cache;
+
+std::mutex g_dev_mu;
+std::map<int, std::string> g_dev_tags;
+
+int64_t split_units(const wq_weight* w) { return w->K / split_granule(w->fmt); }
+
+// Largest power of two <= min(v, units, 32).
+int clamp_split(int v, int64_t units) {
+  int s = 1;
+  while (s * 2 <= v && s * 2 <= units && s * 2 <= kMaxSplit) s *= 2;
+  return s;
+}
+
+constexpr int kDefaultSplit = 8;  // untuned default of the awq tuning heuristic
+constexpr int kDefaultTile = 1;
+
+std::string resolve_tag(const char* tag) {
+  if (tag && tag[0]) return std::string(tag);
+  return current_device_tag();
+}
+
+bool cache_lookup(const std::string& tag, int fmt, int64_t K, int64_t N, int64_t M, int kind,
+                  int* v) {
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  auto it = g_cache.find(Key{tag, fmt, K, N, M, kind});
+  if (it == g_cache.end()) return false;
+  *v = it->second;
+  return true;
+}
+
+wq_status check_gemv_split(const wq_weight* w, int M, int split, void* ws, size_t ws_bytes) {
+  const int64_t units = split_units(w);
+  if (!pow2(split) || split > kMaxSplit || split > units)
+    return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= 32 and <= K/" +
+                                        std::to_string(split_granule(w->fmt)));
+  if (split > 1) {
+    if (w->N > gemv_max_rows())
+      return fail(WQ_ERR_UNSUPPORTED, "split-K GEMV supports N <= " + std::to_string(gemv_max_rows()));
+    if (!ws) return fail(WQ_ERR_WORKSPACE, "split_k > 1 needs a workspace");
+    if (!aligned(ws, 256)) return fail(WQ_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    if (ws_bytes < gemv_workspace_bytes(w->N, M, split))
+      return fail(WQ_ERR_WORKSPACE, "workspace too small: need " +
+                                        std::to_string(gemv_workspace_bytes(w->N, M, split)) + " bytes");
+  }
+  return WQ_OK;
+}
+
+wq_status check_xy(const void* x, const void* y, int64_t M) {
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (!x || !y) return fail(WQ_ERR_INVALID_ARG, "x and y must not be NULL");
+  if (!aligned(x, 16)) return fail(WQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(WQ_ERR_ALIGNMENT, "y must be 2-byte aligned");
+  return WQ_OK;
+}
+
+int resolve_split(const wq_weight* w, int64_t M) {
+  int v = 0;
+  if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) return v;
+  return clamp_split(kDefaultSplit, split_units(w));
+}
+
+int resolve_tile(const wq_weight* w, int64_t M) {
+  int v = 0;
+  if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMM, &v)) return v;
+  return kDefaultTile;
+}
+
+wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
+                    size_t ws_bytes, void* stream) {
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  if ((st = check_xy(x, y, M)) != WQ_OK) return st;
+  if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
+  int split = split_k == 0 ? resolve_split(w, M) : split_k;
+  if (split_k == 0 && split > 1 && (!ws || ws_bytes < gemv_workspace_bytes(w->N, M, split)))
+    split = 1;  // tuned value needs more workspace than given: fall back to one slice
+  if ((st = check_gemv_split(w, (int)M, split, ws, ws_bytes)) != WQ_OK) return st;
+  return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, ws, (hipStream_t)stream);
+}
+
+wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* stream) {
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  if ((st = check_xy(x, y, M)) != WQ_OK) return st;
+  if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
+  const int t = tile == 0 ? resolve_tile(w, M) : tile;
+  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, (hipStream_t)stream);
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_err = msg; }
+wq_status fail(wq_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+wq_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return (e == hipErrorNoDevice || e == hipErrorInvalidDevice) ? WQ_ERR_NO_DEVICE : WQ_ERR_HIP;
+}
+
+std::string current_device_tag() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return std::string();
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_tags.find(dev);
+  if (it != g_dev_tags.end()) return it->second;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return std::string();
+  std::string arch(p.gcnArchName);
+  const size_t colon = arch.find(':');
+  if (colon != std::string::npos) arch.resize(colon);
+  std::string tag = arch + ":" + std::to_string(p.multiProcessorCount);
+  g_dev_tags[dev] = tag;
+  return tag;
+}
+
+wq_status check_shape(int fmt, int64_t K, int64_t N) {
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G128) return fail(WQ_ERR_UNSUPPORTED, "unknown format");
+  if (K <= 0 || N <= 0) return fail(WQ_ERR_INVALID_ARG, "K and N must be positive");
+  if (K > (1LL << 22) || N > (1LL << 30)) return fail(WQ_ERR_UNSUPPORTED, "K or N too large");
+  if (K % 16) return fail(WQ_ERR_UNSUPPORTED, "K must be a multiple of 16");
+  if (fmt != WQ_FMT_W8_PC && K % kGroup) return fail(WQ_ERR_UNSUPPORTED, "group-128 formats need K % 128 == 0");
+  if (fmt == WQ_FMT_W4_G128 && N % 8) return fail(WQ_ERR_UNSUPPORTED, "W4 needs N % 8 == 0");
+  return WQ_OK;
+}
+
+wq_status check_weight(const wq_weight* w, int want_layout) {
+  if (!w) return fail(WQ_ERR_INVALID_ARG, "weight descriptor is NULL");
+  wq_status st = check_shape(w->fmt, w->K, w->N);
+  if (st != WQ_OK) return st;
+  if (w->layout != want_layout)
+    return fail(WQ_ERR_UNSUPPORTED, want_layout == WQ_LAYOUT_GFX950
+                                        ? "compute kernels need the GFX950 layout (call wq_repack)"
+                                        : "expected the CANONICAL layout");
+  if (!w->qweight || !w->scales) return fail(WQ_ERR_INVALID_ARG, "qweight/scales must not be NULL");
+  if (w->fmt == WQ_FMT_W4_G128 && !w->zeros) return fail(WQ_ERR_INVALID_ARG, "W4 needs zeros");
+  if (!aligned(w->qweight, 16)) return fail(WQ_ERR_ALIGNMENT, "qweight must be 16-byte aligned");
+  if (!aligned(w->scales, 2)) return fail(WQ_ERR_ALIGNMENT, "scales must be 2-byte aligned");
+  if (w->fmt == WQ_FMT_W4_G128 && want_layout == WQ_LAYOUT_CANONICAL && !aligned(w->zeros, 4))
+    return fail(WQ_ERR_ALIGNMENT, "canonical zeros must be 4-byte aligned");
+  return WQ_OK;
+}
+
+}  // namespace wq
+
+using namespace wq;
+
+extern "C" {
+
+int wq_abi_version(void) { return WQ_ABI_VERSION; }
+
+const char* wq_status_string(int s) {
+  switch (s) {
+    case WQ_OK: return "ok";
+    case WQ_ERR_INVALID_ARG: return "invalid argument";
+    case WQ_ERR_UNSUPPORTED: return "unsupported format, layout or shape";
+    case WQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case WQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case WQ_ERR_NO_DEVICE: return "no HIP device";
+    case WQ_ERR_HIP: return "HIP runtime error";
+    case WQ_ERR_CACHE_IO: return "tuner cache I/O error";
+  }
+  return "unknown status";
+}
+
+const char* wq_last_error(void) { return g_err.c_str(); }
+
+wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb, size_t* sb,
+                          size_t* zb) {
+  wq_status st = check_shape(fmt, K, N);
+  if (st != WQ_OK) return st;
+  if (layout != WQ_LAYOUT_CANONICAL && layout != WQ_LAYOUT_GFX950)
+    return fail(WQ_ERR_UNSUPPORTED, "unknown layout");
+  const int64_t G = K / kGroup;
+  size_t q = 0, s = 0, z = 0;
+  switch (fmt) {
+    case WQ_FMT_W8_PC: q = (size_t)(K * N); s = (size_t)(2 * N); break;
+    case WQ_FMT_W8_G128: q = (size_t)(K * N); s = (size_t)(2 * N * G); break;
+    case WQ_FMT_W4_G128:
+      q = (size_t)(K * N / 2);
+      s = (size_t)(2 * N * G);
+      z = layout == WQ_LAYOUT_CANONICAL ? (size_t)(G * (N / 8) * 4) : (size_t)(N * ((G + 1) / 2));
+      break;
+  }
+  if (qb) *qb = q;
+  if (sb) *sb = s;
+  if (zb) *zb = z;
+  return WQ_OK;
+}
+
+int wq_dispatch_kind(int64_t M) {
+  if (M < 1) return -1;
+  return M <= kGemvMaxM ? WQ_KIND_GEMV : WQ_KIND_GEMM;
+}
+
+wq_status wq_pack(const float* w, const wq_weight* out, void* stream) {
+  wq_status st = check_weight(out, WQ_LAYOUT_CANONICAL);
+  if (st != WQ_OK) return st;
+  if (!w) return fail(WQ_ERR_INVALID_ARG, "w must not be NULL");
+  if (!aligned(w, 16)) return fail(WQ_ERR_ALIGNMENT, "w must be 16-byte aligned");
+  return launch_pack(w, out, (hipStream_t)stream);
+}
+
+static wq_status repack_common(const wq_weight* src, const wq_weight* dst, int from, int to,
+                               void* stream) {
+  wq_status st = check_weight(src, from);
+  if (st != WQ_OK) return st;
+  if ((st = check_weight(dst, to)) != WQ_OK) return st;
+  if (src->fmt != dst->fmt || src->K != dst->K || src->N != dst->N)
+    return fail(WQ_ERR_INVALID_ARG, "src and dst differ in format or shape");
+  if (src->qweight == dst->qweight || src->scales == dst->scales ||
+      (src->zeros && src->zeros == dst->zeros))
+    return fail(WQ_ERR_INVALID_ARG, "repack cannot run in place");
+  return launch_repack(src, dst, to == WQ_LAYOUT_GFX950, (hipStream_t)stream);
+}
+
+wq_status wq_repack(const wq_weight* src, const wq_weight* dst, void* stream) {
+  return repack_common(src, dst, WQ_LAYOUT_CANONICAL, WQ_LAYOUT_GFX950, stream);
+}
+
+wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream) {
+  return repack_common(src, dst, WQ_LAYOUT_GFX950, WQ_LAYOUT_CANONICAL, stream);
+}
+
+wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
+  if (!w || !bytes) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  wq_status st = check_shape(w->fmt, w->K, w->N);
+  if (st != WQ_OK) return st;
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  *bytes = M <= kGemvMaxM ? gemv_workspace_bytes(w->N, M, kMaxSplit) : 0;
+  return WQ_OK;
+}
+
+wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
+                  size_t ws_bytes, void* stream) {
+  return gemv_impl(w, x, M, y, split_k, ws, ws_bytes, stream);
+}
+
+wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
+                  size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return gemm_impl(w, x, M, y, tile, stream);
+}
+
+wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, ws, ws_bytes, stream);
+  return gemm_impl(w, x, M, y, 0, stream);
+}
+
+int wq_tune_pick(const double* lat, int n) {
+  if (!lat || n < 1) return -1;
+  int best = -1;
+  for (int i = 0; i < n; ++i) {
+    if (lat[i] < 0) continue;  // candidate not run
+    if (best < 0 || lat[best] >= lat[i]) best = i;
+  }
+  return best;
+}
+
+wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y, void* ws,
+                  size_t ws_bytes, int warmup, int iters, void* stream, int* chosen, double* lat_us) {
+  if (!copies || n_copies < 1 || !chosen || iters < 1 || warmup < 0)
+    return fail(WQ_ERR_INVALID_ARG, "wq_tune: bad arguments");
+  wq_status st;
+  for (int i = 0; i < n_copies; ++i) {
+    if ((st = check_weight(&copies[i], WQ_LAYOUT_GFX950)) != WQ_OK) return st;
+    if (copies[i].fmt != copies[0].fmt || copies[i].K != copies[0].K || copies[i].N != copies[0].N)
+      return fail(WQ_ERR_INVALID_ARG, "wq_tune: copies differ in format or shape");
+  }
+  if ((st = check_xy(x, y, M)) != WQ_OK) return st;
+  const bool gemv = wq_dispatch_kind(M) == WQ_KIND_GEMV;
+  std::vector<int> cand;
+  if (gemv) {
+    for (int s = 1; s <= kMaxSplit; s *= 2) cand.push_back(s);
+  } else {
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back(t);
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  hipEvent_t e0, e1;
+  WQ_HIP_CHECK(hipEventCreate(&e0));
+  WQ_HIP_CHECK(hipEventCreate(&e1));
+  std::vector<double> lat(cand.size(), -1.0);
+  int rot = 0;
+  for (size_t c = 0; c < cand.size(); ++c) {
+    if (gemv) {
+      const int s = cand[c];
+      if (s > split_units(&copies[0])) continue;
+      if (s > 1 && (!ws || ws_bytes < gemv_workspace_bytes(copies[0].N, M, s))) continue;
+    }
+    auto run = [&]() -> wq_status {
+      const wq_weight* w = &copies[rot];
+      rot = (rot + 1) % n_copies;
+      return gemv ? gemv_impl(w, x, M, y, cand[c], ws, ws_bytes, stream)
+                  : gemm_impl(w, x, M, y, cand[c], stream);
+    };
+    for (int i = 0; i < warmup; ++i)
+      if ((st = run()) != WQ_OK) goto out;
+    if (hipEventRecord(e0, hs) != hipSuccess) { st = fail(WQ_ERR_HIP, "hipEventRecord"); goto out; }
+    for (int i = 0; i < iters; ++i)
+      if ((st = run()) != WQ_OK) goto out;
+    if (hipEventRecord(e1, hs) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
+      st = fail(WQ_ERR_HIP, "hipEventSynchronize");
+      goto out;
+    }
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    lat[c] = (double)ms * 1000.0 / iters;
+  }
+  {
+    const int best = wq_tune_pick(lat.data(), (int)lat.size());
+    if (best < 0) {
+      st = fail(WQ_ERR_WORKSPACE, "wq_tune: no candidate could run");
+      goto out;
+    }
+    *chosen = cand[best];
+    if (lat_us)
+      for (size_t c = 0; c < cand.size(); ++c) lat_us[c] = lat[c];
+    st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M,
+                           gemv ? WQ_KIND_GEMV : WQ_KIND_GEMM, cand[best]);
+  }
+out:
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return st;
+}
+
+wq_status wq_tune_cache_set(const char* tag, int fmt, int64_t K, int64_t N, int64_t M, int kind,
+                            int value) {
+  wq_status st = check_shape(fmt, K, N);
+  if (st != WQ_OK) return st;
+  if (M < 1 || (kind != WQ_KIND_GEMV && kind != WQ_KIND_GEMM))
+    return fail(WQ_ERR_INVALID_ARG, "bad M or kind");
+  if (kind == WQ_KIND_GEMV && (!pow2(value) || value > kMaxSplit))
+    return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= 32");
+  if (kind == WQ_KIND_GEMM && (value < 1 || value > WQ_GEMM_TILES))
+    return fail(WQ_ERR_INVALID_ARG, "bad tile id");
+  const std::string t = resolve_tag(tag);
+  if (t.empty()) return fail(WQ_ERR_NO_DEVICE, "no device tag");
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  g_cache[Key{t, fmt, K, N, M, kind}] = value;
+  return WQ_OK;
+}
+
+wq_status wq_tune_cache_get(const char* tag, int fmt, int64_t K, int64_t N, int64_t M, int kind,
+                            int* value) {
+  if (!value) return fail(WQ_ERR_INVALID_ARG, "value is NULL");
+  const std::string t = resolve_tag(tag);
+  if (t.empty()) return fail(WQ_ERR_NO_DEVICE, "no device tag");
+  if (!cache_lookup(t, fmt, K, N, M, kind, value)) return fail(WQ_ERR_INVALID_ARG, "no entry");
+  return WQ_OK;
+}
+
+wq_status wq_tune_cache_clear(void) {
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  g_cache.clear();
+  return WQ_OK;
+}
+
+wq_status wq_tune_cache_save(const char* path) {
+  if (!path) return fail(WQ_ERR_INVALID_ARG, "path is NULL");
+  FILE* f = std::fopen(path, "w");
+  if (!f) return fail(WQ_ERR_CACHE_IO, std::string("cannot write ") + path);
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  std::fprintf(f, "# wq tuner cache v1: tag fmt K N M kind value\n");
+  for (const auto& kv : g_cache)
+    std::fprintf(f, "%s %d %" PRId64 " %" PRId64 " %" PRId64 " %d %d\n", kv.first.tag.c_str(),
+                 kv.first.fmt, kv.first.K, kv.first.N, kv.first.M, kv.first.kind, kv.second);
+  const bool ok = std::fclose(f) == 0;
+  return ok ? WQ_OK : fail(WQ_ERR_CACHE_IO, std::string("cannot write ") + path);
+}
+
+wq_status wq_tune_cache_load(const char* path) {
+  if (!path) return fail(WQ_ERR_INVALID_ARG, "path is NULL");
+  FILE* f = std::fopen(path, "r");
+  if (!f) return fail(WQ_ERR_CACHE_IO, std::string("cannot read ") + path);
+  std::vector<std::pair<Key, int>> entries;
+  char line[512];
+  bool bad = false;
+  while (std::fgets(line, sizeof line, f)) {
+    if (line[0] == '#' || line[0] == '\n') continue;
+    char tag[256];
+    int fmt, kind, value;
+    int64_t K, N, M;
+    if (std::sscanf(line, "%255s %d %" SCNd64 " %" SCNd64 " %" SCNd64 " %d %d", tag, &fmt, &K, &N, &M,
+                    &kind, &value) != 7 ||
+        check_shape(fmt, K, N) != WQ_OK || M < 1 || (kind != WQ_KIND_GEMV && kind != WQ_KIND_GEMM) ||
+        (kind == WQ_KIND_GEMV && (!pow2(value) || value > kMaxSplit)) ||
+        (kind == WQ_KIND_GEMM && (value < 1 || value > WQ_GEMM_TILES))) {
+      bad = true;
+      break;
+    }
+    entries.push_back({Key{tag, fmt, K, N, M, kind}, value});
+  }
+  std::fclose(f);
+  if (bad) return fail(WQ_ERR_CACHE_IO, std::string("malformed tuner cache ") + path);
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  for (auto& e : entries) g_cache[e.first] = e.second;
+  return WQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// Quantize-and-pack kernels (canonical layout) and the canonical <-> gfx950 repack.
+//
+// The formats are those of the tileInfer README (feature table, "INT8 Weight-Only
+// Quantization": int8 codes with one scale per output channel) and of "Marlin
+// register and launch scheduling benchmark" ("Validation and limits": INT8/INT4
+// with per-channel or group-128 scales).  The pages print no quantization
+// arithmetic; the recipe implemented here is the one stated at wq_pack in wq.h:
+// IEEE fp32, round to nearest even, correctly rounded division by the stored
+// (rounded) scale.
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float v) {
+  _Float16 h = (_Float16)v;  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Max over the `width` lanes of a sub-wave (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float group_min(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t w8_codes4(float4 w, float s) {
+  // q = clamp(rint(w / s), -127, 127); s != 0 here.
+  float c[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float q = fminf(fmaxf(rintf(c[j] / s), -127.f), 127.f);
+    out |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * j);
+  }
+  return out;
+}
+
+// W8, one scale per output channel: one 256-thread block per row.
+__global__ __launch_bounds__(256) void pack_w8_pc_kernel(const float* __restrict__ w,
+                                                           int8_t* __restrict__ q,
+                                                           uint16_t* __restrict__ scales, int K) {
+  const int n = blockIdx.x;
+  const float4* row = reinterpret_cast<const float4*>(w + (size_t)n * K);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(q + (size_t)n * K);
+  const int words = K / 4;
+  float a = 0.f;
+  for (int i = threadIdx.x; i < words; i += 256) {
+    float4 v = row[i];
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  a = group_max<64>(a);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const uint16_t sb = f32_to_bf16_rne(a / 127.f);
+  const float s = bf16_to_f32(sb);
+  if (threadIdx.x == 0) scales[n] = sb;
+  for (int i = threadIdx.x; i < words; i += 256) qrow[i] = (s == 0.f) ? 0u : w8_codes4(row[i], s);
+}
+
+// W8, group 128: 256 threads = 8 groups of 32 lanes, each lane 4 consecutive k.
+__global__ __launch_bounds__(256) void pack_w8_g128_kernel(const float* __restrict__ w,
+                                                             int8_t* __restrict__ q,
+                                                             uint16_t* __restrict__ scales,
+                                                             int K, int N) {
+  const int G = K / kGroup;
+  const int64_t gid = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int lane = threadIdx.x & 31;
+  const bool valid = gid < (int64_t)N * G;
+  const int64_t gg = valid ? gid : 0;
+  const int64_t n = gg / G, g = gg % G;
+  const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
+  float4 v = *reinterpret_cast<const float4*>(w + off);
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = group_max<32>(a);
+  const uint16_t sb = f32_to_bf16_rne(a / 127.f);
+  const float s = bf16_to_f32(sb);
+  if (!valid) return;
+  if (lane == 0) scales[n * G + g] = sb;
+  *reinterpret_cast<uint32_t*>(q + off) = (s == 0.f) ? 0u : w8_codes4(v, s);
+}
+
+// W4 asymmetric group 128, canonical layout: a block handles 8 rows x 1 group,
+// 32 lanes per row, 4 consecutive k per lane; the 8 zero-points form one word.
+__global__ __launch_bounds__(256) void pack_w4_g128_kernel(const float* __restrict__ w,
+                                                             uint32_t* __restrict__ qw,
+                                                             uint16_t* __restrict__ scales,
+                                                             uint32_t* __restrict__ zeros, int K,
+                                                             int N) {
+  const int G = K / kGroup;
+  const int c8 = blockIdx.x;  // rows 8*c8 .. 8*c8+7
+  const int g = blockIdx.y;
+  const int r = threadIdx.x >> 5, lane = threadIdx.x & 31;
+  const int n = 8 * c8 + r;
+  const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
+  float4 v = *reinterpret_cast<const float4*>(w + off);
+  float hi = group_max<32>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  float lo = group_min<32>(fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+  const uint16_t sh = f32_to_f16_rne((hi - lo) / 15.f);
+  const float s = f16_to_f32(sh);
+  uint32_t z = 0, nib = 0;
+  if (s != 0.f) {
+    z = (uint32_t)fminf(fmaxf(rintf(-lo / s), 0.f), 15.f);
+    float c[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float qq = fminf(fmaxf(rintf(c[j] / s) + (float)z, 0.f), 15.f);
+      nib |= ((uint32_t)qq) << (4 * j);
+    }
+  }
+  // lanes 2i and 2i+1 hold k = 8i..8i+3 and 8i+4..8i+7 of the same word
+  const uint32_t partner = (uint32_t)__shfl_xor((int)nib, 1, 32);
+  if ((lane & 1) == 0) qw[(size_t)n * (K / 8) + (size_t)g * 16 + (lane >> 1)] = nib | (partner << 16);
+  __shared__ uint32_t zs[8];
+  if (lane == 0) {
+    scales[(size_t)n * G + g] = sh;
+    zs[r] = z;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= zs[j] << (4 * j);
+    zeros[(size_t)g * (N / 8) + c8] = word;
+  }
+}
+
+// Nibble position p of a gfx950 W4 word holds canonical nibble kPerm[p].
+__device__ __forceinline__ uint32_t nibbles_to_gfx950(uint32_t c) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int src = (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+    o |= ((c >> (4 * src)) & 0xFu) << (4 * p);
+  }
+  return o;
+}
+__device__ __forceinline__ uint32_t nibbles_from_gfx950(uint32_t o) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int dst = (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+    c |= ((o >> (4 * p)) & 0xFu) << (4 * dst);
+  }
+  return c;
+}
+
+__global__ void w4_words_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                size_t n_words, int to_gfx950) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+       i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t v = src[i];
+    dst[i] = to_gfx950 ? nibbles_to_gfx950(v) : nibbles_from_gfx950(v);
+  }
+}
+
+// canonical zeros uint32 [G][N/8]  ->  gfx950 zeros uint8 [N][ceil(G/2)]
+__global__ void w4_zeros_to_gfx950_kernel(const uint32_t* __restrict__ zc, uint8_t* __restrict__ zg,
+                                          int G, int N) {
+  const int Gh = (G + 1) / 2;
+  const size_t total = (size_t)N * Gh;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / Gh), h = (int)(i % Gh);
+    const int sh = 4 * (n % 8);
+    uint32_t lo = (zc[(size_t)(2 * h) * (N / 8) + n / 8] >> sh) & 0xFu;
+    uint32_t hi = (2 * h + 1 < G) ? (zc[(size_t)(2 * h + 1) * (N / 8) + n / 8] >> sh) & 0xFu : 0u;
+    zg[i] = (uint8_t)(lo | (hi << 4));
+  }
+}
+
+// gfx950 zeros uint8 [N][ceil(G/2)]  ->  canonical zeros uint32 [G][N/8]
+__global__ void w4_zeros_from_gfx950_kernel(const uint8_t* __restrict__ zg, uint32_t* __restrict__ zc,
+                                            int G, int N) {
+  const int Gh = (G + 1) / 2;
+  const size_t total = (size_t)G * (N / 8);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int g = (int)(i / (N / 8)), c = (int)(i % (N / 8));
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint8_t b = zg[(size_t)(8 * c + j) * Gh + g / 2];
+      word |= (uint32_t)((b >> (4 * (g & 1))) & 0xF) << (4 * j);
+    }
+    zc[i] = word;
+  }
+}
+
+unsigned grid_for(size_t n, unsigned block) {
+  size_t b = (n + block - 1) / block;
+  if (b > 65535u * 16u) b = 65535u * 16u;
+  return (unsigned)(b ? b : 1);
+}
+
+}  // namespace
+
+wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s) {
+  const int K = (int)out->K, N = (int)out->N;
+  switch (out->fmt) {
+    case WQ_FMT_W8_PC:
+      pack_w8_pc_kernel<<<N, 256, 0, s>>>(w, (int8_t*)out->qweight, (uint16_t*)out->scales, K);
+      break;
+    case WQ_FMT_W8_G128: {
+      const int64_t groups = (int64_t)N * (K / kGroup);
+      pack_w8_g128_kernel<<<(unsigned)((groups + 7) / 8), 256, 0, s>>>(
+          w, (int8_t*)out->qweight, (uint16_t*)out->scales, K, N);
+      break;
+    }
+    case WQ_FMT_W4_G128:
+      pack_w4_g128_kernel<<<dim3(N / 8, K / kGroup), 256, 0, s>>>(
+          w, (uint32_t*)out->qweight, (uint16_t*)out->scales, (uint32_t*)out->zeros, K, N);
+      break;
+    default:
+      return fail(WQ_ERR_UNSUPPORTED, "wq_pack: unknown format");
+  }
+  WQ_HIP_CHECK(hipGetLastError());
+  return WQ_OK;
+}
+
+wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s) {
+  size_t qb = 0, sb = 0, zb = 0;
+  wq_status st = wq_packed_sizes(src->fmt, src->layout, src->K, src->N, &qb, &sb, &zb);
+  if (st != WQ_OK) return st;
+  WQ_HIP_CHECK(hipMemcpyAsync(dst->scales, src->scales, sb, hipMemcpyDeviceToDevice, s));
+  if (src->fmt != WQ_FMT_W4_G128) {
+    // W8: the gfx950 layout keeps the canonical bytes.
+    WQ_HIP_CHECK(hipMemcpyAsync(dst->qweight, src->qweight, qb, hipMemcpyDeviceToDevice, s));
+    return WQ_OK;
+  }
+  const size_t words = qb / 4;
+  w4_words_kernel<<<grid_for(words, 256), 256, 0, s>>>((const uint32_t*)src->qweight,
+                                                       (uint32_t*)dst->qweight, words, to_gfx950);
+  WQ_HIP_CHECK(hipGetLastError());
+  const int G = (int)(src->K / kGroup), N = (int)src->N;
+  if (to_gfx950) {
+    w4_zeros_to_gfx950_kernel<<<grid_for((size_t)N * ((G + 1) / 2), 256), 256, 0, s>>>(
+        (const uint32_t*)src->zeros, (uint8_t*)dst->zeros, G, N);
+  } else {
+    w4_zeros_from_gfx950_kernel<<<grid_for((size_t)G * (N / 8), 256), 256, 0, s>>>(
+        (const uint8_t*)src->zeros, (uint32_t*)dst->zeros, G, N);
+  }
+  WQ_HIP_CHECK(hipGetLastError());
+  return WQ_OK;
+}
+
+}  // namespace wq

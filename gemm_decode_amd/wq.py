@@ -1,0 +1,257 @@
+"""Python binding of libwq.so (the C ABI in include/wq.h), loaded with ctypes.
+
+Argument marshalling only: every computation runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors) and streams; the functions below have
+the names of the C entry points declared in include/wq.h and take tensors where
+the C functions take device pointers.
+
+Importing this package fails loudly (ImportError) when libwq.so has not been
+built; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "FMT", "CANONICAL", "GFX950", "WqError", "PackedWeight", "lib",
+    "wq_abi_version", "wq_status_string", "wq_last_error", "wq_packed_sizes", "wq_dispatch_kind",
+    "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear",
+    "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
+    "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwq.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m gemm_decode_amd.build` "
+                      "(or __graft_entry__.build()) first")
+lib = C.CDLL(LIB_PATH)
+
+FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2}
+FMT_NAME = {v: k for k, v in FMT.items()}
+CANONICAL, GFX950 = 0, 1
+KIND_GEMV, KIND_GEMM = 0, 1
+GEMM_TILES = 2
+SPLIT_GRID = (1, 2, 4, 8, 16, 32)
+
+
+class WqWeightC(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("layout", C.c_int32), ("K", C.c_int64), ("N", C.c_int64),
+                ("qweight", C.c_void_p), ("scales", C.c_void_p), ("zeros", C.c_void_p)]
+
+
+_P = C.POINTER
+_W = _P(WqWeightC)
+_SIGS = {
+    "wq_abi_version": (C.c_int, []),
+    "wq_status_string": (C.c_char_p, [C.c_int]),
+    "wq_last_error": (C.c_char_p, []),
+    "wq_packed_sizes": (C.c_int, [C.c_int, C.c_int, C.c_int64, C.c_int64, _P(C.c_size_t), _P(C.c_size_t), _P(C.c_size_t)]),
+    "wq_dispatch_kind": (C.c_int, [C.c_int64]),
+    "wq_pack": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
+    "wq_repack": (C.c_int, [_W, _W, C.c_void_p]),
+    "wq_unrepack": (C.c_int, [_W, _W, C.c_void_p]),
+    "wq_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
+    "wq_gemv": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_tune_pick": (C.c_int, [_P(C.c_double), C.c_int]),
+    "wq_tune": (C.c_int, [_W, C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                          C.c_int, C.c_int, C.c_void_p, _P(C.c_int), _P(C.c_double)]),
+    "wq_tune_cache_set": (C.c_int, [C.c_char_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int]),
+    "wq_tune_cache_get": (C.c_int, [C.c_char_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, _P(C.c_int)]),
+    "wq_tune_cache_clear": (C.c_int, []),
+    "wq_tune_cache_save": (C.c_int, [C.c_char_p]),
+    "wq_tune_cache_load": (C.c_int, [C.c_char_p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+class WqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {wq_status_string(status)} ({wq_last_error()})")
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise WqError(st, where)
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t) -> C.c_void_p:
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+# ------------------------------------------------------------------ host info
+def wq_abi_version() -> int:
+    return lib.wq_abi_version()
+
+
+def wq_status_string(st: int) -> str:
+    return lib.wq_status_string(st).decode()
+
+
+def wq_last_error() -> str:
+    return lib.wq_last_error().decode()
+
+
+def wq_packed_sizes(fmt, layout: int, K: int, N: int):
+    q, s, z = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check(lib.wq_packed_sizes(_fmt(fmt), layout, K, N, C.byref(q), C.byref(s), C.byref(z)),
+           "wq_packed_sizes")
+    return q.value, s.value, z.value
+
+
+def wq_dispatch_kind(M: int) -> int:
+    return lib.wq_dispatch_kind(M)
+
+
+def _fmt(fmt) -> int:
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+# ------------------------------------------------------------- packed weights
+class PackedWeight:
+    """Device buffers of one packed weight (owned by torch tensors) plus its
+    descriptor.  ``qweight``/``scales``/``zeros`` are flat uint8 tensors."""
+
+    def __init__(self, fmt, layout: int, K: int, N: int, device="cuda"):
+        self.fmt, self.layout, self.K, self.N = _fmt(fmt), layout, K, N
+        qb, sb, zb = wq_packed_sizes(self.fmt, layout, K, N)
+        self.qweight = torch.empty(qb, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb, dtype=torch.uint8, device=device)
+        self.zeros = torch.empty(zb, dtype=torch.uint8, device=device) if zb else None
+
+    @property
+    def fmt_name(self) -> str:
+        return FMT_NAME[self.fmt]
+
+    def desc(self) -> WqWeightC:
+        return WqWeightC(self.fmt, self.layout, self.K, self.N, self.qweight.data_ptr(),
+                         self.scales.data_ptr(), 0 if self.zeros is None else self.zeros.data_ptr())
+
+    def nbytes(self) -> int:
+        return self.qweight.numel() + self.scales.numel() + (0 if self.zeros is None else self.zeros.numel())
+
+    def clone(self) -> "PackedWeight":
+        c = PackedWeight.__new__(PackedWeight)
+        c.fmt, c.layout, c.K, c.N = self.fmt, self.layout, self.K, self.N
+        c.qweight, c.scales = self.qweight.clone(), self.scales.clone()
+        c.zeros = None if self.zeros is None else self.zeros.clone()
+        return c
+
+
+def wq_pack(w: torch.Tensor, out: PackedWeight, stream=None) -> None:
+    assert w.dtype == torch.float32 and w.is_contiguous() and tuple(w.shape) == (out.N, out.K)
+    d = out.desc()
+    _check(lib.wq_pack(_ptr(w), C.byref(d), _stream(stream)), "wq_pack")
+
+
+def wq_repack(src: PackedWeight, dst: PackedWeight, stream=None) -> None:
+    a, b = src.desc(), dst.desc()
+    _check(lib.wq_repack(C.byref(a), C.byref(b), _stream(stream)), "wq_repack")
+
+
+def wq_unrepack(src: PackedWeight, dst: PackedWeight, stream=None) -> None:
+    a, b = src.desc(), dst.desc()
+    _check(lib.wq_unrepack(C.byref(a), C.byref(b), _stream(stream)), "wq_unrepack")
+
+
+def quantize(w: torch.Tensor, fmt, stream=None, keep_canonical: bool = False):
+    """wq_pack into the canonical layout, then wq_repack into the gfx950 layout."""
+    N, K = w.shape
+    can = PackedWeight(fmt, CANONICAL, K, N, device=w.device)
+    wq_pack(w, can, stream)
+    g = PackedWeight(fmt, GFX950, K, N, device=w.device)
+    wq_repack(can, g, stream)
+    return (g, can) if keep_canonical else g
+
+
+# ---------------------------------------------------------------- the linear
+def wq_workspace_size(w: PackedWeight, M: int) -> int:
+    d, n = w.desc(), C.c_size_t()
+    _check(lib.wq_workspace_size(C.byref(d), M, C.byref(n)), "wq_workspace_size")
+    return n.value
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (the split-K counters must start at zero)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _xy(x: torch.Tensor, y: torch.Tensor, w: PackedWeight):
+    assert x.dtype == torch.bfloat16 and y.dtype == torch.bfloat16
+    assert x.is_contiguous() and y.is_contiguous()
+    M = x.numel() // w.K
+    assert x.numel() == M * w.K and y.numel() == M * w.N, "x/y sizes do not match the weight"
+    return M
+
+
+def wq_gemv(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int = 0,
+            ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w), w.desc()
+    _check(lib.wq_gemv(C.byref(d), _ptr(x), M, _ptr(y), split_k, _ptr(ws),
+                       0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv")
+
+
+def wq_gemm(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0, stream=None) -> None:
+    M, d = _xy(x, y, w), w.desc()
+    _check(lib.wq_gemm(C.byref(d), _ptr(x), M, _ptr(y), tile, None, 0, _stream(stream)), "wq_gemm")
+
+
+def wq_linear(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = None,
+              stream=None) -> None:
+    M, d = _xy(x, y, w), w.desc()
+    _check(lib.wq_linear(C.byref(d), _ptr(x), M, _ptr(y), _ptr(ws),
+                         0 if ws is None else ws.numel(), _stream(stream)), "wq_linear")
+
+
+# ---------------------------------------------------------------------- tuner
+def wq_tune_pick(lat) -> int:
+    arr = (C.c_double * len(lat))(*lat)
+    return lib.wq_tune_pick(arr, len(lat))
+
+
+def wq_tune(copies, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = None,
+            warmup: int = 1000, iters: int = 1000, stream=None):
+    """Returns (chosen split_k or tile, per-candidate mean microseconds)."""
+    M = _xy(x, y, copies[0])
+    arr = (WqWeightC * len(copies))(*[c.desc() for c in copies])
+    chosen = C.c_int()
+    lat = (C.c_double * 6)(*([-1.0] * 6))
+    _check(lib.wq_tune(arr, len(copies), M, _ptr(x), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                       warmup, iters, _stream(stream), C.byref(chosen), lat), "wq_tune")
+    n = len(SPLIT_GRID) if wq_dispatch_kind(M) == KIND_GEMV else GEMM_TILES
+    return chosen.value, list(lat)[:n]
+
+
+def wq_tune_cache_set(fmt, K: int, N: int, M: int, kind: int, value: int, device_tag: str = "") -> None:
+    _check(lib.wq_tune_cache_set(device_tag.encode(), _fmt(fmt), K, N, M, kind, value), "wq_tune_cache_set")
+
+
+def wq_tune_cache_get(fmt, K: int, N: int, M: int, kind: int, device_tag: str = ""):
+    v = C.c_int()
+    st = lib.wq_tune_cache_get(device_tag.encode(), _fmt(fmt), K, N, M, kind, C.byref(v))
+    return v.value if st == 0 else None
+
+
+def wq_tune_cache_clear() -> None:
+    _check(lib.wq_tune_cache_clear(), "wq_tune_cache_clear")
+
+
+def wq_tune_cache_save(path: str) -> None:
+    _check(lib.wq_tune_cache_save(os.fsencode(path)), "wq_tune_cache_save")
+
+
+def wq_tune_cache_load(path: str) -> None:
+    _check(lib.wq_tune_cache_load(os.fsencode(path)), "wq_tune_cache_load")

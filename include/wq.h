@@ -1,0 +1,215 @@
+/*
+ * wq.h -- C ABI of the weight-only quantized linear library for MI355X (gfx950).
+ *
+ * The layer computes y = x . dequant(Wq, s[, z])^T with bf16 activations x[M][K],
+ * quantized weights W[N][K] (N output channels, K input features), fp32
+ * accumulation and bf16 output y[M][N].  This is the int8 weight-only linear of
+ * the tileInfer README (feature table, "INT8 Weight-Only Quantization": int8
+ * weights with one scale per output channel, bf16 activations; "Key
+ * Optimizations": decode dequantizes in registers inside a GEMV, prefill
+ * dequantizes to bf16 on the fly for a GEMM), extended to the group-128 INT8 and
+ * INT4 formats of "Marlin register and launch scheduling benchmark" ("Validation
+ * and limits"; "Full inference" for the group-128 vocabulary heads).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named in a wq_weight, x, y and ws are DEVICE pointers (memory from
+ *     hipMalloc or a PyTorch HIP tensor); size_t/int64_t out-parameters and the
+ *     path strings are HOST pointers.
+ *   - The caller owns every buffer.  The library never allocates device memory,
+ *     never frees anything it was given and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
+ *     enqueued asynchronously on it; wq_gemv, wq_gemm and wq_linear neither
+ *     synchronize nor read device memory on the host, so they may be captured
+ *     into a HIP graph.  Only wq_tune synchronizes.
+ *   - Every precondition is checked on the host before anything is enqueued; on
+ *     an error status nothing has been written.  A failed HIP call returns
+ *     WQ_ERR_HIP.  wq_last_error() gives the detail text (per calling thread).
+ *   - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_ABI_VERSION 1
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size or value                       */
+  WQ_ERR_UNSUPPORTED = 2,  /* format/layout/shape combination not provided          */
+  WQ_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned               */
+  WQ_ERR_WORKSPACE = 4,    /* workspace missing or smaller than wq_workspace_size   */
+  WQ_ERR_NO_DEVICE = 5,    /* no HIP device is visible                              */
+  WQ_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed            */
+  WQ_ERR_CACHE_IO = 7      /* tuner cache file could not be read or written         */
+} wq_status;
+
+/* Weight formats (the quantization recipe is stated at wq_pack). */
+typedef enum {
+  WQ_FMT_W8_PC = 0,    /* int8, symmetric, one bf16 scale per output channel       */
+  WQ_FMT_W8_G128 = 1,  /* int8, symmetric, one bf16 scale per 128 consecutive k     */
+  WQ_FMT_W4_G128 = 2   /* uint4, asymmetric, fp16 scale + uint4 zero per 128 k      */
+} wq_format;
+
+/* Memory layouts of a packed weight.
+ *
+ * WQ_LAYOUT_CANONICAL (interchange; what wq_pack writes):
+ *   W8:  qweight int8 [N][K] row-major; scales bf16 [N] (per channel) or [N][K/128].
+ *   W4:  qweight uint32 [N][K/8], bits 4j..4j+3 of word (n,c) hold q[n][8c+j];
+ *        scales fp16 [N][K/128];
+ *        zeros uint32 [K/128][N/8], bits 4j..4j+3 of word (g,c) hold z[8c+j][g].
+ *
+ * WQ_LAYOUT_GFX950 (what the compute kernels read; written by wq_repack):
+ *   W8:  identical bytes to the canonical layout: each lane's 16-byte load of a row
+ *        is contiguous along k and a sign-extending byte convert feeds the math.
+ *   W4:  qweight uint32 [N][K/8] whose word (n,c) holds the same 8 codes with the
+ *        nibbles interleaved: bits 4p..4p+3 hold q[n][8c + (2p mod 8) + (p >= 4)],
+ *        i.e. nibble order q0 q2 q4 q6 q1 q3 q5 q7, so that (word >> 4i) & 0x000F000F
+ *        yields the consecutive pair (q[8c+2i], q[8c+2i+1]) in the two 16-bit halves;
+ *        scales fp16 [N][K/128] (unchanged);
+ *        zeros uint8 [N][ceil(K/256)], byte (n,h) holds z[n][2h] in bits 0..3 and
+ *        z[n][2h+1] in bits 4..7 (row-major, so a row's zero-points sit beside it).
+ */
+typedef enum { WQ_LAYOUT_CANONICAL = 0, WQ_LAYOUT_GFX950 = 1 } wq_layout;
+
+/* Non-owning view of one packed weight.  zeros is NULL for the W8 formats. */
+typedef struct {
+  int32_t fmt;     /* wq_format */
+  int32_t layout;  /* wq_layout */
+  int64_t K;       /* input features (reduction length)  */
+  int64_t N;       /* output channels                     */
+  void* qweight;
+  void* scales;
+  void* zeros;
+} wq_weight;
+
+/* Which kernel family wq_linear uses for M tokens. */
+typedef enum { WQ_KIND_GEMV = 0, WQ_KIND_GEMM = 1 } wq_kind;
+
+/* ---------------------------------------------------------------- host info */
+
+/* WQ_ABI_VERSION of the built library. */
+int wq_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* wq_status_string(int status);
+
+/* Detail text of the last failing call on this thread ("" if none). */
+const char* wq_last_error(void);
+
+/* Bytes of qweight, scales and zeros for a format/layout/shape (host only, no
+ * device access).  Shape rules: K > 0, N > 0, K % 16 == 0; group-128 formats need
+ * K % 128 == 0; W4 needs N % 8 == 0.  zero_bytes is 0 for W8.  Any out-pointer
+ * may be NULL. */
+wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qweight_bytes,
+                          size_t* scale_bytes, size_t* zero_bytes);
+
+/* Kernel family for M tokens: M < 8 -> WQ_KIND_GEMV, M >= 8 -> WQ_KIND_GEMM.  The
+ * threshold and the token count M = numel(x) / K follow "Heuristic: Mit han lab Llm
+ * awq Kernel Selection Thresholds" ("The Insight (Rule of Thumb)", Linear Kernel,
+ * and its awq/quantize/qmodule.py excerpt).  Returns -1 for M < 1. */
+int wq_dispatch_kind(int64_t M);
+
+/* --------------------------------------------------------------- packing */
+
+/* Quantize an fp32 weight w[N][K] (device, row-major) into `out`, which must
+ * describe CANONICAL-layout buffers of wq_packed_sizes bytes.  Recipe (IEEE fp32,
+ * round to nearest even, correctly rounded division):
+ *   W8 (group G = K for per-channel, 128 otherwise):
+ *     a = max|w| over the group; s = bf16(a / 127);
+ *     q = 0 if s == 0 else clamp(rint(w / s), -127, 127)   (divides by the stored s)
+ *   W4 (group 128): hi = max w, lo = min w; s = fp16((hi - lo) / 15);
+ *     s == 0 -> z = 0, q = 0; else z = clamp(rint(-lo / s), 0, 15),
+ *     q = clamp(rint(w / s) + z, 0, 15).
+ * The output is bit-exact and deterministic.  `w` must not alias the outputs. */
+wq_status wq_pack(const float* w, const wq_weight* out, void* stream);
+
+/* CANONICAL -> GFX950 (wq_repack) and back (wq_unrepack); src and dst describe
+ * distinct buffers of the same format and shape in the named layouts.  The two are
+ * exact inverses on every valid packed weight. */
+wq_status wq_repack(const wq_weight* src, const wq_weight* dst, void* stream);
+wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
+
+/* ------------------------------------------------------------- the linear */
+
+/* Workspace bytes needed by wq_gemv / wq_gemm / wq_linear for this weight and M
+ * under any split_k the library may pick (host only).  The workspace holds fp32
+ * split-K partial sums and per-row-tile arrival counters.  It must be zero-filled
+ * before its first use; every call leaves the counters at zero again, so one
+ * zero-fill suffices for any number of later calls.  Calls that share a
+ * workspace must not run concurrently. */
+wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
+
+/* Decode GEMV, 1 <= M <= 7 (the "Key Optimizations" register-dequant GEMV of the
+ * tileInfer README; the Marlin page's intro for the FP32 reduction scratch that
+ * split-K partials need).  w must be in the GFX950 layout.  x: bf16 [M][K], y:
+ * bf16 [M][N], both row-major and 16-byte aligned.  split_k: 0 = the tuned value
+ * for this shape (8 when untuned, clamped to what the shape allows), else a power
+ * of two in 1..32 that does not exceed K/16 (per-channel W8) or K/128 (group-128)
+ * slices.  Each slice is a contiguous run of whole 16-element chunks (whole
+ * 128-groups for group-128 formats); the slices' fp32 partials are summed in a
+ * fixed order by the last workgroup to finish a row tile, so results are
+ * bit-identical from run to run for a given split_k. */
+wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* Prefill GEMM, M >= 1 (used by wq_linear for M >= 8; smaller M are accepted so
+ * the two paths can be compared): codes are converted to exact bf16 values in LDS
+ * and multiplied by bf16 x tiles on the matrix cores with fp32 accumulation; the
+ * per-channel scale is applied in the epilogue, group-128 scales to each group's
+ * fp32 partial.  tile: 0 = the tuned tile (default when untuned), else a tile id
+ * from 1..WQ_GEMM_TILES.  ws/ws_bytes may be NULL/0 (the GEMM needs none). */
+#define WQ_GEMM_TILES 2
+wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* The layer: M = tokens; M < 8 -> wq_gemv with the tuned split_k, else wq_gemm with
+ * the tuned tile (see wq_dispatch_kind). */
+wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ tuner */
+
+/* Choose among measured candidates: the smallest latency wins and a tie goes to
+ * the later candidate, as in the split_k loop of "Heuristic: Mit han lab Llm awq
+ * Kernel Selection Thresholds" (tinychat/utils/tune.py excerpt, "best >= cur").
+ * Host only; returns the index into lat[0..n-1], or -1 if n < 1. */
+int wq_tune_pick(const double* lat, int n);
+
+/* Time every candidate for (format, K, N, M) on the current device and store the
+ * winner in the tuner cache: for M < 8 the split_k grid {1,2,4,8,16,32} (those the
+ * shape allows), else the GEMM tiles.  Each candidate runs `warmup` untimed and
+ * `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
+ * weights (distinct buffers with the same format and shape) so that the weights
+ * do not stay cached.  x, y and ws are as for wq_linear (ws sized for M).  Writes
+ * the chosen split_k or tile to *chosen (host) and, if lat_us is not NULL, the
+ * mean microseconds per call of each candidate into lat_us[0..5] (host; -1 for
+ * candidates the shape does not allow).  Synchronizes the stream. */
+wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
+                  void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
+                  double* lat_us);
+
+/* Tuner cache: entries keyed by (device tag, format, K, N, M, kind), where the
+ * device tag is "<gcnArchName>:<compute units>" of the device the entry was tuned
+ * on ("" in set/get = the current device).  get returns WQ_OK and the value, or
+ * WQ_ERR_INVALID_ARG when absent.  save/load use a plain text file, one entry per
+ * line; load merges into the cache and fails with WQ_ERR_CACHE_IO (leaving the
+ * cache unchanged) on a missing or malformed file. */
+wq_status wq_tune_cache_set(const char* device_tag, int fmt, int64_t K, int64_t N, int64_t M,
+                            int kind, int value);
+wq_status wq_tune_cache_get(const char* device_tag, int fmt, int64_t K, int64_t N, int64_t M,
+                            int kind, int* value);
+wq_status wq_tune_cache_clear(void);
+wq_status wq_tune_cache_save(const char* path);
+wq_status wq_tune_cache_load(const char* path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

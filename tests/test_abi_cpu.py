@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol include/wq.h declares, and its
+host-only logic (sizes, dispatch rule, tuner choice, tuner cache, argument
+validation) behaves as documented.  No device work: CPU only."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle.quant as OQ
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "wq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(wqlib):
+    names = _declared()
+    assert len(names) >= 19, names
+    for n in names:
+        assert hasattr(wqlib.lib, n), n
+
+
+def test_abi_version_and_status_strings(wqlib):
+    assert wqlib.wq_abi_version() == 1
+    for st in range(8):
+        assert wqlib.wq_status_string(st)
+    assert wqlib.wq_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("K,N", [(1024, 1024), (5120, 27648), (13824, 5120), (5120, 151936), (384, 40)])
+def test_packed_sizes_match_the_oracle_layout(wqlib, fmt, K, N):
+    if fmt == "w4g128" and N % 8:
+        pytest.skip("W4 needs N % 8 == 0")
+    assert wqlib.wq_packed_sizes(fmt, wqlib.CANONICAL, K, N) == OQ.packed_sizes(fmt, K, N)
+    q, s, z = wqlib.wq_packed_sizes(fmt, wqlib.GFX950, K, N)
+    assert (q, s) == OQ.packed_sizes(fmt, K, N)[:2]
+    assert z == (N * ((K // 128 + 1) // 2) if fmt == "w4g128" else 0)
+
+
+@pytest.mark.parametrize("fmt,K,N,status", [
+    ("w8pc", 1000, 64, 2),      # K % 16
+    ("w8g128", 1040, 64, 2),    # K % 128
+    ("w4g128", 1024, 60, 2),    # N % 8
+    ("w8pc", 0, 64, 1),
+    (7, 1024, 64, 2),           # unknown format
+])
+def test_packed_sizes_rejects_bad_shapes(wqlib, fmt, K, N, status):
+    with pytest.raises(wqlib.WqError) as e:
+        wqlib.wq_packed_sizes(fmt, wqlib.CANONICAL, K, N)
+    assert e.value.status == status
+    assert wqlib.wq_last_error()
+
+
+def test_dispatch_threshold(wqlib):
+    assert [wqlib.wq_dispatch_kind(m) for m in (0, 1, 7, 8, 2048)] == [-1, 0, 0, 1, 1]
+
+
+def test_tuner_pick_min_with_ties_to_the_later_candidate(wqlib):
+    assert wqlib.wq_tune_pick([5.0, 3.0, 4.0]) == 1
+    assert wqlib.wq_tune_pick([5.0, 3.0, 3.0, 4.0]) == 2          # tie -> later (">=")
+    assert wqlib.wq_tune_pick([2.0, -1.0, 2.0, -1.0]) == 2        # -1 = not run
+    assert wqlib.wq_tune_pick([-1.0, -1.0]) == -1
+    assert wqlib.lib.wq_tune_pick(None, 0) == -1
+
+
+def test_tuner_cache_roundtrip_and_corrupt_file(wqlib, tmp_path):
+    tag = "gfx950:256"
+    wqlib.wq_tune_cache_clear()
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) is None
+    wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, 4, tag)
+    wqlib.wq_tune_cache_set("w4g128", 13824, 5120, 1, 0, 16, tag)
+    wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 2048, 1, 2, tag)
+    with pytest.raises(wqlib.WqError):
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, 3, tag)    # not a power of two
+    with pytest.raises(wqlib.WqError):
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 8, 1, 9, tag)    # no such tile
+    p = str(tmp_path / "tune.txt")
+    wqlib.wq_tune_cache_save(p)
+    wqlib.wq_tune_cache_clear()
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) is None
+    wqlib.wq_tune_cache_load(p)
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) == 4
+    assert wqlib.wq_tune_cache_get("w4g128", 13824, 5120, 1, 0, tag) == 16
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 2048, 1, tag) == 2
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, "gfx942:304") is None
+    bad = tmp_path / "bad.txt"
+    bad.write_text("gfx950:256 0 5120 27648 1 0 4\nthis is not an entry\n")
+    wqlib.wq_tune_cache_clear()
+    with pytest.raises(wqlib.WqError) as e:
+        wqlib.wq_tune_cache_load(str(bad))
+    assert e.value.status == 7
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) is None   # unchanged on failure
+    with pytest.raises(wqlib.WqError) as e:
+        wqlib.wq_tune_cache_load(str(tmp_path / "missing.txt"))
+    assert e.value.status == 7
+
+
+def _desc(wqlib, fmt=0, layout=1, K=1024, N=1024, q=0x1000, s=0x2000, z=0):
+    return wqlib.WqWeightC(fmt, layout, K, N, q, s, z)
+
+
+def test_validation_rejects_before_any_device_work(wqlib):
+    """Bad arguments are refused on the host (nothing is launched, so this runs
+    without a GPU)."""
+    L = wqlib.lib
+    d = _desc(wqlib)
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    assert L.wq_gemv(None, x, 1, y, 1, None, 0, None) == 1                  # NULL weight
+    assert L.wq_gemv(C.byref(d), x, 8, y, 1, None, 0, None) == 1            # M > 7
+    assert L.wq_gemv(C.byref(d), x, 0, y, 1, None, 0, None) == 1            # M < 1
+    assert L.wq_gemv(C.byref(d), None, 1, y, 1, None, 0, None) == 1         # NULL x
+    assert L.wq_gemv(C.byref(d), C.c_void_p(0x10008), 1, y, 1, None, 0, None) == 3   # x misaligned
+    assert L.wq_gemv(C.byref(d), x, 1, y, 3, None, 0, None) == 1            # split not pow2
+    assert L.wq_gemv(C.byref(d), x, 1, y, 64, None, 0, None) == 1           # split > 32
+    assert L.wq_gemv(C.byref(d), x, 1, y, 4, None, 0, None) == 4            # no workspace
+    assert L.wq_gemv(C.byref(d), x, 1, y, 4, C.c_void_p(0x30000), 16, None) == 4   # too small
+    dc = _desc(wqlib, layout=0)
+    assert L.wq_gemv(C.byref(dc), x, 1, y, 1, None, 0, None) == 2           # canonical layout
+    dq = _desc(wqlib, q=0x1004)
+    assert L.wq_gemv(C.byref(dq), x, 1, y, 1, None, 0, None) == 3           # qweight misaligned
+    d4 = _desc(wqlib, fmt=2)
+    assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
+    assert L.wq_gemm(C.byref(d), x, 16, y, 9, None, 0, None) == 1           # bad tile
+    d8 = _desc(wqlib, fmt=1, K=64)
+    assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
+    assert L.wq_pack(None, C.byref(dc), None) == 1
+    assert L.wq_repack(C.byref(d), C.byref(d), None) == 2                   # src not canonical
+    assert L.wq_repack(C.byref(dc), C.byref(_desc(wqlib, q=0x1000)), None) == 1  # in place
+    n = C.c_size_t()
+    assert L.wq_workspace_size(C.byref(d), 1, C.byref(n)) == 0 and n.value == 256 * 1024 + 32 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 0

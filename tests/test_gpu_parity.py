@@ -1,0 +1,335 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.  Packed bytes must be bit-exact; every bf16 output element must
+satisfy |y - y_ref| <= 1e-2 * max(1, |y_ref|); one-hot and identity inputs must
+reproduce the dequantised weights bit-exactly.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.linear as OL
+import oracle.quant as OQ
+import synth
+from gpu_util import (DEV, assert_parity, bf16_bits, canonical_to_host, host_weight, oracle_pack_rows,
+                      quantize_on_gpu, sample_rows, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = (1, 2, 4, 8, 16, 32)
+
+
+@pytest.fixture(scope="module")
+def wq(wqlib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return wqlib
+
+
+def _allowed_splits(fmt, K):
+    units = K // (16 if fmt == "w8pc" else 128)
+    return [s for s in SPLITS if s <= units]
+
+
+def _run_gemv(wq, g, x_bits, split):
+    M = x_bits.shape[0]
+    x = to_dev_bf16(x_bits)
+    y = torch.empty((M, g.N), dtype=torch.bfloat16, device=DEV)
+    ws = wq.workspace(wq.wq_workspace_size(g, M))
+    wq.wq_gemv(g, x, y, split_k=split, ws=ws)
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+def _run_gemm(wq, g, x_bits, tile=0):
+    M = x_bits.shape[0]
+    x = to_dev_bf16(x_bits)
+    y = torch.empty((M, g.N), dtype=torch.bfloat16, device=DEV)
+    wq.wq_gemm(g, x, y, tile=tile)
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+# ------------------------------------------------------------------ packing
+SMALL = [("w8pc", 1024, 1024), ("w8pc", 2320, 1000), ("w8g128", 1280, 1000), ("w4g128", 1280, 776),
+         ("w8g128", 384, 264), ("w4g128", 384, 264)]
+
+
+@pytest.mark.parametrize("fmt,K,N", SMALL)
+def test_pack_bitexact_small(wq, fmt, K, N):
+    W = synth.weight(91, K, N, synth.uses_outliers(fmt))
+    W[3] = 0                                      # an all-zero row
+    W[5, :128] = 0                                # an all-zero group
+    g, can = quantize_on_gpu(wq, W, fmt)
+    got, want = canonical_to_host(can, fmt), OQ.pack(fmt, W)
+    for key in ("qweight", "scales", "zeros"):
+        if key in want:
+            assert np.array_equal(got[key].view(np.uint8), want[key].view(np.uint8)), key
+    back = wq.PackedWeight(fmt, wq.CANONICAL, K, N)
+    wq.wq_unrepack(g, back)
+    torch.cuda.synchronize()
+    for a, b in ((back.qweight, can.qweight), (back.scales, can.scales), (back.zeros, can.zeros)):
+        if a is not None:
+            assert torch.equal(a, b)
+
+
+BIG = [(2, "w8pc", 5120, 27648), (2, "w8pc", 13824, 5120), (2, "w8pc", 5120, 7168),
+       (2, "w8pc", 6144, 5120), (3, "w4g128", 5120, 27648), (3, "w4g128", 13824, 5120),
+       (4, "w8pc", 27648, 5120), (4, "w8g128", 27648, 5120), (4, "w4g128", 27648, 5120),
+       (4, "w8pc", 5120, 151936), (4, "w8g128", 5120, 151936), (4, "w4g128", 5120, 151936)]
+
+
+def _big_case(wq, cfg, fmt, K, N):
+    W = host_weight(cfg, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    rows = sample_rows(N, 64, seed=cfg)
+    return W, g, can, rows
+
+
+@pytest.mark.parametrize("cfg,fmt,K,N", BIG)
+def test_full_size_pack_and_gemv(wq, cfg, fmt, K, N):
+    """Full-size weights in the configuration the bench times: canonical bytes
+    bit-exact on sampled 8-row blocks; GEMV (tuned default and every split) on
+    sampled output channels against the oracle."""
+    W, g, can, rows = _big_case(wq, cfg, fmt, K, N)
+    got = canonical_to_host(can, fmt)
+    want = oracle_pack_rows(fmt, W, rows)
+    assert np.array_equal(got["qweight"][rows].view(np.uint8), want["qweight"].view(np.uint8))
+    assert np.array_equal(got["scales"][rows].view(np.uint8), want["scales"].view(np.uint8))
+    if fmt == "w4g128":
+        assert np.array_equal(got["zeros"][:, rows[::8] // 8], want["zeros"])
+    Ms = synth.CONFIGS[cfg]["Ms"]
+    splits = [0] + (_allowed_splits(fmt, K) if cfg == 4 else [1])
+    for M in Ms:
+        x = synth.activation(cfg, K, M)
+        y_ref = OL.ref_linear(x, want)
+        for split in splits:
+            y = _run_gemv(wq, g, x, split)
+            assert_parity(y[:, rows], y_ref, f"{fmt} K={K} N={N} M={M} split={split}")
+
+
+GEMM_BIG = [(5, "w8pc", 5120, 27648), (5, "w8pc", 13824, 5120), (5, "w4g128", 5120, 27648),
+            (5, "w4g128", 13824, 5120)]
+
+
+@pytest.mark.parametrize("cfg,fmt,K,N", GEMM_BIG)
+def test_full_size_gemm(wq, cfg, fmt, K, N):
+    W, g, can, rows = _big_case(wq, cfg, fmt, K, N)
+    want = oracle_pack_rows(fmt, W, rows)
+    for M in (8, 64, 512, 2048):
+        x = synth.activation(cfg, K, M)
+        y_ref = OL.ref_linear(x, want)
+        for tile in range(1, wq.GEMM_TILES + 1):
+            y = _run_gemm(wq, g, x, tile)
+            assert_parity(y[:, rows], y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
+        yl = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        wq.wq_linear(g, to_dev_bf16(x), yl)
+        torch.cuda.synchronize()
+        assert_parity(bf16_bits(yl)[:, rows], y_ref, f"linear {fmt} M={M}")
+
+
+# ------------------------------------------------------------- small, full
+@pytest.mark.parametrize("fmt,K,N", SMALL)
+def test_gemv_small_every_m_and_split(wq, fmt, K, N):
+    W = synth.weight(92, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    P = OQ.pack(fmt, W)
+    for M in range(1, 8):
+        x = synth.activation(92, K, M)
+        y_ref = OL.ref_linear(x, P)
+        for split in [0] + _allowed_splits(fmt, K):
+            assert_parity(_run_gemv(wq, g, x, split), y_ref, f"gemv {fmt} M={M} split={split}")
+
+
+@pytest.mark.parametrize("fmt,K,N", [("w8pc", 384, 264), ("w8g128", 384, 264), ("w4g128", 384, 264),
+                                     ("w8pc", 1040, 200), ("w4g128", 1024, 520)])
+@pytest.mark.parametrize("M", [1, 7, 8, 37, 150, 300])
+def test_gemm_small(wq, fmt, K, N, M):
+    W = synth.weight(93, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    x = synth.activation(93, K, M)
+    y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
+    for tile in range(1, wq.GEMM_TILES + 1):
+        assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
+
+
+# ---------------------------------------------------------- exact special inputs
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_one_hot_is_exact(wq, fmt):
+    """x = e_k: every path returns bf16(dequant(W)[n, k]) bit-exactly (one exact
+    nonzero term in every fp32 sum), for every split and both GEMM tiles."""
+    K, N = 1024, 264
+    W = synth.weight(94, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    P = OQ.pack(fmt, W)
+    ks = [0, 127, 128, 513, 1023]
+    x = synth.one_hot_activation(K, ks)
+    want = OQ.bf16_rne_bits(OQ.dequant(P)[:, ks].T.astype(np.float32))
+    for split in _allowed_splits(fmt, K):
+        assert np.array_equal(_run_gemv(wq, g, x, split), want), f"gemv split={split}"
+    for tile in range(1, wq.GEMM_TILES + 1):
+        assert np.array_equal(_run_gemm(wq, g, x, tile), want), f"gemm tile={tile}"
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_identity_is_exact(wq, fmt):
+    K, N = 1024, 264
+    W = synth.weight(95, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    want = OQ.bf16_rne_bits(OQ.dequant(OQ.pack(fmt, W)).T.copy())
+    for tile in range(1, wq.GEMM_TILES + 1):
+        assert np.array_equal(_run_gemm(wq, g, synth.identity_activation(K), tile), want)
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_zero_and_power_of_two_scaling(wq, fmt):
+    K, N = 1024, 264
+    W = synth.weight(96, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    zero = np.zeros((3, K), dtype=np.uint16)
+    assert not np.any(_run_gemv(wq, g, zero, 4) & 0x7FFF)
+    assert not np.any(_run_gemm(wq, g, np.zeros((20, K), dtype=np.uint16)) & 0x7FFF)
+    x = synth.activation(96, K, 4)
+    x4 = OQ.bf16_rne_bits(OQ.bf16_bits_to_f32(x) * np.float32(4.0))
+    for split in (1, 4):
+        a = OQ.bf16_bits_to_f32(_run_gemv(wq, g, x, split))
+        b = OQ.bf16_bits_to_f32(_run_gemv(wq, g, x4, split))
+        assert np.array_equal(a * np.float32(4.0), b)
+
+
+def test_all_zero_rows_give_zero(wq):
+    K, N = 1024, 264
+    for fmt in OQ.FORMATS:
+        W = synth.weight(97, K, N, synth.uses_outliers(fmt))
+        W[10] = 0
+        g, can = quantize_on_gpu(wq, W, fmt)
+        x = synth.activation(97, K, 5)
+        assert not np.any(_run_gemv(wq, g, x, 2)[:, 10] & 0x7FFF)
+        assert not np.any(_run_gemm(wq, g, synth.activation(97, K, 40))[:, 10] & 0x7FFF)
+
+
+def test_repeat_runs_are_bit_identical(wq):
+    K, N = 5120, 7168
+    W = synth.weight(98, K, N)
+    g, _ = quantize_on_gpu(wq, W, "w8pc")
+    x = synth.activation(98, K, 4)
+    for split in (1, 8, 32):
+        first = _run_gemv(wq, g, x, split)
+        for _ in range(3):
+            assert np.array_equal(_run_gemv(wq, g, x, split), first)
+
+
+def test_dispatch_boundary_m7_m8(wq):
+    """wq_linear takes the GEMV at M = 7 and the GEMM at M = 8; both paths agree
+    with the oracle, and the GEMM also accepts M = 1..7."""
+    K, N = 5120, 7168
+    W = synth.weight(99, K, N)
+    g, _ = quantize_on_gpu(wq, W, "w8pc")
+    rows = sample_rows(N, 64)
+    P = oracle_pack_rows("w8pc", W, rows)
+    ws = wq.workspace(wq.wq_workspace_size(g, 7))
+    for M in (7, 8):
+        x = synth.activation(99, K, M)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        wq.wq_linear(g, to_dev_bf16(x), y, ws=ws)
+        torch.cuda.synchronize()
+        y_ref = OL.ref_linear(x, P)
+        assert_parity(bf16_bits(y)[:, rows], y_ref, f"linear M={M}")
+        if M == 7:
+            assert_parity(_run_gemm(wq, g, x)[:, rows], y_ref, "gemm M=7")
+
+
+def test_no_writes_outside_y_and_workspace(wq):
+    """Canary bytes around y and the workspace stay untouched (ragged N tile,
+    split-K)."""
+    K, N, M = 1280, 1000, 3
+    W = synth.weight(100, K, N)
+    g, _ = quantize_on_gpu(wq, W, "w8g128")
+    x = to_dev_bf16(synth.activation(100, K, M))
+    pad = 4096
+    ybuf = torch.full((M * N + 2 * pad,), 12345, dtype=torch.int16, device=DEV)
+    y = ybuf[pad:pad + M * N].view(torch.bfloat16)
+    nws = wq.wq_workspace_size(g, M)
+    wsbuf = torch.zeros(nws + 2 * pad, dtype=torch.uint8, device=DEV)
+    wsbuf[:pad] = 0xAB
+    wsbuf[pad + nws:] = 0xCD
+    ws = wsbuf[pad:pad + nws]
+    for split in (1, 4, 8):
+        wq.wq_gemv(g, x, y, split_k=split, ws=ws)
+    yg = torch.full((40 * N + 2 * pad,), 321, dtype=torch.int16, device=DEV)
+    wq.wq_gemm(g, to_dev_bf16(synth.activation(100, K, 40)), yg[pad:pad + 40 * N].view(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(ybuf[:pad] == 12345) and torch.all(ybuf[pad + M * N:] == 12345)
+    assert torch.all(wsbuf[:pad] == 0xAB) and torch.all(wsbuf[pad + nws:] == 0xCD)
+    assert torch.all(yg[:pad] == 321) and torch.all(yg[pad + 40 * N:] == 321)
+    # the arrival counters are back at zero after every call
+    assert not torch.any(ws[:256 * 1024])
+
+
+def test_hip_graph_replay(wq):
+    """wq_linear captured in a HIP graph replays correctly, repeatedly, with eager
+    work and synchronisation between replays."""
+    K, N = 5120, 7168
+    W = synth.weight(101, K, N)
+    g, _ = quantize_on_gpu(wq, W, "w8pc")
+    xs = {M: to_dev_bf16(synth.activation(101, K, M)) for M in (1, 4, 64)}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for M in xs}
+    ws = wq.workspace(wq.wq_workspace_size(g, 7))
+    eager = {}
+    for M in xs:
+        wq.wq_linear(g, xs[M], ys[M], ws=ws)
+    torch.cuda.synchronize()
+    eager = {M: ys[M].clone() for M in xs}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for M in xs:
+                wq.wq_linear(g, xs[M], ys[M], ws=ws)
+    torch.cuda.synchronize()
+    for it in range(4):
+        for M in xs:
+            ys[M].fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for M in xs:
+            assert torch.equal(ys[M], eager[M]), (it, M)
+
+
+def test_tuner_runs_and_caches(wq, tmp_path):
+    K, N = 5120, 7168
+    W = synth.weight(102, K, N)
+    g, _ = quantize_on_gpu(wq, W, "w8pc")
+    copies = [g, g.clone(), g.clone()]
+    x = to_dev_bf16(synth.activation(102, K, 1))
+    y = torch.empty((1, N), dtype=torch.bfloat16, device=DEV)
+    ws = wq.workspace(wq.wq_workspace_size(g, 1))
+    chosen, lat = wq.wq_tune(copies, x, y, ws, warmup=5, iters=10)
+    assert chosen in SPLITS and all(v > 0 for v in lat)
+    assert wq.wq_tune_cache_get("w8pc", K, N, 1, 0) == chosen
+    p = str(tmp_path / "cache.txt")
+    wq.wq_tune_cache_save(p)
+    assert f" 0 {K} {N} 1 0 {chosen}" in open(p).read()
+    xg = to_dev_bf16(synth.activation(102, K, 64))
+    yg = torch.empty((64, N), dtype=torch.bfloat16, device=DEV)
+    tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
+    assert tile in (1, 2) and all(v > 0 for v in lat)
+
+
+def test_error_paths_on_device(wq):
+    K, N = 1024, 264
+    W = synth.weight(103, K, N)
+    g, can = quantize_on_gpu(wq, W, "w8pc")
+    x = to_dev_bf16(synth.activation(103, K, 2))
+    y = torch.empty((2, N), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_gemv(can, x, y, split_k=1)              # canonical layout
+    assert e.value.status == 2
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_gemv(g, x, y, split_k=8, ws=torch.zeros(64, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 4
+    # untuned split with no workspace falls back to one slice and still computes
+    wq.wq_tune_cache_clear()
+    wq.wq_linear(g, x, y)
+    torch.cuda.synchronize()
+    assert_parity(bf16_bits(y), OL.ref_linear(synth.activation(103, K, 2), OQ.pack("w8pc", W)), "no-ws")
