@@ -15,9 +15,6 @@
 #include "wq_internal.h"
 
 namespace wq {
-
-int64_t gemv_max_rows();
-
 namespace {
 thread_local std::string g_err;
 
@@ -48,8 +45,18 @@ int clamp_split(int v, int64_t units) {
   return s;
 }
 
-constexpr int kDefaultSplit = 8;  // untuned default of the awq tuning heuristic
+// Untuned defaults.  The awq heuristic page starts from split_k = 8 on its GPUs; here
+// the workgroup's own waves already split K (no second launch, no workspace), so one
+// cross-workgroup slice is the default and split_k > 1 is left to the tuner.
+constexpr int kDefaultSplit = 1;
 constexpr int kDefaultTile = 1;
+
+// Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15 (0 = default).
+int gemv_value(int split, int waves) { return split | (waves << 8); }
+bool valid_gemv_value(int v) {
+  const int split = v & 0xFF, waves = (v >> 8) & 0xFF;
+  return (v >> 16) == 0 && pow2(split) && split <= kMaxSplit && (waves == 0 || (pow2(waves) && waves <= kGemvMaxWaves));
+}
 
 std::string resolve_tag(const char* tag) {
   if (tag && tag[0]) return std::string(tag);
@@ -71,10 +78,8 @@ wq_status check_gemv_split(const wq_weight* w, int M, int split, void* ws, size_
     return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= 32 and <= K/" +
                                         std::to_string(split_granule(w->fmt)));
   if (split > 1) {
-    if (w->N > gemv_max_rows())
-      return fail(WQ_ERR_UNSUPPORTED, "split-K GEMV supports N <= " + std::to_string(gemv_max_rows()));
     if (!ws) return fail(WQ_ERR_WORKSPACE, "split_k > 1 needs a workspace");
-    if (!aligned(ws, 256)) return fail(WQ_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    if (!aligned(ws, 16)) return fail(WQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     if (ws_bytes < gemv_workspace_bytes(w->N, M, split))
       return fail(WQ_ERR_WORKSPACE, "workspace too small: need " +
                                         std::to_string(gemv_workspace_bytes(w->N, M, split)) + " bytes");
@@ -90,10 +95,16 @@ wq_status check_xy(const void* x, const void* y, int64_t M) {
   return WQ_OK;
 }
 
-int resolve_split(const wq_weight* w, int64_t M) {
+// Tuned (split_k, waves) for this shape, or the defaults.
+void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves) {
   int v = 0;
-  if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) return v;
-  return clamp_split(kDefaultSplit, split_units(w));
+  if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) {
+    *split = v & 0xFF;
+    *waves = (v >> 8) & 0xFF;
+    return;
+  }
+  *split = clamp_split(kDefaultSplit, split_units(w));
+  *waves = 0;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {
@@ -102,17 +113,27 @@ int resolve_tile(const wq_weight* w, int64_t M) {
   return kDefaultTile;
 }
 
-wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
-                    size_t ws_bytes, void* stream) {
+wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
+                    void* ws, size_t ws_bytes, void* stream) {
   wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
-  int split = split_k == 0 ? resolve_split(w, M) : split_k;
-  if (split_k == 0 && split > 1 && (!ws || ws_bytes < gemv_workspace_bytes(w->N, M, split)))
-    split = 1;  // tuned value needs more workspace than given: fall back to one slice
+  if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves || (waves & (waves - 1)))
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default), 1, 2, 4, 8 or 16");
+  int split = split_k, wv = waves;
+  if (split_k == 0) {
+    int tuned_waves = 0;
+    resolve_gemv(w, M, &split, &tuned_waves);
+    if (wv == 0) wv = tuned_waves;
+    if (split > 1 && (!ws || ws_bytes < gemv_workspace_bytes(w->N, M, split))) {
+      split = 1;  // the tuned split needs more workspace than given: one slice
+      wv = 0;
+    }
+  }
   if ((st = check_gemv_split(w, (int)M, split, ws, ws_bytes)) != WQ_OK) return st;
-  return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, ws, (hipStream_t)stream);
+  if (wv == 0) wv = gemv_default_waves(w->K, w->N, w->fmt, (int)M, split);
+  return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, wv, ws, (hipStream_t)stream);
 }
 
 wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* stream) {
@@ -226,6 +247,11 @@ wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb,
   return WQ_OK;
 }
 
+int wq_gemv_max_waves(int fmt, int64_t M) {
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G128 || M < 1 || M > kGemvMaxM) return -1;
+  return gemv_max_waves(fmt, (int)M);
+}
+
 int wq_dispatch_kind(int64_t M) {
   if (M < 1) return -1;
   return M <= kGemvMaxM ? WQ_KIND_GEMV : WQ_KIND_GEMM;
@@ -271,7 +297,13 @@ wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
 
 wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
                   size_t ws_bytes, void* stream) {
-  return gemv_impl(w, x, M, y, split_k, ws, ws_bytes, stream);
+  return gemv_impl(w, x, M, y, split_k, 0, ws, ws_bytes, stream);
+}
+
+wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (split_k < 1) return fail(WQ_ERR_INVALID_ARG, "wq_gemv_ex: split_k must be given (>= 1)");
+  return gemv_impl(w, x, M, y, split_k, waves, ws, ws_bytes, stream);
 }
 
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
@@ -284,7 +316,7 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws, size_t ws_bytes,
                     void* stream) {
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
-  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, ws, ws_bytes, stream);
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, ws, ws_bytes, stream);
   return gemm_impl(w, x, M, y, 0, stream);
 }
 
@@ -310,11 +342,16 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   }
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   const bool gemv = wq_dispatch_kind(M) == WQ_KIND_GEMV;
-  std::vector<int> cand;
+  // GEMV candidates: every (split_k, waves) pair; GEMM candidates: the tiles
+  struct Cand {
+    int split, waves, tile;
+  };
+  std::vector<Cand> cand;
   if (gemv) {
-    for (int s = 1; s <= kMaxSplit; s *= 2) cand.push_back(s);
+    for (int s = 1; s <= kMaxSplit; s *= 2)
+      for (int wv = 1; wv <= gemv_max_waves(copies[0].fmt, (int)M); wv *= 2) cand.push_back({s, wv, 0});
   } else {
-    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back(t);
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, t});
   }
   hipStream_t hs = (hipStream_t)stream;
   hipEvent_t e0, e1;
@@ -324,15 +361,15 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   int rot = 0;
   for (size_t c = 0; c < cand.size(); ++c) {
     if (gemv) {
-      const int s = cand[c];
+      const int s = cand[c].split;
       if (s > split_units(&copies[0])) continue;
       if (s > 1 && (!ws || ws_bytes < gemv_workspace_bytes(copies[0].N, M, s))) continue;
     }
     auto run = [&]() -> wq_status {
       const wq_weight* w = &copies[rot];
       rot = (rot + 1) % n_copies;
-      return gemv ? gemv_impl(w, x, M, y, cand[c], ws, ws_bytes, stream)
-                  : gemm_impl(w, x, M, y, cand[c], stream);
+      return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, ws, ws_bytes, stream)
+                  : gemm_impl(w, x, M, y, cand[c].tile, stream);
     };
     for (int i = 0; i < warmup; ++i)
       if ((st = run()) != WQ_OK) goto out;
@@ -353,11 +390,25 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       st = fail(WQ_ERR_WORKSPACE, "wq_tune: no candidate could run");
       goto out;
     }
-    *chosen = cand[best];
-    if (lat_us)
-      for (size_t c = 0; c < cand.size(); ++c) lat_us[c] = lat[c];
-    st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M,
-                           gemv ? WQ_KIND_GEMV : WQ_KIND_GEMM, cand[best]);
+    if (gemv) {
+      *chosen = cand[best].split;
+      if (lat_us) {
+        // per split_k: the best time over the waves candidates
+        for (int i = 0, s = 1; s <= kMaxSplit; s *= 2, ++i) {
+          double b = -1.0;
+          for (size_t c = 0; c < cand.size(); ++c)
+            if (cand[c].split == s && lat[c] >= 0 && (b < 0 || lat[c] < b)) b = lat[c];
+          lat_us[i] = b;
+        }
+      }
+      st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M, WQ_KIND_GEMV,
+                             gemv_value(cand[best].split, cand[best].waves));
+    } else {
+      *chosen = cand[best].tile;
+      if (lat_us)
+        for (size_t c = 0; c < cand.size(); ++c) lat_us[c] = lat[c];
+      st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M, WQ_KIND_GEMM, cand[best].tile);
+    }
   }
 out:
   (void)hipEventDestroy(e0);
@@ -371,8 +422,8 @@ wq_status wq_tune_cache_set(const char* tag, int fmt, int64_t K, int64_t N, int6
   if (st != WQ_OK) return st;
   if (M < 1 || (kind != WQ_KIND_GEMV && kind != WQ_KIND_GEMM))
     return fail(WQ_ERR_INVALID_ARG, "bad M or kind");
-  if (kind == WQ_KIND_GEMV && (!pow2(value) || value > kMaxSplit))
-    return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= 32");
+  if (kind == WQ_KIND_GEMV && !valid_gemv_value(value))
+    return fail(WQ_ERR_INVALID_ARG, "GEMV value must be split_k | waves << 8 (powers of two, <= 32 / <= 16)");
   if (kind == WQ_KIND_GEMM && (value < 1 || value > WQ_GEMM_TILES))
     return fail(WQ_ERR_INVALID_ARG, "bad tile id");
   const std::string t = resolve_tag(tag);
@@ -425,7 +476,7 @@ wq_status wq_tune_cache_load(const char* path) {
     if (std::sscanf(line, "%255s %d %" SCNd64 " %" SCNd64 " %" SCNd64 " %d %d", tag, &fmt, &K, &N, &M,
                     &kind, &value) != 7 ||
         check_shape(fmt, K, N) != WQ_OK || M < 1 || (kind != WQ_KIND_GEMV && kind != WQ_KIND_GEMM) ||
-        (kind == WQ_KIND_GEMV && (!pow2(value) || value > kMaxSplit)) ||
+        (kind == WQ_KIND_GEMV && !valid_gemv_value(value)) ||
         (kind == WQ_KIND_GEMM && (value < 1 || value > WQ_GEMM_TILES))) {
       bad = true;
       break;

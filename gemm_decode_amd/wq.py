@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "FMT", "CANONICAL", "GFX950", "WqError", "PackedWeight", "lib",
     "wq_abi_version", "wq_status_string", "wq_last_error", "wq_packed_sizes", "wq_dispatch_kind",
-    "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear",
+    "wq_gemv_max_waves",
+    "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -35,6 +36,12 @@ CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1
 GEMM_TILES = 2
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
+WAVES_GRID = (1, 2, 4, 8, 16)
+
+
+def gemv_cache_value(split_k: int, waves: int = 0) -> int:
+    """Tuner-cache encoding of a GEMV choice (split_k | waves << 8)."""
+    return split_k | (waves << 8)
 
 
 class WqWeightC(C.Structure):
@@ -50,11 +57,13 @@ _SIGS = {
     "wq_last_error": (C.c_char_p, []),
     "wq_packed_sizes": (C.c_int, [C.c_int, C.c_int, C.c_int64, C.c_int64, _P(C.c_size_t), _P(C.c_size_t), _P(C.c_size_t)]),
     "wq_dispatch_kind": (C.c_int, [C.c_int64]),
+    "wq_gemv_max_waves": (C.c_int, [C.c_int, C.c_int64]),
     "wq_pack": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
     "wq_repack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_unrepack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
     "wq_gemv": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_gemv_ex": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_tune_pick": (C.c_int, [_P(C.c_double), C.c_int]),
@@ -114,6 +123,10 @@ def wq_packed_sizes(fmt, layout: int, K: int, N: int):
 
 def wq_dispatch_kind(M: int) -> int:
     return lib.wq_dispatch_kind(M)
+
+
+def wq_gemv_max_waves(fmt, M: int) -> int:
+    return lib.wq_gemv_max_waves(_fmt(fmt), M)
 
 
 def _fmt(fmt) -> int:
@@ -185,8 +198,8 @@ def wq_workspace_size(w: PackedWeight, M: int) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (the split-K counters must start at zero)."""
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """A workspace buffer (scratch for split-K partial sums; needs no initialisation)."""
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def _xy(x: torch.Tensor, y: torch.Tensor, w: PackedWeight):
@@ -202,6 +215,13 @@ def wq_gemv(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int = 0,
     M, d = _xy(x, y, w), w.desc()
     _check(lib.wq_gemv(C.byref(d), _ptr(x), M, _ptr(y), split_k, _ptr(ws),
                        0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv")
+
+
+def wq_gemv_ex(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int, waves: int = 0,
+               ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w), w.desc()
+    _check(lib.wq_gemv_ex(C.byref(d), _ptr(x), M, _ptr(y), split_k, waves, _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv_ex")
 
 
 def wq_gemm(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0, stream=None) -> None:
@@ -224,7 +244,7 @@ def wq_tune_pick(lat) -> int:
 
 def wq_tune(copies, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = None,
             warmup: int = 1000, iters: int = 1000, stream=None):
-    """Returns (chosen split_k or tile, per-candidate mean microseconds)."""
+    """Returns (chosen split_k or tile, mean microseconds per split_k (best waves) or tile)."""
     M = _xy(x, y, copies[0])
     arr = (WqWeightC * len(copies))(*[c.desc() for c in copies])
     chosen = C.c_int()

@@ -138,25 +138,45 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
 /* ------------------------------------------------------------- the linear */
 
 /* Workspace bytes needed by wq_gemv / wq_gemm / wq_linear for this weight and M
- * under any split_k the library may pick (host only).  The workspace holds fp32
- * split-K partial sums and per-row-tile arrival counters.  It must be zero-filled
- * before its first use; every call leaves the counters at zero again, so one
- * zero-fill suffices for any number of later calls.  Calls that share a
- * workspace must not run concurrently. */
+ * under any split_k the library may pick (host only): the fp32 partial sums of
+ * every K slice of a cross-workgroup split, 32 * M * N * 4 bytes for M < 8, and 0
+ * for M >= 8 (the GEMM needs none).  The contents are scratch: no initialisation
+ * is needed and nothing is kept between calls.  Calls that share a workspace must
+ * not run concurrently. */
 wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
 
 /* Decode GEMV, 1 <= M <= 7 (the "Key Optimizations" register-dequant GEMV of the
- * tileInfer README; the Marlin page's intro for the FP32 reduction scratch that
- * split-K partials need).  w must be in the GFX950 layout.  x: bf16 [M][K], y:
- * bf16 [M][N], both row-major and 16-byte aligned.  split_k: 0 = the tuned value
- * for this shape (8 when untuned, clamped to what the shape allows), else a power
- * of two in 1..32 that does not exceed K/16 (per-channel W8) or K/128 (group-128)
- * slices.  Each slice is a contiguous run of whole 16-element chunks (whole
- * 128-groups for group-128 formats); the slices' fp32 partials are summed in a
- * fixed order by the last workgroup to finish a row tile, so results are
- * bit-identical from run to run for a given split_k. */
+ * tileInfer README).  w must be in the GFX950 layout.  x: bf16 [M][K], y: bf16
+ * [M][N], row-major; x 16-byte aligned.
+ *
+ * K is split at two levels.  Inside a workgroup, 1..16 waves share a tile of output
+ * rows and interleave over its K range; their fp32 partial sums are added in LDS in
+ * wave order.  Across workgroups, split_k slices (the split_k of "Heuristic: Mit han
+ * lab Llm awq Kernel Selection Thresholds": K partitioned across thread blocks)
+ * each write fp32 partials to the workspace (the FP32 reduction scratch of the
+ * Marlin page's intro) and a second kernel adds them in slice order.  Each slice
+ * is a contiguous run of whole 16-element chunks (whole 128-groups for the
+ * group-128 formats).  Results are bit-identical from run to run for a given
+ * (split_k, waves).
+ *
+ * split_k: 0 = the tuned (split_k, waves) of this shape (1 slice with the default
+ * waves when untuned, or when the tuned split needs more workspace than given),
+ * else a power of two in 1..32 that does not exceed K/16 (per-channel W8) or
+ * K/128 (group-128); waves then take the default for the shape.  ws/ws_bytes may
+ * be NULL/0 when split_k resolves to 1. */
 wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
                   size_t ws_bytes, void* stream);
+
+/* Largest waves per GEMV workgroup for a format and 1 <= M <= 7 (host only): the
+ * register budget per lane shrinks as a workgroup grows, so larger M allow fewer
+ * waves.  Returns -1 for an unknown format or M outside 1..7. */
+int wq_gemv_max_waves(int fmt, int64_t M);
+
+/* wq_gemv with both levels explicit: split_k >= 1 as above and waves in {0 (the
+ * default for the shape), 1, 2, 4, 8, 16} per workgroup, at most
+ * wq_gemv_max_waves(fmt, M) (else WQ_ERR_UNSUPPORTED).  For tests and tuning. */
+wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill GEMM, M >= 1 (used by wq_linear for M >= 8; smaller M are accepted so
  * the two paths can be compared): codes are converted to exact bf16 values in LDS
@@ -182,21 +202,23 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
 int wq_tune_pick(const double* lat, int n);
 
 /* Time every candidate for (format, K, N, M) on the current device and store the
- * winner in the tuner cache: for M < 8 the split_k grid {1,2,4,8,16,32} (those the
- * shape allows), else the GEMM tiles.  Each candidate runs `warmup` untimed and
- * `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
+ * winner in the tuner cache: for M < 8 every (split_k, waves) pair with split_k in
+ * the grid {1,2,4,8,16,32} (those the shape and workspace allow) and waves in
+ * {1,2,4,8,16}; for M >= 8 the GEMM tiles.  Each candidate runs `warmup` untimed
+ * and `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
  * weights (distinct buffers with the same format and shape) so that the weights
- * do not stay cached.  x, y and ws are as for wq_linear (ws sized for M).  Writes
- * the chosen split_k or tile to *chosen (host) and, if lat_us is not NULL, the
- * mean microseconds per call of each candidate into lat_us[0..5] (host; -1 for
- * candidates the shape does not allow).  Synchronizes the stream. */
+ * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k
+ * (GEMV) or tile (GEMM) to *chosen (host) and, if lat_us is not NULL, the mean
+ * microseconds per call of each split_k (its best waves) or tile into lat_us[0..5]
+ * (host; -1 for candidates that could not run).  Synchronizes the stream. */
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);
 
 /* Tuner cache: entries keyed by (device tag, format, K, N, M, kind), where the
  * device tag is "<gcnArchName>:<compute units>" of the device the entry was tuned
- * on ("" in set/get = the current device).  get returns WQ_OK and the value, or
+ * on ("" in set/get = the current device).  A GEMV value is split_k | (waves << 8)
+ * (waves 0 = the default for the shape); a GEMM value is a tile id.  get returns WQ_OK and the value, or
  * WQ_ERR_INVALID_ARG when absent.  save/load use a plain text file, one entry per
  * line; load merges into the cache and fails with WQ_ERR_CACHE_IO (leaving the
  * cache unchanged) on a missing or malformed file. */
