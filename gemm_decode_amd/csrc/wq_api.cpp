@@ -36,7 +36,7 @@ std::map<Key, int> g_cache;
 std::mutex g_dev_mu;
 std::map<int, std::string> g_dev_tags;
 
-int64_t split_units(const wq_weight* w) { return w->K / split_granule(w->fmt); }
+int64_t split_units(const wq_weight* w) { return gemv_slices(w->K, w->fmt); }
 
 // Largest power of two <= min(v, units, 32).
 int clamp_split(int v, int64_t units) {
@@ -55,7 +55,7 @@ constexpr int kDefaultTile = 1;
 int gemv_value(int split, int waves) { return split | (waves << 8); }
 bool valid_gemv_value(int v) {
   const int split = v & 0xFF, waves = (v >> 8) & 0xFF;
-  return (v >> 16) == 0 && pow2(split) && split <= kMaxSplit && (waves == 0 || (pow2(waves) && waves <= kGemvMaxWaves));
+  return (v >> 16) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves;
 }
 
 std::string resolve_tag(const char* tag) {
@@ -75,8 +75,8 @@ bool cache_lookup(const std::string& tag, int fmt, int64_t K, int64_t N, int64_t
 wq_status check_gemv_split(const wq_weight* w, int M, int split, void* ws, size_t ws_bytes) {
   const int64_t units = split_units(w);
   if (!pow2(split) || split > kMaxSplit || split > units)
-    return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= 32 and <= K/" +
-                                        std::to_string(split_granule(w->fmt)));
+    return fail(WQ_ERR_INVALID_ARG, "split_k must be a power of two <= " +
+                                        std::to_string(clamp_split(kMaxSplit, units)) + " for this K");
   if (split > 1) {
     if (!ws) return fail(WQ_ERR_WORKSPACE, "split_k > 1 needs a workspace");
     if (!aligned(ws, 16)) return fail(WQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
@@ -119,8 +119,8 @@ wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int s
   if (st != WQ_OK) return st;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
-  if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves || (waves & (waves - 1)))
-    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default), 1, 2, 4, 8 or 16");
+  if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves)
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default) or 1..16");
   int split = split_k, wv = waves;
   if (split_k == 0) {
     int tuned_waves = 0;
@@ -194,7 +194,10 @@ wq_status check_weight(const wq_weight* w, int want_layout) {
   if (!w->qweight || !w->scales) return fail(WQ_ERR_INVALID_ARG, "qweight/scales must not be NULL");
   if (w->fmt == WQ_FMT_W4_G128 && !w->zeros) return fail(WQ_ERR_INVALID_ARG, "W4 needs zeros");
   if (!aligned(w->qweight, 16)) return fail(WQ_ERR_ALIGNMENT, "qweight must be 16-byte aligned");
-  if (!aligned(w->scales, 2)) return fail(WQ_ERR_ALIGNMENT, "scales must be 2-byte aligned");
+  if (!aligned(w->scales, want_layout == WQ_LAYOUT_GFX950 && w->fmt != WQ_FMT_W8_PC ? 16 : 2))
+    return fail(WQ_ERR_ALIGNMENT, "scales must be 2-byte aligned (16-byte for tiled gfx950 scales)");
+  if (w->fmt == WQ_FMT_W4_G128 && want_layout == WQ_LAYOUT_GFX950 && !aligned(w->zeros, 8))
+    return fail(WQ_ERR_ALIGNMENT, "gfx950 zeros must be 8-byte aligned");
   if (w->fmt == WQ_FMT_W4_G128 && want_layout == WQ_LAYOUT_CANONICAL && !aligned(w->zeros, 4))
     return fail(WQ_ERR_ALIGNMENT, "canonical zeros must be 4-byte aligned");
   return WQ_OK;
@@ -234,17 +237,26 @@ wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb,
   size_t q = 0, s = 0, z = 0;
   switch (fmt) {
     case WQ_FMT_W8_PC: q = (size_t)(K * N); s = (size_t)(2 * N); break;
-    case WQ_FMT_W8_G128: q = (size_t)(K * N); s = (size_t)(2 * N * G); break;
+    case WQ_FMT_W8_G128:
+      q = (size_t)(K * N);
+      s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * G) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
+      break;
     case WQ_FMT_W4_G128:
       q = (size_t)(K * N / 2);
-      s = (size_t)(2 * N * G);
-      z = layout == WQ_LAYOUT_CANONICAL ? (size_t)(G * (N / 8) * 4) : (size_t)(N * ((G + 1) / 2));
+      s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * G) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
+      z = layout == WQ_LAYOUT_CANONICAL ? (size_t)(G * (N / 8) * 4)
+                                        : (size_t)(row_tiles(N) * G * (kGemvTileRows / 2));
       break;
   }
   if (qb) *qb = q;
   if (sb) *sb = s;
   if (zb) *zb = z;
   return WQ_OK;
+}
+
+int wq_gemv_max_split(int fmt, int64_t K) {
+  if (check_shape(fmt, K, 8) != WQ_OK) return -1;
+  return clamp_split(kMaxSplit, gemv_slices(K, fmt));
 }
 
 int wq_gemv_max_waves(int fmt, int64_t M) {
@@ -348,8 +360,12 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   };
   std::vector<Cand> cand;
   if (gemv) {
-    for (int s = 1; s <= kMaxSplit; s *= 2)
-      for (int wv = 1; wv <= gemv_max_waves(copies[0].fmt, (int)M); wv *= 2) cand.push_back({s, wv, 0});
+    const int cap = gemv_max_waves(copies[0].fmt, (int)M);
+    for (int s = 1; s <= kMaxSplit; s *= 2) {
+      const int dflt = gemv_default_waves(copies[0].K, copies[0].N, copies[0].fmt, (int)M, s);
+      for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, 0});
+      if (dflt & (dflt - 1)) cand.push_back({s, dflt, 0});  // the default when not a power of two
+    }
   } else {
     for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, t});
   }

@@ -37,8 +37,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// gfx950 int8 codes are u = q + 128; flipping the sign bit gives q.
 __device__ __forceinline__ uint4 i8x16_to_bf16_lo(uint4 v) {
   auto cvt = [](uint32_t d) -> uint2 {
+    d ^= 0x80808080u;
     return make_uint2(pack_bf16x2((float)(int8_t)(d & 0xFFu), (float)(int8_t)((d >> 8) & 0xFFu)),
                       pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24)));
   };
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int G = K / kGroup, Gh = (G + 1) / 2;
+  const int G = K / kGroup;
   constexpr bool kGrouped = FMT != WQ_FMT_W8_PC;
 
   // ---- global -> register staging
@@ -94,12 +96,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
         const int i = tid + 256 * j;
         const int row = i >> 2, col = (i & 3) * 16;
         const int n = min(n0 + row, N - 1), k = k0 + col;
-        wb[j] = (k < K) ? *reinterpret_cast<const uint4*>(qw + (size_t)n * K + k) : make_uint4(0, 0, 0, 0);
+        wb[j] = (k < K) ? *reinterpret_cast<const uint4*>(qw + tiled_offset(n, k, N, K)) : make_uint4(0, 0, 0, 0);
       }
     } else {
       const int row = tid >> 1, col = (tid & 1) * 32;
       const int n = min(n0 + row, N - 1);
-      wb[0] = *reinterpret_cast<const uint4*>(qw + (size_t)n * (K / 2) + (k0 + col) / 2);
+      wb[0] = *reinterpret_cast<const uint4*>(qw + tiled_offset(n, (k0 + col) / 2, N, K / 2));
     }
   };
   auto store_tile = [&](int k0) {
@@ -121,8 +123,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
       const int row = tid >> 1, col = (tid & 1) * 32;
       const int n = min(n0 + row, N - 1);
       const int g = k0 / kGroup;
-      const uint32_t zb = zeros[(size_t)n * Gh + (g >> 1)];
-      const float z = (float)((zb >> ((g & 1) * 4)) & 0xFu);
+      const uint32_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows) / 2];
+      const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
       *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 0]) = w4_word_to_bf16(wb[0].x, z);
       *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 8]) = w4_word_to_bf16(wb[0].y, z);
       *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 16]) = w4_word_to_bf16(wb[0].z, z);
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = min(n0 + wn * 64 + j * 32 + l32, N - 1);
-          const uint16_t sb = scales[(size_t)n * G + g];
+          const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
           const float s = (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
 #pragma unroll
           for (int i = 0; i < 2; ++i)

@@ -1,27 +1,40 @@
 // Decode GEMV for 1 <= M <= 7 tokens: y[m][n] = sum_k x[m][k] * dequant(W)[n][k].
 //
-// Work decomposition (gfx950, wave64):
-//   * A workgroup owns a tile of kGemvRowsPerWave (RW) consecutive output rows
-//     and one split-K slice of K.  Its W waves (W = 1..16) interleave over the
-//     slice in 1 KB steps: wave w reads chunks (i*W + w)*64 + lane, so at every
-//     step the workgroup streams W contiguous kilobytes of each row with 128-bit
-//     loads, and every lane reuses its x chunk for the RW rows.
-//   * The loop is software-pipelined: the codes (and group metadata) and x of
-//     the next step are in flight while the current step is multiplied.
-//   * Codes become exact bf16 pairs in registers and meet bf16 x pairs in
-//     v_dot2 (two multiply-adds, fp32 accumulate):
-//       - int8: v_cvt_f32_i32 with a sign-extended byte select, then
-//         v_cvt_pk_bf16_f32 (|q| <= 127 is exact in bf16);
-//       - uint4 (nibbles interleaved by the gfx950 repack): (word >> 4i) &
-//         0x000F000F | 0x43004300 is the bf16 pair (128 + q_2i, 128 + q_2i+1);
-//         the offset is removed per 32-element chunk as (128 + z) * sum(x).
+// Work decomposition (gfx950, wave64), "x-stationary":
+//   * K is cut into slices of 64 lanes x one 16-byte code chunk (1024 k for int8,
+//     2048 k for uint4).  A wave takes one slice at a time: every lane keeps its
+//     chunk of x (all M tokens) in registers and streams the same chunk of each
+//     of the 16 rows of the workgroup's row tile; the 16 row loads of a slice are
+//     issued together (16 x 1 KB contiguous per wave), so a wave keeps 16 KB in
+//     flight without software pipelining.
+//   * A workgroup owns one 16-row tile and one split-K range of slices; its W
+//     waves share the slices of that range round-robin.
+//   * Per lane the 16 x M partial sums are reduced across the wave by a butterfly
+//     reduce-scatter (after four exchange levels lane l holds row l & 15), the W
+//     waves' rows meet in LDS and are added in wave order.
+//   * split_k > 1 splits the slices across workgroups: each range writes fp32
+//     partials to the workspace and a second kernel adds them in range order
+//     (deterministic, and no cross-workgroup fence is needed).
+//
+// In-register dequantisation, exact products with fp32 accumulation:
+//   * int8 (gfx950 layout stores u = q + 128): v_perm_b32 places two code bytes
+//     under the fp16 exponent byte 0x64, giving the fp16 pair (1024 + u_a,
+//     1024 + u_b) exactly in one instruction; x is converted to fp16 (exact for
+//     every bf16 value of magnitude 2^-17 .. 65280; smaller magnitudes round to
+//     the fp16 subnormal grid, an absolute change below 2^-25); v_dot2_f32_f16
+//     multiplies, and (1024 + 128) * sum(x) removes the offset.
+//   * uint4 (nibbles interleaved by the gfx950 repack): (word >> 4i) &
+//     0x000F000F | 0x43004300 is the bf16 pair (128 + q_2i, 128 + q_2i+1)
+//     exactly; v_dot2_f32_bf16 with bf16 x, and (128 + z) * sum(x) per 32-element
+//     chunk removes offset and zero-point before the group scale.
+//   * Removing an offset cancels: the fp32 partials carry terms up to
+//     (1152 / |q|) resp. (143 / |q - z|) times larger than the product itself, and
+//     their rounding grows with |x|.  A slice in which some |x| >= 512 therefore
+//     takes the exact path (codes -> exact bf16 q or q - z, v_dot2_f32_bf16), which
+//     also covers magnitudes beyond fp16.  Below 512 the worst case of the offset
+//     paths stays under a third of the tolerance.
 //   * Scales multiply fp32 partial sums (per row at the end for per-channel W8,
-//     per chunk for group-128), so the codes stay exact.
-//   * Each wave reduces its RW x M partials with DPP row operations and lane
-//     reads; the W waves' partials meet in LDS and are summed in wave order.
-//   * split_k > 1 splits K across workgroups: each slice writes fp32 partials
-//     to the workspace and a second kernel sums them in slice order, so the
-//     result is deterministic and no cross-workgroup fence is needed.
+//     per chunk for group-128), so codes are never rounded.
 //
 // Prior art: the tileInfer README ("Key Optimizations": register-only dequantize
 // GEMV with 128-bit loads and warp-shuffle reduction, split-K by its kernel's
@@ -34,282 +47,340 @@ namespace wq {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int RW = kGemvRowsPerWave;
-constexpr int kMaxWaves = 16;
+constexpr int R = kGemvTileRows;  // rows per workgroup tile (16)
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v;
   v.x = (__bf16)lo;
   v.y = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
-
-// Four int8 codes of `d` -> two exact bf16 pairs.
-__device__ __forceinline__ void i8x4_to_bf16(uint32_t d, uint32_t& p0, uint32_t& p1) {
-  p0 = pack_bf16x2((float)(int8_t)(d & 0xFFu), (float)(int8_t)((d >> 8) & 0xFFu));
-  p1 = pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24));
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: nearest even
 }
+// bf16 pair -> fp16 pair (exact in the range described above)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
+  auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
+  return __builtin_bit_cast(uint32_t, h);
+}
 
-#define WQ_DPP(v, ctrl) \
-  __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+// Cross-lane exchange partners.  xor 1 and 2 by DPP quad permutes, xor 4, 8 and 16
+// by ds_swizzle (bit-mask mode), xor 32 by ds_bpermute.
+template <int J>
+__device__ __forceinline__ float xchg(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (J == 1) r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);
+  else if constexpr (J == 2) r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);
+  else if constexpr (J == 4) r = __builtin_amdgcn_ds_swizzle(i, 0x101F);
+  else if constexpr (J == 8) r = __builtin_amdgcn_ds_swizzle(i, 0x201F);
+  else if constexpr (J == 16) r = __builtin_amdgcn_ds_swizzle(i, 0x401F);
+  else r = __shfl_xor(i, 32);
+  return __builtin_bit_cast(float, r);
+}
 
-// Sum over the 64 lanes of a wave; the result is wave-uniform.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += WQ_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
-  v += WQ_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
-  v += WQ_DPP(v, 0x141);  // row_half_mirror
-  v += WQ_DPP(v, 0x140);  // row_mirror
-  const int iv = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
-  return (r0 + r1) + (r2 + r3);
+// One reduce-scatter level over lanes differing in bit log2(J): values at
+// positions 2i and 2i+1 hold rows that differ in the corresponding row bit; the
+// lane keeps the one its lane bit selects and adds the partner's copy.
+template <int J, int NV, int M>
+__device__ __forceinline__ void rs_level(float (&v)[R][M], bool hi) {
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float keep = hi ? v[2 * i + 1][m] : v[2 * i][m];
+      const float send = hi ? v[2 * i][m] : v[2 * i + 1][m];
+      v[i][m] = keep + xchg<J>(send);
+    }
 }
 
 template <int FMT>
 struct Fmt;
 template <>
 struct Fmt<WQ_FMT_W8_PC> {
-  static constexpr int kPerChunk = 16;  // k values per 16-byte chunk of codes
-  static constexpr int kChunksPerUnit = 1;
-  static constexpr int kXWords = 8;     // uint32 (bf16 pairs) of x per chunk and token
+  static constexpr int kChunk = 16;   // k per lane and slice (16 code bytes)
+  static constexpr int kXWords = 8;   // bf16 pairs of x per lane and token
 };
 template <>
 struct Fmt<WQ_FMT_W8_G128> {
-  static constexpr int kPerChunk = 16;
-  static constexpr int kChunksPerUnit = 8;  // one 128-group
+  static constexpr int kChunk = 16;
   static constexpr int kXWords = 8;
 };
 template <>
 struct Fmt<WQ_FMT_W4_G128> {
-  static constexpr int kPerChunk = 32;
-  static constexpr int kChunksPerUnit = 4;
+  static constexpr int kChunk = 32;
   static constexpr int kXWords = 16;
 };
 
-// Registers of one pipeline stage: codes of RW rows, x for M tokens, metadata.
-template <int FMT, int M>
-struct Stage {
-  uint4 w[RW];
-  uint32_t x[M][Fmt<FMT>::kXWords];
-  uint16_t s[RW];
-  uint8_t z[RW];
-};
-
-template <int FMT, int M>
-__device__ __forceinline__ void load_stage(Stage<FMT, M>& st, const uint8_t* const* rowp,
-                                           const int* rown, const uint16_t* __restrict__ x,
-                                           const uint16_t* __restrict__ scales,
-                                           const uint8_t* __restrict__ zeros, int K, int G, int Gh,
-                                           int c) {
+// grid = (row tiles, split_k); block = 64 * W threads, W <= MAXW.
+template <int FMT, int M, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros,
+                                                           const uint16_t* __restrict__ x,
+                                                           uint16_t* __restrict__ y,
+                                                           float* __restrict__ part, int K, int N) {
   using F = Fmt<FMT>;
-#pragma unroll
-  for (int r = 0; r < RW; ++r) st.w[r] = *reinterpret_cast<const uint4*>(rowp[r] + (size_t)c * 16);
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint4* xs = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)c * F::kPerChunk);
-#pragma unroll
-    for (int j = 0; j < F::kXWords / 4; ++j) {
-      const uint4 a = xs[j];
-      st.x[m][4 * j + 0] = a.x;
-      st.x[m][4 * j + 1] = a.y;
-      st.x[m][4 * j + 2] = a.z;
-      st.x[m][4 * j + 3] = a.w;
-    }
-  }
-  if constexpr (FMT == WQ_FMT_W8_G128) {
-#pragma unroll
-    for (int r = 0; r < RW; ++r) st.s[r] = scales[(size_t)rown[r] * G + (c >> 3)];
-  } else if constexpr (FMT == WQ_FMT_W4_G128) {
-    const int g = c >> 2;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      st.s[r] = scales[(size_t)rown[r] * G + g];
-      st.z[r] = zeros[(size_t)rown[r] * Gh + (g >> 1)];
-    }
-  }
-}
+  constexpr int kSlice = 64 * F::kChunk;
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  __shared__ float red[MAXW][M * R];
 
-template <int FMT, int M>
-__device__ __forceinline__ void compute_stage(const Stage<FMT, M>& st, float (&acc)[RW][M], int c) {
-  if constexpr (FMT != WQ_FMT_W4_G128) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int tile = blockIdx.x, n0 = tile * R;
+  const int s = blockIdx.y, S = gridDim.y;
+  const int T = (K + kSlice - 1) / kSlice;
+  const int sl0 = (int)(((int64_t)s * T) / S), sl1 = (int)(((int64_t)(s + 1) * T) / S);
+  const int G = K / kGroup;
+  const size_t row_bytes = kW4 ? (size_t)K / 2 : (size_t)K;
+
+  // tile base in the gfx950 code layout and its row count (the last tile may be short)
+  const uint8_t* tile_base = qw + (size_t)tile * R * row_bytes;
+  const int nr = min(R, N - n0);
+
+  float acc[R][M];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      uint32_t wp[8];
-      i8x4_to_bf16(st.w[r].x, wp[0], wp[1]);
-      i8x4_to_bf16(st.w[r].y, wp[2], wp[3]);
-      i8x4_to_bf16(st.w[r].z, wp[4], wp[5]);
-      i8x4_to_bf16(st.w[r].w, wp[6], wp[7]);
-      if constexpr (FMT == WQ_FMT_W8_PC) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+  float xs_total[M];  // W8: sum of x over this lane's chunks (offset removal)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[r][m] = dot2(wp[i], st.x[m][i], acc[r][m]);
-      } else {
-        const float sc = bf16_to_f32(st.s[r]);
+  for (int m = 0; m < M; ++m) xs_total[m] = 0.f;
+
+  for (int sl = sl0 + wave; sl < sl1; sl += W) {
+    const int k = sl * kSlice + lane * F::kChunk;
+    const bool valid = k < K;           // the last slice may be ragged
+    const int kk = valid ? k : 0;
+
+    // ---- loads: 16 row chunks (one contiguous block per slice), x chunk, metadata
+    const int wsl = (int)min((size_t)kSliceBytes, row_bytes - (size_t)sl * kSliceBytes);  // bytes per row
+    const uint8_t* sbase = tile_base + (size_t)nr * kSliceBytes * sl + (valid ? lane * 16 : 0);
+    uint4 cw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(r, nr - 1) * wsl);
+    uint32_t xb[M][F::kXWords];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)m * K + kk);
+#pragma unroll
+      for (int j = 0; j < F::kXWords / 4; ++j) {
+        const uint4 a = xp[j];
+        xb[m][4 * j + 0] = valid ? a.x : 0u;
+        xb[m][4 * j + 1] = valid ? a.y : 0u;
+        xb[m][4 * j + 2] = valid ? a.z : 0u;
+        xb[m][4 * j + 3] = valid ? a.w : 0u;
+      }
+    }
+    const int g = kk / kGroup;
+    uint4 sv0 = make_uint4(0, 0, 0, 0), sv1 = make_uint4(0, 0, 0, 0);
+    uint2 zv = make_uint2(0, 0);
+    if constexpr (FMT != WQ_FMT_W8_PC) {
+      const uint4* sp = reinterpret_cast<const uint4*>(scales + ((size_t)tile * G + g) * R);
+      sv0 = sp[0];
+      sv1 = sp[1];
+    }
+    if constexpr (kW4) zv = *reinterpret_cast<const uint2*>(zeros + ((size_t)tile * G + g) * (R / 2));
+    const uint32_t sw[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
+
+    // any |x| >= 512 in this slice?  (a bf16 exponent field >= 136 carries into bit
+    // 15 of its half when 0x3C00 is added)
+    uint32_t big = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < F::kXWords; ++i) big |= ((xb[m][i] & 0x7F807F80u) + 0x3C003C00u) & 0x80008000u;
+    const bool exact_path = __builtin_amdgcn_ballot_w64(big != 0) != 0;
+
+    if constexpr (!kW4) {
+      // ---- int8
+      if (!exact_path) {
+        uint32_t xh[M][8];
+        float xs[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           float t = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) t = dot2(wp[i], st.x[m][i], t);
-          acc[r][m] = fmaf(sc, t, acc[r][m]);
+          for (int i = 0; i < 8; ++i) {
+            xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
+            t = dot2_f16(xh[m][i], 0x3C003C00u, t);  // x . (1, 1)
+          }
+          xs[m] = t;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t d[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+          uint32_t hp[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            hp[2 * j] = __builtin_amdgcn_perm(0x64646464u, d[j], 0x04010400u);
+            hp[2 * j + 1] = __builtin_amdgcn_perm(0x64646464u, d[j], 0x04030402u);
+          }
+          if constexpr (FMT == WQ_FMT_W8_PC) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[r][m] = dot2_f16(hp[i], xh[m][i], acc[r][m]);
+          } else {
+            const uint32_t word = sw[r >> 1];
+            const float sc = bf16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              float t = 0.f;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) t = dot2_f16(hp[i], xh[m][i], t);
+              acc[r][m] = fmaf(sc, fmaf(-1152.f, xs[m], t), acc[r][m]);
+            }
+          }
+        }
+        if constexpr (FMT == WQ_FMT_W8_PC) {
+#pragma unroll
+          for (int m = 0; m < M; ++m) xs_total[m] += xs[m];
+        }
+      } else {
+        // exact bf16 path: signed code -> fp32 -> bf16 pairs
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t d[4] = {cw[r].x ^ 0x80808080u, cw[r].y ^ 0x80808080u, cw[r].z ^ 0x80808080u,
+                                 cw[r].w ^ 0x80808080u};
+          uint32_t bp[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bp[2 * j] = pack_bf16x2((float)(int8_t)(d[j] & 0xFFu), (float)(int8_t)((d[j] >> 8) & 0xFFu));
+            bp[2 * j + 1] = pack_bf16x2((float)(int8_t)((d[j] >> 16) & 0xFFu), (float)(int8_t)(d[j] >> 24));
+          }
+          float sc = 1.f;
+          if constexpr (FMT == WQ_FMT_W8_G128) {
+            const uint32_t word = sw[r >> 1];
+            sc = bf16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
+          }
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t = dot2_bf16(bp[i], xb[m][i], t);
+            acc[r][m] = fmaf(sc, t, acc[r][m]);
+          }
         }
       }
-    }
-  } else {
-    float xsum[M];
+    } else if (!exact_path) {
+      // ---- uint4 group-128, offset path
+      float xs[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float t = 0.f;
+      for (int m = 0; m < M; ++m) {
+        float t = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t = dot2(st.x[m][i], 0x3F803F80u, t);  // x . (1, 1)
-      xsum[m] = t;
-    }
-    const int g = c >> 2;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const float sc = f16_to_f32(st.s[r]);
-      const float off = 128.f + (float)((st.z[r] >> ((g & 1) * 4)) & 0xFu);
-      const uint32_t words[4] = {st.w[r].x, st.w[r].y, st.w[r].z, st.w[r].w};
-      float t[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) t[m] = 0.f;
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t p = ((words[wi] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-#pragma unroll
-          for (int m = 0; m < M; ++m) t[m] = dot2(p, st.x[m][4 * wi + i], t[m]);
-        }
+        for (int i = 0; i < 16; ++i) t = dot2_bf16(xb[m][i], 0x3F803F80u, t);  // x . (1, 1)
+        xs[m] = t;
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, fmaf(-off, xsum[m], t[m]), acc[r][m]);
-    }
-  }
-}
-
-// grid = (row tiles, split_k); block = 64 * W threads, W <= MAXW (the register
-// budget per thread shrinks as the workgroup grows: 512 VGPRs per SIMD lane are
-// shared by the W/4 waves a SIMD hosts).
-template <int FMT, int M, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restrict__ qw,
-                                                      const uint16_t* __restrict__ scales,
-                                                      const uint8_t* __restrict__ zeros,
-                                                      const uint16_t* __restrict__ x,
-                                                      uint16_t* __restrict__ y,
-                                                      float* __restrict__ part, int K, int N) {
-  using F = Fmt<FMT>;
-  __shared__ float red[MAXW][RW * M];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  const int n0 = blockIdx.x * RW;
-  const int s = blockIdx.y, S = gridDim.y;
-
-  const int chunks_row = K / F::kPerChunk;
-  const int units = chunks_row / F::kChunksPerUnit;
-  const int c0 = (int)(((int64_t)s * units) / S) * F::kChunksPerUnit;
-  const int c1 = (int)(((int64_t)(s + 1) * units) / S) * F::kChunksPerUnit;
-  const int G = K / kGroup;
-  const int Gh = (G + 1) / 2;
-  const size_t row_bytes = (FMT == WQ_FMT_W4_G128) ? (size_t)K / 2 : (size_t)K;
-
-  const uint8_t* rowp[RW];
-  int rown[RW];
+      for (int r = 0; r < R; ++r) {
+        const uint32_t word = sw[r >> 1];
+        const float sc = f16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
+        const uint32_t zsrc = r < 8 ? zv.x : zv.y;
+        const float off = 128.f + (float)((zsrc >> (4 * (r & 7))) & 0xFu);
+        const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+        float t[M];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    rown[r] = min(n0 + r, N - 1);
-    rowp[r] = qw + (size_t)rown[r] * row_bytes;
-  }
-
-  float acc[RW][M];
+        for (int m = 0; m < M; ++m) t[m] = 0.f;
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+        for (int wi = 0; wi < 4; ++wi)
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-
-  // Two register stages in ping-pong: the loads of one are in flight while the
-  // other is multiplied.  The loop is counted so that every prefetched stage is
-  // consumed (the compiler then keeps the prefetch ahead of the math and the wait
-  // counters only wait for the older stage).
-  const int step = 64 * W;
-  const int cfirst = c0 + wave * 64 + lane;
-  const int n = cfirst < c1 ? (c1 - cfirst + step - 1) / step : 0;  // chunks of this lane
-  if (n > 0) {
-    Stage<FMT, M> A, B;
-    int c = cfirst;
-    load_stage<FMT, M>(A, rowp, rown, x, scales, zeros, K, G, Gh, c);
-    int left = n;  // stages not yet multiplied, the first of them in A
-    while (left >= 3) {
-      load_stage<FMT, M>(B, rowp, rown, x, scales, zeros, K, G, Gh, c + step);
-      compute_stage<FMT, M>(A, acc, c);
-      load_stage<FMT, M>(A, rowp, rown, x, scales, zeros, K, G, Gh, c + 2 * step);
-      compute_stage<FMT, M>(B, acc, c + step);
-      c += 2 * step;
-      left -= 2;
-    }
-    if (left == 2) {
-      load_stage<FMT, M>(B, rowp, rown, x, scales, zeros, K, G, Gh, c + step);
-      compute_stage<FMT, M>(A, acc, c);
-      compute_stage<FMT, M>(B, acc, c + step);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t p = ((words[wi] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+#pragma unroll
+            for (int m = 0; m < M; ++m) t[m] = dot2_bf16(p, xb[m][4 * wi + i], t[m]);
+          }
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, fmaf(-off, xs[m], t[m]), acc[r][m]);
+      }
     } else {
-      compute_stage<FMT, M>(A, acc, c);
+      // ---- uint4 group-128, exact path: bf16(q - z) pairs
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t word = sw[r >> 1];
+        const float sc = f16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
+        const uint32_t zsrc = r < 8 ? zv.x : zv.y;
+        const float z = (float)((zsrc >> (4 * (r & 7))) & 0xFu);
+        const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+        float t[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[m] = 0.f;
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t p = pack_bf16x2((float)((words[wi] >> (4 * i)) & 0xFu) - z,
+                                           (float)((words[wi] >> (16 + 4 * i)) & 0xFu) - z);
+#pragma unroll
+            for (int m = 0; m < M; ++m) t[m] = dot2_bf16(p, xb[m][4 * wi + i], t[m]);
+          }
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, t[m], acc[r][m]);
+      }
     }
   }
-
-  float tot[RW][M];
+  if constexpr (FMT == WQ_FMT_W8_PC) {
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) tot[r][m] = wave_sum(acc[r][m]);
+      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(-1152.f, xs_total[m], acc[r][m]);
+  }
 
-  const int t = threadIdx.x;
-  float v = 0.f;
+  // ---- wave reduce-scatter: afterwards lane l holds row (l & 15), all M tokens
+  rs_level<1, 16, M>(acc, lane & 1);
+  rs_level<2, 8, M>(acc, lane & 2);
+  rs_level<4, 4, M>(acc, lane & 4);
+  rs_level<8, 2, M>(acc, lane & 8);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    acc[0][m] += xchg<16>(acc[0][m]);
+    acc[0][m] += xchg<32>(acc[0][m]);
+  }
+
+  const int row = lane & 15, n = n0 + row;
+  float v[M];
   if (W == 1) {
-    // lane j < RW*M takes (r, m) = (j % RW, j / RW); values are wave-uniform
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        if (t == m * RW + r) v = tot[r][m];
+    for (int m = 0; m < M; ++m) v[m] = acc[0][m];
   } else {
-    if (lane == 0) {
+    if (lane < R) {
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) red[wave][m * RW + r] = tot[r][m];
+      for (int m = 0; m < M; ++m) red[wave][m * R + row] = acc[0][m];
     }
     __syncthreads();
-    if (t < RW * M)
-      for (int w = 0; w < W; ++w) v += red[w][t];
+    if (wave != 0) return;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f;
+      for (int w = 0; w < W; ++w) a += red[w][m * R + row];
+      v[m] = a;
+    }
   }
-  if (t < RW * M) {
-    const int r = t % RW, m = t / RW, n = n0 + r;
-    if (n < N) {
-      if (S == 1) {
-        const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
-        y[(size_t)m * N + n] = f32_to_bf16(sc * v);
-      } else {
-        part[((size_t)s * M + m) * N + n] = v;
-      }
+  if (lane < R && n < N) {
+    if (S == 1) {
+      const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) y[(size_t)m * N + n] = f32_to_bf16(sc * v[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[((size_t)s * M + m) * N + n] = v[m];
     }
   }
 }
 
-// y[m][n] = bf16(scale[n] * sum_s part[s][m][n]), slices summed in order.
+// y[m][n] = bf16(scale[n] * sum_s part[s][m][n]), ranges added in order.
 template <int FMT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ scales,
@@ -325,19 +396,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   y[i] = f32_to_bf16(sc * v);
 }
 
-// Largest waves per workgroup whose register budget (512 / (W/4) VGPRs per lane)
-// holds this format and M without spilling.
+// Largest waves per workgroup whose register budget (512 / ceil(W/4) VGPRs per
+// lane) holds this format and M without spilling.
 constexpr int max_waves(int fmt, int M) {
-  return fmt == WQ_FMT_W8_PC ? (M <= 4 ? 16 : 8)
-         : fmt == WQ_FMT_W8_G128 ? (M <= 3 ? 16 : 8)
-                                 : (M <= 1 ? 16 : M <= 5 ? 8 : 4);
+  return fmt == WQ_FMT_W8_PC ? (M <= 1 ? 16 : M <= 4 ? 8 : 4) : fmt == WQ_FMT_W8_G128 ? (M <= 4 ? 8 : 4) : (M <= 3 ? 8 : 4);
 }
 
 template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
                      int waves, void* ws, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
-  const int tiles = (N + RW - 1) / RW;
+  const int tiles = (N + R - 1) / R;
   dim3 grid(tiles, split_k);
   dim3 block(64 * waves);
   float* part = (float*)ws;
@@ -385,24 +454,24 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
 
 int gemv_max_waves(int fmt, int M) { return max_waves(fmt, M); }
 
+int64_t gemv_slices(int64_t K, int fmt) {
+  const int64_t slice = 64 * (fmt == WQ_FMT_W4_G128 ? 32 : 16);
+  return (K + slice - 1) / slice;
+}
+
 int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k) {
-  // aim at about 8192 resident waves (32 per CU) with at least two 1-KB steps
-  // of each row per wave
-  const int64_t tiles = (N + RW - 1) / RW;
-  const int64_t per_chunk = fmt == WQ_FMT_W4_G128 ? 32 : 16;
-  const int64_t slice_chunks = (K / per_chunk) / split_k;
-  const int cap = gemv_max_waves(fmt, M);
-  int w = 1;
-  while (w < cap && tiles * split_k * (w * 2) <= 8192 && slice_chunks >= (int64_t)(w * 2) * 128) w *= 2;
-  return w;
+  // one slice per wave: the waves of a workgroup cover its range of K slices
+  // (capped by the register budget; the waves then take several slices each)
+  const int64_t per_split = (gemv_slices(K, fmt) + split_k - 1) / split_k;
+  (void)N;
+  const int cap = max_waves(fmt, M);
+  return (int)(per_split < cap ? (per_split < 1 ? 1 : per_split) : cap);
 }
 
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
                       int waves, void* ws, hipStream_t s) {
-  if (waves < 1 || waves > kMaxWaves || (waves & (waves - 1)))
-    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 1, 2, 4, 8 or 16");
-  if (waves > gemv_max_waves(w->fmt, M))
-    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: at this M a workgroup holds at most " +
+  if (waves < 1 || waves > gemv_max_waves(w->fmt, M))
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: at this M a workgroup holds 1.." +
                                         std::to_string(gemv_max_waves(w->fmt, M)) + " waves");
   switch (w->fmt) {
     case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, ws, s);

@@ -13,7 +13,8 @@ namespace wq {
 constexpr int kGroup = 128;        // group size along K for the group-128 formats
 constexpr int kMaxSplit = 32;      // largest split_k of the tuning grid
 constexpr int kGemvMaxM = 7;       // tokens < 8 take the GEMV
-constexpr int kGemvRowsPerWave = 4;  // output rows per GEMV workgroup tile
+constexpr int kGemvTileRows = 16;    // output rows per GEMV workgroup tile (and per
+                                     // gfx950 metadata tile of the group-128 formats)
 constexpr int kGemvMaxWaves = 16;    // waves per GEMV workgroup (intra-workgroup K split)
 
 // Thread-local error text behind wq_last_error().
@@ -31,8 +32,21 @@ wq_status hip_fail(hipError_t e, const char* what);
 wq_status check_shape(int fmt, int64_t K, int64_t N);
 wq_status check_weight(const wq_weight* w, int want_layout);
 
-// K granule that split-K slices align to: 16 (per-channel W8) or 128 (group-128).
-inline int64_t split_granule(int fmt) { return fmt == WQ_FMT_W8_PC ? 16 : kGroup; }
+// Number of 16-row tiles of N (the gfx950 metadata of group-128 formats is padded to them).
+__host__ __device__ inline int64_t row_tiles(int64_t N) { return (N + kGemvTileRows - 1) / kGemvTileRows; }
+
+// gfx950 code layout: byte b of packed row n (row_bytes = K for int8, K/2 for uint4)
+// lives in the 1 KB slice b / 1024 of its 16-row tile; a tile stores its slices one
+// after another and a slice stores its rows one after another, so the 16 rows x
+// 1 KB a GEMV wave reads for one slice are one contiguous block.
+constexpr int kSliceBytes = 1024;
+__host__ __device__ inline size_t tiled_offset(int64_t n, int64_t b, int64_t N, int64_t row_bytes) {
+  const int64_t t = n / kGemvTileRows, r = n % kGemvTileRows;
+  const int64_t nr = N - t * kGemvTileRows < kGemvTileRows ? N - t * kGemvTileRows : kGemvTileRows;
+  const int64_t sl = b / kSliceBytes, j = b % kSliceBytes;
+  const int64_t w = row_bytes - sl * kSliceBytes < kSliceBytes ? row_bytes - sl * kSliceBytes : kSliceBytes;
+  return (size_t)(t * kGemvTileRows * row_bytes + nr * kSliceBytes * sl + r * w + j);
+}
 
 // --- kernel launchers (implemented in the .hip files) ---
 wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s);
@@ -43,6 +57,9 @@ wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y,
 int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k);
 // Largest waves per GEMV workgroup that fits the registers at this format and M.
 int gemv_max_waves(int fmt, int M);
+// K slices of the GEMV (64 lanes x one 16-byte chunk: 1024 k int8, 2048 k uint4);
+// split-K ranges are whole slices.
+int64_t gemv_slices(int64_t K, int fmt);
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       hipStream_t s);
 

@@ -164,34 +164,75 @@ __device__ __forceinline__ uint32_t nibbles_from_gfx950(uint32_t o) {
   return c;
 }
 
-__global__ void w4_words_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
-                                size_t n_words, int to_gfx950) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
-       i += (size_t)gridDim.x * blockDim.x) {
-    uint32_t v = src[i];
-    dst[i] = to_gfx950 ? nibbles_to_gfx950(v) : nibbles_from_gfx950(v);
-  }
-}
-
-// canonical zeros uint32 [G][N/8]  ->  gfx950 zeros uint8 [N][ceil(G/2)]
-__global__ void w4_zeros_to_gfx950_kernel(const uint32_t* __restrict__ zc, uint8_t* __restrict__ zg,
-                                          int G, int N) {
-  const int Gh = (G + 1) / 2;
-  const size_t total = (size_t)N * Gh;
+// Codes, one 16-byte chunk per thread: canonical row-major [N][row_bytes] <->
+// gfx950 tiled order (tiled_offset); int8 codes get their sign bit flipped
+// (u = q + 128), uint4 words get their nibbles interleaved.
+template <bool W4>
+__global__ void codes_repack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                    int64_t N, int64_t row_bytes, int to_gfx950) {
+  const int64_t chunks_row = row_bytes / 16;
+  const size_t total = (size_t)N * chunks_row;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
-    const int n = (int)(i / Gh), h = (int)(i % Gh);
-    const int sh = 4 * (n % 8);
-    uint32_t lo = (zc[(size_t)(2 * h) * (N / 8) + n / 8] >> sh) & 0xFu;
-    uint32_t hi = (2 * h + 1 < G) ? (zc[(size_t)(2 * h + 1) * (N / 8) + n / 8] >> sh) & 0xFu : 0u;
-    zg[i] = (uint8_t)(lo | (hi << 4));
+    const int64_t n = (int64_t)(i / chunks_row), b = (int64_t)(i % chunks_row) * 16;
+    const size_t lin = (size_t)n * row_bytes + b, til = tiled_offset(n, b, N, row_bytes);
+    uint4 v = *reinterpret_cast<const uint4*>(src + (to_gfx950 ? lin : til));
+    if (W4) {
+      if (to_gfx950) {
+        v.x = nibbles_to_gfx950(v.x); v.y = nibbles_to_gfx950(v.y);
+        v.z = nibbles_to_gfx950(v.z); v.w = nibbles_to_gfx950(v.w);
+      } else {
+        v.x = nibbles_from_gfx950(v.x); v.y = nibbles_from_gfx950(v.y);
+        v.z = nibbles_from_gfx950(v.z); v.w = nibbles_from_gfx950(v.w);
+      }
+    } else {
+      v.x ^= 0x80808080u; v.y ^= 0x80808080u; v.z ^= 0x80808080u; v.w ^= 0x80808080u;
+    }
+    *reinterpret_cast<uint4*>(dst + (to_gfx950 ? til : lin)) = v;
   }
 }
 
-// gfx950 zeros uint8 [N][ceil(G/2)]  ->  canonical zeros uint32 [G][N/8]
-__global__ void w4_zeros_from_gfx950_kernel(const uint8_t* __restrict__ zg, uint32_t* __restrict__ zc,
+// Group scales: canonical [N][G]  <->  gfx950 tiles [N16][G][16] (16 rows of one
+// group side by side; rows past N hold 0).
+__global__ void scales_tile_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                   int N, int G, int to_tiled) {
+  const size_t total = to_tiled ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * G;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    if (to_tiled) {
+      const size_t t = i / ((size_t)G * kGemvTileRows), rem = i % ((size_t)G * kGemvTileRows);
+      const int g = (int)(rem / kGemvTileRows), j = (int)(rem % kGemvTileRows);
+      const size_t n = t * kGemvTileRows + j;
+      dst[i] = n < (size_t)N ? src[n * G + g] : (uint16_t)0;
+    } else {
+      const size_t n = i / G, g = i % G;
+      dst[i] = src[((n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
+    }
+  }
+}
+
+// canonical zeros uint32 [G][N/8]  ->  gfx950 zeros uint8 [N16][G][8], byte (t,g,h)
+// holding z[16t+2h][g] (bits 0..3) and z[16t+2h+1][g] (bits 4..7)
+__global__ void w4_zeros_to_gfx950_kernel(const uint32_t* __restrict__ zc, uint8_t* __restrict__ zt,
+                                          int G, int N) {
+  const size_t total = (size_t)row_tiles(N) * G * (kGemvTileRows / 2);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / ((size_t)G * 8), rem = i % ((size_t)G * 8);
+    const int g = (int)(rem / 8), h = (int)(rem % 8);
+    uint32_t b = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const size_t n = t * kGemvTileRows + 2 * h + e;
+      if (n < (size_t)N) b |= ((zc[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu) << (4 * e);
+    }
+    zt[i] = (uint8_t)b;
+  }
+}
+
+// gfx950 zeros uint8 [N16][G][8]  ->  canonical zeros uint32 [G][N/8]
+__global__ void w4_zeros_from_gfx950_kernel(const uint8_t* __restrict__ zt, uint32_t* __restrict__ zc,
                                             int G, int N) {
-  const int Gh = (G + 1) / 2;
   const size_t total = (size_t)G * (N / 8);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -199,8 +240,9 @@ __global__ void w4_zeros_from_gfx950_kernel(const uint8_t* __restrict__ zg, uint
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint8_t b = zg[(size_t)(8 * c + j) * Gh + g / 2];
-      word |= (uint32_t)((b >> (4 * (g & 1))) & 0xF) << (4 * j);
+      const size_t n = (size_t)8 * c + j;
+      const uint8_t b = zt[((n / kGemvTileRows) * G + g) * 8 + (n % kGemvTileRows) / 2];
+      word |= (uint32_t)((b >> (4 * (n & 1))) & 0xF) << (4 * j);
     }
     zc[i] = word;
   }
@@ -239,27 +281,40 @@ wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s) {
 
 wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s) {
   size_t qb = 0, sb = 0, zb = 0;
-  wq_status st = wq_packed_sizes(src->fmt, src->layout, src->K, src->N, &qb, &sb, &zb);
+  wq_status st = wq_packed_sizes(src->fmt, WQ_LAYOUT_CANONICAL, src->K, src->N, &qb, &sb, &zb);
   if (st != WQ_OK) return st;
-  WQ_HIP_CHECK(hipMemcpyAsync(dst->scales, src->scales, sb, hipMemcpyDeviceToDevice, s));
-  if (src->fmt != WQ_FMT_W4_G128) {
-    // W8: the gfx950 layout keeps the canonical bytes.
-    WQ_HIP_CHECK(hipMemcpyAsync(dst->qweight, src->qweight, qb, hipMemcpyDeviceToDevice, s));
-    return WQ_OK;
-  }
-  const size_t words = qb / 4;
-  w4_words_kernel<<<grid_for(words, 256), 256, 0, s>>>((const uint32_t*)src->qweight,
-                                                       (uint32_t*)dst->qweight, words, to_gfx950);
-  WQ_HIP_CHECK(hipGetLastError());
   const int G = (int)(src->K / kGroup), N = (int)src->N;
-  if (to_gfx950) {
-    w4_zeros_to_gfx950_kernel<<<grid_for((size_t)N * ((G + 1) / 2), 256), 256, 0, s>>>(
-        (const uint32_t*)src->zeros, (uint8_t*)dst->zeros, G, N);
+  const int64_t row_bytes = (int64_t)(qb / (size_t)N);
+  const size_t chunks = qb / 16;
+  // codes
+  if (src->fmt == WQ_FMT_W4_G128) {
+    codes_repack_kernel<true><<<grid_for(chunks, 256), 256, 0, s>>>(
+        (const uint8_t*)src->qweight, (uint8_t*)dst->qweight, N, row_bytes, to_gfx950);
   } else {
-    w4_zeros_from_gfx950_kernel<<<grid_for((size_t)G * (N / 8), 256), 256, 0, s>>>(
-        (const uint8_t*)src->zeros, (uint32_t*)dst->zeros, G, N);
+    codes_repack_kernel<false><<<grid_for(chunks, 256), 256, 0, s>>>(
+        (const uint8_t*)src->qweight, (uint8_t*)dst->qweight, N, row_bytes, to_gfx950);
   }
   WQ_HIP_CHECK(hipGetLastError());
+  // scales
+  if (src->fmt == WQ_FMT_W8_PC) {
+    WQ_HIP_CHECK(hipMemcpyAsync(dst->scales, src->scales, sb, hipMemcpyDeviceToDevice, s));
+  } else {
+    const size_t n = to_gfx950 ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * G;
+    scales_tile_kernel<<<grid_for(n, 256), 256, 0, s>>>((const uint16_t*)src->scales,
+                                                        (uint16_t*)dst->scales, N, G, to_gfx950);
+    WQ_HIP_CHECK(hipGetLastError());
+  }
+  // zero-points
+  if (src->fmt == WQ_FMT_W4_G128) {
+    if (to_gfx950) {
+      w4_zeros_to_gfx950_kernel<<<grid_for((size_t)row_tiles(N) * G * 8, 256), 256, 0, s>>>(
+          (const uint32_t*)src->zeros, (uint8_t*)dst->zeros, G, N);
+    } else {
+      w4_zeros_from_gfx950_kernel<<<grid_for((size_t)G * (N / 8), 256), 256, 0, s>>>(
+          (const uint8_t*)src->zeros, (uint32_t*)dst->zeros, G, N);
+    }
+    WQ_HIP_CHECK(hipGetLastError());
+  }
   return WQ_OK;
 }
 

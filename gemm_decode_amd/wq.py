@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "FMT", "CANONICAL", "GFX950", "WqError", "PackedWeight", "lib",
     "wq_abi_version", "wq_status_string", "wq_last_error", "wq_packed_sizes", "wq_dispatch_kind",
-    "wq_gemv_max_waves",
+    "wq_gemv_max_waves", "wq_gemv_max_split",
     "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
@@ -58,6 +58,7 @@ _SIGS = {
     "wq_packed_sizes": (C.c_int, [C.c_int, C.c_int, C.c_int64, C.c_int64, _P(C.c_size_t), _P(C.c_size_t), _P(C.c_size_t)]),
     "wq_dispatch_kind": (C.c_int, [C.c_int64]),
     "wq_gemv_max_waves": (C.c_int, [C.c_int, C.c_int64]),
+    "wq_gemv_max_split": (C.c_int, [C.c_int, C.c_int64]),
     "wq_pack": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
     "wq_repack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_unrepack": (C.c_int, [_W, _W, C.c_void_p]),
@@ -127,6 +128,10 @@ def wq_dispatch_kind(M: int) -> int:
 
 def wq_gemv_max_waves(fmt, M: int) -> int:
     return lib.wq_gemv_max_waves(_fmt(fmt), M)
+
+
+def wq_gemv_max_split(fmt, K: int) -> int:
+    return lib.wq_gemv_max_split(_fmt(fmt), K)
 
 
 def _fmt(fmt) -> int:

@@ -64,16 +64,25 @@ typedef enum {
  *        scales fp16 [N][K/128];
  *        zeros uint32 [K/128][N/8], bits 4j..4j+3 of word (g,c) hold z[8c+j][g].
  *
- * WQ_LAYOUT_GFX950 (what the compute kernels read; written by wq_repack):
- *   W8:  identical bytes to the canonical layout: each lane's 16-byte load of a row
- *        is contiguous along k and a sign-extending byte convert feeds the math.
- *   W4:  qweight uint32 [N][K/8] whose word (n,c) holds the same 8 codes with the
- *        nibbles interleaved: bits 4p..4p+3 hold q[n][8c + (2p mod 8) + (p >= 4)],
+ * WQ_LAYOUT_GFX950 (what the compute kernels read; written by wq_repack).  N16 =
+ * ceil(N/16) tiles of 16 output rows; metadata entries for rows >= N are 0.
+ *   Codes (both formats) keep the bytes of each packed row (row_bytes = K for int8,
+ *   K/2 for uint4) but store them tile by tile and, inside a tile, 1 KB slice by
+ *   slice: byte b of row n = 16t + r (tile t holding nr = min(16, N - 16t) rows)
+ *   lies in slice sl = b / 1024 of width w = min(1024, row_bytes - 1024 sl) at
+ *       16 * row_bytes * t + nr * 1024 * sl + r * w + (b mod 1024),
+ *   so the 16 rows x 1 KB that a GEMV wave reads for one K slice are contiguous.
+ *   W8:  the code bytes hold u = q + 128 (the sign bit of q flipped), so that a
+ *        byte placed under the fp16 exponent byte 0x64 reads 1024 + u exactly;
+ *        scales bf16 [N] for per-channel; for group-128 bf16 [N16][G][16] with
+ *        element (t,g,j) = s[16t+j][g] (G = K/128): the 16 rows of a tile side by side.
+ *   W4:  each 32-bit word of codes holds the same 8 codes as the canonical word with
+ *        the nibbles interleaved: bits 4p..4p+3 hold q[n][8c + (2p mod 8) + (p >= 4)],
  *        i.e. nibble order q0 q2 q4 q6 q1 q3 q5 q7, so that (word >> 4i) & 0x000F000F
  *        yields the consecutive pair (q[8c+2i], q[8c+2i+1]) in the two 16-bit halves;
- *        scales fp16 [N][K/128] (unchanged);
- *        zeros uint8 [N][ceil(K/256)], byte (n,h) holds z[n][2h] in bits 0..3 and
- *        z[n][2h+1] in bits 4..7 (row-major, so a row's zero-points sit beside it).
+ *        scales fp16 [N16][G][16] as for W8 group-128;
+ *        zeros uint8 [N16][G][8], byte (t,g,h) holds z[16t+2h][g] in bits 0..3 and
+ *        z[16t+2h+1][g] in bits 4..7.
  */
 typedef enum { WQ_LAYOUT_CANONICAL = 0, WQ_LAYOUT_GFX950 = 1 } wq_layout;
 
@@ -154,27 +163,32 @@ wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
  * wave order.  Across workgroups, split_k slices (the split_k of "Heuristic: Mit han
  * lab Llm awq Kernel Selection Thresholds": K partitioned across thread blocks)
  * each write fp32 partials to the workspace (the FP32 reduction scratch of the
- * Marlin page's intro) and a second kernel adds them in slice order.  Each slice
- * is a contiguous run of whole 16-element chunks (whole 128-groups for the
- * group-128 formats).  Results are bit-identical from run to run for a given
- * (split_k, waves).
+ * Marlin page's intro) and a second kernel adds them in range order.  K is cut into
+ * slices of 1024 (int8) or 2048 (uint4) k, each a run of whole 128-groups; a split
+ * range is a run of whole slices.  Results are bit-identical from run to run for a
+ * given (split_k, waves).
  *
  * split_k: 0 = the tuned (split_k, waves) of this shape (1 slice with the default
  * waves when untuned, or when the tuned split needs more workspace than given),
- * else a power of two in 1..32 that does not exceed K/16 (per-channel W8) or
- * K/128 (group-128); waves then take the default for the shape.  ws/ws_bytes may
- * be NULL/0 when split_k resolves to 1. */
+ * else a power of two in 1..wq_gemv_max_split(fmt, K); waves then take the default
+ * for the shape.  ws/ws_bytes may be NULL/0 when split_k resolves to 1. */
 wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
                   size_t ws_bytes, void* stream);
+
+/* Largest split_k the GEMV accepts for a format and K (host only): split-K ranges
+ * are whole K slices of 1024 (int8) or 2048 (uint4) k, so this is the largest power
+ * of two <= min(32, number of slices).  -1 for an invalid format or K. */
+int wq_gemv_max_split(int fmt, int64_t K);
 
 /* Largest waves per GEMV workgroup for a format and 1 <= M <= 7 (host only): the
  * register budget per lane shrinks as a workgroup grows, so larger M allow fewer
  * waves.  Returns -1 for an unknown format or M outside 1..7. */
 int wq_gemv_max_waves(int fmt, int64_t M);
 
-/* wq_gemv with both levels explicit: split_k >= 1 as above and waves in {0 (the
- * default for the shape), 1, 2, 4, 8, 16} per workgroup, at most
- * wq_gemv_max_waves(fmt, M) (else WQ_ERR_UNSUPPORTED).  For tests and tuning. */
+/* wq_gemv with both levels explicit: split_k >= 1 as above and waves per workgroup
+ * 0 (the default for the shape: one K slice per wave, as many as the registers
+ * allow) or 1..wq_gemv_max_waves(fmt, M) (else WQ_ERR_UNSUPPORTED).  For tests and
+ * tuning. */
 wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
                      void* ws, size_t ws_bytes, void* stream);
 
@@ -204,7 +218,8 @@ int wq_tune_pick(const double* lat, int n);
 /* Time every candidate for (format, K, N, M) on the current device and store the
  * winner in the tuner cache: for M < 8 every (split_k, waves) pair with split_k in
  * the grid {1,2,4,8,16,32} (those the shape and workspace allow) and waves in
- * {1,2,4,8,16}; for M >= 8 the GEMM tiles.  Each candidate runs `warmup` untimed
+ * {1,2,4,8,16} plus the default (capped at wq_gemv_max_waves); for M >= 8 the GEMM
+ * tiles.  Each candidate runs `warmup` untimed
  * and `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
  * weights (distinct buffers with the same format and shape) so that the weights
  * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k

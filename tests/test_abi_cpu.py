@@ -39,8 +39,10 @@ def test_packed_sizes_match_the_oracle_layout(wqlib, fmt, K, N):
         pytest.skip("W4 needs N % 8 == 0")
     assert wqlib.wq_packed_sizes(fmt, wqlib.CANONICAL, K, N) == OQ.packed_sizes(fmt, K, N)
     q, s, z = wqlib.wq_packed_sizes(fmt, wqlib.GFX950, K, N)
-    assert (q, s) == OQ.packed_sizes(fmt, K, N)[:2]
-    assert z == (N * ((K // 128 + 1) // 2) if fmt == "w4g128" else 0)
+    n16, G = -(-N // 16), K // 128
+    assert q == OQ.packed_sizes(fmt, K, N)[0]
+    assert s == (2 * N if fmt == "w8pc" else 2 * n16 * 16 * G)
+    assert z == (n16 * G * 8 if fmt == "w4g128" else 0)
 
 
 @pytest.mark.parametrize("fmt,K,N,status", [
@@ -57,10 +59,19 @@ def test_packed_sizes_rejects_bad_shapes(wqlib, fmt, K, N, status):
     assert wqlib.wq_last_error()
 
 
+def test_gemv_max_split(wqlib):
+    assert wqlib.wq_gemv_max_split("w8pc", 1024) == 1
+    assert wqlib.wq_gemv_max_split("w8pc", 5120) == 4       # 5 slices of 1024
+    assert wqlib.wq_gemv_max_split("w8pc", 27648) == 16     # 27 slices
+    assert wqlib.wq_gemv_max_split("w4g128", 5120) == 2     # 3 slices of 2048 (ragged)
+    assert wqlib.wq_gemv_max_split("w8g128", 5120 * 16) == 32
+    assert wqlib.wq_gemv_max_split("w8pc", 1000) == -1
+
+
 def test_gemv_max_waves(wqlib):
     for fmt in ("w8pc", "w8g128", "w4g128"):
         caps = [wqlib.wq_gemv_max_waves(fmt, m) for m in range(1, 8)]
-        assert caps[0] == 16 and all(c in (4, 8, 16) for c in caps) and caps == sorted(caps, reverse=True)
+        assert caps[0] in (8, 16) and all(c in (4, 8, 16) for c in caps) and caps == sorted(caps, reverse=True)
     assert wqlib.wq_gemv_max_waves("w8pc", 0) == -1 and wqlib.wq_gemv_max_waves("w8pc", 8) == -1
     assert wqlib.wq_gemv_max_waves(9, 1) == -1
 
@@ -84,9 +95,9 @@ def test_tuner_cache_roundtrip_and_corrupt_file(wqlib, tmp_path):
     wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 8), tag)
     wqlib.wq_tune_cache_set("w4g128", 13824, 5120, 1, 0, 16, tag)
     with pytest.raises(wqlib.WqError):
-        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 3), tag)
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(3, 4), tag)
     with pytest.raises(wqlib.WqError):
-        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 32), tag)
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 17), tag)
     wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 2048, 1, 2, tag)
     with pytest.raises(wqlib.WqError):
         wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, 3, tag)    # not a power of two
@@ -129,12 +140,12 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(d), None, 1, y, 1, None, 0, None) == 1         # NULL x
     assert L.wq_gemv(C.byref(d), C.c_void_p(0x10008), 1, y, 1, None, 0, None) == 3   # x misaligned
     assert L.wq_gemv(C.byref(d), x, 1, y, 3, None, 0, None) == 1            # split not pow2
-    assert L.wq_gemv(C.byref(d), x, 1, y, 64, None, 0, None) == 1           # split > 32
-    assert L.wq_gemv(C.byref(d), x, 1, y, 4, None, 0, None) == 4            # no workspace
-    assert L.wq_gemv(C.byref(d), x, 1, y, 4, C.c_void_p(0x30000), 16, None) == 4   # too small
-    assert L.wq_gemv(C.byref(d), x, 1, y, 4, C.c_void_p(0x30004), 1 << 20, None) == 3  # ws misaligned
-    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 3, None, 0, None) == 1      # waves not pow2
-    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 32, None, 0, None) == 1     # waves > 16
+    assert L.wq_gemv(C.byref(d), x, 1, y, 2, None, 0, None) == 1            # split > K slices (1)
+    dk = _desc(wqlib, K=8192)
+    assert L.wq_gemv(C.byref(dk), x, 1, y, 4, None, 0, None) == 4           # no workspace
+    assert L.wq_gemv(C.byref(dk), x, 1, y, 4, C.c_void_p(0x30000), 16, None) == 4   # too small
+    assert L.wq_gemv(C.byref(dk), x, 1, y, 4, C.c_void_p(0x30004), 1 << 20, None) == 3  # ws misaligned
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 17, None, 0, None) == 1     # waves > 16
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, None, 0, None) == 1      # split must be given
     dc = _desc(wqlib, layout=0)
     assert L.wq_gemv(C.byref(dc), x, 1, y, 1, None, 0, None) == 2           # canonical layout
@@ -142,6 +153,8 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(dq), x, 1, y, 1, None, 0, None) == 3           # qweight misaligned
     d4 = _desc(wqlib, fmt=2)
     assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
+    dsa = _desc(wqlib, fmt=1, s=0x2002)
+    assert L.wq_gemv(C.byref(dsa), x, 1, y, 1, None, 0, None) == 3          # tiled scales misaligned
     assert L.wq_gemm(C.byref(d), x, 16, y, 9, None, 0, None) == 1           # bad tile
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64

@@ -25,8 +25,8 @@ def wq(wqlib):
 
 
 def _allowed_splits(fmt, K):
-    units = K // (16 if fmt == "w8pc" else 128)
-    return [s for s in SPLITS if s <= units]
+    import gemm_decode_amd.wq as wqb
+    return [s for s in SPLITS if s <= wqb.wq_gemv_max_split(fmt, K)]
 
 
 def _run_gemv(wq, g, x_bits, split):
@@ -50,7 +50,7 @@ def _run_gemm(wq, g, x_bits, tile=0):
 
 # ------------------------------------------------------------------ packing
 SMALL = [("w8pc", 1024, 1024), ("w8pc", 2320, 1000), ("w8g128", 1280, 1000), ("w4g128", 1280, 776),
-         ("w8g128", 384, 264), ("w4g128", 384, 264)]
+         ("w8g128", 384, 264), ("w4g128", 384, 264), ("w8pc", 5200, 1000), ("w4g128", 9088, 264)]
 
 
 @pytest.mark.parametrize("fmt,K,N", SMALL)
@@ -127,7 +127,7 @@ def test_full_size_gemm(wq, cfg, fmt, K, N):
 
 
 # ------------------------------------------------------------- small, full
-@pytest.mark.parametrize("fmt,K,N", [("w8pc", 2320, 1000), ("w8g128", 1280, 1000), ("w4g128", 1280, 776)])
+@pytest.mark.parametrize("fmt,K,N", [("w8pc", 5200, 1000), ("w8g128", 9088, 1000), ("w4g128", 9088, 776)])
 def test_gemv_every_split_and_waves(wq, fmt, K, N):
     """Both levels of the K split: every (split_k, waves per workgroup) pair."""
     W = synth.weight(90, K, N, synth.uses_outliers(fmt))
@@ -139,7 +139,7 @@ def test_gemv_every_split_and_waves(wq, fmt, K, N):
         x = to_dev_bf16(xb)
         ws = wq.workspace(wq.wq_workspace_size(g, M))
         for split in _allowed_splits(fmt, K):
-            for waves in [v for v in wq.WAVES_GRID if v <= wq.wq_gemv_max_waves(fmt, M)]:
+            for waves in range(1, wq.wq_gemv_max_waves(fmt, M) + 1):
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
                 wq.wq_gemv_ex(g, x, y, split, waves, ws=ws)
                 torch.cuda.synchronize()
@@ -174,20 +174,21 @@ def test_gemm_small(wq, fmt, K, N, M):
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_one_hot_is_exact(wq, fmt):
     """x = e_k: every path returns bf16(dequant(W)[n, k]) bit-exactly (one exact
-    nonzero term in every fp32 sum), for every split and both GEMM tiles."""
-    K, N = 1024, 264
+    nonzero term in every fp32 sum), for every split, every waves count and both
+    GEMM tiles.  K spans several (and a ragged) K slices."""
+    K, N = 9216, 264
     W = synth.weight(94, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
     P = OQ.pack(fmt, W)
-    ks = [0, 127, 128, 513, 1023]
+    ks = [0, 127, 128, 4999, 5120, K - 1]
     x = synth.one_hot_activation(K, ks)
     want = OQ.bf16_rne_bits(OQ.dequant(P)[:, ks].T.astype(np.float32))
     for split in _allowed_splits(fmt, K):
         assert np.array_equal(_run_gemv(wq, g, x, split), want), f"gemv split={split}"
     xd = to_dev_bf16(x)
     ws = wq.workspace(wq.wq_workspace_size(g, len(ks)))
-    for waves in [v for v in wq.WAVES_GRID if v <= wq.wq_gemv_max_waves(fmt, len(ks))]:
-        for split in (1, 4):
+    for waves in range(1, wq.wq_gemv_max_waves(fmt, len(ks)) + 1):
+        for split in (1, 2):
             y = torch.empty((len(ks), N), dtype=torch.bfloat16, device=DEV)
             wq.wq_gemv_ex(g, xd, y, split, waves, ws=ws)
             torch.cuda.synchronize()
@@ -208,13 +209,18 @@ def test_identity_is_exact(wq, fmt):
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_zero_and_power_of_two_scaling(wq, fmt):
-    K, N = 1024, 264
+    """x = 0 gives y = 0; x * 4 gives y * 4 bit-exactly.  The scaling invariant
+    holds when no intermediate is subnormal, so x is kept at |x| >= 2^-8 (the int8
+    path carries x as fp16, whose subnormals start below 2^-14)."""
+    K, N = 8192, 264
     W = synth.weight(96, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
     zero = np.zeros((3, K), dtype=np.uint16)
     assert not np.any(_run_gemv(wq, g, zero, 4) & 0x7FFF)
     assert not np.any(_run_gemm(wq, g, np.zeros((20, K), dtype=np.uint16)) & 0x7FFF)
-    x = synth.activation(96, K, 4)
+    xf = OQ.bf16_bits_to_f32(synth.activation(96, K, 4))
+    xf = np.where(np.abs(xf) < 2.0 ** -8, np.copysign(np.float32(2.0 ** -8), xf), xf).astype(np.float32)
+    x = OQ.bf16_rne_bits(xf)
     x4 = OQ.bf16_rne_bits(OQ.bf16_bits_to_f32(x) * np.float32(4.0))
     for split in (1, 4):
         a = OQ.bf16_bits_to_f32(_run_gemv(wq, g, x, split))
@@ -222,8 +228,30 @@ def test_zero_and_power_of_two_scaling(wq, fmt):
         assert np.array_equal(a * np.float32(4.0), b)
 
 
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_gemv_with_large_and_tiny_activations(wq, fmt):
+    """Slices holding some |x| >= 512 take the exact code path of the GEMV (beyond
+    fp16 too); values just below the switch, at the fp16 limit and in the fp16
+    subnormal range stay well within tolerance."""
+    K, N = 8192, 264
+    W = synth.weight(104, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    P = OQ.pack(fmt, W)
+    xf = OQ.bf16_bits_to_f32(synth.activation(104, K, 4)).copy()
+    xf[0, 17] = 3.0e5           # exact path, beyond fp16
+    xf[1, 2100] = -65280.0      # exact path, largest bf16 magnitude fp16 holds
+    xf[2, 3000] = 1.0e-6        # fp16 subnormal range (int8 offset path)
+    xf[2, 3001] = -3.0e-8
+    xf[3, 4100] = 510.0         # just below the switch: offset path
+    xf[3, 6000] = -500.0
+    x = OQ.bf16_rne_bits(xf.astype(np.float32))
+    y_ref = OL.ref_linear(x, P)
+    for split in _allowed_splits(fmt, K)[:3]:
+        assert_parity(_run_gemv(wq, g, x, split), y_ref, f"{fmt} large-x split={split}")
+
+
 def test_all_zero_rows_give_zero(wq):
-    K, N = 1024, 264
+    K, N = 4096, 264
     for fmt in OQ.FORMATS:
         W = synth.weight(97, K, N, synth.uses_outliers(fmt))
         W[10] = 0
@@ -238,7 +266,7 @@ def test_repeat_runs_are_bit_identical(wq):
     W = synth.weight(98, K, N)
     g, _ = quantize_on_gpu(wq, W, "w8pc")
     x = synth.activation(98, K, 4)
-    for split in (1, 8, 32):
+    for split in (1, 2, 4):
         first = _run_gemv(wq, g, x, split)
         for _ in range(3):
             assert np.array_equal(_run_gemv(wq, g, x, split), first)
@@ -267,7 +295,7 @@ def test_dispatch_boundary_m7_m8(wq):
 def test_no_writes_outside_y_and_workspace(wq):
     """Canary bytes around y and the workspace stay untouched (ragged N tile,
     split-K)."""
-    K, N, M = 1280, 1000, 3
+    K, N, M = 5120, 1000, 3
     W = synth.weight(100, K, N)
     g, _ = quantize_on_gpu(wq, W, "w8g128")
     x = to_dev_bf16(synth.activation(100, K, M))
@@ -279,7 +307,7 @@ def test_no_writes_outside_y_and_workspace(wq):
     wsbuf[:pad] = 0xAB
     wsbuf[pad + nws:] = 0xCD
     ws = wsbuf[pad:pad + nws]
-    for split in (1, 4, 8):
+    for split in (1, 2, 4):
         wq.wq_gemv(g, x, y, split_k=split, ws=ws)
     yg = torch.full((40 * N + 2 * pad,), 321, dtype=torch.int16, device=DEV)
     wq.wq_gemm(g, to_dev_bf16(synth.activation(100, K, 40)), yg[pad:pad + 40 * N].view(torch.bfloat16))
@@ -330,7 +358,9 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     y = torch.empty((1, N), dtype=torch.bfloat16, device=DEV)
     ws = wq.workspace(wq.wq_workspace_size(g, 1))
     chosen, lat = wq.wq_tune(copies, x, y, ws, warmup=5, iters=10)
-    assert chosen in SPLITS and all(v > 0 for v in lat)
+    smax = wq.wq_gemv_max_split("w8pc", K)
+    assert chosen in SPLITS and chosen <= smax
+    assert all((v > 0) == (s <= smax) for s, v in zip(SPLITS, lat)), lat
     v = wq.wq_tune_cache_get("w8pc", K, N, 1, 0)
     assert v & 0xFF == chosen and (v >> 8) in wq.WAVES_GRID
     p = str(tmp_path / "cache.txt")
@@ -343,7 +373,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
 
 
 def test_error_paths_on_device(wq):
-    K, N = 1024, 264
+    K, N = 9216, 264
     W = synth.weight(103, K, N)
     g, can = quantize_on_gpu(wq, W, "w8pc")
     x = to_dev_bf16(synth.activation(103, K, 2))
