@@ -51,11 +51,13 @@ int clamp_split(int v, int64_t units) {
 constexpr int kDefaultSplit = 1;
 constexpr int kDefaultTile = 1;
 
-// Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15 (0 = default).
-int gemv_value(int split, int waves) { return split | (waves << 8); }
+// Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15 and rows
+// per wave in bits 16..23 (0 = the default for the shape).
+int gemv_value(int split, int waves, int rows) { return split | (waves << 8) | (rows << 16); }
 bool valid_gemv_value(int v) {
-  const int split = v & 0xFF, waves = (v >> 8) & 0xFF;
-  return (v >> 16) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves;
+  const int split = v & 0xFF, waves = (v >> 8) & 0xFF, rows = (v >> 16) & 0xFF;
+  return (v >> 24) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves &&
+         (rows == 0 || rows == 4 || rows == 8 || rows == 16);
 }
 
 std::string resolve_tag(const char* tag) {
@@ -95,16 +97,18 @@ wq_status check_xy(const void* x, const void* y, int64_t M) {
   return WQ_OK;
 }
 
-// Tuned (split_k, waves) for this shape, or the defaults.
-void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves) {
+// Tuned (split_k, waves, rows) for this shape, or the defaults (0 = default).
+void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* rows) {
   int v = 0;
   if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) {
     *split = v & 0xFF;
     *waves = (v >> 8) & 0xFF;
+    *rows = (v >> 16) & 0xFF;
     return;
   }
   *split = clamp_split(kDefaultSplit, split_units(w));
   *waves = 0;
+  *rows = 0;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {
@@ -114,26 +118,31 @@ int resolve_tile(const wq_weight* w, int64_t M) {
 }
 
 wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
-                    void* ws, size_t ws_bytes, void* stream) {
+                    int rows, void* ws, size_t ws_bytes, void* stream) {
   wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves)
     return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default) or 1..16");
-  int split = split_k, wv = waves;
+  if (rows != 0 && rows != 4 && rows != 8 && rows != 16)
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 0 (default), 4, 8 or 16");
+  int split = split_k, wv = waves, rw = rows;
   if (split_k == 0) {
-    int tuned_waves = 0;
-    resolve_gemv(w, M, &split, &tuned_waves);
-    if (wv == 0) wv = tuned_waves;
+    int tw = 0, tr = 0;
+    resolve_gemv(w, M, &split, &tw, &tr);
+    if (wv == 0) wv = tw;
+    if (rw == 0) rw = tr;
     if (split > 1 && (!ws || ws_bytes < gemv_workspace_bytes(w->N, M, split))) {
-      split = 1;  // the tuned split needs more workspace than given: one slice
+      split = 1;  // the tuned split needs more workspace than given: one slice range
       wv = 0;
     }
   }
   if ((st = check_gemv_split(w, (int)M, split, ws, ws_bytes)) != WQ_OK) return st;
-  if (wv == 0) wv = gemv_default_waves(w->K, w->N, w->fmt, (int)M, split);
-  return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, wv, ws, (hipStream_t)stream);
+  if (rw == 0) rw = gemv_default_rows(w->K, w->N, w->fmt, (int)M);
+  if (wv == 0) wv = gemv_default_waves(w->K, w->N, w->fmt, (int)M, split, rw);
+  return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, wv, rw, ws,
+                     (hipStream_t)stream);
 }
 
 wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* stream) {
@@ -259,9 +268,10 @@ int wq_gemv_max_split(int fmt, int64_t K) {
   return clamp_split(kMaxSplit, gemv_slices(K, fmt));
 }
 
-int wq_gemv_max_waves(int fmt, int64_t M) {
+int wq_gemv_max_waves(int fmt, int64_t M, int rows) {
   if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G128 || M < 1 || M > kGemvMaxM) return -1;
-  return gemv_max_waves(fmt, (int)M);
+  const int cap = gemv_max_waves(fmt, (int)M, rows);
+  return cap > 0 ? cap : -1;
 }
 
 int wq_dispatch_kind(int64_t M) {
@@ -309,13 +319,13 @@ wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
 
 wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, void* ws,
                   size_t ws_bytes, void* stream) {
-  return gemv_impl(w, x, M, y, split_k, 0, ws, ws_bytes, stream);
+  return gemv_impl(w, x, M, y, split_k, 0, 0, ws, ws_bytes, stream);
 }
 
 wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
-                     void* ws, size_t ws_bytes, void* stream) {
+                     int rows, void* ws, size_t ws_bytes, void* stream) {
   if (split_k < 1) return fail(WQ_ERR_INVALID_ARG, "wq_gemv_ex: split_k must be given (>= 1)");
-  return gemv_impl(w, x, M, y, split_k, waves, ws, ws_bytes, stream);
+  return gemv_impl(w, x, M, y, split_k, waves, rows, ws, ws_bytes, stream);
 }
 
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
@@ -328,7 +338,7 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws, size_t ws_bytes,
                     void* stream) {
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
-  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, ws, ws_bytes, stream);
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream);
   return gemm_impl(w, x, M, y, 0, stream);
 }
 
@@ -356,18 +366,20 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   const bool gemv = wq_dispatch_kind(M) == WQ_KIND_GEMV;
   // GEMV candidates: every (split_k, waves) pair; GEMM candidates: the tiles
   struct Cand {
-    int split, waves, tile;
+    int split, waves, rows, tile;
   };
   std::vector<Cand> cand;
   if (gemv) {
-    const int cap = gemv_max_waves(copies[0].fmt, (int)M);
-    for (int s = 1; s <= kMaxSplit; s *= 2) {
-      const int dflt = gemv_default_waves(copies[0].K, copies[0].N, copies[0].fmt, (int)M, s);
-      for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, 0});
-      if (dflt & (dflt - 1)) cand.push_back({s, dflt, 0});  // the default when not a power of two
-    }
+    const int fmt = copies[0].fmt;
+    for (int s = 1; s <= kMaxSplit; s *= 2)
+      for (int rw = 4; rw <= 16; rw *= 2) {
+        const int cap = gemv_max_waves(fmt, (int)M, rw);
+        const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
+        for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, rw, 0});
+        if (dflt & (dflt - 1)) cand.push_back({s, dflt, rw, 0});  // the default when not a power of two
+      }
   } else {
-    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, t});
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, 0, t});
   }
   hipStream_t hs = (hipStream_t)stream;
   hipEvent_t e0, e1;
@@ -384,7 +396,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
     auto run = [&]() -> wq_status {
       const wq_weight* w = &copies[rot];
       rot = (rot + 1) % n_copies;
-      return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, ws, ws_bytes, stream)
+      return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, cand[c].rows, ws, ws_bytes, stream)
                   : gemm_impl(w, x, M, y, cand[c].tile, stream);
     };
     for (int i = 0; i < warmup; ++i)
@@ -418,7 +430,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
         }
       }
       st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M, WQ_KIND_GEMV,
-                             gemv_value(cand[best].split, cand[best].waves));
+                             gemv_value(cand[best].split, cand[best].waves, cand[best].rows));
     } else {
       *chosen = cand[best].tile;
       if (lat_us)

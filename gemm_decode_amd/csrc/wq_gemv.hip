@@ -4,14 +4,15 @@
 //   * K is cut into slices of 64 lanes x one 16-byte code chunk (1024 k for int8,
 //     2048 k for uint4).  A wave takes one slice at a time: every lane keeps its
 //     chunk of x (all M tokens) in registers and streams the same chunk of each
-//     of the 16 rows of the workgroup's row tile; the 16 row loads of a slice are
-//     issued together (16 x 1 KB contiguous per wave), so a wave keeps 16 KB in
-//     flight without software pipelining.
-//   * A workgroup owns one 16-row tile and one split-K range of slices; its W
-//     waves share the slices of that range round-robin.
-//   * Per lane the 16 x M partial sums are reduced across the wave by a butterfly
-//     reduce-scatter (after four exchange levels lane l holds row l & 15), the W
-//     waves' rows meet in LDS and are added in wave order.
+//     of the workgroup's rows; the row loads of a slice are issued together and,
+//     in the gfx950 tiled layout, form one contiguous block (RR x 1 KB per wave).
+//   * A workgroup owns RR rows (4, 8 or 16: a whole 16-row tile or a part of one)
+//     and one split-K range of slices; its W waves share the slices of that range
+//     round-robin.  Few rows per wave means thin waves (few registers, many waves
+//     resident to hide memory latency); many rows share each x chunk more widely.
+//   * Per lane the RR x M partial sums are reduced across the wave by a butterfly
+//     reduce-scatter (after log2(RR) exchange levels lane l holds row l % RR), the
+//     W waves' rows meet in LDS and are added in wave order.
 //   * split_k > 1 splits the slices across workgroups: each range writes fp32
 //     partials to the workspace and a second kernel adds them in range order
 //     (deterministic, and no cross-workgroup fence is needed).
@@ -93,8 +94,8 @@ __device__ __forceinline__ float xchg(float v) {
 // One reduce-scatter level over lanes differing in bit log2(J): values at
 // positions 2i and 2i+1 hold rows that differ in the corresponding row bit; the
 // lane keeps the one its lane bit selects and adds the partner's copy.
-template <int J, int NV, int M>
-__device__ __forceinline__ void rs_level(float (&v)[R][M], bool hi) {
+template <int J, int NV, int M, int RR>
+__device__ __forceinline__ void rs_level(float (&v)[RR][M], bool hi) {
 #pragma unroll
   for (int i = 0; i < NV / 2; ++i)
 #pragma unroll
@@ -123,35 +124,43 @@ struct Fmt<WQ_FMT_W4_G128> {
   static constexpr int kXWords = 16;
 };
 
-// grid = (row tiles, split_k); block = 64 * W threads, W <= MAXW.
-template <int FMT, int M, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restrict__ qw,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint8_t* __restrict__ zeros,
-                                                           const uint16_t* __restrict__ x,
-                                                           uint16_t* __restrict__ y,
-                                                           float* __restrict__ part, int K, int N) {
+// Registers a lane needs (estimate: codes, accumulators, x in two forms, addresses)
+// and the largest workgroup whose per-lane budget (512 / ceil(W/4) VGPRs) holds them.
+constexpr int lane_regs(int fmt, int RR, int M) { return 40 + 4 * RR + RR * M + 16 * M + (fmt != WQ_FMT_W8_PC ? 8 : 0); }
+constexpr int max_waves_r(int fmt, int RR, int M) {
+  return lane_regs(fmt, RR, M) <= 118 ? 16 : lane_regs(fmt, RR, M) <= 236 ? 8 : 4;
+}
+
+// grid = (16-row tiles x sub-tiles of RR rows, split_k); block = 64 * W threads.
+template <int FMT, int M, int RR>
+__global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
+    const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ part, int K, int N) {
   using F = Fmt<FMT>;
   constexpr int kSlice = 64 * F::kChunk;
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
-  __shared__ float red[MAXW][M * R];
+  constexpr int MAXW = max_waves_r(FMT, RR, M);
+  constexpr int NSUB = R / RR;
+  __shared__ float red[MAXW][M * RR];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
-  const int tile = blockIdx.x, n0 = tile * R;
+  const int tile = blockIdx.x / NSUB, sub = blockIdx.x % NSUB;
+  const int n0 = tile * R + sub * RR;
+  if (n0 >= N) return;  // the whole workgroup leaves together
   const int s = blockIdx.y, S = gridDim.y;
   const int T = (K + kSlice - 1) / kSlice;
   const int sl0 = (int)(((int64_t)s * T) / S), sl1 = (int)(((int64_t)(s + 1) * T) / S);
   const int G = K / kGroup;
   const size_t row_bytes = kW4 ? (size_t)K / 2 : (size_t)K;
-
   // tile base in the gfx950 code layout and its row count (the last tile may be short)
   const uint8_t* tile_base = qw + (size_t)tile * R * row_bytes;
-  const int nr = min(R, N - n0);
+  const int nr = min(R, N - tile * R);
 
-  float acc[R][M];
+  float acc[RR][M];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
   float xs_total[M];  // W8: sum of x over this lane's chunks (offset removal)
@@ -163,13 +172,13 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
     const bool valid = k < K;           // the last slice may be ragged
     const int kk = valid ? k : 0;
 
-    // ---- loads: 16 row chunks (one contiguous block per slice), x chunk, metadata
+    // ---- loads: RR row chunks (one contiguous block per slice), x chunk, metadata
     const int wsl = (int)min((size_t)kSliceBytes, row_bytes - (size_t)sl * kSliceBytes);  // bytes per row
     const uint8_t* sbase = tile_base + (size_t)nr * kSliceBytes * sl + (valid ? lane * 16 : 0);
-    uint4 cw[R];
+    uint4 cw[RR];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(r, nr - 1) * wsl);
+    for (int r = 0; r < RR; ++r)
+      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(sub * RR + r, nr - 1) * wsl);
     uint32_t xb[M][F::kXWords];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -184,15 +193,39 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
       }
     }
     const int g = kk / kGroup;
-    uint4 sv0 = make_uint4(0, 0, 0, 0), sv1 = make_uint4(0, 0, 0, 0);
-    uint2 zv = make_uint2(0, 0);
+    uint32_t sw[RR / 2];  // RR 16-bit scales of this sub-tile's rows for group g
+    uint32_t zw = 0;      // RR 4-bit zero-points
     if constexpr (FMT != WQ_FMT_W8_PC) {
-      const uint4* sp = reinterpret_cast<const uint4*>(scales + ((size_t)tile * G + g) * R);
-      sv0 = sp[0];
-      sv1 = sp[1];
+      const uint16_t* sp = scales + ((size_t)tile * G + g) * R + sub * RR;
+      if constexpr (RR == 16) {
+        const uint4 a = reinterpret_cast<const uint4*>(sp)[0], b = reinterpret_cast<const uint4*>(sp)[1];
+        sw[0] = a.x; sw[1] = a.y; sw[2] = a.z; sw[3] = a.w; sw[4] = b.x; sw[5] = b.y; sw[6] = b.z; sw[7] = b.w;
+      } else if constexpr (RR == 8) {
+        const uint4 a = reinterpret_cast<const uint4*>(sp)[0];
+        sw[0] = a.x; sw[1] = a.y; sw[2] = a.z; sw[3] = a.w;
+      } else {
+        const uint2 a = reinterpret_cast<const uint2*>(sp)[0];
+        sw[0] = a.x; sw[1] = a.y;
+      }
     }
-    if constexpr (kW4) zv = *reinterpret_cast<const uint2*>(zeros + ((size_t)tile * G + g) * (R / 2));
-    const uint32_t sw[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
+    uint32_t zw_hi = 0;
+    if constexpr (kW4) {
+      const uint8_t* zp = zeros + ((size_t)tile * G + g) * (R / 2) + sub * (RR / 2);
+      if constexpr (RR == 16) {
+        const uint2 a = *reinterpret_cast<const uint2*>(zp);
+        zw = a.x;
+        zw_hi = a.y;
+      } else if constexpr (RR == 8) {
+        zw = *reinterpret_cast<const uint32_t*>(zp);
+      } else {
+        zw = *reinterpret_cast<const uint16_t*>(zp);
+      }
+    }
+    auto scale_of = [&](int r) -> uint16_t {
+      const uint32_t word = sw[r >> 1];
+      return (uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu));
+    };
+    auto zero_of = [&](int r) -> uint32_t { return ((r < 8 ? zw : zw_hi) >> (4 * (r & 7))) & 0xFu; };
 
     // any |x| >= 512 in this slice?  (a bf16 exponent field >= 136 carries into bit
     // 15 of its half when 0x3C00 is added)
@@ -219,7 +252,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
           xs[m] = t;
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RR; ++r) {
           const uint32_t d[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
           uint32_t hp[8];
 #pragma unroll
@@ -233,8 +266,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
 #pragma unroll
               for (int i = 0; i < 8; ++i) acc[r][m] = dot2_f16(hp[i], xh[m][i], acc[r][m]);
           } else {
-            const uint32_t word = sw[r >> 1];
-            const float sc = bf16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
+            const float sc = bf16_to_f32(scale_of(r));
 #pragma unroll
             for (int m = 0; m < M; ++m) {
               float t = 0.f;
@@ -251,7 +283,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
       } else {
         // exact bf16 path: signed code -> fp32 -> bf16 pairs
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RR; ++r) {
           const uint32_t d[4] = {cw[r].x ^ 0x80808080u, cw[r].y ^ 0x80808080u, cw[r].z ^ 0x80808080u,
                                  cw[r].w ^ 0x80808080u};
           uint32_t bp[8];
@@ -260,11 +292,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
             bp[2 * j] = pack_bf16x2((float)(int8_t)(d[j] & 0xFFu), (float)(int8_t)((d[j] >> 8) & 0xFFu));
             bp[2 * j + 1] = pack_bf16x2((float)(int8_t)((d[j] >> 16) & 0xFFu), (float)(int8_t)(d[j] >> 24));
           }
-          float sc = 1.f;
-          if constexpr (FMT == WQ_FMT_W8_G128) {
-            const uint32_t word = sw[r >> 1];
-            sc = bf16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
-          }
+          const float sc = (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(scale_of(r)) : 1.f;
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             float t = 0.f;
@@ -285,11 +313,9 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
         xs[m] = t;
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t word = sw[r >> 1];
-        const float sc = f16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
-        const uint32_t zsrc = r < 8 ? zv.x : zv.y;
-        const float off = 128.f + (float)((zsrc >> (4 * (r & 7))) & 0xFu);
+      for (int r = 0; r < RR; ++r) {
+        const float sc = f16_to_f32(scale_of(r));
+        const float off = 128.f + (float)zero_of(r);
         const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
         float t[M];
 #pragma unroll
@@ -308,11 +334,9 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
     } else {
       // ---- uint4 group-128, exact path: bf16(q - z) pairs
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t word = sw[r >> 1];
-        const float sc = f16_to_f32((uint16_t)((r & 1) ? (word >> 16) : (word & 0xFFFFu)));
-        const uint32_t zsrc = r < 8 ? zv.x : zv.y;
-        const float z = (float)((zsrc >> (4 * (r & 7))) & 0xFu);
+      for (int r = 0; r < RR; ++r) {
+        const float sc = f16_to_f32(scale_of(r));
+        const float z = (float)zero_of(r);
         const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
         float t[M];
 #pragma unroll
@@ -333,42 +357,44 @@ __global__ __launch_bounds__(64 * MAXW) void gemv_kernel(const uint8_t* __restri
   }
   if constexpr (FMT == WQ_FMT_W8_PC) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RR; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[r][m] = fmaf(-1152.f, xs_total[m], acc[r][m]);
   }
 
-  // ---- wave reduce-scatter: afterwards lane l holds row (l & 15), all M tokens
-  rs_level<1, 16, M>(acc, lane & 1);
-  rs_level<2, 8, M>(acc, lane & 2);
-  rs_level<4, 4, M>(acc, lane & 4);
-  rs_level<8, 2, M>(acc, lane & 8);
+  // ---- wave reduce-scatter: afterwards lane l holds row (l % RR), all M tokens
+  rs_level<1, RR, M>(acc, lane & 1);
+  if constexpr (RR >= 4) rs_level<2, RR / 2, M>(acc, lane & 2);
+  if constexpr (RR >= 8) rs_level<4, RR / 4, M>(acc, lane & 4);
+  if constexpr (RR >= 16) rs_level<8, RR / 8, M>(acc, lane & 8);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
+    if constexpr (RR <= 4) acc[0][m] += xchg<4>(acc[0][m]);
+    if constexpr (RR <= 8) acc[0][m] += xchg<8>(acc[0][m]);
     acc[0][m] += xchg<16>(acc[0][m]);
     acc[0][m] += xchg<32>(acc[0][m]);
   }
 
-  const int row = lane & 15, n = n0 + row;
+  const int row = lane % RR, n = n0 + row;
   float v[M];
   if (W == 1) {
 #pragma unroll
     for (int m = 0; m < M; ++m) v[m] = acc[0][m];
   } else {
-    if (lane < R) {
+    if (lane < RR) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) red[wave][m * R + row] = acc[0][m];
+      for (int m = 0; m < M; ++m) red[wave][m * RR + row] = acc[0][m];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float a = 0.f;
-      for (int w = 0; w < W; ++w) a += red[w][m * R + row];
+      for (int w = 0; w < W; ++w) a += red[w][m * RR + row];
       v[m] = a;
     }
   }
-  if (lane < R && n < N) {
+  if (lane < RR && n < N) {
     if (S == 1) {
       const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
 #pragma unroll
@@ -396,46 +422,41 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   y[i] = f32_to_bf16(sc * v);
 }
 
-// Largest waves per workgroup whose register budget (512 / ceil(W/4) VGPRs per
-// lane) holds this format and M without spilling.
-constexpr int max_waves(int fmt, int M) {
-  return fmt == WQ_FMT_W8_PC ? (M <= 1 ? 16 : M <= 4 ? 8 : 4) : fmt == WQ_FMT_W8_G128 ? (M <= 4 ? 8 : 4) : (M <= 3 ? 8 : 4);
+template <int FMT, int M>
+wq_status launch_m(int rows, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
+                   const uint8_t* zs, const uint16_t* x, uint16_t* y, float* part, int K, int N,
+                   hipStream_t st) {
+  switch (rows) {
+    case 4: gemv_kernel<FMT, M, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    case 8: gemv_kernel<FMT, M, 8><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    case 16: gemv_kernel<FMT, M, 16><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
+  }
+  return WQ_OK;
 }
 
 template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                     int waves, void* ws, hipStream_t st) {
+                     int waves, int rows, void* ws, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
-  const int tiles = (N + R - 1) / R;
-  dim3 grid(tiles, split_k);
+  dim3 grid((unsigned)(row_tiles(N) * (R / rows)), split_k);
   dim3 block(64 * waves);
   float* part = (float*)ws;
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
-#define WQ_GEMV_CASE(MM)                                                                     \
-  case MM:                                                                                   \
-    if (waves <= 4)                                                                          \
-      gemv_kernel<FMT, MM, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);        \
-    else if constexpr (max_waves(FMT, MM) >= 8) {                                            \
-      if (waves <= 8)                                                                        \
-        gemv_kernel<FMT, MM, 8><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);      \
-      else if constexpr (max_waves(FMT, MM) >= 16)                                           \
-        gemv_kernel<FMT, MM, 16><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);     \
-    }                                                                                        \
-    break;
+  wq_status r = WQ_OK;
   switch (M) {
-    WQ_GEMV_CASE(1)
-    WQ_GEMV_CASE(2)
-    WQ_GEMV_CASE(3)
-    WQ_GEMV_CASE(4)
-    WQ_GEMV_CASE(5)
-    WQ_GEMV_CASE(6)
-    WQ_GEMV_CASE(7)
-    default:
-      return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
+    case 1: r = launch_m<FMT, 1>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 2: r = launch_m<FMT, 2>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 3: r = launch_m<FMT, 3>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 4: r = launch_m<FMT, 4>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 5: r = launch_m<FMT, 5>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 6: r = launch_m<FMT, 6>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 7: r = launch_m<FMT, 7>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   }
-#undef WQ_GEMV_CASE
+  if (r != WQ_OK) return r;
   WQ_HIP_CHECK(hipGetLastError());
   if (split_k > 1) {
     const int64_t MN = (int64_t)M * N;
@@ -452,31 +473,45 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
   return (size_t)split_k * (size_t)M * (size_t)N * sizeof(float);
 }
 
-int gemv_max_waves(int fmt, int M) { return max_waves(fmt, M); }
+int gemv_max_waves(int fmt, int M, int rows) {
+  if (rows != 4 && rows != 8 && rows != 16) return 0;
+  return max_waves_r(fmt, rows, M);
+}
 
 int64_t gemv_slices(int64_t K, int fmt) {
   const int64_t slice = 64 * (fmt == WQ_FMT_W4_G128 ? 32 : 16);
   return (K + slice - 1) / slice;
 }
 
-int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k) {
-  // one slice per wave: the waves of a workgroup cover its range of K slices
-  // (capped by the register budget; the waves then take several slices each)
+int gemv_default_rows(int64_t K, int64_t N, int fmt, int M) {
+  // thin waves (4 rows) keep many waves resident when the matrix is small; more
+  // rows per wave share each x chunk (and its conversion) among more rows, which
+  // pays when there are many row tiles or several tokens (measured on MI355X)
+  (void)K;
+  if (M >= 4) return N >= 16384 ? 16 : 8;
+  if (fmt == WQ_FMT_W4_G128) return 8;
+  return N >= 16384 ? 8 : 4;
+}
+
+int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int rows) {
+  // one K slice per wave, as many waves as the register budget allows
   const int64_t per_split = (gemv_slices(K, fmt) + split_k - 1) / split_k;
   (void)N;
-  const int cap = max_waves(fmt, M);
+  const int cap = gemv_max_waves(fmt, M, rows);
   return (int)(per_split < cap ? (per_split < 1 ? 1 : per_split) : cap);
 }
 
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                      int waves, void* ws, hipStream_t s) {
-  if (waves < 1 || waves > gemv_max_waves(w->fmt, M))
-    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: at this M a workgroup holds 1.." +
-                                        std::to_string(gemv_max_waves(w->fmt, M)) + " waves");
+                      int waves, int rows, void* ws, hipStream_t s) {
+  const int cap = gemv_max_waves(w->fmt, M, rows);
+  if (cap == 0) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
+  if (waves < 1 || waves > cap)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: at this M and rows a workgroup holds 1.." +
+                                        std::to_string(cap) + " waves");
   switch (w->fmt) {
-    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, ws, s);
-    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, ws, s);
-    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, ws, s);
+    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, s);
+    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, s);
+    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, s);
   }
   return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: unknown format");
 }

@@ -52,11 +52,13 @@ __host__ __device__ inline size_t tiled_offset(int64_t n, int64_t b, int64_t N, 
 wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s);
 wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s);
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                      int waves, void* ws, hipStream_t s);
-// Waves per GEMV workgroup when none is tuned or given.
-int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k);
-// Largest waves per GEMV workgroup that fits the registers at this format and M.
-int gemv_max_waves(int fmt, int M);
+                      int waves, int rows, void* ws, hipStream_t s);
+// Rows per GEMV wave (4, 8 or 16) and waves per workgroup when none is tuned or given.
+int gemv_default_rows(int64_t K, int64_t N, int fmt, int M);
+int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int rows);
+// Largest waves per GEMV workgroup that fits the registers at this format, M and
+// rows per wave (0 for rows other than 4, 8, 16).
+int gemv_max_waves(int fmt, int M, int rows);
 // K slices of the GEMV (64 lanes x one 16-byte chunk: 1024 k int8, 2048 k uint4);
 // split-K ranges are whole slices.
 int64_t gemv_slices(int64_t K, int fmt);

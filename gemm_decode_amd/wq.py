@@ -37,11 +37,12 @@ KIND_GEMV, KIND_GEMM = 0, 1
 GEMM_TILES = 2
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
+ROWS_GRID = (4, 8, 16)
 
 
-def gemv_cache_value(split_k: int, waves: int = 0) -> int:
-    """Tuner-cache encoding of a GEMV choice (split_k | waves << 8)."""
-    return split_k | (waves << 8)
+def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:
+    """Tuner-cache encoding of a GEMV choice (split_k | waves << 8 | rows << 16)."""
+    return split_k | (waves << 8) | (rows << 16)
 
 
 class WqWeightC(C.Structure):
@@ -57,14 +58,14 @@ _SIGS = {
     "wq_last_error": (C.c_char_p, []),
     "wq_packed_sizes": (C.c_int, [C.c_int, C.c_int, C.c_int64, C.c_int64, _P(C.c_size_t), _P(C.c_size_t), _P(C.c_size_t)]),
     "wq_dispatch_kind": (C.c_int, [C.c_int64]),
-    "wq_gemv_max_waves": (C.c_int, [C.c_int, C.c_int64]),
+    "wq_gemv_max_waves": (C.c_int, [C.c_int, C.c_int64, C.c_int]),
     "wq_gemv_max_split": (C.c_int, [C.c_int, C.c_int64]),
     "wq_pack": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
     "wq_repack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_unrepack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
     "wq_gemv": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
-    "wq_gemv_ex": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_gemv_ex": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_tune_pick": (C.c_int, [_P(C.c_double), C.c_int]),
@@ -126,8 +127,8 @@ def wq_dispatch_kind(M: int) -> int:
     return lib.wq_dispatch_kind(M)
 
 
-def wq_gemv_max_waves(fmt, M: int) -> int:
-    return lib.wq_gemv_max_waves(_fmt(fmt), M)
+def wq_gemv_max_waves(fmt, M: int, rows: int = 16) -> int:
+    return lib.wq_gemv_max_waves(_fmt(fmt), M, rows)
 
 
 def wq_gemv_max_split(fmt, K: int) -> int:
@@ -223,9 +224,9 @@ def wq_gemv(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int = 0,
 
 
 def wq_gemv_ex(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int, waves: int = 0,
-               ws: torch.Tensor | None = None, stream=None) -> None:
+               rows: int = 0, ws: torch.Tensor | None = None, stream=None) -> None:
     M, d = _xy(x, y, w), w.desc()
-    _check(lib.wq_gemv_ex(C.byref(d), _ptr(x), M, _ptr(y), split_k, waves, _ptr(ws),
+    _check(lib.wq_gemv_ex(C.byref(d), _ptr(x), M, _ptr(y), split_k, waves, rows, _ptr(ws),
                           0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv_ex")
 
 

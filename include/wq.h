@@ -180,17 +180,18 @@ wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int spl
  * of two <= min(32, number of slices).  -1 for an invalid format or K. */
 int wq_gemv_max_split(int fmt, int64_t K);
 
-/* Largest waves per GEMV workgroup for a format and 1 <= M <= 7 (host only): the
- * register budget per lane shrinks as a workgroup grows, so larger M allow fewer
- * waves.  Returns -1 for an unknown format or M outside 1..7. */
-int wq_gemv_max_waves(int fmt, int64_t M);
+/* Largest waves per GEMV workgroup for a format, 1 <= M <= 7 and rows per wave (4, 8
+ * or 16) (host only): the register budget per lane shrinks as a workgroup grows, so
+ * larger M and more rows allow fewer waves.  -1 for an invalid argument. */
+int wq_gemv_max_waves(int fmt, int64_t M, int rows);
 
-/* wq_gemv with both levels explicit: split_k >= 1 as above and waves per workgroup
- * 0 (the default for the shape: one K slice per wave, as many as the registers
- * allow) or 1..wq_gemv_max_waves(fmt, M) (else WQ_ERR_UNSUPPORTED).  For tests and
+/* wq_gemv with the work decomposition explicit: split_k >= 1 as above; rows: output
+ * rows per wave, 4, 8 or 16 (0 = the default for the shape); waves per workgroup: 0
+ * (the default: one K slice per wave, as many as the registers allow) or
+ * 1..wq_gemv_max_waves(fmt, M, rows) (else WQ_ERR_UNSUPPORTED).  For tests and
  * tuning. */
 wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
-                     void* ws, size_t ws_bytes, void* stream);
+                     int rows, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill GEMM, M >= 1 (used by wq_linear for M >= 8; smaller M are accepted so
  * the two paths can be compared): codes are converted to exact bf16 values in LDS
@@ -224,7 +225,7 @@ int wq_tune_pick(const double* lat, int n);
  * weights (distinct buffers with the same format and shape) so that the weights
  * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k
  * (GEMV) or tile (GEMM) to *chosen (host) and, if lat_us is not NULL, the mean
- * microseconds per call of each split_k (its best waves) or tile into lat_us[0..5]
+ * microseconds per call of each split_k (its best rows and waves) or tile into lat_us[0..5]
  * (host; -1 for candidates that could not run).  Synchronizes the stream. */
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
@@ -232,8 +233,9 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
 
 /* Tuner cache: entries keyed by (device tag, format, K, N, M, kind), where the
  * device tag is "<gcnArchName>:<compute units>" of the device the entry was tuned
- * on ("" in set/get = the current device).  A GEMV value is split_k | (waves << 8)
- * (waves 0 = the default for the shape); a GEMM value is a tile id.  get returns WQ_OK and the value, or
+ * on ("" in set/get = the current device).  A GEMV value is split_k | (waves << 8) |
+ * (rows << 16) (waves or rows 0 = the default for the shape); a GEMM value is a
+ * tile id.  get returns WQ_OK and the value, or
  * WQ_ERR_INVALID_ARG when absent.  save/load use a plain text file, one entry per
  * line; load merges into the cache and fails with WQ_ERR_CACHE_IO (leaving the
  * cache unchanged) on a missing or malformed file. */

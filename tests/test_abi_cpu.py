@@ -70,10 +70,12 @@ def test_gemv_max_split(wqlib):
 
 def test_gemv_max_waves(wqlib):
     for fmt in ("w8pc", "w8g128", "w4g128"):
-        caps = [wqlib.wq_gemv_max_waves(fmt, m) for m in range(1, 8)]
-        assert caps[0] in (8, 16) and all(c in (4, 8, 16) for c in caps) and caps == sorted(caps, reverse=True)
-    assert wqlib.wq_gemv_max_waves("w8pc", 0) == -1 and wqlib.wq_gemv_max_waves("w8pc", 8) == -1
-    assert wqlib.wq_gemv_max_waves(9, 1) == -1
+        for rows in (4, 8, 16):
+            caps = [wqlib.wq_gemv_max_waves(fmt, m, rows) for m in range(1, 8)]
+            assert all(c in (4, 8, 16) for c in caps) and caps == sorted(caps, reverse=True)
+        assert wqlib.wq_gemv_max_waves(fmt, 1, 4) == 16
+    assert wqlib.wq_gemv_max_waves("w8pc", 0, 4) == -1 and wqlib.wq_gemv_max_waves("w8pc", 8, 4) == -1
+    assert wqlib.wq_gemv_max_waves(9, 1, 4) == -1 and wqlib.wq_gemv_max_waves("w8pc", 1, 5) == -1
 
 
 def test_dispatch_threshold(wqlib):
@@ -92,12 +94,14 @@ def test_tuner_cache_roundtrip_and_corrupt_file(wqlib, tmp_path):
     tag = "gfx950:256"
     wqlib.wq_tune_cache_clear()
     assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) is None
-    wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 8), tag)
+    wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 8, 16), tag)
     wqlib.wq_tune_cache_set("w4g128", 13824, 5120, 1, 0, 16, tag)
     with pytest.raises(wqlib.WqError):
         wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(3, 4), tag)
     with pytest.raises(wqlib.WqError):
         wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 17), tag)
+    with pytest.raises(wqlib.WqError):
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(4, 2, 6), tag)
     wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 2048, 1, 2, tag)
     with pytest.raises(wqlib.WqError):
         wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, 3, tag)    # not a power of two
@@ -108,7 +112,7 @@ def test_tuner_cache_roundtrip_and_corrupt_file(wqlib, tmp_path):
     wqlib.wq_tune_cache_clear()
     assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) is None
     wqlib.wq_tune_cache_load(p)
-    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) == 4 | (8 << 8)
+    assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, tag) == 4 | (8 << 8) | (16 << 16)
     assert wqlib.wq_tune_cache_get("w4g128", 13824, 5120, 1, 0, tag) == 16
     assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 2048, 1, tag) == 2
     assert wqlib.wq_tune_cache_get("w8pc", 5120, 27648, 1, 0, "gfx942:304") is None
@@ -145,8 +149,9 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(dk), x, 1, y, 4, None, 0, None) == 4           # no workspace
     assert L.wq_gemv(C.byref(dk), x, 1, y, 4, C.c_void_p(0x30000), 16, None) == 4   # too small
     assert L.wq_gemv(C.byref(dk), x, 1, y, 4, C.c_void_p(0x30004), 1 << 20, None) == 3  # ws misaligned
-    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 17, None, 0, None) == 1     # waves > 16
-    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, None, 0, None) == 1      # split must be given
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 17, 0, None, 0, None) == 1  # waves > 16
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 5, None, 0, None) == 1   # rows not 4/8/16
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, 0, None, 0, None) == 1   # split must be given
     dc = _desc(wqlib, layout=0)
     assert L.wq_gemv(C.byref(dc), x, 1, y, 1, None, 0, None) == 2           # canonical layout
     dq = _desc(wqlib, q=0x1004)

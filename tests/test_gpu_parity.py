@@ -139,11 +139,13 @@ def test_gemv_every_split_and_waves(wq, fmt, K, N):
         x = to_dev_bf16(xb)
         ws = wq.workspace(wq.wq_workspace_size(g, M))
         for split in _allowed_splits(fmt, K):
-            for waves in range(1, wq.wq_gemv_max_waves(fmt, M) + 1):
-                y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-                wq.wq_gemv_ex(g, x, y, split, waves, ws=ws)
-                torch.cuda.synchronize()
-                assert_parity(bf16_bits(y), y_ref, f"gemv {fmt} M={M} split={split} waves={waves}")
+            for rows in wq.ROWS_GRID:
+                cap = wq.wq_gemv_max_waves(fmt, M, rows)
+                for waves in sorted(set(v for v in (1, 2, 3, 5, cap) if v <= cap)):
+                    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+                    wq.wq_gemv_ex(g, x, y, split, waves, rows, ws=ws)
+                    torch.cuda.synchronize()
+                    assert_parity(bf16_bits(y), y_ref, f"gemv {fmt} M={M} split={split} rows={rows} waves={waves}")
 
 
 @pytest.mark.parametrize("fmt,K,N", SMALL)
@@ -187,12 +189,13 @@ def test_one_hot_is_exact(wq, fmt):
         assert np.array_equal(_run_gemv(wq, g, x, split), want), f"gemv split={split}"
     xd = to_dev_bf16(x)
     ws = wq.workspace(wq.wq_workspace_size(g, len(ks)))
-    for waves in range(1, wq.wq_gemv_max_waves(fmt, len(ks)) + 1):
-        for split in (1, 2):
-            y = torch.empty((len(ks), N), dtype=torch.bfloat16, device=DEV)
-            wq.wq_gemv_ex(g, xd, y, split, waves, ws=ws)
-            torch.cuda.synchronize()
-            assert np.array_equal(bf16_bits(y), want), f"gemv split={split} waves={waves}"
+    for rows in wq.ROWS_GRID:
+        for waves in range(1, wq.wq_gemv_max_waves(fmt, len(ks), rows) + 1):
+            for split in (1, 2):
+                y = torch.empty((len(ks), N), dtype=torch.bfloat16, device=DEV)
+                wq.wq_gemv_ex(g, xd, y, split, waves, rows, ws=ws)
+                torch.cuda.synchronize()
+                assert np.array_equal(bf16_bits(y), want), f"gemv split={split} rows={rows} waves={waves}"
     for tile in range(1, wq.GEMM_TILES + 1):
         assert np.array_equal(_run_gemm(wq, g, x, tile), want), f"gemm tile={tile}"
 
@@ -362,7 +365,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert chosen in SPLITS and chosen <= smax
     assert all((v > 0) == (s <= smax) for s, v in zip(SPLITS, lat)), lat
     v = wq.wq_tune_cache_get("w8pc", K, N, 1, 0)
-    assert v & 0xFF == chosen and (v >> 8) in wq.WAVES_GRID
+    assert v & 0xFF == chosen and 1 <= (v >> 8) & 0xFF <= 16 and (v >> 16) in wq.ROWS_GRID
     p = str(tmp_path / "cache.txt")
     wq.wq_tune_cache_save(p)
     assert f" 0 {K} {N} 1 0 {v}" in open(p).read()
