@@ -206,17 +206,218 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Large-M kernel: 4 waves (2 x 2).  Per-channel W8: 256 x 256 workgroup tile, each wave
+// 128 x 128 = a 4 x 4 grid of 32 x 32 MFMA blocks (256 fp32 accumulators per lane).
+// Wave tiles this large halve the LDS operand traffic per MFMA compared with 64 x 64
+// tiles, which would otherwise keep LDS as busy as the matrix cores.  Group-128
+// formats keep a second accumulator for the current group (its fp32 partial is
+// scaled by s[n][g] and added at the end of the group), so their wave tile is
+// 128 x 64 (256 x 128 per workgroup).  Two LDS stages (x tile and exact-bf16 weight
+// tile): while the MFMAs read one, the next K step is loaded from memory, converted
+// and written into the other; one barrier per step.
+//
+// Workgroups are numbered so that XCD x (workgroup ids x, x + 8, ...) runs a
+// contiguous range of column blocks, each for every row block in turn: a weight
+// strip is fetched into that XCD's L2 once and reused by all row blocks.
+constexpr int BM2 = 256, BK2 = 64;
+constexpr int P2 = BK2 + 8;                  // LDS row pitch in bf16 (16-byte pad)
+
+template <int FMT>
+struct Big {
+  static constexpr bool kGrouped = FMT != WQ_FMT_W8_PC;
+  static constexpr int JN = kGrouped ? 2 : 4;  // 32-wide column blocks per wave
+  static constexpr int BN = 64 * JN;           // columns per workgroup
+  static constexpr int STAGE = (BM2 + BN) * P2;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const uint8_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros,
+                                                           const uint16_t* __restrict__ x,
+                                                           uint16_t* __restrict__ y, int M, int K, int N) {
+  using B_ = Big<FMT>;
+  constexpr int JN = B_::JN, BN2 = B_::BN, STAGE2 = B_::STAGE;
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  constexpr bool kGrouped = B_::kGrouped;
+  constexpr int TPR = 256 / BN2;                 // threads staging one weight row
+  constexpr int WCH = (kW4 ? 2 : 4) / TPR;      // 16-byte code chunks per thread and K step
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE2];
+
+  // ---- XCD-aware tile order
+  const int mblocks = (M + BM2 - 1) / BM2, nblocks = (N + BN2 - 1) / BN2;
+  const int total = mblocks * nblocks;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int nb = lin / mblocks, mb = lin % mblocks;
+  const int n0 = nb * BN2, m0 = mb * BM2;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int G = K / kGroup;
+  const int64_t row_bytes = kW4 ? K / 2 : K;
+  const int brow = tid / TPR, bpart = tid % TPR;  // weight row and part this thread stages
+  const int nrow = min(n0 + brow, N - 1);
+
+  uint4 xr[8], wr[WCH];
+  auto load_global = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j, row = c >> 3, col = (c & 7) * 8;
+      const int m = m0 + row, k = k0 + col;
+      xr[j] = (m < M && k < K) ? *reinterpret_cast<const uint4*>(x + (size_t)m * K + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < WCH; ++j) {
+      const int b = (kW4 ? k0 / 2 : k0) + 16 * (bpart * WCH + j);  // byte of the packed row
+      wr[j] = b < row_bytes ? *reinterpret_cast<const uint4*>(qw + tiled_offset(nrow, b, N, row_bytes))
+                            : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_lds = [&](int st, int k0) {
+    uint16_t* A = lds + st * STAGE2;
+    uint16_t* Bt = A + BM2 * P2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j, row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<uint4*>(&A[row * P2 + col]) = xr[j];
+    }
+    uint16_t* Brow = Bt + brow * P2;
+    if constexpr (!kW4) {
+#pragma unroll
+      for (int j = 0; j < WCH; ++j) {
+        const int kc = 16 * (bpart * WCH + j);
+        *reinterpret_cast<uint4*>(&Brow[kc]) = i8x16_to_bf16_lo(wr[j]);
+        *reinterpret_cast<uint4*>(&Brow[kc + 8]) = i8x16_to_bf16_hi(wr[j]);
+      }
+    } else {
+      const int g = k0 / kGroup;
+      const uint8_t zb = zeros[(((size_t)(nrow / kGemvTileRows) * G + g) * kGemvTileRows + nrow % kGemvTileRows) / 2];
+      const float z = (float)((zb >> ((nrow & 1) * 4)) & 0xFu);
+#pragma unroll
+      for (int j = 0; j < WCH; ++j) {
+        const int kc = 32 * (bpart * WCH + j);
+        *reinterpret_cast<uint4*>(&Brow[kc + 0]) = w4_word_to_bf16(wr[j].x, z);
+        *reinterpret_cast<uint4*>(&Brow[kc + 8]) = w4_word_to_bf16(wr[j].y, z);
+        *reinterpret_cast<uint4*>(&Brow[kc + 16]) = w4_word_to_bf16(wr[j].z, z);
+        *reinterpret_cast<uint4*>(&Brow[kc + 24]) = w4_word_to_bf16(wr[j].w, z);
+      }
+    }
+  };
+
+  int ncol[JN];
+#pragma unroll
+  for (int j = 0; j < JN; ++j) ncol[j] = min(n0 + wn * (32 * JN) + j * 32 + l32, N - 1);
+  auto gscale = [&](int n, int g) -> float {
+    const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
+    return (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
+  };
+
+  floatx16 acc[4][JN], tmp[4][JN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[i][j][a] = tmp[i][j][a] = 0.f;
+
+  const int KS = (K + BK2 - 1) / BK2;
+  load_global(0);
+  store_lds(0, 0);
+  __syncthreads();
+  for (int ks = 0; ks < KS; ++ks) {
+    const int k0 = ks * BK2;
+    if (ks + 1 < KS) load_global(k0 + BK2);
+    const uint16_t* A = lds + (ks & 1) * STAGE2;
+    const uint16_t* Bt = A + BM2 * P2;
+#pragma unroll
+    for (int kk = 0; kk < BK2; kk += 16) {
+      bf16x8_t af[4], bfr[JN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&A[(wm * 128 + i * 32 + l32) * P2 + kk + 8 * lh]);
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bt[(wn * (32 * JN) + j * 32 + l32) * P2 + kk + 8 * lh]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+          if constexpr (kGrouped)
+            tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], tmp[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    if constexpr (kGrouped) {
+      if ((k0 + BK2) % kGroup == 0) {
+        const int g = k0 / kGroup;
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+          const float sc = gscale(ncol[j], g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+              acc[i][j][a] = fmaf(sc, tmp[i][j][a], acc[i][j][a]);
+              tmp[i][j][a] = 0.f;
+            }
+        }
+      }
+    }
+    if (ks + 1 < KS) store_lds((ks + 1) & 1, k0 + BK2);
+    __syncthreads();
+  }
+
+  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block
+#pragma unroll
+  for (int j = 0; j < JN; ++j) {
+    const int n = n0 + wn * (32 * JN) + j * 32 + l32;
+    const float sc = kGrouped ? 1.f : bf16_to_f32(scales[ncol[j]]);
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+      }
+  }
+}
+
 }  // namespace
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       hipStream_t s) {
-  (void)tile;
   const int K = (int)w->K, N = (int)w->N;
   if (M > 65535LL * BM) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: M too large");
-  dim3 grid((N + BN - 1) / BN, (unsigned)((M + BM - 1) / BM));
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
+  if (tile == 1) {
+    const int bn = w->fmt == WQ_FMT_W8_PC ? Big<WQ_FMT_W8_PC>::BN : Big<WQ_FMT_W8_G128>::BN;
+    const int64_t total = ((M + BM2 - 1) / BM2) * ((N + bn - 1) / bn);
+    const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
+    switch (w->fmt) {
+      case WQ_FMT_W8_PC:
+        gemm_big_kernel<WQ_FMT_W8_PC><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        break;
+      case WQ_FMT_W8_G128:
+        gemm_big_kernel<WQ_FMT_W8_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        break;
+      case WQ_FMT_W4_G128:
+        gemm_big_kernel<WQ_FMT_W4_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        break;
+      default:
+        return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");
+    }
+    WQ_HIP_CHECK(hipGetLastError());
+    return WQ_OK;
+  }
+  dim3 grid((N + BN - 1) / BN, (unsigned)((M + BM - 1) / BM));
   switch (w->fmt) {
     case WQ_FMT_W8_PC:
       gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
