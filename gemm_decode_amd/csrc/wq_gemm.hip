@@ -388,6 +388,219 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const uint8_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Per-channel W8, large M: operands travel global -> LDS by LDS-DMA
+// (global_load_lds_dwordx4), so no register staging, and three LDS stages let each
+// K step's loads be issued two steps before use.  The 256 x 256 workgroup tile is
+// split over 4 waves of 128 x 128 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16).
+//
+// LDS stage (48 KB): x tile [256 rows][64 k] bf16 as 128-byte rows, then codes
+// [256 rows][64 k] int8 as 64-byte rows.  A DMA instruction writes 64 lanes x 16 bytes
+// to 1 KB of consecutive LDS, so bank conflicts are avoided by choosing which 16-byte
+// chunk each lane fetches: chunk c of x row r sits at position c ^ fx(r), chunk c of
+// code row n at position c ^ fw(n).  Both swizzles keep any 8 (and any 16) rows that
+// one ds_read_b128 phase touches on distinct banks.
+//
+// K order inside a 32-wide slice: lane half h of MFMA s (0 or 1) takes k = 16h + 8s +
+// 0..7, so one 16-byte code chunk (16 k) feeds both MFMAs of a lane half.  The same
+// permutation is applied to x, so every product pairs equal k.
+//
+// Per step t: MFMAs of slice 0 while slice 1's fragments are read and its codes
+// converted to exact bf16 (q = u - 128); wait for this wave's DMA of step t + 1,
+// barrier; issue the DMA of step t + 3 into the stage just finished (so each DMA has
+// two steps to land); MFMAs of slice 1 while slice 0 of step t + 1 is read.
+constexpr int DBM = 256, DBN = 256, DBK = 64;
+constexpr int DA_BYTES = DBM * DBK * 2, DB_BYTES = DBN * DBK, DSTAGE = DA_BYTES + DB_BYTES;
+constexpr int kDmaPerStep = 12;  // DMA instructions per wave and step (8 for x, 4 for codes)
+
+__device__ __forceinline__ int swz_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_w(int n) { return ((n >> 2) ^ (((n >> 1) & 1) << 1)) & 3; }
+
+// One LDS-DMA instruction: lane i copies 16 bytes from g (its own address) to LDS
+// byte l + 16 i (l is wave-uniform).  It is written out rather than taken from
+// __builtin_amdgcn_global_load_lds because the compiler cannot tell the three stages
+// apart and would drain every DMA in flight (vmcnt(0)) before each LDS read; the
+// kernel instead waits explicitly, and only for the step it is about to read.  The
+// instruction writes no register.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  // The low 32 bits of a generic pointer into the LDS aperture are the LDS address.
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(g) : "memory", "m0");
+}
+
+// WM x WN waves (2 x 2 or 1 x 4) over the 256 x 256 tile: each wave owns RB = 8 / WM
+// row blocks and CB = 8 / WN column blocks of 32.  With 1 x 4 every code chunk is
+// converted by exactly one wave (half the conversion work of 2 x 2) at the price of
+// every wave reading the whole x tile from LDS.
+template <int WM>
+__global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
+                                                                const uint16_t* __restrict__ scales,
+                                                                const uint16_t* __restrict__ x,
+                                                                uint16_t* __restrict__ y, int M, int K, int N) {
+  constexpr int WN = 4 / WM, RB = 8 / WM, CB = 8 / WN;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGE];
+
+  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN;
+  const int total = mblocks * nblocks;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int nb = lin / mblocks, mb = lin % mblocks;
+  const int n0 = nb * DBN, m0 = mb * DBM;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int KS = K / DBK;
+
+  // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = 8 wave + j.
+  uint32_t xo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * (8 * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ swz_x(r);
+    xo[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 8 * c;  // M * K < 2^31 (launcher)
+  }
+  // codes: instruction j covers the 16-row gfx950 tile n0/16 + 4 wave + j (rows past
+  // N are clamped to the last row).
+  const int T = (N + kGemvTileRows - 1) / kGemvTileRows;
+  size_t wt_base[4];
+  int wt_nr[4], wlane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = min(n0 / kGemvTileRows + 4 * wave + j, T - 1);
+    const int nr = min(kGemvTileRows, N - t * kGemvTileRows);
+    wt_base[j] = (size_t)t * kGemvTileRows * K;
+    wt_nr[j] = nr;
+    wlane[j] = min(lane >> 2, nr - 1);
+  }
+  const int wc = 16 * ((lane & 3) ^ swz_w(lane >> 2));
+
+  auto code_src = [&](int j, int k0) {
+    const int sl = k0 / kSliceBytes, jb = k0 % kSliceBytes;
+    const int w = min(kSliceBytes, K - sl * kSliceBytes);
+    return qw + wt_base[j] + (size_t)wt_nr[j] * kSliceBytes * sl + wlane[j] * w + jb + wc;
+  };
+  auto dma = [&](uint8_t* st, int ks) {
+    const int k0 = min(ks, KS - 1) * DBK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(x + xo[j] + k0, st + (8 * wave + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(code_src(j, k0), st + DA_BYTES + (4 * wave + j) * 1024);
+  };
+  // ---- fragment addresses (bytes within a stage); the swizzles depend only on l32.
+  int aaddr[2][2], baddr[2];
+#pragma unroll
+  for (int P = 0; P < 2; ++P) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      aaddr[P][s2] = (wm * 32 * RB + l32) * 128 + 16 * ((4 * P + 2 * lh + s2) ^ swz_x(l32));
+    baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
+  }
+
+  bf16x8_t A0[2][RB], B0[2][CB], A1[2][RB], B1[2][CB];
+  auto fread = [&](const uint8_t* st, int P, bf16x8_t (*A)[RB], bf16x8_t (*B)[CB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        A[s2][i] = *reinterpret_cast<const bf16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(st + baddr[P] + j * 32 * 64);
+      B[0][j] = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(raw));
+      B[1][j] = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(raw));
+    }
+  };
+
+  floatx16 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[i][j][a] = 0.f;
+  auto mma = [&](bf16x8_t (*A)[RB], bf16x8_t (*B)[CB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+  };
+  // This wave's DMA of the step after the current one is complete (only the newest
+  // step's kDmaPerStep may still be in flight) and every wave has finished reading
+  // the stage that the next DMA overwrites.
+  auto step_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStep) : "memory");
+  };
+
+  // Issue order inside a phase: the next slice's LDS reads first, then the MFMAs of
+  // the current slice with the code conversions threaded between them, so the matrix
+  // core never waits for a burst of VALU work.
+  constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + CB;
+  constexpr int kCvtPerPhase = 28 * CB;  // per 16 codes: 4 xor, 16 int -> f32, 8 packs
+  constexpr int kLead = 4;               // MFMAs that cover the LDS read latency
+  constexpr int kv = (kCvtPerPhase + kMfmaPerPhase - kLead - 1) / (kMfmaPerPhase - kLead) + 1;
+  auto phase_order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+#pragma unroll
+    for (int i = kLead; i < kMfmaPerPhase; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kv, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  dma(st0, 0);
+  dma(st1, 1);
+  dma(st2, 2);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerStep) : "memory");
+  fread(st0, 0, A0, B0);
+  auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
+    fread(cur, 1, A1, B1);
+    mma(A0, B0);
+    phase_order();
+    step_barrier();
+    dma(cur, t + 3);  // every wave is done with this stage
+    __builtin_amdgcn_sched_barrier(0);
+    fread(nxt, 0, A0, B0);
+    mma(A1, B1);
+    phase_order();
+  };
+  // Three steps per iteration keep every stage address static; the K % 3 steps left
+  // over run after the loop (an early exit inside the loop body makes the register
+  // allocator spill the accumulators).
+  const int KS3 = KS - KS % 3;
+  for (int t = 0; t < KS3; t += 3) {
+    step(st0, st1, t);
+    step(st1, st2, t + 1);
+    step(st2, st0, t + 2);
+  }
+  if (KS % 3 >= 1) step(st0, st1, KS3);
+  if (KS % 3 == 2) step(st1, st2, KS3 + 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int n = n0 + wn * 32 * CB + j * 32 + l32;
+    if (n >= N) continue;
+    const float sc = bf16_to_f32(scales[n]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+      }
+  }
+}
+
 }  // namespace
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
@@ -397,6 +610,17 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
+  if (tile >= 3 && w->fmt == WQ_FMT_W8_PC && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
+    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+    const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
+    if (tile == 3)
+      gemm_dma_w8pc_kernel<2><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+    else
+      gemm_dma_w8pc_kernel<1><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+    WQ_HIP_CHECK(hipGetLastError());
+    return WQ_OK;
+  }
+  if (tile >= 3) tile = 1;
   if (tile == 1) {
     const int bn = w->fmt == WQ_FMT_W8_PC ? Big<WQ_FMT_W8_PC>::BN : Big<WQ_FMT_W8_G128>::BN;
     const int64_t total = ((M + BM2 - 1) / BM2) * ((N + bn - 1) / bn);
