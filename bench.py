@@ -235,6 +235,27 @@ def profile_pass(steps: int = 10, replays: int = 2):
     log(f"profile pass: {replays} replays x {steps} steps x {len(pools)} GEMV launches")
 
 
+PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 3), ("w4g128", 5120, 27648, 2048, 2)]
+
+
+def profile_prefill(calls: int = 10):
+    """Kernels for a rocprofv3 run of the prefill GEMM: for each (fmt, K, N, M, tile) of
+    PREFILL_PROFILE, `calls` wq_linear calls on rotating weight copies with the GEMM
+    tile fixed, as one HIP graph replayed once."""
+    import torch
+    import gemm_decode_amd.wq as wq
+    for fmt, K, N, M, tile in PREFILL_PROFILE:
+        p = Pool(wq, torch, 5, fmt, K, N, M)
+        wq.wq_tune_cache_set(fmt, K, N, M, wq.KIND_GEMM, tile)
+        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1)
+        us = ms * 1e3 / calls
+        log(f"profile prefill {fmt} K={K} N={N} M={M} tile={tile}: {us:.1f} us per call "
+            f"(HIP events), {2.0 * M * K * N / us / 1e6:.1f} TFLOP/s")
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+
+
 def _read_csv_rows(path):
     import csv
     with open(path) as f:
@@ -315,6 +336,8 @@ def main():
     ap.add_argument("--tune-iters", type=int, default=1000)
     ap.add_argument("--profile-pass", action="store_true",
                     help="launch the copy reference and the headline GEMVs for a rocprofv3 counter run")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="run the prefill GEMM profile workload (for rocprofv3) and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
                     help="turn rocprofv3 runs of --profile-pass into the traffic record and a summary")
     args = ap.parse_args()
@@ -334,6 +357,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_pass:
         profile_pass()
+        return
+    if args.profile_prefill:
+        profile_prefill()
         return
     device_warmup(torch)
     log("warm-up done")

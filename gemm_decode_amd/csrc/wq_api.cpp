@@ -3,6 +3,7 @@
 // the .hip files.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cinttypes>
 #include <cstdio>
 #include <cstring>
@@ -111,10 +112,25 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
   *rows = 0;
 }
 
+// Untuned GEMM tile: the skinny kernel up to kSkinnyMaxM tokens, with the smallest
+// split-K that gives about two workgroups per CU; above that the LDS-DMA kernel for
+// per-channel W8 and the 256-row kernel for the group-128 formats.
+int default_tile(const wq_weight* w, int64_t M) {
+  if (M <= kSkinnyMaxM) {
+    const int64_t blocks = (w->N + 127) / 128;
+    int t = kSkinnyTile0;
+    while (t < WQ_GEMM_TILES && blocks * gemm_skinny_split(t, M, w->N) < 512 &&
+           gemm_skinny_split(t + 1, M, w->N) > gemm_skinny_split(t, M, w->N))
+      ++t;
+    return t;
+  }
+  return w->fmt == WQ_FMT_W8_PC ? 3 : kDefaultTile;
+}
+
 int resolve_tile(const wq_weight* w, int64_t M) {
   int v = 0;
   if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMM, &v)) return v;
-  return kDefaultTile;
+  return default_tile(w, M);
 }
 
 wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
@@ -145,13 +161,17 @@ wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int s
                      (hipStream_t)stream);
 }
 
-wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* stream) {
+wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
+                    size_t ws_bytes, void* stream) {
   wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
   const int t = tile == 0 ? resolve_tile(w, M) : tile;
-  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, (hipStream_t)stream);
+  if (tile != 0 && gemm_workspace_bytes(w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->N, M, t)))
+    return fail(WQ_ERR_WORKSPACE, "wq_gemm: tile " + std::to_string(t) + " needs a workspace of " +
+                                      std::to_string(gemm_workspace_bytes(w->N, M, t)) + " bytes");
+  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -313,7 +333,13 @@ wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
   wq_status st = check_shape(w->fmt, w->K, w->N);
   if (st != WQ_OK) return st;
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
-  *bytes = M <= kGemvMaxM ? gemv_workspace_bytes(w->N, M, kMaxSplit) : 0;
+  if (M <= kGemvMaxM) {
+    *bytes = gemv_workspace_bytes(w->N, M, kMaxSplit);
+  } else {
+    size_t b = 0;
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t) b = std::max(b, gemm_workspace_bytes(w->N, M, t));
+    *bytes = b;
+  }
   return WQ_OK;
 }
 
@@ -330,16 +356,14 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
 
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  return gemm_impl(w, x, M, y, tile, stream);
+  return gemm_impl(w, x, M, y, tile, ws, ws_bytes, stream);
 }
 
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws, size_t ws_bytes,
                     void* stream) {
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
   if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream);
-  return gemm_impl(w, x, M, y, 0, stream);
+  return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream);
 }
 
 int wq_tune_pick(const double* lat, int n) {
@@ -392,12 +416,16 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       const int s = cand[c].split;
       if (s > split_units(&copies[0])) continue;
       if (s > 1 && (!ws || ws_bytes < gemv_workspace_bytes(copies[0].N, M, s))) continue;
+    } else {
+      const size_t need = gemm_workspace_bytes(copies[0].N, M, cand[c].tile);
+      if (need > 0 && (!ws || ws_bytes < need)) continue;
+      if (cand[c].tile >= kSkinnyTile0 && gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0) continue;
     }
     auto run = [&]() -> wq_status {
       const wq_weight* w = &copies[rot];
       rot = (rot + 1) % n_copies;
       return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, cand[c].rows, ws, ws_bytes, stream)
-                  : gemm_impl(w, x, M, y, cand[c].tile, stream);
+                  : gemm_impl(w, x, M, y, cand[c].tile, ws, ws_bytes, stream);
     };
     for (int i = 0; i < warmup; ++i)
       if ((st = run()) != WQ_OK) goto out;

@@ -601,15 +601,482 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Skinny GEMM, 8 <= M <= 128 tokens.  At these M the layer is still bound by the
+// weight stream (2 M flops per int8 byte), so the kernel is built like the decode
+// GEMV with the dot products moved onto the matrix cores:
+//
+//   * a workgroup owns 128 weight rows (4 waves x 2 tiles of 16) and a range of K
+//     (split-K over gridDim.y: fp32 partials, summed in order by a second kernel);
+//   * each wave loads its codes straight from memory into registers -- no weight
+//     byte is used by two waves, so LDS would only add a round trip.  One 16-byte
+//     load per lane covers 16 rows x 64 k (W8) or 16 rows x 128 k (W4) of a tile;
+//   * the x slice of a K step (TB*16 tokens x 128 k, bf16) goes through LDS once per
+//     workgroup and feeds all four waves;
+//   * v_mfma_f32_16x16x32_bf16 with x as the A operand (16 tokens) and the exact
+//     bf16 codes as B (16 weight rows).  Lane group c (lanes 16c .. 16c+15) of MFMA s
+//     takes k = 16c + 8s + 0..7 (W8, per 64 k) or 32c + 8s + 0..7 (W4, per 128 k), so
+//     a lane's 16-byte code chunk feeds 2 (W8) or 4 (W4) MFMAs; x is read with the
+//     same permutation;
+//   * a K step is 128 = one group: group-128 formats add s[n][g] times the step's fp32
+//     partial to the accumulator; per-channel W8 scales at the end.
+constexpr int SK_ROWS = 128, SK_STEP = 128;
+constexpr int SK_XP = SK_STEP * 2 + 16;  // LDS pitch of one token's x slice, bytes (16-byte pad)
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int FMT, int TB>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros,
+                                                           const uint16_t* __restrict__ x,
+                                                           uint16_t* __restrict__ y, float* __restrict__ part,
+                                                           int M, int K, int N, int S) {
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
+  constexpr int RT = 2;                  // 16-row tiles per wave
+  constexpr int CH = kW4 ? 1 : 2;        // 16-byte code chunks per lane, tile and step
+  constexpr int XJ = TB;                 // x chunks (16 bytes) per thread and step
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TB * 16 * SK_XP];
+  constexpr int kTrPitch = SK_STEP + 16;  // LDS pitch of a transposed code row (bytes, padded)
+  __shared__ __attribute__((aligned(16))) uint8_t trs[4][kW4 ? 1 : RT * 16 * kTrPitch];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, c4 = lane >> 4;
+  const int n0 = blockIdx.x * SK_ROWS;
+  const int KS = K / SK_STEP, G = K / kGroup;
+  const int ks0 = (int)((int64_t)KS * blockIdx.y / S), ks1 = (int)((int64_t)KS * (blockIdx.y + 1) / S);
+  const int64_t row_bytes = kW4 ? K / 2 : K;
+
+  int nrow[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) nrow[t] = min(n0 + wave * 32 + t * 16 + r16, N - 1);
+
+  // x staging: chunk c = tid + 256 j is token c / 16, bf16 elements 8 (c % 16) .. + 7.
+  auto xload = [&](u32x4* xr, int ks) {
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int c = tid + 256 * j;
+      const int m = min(c >> 4, M - 1);  // tokens past M feed only outputs never stored
+      xr[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + ks * SK_STEP + (c & 15) * 8);
+    }
+  };
+  auto xstore = [&](const u32x4* xr, int buf) {
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<u32x4*>(&xs[buf][(c >> 4) * SK_XP + (c & 15) * 16]) = xr[j];
+    }
+  };
+  uint4 cw[RT][CH];
+  // W4: lane l loads row l % 16, chunk l / 16 (the fragment layout).  W8: lane l loads
+  // row l / 8 + 8 j, chunk l % 8 -- whole 128-byte lines per instruction -- and the
+  // chunks reach the fragment layout through the wave's own LDS area (transpose()).
+  auto code_ptr = [&](int t, int j, int ks) {
+    if constexpr (kW4) {
+      return reinterpret_cast<const uint4*>(qw + tiled_offset(nrow[t], (int64_t)ks * (SK_STEP / 2) + 16 * c4, N, row_bytes));
+    } else {
+      const int rr = min(n0 + wave * 32 + t * 16 + (lane >> 3) + 8 * j, N - 1);
+      return reinterpret_cast<const uint4*>(qw + tiled_offset(rr, (int64_t)ks * SK_STEP + 16 * (lane & 7), N, row_bytes));
+    }
+  };
+  auto transpose = [&](uint4 (*c)[CH]) {
+    if constexpr (!kW4) {
+      uint8_t* tw = trs[wave];
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+          *reinterpret_cast<uint4*>(tw + (t * 16 + (lane >> 3) + 8 * i) * kTrPitch + 16 * (lane & 7)) = c[t][i];
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          c[t][j] = *reinterpret_cast<const uint4*>(tw + (t * 16 + r16) * kTrPitch + 16 * (4 * j + c4));
+    }
+  };
+  auto gscale = [&](int n, int g) -> float {
+    const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
+    return (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
+  };
+
+  floatx4 acc[RT][TB];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (ks0 < ks1) {
+    u32x4 xr[XJ];
+    xload(xr, ks0);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) cw[t][j] = *code_ptr(t, j, ks0);
+    xstore(xr, 0);
+    __syncthreads();
+  }
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int buf = (ks - ks0) & 1;
+    const bool more = ks + 1 < ks1;
+    // The next step (the last step reloads itself: harmless, and branch free), in
+    // flight during this one.
+    const int kn = more ? ks + 1 : ks;
+    u32x4 xr[XJ];
+    uint4 cn[RT][CH];
+    xload(xr, kn);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) cn[t][j] = *code_ptr(t, j, kn);
+    const uint8_t* xb = xs[buf];
+    transpose(cw);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      floatx4 part_acc[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) part_acc[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
+      if constexpr (!kW4) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(cw[t][j]));
+          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(cw[t][j]));
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            const uint8_t* xrow = xb + (16 * b + r16) * SK_XP + 128 * j + 32 * c4;
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(xrow);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(xrow + 16);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, part_acc[b], 0, 0, 0);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1, part_acc[b], 0, 0, 0);
+          }
+        }
+      } else {
+        const int n = nrow[t];
+        const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
+        const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
+        const uint32_t wd[4] = {cw[t][0].x, cw[t][0].y, cw[t][0].z, cw[t][0].w};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, w4_word_to_bf16(wd[s2], z));
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xb + (16 * b + r16) * SK_XP + 64 * c4 + 16 * s2);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wv, part_acc[b], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (kGrouped) {
+        const float sc = gscale(nrow[t], ks);
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, part_acc[b][q], acc[t][b][q]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[t][b] = part_acc[b];
+      }
+    }
+    xstore(xr, buf ^ 1);  // that buffer was last read before the previous barrier
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) cw[t][j] = cn[t][j];
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[token 4 c4 + q][weight row r16] of each 16 x 16 block
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int n = n0 + wave * 32 + t * 16 + r16;
+    if (n >= N) continue;
+    const float sc = (S == 1 && !kGrouped) ? bf16_to_f32(scales[n]) : 1.f;
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 16 * b + 4 * c4 + q;
+        if (m >= M) continue;
+        if (S == 1)
+          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
+        else
+          part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
+      }
+  }
+}
+
+// Skinny GEMM for M <= 32 (one or two token blocks): the x fragments are small enough
+// to come straight from memory (x is a few hundred KB and stays in L2), so every
+// wave streams on its own -- no LDS, no barrier -- with the next step's codes and x
+// in flight while the current step's MFMAs run.  Same operand mapping, K order and
+// epilogue as gemm_skinny_kernel.
+template <int FMT, int TB>
+__global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* __restrict__ qw,
+                                                                  const uint16_t* __restrict__ scales,
+                                                                  const uint8_t* __restrict__ zeros,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  uint16_t* __restrict__ y,
+                                                                  float* __restrict__ part, int M, int K,
+                                                                  int N, int S) {
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
+  constexpr int RT = 2;              // 16-row tiles per wave
+  constexpr int CH = kW4 ? 1 : 2;    // 16-byte code chunks per lane, tile and step
+  constexpr int NX = 4;              // x fragments per token block and step (one per MFMA k slice)
+  constexpr int kTrPitch = SK_STEP + 16;  // LDS pitch of a transposed code row (bytes, padded)
+  __shared__ __attribute__((aligned(16))) uint8_t trs[4][kW4 ? 1 : RT * 16 * kTrPitch];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, c4 = lane >> 4;
+  const int n0 = blockIdx.x * SK_ROWS;
+  const int KS = K / SK_STEP, G = K / kGroup;
+  const int ks0 = (int)((int64_t)KS * blockIdx.y / S), ks1 = (int)((int64_t)KS * (blockIdx.y + 1) / S);
+  const int64_t row_bytes = kW4 ? K / 2 : K;
+
+  int nrow[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) nrow[t] = min(n0 + wave * 32 + t * 16 + r16, N - 1);
+  // gfx950 code addressing per 16-row tile, split into wave-uniform parts (tile base,
+  // rows in the tile) and the lane's row; a step never crosses a 1 KB slice.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int T = (N + kGemvTileRows - 1) / kGemvTileRows;
+  const uint8_t* tbase[RT];
+  int tnr[RT], trow[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int ti = min((n0 + wu * 32 + t * 16) / kGemvTileRows, T - 1);
+    tnr[t] = min(kGemvTileRows, N - ti * kGemvTileRows);
+    tbase[t] = qw + (size_t)ti * kGemvTileRows * row_bytes;
+    trow[t] = min(r16, tnr[t] - 1);
+  }
+  const uint16_t* xrow[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) xrow[b] = x + (size_t)min(16 * b + r16, M - 1) * K;
+  // k offset (elements) of x fragment i within a step: W8 i = 2 j + s -> 64 j + 16 c + 8 s;
+  // W4 i = s -> 32 c + 8 s.
+  auto xoff = [&](int i) { return kW4 ? 32 * c4 + 8 * i : 64 * (i >> 1) + 16 * c4 + 8 * (i & 1); };
+  constexpr int kStepBytes = kW4 ? SK_STEP / 2 : SK_STEP;
+  auto load_codes = [&](u32x4 (*dst)[CH], int ks) {
+    const int64_t b0 = (int64_t)ks * kStepBytes;
+    const int64_t sl = b0 / kSliceBytes;
+    const int w = (int)min((int64_t)kSliceBytes, row_bytes - sl * kSliceBytes);
+    const int jb = (int)(b0 - sl * kSliceBytes) + 16 * c4;
+    if constexpr (kW4) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        dst[t][0] = *reinterpret_cast<const u32x4*>(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + trow[t] * w + jb);
+    } else {
+      // W8: a step is 16 rows x 128 bytes; lane l loads row l / 8 + 8 i, chunk l % 8, so
+      // each load instruction covers eight whole 128-byte lines (the fragment layout,
+      // 16 rows x 64 bytes per instruction, would fetch half lines).  step() moves the
+      // chunks into the fragment layout through this wave's LDS.
+      const int jl = (int)(b0 - sl * kSliceBytes) + 16 * (lane & 7);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const int rr = min((lane >> 3) + 8 * i, tnr[t] - 1);
+          dst[t][i] = *reinterpret_cast<const u32x4*>(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + rr * w + jl);
+        }
+    }
+  };
+  auto load_x = [&](bf16x8_t (*dst)[NX], int ks) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int i = 0; i < NX; ++i) dst[b][i] = *reinterpret_cast<const bf16x8_t*>(xrow[b] + ks * SK_STEP + xoff(i));
+  };
+  auto gscale = [&](int n, int g) -> float {
+    const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
+    return (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
+  };
+
+  floatx4 acc[RT][TB];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Three register sets with fixed roles, so no set is copied (a copy would wait for
+  // its loads): while set s is multiplied, the sets for the next two steps are in
+  // flight.
+  auto step = [&](const u32x4 (*ld)[CH], const bf16x8_t (*xf_)[NX], int ks) {
+    u32x4 cw_[RT][CH];
+    if constexpr (kW4) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) cw_[t][0] = ld[t][0];
+    } else {
+      // row-major [row][128 bytes] (pitch kTrPitch) -> lane l gets row l % 16, chunk
+      // 4 j + l / 16.  One wave's own region: LDS keeps a wave's accesses in order.
+      uint8_t* tw = trs[wave];
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+          *reinterpret_cast<u32x4*>(tw + (t * 16 + (lane >> 3) + 8 * i) * kTrPitch + 16 * (lane & 7)) = ld[t][i];
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          cw_[t][j] = *reinterpret_cast<const u32x4*>(tw + (t * 16 + r16) * kTrPitch + 16 * (4 * j + c4));
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      floatx4 pa[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) pa[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
+      if constexpr (!kW4) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const uint4 c = make_uint4(cw_[t][j].x, cw_[t][j].y, cw_[t][j].z, cw_[t][j].w);
+          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(c));
+          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(c));
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][2 * j], w0, pa[b], 0, 0, 0);
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][2 * j + 1], w1, pa[b], 0, 0, 0);
+          }
+        }
+      } else {
+        const int n = nrow[t];
+        const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
+        const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, w4_word_to_bf16(cw_[t][0][s2], z));
+#pragma unroll
+          for (int b = 0; b < TB; ++b)
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][s2], wv, pa[b], 0, 0, 0);
+        }
+      }
+      if constexpr (kGrouped) {
+        const float sc = gscale(nrow[t], ks);
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, pa[b][q], acc[t][b][q]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[t][b] = pa[b];
+      }
+    }
+  };
+  u32x4 ca[RT][CH], cb[RT][CH], cc[RT][CH];
+  bf16x8_t xa[TB][NX], xb[TB][NX], xc[TB][NX];
+  auto last = [&](int k) { return min(k, ks1 - 1); };  // past the end: reload the last step
+  if (ks0 < ks1) {
+    load_codes(ca, ks0);
+    load_x(xa, ks0);
+    load_codes(cb, last(ks0 + 1));
+    load_x(xb, last(ks0 + 1));
+  }
+  for (int ks = ks0; ks < ks1; ks += 3) {
+    load_codes(cc, last(ks + 2));
+    load_x(xc, last(ks + 2));
+    step(ca, xa, ks);
+    if (ks + 1 >= ks1) break;
+    load_codes(ca, last(ks + 3));
+    load_x(xa, last(ks + 3));
+    step(cb, xb, ks + 1);
+    if (ks + 2 >= ks1) break;
+    load_codes(cb, last(ks + 4));
+    load_x(xb, last(ks + 4));
+    step(cc, xc, ks + 2);
+  }
+
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int n = n0 + wave * 32 + t * 16 + r16;
+    if (n >= N) continue;
+    const float sc = (S == 1 && !kGrouped) ? bf16_to_f32(scales[n]) : 1.f;
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 16 * b + 4 * c4 + q;
+        if (m >= M) continue;
+        if (S == 1)
+          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
+        else
+          part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
+      }
+  }
+}
+
+// y[m][n] = bf16(s[n] * sum_s part[s][m][n]) (per channel) or bf16(sum_s part[s][m][n]),
+// the split ranges added in order.
+template <bool kPerChannel>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ part,
+                                                                  const uint16_t* __restrict__ scales,
+                                                                  uint16_t* __restrict__ y, int M, int N,
+                                                                  int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t MN = (int64_t)M * N;
+  if (i >= MN) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[(int64_t)s * MN + i];
+  const float sc = kPerChannel ? bf16_to_f32(scales[i % N]) : 1.f;
+  y[i] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+}
+
+template <int FMT>
+wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, const uint16_t* x,
+                        uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st) {
+  const dim3 grid((unsigned)((N + SK_ROWS - 1) / SK_ROWS), (unsigned)S);
+  const int TB = (M + 15) / 16;
+  if (TB <= 1)
+    gemm_skinny_direct_kernel<FMT, 1><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else if (TB <= 2)
+    gemm_skinny_direct_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else if (TB <= 4)
+    gemm_skinny_kernel<FMT, 4><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else
+    gemm_skinny_kernel<FMT, 8><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  WQ_HIP_CHECK(hipGetLastError());
+  if (S > 1) {
+    const int64_t MN = (int64_t)M * N;
+    gemm_splitk_reduce_kernel<FMT == WQ_FMT_W8_PC>
+        <<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, S);
+    WQ_HIP_CHECK(hipGetLastError());
+  }
+  return WQ_OK;
+}
+
 }  // namespace
 
+int gemm_skinny_split(int tile, int64_t M, int64_t N) {
+  if (tile < kSkinnyTile0 || tile > WQ_GEMM_TILES || M > kSkinnyMaxM) return 0;
+  const int64_t blocks = (N + SK_ROWS - 1) / SK_ROWS;
+  int S = 2 << (tile - kSkinnyTile0);
+  // more than kSkinnyMaxBlocks workgroups buys nothing but workspace
+  while (S > 1 && (S * M > kSkinnyMaxSplitTokens || blocks * S > 2 * kSkinnyMaxBlocks)) S >>= 1;
+  return S;
+}
+
+size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
+  const int S = gemm_skinny_split(tile, M, N);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
-                      hipStream_t s) {
+                      void* ws, size_t ws_bytes, hipStream_t s) {
   const int K = (int)w->K, N = (int)w->N;
   if (M > 65535LL * BM) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: M too large");
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
+  if (tile >= kSkinnyTile0) {
+    int S = gemm_skinny_split(tile, M, N);
+    if (S > 0 && K % SK_STEP == 0 && (int64_t)M * K < (int64_t(1) << 31)) {
+      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;  // no room for partials
+      float* part = (float*)ws;
+      switch (w->fmt) {
+        case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W8_G128: return launch_skinny<WQ_FMT_W8_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W4_G128: return launch_skinny<WQ_FMT_W4_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        default: return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");
+      }
+    }
+    tile = 2;  // shape outside the skinny kernel's range
+  }
   if (tile >= 3 && w->fmt == WQ_FMT_W8_PC && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));

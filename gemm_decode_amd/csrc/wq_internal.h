@@ -62,8 +62,19 @@ int gemv_max_waves(int fmt, int M, int rows);
 // K slices of the GEMV (64 lanes x one 16-byte chunk: 1024 k int8, 2048 k uint4);
 // split-K ranges are whole slices.
 int64_t gemv_slices(int64_t K, int fmt);
+// GEMM tiles kSkinnyTile0 .. WQ_GEMM_TILES are the skinny kernel (M <= kSkinnyMaxM)
+// with split-K 2, 4, 8, 16, capped so that split * M <= kSkinnyMaxSplitTokens and the
+// grid stays within twice kSkinnyMaxBlocks workgroups (split 1 when the caller gives
+// no workspace).
+constexpr int kSkinnyTile0 = 5;
+constexpr int kSkinnyMaxM = 128;
+constexpr int kSkinnyMaxSplitTokens = 1024;
+constexpr int kSkinnyMaxBlocks = 1024;
+int gemm_skinny_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a skinny one
+// Workspace bytes a GEMM tile needs at this M (fp32 split-K partials; 0 for most tiles).
+size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile);
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
-                      hipStream_t s);
+                      void* ws, size_t ws_bytes, hipStream_t s);
 
 // Workspace bytes for a GEMV with the given split (fp32 partials of every slice).
 size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k);

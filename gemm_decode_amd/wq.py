@@ -34,7 +34,7 @@ FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2}
 FMT_NAME = {v: k for k, v in FMT.items()}
 CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1
-GEMM_TILES = 4
+GEMM_TILES = 8
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)
@@ -230,9 +230,11 @@ def wq_gemv_ex(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int, 
                           0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv_ex")
 
 
-def wq_gemm(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0, stream=None) -> None:
+def wq_gemm(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0,
+            ws: torch.Tensor | None = None, stream=None) -> None:
     M, d = _xy(x, y, w), w.desc()
-    _check(lib.wq_gemm(C.byref(d), _ptr(x), M, _ptr(y), tile, None, 0, _stream(stream)), "wq_gemm")
+    _check(lib.wq_gemm(C.byref(d), _ptr(x), M, _ptr(y), tile, _ptr(ws),
+                       0 if ws is None else ws.numel(), _stream(stream)), "wq_gemm")
 
 
 def wq_linear(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = None,

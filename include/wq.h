@@ -199,7 +199,7 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * per-channel scale is applied in the epilogue, group-128 scales to each group's
  * fp32 partial.  tile: 0 = the tuned tile (default when untuned), else a tile id
  * from 1..WQ_GEMM_TILES.  ws/ws_bytes may be NULL/0 (the GEMM needs none). */
-#define WQ_GEMM_TILES 4
+#define WQ_GEMM_TILES 8
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 

@@ -169,4 +169,8 @@ def test_validation_rejects_before_any_device_work(wqlib):
     n = C.c_size_t()
     assert L.wq_workspace_size(C.byref(d), 1, C.byref(n)) == 0 and n.value == 32 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 7, C.byref(n)) == 0 and n.value == 32 * 7 * 1024 * 4
-    assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 0
+    # M >= 8: the skinny GEMM's split-K partials (split <= 16, split * M <= 1024), none past M = 128
+    assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 16 * 8 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == 16 * 64 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 8 * 128 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 0

@@ -43,7 +43,8 @@ def _run_gemm(wq, g, x_bits, tile=0):
     M = x_bits.shape[0]
     x = to_dev_bf16(x_bits)
     y = torch.empty((M, g.N), dtype=torch.bfloat16, device=DEV)
-    wq.wq_gemm(g, x, y, tile=tile)
+    ws = wq.workspace(wq.wq_workspace_size(g, M))   # split-K partials of the skinny tiles
+    wq.wq_gemm(g, x, y, tile=tile, ws=ws)
     torch.cuda.synchronize()
     return bf16_bits(y)
 
@@ -114,7 +115,7 @@ GEMM_BIG = [(5, "w8pc", 5120, 27648), (5, "w8pc", 13824, 5120), (5, "w4g128", 51
 def test_full_size_gemm(wq, cfg, fmt, K, N):
     W, g, can, rows = _big_case(wq, cfg, fmt, K, N)
     want = oracle_pack_rows(fmt, W, rows)
-    for M in (8, 64, 512, 2048):
+    for M in (8, 16, 64, 128, 512, 2048):
         x = synth.activation(cfg, K, M)
         y_ref = OL.ref_linear(x, want)
         for tile in range(1, wq.GEMM_TILES + 1):
