@@ -51,6 +51,8 @@ int clamp_split(int v, int64_t units) {
 // cross-workgroup slice is the default and split_k > 1 is left to the tuner.
 constexpr int kDefaultSplit = 1;
 constexpr int kDefaultTile = 1;
+static_assert(WQ_GEMM_TILES <= WQ_TUNE_LAT_SLOTS && 6 <= WQ_TUNE_LAT_SLOTS,
+              "wq_tune writes one lat_us slot per GEMM tile or GEMV split");
 
 // Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15 and rows
 // per wave in bits 16..23 (0 = the default for the shape).
@@ -446,6 +448,8 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       st = fail(WQ_ERR_WORKSPACE, "wq_tune: no candidate could run");
       goto out;
     }
+    if (lat_us)
+      for (int i = 0; i < WQ_TUNE_LAT_SLOTS; ++i) lat_us[i] = -1.0;
     if (gemv) {
       *chosen = cand[best].split;
       if (lat_us) {
@@ -462,7 +466,8 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
     } else {
       *chosen = cand[best].tile;
       if (lat_us)
-        for (size_t c = 0; c < cand.size(); ++c) lat_us[c] = lat[c];
+        for (size_t c = 0; c < cand.size(); ++c)
+          if (cand[c].tile >= 1 && cand[c].tile <= WQ_TUNE_LAT_SLOTS) lat_us[cand[c].tile - 1] = lat[c];
       st = wq_tune_cache_set("", copies[0].fmt, copies[0].K, copies[0].N, M, WQ_KIND_GEMM, cand[best].tile);
     }
   }

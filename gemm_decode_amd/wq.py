@@ -35,6 +35,7 @@ FMT_NAME = {v: k for k, v in FMT.items()}
 CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1
 GEMM_TILES = 8
+TUNE_LAT_SLOTS = 8                       # WQ_TUNE_LAT_SLOTS: entries wq_tune writes to lat_us
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)
@@ -256,7 +257,7 @@ def wq_tune(copies, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = 
     M = _xy(x, y, copies[0])
     arr = (WqWeightC * len(copies))(*[c.desc() for c in copies])
     chosen = C.c_int()
-    lat = (C.c_double * 6)(*([-1.0] * 6))
+    lat = (C.c_double * TUNE_LAT_SLOTS)(*([-1.0] * TUNE_LAT_SLOTS))
     _check(lib.wq_tune(arr, len(copies), M, _ptr(x), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                        warmup, iters, _stream(stream), C.byref(chosen), lat), "wq_tune")
     n = len(SPLIT_GRID) if wq_dispatch_kind(M) == KIND_GEMV else GEMM_TILES

@@ -147,11 +147,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
 /* ------------------------------------------------------------- the linear */
 
 /* Workspace bytes needed by wq_gemv / wq_gemm / wq_linear for this weight and M
- * under any split_k the library may pick (host only): the fp32 partial sums of
- * every K slice of a cross-workgroup split, 32 * M * N * 4 bytes for M < 8, and 0
- * for M >= 8 (the GEMM needs none).  The contents are scratch: no initialisation
- * is needed and nothing is kept between calls.  Calls that share a workspace must
- * not run concurrently. */
+ * under any split the library may pick (host only): fp32 partial sums of the
+ * ranges of a cross-workgroup K split -- 32 * M * N * 4 bytes for M < 8 (GEMV); for
+ * 8 <= M <= 128 the largest split * M * N * 4 of the skinny GEMM tiles (split <= 16,
+ * split * M <= 1024, at most 2048 workgroups); 0 for M > 128.  The contents are
+ * scratch: no initialisation is needed and nothing is kept between calls.  Calls
+ * that share a workspace must not run concurrently. */
 wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
 
 /* Decode GEMV, 1 <= M <= 7 (the "Key Optimizations" register-dequant GEMV of the
@@ -194,11 +195,22 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
                      int rows, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill GEMM, M >= 1 (used by wq_linear for M >= 8; smaller M are accepted so
- * the two paths can be compared): codes are converted to exact bf16 values in LDS
- * and multiplied by bf16 x tiles on the matrix cores with fp32 accumulation; the
- * per-channel scale is applied in the epilogue, group-128 scales to each group's
- * fp32 partial.  tile: 0 = the tuned tile (default when untuned), else a tile id
- * from 1..WQ_GEMM_TILES.  ws/ws_bytes may be NULL/0 (the GEMM needs none). */
+ * the two paths can be compared), the tileInfer README's dequantize-to-bf16 GEMM
+ * ("Key Optimizations"): codes are converted to exact bf16 values (q, or q - z) and
+ * multiplied by bf16 x on the matrix cores with fp32 accumulation; the per-channel
+ * scale is applied to the finished fp32 sum, group-128 scales to each group's fp32
+ * partial.  w must be in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
+ *
+ * tile: 0 = the tuned tile (a default by M and format when untuned), else
+ *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;
+ *   2  128 x 128 tile, 4 waves of 64 x 64;
+ *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
+ *   4  as 3 with 1 x 4 waves (other formats or shapes: tile 1);
+ *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
+ *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
+ *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
+ * ws/ws_bytes may be NULL/0 for tiles 1-4.  Results are bit-identical from run to
+ * run for a given tile. */
 #define WQ_GEMM_TILES 8
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
@@ -225,8 +237,10 @@ int wq_tune_pick(const double* lat, int n);
  * weights (distinct buffers with the same format and shape) so that the weights
  * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k
  * (GEMV) or tile (GEMM) to *chosen (host) and, if lat_us is not NULL, the mean
- * microseconds per call of each split_k (its best rows and waves) or tile into lat_us[0..5]
- * (host; -1 for candidates that could not run).  Synchronizes the stream. */
+ * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
+ * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
+ * for candidates that could not run and for unused slots).  Synchronizes the stream. */
+#define WQ_TUNE_LAT_SLOTS 8
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

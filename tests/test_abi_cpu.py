@@ -174,3 +174,15 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == 16 * 64 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 8 * 128 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 0
+
+
+def test_binding_constants_match_the_header(wqlib):
+    """The binding's copies of the header's array sizes and limits (a mismatch once let
+    wq_tune write past the binding's latency buffer)."""
+    import re
+    import gemm_decode_amd.wq as wq
+    hdr = open(os.path.join(ROOT, "include", "wq.h")).read()
+    defs = dict(re.findall(r"#define (WQ_[A-Z_]+) (\d+)", hdr))
+    assert int(defs["WQ_GEMM_TILES"]) == wq.GEMM_TILES
+    assert int(defs["WQ_TUNE_LAT_SLOTS"]) == wq.TUNE_LAT_SLOTS
+    assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))

@@ -372,8 +372,13 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert f" 0 {K} {N} 1 0 {v}" in open(p).read()
     xg = to_dev_bf16(synth.activation(102, K, 64))
     yg = torch.empty((64, N), dtype=torch.bfloat16, device=DEV)
+    wsg = wq.workspace(wq.wq_workspace_size(g, 64))
+    tile, lat = wq.wq_tune(copies, xg, yg, wsg, warmup=2, iters=3)
+    assert 1 <= tile <= wq.GEMM_TILES and all(v > 0 for v in lat), (tile, lat)
+    assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
+    # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
-    assert tile in (1, 2) and all(v > 0 for v in lat)
+    assert 1 <= tile <= 4 and all(v > 0 for v in lat[:4]) and all(v < 0 for v in lat[4:]), (tile, lat)
 
 
 def test_error_paths_on_device(wq):
