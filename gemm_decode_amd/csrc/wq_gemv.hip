@@ -167,31 +167,17 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) xs_total[m] = 0.f;
 
-  for (int sl = sl0 + wave; sl < sl1; sl += W) {
-    const int k = sl * kSlice + lane * F::kChunk;
-    const bool valid = k < K;           // the last slice may be ragged
-    const int kk = valid ? k : 0;
+  // Full slices of a full tile (every row a whole 1 KB, no row past N) take the fast
+  // form: wave-uniform slice base + a 32-bit lane offset + r KB, so the loads need no
+  // 64-bit address arithmetic; the ragged last slice and a short last tile take the
+  // general form.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int t_full = nr == R ? (int)(row_bytes / kSliceBytes) : 0;  // slices with whole 1 KB rows
+  const uint32_t rlane = (uint32_t)(sub * RR) * kSliceBytes + lane * 16;
+  const uint32_t xlane = (uint32_t)lane * F::kChunk * 2;  // byte offset of this lane's x chunk in a slice
 
-    // ---- loads: RR row chunks (one contiguous block per slice), x chunk, metadata
-    const int wsl = (int)min((size_t)kSliceBytes, row_bytes - (size_t)sl * kSliceBytes);  // bytes per row
-    const uint8_t* sbase = tile_base + (size_t)nr * kSliceBytes * sl + (valid ? lane * 16 : 0);
-    uint4 cw[RR];
-#pragma unroll
-    for (int r = 0; r < RR; ++r)
-      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(sub * RR + r, nr - 1) * wsl);
-    uint32_t xb[M][F::kXWords];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)m * K + kk);
-#pragma unroll
-      for (int j = 0; j < F::kXWords / 4; ++j) {
-        const uint4 a = xp[j];
-        xb[m][4 * j + 0] = valid ? a.x : 0u;
-        xb[m][4 * j + 1] = valid ? a.y : 0u;
-        xb[m][4 * j + 2] = valid ? a.z : 0u;
-        xb[m][4 * j + 3] = valid ? a.w : 0u;
-      }
-    }
+  // The arithmetic of one slice, given its codes (RR rows) and x chunk.
+  auto slice_math = [&](const uint4* cw, const uint32_t (*xb)[F::kXWords], int kk) {
     const int g = kk / kGroup;
     uint32_t sw[RR / 2];  // RR 16-bit scales of this sub-tile's rows for group g
     uint32_t zw = 0;      // RR 4-bit zero-points
@@ -354,6 +340,56 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
         for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, t[m], acc[r][m]);
       }
     }
+  };
+
+  int sl = sl0 + wu;
+  // full slices: no bounds logic, 32-bit lane offsets from wave-uniform bases
+  for (const int sl_end = min(sl1, t_full); sl < sl_end; sl += W) {
+    const uint8_t* sblock = tile_base + (size_t)nr * kSliceBytes * sl;
+    uint4 cw[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) cw[r] = *reinterpret_cast<const uint4*>(sblock + rlane + r * kSliceBytes);
+    const uint8_t* xs_base = reinterpret_cast<const uint8_t*>(x + (size_t)sl * kSlice);
+    uint32_t xb[M][F::kXWords];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xs_base + (uint32_t)m * (uint32_t)K * 2 + xlane);
+#pragma unroll
+      for (int j = 0; j < F::kXWords / 4; ++j) {
+        const uint4 a = xp[j];
+        xb[m][4 * j + 0] = a.x;
+        xb[m][4 * j + 1] = a.y;
+        xb[m][4 * j + 2] = a.z;
+        xb[m][4 * j + 3] = a.w;
+      }
+    }
+    slice_math(cw, xb, sl * kSlice + lane * F::kChunk);
+  }
+  // the ragged last slice, or every slice of a short last tile: general addressing
+  for (; sl < sl1; sl += W) {
+    const int k = sl * kSlice + lane * F::kChunk;
+    const bool valid = k < K;
+    const int kk = valid ? k : 0;
+    const int wsl = (int)min((size_t)kSliceBytes, row_bytes - (size_t)sl * kSliceBytes);  // bytes per row
+    const uint8_t* sbase = tile_base + (size_t)nr * kSliceBytes * sl + (valid ? lane * 16 : 0);
+    uint4 cw[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r)
+      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(sub * RR + r, nr - 1) * wsl);
+    uint32_t xb[M][F::kXWords];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)m * K + kk);
+#pragma unroll
+      for (int j = 0; j < F::kXWords / 4; ++j) {
+        const uint4 a = xp[j];
+        xb[m][4 * j + 0] = valid ? a.x : 0u;
+        xb[m][4 * j + 1] = valid ? a.y : 0u;
+        xb[m][4 * j + 2] = valid ? a.z : 0u;
+        xb[m][4 * j + 3] = valid ? a.w : 0u;
+      }
+    }
+    slice_math(cw, xb, kk);
   }
   if constexpr (FMT == WQ_FMT_W8_PC) {
 #pragma unroll
@@ -488,6 +524,7 @@ int gemv_default_rows(int64_t K, int64_t N, int fmt, int M) {
   // rows per wave share each x chunk (and its conversion) among more rows, which
   // pays when there are many row tiles or several tokens (measured on MI355X)
   (void)K;
+  if (fmt == WQ_FMT_W4_G128 && M >= 5) return 8;  // 16 rows x 5+ tokens of uint4 spill registers
   if (M >= 4) return N >= 16384 ? 16 : 8;
   if (fmt == WQ_FMT_W4_G128) return 8;
   return N >= 16384 ? 8 : 4;
