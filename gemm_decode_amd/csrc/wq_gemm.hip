@@ -712,7 +712,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int j = 0; j < CH; ++j) cw[t][j] = *code_ptr(t, j, ks0);
+      for (int j = 0; j < CH; ++j) cw[t][j] = load_stream16(code_ptr(t, j, ks0));
     xstore(xr, 0);
     __syncthreads();
   }
@@ -728,7 +728,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int j = 0; j < CH; ++j) cn[t][j] = *code_ptr(t, j, kn);
+      for (int j = 0; j < CH; ++j) cn[t][j] = load_stream16(code_ptr(t, j, kn));
     const uint8_t* xb = xs[buf];
     transpose(cw);
 #pragma unroll
@@ -861,8 +861,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
     const int jb = (int)(b0 - sl * kSliceBytes) + 16 * c4;
     if constexpr (kW4) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        dst[t][0] = *reinterpret_cast<const u32x4*>(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + trow[t] * w + jb);
+      for (int t = 0; t < RT; ++t) {
+        const uint4 v = load_stream16(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + trow[t] * w + jb);
+        dst[t][0] = u32x4{v.x, v.y, v.z, v.w};
+      }
     } else {
       // W8: a step is 16 rows x 128 bytes; lane l loads row l / 8 + 8 i, chunk l % 8, so
       // each load instruction covers eight whole 128-byte lines (the fragment layout,
@@ -874,7 +876,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
           const int rr = min((lane >> 3) + 8 * i, tnr[t] - 1);
-          dst[t][i] = *reinterpret_cast<const u32x4*>(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + rr * w + jl);
+          const uint4 v = load_stream16(tbase[t] + (size_t)tnr[t] * kSliceBytes * sl + rr * w + jl);
+          dst[t][i] = u32x4{v.x, v.y, v.z, v.w};
         }
     }
   };

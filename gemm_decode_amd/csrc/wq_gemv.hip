@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
     const uint8_t* sblock = tile_base + (size_t)nr * kSliceBytes * sl;
     uint4 cw[RR];
 #pragma unroll
-    for (int r = 0; r < RR; ++r) cw[r] = *reinterpret_cast<const uint4*>(sblock + rlane + r * kSliceBytes);
+    for (int r = 0; r < RR; ++r) cw[r] = load_stream16(sblock + rlane + r * kSliceBytes);
     const uint8_t* xs_base = reinterpret_cast<const uint8_t*>(x + (size_t)sl * kSlice);
     uint32_t xb[M][F::kXWords];
 #pragma unroll
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
     uint4 cw[RR];
 #pragma unroll
     for (int r = 0; r < RR; ++r)
-      cw[r] = *reinterpret_cast<const uint4*>(sbase + (size_t)min(sub * RR + r, nr - 1) * wsl);
+      cw[r] = load_stream16(sbase + (size_t)min(sub * RR + r, nr - 1) * wsl);
     uint32_t xb[M][F::kXWords];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
