@@ -193,7 +193,7 @@ def traffic_entry(kernel_src_sha: str):
 
 # Launch configuration of the headline GEMV per shape (split_k, waves, rows) used by
 # the counter pass, so the profiled kernels are the ones the tuner picks on MI355X.
-PROFILE_CONFIG = {(5120, 27648): (1, 8, 8), (13824, 5120): (1, 6, 4), (5120, 7168): (1, 8, 4),
+PROFILE_CONFIG = {(5120, 27648): (1, 8, 4), (13824, 5120): (1, 4, 4), (5120, 7168): (1, 1, 4),
                   (6144, 5120): (1, 6, 4)}
 COPY_BYTES = 1 << 30
 
