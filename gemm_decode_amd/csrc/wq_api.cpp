@@ -115,18 +115,18 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 }
 
 // Untuned GEMM tile: the skinny kernel up to kSkinnyMaxM tokens, with the smallest
-// split-K that gives about two workgroups per CU; above that the LDS-DMA kernel for
-// per-channel W8 and the 256-row kernel for the group-128 formats.
+// split-K that gives about two workgroups per CU; above that the 8-wave LDS-DMA kernel
+// for per-channel W8 and the 256-row kernel for the group-128 formats.
 int default_tile(const wq_weight* w, int64_t M) {
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
     int t = kSkinnyTile0;
-    while (t < WQ_GEMM_TILES && blocks * gemm_skinny_split(t, M, w->N) < 512 &&
+    while (t < kSkinnyTileLast && blocks * gemm_skinny_split(t, M, w->N) < 512 &&
            gemm_skinny_split(t + 1, M, w->N) > gemm_skinny_split(t, M, w->N))
       ++t;
     return t;
   }
-  return w->fmt == WQ_FMT_W8_PC ? 3 : kDefaultTile;
+  return w->fmt == WQ_FMT_W8_PC ? 9 : kDefaultTile;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {
@@ -421,7 +421,9 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
     } else {
       const size_t need = gemm_workspace_bytes(copies[0].N, M, cand[c].tile);
       if (need > 0 && (!ws || ws_bytes < need)) continue;
-      if (cand[c].tile >= kSkinnyTile0 && gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0) continue;
+      if (cand[c].tile >= kSkinnyTile0 && cand[c].tile <= kSkinnyTileLast &&
+          gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0)
+        continue;
     }
     auto run = [&]() -> wq_status {
       const wq_weight* w = &copies[rot];

@@ -411,7 +411,6 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const uint8_t* __restr
 // two steps to land); MFMAs of slice 1 while slice 0 of step t + 1 is read.
 constexpr int DBM = 256, DBN = 256, DBK = 64;
 constexpr int DA_BYTES = DBM * DBK * 2, DB_BYTES = DBN * DBK, DSTAGE = DA_BYTES + DB_BYTES;
-constexpr int kDmaPerStep = 12;  // DMA instructions per wave and step (8 for x, 4 for codes)
 
 __device__ __forceinline__ int swz_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_w(int n) { return ((n >> 2) ^ (((n >> 1) & 1) << 1)) & 3; }
@@ -432,12 +431,15 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
 // row blocks and CB = 8 / WN column blocks of 32.  With 1 x 4 every code chunk is
 // converted by exactly one wave (half the conversion work of 2 x 2) at the price of
 // every wave reading the whole x tile from LDS.
-template <int WM>
-__global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
-                                                                const uint16_t* __restrict__ scales,
-                                                                const uint16_t* __restrict__ x,
-                                                                uint16_t* __restrict__ y, int M, int K, int N) {
-  constexpr int WN = 4 / WM, RB = 8 / WM, CB = 8 / WN;
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
+                                                                         const uint16_t* __restrict__ scales,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         uint16_t* __restrict__ y, int M, int K,
+                                                                         int N) {
+  constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
+  constexpr int XI = 32 / NW, WI = 16 / NW;  // x and code DMA instructions per wave and step
+  constexpr int kDmaPerStep = XI + WI;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGE];
@@ -456,22 +458,22 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __
   const int l32 = lane & 31, lh = lane >> 5;
   const int KS = K / DBK;
 
-  // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = 8 wave + j.
-  uint32_t xo[8];
+  // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = XI wave + j.
+  uint32_t xo[XI];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * (8 * wave + j) + (lane >> 3);
+  for (int j = 0; j < XI; ++j) {
+    const int r = 8 * (XI * wave + j) + (lane >> 3);
     const int c = (lane & 7) ^ swz_x(r);
     xo[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 8 * c;  // M * K < 2^31 (launcher)
   }
-  // codes: instruction j covers the 16-row gfx950 tile n0/16 + 4 wave + j (rows past
+  // codes: instruction j covers the 16-row gfx950 tile n0/16 + WI wave + j (rows past
   // N are clamped to the last row).
   const int T = (N + kGemvTileRows - 1) / kGemvTileRows;
-  size_t wt_base[4];
-  int wt_nr[4], wlane[4];
+  size_t wt_base[WI];
+  int wt_nr[WI], wlane[WI];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = min(n0 / kGemvTileRows + 4 * wave + j, T - 1);
+  for (int j = 0; j < WI; ++j) {
+    const int t = min(n0 / kGemvTileRows + WI * wave + j, T - 1);
     const int nr = min(kGemvTileRows, N - t * kGemvTileRows);
     wt_base[j] = (size_t)t * kGemvTileRows * K;
     wt_nr[j] = nr;
@@ -487,9 +489,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __
   auto dma = [&](uint8_t* st, int ks) {
     const int k0 = min(ks, KS - 1) * DBK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(x + xo[j] + k0, st + (8 * wave + j) * 1024);
+    for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(code_src(j, k0), st + DA_BYTES + (4 * wave + j) * 1024);
+    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + DA_BYTES + (WI * wave + j) * 1024);
   };
   // ---- fragment addresses (bytes within a stage); the swizzles depend only on l32.
   int aaddr[2][2], baddr[2];
@@ -501,7 +503,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __
     baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
   }
 
-  bf16x8_t A0[2][RB], B0[2][CB], A1[2][RB], B1[2][CB];
+  bf16x8_t A0[2][RB], B0[2][CB];
+  bf16x8_t A1[NW == 4 ? 2 : 1][RB], B1[NW == 4 ? 2 : 1][CB];
   auto fread = [&](const uint8_t* st, int P, bf16x8_t (*A)[RB], bf16x8_t (*B)[CB]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -560,17 +563,31 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_w8pc_kernel(const uint8_t* __
   dma(st1, 1);
   dma(st2, 2);
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerStep) : "memory");
-  fread(st0, 0, A0, B0);
+  // Four waves (one per SIMD) software-pipeline their fragment reads one slice ahead
+  // (two fragment sets); with eight waves (two per SIMD) the registers hold one set and
+  // the other wave on the SIMD covers the LDS latency.
+  constexpr bool kPipelined = NW == 4;
+  if constexpr (kPipelined) fread(st0, 0, A0, B0);
   auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
-    fread(cur, 1, A1, B1);
-    mma(A0, B0);
-    phase_order();
-    step_barrier();
-    dma(cur, t + 3);  // every wave is done with this stage
-    __builtin_amdgcn_sched_barrier(0);
-    fread(nxt, 0, A0, B0);
-    mma(A1, B1);
-    phase_order();
+    if constexpr (kPipelined) {
+      fread(cur, 1, A1, B1);
+      mma(A0, B0);
+      phase_order();
+      step_barrier();
+      dma(cur, t + 3);  // every wave is done with this stage
+      __builtin_amdgcn_sched_barrier(0);
+      fread(nxt, 0, A0, B0);
+      mma(A1, B1);
+      phase_order();
+    } else {
+      (void)nxt;
+      fread(cur, 0, A0, B0);
+      mma(A0, B0);
+      fread(cur, 1, A0, B0);
+      mma(A0, B0);
+      step_barrier();
+      dma(cur, t + 3);
+    }
   };
   // Three steps per iteration keep every stage address static; the K % 3 steps left
   // over run after the loop (an early exit inside the loop body makes the register
@@ -1046,7 +1063,7 @@ wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs
 }  // namespace
 
 int gemm_skinny_split(int tile, int64_t M, int64_t N) {
-  if (tile < kSkinnyTile0 || tile > WQ_GEMM_TILES || M > kSkinnyMaxM) return 0;
+  if (tile < kSkinnyTile0 || tile > kSkinnyTileLast || M > kSkinnyMaxM) return 0;
   const int64_t blocks = (N + SK_ROWS - 1) / SK_ROWS;
   int S = 2 << (tile - kSkinnyTile0);
   // more than kSkinnyMaxBlocks workgroups buys nothing but workspace
@@ -1066,7 +1083,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
-  if (tile >= kSkinnyTile0) {
+  if (tile >= kSkinnyTile0 && tile <= kSkinnyTileLast) {
     int S = gemm_skinny_split(tile, M, N);
     if (S > 0 && K % SK_STEP == 0 && (int64_t)M * K < (int64_t(1) << 31)) {
       if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;  // no room for partials
@@ -1080,17 +1097,20 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     }
     tile = 2;  // shape outside the skinny kernel's range
   }
-  if (tile >= 3 && w->fmt == WQ_FMT_W8_PC && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
+  const bool dma_tile = tile == 3 || tile == 4 || tile == 9;
+  if (dma_tile && w->fmt == WQ_FMT_W8_PC && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
     if (tile == 3)
-      gemm_dma_w8pc_kernel<2><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+      gemm_dma_w8pc_kernel<2, 2><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+    else if (tile == 4)
+      gemm_dma_w8pc_kernel<1, 4><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
     else
-      gemm_dma_w8pc_kernel<1><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+      gemm_dma_w8pc_kernel<2, 4><<<blocks, 512, 0, s>>>(qw, sc, x, y, (int)M, K, N);
     WQ_HIP_CHECK(hipGetLastError());
     return WQ_OK;
   }
-  if (tile >= 3) tile = 1;
+  if (dma_tile) tile = 1;
   if (tile == 1) {
     const int bn = w->fmt == WQ_FMT_W8_PC ? Big<WQ_FMT_W8_PC>::BN : Big<WQ_FMT_W8_G128>::BN;
     const int64_t total = ((M + BM2 - 1) / BM2) * ((N + bn - 1) / bn);

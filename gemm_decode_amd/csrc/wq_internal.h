@@ -79,7 +79,7 @@ int64_t gemv_slices(int64_t K, int fmt);
 // with split-K 2, 4, 8, 16, capped so that split * M <= kSkinnyMaxSplitTokens and the
 // grid stays within twice kSkinnyMaxBlocks workgroups (split 1 when the caller gives
 // no workspace).
-constexpr int kSkinnyTile0 = 5;
+constexpr int kSkinnyTile0 = 5, kSkinnyTileLast = 8;
 constexpr int kSkinnyMaxM = 128;
 constexpr int kSkinnyMaxSplitTokens = 1024;
 constexpr int kSkinnyMaxBlocks = 1024;

@@ -205,13 +205,15 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;
  *   2  128 x 128 tile, 4 waves of 64 x 64;
  *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
- *   4  as 3 with 1 x 4 waves (other formats or shapes: tile 1);
+ *   4  as 3 with 1 x 4 waves;
+ *   9  as 3 with 8 waves (2 x 4, two per SIMD) (tiles 3, 4, 9 for other formats or
+ *      shapes: tile 1);
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
  * ws/ws_bytes may be NULL/0 for tiles 1-4.  Results are bit-identical from run to
  * run for a given tile. */
-#define WQ_GEMM_TILES 8
+#define WQ_GEMM_TILES 9
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -240,7 +242,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 8
+#define WQ_TUNE_LAT_SLOTS 12
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

@@ -106,7 +106,7 @@ def test_tuner_cache_roundtrip_and_corrupt_file(wqlib, tmp_path):
     with pytest.raises(wqlib.WqError):
         wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 1, 0, 3, tag)    # not a power of two
     with pytest.raises(wqlib.WqError):
-        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 8, 1, 9, tag)    # no such tile
+        wqlib.wq_tune_cache_set("w8pc", 5120, 27648, 8, 1, wqlib.GEMM_TILES + 1, tag)  # no such tile
     p = str(tmp_path / "tune.txt")
     wqlib.wq_tune_cache_save(p)
     wqlib.wq_tune_cache_clear()
@@ -160,7 +160,7 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
     dsa = _desc(wqlib, fmt=1, s=0x2002)
     assert L.wq_gemv(C.byref(dsa), x, 1, y, 1, None, 0, None) == 3          # tiled scales misaligned
-    assert L.wq_gemm(C.byref(d), x, 16, y, 9, None, 0, None) == 1           # bad tile
+    assert L.wq_gemm(C.byref(d), x, 16, y, 10, None, 0, None) == 1          # bad tile
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
     assert L.wq_pack(None, C.byref(dc), None) == 1
