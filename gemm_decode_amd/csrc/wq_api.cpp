@@ -54,13 +54,15 @@ constexpr int kDefaultTile = 1;
 static_assert(WQ_GEMM_TILES <= WQ_TUNE_LAT_SLOTS && 6 <= WQ_TUNE_LAT_SLOTS,
               "wq_tune writes one lat_us slot per GEMM tile or GEMV split");
 
-// Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15 and rows
-// per wave in bits 16..23 (0 = the default for the shape).
+// Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15, rows per
+// wave in bits 16..23 (0 = the default for the shape) and the slice-prefetch flag in
+// bit 24 (rows | WQ_GEMV_PREFETCH, shifted like rows).
 int gemv_value(int split, int waves, int rows) { return split | (waves << 8) | (rows << 16); }
 bool valid_gemv_value(int v) {
   const int split = v & 0xFF, waves = (v >> 8) & 0xFF, rows = (v >> 16) & 0xFF;
-  return (v >> 24) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves &&
-         (rows == 0 || rows == 4 || rows == 8 || rows == 16);
+  const bool pf = (v >> 24) & 1;
+  return (v >> 25) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves &&
+         (rows == 0 || rows == 4 || rows == 8 || rows == 16) && !(pf && rows == 0);
 }
 
 std::string resolve_tag(const char* tag) {
@@ -106,7 +108,7 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
   if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) {
     *split = v & 0xFF;
     *waves = (v >> 8) & 0xFF;
-    *rows = (v >> 16) & 0xFF;
+    *rows = (v >> 16) & (0xFF | kGemvPrefetch);
     return;
   }
   *split = clamp_split(kDefaultSplit, split_units(w));
@@ -143,8 +145,12 @@ wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int s
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves)
     return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default) or 1..16");
-  if (rows != 0 && rows != 4 && rows != 8 && rows != 16)
-    return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 0 (default), 4, 8 or 16");
+  const int rr = rows & ~kGemvPrefetch;
+  if ((rr != 0 && rr != 4 && rr != 8 && rr != 16) || (rows & kGemvPrefetch && rr == 0))
+    return fail(WQ_ERR_INVALID_ARG,
+                "wq_gemv: rows per wave must be 0 (default), 4, 8 or 16 (optionally | WQ_GEMV_PREFETCH)");
+  if (rows & kGemvPrefetch && gemv_max_waves(w->fmt, (int)M, rows) == 0)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: slice prefetch is not offered at this format, M and rows");
   int split = split_k, wv = waves, rw = rows;
   if (split_k == 0) {
     int tw = 0, tr = 0;
@@ -398,12 +404,14 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   if (gemv) {
     const int fmt = copies[0].fmt;
     for (int s = 1; s <= kMaxSplit; s *= 2)
-      for (int rw = 4; rw <= 16; rw *= 2) {
-        const int cap = gemv_max_waves(fmt, (int)M, rw);
-        const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
-        for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, rw, 0});
-        if (dflt & (dflt - 1)) cand.push_back({s, dflt, rw, 0});  // the default when not a power of two
-      }
+      for (int rr = 4; rr <= 16; rr *= 2)
+        for (const int rw : {rr, rr | kGemvPrefetch}) {
+          const int cap = gemv_max_waves(fmt, (int)M, rw);
+          if (cap == 0) continue;  // prefetch not offered here
+          const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
+          for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, rw, 0});
+          if (dflt & (dflt - 1)) cand.push_back({s, dflt, rw, 0});  // the default when not a power of two
+        }
   } else {
     for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, 0, t});
   }

@@ -124,23 +124,32 @@ struct Fmt<WQ_FMT_W4_G128> {
   static constexpr int kXWords = 16;
 };
 
-// Registers a lane needs (estimate: codes, accumulators, x in two forms, addresses)
-// and the largest workgroup whose per-lane budget (512 / ceil(W/4) VGPRs) holds them.
-constexpr int lane_regs(int fmt, int RR, int M) { return 40 + 4 * RR + RR * M + 16 * M + (fmt != WQ_FMT_W8_PC ? 8 : 0); }
-constexpr int max_waves_r(int fmt, int RR, int M) {
-  return lane_regs(fmt, RR, M) <= 118 ? 16 : lane_regs(fmt, RR, M) <= 236 ? 8 : 4;
+// x words (bf16 pairs) per lane and token of a slice
+constexpr int x_words(int fmt) { return fmt == WQ_FMT_W4_G128 ? 16 : 8; }
+// Slice prefetch (a launch option): a wave loads its next slice while it multiplies
+// the current one, at the price of a second register set of codes and x -- offered
+// while that set is small.
+constexpr bool prefetch_allowed(int fmt, int RR, int M) { return 4 * RR + M * x_words(fmt) <= 48; }
+// Registers a lane needs (estimate: codes, accumulators, x in two forms, addresses,
+// the prefetch set) and the largest workgroup whose per-lane budget (512 / ceil(W/4)
+// VGPRs) holds them.
+constexpr int lane_regs(int fmt, int RR, int M, bool PF) {
+  return 40 + 4 * RR + RR * M + 16 * M + (fmt != WQ_FMT_W8_PC ? 8 : 0) + (PF ? 4 * RR + M * x_words(fmt) : 0);
+}
+constexpr int max_waves_r(int fmt, int RR, int M, bool PF) {
+  return lane_regs(fmt, RR, M, PF) <= 118 ? 16 : lane_regs(fmt, RR, M, PF) <= 236 ? 8 : 4;
 }
 
 // grid = (16-row tiles x sub-tiles of RR rows, split_k); block = 64 * W threads.
-template <int FMT, int M, int RR>
-__global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
+template <int FMT, int M, int RR, bool PF>
+__global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     float* __restrict__ part, int K, int N) {
   using F = Fmt<FMT>;
   constexpr int kSlice = 64 * F::kChunk;
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
-  constexpr int MAXW = max_waves_r(FMT, RR, M);
+  constexpr int MAXW = max_waves_r(FMT, RR, M, PF);
   constexpr int NSUB = R / RR;
   __shared__ float red[MAXW][M * RR];
 
@@ -342,28 +351,61 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M)) void gemv_kernel(
     }
   };
 
-  int sl = sl0 + wu;
-  // full slices: no bounds logic, 32-bit lane offsets from wave-uniform bases
-  for (const int sl_end = min(sl1, t_full); sl < sl_end; sl += W) {
-    const uint8_t* sblock = tile_base + (size_t)nr * kSliceBytes * sl;
-    uint4 cw[RR];
+  // Full slices: no bounds logic, 32-bit lane offsets from wave-uniform bases.  A wave
+  // with several slices loads the next one while it multiplies the current one (two
+  // register sets with fixed roles: copying a set would wait for its loads).
+  auto load_full = [&](uint4* cw, uint32_t (*xb)[F::kXWords], int sl) {
+    // (a tile is at most 16 x 2^22 bytes: 32-bit scalar offsets)
+    const uint8_t* sblock = tile_base + (uint32_t)(nr * kSliceBytes) * (uint32_t)sl;
 #pragma unroll
     for (int r = 0; r < RR; ++r) cw[r] = load_stream16(sblock + rlane + r * kSliceBytes);
-    const uint8_t* xs_base = reinterpret_cast<const uint8_t*>(x + (size_t)sl * kSlice);
-    uint32_t xb[M][F::kXWords];
+    const uint8_t* xs_base = reinterpret_cast<const uint8_t*>(x) + (uint32_t)sl * (uint32_t)(kSlice * 2);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const uint4* xp = reinterpret_cast<const uint4*>(xs_base + (uint32_t)m * (uint32_t)K * 2 + xlane);
 #pragma unroll
       for (int j = 0; j < F::kXWords / 4; ++j) {
-        const uint4 a = xp[j];
-        xb[m][4 * j + 0] = a.x;
-        xb[m][4 * j + 1] = a.y;
-        xb[m][4 * j + 2] = a.z;
-        xb[m][4 * j + 3] = a.w;
+        const uint4 v = xp[j];
+        xb[m][4 * j + 0] = v.x;
+        xb[m][4 * j + 1] = v.y;
+        xb[m][4 * j + 2] = v.z;
+        xb[m][4 * j + 3] = v.w;
       }
     }
-    slice_math(cw, xb, sl * kSlice + lane * F::kChunk);
+  };
+  int sl = sl0 + wu;
+  const int sl_end = min(sl1, t_full);
+  if constexpr (!PF) {
+    for (; sl < sl_end; sl += W) {
+      uint4 cw[RR];
+      uint32_t xb[M][F::kXWords];
+      load_full(cw, xb, sl);
+      slice_math(cw, xb, sl * kSlice + lane * F::kChunk);
+    }
+  } else if (sl < sl_end) {
+    // Every load of the next slice is unconditional inside its block (a load under a
+    // branch would make the compiler wait for it before touching the current slice).
+    uint4 ca[RR], cb[RR];
+    uint32_t xa[M][F::kXWords], xbb[M][F::kXWords];
+    load_full(ca, xa, sl);
+    for (;;) {
+      if (sl + W >= sl_end) {
+        slice_math(ca, xa, sl * kSlice + lane * F::kChunk);
+        sl += W;
+        break;
+      }
+      load_full(cb, xbb, sl + W);
+      slice_math(ca, xa, sl * kSlice + lane * F::kChunk);
+      sl += W;
+      if (sl + W >= sl_end) {
+        slice_math(cb, xbb, sl * kSlice + lane * F::kChunk);
+        sl += W;
+        break;
+      }
+      load_full(ca, xa, sl + W);
+      slice_math(cb, xbb, sl * kSlice + lane * F::kChunk);
+      sl += W;
+    }
   }
   // the ragged last slice, or every slice of a short last tile: general addressing
   for (; sl < sl1; sl += W) {
@@ -458,14 +500,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   y[i] = f32_to_bf16(sc * v);
 }
 
+template <int FMT, int M, int RR>
+void launch_rr(bool pf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
+               const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+  if constexpr (prefetch_allowed(FMT, RR, M)) {
+    if (pf) {
+      gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+      return;
+    }
+  }
+  gemv_kernel<FMT, M, RR, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+}
+
+// rows: 4, 8 or 16, optionally | kGemvPrefetch (checked by the caller)
 template <int FMT, int M>
 wq_status launch_m(int rows, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
                    const uint8_t* zs, const uint16_t* x, uint16_t* y, float* part, int K, int N,
                    hipStream_t st) {
-  switch (rows) {
-    case 4: gemv_kernel<FMT, M, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    case 8: gemv_kernel<FMT, M, 8><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    case 16: gemv_kernel<FMT, M, 16><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+  const bool pf = (rows & kGemvPrefetch) != 0;
+  switch (rows & ~kGemvPrefetch) {
+    case 4: launch_rr<FMT, M, 4>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 8: launch_rr<FMT, M, 8>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 16: launch_rr<FMT, M, 16>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   }
   return WQ_OK;
@@ -475,7 +531,7 @@ template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
                      int waves, int rows, void* ws, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
-  dim3 grid((unsigned)(row_tiles(N) * (R / rows)), split_k);
+  dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
   dim3 block(64 * waves);
   float* part = (float*)ws;
   const uint8_t* qw = (const uint8_t*)w->qweight;
@@ -510,8 +566,11 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
 }
 
 int gemv_max_waves(int fmt, int M, int rows) {
-  if (rows != 4 && rows != 8 && rows != 16) return 0;
-  return max_waves_r(fmt, rows, M);
+  const int rr = rows & ~kGemvPrefetch;
+  const bool pf = (rows & kGemvPrefetch) != 0;
+  if (rr != 4 && rr != 8 && rr != 16) return 0;
+  if (pf && !prefetch_allowed(fmt, rr, M)) return 0;
+  return max_waves_r(fmt, rr, M, pf);
 }
 
 int64_t gemv_slices(int64_t K, int fmt) {

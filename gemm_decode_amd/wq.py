@@ -39,6 +39,7 @@ TUNE_LAT_SLOTS = 12                      # WQ_TUNE_LAT_SLOTS: entries wq_tune wr
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)
+GEMV_PREFETCH = 0x100                    # WQ_GEMV_PREFETCH: rows flag, slice prefetch
 
 
 def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:

@@ -181,13 +181,20 @@ wq_status wq_gemv(const wq_weight* w, const void* x, int64_t M, void* y, int spl
  * of two <= min(32, number of slices).  -1 for an invalid format or K. */
 int wq_gemv_max_split(int fmt, int64_t K);
 
+/* rows flag of wq_gemv_ex / wq_gemv_max_waves: each wave loads its next K slice while
+ * it multiplies the current one (a second register set; offered where that set is
+ * small: 4 * rows + M * (8 for int8, 16 for uint4) <= 48). */
+#define WQ_GEMV_PREFETCH 0x100
+
 /* Largest waves per GEMV workgroup for a format, 1 <= M <= 7 and rows per wave (4, 8
- * or 16) (host only): the register budget per lane shrinks as a workgroup grows, so
- * larger M and more rows allow fewer waves.  -1 for an invalid argument. */
+ * or 16, optionally | WQ_GEMV_PREFETCH) (host only): the register budget per lane
+ * shrinks as a workgroup grows, so larger M and more rows allow fewer waves.  -1 for
+ * an invalid argument or a prefetch flag that is not offered. */
 int wq_gemv_max_waves(int fmt, int64_t M, int rows);
 
 /* wq_gemv with the work decomposition explicit: split_k >= 1 as above; rows: output
- * rows per wave, 4, 8 or 16 (0 = the default for the shape); waves per workgroup: 0
+ * rows per wave, 4, 8 or 16, optionally | WQ_GEMV_PREFETCH (0 = the default for the
+ * shape; a prefetch flag that is not offered: WQ_ERR_UNSUPPORTED); waves per workgroup: 0
  * (the default: one K slice per wave, as many as the registers allow) or
  * 1..wq_gemv_max_waves(fmt, M, rows) (else WQ_ERR_UNSUPPORTED).  For tests and
  * tuning. */
@@ -250,7 +257,8 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
 /* Tuner cache: entries keyed by (device tag, format, K, N, M, kind), where the
  * device tag is "<gcnArchName>:<compute units>" of the device the entry was tuned
  * on ("" in set/get = the current device).  A GEMV value is split_k | (waves << 8) |
- * (rows << 16) (waves or rows 0 = the default for the shape); a GEMM value is a
+ * (rows << 16), rows possibly | WQ_GEMV_PREFETCH (waves or rows 0 = the default for
+ * the shape); a GEMM value is a
  * tile id.  get returns WQ_OK and the value, or
  * WQ_ERR_INVALID_ARG when absent.  save/load use a plain text file, one entry per
  * line; load merges into the cache and fails with WQ_ERR_CACHE_IO (leaving the

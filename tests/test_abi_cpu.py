@@ -76,6 +76,17 @@ def test_gemv_max_waves(wqlib):
         assert wqlib.wq_gemv_max_waves(fmt, 1, 4) == 16
     assert wqlib.wq_gemv_max_waves("w8pc", 0, 4) == -1 and wqlib.wq_gemv_max_waves("w8pc", 8, 4) == -1
     assert wqlib.wq_gemv_max_waves(9, 1, 4) == -1 and wqlib.wq_gemv_max_waves("w8pc", 1, 5) == -1
+    # the slice-prefetch flag: offered while 4 * rows + M * (8 int8 / 16 uint4 x words) <= 48
+    pf = wqlib.GEMV_PREFETCH
+    for fmt, xw in (("w8pc", 8), ("w8g128", 8), ("w4g128", 16)):
+        for rows in (4, 8, 16):
+            for m in range(1, 8):
+                cap = wqlib.wq_gemv_max_waves(fmt, m, rows | pf)
+                offered = 4 * rows + m * xw <= 48
+                assert (cap > 0) == offered, (fmt, rows, m, cap)
+                if offered:
+                    assert cap <= wqlib.wq_gemv_max_waves(fmt, m, rows)
+    assert wqlib.wq_gemv_max_waves("w8pc", 1, pf) == -1                     # flag without rows
 
 
 def test_dispatch_threshold(wqlib):
@@ -152,6 +163,8 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 17, 0, None, 0, None) == 1  # waves > 16
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 5, None, 0, None) == 1   # rows not 4/8/16
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, 0, None, 0, None) == 1   # split must be given
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 0x100, None, 0, None) == 1   # prefetch without rows
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x100, None, 0, None) == 2  # prefetch not offered
     dc = _desc(wqlib, layout=0)
     assert L.wq_gemv(C.byref(dc), x, 1, y, 1, None, 0, None) == 2           # canonical layout
     dq = _desc(wqlib, q=0x1004)
@@ -185,4 +198,5 @@ def test_binding_constants_match_the_header(wqlib):
     defs = dict(re.findall(r"#define (WQ_[A-Z_]+) (\d+)", hdr))
     assert int(defs["WQ_GEMM_TILES"]) == wq.GEMM_TILES
     assert int(defs["WQ_TUNE_LAT_SLOTS"]) == wq.TUNE_LAT_SLOTS
+    assert int(re.search(r"#define WQ_GEMV_PREFETCH (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_PREFETCH
     assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))

@@ -39,6 +39,16 @@ def _run_gemv(wq, g, x_bits, split):
     return bf16_bits(y)
 
 
+def _rows_options(wq, fmt, M):
+    """Rows per wave, each also with the slice-prefetch flag where it is offered."""
+    out = []
+    for rows in wq.ROWS_GRID:
+        out.append(rows)
+        if wq.wq_gemv_max_waves(fmt, M, rows | wq.GEMV_PREFETCH) > 0:
+            out.append(rows | wq.GEMV_PREFETCH)
+    return out
+
+
 def _run_gemm(wq, g, x_bits, tile=0):
     M = x_bits.shape[0]
     x = to_dev_bf16(x_bits)
@@ -140,7 +150,7 @@ def test_gemv_every_split_and_waves(wq, fmt, K, N):
         x = to_dev_bf16(xb)
         ws = wq.workspace(wq.wq_workspace_size(g, M))
         for split in _allowed_splits(fmt, K):
-            for rows in wq.ROWS_GRID:
+            for rows in _rows_options(wq, fmt, M):
                 cap = wq.wq_gemv_max_waves(fmt, M, rows)
                 for waves in sorted(set(v for v in (1, 2, 3, 5, cap) if v <= cap)):
                     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
@@ -190,7 +200,7 @@ def test_one_hot_is_exact(wq, fmt):
         assert np.array_equal(_run_gemv(wq, g, x, split), want), f"gemv split={split}"
     xd = to_dev_bf16(x)
     ws = wq.workspace(wq.wq_workspace_size(g, len(ks)))
-    for rows in wq.ROWS_GRID:
+    for rows in _rows_options(wq, fmt, len(ks)):
         for waves in range(1, wq.wq_gemv_max_waves(fmt, len(ks), rows) + 1):
             for split in (1, 2):
                 y = torch.empty((len(ks), N), dtype=torch.bfloat16, device=DEV)
@@ -366,7 +376,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert chosen in SPLITS and chosen <= smax
     assert all((v > 0) == (s <= smax) for s, v in zip(SPLITS, lat)), lat
     v = wq.wq_tune_cache_get("w8pc", K, N, 1, 0)
-    assert v & 0xFF == chosen and 1 <= (v >> 8) & 0xFF <= 16 and (v >> 16) in wq.ROWS_GRID
+    assert v & 0xFF == chosen and 1 <= (v >> 8) & 0xFF <= 16 and (v >> 16) & 0xFF in wq.ROWS_GRID
     p = str(tmp_path / "cache.txt")
     wq.wq_tune_cache_save(p)
     assert f" 0 {K} {N} 1 0 {v}" in open(p).read()
