@@ -49,6 +49,7 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int R = kGemvTileRows;  // rows per workgroup tile (16)
 
@@ -222,14 +223,17 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     };
     auto zero_of = [&](int r) -> uint32_t { return ((r < 8 ? zw : zw_hi) >> (4 * (r & 7))) & 0xFu; };
 
-    // any |x| >= 512 in this slice?  (a bf16 exponent field >= 136 carries into bit
-    // 15 of its half when 0x3C00 is added)
-    uint32_t big = 0;
+    // any |x| >= 512 in this slice?  With the sign cleared, a bf16 bit pattern orders
+    // like its magnitude, and 512 is 0x4400 (Inf and NaN lie above): a packed 16-bit
+    // running maximum over the slice's x words, then one comparison per half.
+    u16x2_t mx = {0, 0};
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int i = 0; i < F::kXWords; ++i) big |= ((xb[m][i] & 0x7F807F80u) + 0x3C003C00u) & 0x80008000u;
-    const bool exact_path = __builtin_amdgcn_ballot_w64(big != 0) != 0;
+      for (int i = 0; i < F::kXWords; ++i)
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xb[m][i] & 0x7FFF7FFFu));
+    const bool big = mx.x >= 0x4400 || mx.y >= 0x4400;
+    const bool exact_path = __builtin_amdgcn_ballot_w64(big) != 0;
 
     if constexpr (!kW4) {
       // ---- int8
