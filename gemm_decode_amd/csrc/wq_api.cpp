@@ -55,14 +55,23 @@ static_assert(WQ_GEMM_TILES <= WQ_TUNE_LAT_SLOTS && 6 <= WQ_TUNE_LAT_SLOTS,
               "wq_tune writes one lat_us slot per GEMM tile or GEMV split");
 
 // Tuned GEMV choice: split_k in bits 0..7, waves per workgroup in bits 8..15, rows per
-// wave in bits 16..23 (0 = the default for the shape) and the slice-prefetch flag in
-// bit 24 (rows | WQ_GEMV_PREFETCH, shifted like rows).
+// wave in bits 16..23 (0 = the default for the shape), the slice-prefetch flag in bit
+// 24 and the matrix-core flag in bit 25 (rows | WQ_GEMV_PREFETCH / WQ_GEMV_MFMA,
+// shifted like rows).
 int gemv_value(int split, int waves, int rows) { return split | (waves << 8) | (rows << 16); }
+// rows argument of the GEMV: 0, 4, 8 or 16 (optionally | prefetch) or 16 NB | mfma
+bool valid_gemv_rows(int rows) {
+  if (rows & kGemvMfma) {
+    const int rr = rows & ~kGemvMfma;
+    return rr == 16 || rr == 32 || rr == 64;
+  }
+  const int rr = rows & ~kGemvPrefetch;
+  return (rr == 0 || rr == 4 || rr == 8 || rr == 16) && !((rows & kGemvPrefetch) && rr == 0);
+}
 bool valid_gemv_value(int v) {
-  const int split = v & 0xFF, waves = (v >> 8) & 0xFF, rows = (v >> 16) & 0xFF;
-  const bool pf = (v >> 24) & 1;
-  return (v >> 25) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves &&
-         (rows == 0 || rows == 4 || rows == 8 || rows == 16) && !(pf && rows == 0);
+  const int split = v & 0xFF, waves = (v >> 8) & 0xFF;
+  return (v >> 26) == 0 && pow2(split) && split <= kMaxSplit && waves <= kGemvMaxWaves &&
+         valid_gemv_rows((v >> 16) & (0xFF | kGemvPrefetch | kGemvMfma));
 }
 
 std::string resolve_tag(const char* tag) {
@@ -108,7 +117,7 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
   if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMV, &v)) {
     *split = v & 0xFF;
     *waves = (v >> 8) & 0xFF;
-    *rows = (v >> 16) & (0xFF | kGemvPrefetch);
+    *rows = (v >> 16) & (0xFF | kGemvPrefetch | kGemvMfma);
     return;
   }
   *split = clamp_split(kDefaultSplit, split_units(w));
@@ -145,12 +154,12 @@ wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int s
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves)
     return fail(WQ_ERR_INVALID_ARG, "wq_gemv: waves per workgroup must be 0 (default) or 1..16");
-  const int rr = rows & ~kGemvPrefetch;
-  if ((rr != 0 && rr != 4 && rr != 8 && rr != 16) || (rows & kGemvPrefetch && rr == 0))
+  if (!valid_gemv_rows(rows))
     return fail(WQ_ERR_INVALID_ARG,
-                "wq_gemv: rows per wave must be 0 (default), 4, 8 or 16 (optionally | WQ_GEMV_PREFETCH)");
-  if (rows & kGemvPrefetch && gemv_max_waves(w->fmt, (int)M, rows) == 0)
-    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: slice prefetch is not offered at this format, M and rows");
+                "wq_gemv: rows per wave must be 0 (default), 4, 8 or 16 (optionally | WQ_GEMV_PREFETCH), "
+                "or 16, 32, 64 or 128 | WQ_GEMV_MFMA");
+  if (rows & (kGemvPrefetch | kGemvMfma) && gemv_max_waves(w->fmt, (int)M, rows) == 0)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: this rows flag is not offered at this format, M and rows");
   int split = split_k, wv = waves, rw = rows;
   if (split_k == 0) {
     int tw = 0, tr = 0;
@@ -404,14 +413,14 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   if (gemv) {
     const int fmt = copies[0].fmt;
     for (int s = 1; s <= kMaxSplit; s *= 2)
-      for (int rr = 4; rr <= 16; rr *= 2)
-        for (const int rw : {rr, rr | kGemvPrefetch}) {
-          const int cap = gemv_max_waves(fmt, (int)M, rw);
-          if (cap == 0) continue;  // prefetch not offered here
-          const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
-          for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, rw, 0});
-          if (dflt & (dflt - 1)) cand.push_back({s, dflt, rw, 0});  // the default when not a power of two
-        }
+      for (const int rw : {4, 8, 16, 4 | kGemvPrefetch, 8 | kGemvPrefetch, 16 | kGemvPrefetch,
+                           16 | kGemvMfma, 32 | kGemvMfma, 64 | kGemvMfma}) {
+        const int cap = gemv_max_waves(fmt, (int)M, rw);
+        if (cap == 0) continue;  // flag not offered at this format and M
+        const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
+        for (int wv = 1; wv <= cap; wv *= 2) cand.push_back({s, wv, rw, 0});
+        if (dflt & (dflt - 1)) cand.push_back({s, dflt, rw, 0});  // the default when not a power of two
+      }
   } else {
     for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, 0, t});
   }

@@ -17,6 +17,7 @@ constexpr int kGemvTileRows = 16;    // output rows per GEMV workgroup tile (and
                                      // gfx950 metadata tile of the group-128 formats)
 constexpr int kGemvMaxWaves = 16;    // waves per GEMV workgroup (intra-workgroup K split)
 constexpr int kGemvPrefetch = WQ_GEMV_PREFETCH;  // "rows" flag: slice prefetch
+constexpr int kGemvMfma = WQ_GEMV_MFMA;          // "rows" flag: matrix-core GEMV (uint4)
 
 // Thread-local error text behind wq_last_error().
 void set_error(const std::string& msg);
@@ -71,8 +72,8 @@ wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y,
 int gemv_default_rows(int64_t K, int64_t N, int fmt, int M);
 int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int rows);
 // Largest waves per GEMV workgroup that fits the registers at this format, M and
-// rows per wave (4, 8 or 16, optionally | kGemvPrefetch); 0 for any other rows value
-// and for the prefetch flag where it is not offered.
+// rows per wave (4, 8 or 16, optionally | kGemvPrefetch; 16, 32 or 64 |
+// kGemvMfma); 0 for any other rows value and for a flag where it is not offered.
 int gemv_max_waves(int fmt, int M, int rows);
 // K slices of the GEMV (64 lanes x one 16-byte chunk: 1024 k int8, 2048 k uint4);
 // split-K ranges are whole slices.

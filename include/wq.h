@@ -186,15 +186,24 @@ int wq_gemv_max_split(int fmt, int64_t K);
  * small: 4 * rows + M * (8 for int8, 16 for uint4) <= 48). */
 #define WQ_GEMV_PREFETCH 0x100
 
+/* rows flag of wq_gemv_ex / wq_gemv_max_waves, uint4 group-128 only: the matrix-core
+ * GEMV.  rows = 16 * NB | WQ_GEMV_MFMA with NB in {1, 2, 4} 16-row tiles per
+ * workgroup; its 1..8 waves interleave over the 128-groups of the workgroup's K range
+ * and multiply on v_mfma_f32_16x16x32 (bf16 and fp16) with exact code values; the
+ * fp32 partial sums meet in LDS in wave order.  Other formats: WQ_ERR_UNSUPPORTED. */
+#define WQ_GEMV_MFMA 0x200
+
 /* Largest waves per GEMV workgroup for a format, 1 <= M <= 7 and rows per wave (4, 8
- * or 16, optionally | WQ_GEMV_PREFETCH) (host only): the register budget per lane
- * shrinks as a workgroup grows, so larger M and more rows allow fewer waves.  -1 for
- * an invalid argument or a prefetch flag that is not offered. */
+ * or 16, optionally | WQ_GEMV_PREFETCH; or 16, 32, 64 | WQ_GEMV_MFMA) (host
+ * only): the register budget per lane shrinks as a workgroup grows, so larger M and
+ * more rows allow fewer waves.  -1 for an invalid argument or a flag that is not
+ * offered at this format, M and rows. */
 int wq_gemv_max_waves(int fmt, int64_t M, int rows);
 
 /* wq_gemv with the work decomposition explicit: split_k >= 1 as above; rows: output
- * rows per wave, 4, 8 or 16, optionally | WQ_GEMV_PREFETCH (0 = the default for the
- * shape; a prefetch flag that is not offered: WQ_ERR_UNSUPPORTED); waves per workgroup: 0
+ * rows per wave, 4, 8 or 16, optionally | WQ_GEMV_PREFETCH, or the matrix-core GEMV
+ * (16, 32 or 64 | WQ_GEMV_MFMA) (0 = the default for the shape; a flag that is
+ * not offered: WQ_ERR_UNSUPPORTED); waves per workgroup: 0
  * (the default: one K slice per wave, as many as the registers allow) or
  * 1..wq_gemv_max_waves(fmt, M, rows) (else WQ_ERR_UNSUPPORTED).  For tests and
  * tuning. */
@@ -257,7 +266,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
 /* Tuner cache: entries keyed by (device tag, format, K, N, M, kind), where the
  * device tag is "<gcnArchName>:<compute units>" of the device the entry was tuned
  * on ("" in set/get = the current device).  A GEMV value is split_k | (waves << 8) |
- * (rows << 16), rows possibly | WQ_GEMV_PREFETCH (waves or rows 0 = the default for
+ * (rows << 16), rows possibly | WQ_GEMV_PREFETCH or WQ_GEMV_MFMA (waves or rows 0 = the default for
  * the shape); a GEMM value is a
  * tile id.  get returns WQ_OK and the value, or
  * WQ_ERR_INVALID_ARG when absent.  save/load use a plain text file, one entry per

@@ -87,6 +87,16 @@ def test_gemv_max_waves(wqlib):
                 if offered:
                     assert cap <= wqlib.wq_gemv_max_waves(fmt, m, rows)
     assert wqlib.wq_gemv_max_waves("w8pc", 1, pf) == -1                     # flag without rows
+    # the matrix-core GEMV: uint4 group-128 only, 16 NB rows with NB in 1, 2, 4
+    mf = wqlib.GEMV_MFMA
+    for m in range(1, 8):
+        for rows in (16, 32, 64):
+            assert wqlib.wq_gemv_max_waves("w4g128", m, rows | mf) == 8
+            assert wqlib.wq_gemv_max_waves("w8pc", m, rows | mf) == -1
+            assert wqlib.wq_gemv_max_waves("w8g128", m, rows | mf) == -1
+    for rows in (0, 4, 8, 48, 128, 256):
+        assert wqlib.wq_gemv_max_waves("w4g128", 1, rows | mf) == -1
+    assert wqlib.wq_gemv_max_waves("w4g128", 1, 16 | mf | pf) == -1
 
 
 def test_dispatch_threshold(wqlib):
@@ -165,6 +175,9 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, 0, None, 0, None) == 1   # split must be given
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 0x100, None, 0, None) == 1   # prefetch without rows
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x100, None, 0, None) == 2  # prefetch not offered
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x200, None, 0, None) == 2  # matrix-core GEMV: uint4 only
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 8 | 0x200, None, 0, None) == 1   # not 16 NB rows
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x300, None, 0, None) == 1  # both flags
     dc = _desc(wqlib, layout=0)
     assert L.wq_gemv(C.byref(dc), x, 1, y, 1, None, 0, None) == 2           # canonical layout
     dq = _desc(wqlib, q=0x1004)
@@ -199,4 +212,5 @@ def test_binding_constants_match_the_header(wqlib):
     assert int(defs["WQ_GEMM_TILES"]) == wq.GEMM_TILES
     assert int(defs["WQ_TUNE_LAT_SLOTS"]) == wq.TUNE_LAT_SLOTS
     assert int(re.search(r"#define WQ_GEMV_PREFETCH (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_PREFETCH
+    assert int(re.search(r"#define WQ_GEMV_MFMA (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_MFMA
     assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))

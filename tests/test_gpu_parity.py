@@ -40,12 +40,16 @@ def _run_gemv(wq, g, x_bits, split):
 
 
 def _rows_options(wq, fmt, M):
-    """Rows per wave, each also with the slice-prefetch flag where it is offered."""
+    """Rows per wave, each also with the slice-prefetch flag where it is offered, and
+    the matrix-core GEMV's tiles per workgroup where it is offered."""
     out = []
     for rows in wq.ROWS_GRID:
         out.append(rows)
         if wq.wq_gemv_max_waves(fmt, M, rows | wq.GEMV_PREFETCH) > 0:
             out.append(rows | wq.GEMV_PREFETCH)
+    for rows in (16, 32, 64):
+        if wq.wq_gemv_max_waves(fmt, M, rows | wq.GEMV_MFMA) > 0:
+            out.append(rows | wq.GEMV_MFMA)
     return out
 
 
@@ -183,6 +187,33 @@ def test_gemm_small(wq, fmt, K, N, M):
         assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
 
 
+EDGE = [("w8pc", 16, 8), ("w4g128", 128, 8), ("w8g128", 128, 24), ("w8pc", 64, 17),
+        ("w8pc", 2176, 300), ("w8pc", 4160, 272), ("w4g128", 2176, 136)]
+
+
+@pytest.mark.parametrize("fmt,K,N", EDGE)
+def test_edge_shapes_every_path(wq, fmt, K, N):
+    """Boundary shapes on every path: minimum K and N, a short last 16-row tile, a lone
+    row in it, a ragged 1 KB slice, DMA K steps that leave 1 or 2 steps after the
+    three-step loop, and M at the edges of the 16-, 32-, 128- and 256-row tiles."""
+    W = synth.weight(96, K, N, synth.uses_outliers(fmt))
+    g, can = quantize_on_gpu(wq, W, fmt)
+    P = OQ.pack(fmt, W)
+    for M in (1, 5, 7, 8, 16, 17, 33, 64, 128, 129, 257):
+        x = synth.activation(96, K, M)
+        y_ref = OL.ref_linear(x, P)
+        if M < 8:
+            for split in [0] + _allowed_splits(fmt, K):
+                assert_parity(_run_gemv(wq, g, x, split), y_ref, f"gemv {fmt} K={K} N={N} M={M} split={split}")
+        for tile in range(1, wq.GEMM_TILES + 1):
+            assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
+        yl = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        ws = wq.workspace(wq.wq_workspace_size(g, M))
+        wq.wq_linear(g, to_dev_bf16(x), yl, ws=ws)
+        torch.cuda.synchronize()
+        assert_parity(bf16_bits(yl), y_ref, f"linear {fmt} K={K} N={N} M={M}")
+
+
 # ---------------------------------------------------------- exact special inputs
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_one_hot_is_exact(wq, fmt):
@@ -262,6 +293,14 @@ def test_gemv_with_large_and_tiny_activations(wq, fmt):
     y_ref = OL.ref_linear(x, P)
     for split in _allowed_splits(fmt, K)[:3]:
         assert_parity(_run_gemv(wq, g, x, split), y_ref, f"{fmt} large-x split={split}")
+    # the matrix-core GEMV takes the same switch per 128-group
+    xd = to_dev_bf16(x)
+    for rows in (16 | wq.GEMV_MFMA, 64 | wq.GEMV_MFMA):
+        if wq.wq_gemv_max_waves(fmt, 4, rows) > 0:
+            y = torch.empty((4, N), dtype=torch.bfloat16, device=DEV)
+            wq.wq_gemv_ex(g, xd, y, 1, 4, rows, ws=None)
+            torch.cuda.synchronize()
+            assert_parity(bf16_bits(y), y_ref, f"{fmt} large-x rows={rows}")
 
 
 def test_all_zero_rows_give_zero(wq):
