@@ -510,29 +510,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------------
-// Matrix-core GEMV for uint4 group-128 (launch option: rows = 16 NB | kGemvMfma).
+// Matrix-core GEMV (launch option: rows = 16 NB | kGemvMfma).
 //
 // The multiply-adds of the decode GEMV go to v_mfma_f32_16x16x32 (bf16 and fp16)
-// instead of v_dot2, which leaves the VALU only the nibble extraction and one
-// fold per group.  Operand layouts of the 16x16x32 matrix instructions: lane l holds
-// A[row l % 16][k 8 (l / 16) .. +7] and B[k 8 (l / 16) .. +7][column l % 16] and
-// receives D[rows 4 (l / 16) .. +3][column l % 16].  Here A is x (row = token, rows
-// >= M are don't-care) and B is 16 weight rows of one gfx950 tile, so lane l reads
-// the codes of tile row l % 16: for group g, the 16 bytes at 64 (g % 16) + 16 (l / 16)
-// of its 1 KB row slice (k = 128 g + 32 (l / 16) .. +31, four 8-code words), and x
-// at the same k.  The contraction index of each instruction is a permutation of the
-// group's k, the same for A and B.
+// instead of v_dot2, which leaves the VALU the code extraction and, for group-128,
+// one fold per group; the cost no longer grows with the token count M.  Operand
+// layouts of the 16x16x32 matrix instructions: lane l holds A[row l % 16][k 8 (l / 16)
+// .. +7] and B[k 8 (l / 16) .. +7][column l % 16] and receives D[rows 4 (l / 16) .. +3]
+// [column l % 16].  Here A is x (row = token; rows >= M repeat token M - 1 and their
+// D rows are never read) and B is 16 weight rows of one gfx950 tile.  K is walked in
+// units of 128 k (a group of the group-128 formats): lane l takes k = 32 (l / 16) ..
+// +31 of the unit in tile row l % 16 -- 16 code bytes (uint4: at 64 u' + 16 (l / 16)
+// of its 1 KB row slice, u' the unit within the slice) or 32 (int8: at 128 u' + 32 (l
+// / 16)) -- and x at the same k; instruction s (0..3) of a unit contracts k = 32 (l /
+// 16) + 8 s + 0..7 in A and B alike.
 //
-// Codes become exact small numbers in one v_and_or_b32 each: a word's nibble pairs
-// at bits (0, 16) and, after one shift by 8, (8, 24) under the bf16 128.0 pattern give
-// bf16 (128 + q); the pairs at bits (4, 20) and (12, 28) under the fp16 64.0 pattern
-// give fp16 (64 + q) directly (their low nibble bits stay clear).  The bf16 halves
-// multiply bf16 x, the fp16 halves x converted to fp16, all into one fp32 accumulator
-// that starts from -(128 X_lo + 64 X_hi) - z X (X: group sums of x, from two more
-// matrix products against constant B), so after the group's four products it holds
-// sum x (q - z) and is scaled by the group scale.  The offsets are at most those of
-// the dot2 path (128 + 15), so the same |x| < 512 condition bounds the cancellation;
-// a group whose x has some |x| >= 512 takes exact bf16 (q - z) codes.
+// Codes become exact small numbers: int8 (stored u = q + 128) by v_perm_b32 under the
+// fp16 exponent byte 0x64 (fp16 1024 + u, as in the dot2 path) against x converted
+// to fp16; uint4 in one v_and_or_b32 per pair: the pairs at bits (0, 16) and, after a
+// shift by 8, (8, 24) under the bf16 128.0 pattern give bf16 (128 + q) against bf16
+// x, the pairs at bits (4, 20) and (12, 28) under the fp16 64.0 pattern give fp16 (64
+// + q) (their low nibble bits stay clear) against fp16 x.  The offsets leave the
+// products as sums of x times constants, taken out with matrix products of the same A
+// against constant B: int8 per-channel accumulates x sums over all of K and removes
+// 1152 sum(x) at the end; group-128 starts each group's accumulator at -(offset + z)
+// times the group's x sums, scales it by the group scale and adds it up.  The
+// offsets equal those of the dot2 path, so the same |x| < 512 condition bounds the
+// cancellation; a unit whose x has some |x| >= 512 takes exact bf16 codes (q or q - z)
+// against bf16 x.  A ragged last unit (int8 with K % 128 != 0) masks the lanes past K.
 constexpr int kMmaMaxWaves = 8;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -548,12 +553,22 @@ __device__ __forceinline__ f32x4_t mma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
+// exact bf16 pairs of four signed codes stored as u = q + 128
+__device__ __forceinline__ void i8_word_to_bf16(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  d ^= 0x80808080u;
+  lo = pack_bf16x2((float)(int8_t)(d & 0xFFu), (float)(int8_t)((d >> 8) & 0xFFu));
+  hi = pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24));
+}
 
-template <int M, int NB>
-__global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_w4_kernel(
+template <int FMT, int M, int NB>
+__global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part, int K, int N) {
-  constexpr int MI = M < 4 ? M : 4;  // accumulator rows a lane keeps (token 4 (l / 16) + i, i < MI)
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
+  constexpr int MI = M < 4 ? M : 4;             // accumulator rows a lane keeps (token 4 (l / 16) + i, i < MI)
+  constexpr int kUnitBytes = kW4 ? 64 : 128;    // code bytes per row and 128-k unit
+  constexpr int kUnitsPerSlice = kSliceBytes / kUnitBytes;
+  constexpr int CL = kW4 ? 1 : 2;               // 16-byte code loads per lane, tile and unit
   __shared__ float red[kMmaMaxWaves][NB][M][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
@@ -561,12 +576,12 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_w4_kernel(
   const int T16 = (N + 15) >> 4;
   const int tile0 = blockIdx.x * NB;
   const int s = blockIdx.y, S = gridDim.y;
-  const int G = K / kGroup;
-  const int g0 = (int)((int64_t)s * G / S), g1 = (int)((int64_t)(s + 1) * G / S);
-  const uint32_t row_bytes = (uint32_t)K / 2;
+  const int U = (K + kGroup - 1) / kGroup, G = K / kGroup;
+  const int u0 = (int)((int64_t)s * U / S), u1 = (int)((int64_t)(s + 1) * U / S);
+  const uint32_t row_bytes = kW4 ? (uint32_t)K / 2 : (uint32_t)K;
 
-  // Per tile: wave-uniform bases (codes, scales, zero-points) and this lane's row.
-  // Loads take a uniform base plus a 32-bit lane offset.
+  // Per tile: wave-uniform bases (codes, group scales, zero-points) and this lane's
+  // row.  Loads take a uniform base plus a 32-bit lane offset.
   const uint8_t* tbase[NB];
   const uint8_t* sbase[NB];
   const uint8_t* zbase[NB];
@@ -576,51 +591,76 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_w4_kernel(
     const int tt = min(tile0 + t, T16 - 1);  // tiles past the end repeat the last (not stored)
     const int nr = min(16, N - 16 * tt);
     tbase[t] = qw + (size_t)tt * 16 * row_bytes;
-    sbase[t] = reinterpret_cast<const uint8_t*>(scales + (size_t)tt * G * 16);
-    zbase[t] = zeros + (size_t)tt * G * 8;
+    sbase[t] = reinterpret_cast<const uint8_t*>(scales + (kGrouped ? (size_t)tt * G * 16 : 0));
+    zbase[t] = kW4 ? zeros + (size_t)tt * G * 8 : nullptr;
     nr1k[t] = (uint32_t)nr * kSliceBytes;
     rsel[t] = min(ln, (uint32_t)nr - 1u);
   }
-  // x rows (tokens) past M are loaded again from token M - 1: those A rows only feed
-  // D rows that are never read, and the |x| check sees real tokens only.
   const uint8_t* xb8 = reinterpret_cast<const uint8_t*>(x);
-  const uint32_t xlane = min(ln, (uint32_t)M - 1u) * (uint32_t)K * 2u + 64u * lk;  // byte offset of this lane's x
+  const uint32_t xrow = min(ln, (uint32_t)M - 1u) * (uint32_t)K * 2u;  // byte offset of this lane's token
   const uint32_t zshift = 4 * (ln & 1);
   uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_b = 0x43004300u, mag_h = 0x54005400u;
-  asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_b), "+v"(mag_h));
+  if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_b), "+v"(mag_h));
   const u32x4_t one_b = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const u32x4_t one_h = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
 
-  f32x4_t acc[NB];
+  f32x4_t acc[NB];  // group-128: scaled sums; per-channel: raw sums incl. offsets
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t xs_all = {0.f, 0.f, 0.f, 0.f};  // per-channel: x sums of the offset units
 
-  // One 128-group's operands: codes of the NB tiles, x, scales and zero-points.
-  struct Set {  // 32-bit fields only, so that the set stays in registers
-    u32x4_t c[NB];
+  // One unit's operands (32-bit fields only, so that the set stays in registers).
+  struct Set {
+    u32x4_t c[NB][CL];
     uint4 xv[4];
     uint32_t sv[NB], zb[NB];
   };
-  auto load = [&](Set& st, int g) {
-    const uint32_t sl = (uint32_t)g >> 4, gi = (uint32_t)g & 15u;
+  auto load = [&](Set& st, int u) {
+    const uint32_t sl = (uint32_t)u / kUnitsPerSlice, ui = (uint32_t)u % kUnitsPerSlice;
     const uint32_t wsl = min((uint32_t)kSliceBytes, row_bytes - (uint32_t)kSliceBytes * sl);
+    const uint32_t k0 = 128u * (uint32_t)u + 32u * lk;  // this lane's first k
+    if (kW4 || 128 * (u + 1) <= K) {                     // a whole unit (wave-uniform)
 #pragma unroll
-    for (int t = 0; t < NB; ++t)
-      st.c[t] = __builtin_bit_cast(u32x4_t, load_stream16(tbase[t] + (nr1k[t] * sl + 64u * gi) +
-                                                          (__umul24(rsel[t], wsl) + 16u * lk)));
-    const uint4* xp = reinterpret_cast<const uint4*>(xb8 + (xlane + 256u * (uint32_t)g));
+      for (int t = 0; t < NB; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.xv[j] = xp[j];
-    const uint32_t soff = 32u * (uint32_t)g + 2u * ln, zoff = 8u * (uint32_t)g + (ln >> 1);
+        for (int c = 0; c < CL; ++c)
+          st.c[t][c] = __builtin_bit_cast(
+              u32x4_t, load_stream16(tbase[t] + nr1k[t] * sl +
+                                     (__umul24(rsel[t], wsl) + kUnitBytes * ui + (kW4 ? 16u : 32u) * lk + 16u * c)));
+      const uint4* xp = reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * k0));
 #pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      st.sv[t] = *reinterpret_cast<const uint16_t*>(sbase[t] + soff);
-      st.zb[t] = zbase[t][zoff];
+      for (int j = 0; j < 4; ++j) st.xv[j] = xp[j];
+    } else {
+      // the ragged last unit: chunks past K load any in-bounds chunk, their x is zero
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int c = 0; c < CL; ++c) {
+          const bool ok = k0 + 16u * c + 16u <= (uint32_t)K;
+          const uint32_t off = ok ? kUnitBytes * ui + 32u * lk + 16u * c : 0u;
+          st.c[t][c] = __builtin_bit_cast(u32x4_t, load_stream16(tbase[t] + nr1k[t] * sl +
+                                                                 (__umul24(rsel[t], wsl) + off)));
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = k0 + 8u * j;
+        const bool ok = k + 8u <= (uint32_t)K;
+        const uint4 v = *reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * (ok ? k : 0u)));
+        st.xv[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if constexpr (kGrouped) {
+      const uint32_t soff = 32u * (uint32_t)u + 2u * ln, zoff = 8u * (uint32_t)u + (ln >> 1);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        st.sv[t] = *reinterpret_cast<const uint16_t*>(sbase[t] + soff);
+        st.zb[t] = kW4 ? zbase[t][zoff] : 0u;
+      }
     }
   };
   auto compute = [&](const Set& st) {
     const uint4 xv[4] = {st.xv[0], st.xv[1], st.xv[2], st.xv[3]};
-    // any |x| >= 512 among the group's x (see the dot2 path)
+    // any |x| >= 512 among the unit's x (see the dot2 path)
     u16x2_t mx = {0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -630,90 +670,147 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_w4_kernel(
       mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xv[j].w & 0x7FFF7FFFu));
     }
     const bool exact = __builtin_amdgcn_ballot_w64(mx.x >= 0x4400 || mx.y >= 0x4400) != 0;
-    const u32x4_t a_lo0 = {xv[0].x, xv[0].z, xv[1].x, xv[1].z};
-    const u32x4_t a_lo1 = {xv[2].x, xv[2].z, xv[3].x, xv[3].z};
+    // group-128: the unit's contribution d[t] to each tile, times the group scale
+    auto fold1 = [&](int t, const f32x4_t& d) {
+      const float sc = kW4 ? f16_to_f32((uint16_t)st.sv[t]) : bf16_to_f32((uint16_t)st.sv[t]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(sc, d[i], acc[t][i]);
+    };
+    auto fold = [&](const f32x4_t (&d)[NB]) {
+#pragma unroll
+      for (int t = 0; t < NB; ++t) fold1(t, d[t]);
+    };
     if (!exact) {
-      const u32x4_t a_hi0 = {bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
-                             bf16x2_to_f16x2(xv[1].w)};
-      const u32x4_t a_hi1 = {bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
-                             bf16x2_to_f16x2(xv[3].w)};
-      // group sums of x over the bf16 and the fp16 halves (every column alike)
-      f32x4_t xs_lo = {0.f, 0.f, 0.f, 0.f}, xs_hi = {0.f, 0.f, 0.f, 0.f};
-      xs_lo = mma_bf16(a_lo0, one_b, xs_lo);
-      xs_hi = mma_f16(a_hi0, one_h, xs_hi);
-      xs_lo = mma_bf16(a_lo1, one_b, xs_lo);
-      xs_hi = mma_f16(a_hi1, one_h, xs_hi);
-      u32x4_t b[4][NB];  // the four B operands of each tile
+      if constexpr (kW4) {
+        const u32x4_t a_lo0 = {xv[0].x, xv[0].z, xv[1].x, xv[1].z};
+        const u32x4_t a_lo1 = {xv[2].x, xv[2].z, xv[3].x, xv[3].z};
+        const u32x4_t a_hi0 = {bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
+                               bf16x2_to_f16x2(xv[1].w)};
+        const u32x4_t a_hi1 = {bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
+                               bf16x2_to_f16x2(xv[3].w)};
+        // group sums of x over the bf16 and the fp16 halves (every column alike)
+        f32x4_t xs_lo = {0.f, 0.f, 0.f, 0.f}, xs_hi = {0.f, 0.f, 0.f, 0.f};
+        xs_lo = mma_bf16(a_lo0, one_b, xs_lo);
+        xs_hi = mma_f16(a_hi0, one_h, xs_hi);
+        xs_lo = mma_bf16(a_lo1, one_b, xs_lo);
+        xs_hi = mma_f16(a_hi1, one_h, xs_hi);
+        u32x4_t b[4][NB];  // the four B operands of each tile
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        uint32_t lo[4], lo8[4], hi[4], hi8[4];
+        for (int t = 0; t < NB; ++t) {
+          uint32_t lo[4], lo8[4], hi[4], hi8[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = st.c[t][q], w8 = w >> 8;
-          lo[q] = (w & m_lo) | mag_b;
-          hi[q] = (w & m_hi) | mag_h;
-          lo8[q] = (w8 & m_lo) | mag_b;
-          hi8[q] = (w8 & m_hi) | mag_h;
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = st.c[t][0][q], w8 = w >> 8;
+            lo[q] = (w & m_lo) | mag_b;
+            hi[q] = (w & m_hi) | mag_h;
+            lo8[q] = (w8 & m_lo) | mag_b;
+            hi8[q] = (w8 & m_hi) | mag_h;
+          }
+          b[0][t] = u32x4_t{lo[0], lo8[0], lo[1], lo8[1]};
+          b[1][t] = u32x4_t{lo[2], lo8[2], lo[3], lo8[3]};
+          b[2][t] = u32x4_t{hi[0], hi8[0], hi[1], hi8[1]};
+          b[3][t] = u32x4_t{hi[2], hi8[2], hi[3], hi8[3]};
         }
-        b[0][t] = u32x4_t{lo[0], lo8[0], lo[1], lo8[1]};
-        b[1][t] = u32x4_t{lo[2], lo8[2], lo[3], lo8[3]};
-        b[2][t] = u32x4_t{hi[0], hi8[0], hi[1], hi8[1]};
-        b[3][t] = u32x4_t{hi[2], hi8[2], hi[3], hi8[3]};
-      }
-      // each tile's accumulator starts at -(128 + z) X_lo - (64 + z) X_hi
-      f32x4_t d[NB];
+        // each tile's accumulator starts at -(128 + z) X_lo - (64 + z) X_hi
+        f32x4_t d[NB];
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const float z = (float)((st.zb[t] >> zshift) & 15u);
+        for (int t = 0; t < NB; ++t) {
+          const float z = (float)((st.zb[t] >> zshift) & 15u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          d[t][i] = i < MI ? fmaf(-(128.f + z), xs_lo[i], -(64.f + z) * xs_hi[i]) : 0.f;
-      }
-      // the four products, tiles interleaved so that no instruction waits for the previous
+          for (int i = 0; i < 4; ++i)
+            d[t][i] = i < MI ? fmaf(-(128.f + z), xs_lo[i], -(64.f + z) * xs_hi[i]) : 0.f;
+        }
+        // the four products, tiles interleaved so that no instruction waits for the previous
 #pragma unroll
-      for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo0, b[0][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo0, b[0][t], d[t]);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo1, b[1][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo1, b[1][t], d[t]);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_hi0, b[2][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_hi0, b[2][t], d[t]);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_hi1, b[3][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_hi1, b[3][t], d[t]);
+        fold(d);
+      } else {
+        u32x4_t a[4];
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const float sc = f16_to_f32((uint16_t)st.sv[t]);
+        for (int j = 0; j < 4; ++j)
+          a[j] = u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
+                         bf16x2_to_f16x2(xv[j].w)};
+        f32x4_t xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(sc, d[t][i], acc[t][i]);
+        for (int j = 0; j < 4; ++j) xs = mma_f16(a[j], one_h, xs);
+        f32x4_t d[NB];
+        if constexpr (kGrouped) {
+#pragma unroll
+          for (int t = 0; t < NB; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[t][i] = i < MI ? -1152.f * xs[i] : 0.f;
+        } else {
+          xs_all += xs;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const uint32_t w0 = st.c[t][j >> 1][2 * (j & 1)], w1 = st.c[t][j >> 1][2 * (j & 1) + 1];
+            const u32x4_t b = {__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u),
+                               __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u),
+                               __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u),
+                               __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)};
+            if constexpr (kGrouped) d[t] = mma_f16(a[j], b, d[t]);
+            else acc[t] = mma_f16(a[j], b, acc[t]);
+          }
+        if constexpr (kGrouped) fold(d);
       }
     } else {
-      // exact path: bf16 (q - z) codes against bf16 x
-      const u32x4_t a_hb0 = {xv[0].y, xv[0].w, xv[1].y, xv[1].w};
-      const u32x4_t a_hb1 = {xv[2].y, xv[2].w, xv[3].y, xv[3].w};
+      // exact path: bf16 codes (q, or q - z) against bf16 x, one tile at a time
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
-        const float z = (float)((st.zb[t] >> zshift) & 15u);
-        auto ex = [&](uint32_t w, int i) {
-          return pack_bf16x2((float)((w >> (4 * i)) & 15u) - z, (float)((w >> (16 + 4 * i)) & 15u) - z);
-        };
-        const uint32_t w0 = st.c[t][0], w1 = st.c[t][1], w2 = st.c[t][2], w3 = st.c[t][3];
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        d = mma_bf16(a_lo0, u32x4_t{ex(w0, 0), ex(w0, 2), ex(w1, 0), ex(w1, 2)}, d);
-        d = mma_bf16(a_lo1, u32x4_t{ex(w2, 0), ex(w2, 2), ex(w3, 0), ex(w3, 2)}, d);
-        d = mma_bf16(a_hb0, u32x4_t{ex(w0, 1), ex(w0, 3), ex(w1, 1), ex(w1, 3)}, d);
-        d = mma_bf16(a_hb1, u32x4_t{ex(w2, 1), ex(w2, 3), ex(w3, 1), ex(w3, 3)}, d);
-        const float sc = f16_to_f32((uint16_t)st.sv[t]);
+        f32x4_t dt = {0.f, 0.f, 0.f, 0.f};  // this tile's partial (group-128)
+        if constexpr (kW4) {
+          const float z = (float)((st.zb[t] >> zshift) & 15u);
+          auto ex = [&](uint32_t w, int i) {
+            return pack_bf16x2((float)((w >> (4 * i)) & 15u) - z, (float)((w >> (16 + 4 * i)) & 15u) - z);
+          };
+          const uint32_t w0 = st.c[t][0][0], w1 = st.c[t][0][1], w2 = st.c[t][0][2], w3 = st.c[t][0][3];
+          const u32x4_t a_lo0 = {xv[0].x, xv[0].z, xv[1].x, xv[1].z};
+          const u32x4_t a_lo1 = {xv[2].x, xv[2].z, xv[3].x, xv[3].z};
+          const u32x4_t a_hb0 = {xv[0].y, xv[0].w, xv[1].y, xv[1].w};
+          const u32x4_t a_hb1 = {xv[2].y, xv[2].w, xv[3].y, xv[3].w};
+          dt = mma_bf16(a_lo0, u32x4_t{ex(w0, 0), ex(w0, 2), ex(w1, 0), ex(w1, 2)}, dt);
+          dt = mma_bf16(a_lo1, u32x4_t{ex(w2, 0), ex(w2, 2), ex(w3, 0), ex(w3, 2)}, dt);
+          dt = mma_bf16(a_hb0, u32x4_t{ex(w0, 1), ex(w0, 3), ex(w1, 1), ex(w1, 3)}, dt);
+          dt = mma_bf16(a_hb1, u32x4_t{ex(w2, 1), ex(w2, 3), ex(w3, 1), ex(w3, 3)}, dt);
+        } else {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(sc, d[i], acc[t][i]);
+          for (int j = 0; j < 4; ++j) {
+            uint32_t b0, b1, b2, b3;
+            i8_word_to_bf16(st.c[t][j >> 1][2 * (j & 1)], b0, b1);
+            i8_word_to_bf16(st.c[t][j >> 1][2 * (j & 1) + 1], b2, b3);
+            const u32x4_t b = {b0, b1, b2, b3};
+            const u32x4_t a = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+            if constexpr (kGrouped) dt = mma_bf16(a, b, dt);
+            else acc[t] = mma_bf16(a, b, acc[t]);
+          }
+        }
+        if constexpr (kGrouped) fold1(t, dt);
       }
     }
   };
 
-  // A wave's groups g0 + wave, + W, ...  (Loading the next group's operands during the
+  // A wave's units u0 + wave, + W, ...  (Loading the next unit's operands during the
   // current one's products measured slower on MI355X: the second operand set halves
   // the resident waves.)
-  for (int g = g0 + wu; g < g1; g += W) {
+  for (int u = u0 + wu; u < u1; u += W) {
     Set st;
-    load(st, g);
+    load(st, u);
     compute(st);
+  }
+  if constexpr (!kGrouped) {
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(-1152.f, xs_all[i], acc[t][i]);
   }
 
   // the waves' partial sums meet in LDS and are added in wave order
@@ -730,18 +827,18 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_w4_kernel(
     if (tile0 + t >= T16 || n >= N) continue;
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[w][t][m][o & 15];
-    if (S == 1) y[(size_t)m * N + n] = f32_to_bf16(v);
+    if (S == 1) y[(size_t)m * N + n] = f32_to_bf16(kGrouped ? v : bf16_to_f32(scales[n]) * v);
     else part[((size_t)s * M + m) * N + n] = v;
   }
 }
 
-template <int M>
-void launch_mma_w4(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-                   const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+template <int FMT, int M>
+void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
+                const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
   switch (nb) {
-    case 1: gemv_mma_w4_kernel<M, 1><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    case 2: gemv_mma_w4_kernel<M, 2><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    default: gemv_mma_w4_kernel<M, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    case 1: gemv_mma_kernel<FMT, M, 1><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    case 2: gemv_mma_kernel<FMT, M, 2><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    default: gemv_mma_kernel<FMT, M, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
   }
 }
 
@@ -782,22 +879,18 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
   const uint8_t* zs = (const uint8_t*)w->zeros;
   wq_status r = WQ_OK;
   if (rows & kGemvMfma) {
-    if constexpr (FMT == WQ_FMT_W4_G128) {
-      const int nb = (rows & 0xFF) / R;
-      dim3 grid((unsigned)((row_tiles(N) + nb - 1) / nb), split_k);
-      dim3 block(64 * waves);
-      switch (M) {
-        case 1: launch_mma_w4<1>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 2: launch_mma_w4<2>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 3: launch_mma_w4<3>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 4: launch_mma_w4<4>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 5: launch_mma_w4<5>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 6: launch_mma_w4<6>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        case 7: launch_mma_w4<7>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-        default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
-      }
-    } else {
-      return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: the matrix-core GEMV is offered for uint4 group-128 only");
+    const int nb = (rows & 0xFF) / R;
+    dim3 grid((unsigned)((row_tiles(N) + nb - 1) / nb), split_k);
+    dim3 block(64 * waves);
+    switch (M) {
+      case 1: launch_mma<FMT, 1>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 2: launch_mma<FMT, 2>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 3: launch_mma<FMT, 3>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 4: launch_mma<FMT, 4>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 5: launch_mma<FMT, 5>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 6: launch_mma<FMT, 6>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      case 7: launch_mma<FMT, 7>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+      default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
     }
   } else {
   dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
@@ -833,7 +926,7 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
 int gemv_max_waves(int fmt, int M, int rows) {
   if (rows & kGemvMfma) {
     const int rr = rows & ~kGemvMfma;
-    if (fmt != WQ_FMT_W4_G128 || M < 1 || M > kGemvMaxM) return 0;
+    if (M < 1 || M > kGemvMaxM) return 0;
     return (rr == 16 || rr == 32 || rr == 64) ? kMmaMaxWaves : 0;
   }
   const int rr = rows & ~kGemvPrefetch;
@@ -861,8 +954,8 @@ int gemv_default_rows(int64_t K, int64_t N, int fmt, int M) {
 
 int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int rows) {
   if (rows & kGemvMfma) {
-    // about four 128-groups per wave
-    const int64_t groups = (K / kGroup + split_k - 1) / split_k;
+    // about four 128-k units per wave
+    const int64_t groups = ((K + kGroup - 1) / kGroup + split_k - 1) / split_k;
     const int64_t wv = (groups + 3) / 4;
     return (int)(wv < 1 ? 1 : (wv > kMmaMaxWaves ? kMmaMaxWaves : wv));
   }

@@ -17,7 +17,7 @@ constexpr int kGemvTileRows = 16;    // output rows per GEMV workgroup tile (and
                                      // gfx950 metadata tile of the group-128 formats)
 constexpr int kGemvMaxWaves = 16;    // waves per GEMV workgroup (intra-workgroup K split)
 constexpr int kGemvPrefetch = WQ_GEMV_PREFETCH;  // "rows" flag: slice prefetch
-constexpr int kGemvMfma = WQ_GEMV_MFMA;          // "rows" flag: matrix-core GEMV (uint4)
+constexpr int kGemvMfma = WQ_GEMV_MFMA;          // "rows" flag: matrix-core GEMV
 
 // Thread-local error text behind wq_last_error().
 void set_error(const std::string& msg);

@@ -40,7 +40,7 @@ SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)
 GEMV_PREFETCH = 0x100                    # WQ_GEMV_PREFETCH: rows flag, slice prefetch
-GEMV_MFMA = 0x200                        # WQ_GEMV_MFMA: rows flag: the matrix-core GEMV (uint4 group-128; rows = 16 NB)
+GEMV_MFMA = 0x200                        # WQ_GEMV_MFMA: rows flag: the matrix-core GEMV (rows = 16 NB)
 
 
 def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:

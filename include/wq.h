@@ -186,11 +186,11 @@ int wq_gemv_max_split(int fmt, int64_t K);
  * small: 4 * rows + M * (8 for int8, 16 for uint4) <= 48). */
 #define WQ_GEMV_PREFETCH 0x100
 
-/* rows flag of wq_gemv_ex / wq_gemv_max_waves, uint4 group-128 only: the matrix-core
- * GEMV.  rows = 16 * NB | WQ_GEMV_MFMA with NB in {1, 2, 4} 16-row tiles per
- * workgroup; its 1..8 waves interleave over the 128-groups of the workgroup's K range
- * and multiply on v_mfma_f32_16x16x32 (bf16 and fp16) with exact code values; the
- * fp32 partial sums meet in LDS in wave order.  Other formats: WQ_ERR_UNSUPPORTED. */
+/* rows flag of wq_gemv_ex / wq_gemv_max_waves: the matrix-core GEMV.  rows = 16 * NB |
+ * WQ_GEMV_MFMA with NB in {1, 2, 4} 16-row tiles per workgroup; its 1..8 waves
+ * interleave over 128-k units of the workgroup's K range and multiply on
+ * v_mfma_f32_16x16x32 (bf16 and fp16) with exact code values, so its cost barely
+ * grows with M; the fp32 partial sums meet in LDS in wave order. */
 #define WQ_GEMV_MFMA 0x200
 
 /* Largest waves per GEMV workgroup for a format, 1 <= M <= 7 and rows per wave (4, 8

@@ -87,13 +87,12 @@ def test_gemv_max_waves(wqlib):
                 if offered:
                     assert cap <= wqlib.wq_gemv_max_waves(fmt, m, rows)
     assert wqlib.wq_gemv_max_waves("w8pc", 1, pf) == -1                     # flag without rows
-    # the matrix-core GEMV: uint4 group-128 only, 16 NB rows with NB in 1, 2, 4
+    # the matrix-core GEMV: 16 NB rows with NB in 1, 2, 4, up to 8 waves
     mf = wqlib.GEMV_MFMA
     for m in range(1, 8):
         for rows in (16, 32, 64):
-            assert wqlib.wq_gemv_max_waves("w4g128", m, rows | mf) == 8
-            assert wqlib.wq_gemv_max_waves("w8pc", m, rows | mf) == -1
-            assert wqlib.wq_gemv_max_waves("w8g128", m, rows | mf) == -1
+            for fmt in ("w8pc", "w8g128", "w4g128"):
+                assert wqlib.wq_gemv_max_waves(fmt, m, rows | mf) == 8
     for rows in (0, 4, 8, 48, 128, 256):
         assert wqlib.wq_gemv_max_waves("w4g128", 1, rows | mf) == -1
     assert wqlib.wq_gemv_max_waves("w4g128", 1, 16 | mf | pf) == -1
@@ -175,7 +174,7 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 0, 4, 0, None, 0, None) == 1   # split must be given
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 0x100, None, 0, None) == 1   # prefetch without rows
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x100, None, 0, None) == 2  # prefetch not offered
-    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x200, None, 0, None) == 2  # matrix-core GEMV: uint4 only
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 9, 16 | 0x200, None, 0, None) == 2  # matrix-core GEMV: <= 8 waves
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 8 | 0x200, None, 0, None) == 1   # not 16 NB rows
     assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | 0x300, None, 0, None) == 1  # both flags
     dc = _desc(wqlib, layout=0)

@@ -205,6 +205,13 @@ def test_edge_shapes_every_path(wq, fmt, K, N):
         if M < 8:
             for split in [0] + _allowed_splits(fmt, K):
                 assert_parity(_run_gemv(wq, g, x, split), y_ref, f"gemv {fmt} K={K} N={N} M={M} split={split}")
+            xd = to_dev_bf16(x)
+            for rows in (16 | wq.GEMV_MFMA, 64 | wq.GEMV_MFMA):   # ragged 128-k units, short tiles
+                for waves in (1, 3):
+                    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+                    wq.wq_gemv_ex(g, xd, y, 1, waves, rows, ws=None)
+                    torch.cuda.synchronize()
+                    assert_parity(bf16_bits(y), y_ref, f"gemv {fmt} K={K} N={N} M={M} rows={rows} waves={waves}")
         for tile in range(1, wq.GEMM_TILES + 1):
             assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
         yl = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
