@@ -235,7 +235,7 @@ def profile_pass(steps: int = 10, replays: int = 2):
     log(f"profile pass: {replays} replays x {steps} steps x {len(pools)} GEMV launches")
 
 
-PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 4), ("w4g128", 5120, 27648, 2048, 1)]
+PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 9), ("w4g128", 5120, 27648, 2048, 9)]
 
 
 def profile_prefill(calls: int = 10):

@@ -50,7 +50,7 @@ int clamp_split(int v, int64_t units) {
 // the workgroup's own waves already split K (no second launch, no workspace), so one
 // cross-workgroup slice is the default and split_k > 1 is left to the tuner.
 constexpr int kDefaultSplit = 1;
-constexpr int kDefaultTile = 1;
+constexpr int kDefaultTile = 9;
 static_assert(WQ_GEMM_TILES <= WQ_TUNE_LAT_SLOTS && 6 <= WQ_TUNE_LAT_SLOTS,
               "wq_tune writes one lat_us slot per GEMM tile or GEMV split");
 
@@ -127,7 +127,7 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 
 // Untuned GEMM tile: the skinny kernel up to kSkinnyMaxM tokens, with the smallest
 // split-K that gives about two workgroups per CU; above that the 8-wave LDS-DMA kernel
-// for per-channel W8 and the 256-row kernel for the group-128 formats.
+// (tile 9) for every format.
 int default_tile(const wq_weight* w, int64_t M) {
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
@@ -137,7 +137,7 @@ int default_tile(const wq_weight* w, int64_t M) {
       ++t;
     return t;
   }
-  return w->fmt == WQ_FMT_W8_PC ? 9 : kDefaultTile;
+  return kDefaultTile;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {

@@ -619,6 +619,392 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 }
 
 // ---------------------------------------------------------------------------------
+// Group-128 formats, large M: the same LDS-DMA pipeline with fp16 matrix products.
+//
+// A group scale cannot stay outside the products the way a per-channel scale does,
+// and bf16 cannot hold s (q - z) exactly (rounding every weight to bf16 costs up to
+// 0.9 of the tolerance at K = 5120, growing with sqrt(K)); fp16 rounds it 8x finer.
+// So the B fragments are fp16(s (q - z)) -- codes under an fp16 exponent pattern
+// (v_perm_b32 for int8: 1024 + u; v_and_or_b32 for uint4: 1024 + q from bits 0..3 of
+// a half, 64 + q from bits 4..7), the offset and zero-point removed exactly by one
+// packed fp16 add, then one packed fp16 multiply by s -- and x is converted to fp16 in
+// LDS, once per step and workgroup, by all threads together (bf16 -> fp16 is exact for
+// |x| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-24).
+// v_mfma_f32_32x32x16_f16 accumulates in fp32.
+//
+// fp16 holds neither |x| >= 2^15 nor s (q - z) beyond 65504: a workgroup that meets
+// such an x in its rows, or a scale above 4096 (uint4) / 512 (int8), recomputes its
+// tile on an exact path (bf16 codes q or q - z, fp32 partial per group times the
+// scale, operands straight from memory: slow, and only for such inputs).
+//
+// A stage also holds the step's group metadata (the 256 rows' scales and, for uint4,
+// zero-points), brought by one more LDS-DMA of waves 0 and 1.  uint4 codes take 32
+// bytes per row and step; chunk c of row n sits at position c ^ ((n >> 3) & 1).
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// The LDS-DMA with 4-byte lanes (lane i writes LDS byte l + 4 i).
+__device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(la), "v"(g) : "memory", "m0");
+}
+
+template <int FMT>
+struct G128Dma {
+  static constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  static constexpr int kCodeRow = kW4 ? DBK / 2 : DBK;  // code bytes per row and step
+  static constexpr int kCodeBytes = DBN * kCodeRow;
+  static constexpr int kMetaBytes = DBN * 2 + (kW4 ? DBN / 2 : 0);
+  static constexpr int kStage = DA_BYTES + kCodeBytes + kMetaBytes;
+  static constexpr int kCodeInst = kCodeBytes / 1024;  // code DMA instructions per step
+};
+
+// Exact fallback for one workgroup tile (see above): each wave takes 32 x 32 blocks in
+// turn; per block and group, eight v_mfma_f32_32x32x16_bf16 on exact codes give the
+// group's fp32 partial, which the group scale adds into the block.
+template <int FMT>
+__device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+                                const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
+                                uint16_t* __restrict__ y, int M, int K, int N, int m0, int n0, int wave, int NW) {
+  constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+  const int G = K / kGroup;
+  const int row_bytes = kW4 ? K / 2 : K;
+  for (int blk = wave; blk < (DBM / 32) * (DBN / 32); blk += NW) {
+    const int bi = blk / (DBN / 32), bj = blk % (DBN / 32);
+    const int m = min(m0 + 32 * bi + l32, M - 1), n = min(n0 + 32 * bj + l32, N - 1);
+    const size_t mi = ((size_t)(n / kGemvTileRows) * G) * kGemvTileRows + n % kGemvTileRows;
+    floatx16 acc;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) acc[a] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const uint16_t sb = scales[mi + (size_t)g * kGemvTileRows];
+      const float sc = kW4 ? f16_to_f32(sb) : bf16_to_f32(sb);
+      float z = 0.f;
+      if constexpr (kW4) z = (float)((zeros[(mi + (size_t)g * kGemvTileRows) / 2] >> (4 * (n & 1))) & 15u);
+      floatx16 tmp;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) tmp[a] = 0.f;
+      for (int kk = 0; kk < kGroup / 16; ++kk) {
+        const int k = g * kGroup + 16 * kk + 8 * lh;
+        const uint4 xa = *reinterpret_cast<const uint4*>(x + (size_t)m * K + k);
+        uint4 wb;
+        if constexpr (kW4) {
+          wb = w4_word_to_bf16(*reinterpret_cast<const uint32_t*>(qw + tiled_offset(n, k / 2, N, row_bytes)), z);
+        } else {
+          const uint2 c = *reinterpret_cast<const uint2*>(qw + tiled_offset(n, k, N, row_bytes));
+          wb = i8x16_to_bf16_lo(make_uint4(c.x, c.y, 0u, 0u));
+        }
+        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                      __builtin_bit_cast(bf16x8_t, wb), tmp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[a] = fmaf(sc, tmp[a], acc[a]);
+    }
+    const int nn = n0 + 32 * bj + l32;
+    if (nn >= N) continue;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int mm = m0 + 32 * bi + 8 * (a >> 2) + 4 * lh + (a & 3);
+      if (mm < M) y[(size_t)mm * N + nn] = __builtin_bit_cast(uint16_t, (__bf16)acc[a]);
+    }
+  }
+}
+
+template <int FMT, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
+                                                                         const uint16_t* __restrict__ scales,
+                                                                         const uint8_t* __restrict__ zeros,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         uint16_t* __restrict__ y, int M, int K,
+                                                                         int N) {
+  using F = G128Dma<FMT>;
+  constexpr bool kW4 = F::kW4;
+  constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
+  constexpr int XI = 32 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
+  constexpr int kDmaPerStep = XI + WI;
+  constexpr int kThreads = 64 * NW, CV = DA_BYTES / (16 * kThreads);  // 16-byte x chunks per thread to convert
+  static_assert(WI >= 1, "every wave takes part in the code DMA");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[F::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[F::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[F::kStage];
+  __shared__ int wave_flag[NW];
+
+  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN;
+  const int total = mblocks * nblocks;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int nb = lin / mblocks, mb = lin % mblocks;
+  const int n0 = nb * DBN, m0 = mb * DBM;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int KS = K / DBK;
+  const int G = K / kGroup;
+  const int row_bytes = kW4 ? K / 2 : K;
+
+  // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = XI wave + j.
+  uint32_t xo[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int r = 8 * (XI * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ swz_x(r);
+    xo[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 8 * c;  // M * K < 2^31 (launcher)
+  }
+  // codes: int8 instruction j covers the 16-row tile n0/16 + WI wave + j (16 rows x 64
+  // bytes), uint4 instruction j the two tiles from n0/16 + 2 (WI wave + j) (32 rows x 32
+  // bytes, lanes 0..31 the first).  Rows past N are clamped to the last row.
+  constexpr int kTilesPerInst = kW4 ? 2 : 1;
+  const int T = (N + kGemvTileRows - 1) / kGemvTileRows;
+  size_t wt_base[WI];
+  int wt_nr[WI], wlane[WI];
+#pragma unroll
+  for (int j = 0; j < WI; ++j) {
+    const int t = min(n0 / kGemvTileRows + kTilesPerInst * (WI * wave + j) + (kW4 ? lane >> 5 : 0), T - 1);
+    const int nr = min(kGemvTileRows, N - t * kGemvTileRows);
+    wt_base[j] = (size_t)t * kGemvTileRows * row_bytes;
+    wt_nr[j] = nr;
+    wlane[j] = min(kW4 ? (lane >> 1) & 15 : lane >> 2, nr - 1);
+  }
+  const int wc = kW4 ? 16 * ((lane & 1) ^ ((lane >> 4) & 1)) : 16 * ((lane & 3) ^ swz_w(lane >> 2));
+  auto code_src = [&](int j, int k0) {
+    const int b0 = kW4 ? k0 / 2 : k0;  // byte of the packed row
+    const int sl = b0 / kSliceBytes, jb = b0 % kSliceBytes;
+    const int w = min(kSliceBytes, row_bytes - sl * kSliceBytes);
+    return qw + wt_base[j] + (size_t)wt_nr[j] * kSliceBytes * sl + wlane[j] * w + jb + wc;
+  };
+  // metadata: wave 0 brings the 16 tiles' scales of the step's group (2 lanes x 16
+  // bytes per tile), wave 1 the uint4 zero-points (2 lanes x 4 bytes per tile)
+  const int mt = min(n0 / kGemvTileRows + (lane >> 1), T - 1);
+  auto dma = [&](uint8_t* st, int ks) {
+    const int k0 = min(ks, KS - 1) * DBK;
+#pragma unroll
+    for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + DA_BYTES + (WI * wave + j) * 1024);
+    const int g = k0 / kGroup;
+    if (wave == 0 && lane < 32)
+      dma16(scales + ((size_t)mt * G + g) * kGemvTileRows + 8 * (lane & 1), st + DA_BYTES + F::kCodeBytes);
+    if (kW4 && wave == 1 && lane < 32)
+      dma4(zeros + ((size_t)mt * G + g) * (kGemvTileRows / 2) + 4 * (lane & 1),
+           st + DA_BYTES + F::kCodeBytes + DBN * 2);
+  };
+  // x of a landed stage, bf16 -> fp16 in place; the running maximum of |x| (as bf16
+  // bit patterns without the sign) decides the exact fallback
+  u16x2_t xmax = {0, 0};
+  auto convert = [&](uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      uint4* p = reinterpret_cast<uint4*>(st + 16 * (threadIdx.x + kThreads * i));
+      const uint4 v = *p;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xmax = __builtin_elementwise_max(xmax, __builtin_bit_cast(u16x2_t, w[q] & 0x7FFF7FFFu));
+        o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[q] << 16),
+                                                                       __uint_as_float(w[q] & 0xFFFF0000u)));
+      }
+      *p = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  // ---- fragment addresses (bytes within a stage); the swizzles depend only on l32.
+  int aaddr[2][2], baddr[2];
+#pragma unroll
+  for (int P = 0; P < 2; ++P) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      aaddr[P][s2] = (wm * 32 * RB + l32) * 128 + 16 * ((4 * P + 2 * lh + s2) ^ swz_x(l32));
+    if constexpr (kW4)
+      baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 32 + 16 * (P ^ ((l32 >> 3) & 1)) + 8 * lh;
+    else
+      baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
+  }
+
+  f16x8_t A0[2][RB], B0[2][CB];
+  f16x8_t A1[NW == 4 ? 2 : 1][RB], B1[NW == 4 ? 2 : 1][CB];
+  // the step's group metadata for this lane's CB columns, as fp16 pairs: the scale,
+  // and minus the code offset plus zero-point (uint4: 1024 + z and 64 + z; int8: 1152)
+  f16x2_t msc[CB], mo0[CB], mo1[CB];
+  bool big_s = false;
+  auto meta_read = [&](const uint8_t* st) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int n = wn * 32 * CB + j * 32 + l32;
+      const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + DA_BYTES + F::kCodeBytes + 2 * n);
+      _Float16 sh;
+      if constexpr (kW4) {
+        const uint8_t zb = st[DA_BYTES + F::kCodeBytes + DBN * 2 + (n >> 1)];
+        const _Float16 z = (_Float16)(float)((zb >> (4 * (n & 1))) & 15u);
+        sh = __builtin_bit_cast(_Float16, sb);
+        big_s |= (sb & 0x7FFFu) >= 0x6C00u;  // |s| >= 4096, Inf or NaN
+        mo0[j] = f16x2_t{-(_Float16)1024.f - z, -(_Float16)1024.f - z};
+        mo1[j] = f16x2_t{-(_Float16)64.f - z, -(_Float16)64.f - z};
+      } else {
+        const float sf = bf16_to_f32(sb);
+        sh = (_Float16)sf;
+        big_s |= (sb & 0x7FFFu) >= 0x4400u;  // |s| >= 512, Inf or NaN
+        mo0[j] = f16x2_t{(_Float16)-1152.f, (_Float16)-1152.f};
+      }
+      msc[j] = f16x2_t{sh, sh};
+    }
+  };
+  uint32_t nib_lo = 0x000F000Fu, nib_hi = 0x00F000F0u, mag_1024 = 0x64006400u, mag_64 = 0x54005400u;
+  if constexpr (kW4) asm volatile("" : "+v"(nib_lo), "+v"(nib_hi), "+v"(mag_1024), "+v"(mag_64));
+  // fp16 pair (offset + q) -> fp16 pair s (q - z): exact add, one rounding multiply
+  auto deq = [&](uint32_t h, f16x2_t off, f16x2_t sc) -> uint32_t {
+    return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, h) + off) * sc);
+  };
+  auto fread = [&](const uint8_t* st, int P, f16x8_t (*A)[RB], f16x8_t (*B)[CB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        A[s2][i] = *reinterpret_cast<const f16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
+    if (P == 0) meta_read(st);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      if constexpr (kW4) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(st + baddr[P] + j * 32 * 32);
+        const uint32_t wd[2] = {raw.x, raw.y};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const uint32_t w = wd[s2], w8 = w >> 8;
+          const uint4 o = make_uint4(deq((w & nib_lo) | mag_1024, mo0[j], msc[j]),
+                                     deq((w & nib_hi) | mag_64, mo1[j], msc[j]),
+                                     deq((w8 & nib_lo) | mag_1024, mo0[j], msc[j]),
+                                     deq((w8 & nib_hi) | mag_64, mo1[j], msc[j]));
+          B[s2][j] = __builtin_bit_cast(f16x8_t, o);
+        }
+      } else {
+        const uint4 raw = *reinterpret_cast<const uint4*>(st + baddr[P] + j * 32 * 64);
+        const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[2 * q] = deq(__builtin_amdgcn_perm(0x64646464u, d[q], 0x04010400u), mo0[j], msc[j]);
+          o[2 * q + 1] = deq(__builtin_amdgcn_perm(0x64646464u, d[q], 0x04030402u), mo0[j], msc[j]);
+        }
+        B[0][j] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        B[1][j] = __builtin_bit_cast(f16x8_t, make_uint4(o[4], o[5], o[6], o[7]));
+      }
+    }
+  };
+
+  floatx16 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[i][j][a] = 0.f;
+  auto mma = [&](f16x8_t (*A)[RB], f16x8_t (*B)[CB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+  };
+  // This wave's DMA of the step after the current one is complete (only the newest
+  // step's kDmaPerStep may still be in flight; waves 0 and 1 issue one more, so they
+  // wait for one instruction more than needed) and every wave has finished reading
+  // the stage that the next DMA overwrites.
+  auto step_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStep) : "memory");
+  };
+  // the conversion of a stage is complete in every wave before any reads it
+  auto convert_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + 3 * CB;
+  constexpr int kCvtPerPhase = 30 * CB;  // per 16 codes: extraction, 8 packed adds, 8 packed multiplies
+  constexpr int kLead = 4;               // MFMAs that cover the LDS read latency
+  constexpr int kv = (kCvtPerPhase + kMfmaPerPhase - kLead - 1) / (kMfmaPerPhase - kLead) + 1;
+  auto phase_order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+#pragma unroll
+    for (int i = kLead; i < kMfmaPerPhase; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kv, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  dma(st0, 0);
+  dma(st1, 1);
+  dma(st2, 2);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerStep) : "memory");
+  convert(st0);
+  convert_barrier();
+  constexpr bool kPipelined = NW == 4;
+  if constexpr (kPipelined) fread(st0, 0, A0, B0);
+  auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
+    if constexpr (kPipelined) {
+      fread(cur, 1, A1, B1);
+      mma(A0, B0);
+      phase_order();
+      step_barrier();
+      dma(cur, t + 3);  // every wave is done with this stage
+      convert(nxt);
+      convert_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      fread(nxt, 0, A0, B0);
+      mma(A1, B1);
+      phase_order();
+    } else {
+      fread(cur, 0, A0, B0);
+      mma(A0, B0);
+      fread(cur, 1, A0, B0);
+      mma(A0, B0);
+      step_barrier();
+      dma(cur, t + 3);
+      convert(nxt);
+      convert_barrier();
+    }
+  };
+  const int KS3 = KS - KS % 3;
+  for (int t = 0; t < KS3; t += 3) {
+    step(st0, st1, t);
+    step(st1, st2, t + 1);
+    step(st2, st0, t + 2);
+  }
+  if (KS % 3 >= 1) step(st0, st1, KS3);
+  if (KS % 3 == 2) step(st1, st2, KS3 + 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- every wave's verdict on its x chunks and scales decides the tile's path
+  const bool big = xmax.x >= 0x4700 || xmax.y >= 0x4700 || big_s;  // |x| >= 2^15 (or Inf / NaN)
+  const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
+  if (lane == 0) wave_flag[wave] = wave_big ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any |= wave_flag[w];
+  if (any) {
+    g128_tile_exact<FMT>(qw, scales, zeros, x, y, M, K, N, m0, n0, wave, NW);
+    return;
+  }
+  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int n = n0 + wn * 32 * CB + j * 32 + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][a]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Skinny GEMM, 8 <= M <= 128 tokens.  At these M the layer is still bound by the
 // weight stream (2 M flops per int8 byte), so the kernel is built like the decode
 // GEMV with the dot products moved onto the matrix cores:
@@ -1107,6 +1493,18 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       gemm_dma_w8pc_kernel<1, 4><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
     else
       gemm_dma_w8pc_kernel<2, 4><<<blocks, 512, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+    WQ_HIP_CHECK(hipGetLastError());
+    return WQ_OK;
+  }
+  // group-128 formats: tile 9 is the fp16 LDS-DMA kernel (2 x 4 waves; the 4-wave
+  // layouts of tiles 3 and 4 would spill its registers and take tile 1 instead)
+  if (tile == 9 && w->fmt != WQ_FMT_W8_PC && M * K < (int64_t(1) << 31)) {
+    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+    const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
+    if (w->fmt == WQ_FMT_W4_G128)
+      gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<blocks, 512, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+    else
+      gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<blocks, 512, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
     WQ_HIP_CHECK(hipGetLastError());
     return WQ_OK;
   }

@@ -215,15 +215,19 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * ("Key Optimizations"): codes are converted to exact bf16 values (q, or q - z) and
  * multiplied by bf16 x on the matrix cores with fp32 accumulation; the per-channel
  * scale is applied to the finished fp32 sum, group-128 scales to each group's fp32
- * partial.  w must be in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
+ * partial -- except tile 9 for the group-128 formats, which stages the dequantised
+ * weight rounded once to fp16, fp16(s (q - z)), against x converted to fp16 (a
+ * workgroup whose x holds some |x| >= 2^15, or whose scales exceed 4096 (uint4) / 512
+ * (int8), recomputes its tile the exact way).  w must be in the GFX950 layout; x:
+ * bf16 [M][K], y: bf16 [M][N].
  *
  * tile: 0 = the tuned tile (a default by M and format when untuned), else
  *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;
  *   2  128 x 128 tile, 4 waves of 64 x 64;
  *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
  *   4  as 3 with 1 x 4 waves;
- *   9  as 3 with 8 waves (2 x 4, two per SIMD) (tiles 3, 4, 9 for other formats or
- *      shapes: tile 1);
+ *   9  as 3 with 8 waves (2 x 4, two per SIMD); for group-128 the fp16 LDS-DMA tile
+ *      above (tiles 3 and 4 for group-128, and 3, 4, 9 for other shapes: tile 1);
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.

@@ -53,6 +53,19 @@ def _rows_options(wq, fmt, M):
     return out
 
 
+def _fp16_staged(fmt, tile):
+    """The group-128 formats' LDS-DMA GEMM (tile 9) stages fp16(dequant(W)): its exact
+    selections return bf16(fp16(w)) rather than bf16(w)."""
+    return fmt != "w8pc" and tile == 9
+
+
+def _selected(fmt, tile, w):
+    """bf16 bits a path returns when x selects the dequantised weights w exactly."""
+    if _fp16_staged(fmt, tile):
+        w = np.asarray(w, dtype=np.float64).astype(np.float16).astype(np.float32)
+    return OQ.bf16_rne_bits(np.ascontiguousarray(w, dtype=np.float32))
+
+
 def _run_gemm(wq, g, x_bits, tile=0):
     M = x_bits.shape[0]
     x = to_dev_bf16(x_bits)
@@ -246,7 +259,8 @@ def test_one_hot_is_exact(wq, fmt):
                 torch.cuda.synchronize()
                 assert np.array_equal(bf16_bits(y), want), f"gemv split={split} rows={rows} waves={waves}"
     for tile in range(1, wq.GEMM_TILES + 1):
-        assert np.array_equal(_run_gemm(wq, g, x, tile), want), f"gemm tile={tile}"
+        assert np.array_equal(_run_gemm(wq, g, x, tile), _selected(fmt, tile, OQ.dequant(P)[:, ks].T)), \
+            f"gemm tile={tile}"
 
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
@@ -254,9 +268,33 @@ def test_identity_is_exact(wq, fmt):
     K, N = 1024, 264
     W = synth.weight(95, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
-    want = OQ.bf16_rne_bits(OQ.dequant(OQ.pack(fmt, W)).T.copy())
+    deq = OQ.dequant(OQ.pack(fmt, W)).T.copy()
     for tile in range(1, wq.GEMM_TILES + 1):
-        assert np.array_equal(_run_gemm(wq, g, synth.identity_activation(K), tile), want)
+        assert np.array_equal(_run_gemm(wq, g, synth.identity_activation(K), tile), _selected(fmt, tile, deq)), \
+            f"gemm tile={tile}"
+
+
+@pytest.mark.parametrize("fmt", ["w8g128", "w4g128"])
+def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
+    """The fp16 LDS-DMA GEMM of the group-128 formats recomputes a workgroup's tile
+    exactly when its x holds some |x| >= 2^15 or a scale exceeds the fp16-safe bound
+    (4096 for uint4, 512 for int8); other workgroups stay on the fp16 path."""
+    K, N, M = 1024, 520, 300   # two 256-row blocks of x, three 256-column blocks
+    W = synth.weight(105, K, N, synth.uses_outliers(fmt))
+    W[300:308] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)  # huge weights in one 8-row block
+    g, can = quantize_on_gpu(wq, W, fmt)
+    P = OQ.pack(fmt, W)
+    sc = np.abs(P["scales"].astype(np.float32) if fmt == "w4g128" else OQ.bf16_bits_to_f32(P["scales"]))
+    assert sc.max() > (4096 if fmt == "w4g128" else 512) and np.isfinite(sc).all()
+    xf = OQ.bf16_bits_to_f32(synth.activation(105, K, M)).copy()
+    for case in ("plain", "big-x"):
+        if case == "big-x":
+            xf[5, 17] = 40000.0                 # first row block only
+            xf[6, 900] = -3.0e5
+        x = OQ.bf16_rne_bits(xf.astype(np.float32))
+        y_ref = OL.ref_linear(x, P)
+        for tile in (9, 1):
+            assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} {case} tile={tile}")
 
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
