@@ -628,21 +628,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 // (v_perm_b32 for int8: 1024 + u; v_and_or_b32 for uint4: 1024 + q from bits 0..3 of
 // a half, 64 + q from bits 4..7), the offset and zero-point removed exactly by one
 // packed fp16 add, then one packed fp16 multiply by s -- and x is converted to fp16 in
-// LDS, once per step and workgroup, by all threads together (bf16 -> fp16 is exact for
-// |x| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-24).
-// v_mfma_f32_32x32x16_f16 accumulates in fp32.
+// LDS, once per step and workgroup: every lane converts the 16-byte chunks its own DMA
+// brought, right after waiting for them, so the step's one barrier also covers the
+// conversion (bf16 -> fp16 is exact for |x| in [2^-14, 65504]; smaller magnitudes keep
+// an absolute error below 2^-24).  v_mfma_f32_32x32x16_f16 accumulates in fp32.
 //
-// fp16 holds neither |x| >= 2^15 nor s (q - z) beyond 65504: a workgroup that meets
-// such an x in its rows, or a scale above 4096 (uint4) / 512 (int8), recomputes its
-// tile on an exact path (bf16 codes q or q - z, fp32 partial per group times the
-// scale, operands straight from memory: slow, and only for such inputs).
+// fp16 holds neither |x| > 65504 nor s (q - z) beyond 65504.  Both round to Inf
+// (nearest-even conversion and multiply), which no finite operand turns finite again,
+// so a workgroup that ends with a non-finite accumulator recomputes its tile on an
+// exact path (bf16 codes q or q - z, fp32 partial per group times the scale, operands
+// straight from memory: slow, and only for such inputs).
 //
 // A stage also holds the step's group metadata (the 256 rows' scales and, for uint4,
 // zero-points), brought by one more LDS-DMA of waves 0 and 1.  uint4 codes take 32
 // bytes per row and step; chunk c of row n sits at position c ^ ((n >> 3) & 1).
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // The LDS-DMA with 4-byte lanes (lane i writes LDS byte l + 4 i).
 __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
@@ -724,7 +726,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
   constexpr int XI = 32 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
   constexpr int kDmaPerStep = XI + WI;
-  constexpr int kThreads = 64 * NW, CV = DA_BYTES / (16 * kThreads);  // 16-byte x chunks per thread to convert
   static_assert(WI >= 1, "every wave takes part in the code DMA");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[F::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[F::kStage];
@@ -793,21 +794,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       dma4(zeros + ((size_t)mt * G + g) * (kGemvTileRows / 2) + 4 * (lane & 1),
            st + DA_BYTES + F::kCodeBytes + DBN * 2);
   };
-  // x of a landed stage, bf16 -> fp16 in place; the running maximum of |x| (as bf16
-  // bit patterns without the sign) decides the exact fallback
-  u16x2_t xmax = {0, 0};
+  // the x chunks this lane's own DMA brought into a stage, bf16 -> fp16 in place
+  // (v_cvt_pk_f16_f32, nearest even: beyond fp16 range gives Inf)
   auto convert = [&](uint8_t* st) {
 #pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      uint4* p = reinterpret_cast<uint4*>(st + 16 * (threadIdx.x + kThreads * i));
+    for (int j = 0; j < XI; ++j) {
+      uint4* p = reinterpret_cast<uint4*>(st + (XI * wave + j) * 1024 + 16 * lane);
       const uint4 v = *p;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        xmax = __builtin_elementwise_max(xmax, __builtin_bit_cast(u16x2_t, w[q] & 0x7FFF7FFFu));
-        o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[q] << 16),
-                                                                       __uint_as_float(w[q] & 0xFFFF0000u)));
+        const float2_t f = {__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xFFFF0000u)};
+        o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
       }
       *p = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -830,7 +829,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   // the step's group metadata for this lane's CB columns, as fp16 pairs: the scale,
   // and minus the code offset plus zero-point (uint4: 1024 + z and 64 + z; int8: 1152)
   f16x2_t msc[CB], mo0[CB], mo1[CB];
-  bool big_s = false;
   auto meta_read = [&](const uint8_t* st) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -841,13 +839,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
         const uint8_t zb = st[DA_BYTES + F::kCodeBytes + DBN * 2 + (n >> 1)];
         const _Float16 z = (_Float16)(float)((zb >> (4 * (n & 1))) & 15u);
         sh = __builtin_bit_cast(_Float16, sb);
-        big_s |= (sb & 0x7FFFu) >= 0x6C00u;  // |s| >= 4096, Inf or NaN
         mo0[j] = f16x2_t{-(_Float16)1024.f - z, -(_Float16)1024.f - z};
         mo1[j] = f16x2_t{-(_Float16)64.f - z, -(_Float16)64.f - z};
       } else {
-        const float sf = bf16_to_f32(sb);
-        sh = (_Float16)sf;
-        big_s |= (sb & 0x7FFFu) >= 0x4400u;  // |s| >= 512, Inf or NaN
+        sh = (_Float16)bf16_to_f32(sb);
         mo0[j] = f16x2_t{(_Float16)-1152.f, (_Float16)-1152.f};
       }
       msc[j] = f16x2_t{sh, sh};
@@ -913,13 +908,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   };
   // This wave's DMA of the step after the current one is complete (only the newest
   // step's kDmaPerStep may still be in flight; waves 0 and 1 issue one more, so they
-  // wait for one instruction more than needed) and every wave has finished reading
-  // the stage that the next DMA overwrites.
-  auto step_barrier = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStep) : "memory");
+  // wait for one instruction more than needed); its x chunks are converted; then
+  // every wave has converted its chunks and finished reading the stage that the next
+  // DMA overwrites.
+  auto step_barrier = [&](uint8_t* nxt) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStep) : "memory");
+    convert(nxt);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  // the conversion of a stage is complete in every wave before any reads it
-  auto convert_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + 3 * CB;
   constexpr int kCvtPerPhase = 30 * CB;  // per 16 codes: extraction, 8 packed adds, 8 packed multiplies
@@ -938,9 +934,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   dma(st0, 0);
   dma(st1, 1);
   dma(st2, 2);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerStep) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerStep) : "memory");
   convert(st0);
-  convert_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   constexpr bool kPipelined = NW == 4;
   if constexpr (kPipelined) fread(st0, 0, A0, B0);
   auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
@@ -948,10 +944,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       fread(cur, 1, A1, B1);
       mma(A0, B0);
       phase_order();
-      step_barrier();
+      step_barrier(nxt);
       dma(cur, t + 3);  // every wave is done with this stage
-      convert(nxt);
-      convert_barrier();
       __builtin_amdgcn_sched_barrier(0);
       fread(nxt, 0, A0, B0);
       mma(A1, B1);
@@ -961,10 +955,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       mma(A0, B0);
       fread(cur, 1, A0, B0);
       mma(A0, B0);
-      step_barrier();
+      step_barrier(nxt);
       dma(cur, t + 3);
-      convert(nxt);
-      convert_barrier();
     }
   };
   const int KS3 = KS - KS % 3;
@@ -977,8 +969,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   if (KS % 3 == 2) step(st1, st2, KS3 + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- every wave's verdict on its x chunks and scales decides the tile's path
-  const bool big = xmax.x >= 0x4700 || xmax.y >= 0x4700 || big_s;  // |x| >= 2^15 (or Inf / NaN)
+  // ---- any non-finite accumulator in the workgroup sends the tile down the exact path
+  bool big = false;
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) big |= !__builtin_isfinite(acc[i][j][a]);
   const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
   if (lane == 0) wave_flag[wave] = wave_big ? 1 : 0;
   __syncthreads();

@@ -217,9 +217,8 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * scale is applied to the finished fp32 sum, group-128 scales to each group's fp32
  * partial -- except tile 9 for the group-128 formats, which stages the dequantised
  * weight rounded once to fp16, fp16(s (q - z)), against x converted to fp16 (a
- * workgroup whose x holds some |x| >= 2^15, or whose scales exceed 4096 (uint4) / 512
- * (int8), recomputes its tile the exact way).  w must be in the GFX950 layout; x:
- * bf16 [M][K], y: bf16 [M][N].
+ * workgroup whose x or dequantised weights leave the fp16 range recomputes its tile
+ * the exact way).  w must be in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
  *
  * tile: 0 = the tuned tile (a default by M and format when untuned), else
  *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;

@@ -277,8 +277,9 @@ def test_identity_is_exact(wq, fmt):
 @pytest.mark.parametrize("fmt", ["w8g128", "w4g128"])
 def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
     """The fp16 LDS-DMA GEMM of the group-128 formats recomputes a workgroup's tile
-    exactly when its x holds some |x| >= 2^15 or a scale exceeds the fp16-safe bound
-    (4096 for uint4, 512 for int8); other workgroups stay on the fp16 path."""
+    exactly when its x or its dequantised weights leave the fp16 range (|x| > 65504,
+    or s (q - z) beyond it: scales above 4096 for uint4, 512 for int8); other
+    workgroups stay on the fp16 path, and |x| up to 65504 is exact in fp16."""
     K, N, M = 1024, 520, 300   # two 256-row blocks of x, three 256-column blocks
     W = synth.weight(105, K, N, synth.uses_outliers(fmt))
     W[300:308] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)  # huge weights in one 8-row block
@@ -289,8 +290,8 @@ def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
     xf = OQ.bf16_bits_to_f32(synth.activation(105, K, M)).copy()
     for case in ("plain", "big-x"):
         if case == "big-x":
-            xf[5, 17] = 40000.0                 # first row block only
-            xf[6, 900] = -3.0e5
+            xf[5, 17] = 40000.0                 # fp16 holds it: first row block stays on fp16
+            xf[6, 900] = -3.0e5                 # beyond fp16: the first row block falls back
         x = OQ.bf16_rne_bits(xf.astype(np.float32))
         y_ref = OL.ref_linear(x, P)
         for tile in (9, 1):
