@@ -127,7 +127,8 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 
 // Untuned GEMM tile: the skinny kernel up to kSkinnyMaxM tokens, with the smallest
 // split-K that gives about two workgroups per CU; above that the 8-wave LDS-DMA kernel
-// (tile 9) for every format.
+// (tile 9) for every format, split over K (tiles 10..12) when its tiles would not
+// occupy half the CUs.
 int default_tile(const wq_weight* w, int64_t M) {
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
@@ -137,7 +138,16 @@ int default_tile(const wq_weight* w, int64_t M) {
       ++t;
     return t;
   }
-  return kDefaultTile;
+  // fewer 256 x 256 tiles than half the CUs: the smallest split-K that gives at least
+  // that many workgroups (measured on MI355X: at M = 512, N = 5120 split 4 beats 8, and
+  // 160 tiles run best unsplit)
+  const int64_t blocks = ((M + 255) / 256) * ((w->N + 255) / 256);
+  if (blocks >= 128) return kDefaultTile;
+  int t = kDmaSplitTile0;
+  while (t < kDmaSplitTileLast && blocks * gemm_dma_split(t, M, w->N) < 128 &&
+         gemm_dma_split(t + 1, M, w->N) > gemm_dma_split(t, M, w->N))
+    ++t;
+  return gemm_dma_split(t, M, w->N) > 1 ? t : kDefaultTile;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {

@@ -435,11 +435,13 @@ template <int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
-                                                                         uint16_t* __restrict__ y, int M, int K,
+                                                                         uint16_t* __restrict__ y,
+                                                                         float* __restrict__ part, int M, int K,
                                                                          int N) {
   constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
   constexpr int XI = 32 / NW, WI = 16 / NW;  // x and code DMA instructions per wave and step
   constexpr int kDmaPerStep = XI + WI;
+  constexpr int KUNIT = 1;  // split-K granularity in steps
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGE];
@@ -456,7 +458,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int KS = K / DBK;
+  // split-K over gridDim.y: this workgroup's steps kb .. kb + KS - 1 (whole groups for
+  // the group-128 formats); with S > 1 it writes fp32 partials (see the epilogue)
+  const int S = gridDim.y, sp = blockIdx.y, U = K / (DBK * KUNIT);
+  const int kb = KUNIT * (int)((int64_t)sp * U / S), KS = KUNIT * (int)((int64_t)(sp + 1) * U / S) - kb;
 
   // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = XI wave + j.
   uint32_t xo[XI];
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
     return qw + wt_base[j] + (size_t)wt_nr[j] * kSliceBytes * sl + wlane[j] * w + jb + wc;
   };
   auto dma = [&](uint8_t* st, int ks) {
-    const int k0 = min(ks, KS - 1) * DBK;
+    const int k0 = (kb + min(ks, KS - 1)) * DBK;
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
@@ -602,7 +607,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   if (KS % 3 == 2) step(st1, st2, KS3 + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block
+  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block;
+  // split-K ranges write raw fp32 partials (the reduction applies the scale)
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
     const int n = n0 + wn * 32 * CB + j * 32 + l32;
@@ -613,7 +619,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+        if (m >= M) continue;
+        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+        else part[((size_t)sp * M + m) * N + n] = acc[i][j][a];
       }
   }
 }
@@ -633,11 +641,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 // conversion (bf16 -> fp16 is exact for |x| in [2^-14, 65504]; smaller magnitudes keep
 // an absolute error below 2^-24).  v_mfma_f32_32x32x16_f16 accumulates in fp32.
 //
-// fp16 holds neither |x| > 65504 nor s (q - z) beyond 65504.  Both round to Inf
-// (nearest-even conversion and multiply), which no finite operand turns finite again,
-// so a workgroup that ends with a non-finite accumulator recomputes its tile on an
-// exact path (bf16 codes q or q - z, fp32 partial per group times the scale, operands
-// straight from memory: slow, and only for such inputs).
+// The fp16 rounding of each weight adds an error of up to 2^-11 |x w| per term, small
+// against the tolerance while the weights are of LLM size, but not for large weights
+// whose products cancel.  So a workgroup recomputes its tile on an exact path (bf16
+// codes q or q - z, fp32 partial per group times the scale, operands straight from
+// memory: slow, and only for such inputs) when a dequantised weight of its groups can
+// exceed 16 in magnitude (|s| times the largest |q - z| or |q|; N(0, 0.02^2) weights
+// with 1 % x8 outliers stay near 1), and when an accumulator ends non-finite: beyond
+// 65504 x and s (q - z) round to Inf (nearest-even conversion and multiply).  Large
+// activations are not bounded this way (tracking max |x| per step cost 7 %).
 //
 // A stage also holds the step's group metadata (the 256 rows' scales and, for uint4,
 // zero-points), brought by one more LDS-DMA of waves 0 and 1.  uint4 codes take 32
@@ -645,6 +657,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // The LDS-DMA with 4-byte lanes (lane i writes LDS byte l + 4 i).
 __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
@@ -668,7 +681,8 @@ struct G128Dma {
 template <int FMT>
 __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                                 const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
-                                uint16_t* __restrict__ y, int M, int K, int N, int m0, int n0, int wave, int NW) {
+                                uint16_t* __restrict__ y, float* __restrict__ part, int M, int K, int N,
+                                int m0, int n0, int g0, int g1, int sp, int S, int wave, int NW) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   const int G = K / kGroup;
@@ -680,7 +694,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
     floatx16 acc;
 #pragma unroll
     for (int a = 0; a < 16; ++a) acc[a] = 0.f;
-    for (int g = 0; g < G; ++g) {
+    for (int g = g0; g < g1; ++g) {
       const uint16_t sb = scales[mi + (size_t)g * kGemvTileRows];
       const float sc = kW4 ? f16_to_f32(sb) : bf16_to_f32(sb);
       float z = 0.f;
@@ -709,7 +723,9 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int mm = m0 + 32 * bi + 8 * (a >> 2) + 4 * lh + (a & 3);
-      if (mm < M) y[(size_t)mm * N + nn] = __builtin_bit_cast(uint16_t, (__bf16)acc[a]);
+      if (mm >= M) continue;
+      if (S == 1) y[(size_t)mm * N + nn] = __builtin_bit_cast(uint16_t, (__bf16)acc[a]);
+      else part[((size_t)sp * M + mm) * N + nn] = acc[a];
     }
   }
 }
@@ -719,18 +735,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
                                                                          const uint16_t* __restrict__ x,
-                                                                         uint16_t* __restrict__ y, int M, int K,
+                                                                         uint16_t* __restrict__ y,
+                                                                         float* __restrict__ part, int M, int K,
                                                                          int N) {
   using F = G128Dma<FMT>;
   constexpr bool kW4 = F::kW4;
   constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
   constexpr int XI = 32 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
   constexpr int kDmaPerStep = XI + WI;
+  constexpr int KUNIT = 2;  // split-K granularity in steps: one group
   static_assert(WI >= 1, "every wave takes part in the code DMA");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[F::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[F::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[F::kStage];
   __shared__ int wave_flag[NW];
+  __shared__ float wave_max[NW];
 
   const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN;
   const int total = mblocks * nblocks;
@@ -744,7 +763,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int KS = K / DBK;
+  // split-K over gridDim.y: this workgroup's steps kb .. kb + KS - 1 (whole groups for
+  // the group-128 formats); with S > 1 it writes fp32 partials (see the epilogue)
+  const int S = gridDim.y, sp = blockIdx.y, U = K / (DBK * KUNIT);
+  const int kb = KUNIT * (int)((int64_t)sp * U / S), KS = KUNIT * (int)((int64_t)(sp + 1) * U / S) - kb;
   const int G = K / kGroup;
   const int row_bytes = kW4 ? K / 2 : K;
 
@@ -782,7 +804,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   // bytes per tile), wave 1 the uint4 zero-points (2 lanes x 4 bytes per tile)
   const int mt = min(n0 / kGemvTileRows + (lane >> 1), T - 1);
   auto dma = [&](uint8_t* st, int ks) {
-    const int k0 = min(ks, KS - 1) * DBK;
+    const int k0 = (kb + min(ks, KS - 1)) * DBK;
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
@@ -849,7 +871,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     }
   };
   uint32_t nib_lo = 0x000F000Fu, nib_hi = 0x00F000F0u, mag_1024 = 0x64006400u, mag_64 = 0x54005400u;
-  if constexpr (kW4) asm volatile("" : "+v"(nib_lo), "+v"(nib_hi), "+v"(mag_1024), "+v"(mag_64));
+  if constexpr (kW4) asm volatile("" : "+v"(nib_lo), "+v"(nib_hi), "+s"(mag_1024), "+s"(mag_64));
   // fp16 pair (offset + q) -> fp16 pair s (q - z): exact add, one rounding multiply
   auto deq = [&](uint32_t h, f16x2_t off, f16x2_t sc) -> uint32_t {
     return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, h) + off) * sc);
@@ -890,6 +912,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     }
   };
 
+  // One half s2 of a slice (eight waves: the registers hold one half at a time): the A
+  // fragments of MFMA s2 and the B fragments they meet.
+  auto fread_half = [&](const uint8_t* st, int P, int s2, f16x8_t* A, f16x8_t* B) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) A[i] = *reinterpret_cast<const f16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
+    if (P == 0 && s2 == 0) meta_read(st);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      if constexpr (kW4) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(st + baddr[P] + j * 32 * 32 + 4 * s2), w8 = w >> 8;
+        const uint4 o = make_uint4(deq((w & nib_lo) | mag_1024, mo0[j], msc[j]),
+                                   deq((w & nib_hi) | mag_64, mo1[j], msc[j]),
+                                   deq((w8 & nib_lo) | mag_1024, mo0[j], msc[j]),
+                                   deq((w8 & nib_hi) | mag_64, mo1[j], msc[j]));
+        B[j] = __builtin_bit_cast(f16x8_t, o);
+      } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(st + baddr[P] + j * 32 * 64 + 8 * s2);
+        const uint4 o = make_uint4(deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04010400u), mo0[j], msc[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04030402u), mo0[j], msc[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04010400u), mo0[j], msc[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04030402u), mo0[j], msc[j]));
+        B[j] = __builtin_bit_cast(f16x8_t, o);
+      }
+    }
+  };
+
   floatx16 acc[RB][CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
@@ -897,6 +945,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int a = 0; a < 16; ++a) acc[i][j][a] = 0.f;
+  auto mma_half = [&](const f16x8_t* A, const f16x8_t* B) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+  };
   auto mma = [&](f16x8_t (*A)[RB], f16x8_t (*B)[CB]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -951,10 +1006,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       mma(A1, B1);
       phase_order();
     } else {
-      fread(cur, 0, A0, B0);
-      mma(A0, B0);
-      fread(cur, 1, A0, B0);
-      mma(A0, B0);
+      f16x8_t Ah[RB], Bh[CB];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          fread_half(cur, P, s2, Ah, Bh);
+          mma_half(Ah, Bh);
+        }
       step_barrier(nxt);
       dma(cur, t + 3);
     }
@@ -969,7 +1028,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   if (KS % 3 == 2) step(st1, st2, KS3 + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- any non-finite accumulator in the workgroup sends the tile down the exact path
+  // ---- a dequantised weight of more than 16 in magnitude, or a non-finite
+  // accumulator, sends the tile down the exact path
   bool big = false;
 #pragma unroll
   for (int i = 0; i < RB; ++i)
@@ -977,17 +1037,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int a = 0; a < 16; ++a) big |= !__builtin_isfinite(acc[i][j][a]);
+  // max |s| of the tile's columns over this range's groups, from the tiled metadata
+  // (per tile a contiguous run of 32 bytes per group)
+  float smax;
+  {
+    const int gb = kb / KUNIT, ng = KS / KUNIT;
+    u16x2_t sm16 = {0, 0};
+    for (int c = threadIdx.x; c < 16 * 2 * ng; c += 64 * NW) {
+      const int tt = min(n0 / kGemvTileRows + c / (2 * ng), T - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(scales + ((size_t)tt * G + gb) * kGemvTileRows +
+                                                      8 * (c % (2 * ng)));
+      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
+      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
+      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
+      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
+    }
+    smax = kW4 ? fmaxf(f16_to_f32(sm16.x), f16_to_f32(sm16.y)) : fmaxf(bf16_to_f32(sm16.x), bf16_to_f32(sm16.y));
+  }
+  for (int d = 1; d < 64; d <<= 1) smax = fmaxf(smax, __shfl_xor(smax, d));
   const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
-  if (lane == 0) wave_flag[wave] = wave_big ? 1 : 0;
+  if (lane == 0) {
+    wave_flag[wave] = wave_big ? 1 : 0;
+    wave_max[wave] = smax;
+  }
   __syncthreads();
   int any = 0;
+  float ws = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) any |= wave_flag[w];
-  if (any) {
-    g128_tile_exact<FMT>(qw, scales, zeros, x, y, M, K, N, m0, n0, wave, NW);
+  for (int w = 0; w < NW; ++w) {
+    any |= wave_flag[w];
+    ws = fmaxf(ws, wave_max[w]);
+  }
+  constexpr float kCodeMax = kW4 ? 15.f : 127.f;  // largest |q - z| or |q|
+  if (any || !(kCodeMax * ws <= 16.f)) {  // (NaN scales fail the comparison)
+    g128_tile_exact<FMT>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, sp, S,
+                         wave, NW);
     return;
   }
-  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block
+  // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block;
+  // split-K ranges write fp32 partials
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
     const int n = n0 + wn * 32 * CB + j * 32 + l32;
@@ -997,7 +1085,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][a]);
+        if (m >= M) continue;
+        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][a]);
+        else part[((size_t)sp * M + m) * N + n] = acc[i][j][a];
       }
   }
 }
@@ -1455,8 +1545,17 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N) {
   return S;
 }
 
+int gemm_dma_split(int tile, int64_t M, int64_t N) {
+  if (tile < kDmaSplitTile0 || tile > kDmaSplitTileLast) return 0;
+  const int64_t blocks = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+  int S = 2 << (tile - kDmaSplitTile0);
+  // about two workgroups per CU at most, and a bounded workspace
+  while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
+  return S;
+}
+
 size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
-  const int S = gemm_skinny_split(tile, M, N);
+  const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : gemm_skinny_split(tile, M, N);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -1481,29 +1580,41 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     }
     tile = 2;  // shape outside the skinny kernel's range
   }
-  const bool dma_tile = tile == 3 || tile == 4 || tile == 9;
-  if (dma_tile && w->fmt == WQ_FMT_W8_PC && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
+  // LDS-DMA tiles: 3, 4 and 9 (per-channel W8; for group-128 only the 8-wave tile 9 --
+  // the 4-wave layouts would spill its registers -- and tiles 3 and 4 take tile 1), and
+  // 10..12: tile 9 with split-K 2, 4, 8 (fp32 partials in the workspace, added in
+  // range order by a second kernel; split 1 when the workspace is too small)
+  const bool dma_tile = tile == 3 || tile == 4 || tile >= 9;
+  const bool pc = w->fmt == WQ_FMT_W8_PC;
+  if (dma_tile && (pc || tile >= 9) && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
-    if (tile == 3)
-      gemm_dma_w8pc_kernel<2, 2><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
-    else if (tile == 4)
-      gemm_dma_w8pc_kernel<1, 4><<<blocks, 256, 0, s>>>(qw, sc, x, y, (int)M, K, N);
-    else
-      gemm_dma_w8pc_kernel<2, 4><<<blocks, 512, 0, s>>>(qw, sc, x, y, (int)M, K, N);
+    int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : 1;
+    if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
+    S = std::min<int>(S, K / (DBK * (pc ? 1 : 2)));  // at least one step (group) per range
+    const dim3 grid(blocks, (unsigned)S);
+    float* part = (float*)ws;
+    if (pc) {
+      if (tile == 3)
+        gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+      else if (tile == 4)
+        gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+      else
+        gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+    } else if (w->fmt == WQ_FMT_W4_G128) {
+      gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, y, part, (int)M, K, N);
+    } else {
+      gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, y, part, (int)M, K, N);
+    }
     WQ_HIP_CHECK(hipGetLastError());
-    return WQ_OK;
-  }
-  // group-128 formats: tile 9 is the fp16 LDS-DMA kernel (2 x 4 waves; the 4-wave
-  // layouts of tiles 3 and 4 would spill its registers and take tile 1 instead)
-  if (tile == 9 && w->fmt != WQ_FMT_W8_PC && M * K < (int64_t(1) << 31)) {
-    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-    const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
-    if (w->fmt == WQ_FMT_W4_G128)
-      gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<blocks, 512, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
-    else
-      gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<blocks, 512, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
-    WQ_HIP_CHECK(hipGetLastError());
+    if (S > 1) {
+      const int64_t MN = M * N;
+      if (pc)
+        gemm_splitk_reduce_kernel<true><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      else
+        gemm_splitk_reduce_kernel<false><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      WQ_HIP_CHECK(hipGetLastError());
+    }
     return WQ_OK;
   }
   if (dma_tile) tile = 1;

@@ -87,6 +87,12 @@ constexpr int kSkinnyMaxM = 128;
 constexpr int kSkinnyMaxSplitTokens = 1024;
 constexpr int kSkinnyMaxBlocks = 1024;
 int gemm_skinny_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a skinny one
+// GEMM tiles kDmaSplitTile0 .. kDmaSplitTileLast are the 8-wave LDS-DMA tile with split-K
+// 2, 4, 8 over K steps (whole groups for group-128), capped so that the grid stays
+// within two workgroups per CU and the fp32 partials within kDmaSplitMaxBytes.
+constexpr int kDmaSplitTile0 = 10, kDmaSplitTileLast = 12;
+constexpr int64_t kDmaSplitMaxBytes = int64_t(256) << 20;
+int gemm_dma_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a split one
 // Workspace bytes a GEMM tile needs at this M (fp32 split-K partials; 0 for most tiles).
 size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile);
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,

@@ -149,10 +149,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
 /* Workspace bytes needed by wq_gemv / wq_gemm / wq_linear for this weight and M
  * under any split the library may pick (host only): fp32 partial sums of the
  * ranges of a cross-workgroup K split -- 32 * M * N * 4 bytes for M < 8 (GEMV); for
- * 8 <= M <= 128 the largest split * M * N * 4 of the skinny GEMM tiles (split <= 16,
- * split * M <= 1024, at most 2048 workgroups); 0 for M > 128.  The contents are
- * scratch: no initialisation is needed and nothing is kept between calls.  Calls
- * that share a workspace must not run concurrently. */
+ * M >= 8 the largest split * M * N * 4 of the split GEMM tiles: the skinny tiles (M <=
+ * 128; split <= 16, split * M <= 1024, at most 2048 workgroups) and the split-K
+ * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB); 0 when no
+ * split applies (a grid that already fills the CUs).  The contents are scratch: no
+ * initialisation is needed and nothing is kept between calls.  Calls that share a
+ * workspace must not run concurrently. */
 wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
 
 /* Decode GEMV, 1 <= M <= 7 (the "Key Optimizations" register-dequant GEMV of the
@@ -217,8 +219,9 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * scale is applied to the finished fp32 sum, group-128 scales to each group's fp32
  * partial -- except tile 9 for the group-128 formats, which stages the dequantised
  * weight rounded once to fp16, fp16(s (q - z)), against x converted to fp16 (a
- * workgroup whose x or dequantised weights leave the fp16 range recomputes its tile
- * the exact way).  w must be in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
+ * workgroup whose x or dequantised weights leave the fp16 range, or whose dequantised
+ * weights can exceed 16 in magnitude, recomputes its tile the exact way).  w must be
+ * in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
  *
  * tile: 0 = the tuned tile (a default by M and format when untuned), else
  *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;
@@ -226,13 +229,18 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
  *   4  as 3 with 1 x 4 waves;
  *   9  as 3 with 8 waves (2 x 4, two per SIMD); for group-128 the fp16 LDS-DMA tile
- *      above (tiles 3 and 4 for group-128, and 3, 4, 9 for other shapes: tile 1);
+ *      above (tiles 3 and 4 for group-128, and 3, 4, 9-12 for other shapes: tile 1);
+ *   10..12  tile 9 with split-K 2, 4, 8 (ranges of whole groups for group-128; fp32
+ *      partials in the workspace, added in range order), capped so that the grid
+ *      stays within 512 workgroups and the partials within 256 MiB (needs that
+ *      workspace, else WQ_ERR_WORKSPACE; with tile 0 and too small a workspace the
+ *      split drops to 1);
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
- * ws/ws_bytes may be NULL/0 for tiles 1-4.  Results are bit-identical from run to
- * run for a given tile. */
-#define WQ_GEMM_TILES 9
+ * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
+ * to run for a given tile. */
+#define WQ_GEMM_TILES 12
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 

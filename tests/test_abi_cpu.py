@@ -185,7 +185,7 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
     dsa = _desc(wqlib, fmt=1, s=0x2002)
     assert L.wq_gemv(C.byref(dsa), x, 1, y, 1, None, 0, None) == 3          # tiled scales misaligned
-    assert L.wq_gemm(C.byref(d), x, 16, y, 10, None, 0, None) == 1          # bad tile
+    assert L.wq_gemm(C.byref(d), x, 16, y, 13, None, 0, None) == 1          # bad tile
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
     assert L.wq_pack(None, C.byref(dc), None) == 1
@@ -194,11 +194,16 @@ def test_validation_rejects_before_any_device_work(wqlib):
     n = C.c_size_t()
     assert L.wq_workspace_size(C.byref(d), 1, C.byref(n)) == 0 and n.value == 32 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 7, C.byref(n)) == 0 and n.value == 32 * 7 * 1024 * 4
-    # M >= 8: the skinny GEMM's split-K partials (split <= 16, split * M <= 1024), none past M = 128
+    # M >= 8: split-K partials -- the skinny GEMM (split <= 16, split * M <= 1024, M <= 128)
+    # and the LDS-DMA tile (split <= 8, at most 512 workgroups of 256 x 256, <= 256 MiB)
     assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 16 * 8 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == 16 * 64 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 8 * 128 * 1024 * 4
-    assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 0
+    assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 8 * 129 * 1024 * 4
+    big = _desc(wqlib, K=5120, N=27648)
+    assert L.wq_workspace_size(C.byref(big), 512, C.byref(n)) == 0 and n.value == 2 * 512 * 27648 * 4
+    assert L.wq_workspace_size(C.byref(big), 2048, C.byref(n)) == 0 and n.value == 0   # 864 tiles: no split
+    assert L.wq_workspace_size(C.byref(big), 1024, C.byref(n)) == 0 and n.value == 0   # 432 tiles, x2 > 512
 
 
 def test_binding_constants_match_the_header(wqlib):

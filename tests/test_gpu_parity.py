@@ -54,9 +54,9 @@ def _rows_options(wq, fmt, M):
 
 
 def _fp16_staged(fmt, tile):
-    """The group-128 formats' LDS-DMA GEMM (tile 9) stages fp16(dequant(W)): its exact
-    selections return bf16(fp16(w)) rather than bf16(w)."""
-    return fmt != "w8pc" and tile == 9
+    """The group-128 formats' LDS-DMA GEMM (tile 9, and 10..12 with split-K) stages
+    fp16(dequant(W)): its exact selections return bf16(fp16(w)) rather than bf16(w)."""
+    return fmt != "w8pc" and tile >= 9
 
 
 def _selected(fmt, tile, w):
@@ -277,9 +277,10 @@ def test_identity_is_exact(wq, fmt):
 @pytest.mark.parametrize("fmt", ["w8g128", "w4g128"])
 def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
     """The fp16 LDS-DMA GEMM of the group-128 formats recomputes a workgroup's tile
-    exactly when its x or its dequantised weights leave the fp16 range (|x| > 65504,
-    or s (q - z) beyond it: scales above 4096 for uint4, 512 for int8); other
-    workgroups stay on the fp16 path, and |x| up to 65504 is exact in fp16."""
+    exactly when its x leaves the fp16 range (|x| > 65504) or its dequantised weights
+    can exceed 16 in magnitude (huge weights whose fp16 rounding would break the
+    tolerance where their products cancel); other workgroups stay on the fp16 path,
+    and |x| up to 65504 is exact in fp16."""
     K, N, M = 1024, 520, 300   # two 256-row blocks of x, three 256-column blocks
     W = synth.weight(105, K, N, synth.uses_outliers(fmt))
     W[300:308] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)  # huge weights in one 8-row block
@@ -294,7 +295,7 @@ def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
             xf[6, 900] = -3.0e5                 # beyond fp16: the first row block falls back
         x = OQ.bf16_rne_bits(xf.astype(np.float32))
         y_ref = OL.ref_linear(x, P)
-        for tile in (9, 1):
+        for tile in (9, 11, 1):   # 11: the same with split-K 4 (fp32 partials, also on the exact path)
             assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} {case} tile={tile}")
 
 
@@ -473,9 +474,9 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
     # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
-    skinny = range(5, 9)  # the split-K tiles
-    assert tile not in skinny, (tile, lat)
-    assert all((v < 0) == (t in skinny) for t, v in enumerate(lat, start=1)), (tile, lat)
+    split_tiles = list(range(5, 9)) + list(range(10, 13))  # the split-K tiles (skinny, LDS-DMA)
+    assert tile not in split_tiles, (tile, lat)
+    assert all((v < 0) == (t in split_tiles) for t, v in enumerate(lat, start=1)), (tile, lat)
 
 
 def test_error_paths_on_device(wq):
