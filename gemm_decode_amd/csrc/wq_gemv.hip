@@ -24,10 +24,13 @@
 //     every bf16 value of magnitude 2^-17 .. 65280; smaller magnitudes round to
 //     the fp16 subnormal grid, an absolute change below 2^-25); v_dot2_f32_f16
 //     multiplies, and (1024 + 128) * sum(x) removes the offset.
-//   * uint4 (nibbles interleaved by the gfx950 repack): (word >> 4i) &
-//     0x000F000F | 0x43004300 is the bf16 pair (128 + q_2i, 128 + q_2i+1)
-//     exactly; v_dot2_f32_bf16 with bf16 x, and (128 + z) * sum(x) per 32-element
-//     chunk removes offset and zero-point before the group scale.
+//   * uint4 (nibbles interleaved by the gfx950 repack, pair i = (q_2i, q_2i+1) at
+//     bits 4i and 16 + 4i): word & 0x000F000F | 0x43004300 is the bf16 pair
+//     (128 + q_0, 128 + q_1) exactly, word & 0x00F000F0 | 0x54005400 the fp16 pair
+//     (64 + q_2, 64 + q_3) (the nibbles sit on the fp16 units place), and the same
+//     on word >> 8 for pairs 2 and 3; v_dot2_f32_bf16 with bf16 x and v_dot2_f32_f16
+//     with fp16 x, and (128 + z) * sum(x) resp. (64 + z) * sum(x) over each kind of
+//     pair per 32-element chunk removes offset and zero-point before the group scale.
 //   * Removing an offset cancels: the fp32 partials carry terms up to
 //     (1152 / |q|) resp. (143 / |q - z|) times larger than the product itself, and
 //     their rounding grows with |x|.  A slice in which some |x| >= 512 therefore
@@ -185,11 +188,11 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
   const int t_full = nr == R ? (int)(row_bytes / kSliceBytes) : 0;  // slices with whole 1 KB rows
   const uint32_t rlane = (uint32_t)(sub * RR) * kSliceBytes + lane * 16;
   const uint32_t xlane = (uint32_t)lane * F::kChunk * 2;  // byte offset of this lane's x chunk in a slice
-  // The uint4 nibble mask and the bf16 128.0 pair live in registers the compiler cannot
-  // see through, so each code pair is one v_and_or_b32 (plus its shift) rather than a
+  // The uint4 nibble masks and the bf16 128.0 / fp16 64.0 pairs live in registers the
+  // compiler cannot see through, so each code pair is one v_and_or_b32 rather than a
   // separate and/or with two literal operands.
-  uint32_t nib_mask = 0x000F000Fu, bf16_128 = 0x43004300u;
-  if constexpr (kW4) asm volatile("" : "+v"(nib_mask), "+v"(bf16_128));
+  uint32_t nib_mask = 0x000F000Fu, bf16_128 = 0x43004300u, nib_mask_hi = 0x00F000F0u, f16_64 = 0x54005400u;
+  if constexpr (kW4) asm volatile("" : "+v"(nib_mask), "+v"(bf16_128), "+v"(nib_mask_hi), "+v"(f16_64));
 
   // The arithmetic of one slice, given its codes (RR rows) and x chunk.
   auto slice_math = [&](const uint4* cw, const uint32_t (*xb)[F::kXWords], int kk) {
@@ -307,33 +310,53 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
         }
       }
     } else if (!exact_path) {
-      // ---- uint4 group-128, offset path
-      float xs[M];
+      // ---- uint4 group-128, offset path.  Of each word's four nibble pairs, those at bits
+      // (0, 16) and, after one shift by 8, (8, 24) go under the bf16 128.0 pattern (bf16
+      // 128 + q, against bf16 x); those at (4, 20) and (12, 28) under the fp16 64.0
+      // pattern, which gives fp16 64 + q with no shift (against x converted to fp16).
+      // Both feed one fp32 sum per token, from which (128 + z) X_lo + (64 + z) X_hi is
+      // removed (X: the sums of x over the two kinds of positions).
+      uint32_t xh[M][8];  // fp16 x of the pairs at the (4, 20) and (12, 28) positions
+      float xs_lo[M], xs_hi[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float t = 0.f;
+        float tl = 0.f, th = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) t = dot2_bf16(xb[m][i], 0x3F803F80u, t);  // x . (1, 1)
-        xs[m] = t;
+        for (int wi = 0; wi < 4; ++wi) {
+          xh[m][2 * wi] = bf16x2_to_f16x2(xb[m][4 * wi + 1]);
+          xh[m][2 * wi + 1] = bf16x2_to_f16x2(xb[m][4 * wi + 3]);
+          tl = dot2_bf16(xb[m][4 * wi], 0x3F803F80u, tl);  // x . (1, 1)
+          tl = dot2_bf16(xb[m][4 * wi + 2], 0x3F803F80u, tl);
+          th = dot2_f16(xh[m][2 * wi], 0x3C003C00u, th);
+          th = dot2_f16(xh[m][2 * wi + 1], 0x3C003C00u, th);
+        }
+        xs_lo[m] = tl;
+        xs_hi[m] = th;
       }
 #pragma unroll
       for (int r = 0; r < RR; ++r) {
         const float sc = f16_to_f32(scale_of(r));
-        const float off = 128.f + (float)zero_of(r);
+        const float z = (float)zero_of(r);
         const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
         float t[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) t[m] = 0.f;
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi)
+        for (int wi = 0; wi < 4; ++wi) {
+          const uint32_t w = words[wi], w8 = w >> 8;
+          const uint32_t p0 = (w & nib_mask) | bf16_128, p1 = (w & nib_mask_hi) | f16_64;
+          const uint32_t p2 = (w8 & nib_mask) | bf16_128, p3 = (w8 & nib_mask_hi) | f16_64;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t p = ((words[wi] >> (4 * i)) & nib_mask) | bf16_128;
-#pragma unroll
-            for (int m = 0; m < M; ++m) t[m] = dot2_bf16(p, xb[m][4 * wi + i], t[m]);
+          for (int m = 0; m < M; ++m) {
+            t[m] = dot2_bf16(p0, xb[m][4 * wi], t[m]);
+            t[m] = dot2_f16(p1, xh[m][2 * wi], t[m]);
+            t[m] = dot2_bf16(p2, xb[m][4 * wi + 2], t[m]);
+            t[m] = dot2_f16(p3, xh[m][2 * wi + 1], t[m]);
           }
+        }
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, fmaf(-off, xs[m], t[m]), acc[r][m]);
+        for (int m = 0; m < M; ++m)
+          acc[r][m] = fmaf(sc, fmaf(-(128.f + z), xs_lo[m], fmaf(-(64.f + z), xs_hi[m], t[m])), acc[r][m]);
       }
     } else {
       // ---- uint4 group-128, exact path: bf16(q - z) pairs
