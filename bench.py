@@ -326,6 +326,42 @@ def summarize_counters(fetch_dir: str, write_dir: str, trace_dir: str | None, ou
     print("\n".join(lines))
 
 
+def summarize_mfma(pmc_dir: str, out_txt: str):
+    """Turn a rocprofv3 --pmc run of --profile-prefill (SQ_INSTS_MFMA,
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) into per-kernel matrix-core figures: busy
+    cycles per SIMD (the counter sums the 1024 SIMDs) and their ratio to GRBM_GUI_ACTIVE
+    / 8 (the GPU's busy cycles, summed over the 8 XCDs; a shader-clock fraction only if
+    that counter runs on the shader clock).  SQ_INSTS_MFMA x 32768 flops
+    (v_mfma_f32_32x32x16) must equal the algorithmic 2 M K N."""
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        rows += _read_csv_rows(f)
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "gemm_dma" not in name:
+            continue
+        kern = "gemm_dma_w8pc_kernel" if "w8pc" in name else "gemm_dma_g128_kernel"
+        d = per.setdefault(kern, {}).setdefault(int(r.get("Dispatch_Id", 0)), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = []
+    for (fmt, K, N, M, tile), kern in zip(PREFILL_PROFILE, ("gemm_dma_w8pc_kernel", "gemm_dma_g128_kernel")):
+        ds = list(per.get(kern, {}).values())
+        if not ds:
+            continue
+        mfma = float(np.mean([d["SQ_INSTS_MFMA"] for d in ds]))
+        busy = float(np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds])) / 1024.0
+        gpu = float(np.mean([d["GRBM_GUI_ACTIVE"] for d in ds])) / 8.0
+        lines.append(f"{kern} ({fmt} K={K} N={N} M={M} tile={tile}), {len(ds)} dispatches: "
+                     f"{mfma:.0f} MFMA instructions = {mfma * 32768 / (2.0 * M * K * N):.4f} x 2MKN/32768; "
+                     f"matrix cores busy {busy:.0f} cycles per SIMD (= {busy / 2.4e3:.1f} us at 2.4 GHz); "
+                     f"GRBM_GUI_ACTIVE / 8 = {gpu:.0f} cycles, ratio {100 * busy / gpu:.1f} %")
+    with open(out_txt, "a") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,7 +376,12 @@ def main():
                     help="run the prefill GEMM profile workload (for rocprofv3) and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
                     help="turn rocprofv3 runs of --profile-pass into the traffic record and a summary")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
+                    help="turn a rocprofv3 --pmc run of --profile-prefill into matrix-core busy fractions")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
