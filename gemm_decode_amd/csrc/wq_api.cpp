@@ -364,7 +364,7 @@ wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
     *bytes = gemv_workspace_bytes(w->N, M, kMaxSplit);
   } else {
     size_t b = 0;
-    for (int t = 1; t <= WQ_GEMM_TILES; ++t) b = std::max(b, gemm_workspace_bytes(w->N, M, t));
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t) b = std::max(b, gemm_workspace_full_bytes(w->fmt, w->K, w->N, M, t));
     *bytes = b;
   }
   return WQ_OK;

@@ -730,11 +730,35 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
   }
 }
 
-template <int FMT, int WM, int WN>
+// Eight bf16 values -> fp16 (v_cvt_pk_f16_f32: nearest even, Inf beyond the fp16 range).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float2_t f = {__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xFFFF0000u)};
+    o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// x converted to fp16 once per call, for the group-128 LDS-DMA tile when the workspace
+// has room: otherwise every workgroup converts the x chunks of each stage it loads, so
+// an x tile is converted once per 256-column block of the output.
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ xh,
+                                                       int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
+    xh[i] = bf16x8_to_f16x8(x[i]);
+}
+
+// XH: xd is x already in fp16 (x_to_f16_kernel); otherwise xd == x and the stages
+// are converted in LDS.  The exact fallback always reads the bf16 x.
+template <int FMT, int WM, int WN, bool XH = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
                                                                          const uint16_t* __restrict__ x,
+                                                                         const uint16_t* __restrict__ xd,
                                                                          uint16_t* __restrict__ y,
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N) {
@@ -806,7 +830,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   auto dma = [&](uint8_t* st, int ks) {
     const int k0 = (kb + min(ks, KS - 1)) * DBK;
 #pragma unroll
-    for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
+    for (int j = 0; j < XI; ++j) dma16(xd + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
     for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + DA_BYTES + (WI * wave + j) * 1024);
     const int g = k0 / kGroup;
@@ -818,19 +842,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   };
   // the x chunks this lane's own DMA brought into a stage, bf16 -> fp16 in place
   // (v_cvt_pk_f16_f32, nearest even: beyond fp16 range gives Inf)
+  // (nothing to do when x arrives as fp16: XH, converted by x_to_f16_kernel)
   auto convert = [&](uint8_t* st) {
+    if constexpr (XH) return;
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
       uint4* p = reinterpret_cast<uint4*>(st + (XI * wave + j) * 1024 + 16 * lane);
-      const uint4 v = *p;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float2_t f = {__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xFFFF0000u)};
-        o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
-      }
-      *p = make_uint4(o[0], o[1], o[2], o[3]);
+      *p = bf16x8_to_f16x8(*p);
     }
   };
   // ---- fragment addresses (bytes within a stage); the swizzles depend only on l32.
@@ -1559,6 +1577,18 @@ size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+size_t gemm_xh_offset(int64_t N, int64_t M, int S) {
+  const size_t part = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  return (part + 255) & ~(size_t)255;
+}
+
+size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
+  const size_t need = gemm_workspace_bytes(N, M, tile);
+  if (fmt == WQ_FMT_W8_PC || tile < 9 || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
+  const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : 1;
+  return gemm_xh_offset(N, M, S) + (size_t)M * (size_t)K * 2;
+}
+
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       void* ws, size_t ws_bytes, hipStream_t s) {
   const int K = (int)w->K, N = (int)w->N;
@@ -1601,10 +1631,28 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
         gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
       else
         gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
-    } else if (w->fmt == WQ_FMT_W4_G128) {
-      gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, y, part, (int)M, K, N);
     } else {
-      gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, y, part, (int)M, K, N);
+      // x in fp16 after the partials when the workspace has room for it
+      const size_t xh_off = gemm_xh_offset(N, M, S);
+      uint16_t* xh = nullptr;
+      if (ws && ws_bytes >= xh_off + (size_t)M * K * 2 && ((uintptr_t)ws + xh_off) % 16 == 0) {
+        xh = (uint16_t*)((uint8_t*)ws + xh_off);
+        const int64_t n8 = M * K / 8;
+        const unsigned cb = (unsigned)std::min<int64_t>((n8 + 255) / 256, 4096);
+        x_to_f16_kernel<<<cb, 256, 0, s>>>((const uint4*)x, (uint4*)xh, n8);
+        WQ_HIP_CHECK(hipGetLastError());
+      }
+      if (w->fmt == WQ_FMT_W4_G128) {
+        if (xh)
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4, true><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N);
+        else
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N);
+      } else {
+        if (xh)
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4, true><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N);
+        else
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N);
+      }
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {

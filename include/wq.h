@@ -152,9 +152,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * M >= 8 the largest split * M * N * 4 of the split GEMM tiles: the skinny tiles (M <=
  * 128; split <= 16, split * M <= 1024, at most 2048 workgroups) and the split-K
  * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB); 0 when no
- * split applies (a grid that already fills the CUs).  The contents are scratch: no
- * initialisation is needed and nothing is kept between calls.  Calls that share a
- * workspace must not run concurrently. */
+ * split applies (a grid that already fills the CUs).  For the group-128 formats the
+ * LDS-DMA tiles 9..12 also use M * K * 2 bytes after the partials (at a 256-byte
+ * boundary) for x converted to fp16 once per call; given less, they convert x inside
+ * every workgroup instead (same results, slower), so that part is never required.
+ * The contents are scratch: no initialisation is needed and nothing is kept between
+ * calls.  Calls that share a workspace must not run concurrently. */
 wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
 
 /* Decode GEMV, 1 <= M <= 7 (the "Key Optimizations" register-dequant GEMV of the

@@ -204,6 +204,11 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_workspace_size(C.byref(big), 512, C.byref(n)) == 0 and n.value == 2 * 512 * 27648 * 4
     assert L.wq_workspace_size(C.byref(big), 2048, C.byref(n)) == 0 and n.value == 0   # 864 tiles: no split
     assert L.wq_workspace_size(C.byref(big), 1024, C.byref(n)) == 0 and n.value == 0   # 432 tiles, x2 > 512
+    # group-128: the LDS-DMA tiles also take x in fp16 (M x K x 2) after the partials
+    big4 = _desc(wqlib, fmt=2, K=5120, N=27648)
+    assert L.wq_workspace_size(C.byref(big4), 2048, C.byref(n)) == 0 and n.value == 2048 * 5120 * 2
+    assert L.wq_workspace_size(C.byref(big4), 512, C.byref(n)) == 0 and \
+        n.value == 2 * 512 * 27648 * 4 + 512 * 5120 * 2
 
 
 def test_binding_constants_match_the_header(wqlib):

@@ -66,11 +66,12 @@ def _selected(fmt, tile, w):
     return OQ.bf16_rne_bits(np.ascontiguousarray(w, dtype=np.float32))
 
 
-def _run_gemm(wq, g, x_bits, tile=0):
+def _run_gemm(wq, g, x_bits, tile=0, with_ws=True):
     M = x_bits.shape[0]
     x = to_dev_bf16(x_bits)
     y = torch.empty((M, g.N), dtype=torch.bfloat16, device=DEV)
-    ws = wq.workspace(wq.wq_workspace_size(g, M))   # split-K partials of the skinny tiles
+    # split-K partials; for group-128 LDS-DMA tiles also x in fp16
+    ws = wq.workspace(wq.wq_workspace_size(g, M)) if with_ws else None
     wq.wq_gemm(g, x, y, tile=tile, ws=ws)
     torch.cuda.synchronize()
     return bf16_bits(y)
@@ -198,6 +199,8 @@ def test_gemm_small(wq, fmt, K, N, M):
     y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
     for tile in range(1, wq.GEMM_TILES + 1):
         assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"gemm {fmt} K={K} N={N} M={M} tile={tile}")
+    if fmt != "w8pc":   # tile 9 without the workspace's fp16 x: converts in LDS, same bits
+        assert np.array_equal(_run_gemm(wq, g, x, 9, with_ws=False), _run_gemm(wq, g, x, 9))
 
 
 EDGE = [("w8pc", 16, 8), ("w4g128", 128, 8), ("w8g128", 128, 24), ("w8pc", 64, 17),
@@ -297,6 +300,8 @@ def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
         y_ref = OL.ref_linear(x, P)
         for tile in (9, 11, 1):   # 11: the same with split-K 4 (fp32 partials, also on the exact path)
             assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} {case} tile={tile}")
+        # without a workspace tile 9 converts x to fp16 inside each workgroup: same bits
+        assert np.array_equal(_run_gemm(wq, g, x, 9, with_ws=False), _run_gemm(wq, g, x, 9)), f"{fmt} {case}"
 
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
@@ -415,6 +420,20 @@ def test_no_writes_outside_y_and_workspace(wq):
     assert torch.all(ybuf[:pad] == 12345) and torch.all(ybuf[pad + M * N:] == 12345)
     assert torch.all(wsbuf[:pad] == 0xAB) and torch.all(wsbuf[pad + nws:] == 0xCD)
     assert torch.all(yg[:pad] == 321) and torch.all(yg[pad + 40 * N:] == 321)
+    # the LDS-DMA tiles at M = 300: split-K partials and x in fp16 stay inside the workspace
+    Mg = 300
+    ng = wq.wq_workspace_size(g, Mg)
+    assert ng >= Mg * K * 2
+    wsg = torch.zeros(ng + 2 * pad, dtype=torch.uint8, device=DEV)
+    wsg[:pad] = 0xAB
+    wsg[pad + ng:] = 0xCD
+    ybig = torch.full((Mg * N + 2 * pad,), 321, dtype=torch.int16, device=DEV)
+    for tile in (9, 10, 11, 12):
+        wq.wq_gemm(g, to_dev_bf16(synth.activation(100, K, Mg)), ybig[pad:pad + Mg * N].view(torch.bfloat16),
+                   tile=tile, ws=wsg[pad:pad + ng])
+    torch.cuda.synchronize()
+    assert torch.all(wsg[:pad] == 0xAB) and torch.all(wsg[pad + ng:] == 0xCD)
+    assert torch.all(ybig[:pad] == 321) and torch.all(ybig[pad + Mg * N:] == 321)
 
 
 def test_hip_graph_replay(wq):
