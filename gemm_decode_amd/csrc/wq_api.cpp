@@ -128,7 +128,7 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 // Untuned GEMM tile: the skinny kernel up to kSkinnyMaxM tokens, with the smallest
 // split-K that gives about two workgroups per CU; above that the 8-wave LDS-DMA kernel
 // (tile 9) for every format, split over K (tiles 10..12) when its tiles would not
-// occupy half the CUs.
+// occupy half the CUs, or with its partial last round split over K (tile 13).
 int default_tile(const wq_weight* w, int64_t M) {
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
@@ -142,7 +142,12 @@ int default_tile(const wq_weight* w, int64_t M) {
   // that many workgroups (measured on MI355X: at M = 512, N = 5120 split 4 beats 8, and
   // 160 tiles run best unsplit)
   const int64_t blocks = ((M + 255) / 256) * ((w->N + 255) / 256);
-  if (blocks >= 128) return kDefaultTile;
+  if (blocks >= 128) {
+    // a partial last round of tiles that would leave at least half the CUs idle: tile 13
+    // spreads it over K (it needs a workspace; without one it runs as tile 9)
+    int tail0 = 0;
+    return gemm_dma_tail(M, w->N, &tail0) > 1 ? kDmaTailTile : kDefaultTile;
+  }
   int t = kDmaSplitTile0;
   while (t < kDmaSplitTileLast && blocks * gemm_dma_split(t, M, w->N) < 128 &&
          gemm_dma_split(t + 1, M, w->N) > gemm_dma_split(t, M, w->N))

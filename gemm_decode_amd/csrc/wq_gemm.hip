@@ -17,6 +17,8 @@
 //     second fp32 accumulator that is scaled by s[n][g] and folded in at the end
 //     of every 128-element group.
 #include "wq_internal.h"
+#include <algorithm>
+#include <atomic>
 
 namespace wq {
 namespace {
@@ -427,6 +429,45 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(g) : "memory", "m0");
 }
 
+// Which 256 x 256 output tile and which K range a workgroup of the LDS-DMA kernels
+// takes, and where its fp32 partials go.  Blocks 0 .. 8 ceil(tail0 / 8) - 1 take
+// tiles 0 .. tail0 - 1 (whole, or split over gridDim.y), spread XCD by XCD (block b
+// runs on XCD b % 8, which gets a contiguous run of tiles: neighbouring tiles share
+// x rows or weight columns in its L2).  The blocks after them take the tiles from
+// tail0 on in tailS K ranges each -- a last round of tiles that would leave CUs idle
+// -- also XCD by XCD.  Partials: [S][M][N] for the gridDim.y split; for a split tail
+// tile its own [tailS][256][256] block, tile by tile from tail0.
+struct DmaWork {
+  int lin, S, sp;     // tile (XCD-aware linear index), K ranges of the tile, this range
+  size_t poff;        // partials of this range: part[poff + (m - pm0) * ppitch + n - pn0]
+  int ppitch, pm0, pn0;
+};
+__device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, DmaWork& w) {
+  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN, total = mblocks * nblocks;
+  const int b = blockIdx.x, per_full = (tail0 + 7) / 8;
+  if (b < 8 * per_full) {
+    w.lin = (b & 7) * per_full + (b >> 3);
+    if (w.lin >= tail0) return false;
+    w.S = gridDim.y;
+    w.sp = blockIdx.y;
+    w.poff = (size_t)w.sp * M * N;
+    w.ppitch = N;
+    w.pm0 = w.pn0 = 0;
+  } else {
+    const int u = b - 8 * per_full, nu = tailS * (total - tail0), per_xcd = (nu + 7) / 8;
+    const int lu = (u & 7) * per_xcd + (u >> 3);
+    if (lu >= nu) return false;
+    w.lin = tail0 + lu / tailS;
+    w.S = tailS;
+    w.sp = lu % tailS;
+    w.poff = (size_t)lu * DBM * DBN;  // [tile - tail0][sp] blocks
+    w.ppitch = DBN;
+    w.pm0 = (w.lin % mblocks) * DBM;
+    w.pn0 = (w.lin / mblocks) * DBN;
+  }
+  return true;
+}
+
 // WM x WN waves (2 x 2 or 1 x 4) over the 256 x 256 tile: each wave owns RB = 8 / WM
 // row blocks and CB = 8 / WN column blocks of 32.  With 1 x 4 every code chunk is
 // converted by exactly one wave (half the conversion work of 2 x 2) at the price of
@@ -437,7 +478,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
                                                                          const uint16_t* __restrict__ x,
                                                                          uint16_t* __restrict__ y,
                                                                          float* __restrict__ part, int M, int K,
-                                                                         int N) {
+                                                                         int N, int tail0,
+                                                                         int tailS) {
   constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
   constexpr int XI = 32 / NW, WI = 16 / NW;  // x and code DMA instructions per wave and step
   constexpr int kDmaPerStep = XI + WI;
@@ -446,12 +488,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGE];
 
-  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN;
-  const int total = mblocks * nblocks;
-  const int per_xcd = (total + 7) / 8;
-  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (lin >= total) return;
-  const int nb = lin / mblocks, mb = lin % mblocks;
+  DmaWork wk;
+  if (!dma_work(M, N, tail0, tailS, wk)) return;
+  const int mblocks = (M + DBM - 1) / DBM;
+  const int nb = wk.lin / mblocks, mb = wk.lin % mblocks;
   const int n0 = nb * DBN, m0 = mb * DBM;
 
   const int lane = threadIdx.x & 63;
@@ -460,7 +500,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   const int l32 = lane & 31, lh = lane >> 5;
   // split-K over gridDim.y: this workgroup's steps kb .. kb + KS - 1 (whole groups for
   // the group-128 formats); with S > 1 it writes fp32 partials (see the epilogue)
-  const int S = gridDim.y, sp = blockIdx.y, U = K / (DBK * KUNIT);
+  const int S = wk.S, sp = wk.sp, U = K / (DBK * KUNIT);
   const int kb = KUNIT * (int)((int64_t)sp * U / S), KS = KUNIT * (int)((int64_t)(sp + 1) * U / S) - kb;
 
   // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = XI wave + j.
@@ -621,7 +661,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
         if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
-        else part[((size_t)sp * M + m) * N + n] = acc[i][j][a];
+        else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = acc[i][j][a];
       }
   }
 }
@@ -682,7 +722,8 @@ template <int FMT>
 __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                                 const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
                                 uint16_t* __restrict__ y, float* __restrict__ part, int M, int K, int N,
-                                int m0, int n0, int g0, int g1, int sp, int S, int wave, int NW) {
+                                int m0, int n0, int g0, int g1, int S, size_t poff, int ppitch, int pm0,
+                                int pn0, int wave, int NW) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   const int G = K / kGroup;
@@ -725,7 +766,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
       const int mm = m0 + 32 * bi + 8 * (a >> 2) + 4 * lh + (a & 3);
       if (mm >= M) continue;
       if (S == 1) y[(size_t)mm * N + nn] = __builtin_bit_cast(uint16_t, (__bf16)acc[a]);
-      else part[((size_t)sp * M + mm) * N + nn] = acc[a];
+      else part[poff + (size_t)(mm - pm0) * ppitch + (nn - pn0)] = acc[a];
     }
   }
 }
@@ -761,7 +802,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
                                                                          const uint16_t* __restrict__ xd,
                                                                          uint16_t* __restrict__ y,
                                                                          float* __restrict__ part, int M, int K,
-                                                                         int N) {
+                                                                         int N, int tail0,
+                                                                         int tailS) {
   using F = G128Dma<FMT>;
   constexpr bool kW4 = F::kW4;
   constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
@@ -775,12 +817,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   __shared__ int wave_flag[NW];
   __shared__ float wave_max[NW];
 
-  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN;
-  const int total = mblocks * nblocks;
-  const int per_xcd = (total + 7) / 8;
-  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (lin >= total) return;
-  const int nb = lin / mblocks, mb = lin % mblocks;
+  DmaWork wk;
+  if (!dma_work(M, N, tail0, tailS, wk)) return;
+  const int mblocks = (M + DBM - 1) / DBM;
+  const int nb = wk.lin / mblocks, mb = wk.lin % mblocks;
   const int n0 = nb * DBN, m0 = mb * DBM;
 
   const int lane = threadIdx.x & 63;
@@ -789,7 +829,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   const int l32 = lane & 31, lh = lane >> 5;
   // split-K over gridDim.y: this workgroup's steps kb .. kb + KS - 1 (whole groups for
   // the group-128 formats); with S > 1 it writes fp32 partials (see the epilogue)
-  const int S = gridDim.y, sp = blockIdx.y, U = K / (DBK * KUNIT);
+  const int S = wk.S, sp = wk.sp, U = K / (DBK * KUNIT);
   const int kb = KUNIT * (int)((int64_t)sp * U / S), KS = KUNIT * (int)((int64_t)(sp + 1) * U / S) - kb;
   const int G = K / kGroup;
   const int row_bytes = kW4 ? K / 2 : K;
@@ -1088,8 +1128,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   }
   constexpr float kCodeMax = kW4 ? 15.f : 127.f;  // largest |q - z| or |q|
   if (any || !(kCodeMax * ws <= 16.f)) {  // (NaN scales fail the comparison)
-    g128_tile_exact<FMT>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, sp, S,
-                         wave, NW);
+    g128_tile_exact<FMT>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, S,
+                         wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
     return;
   }
   // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block;
@@ -1105,7 +1145,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
         if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][a]);
-        else part[((size_t)sp * M + m) * N + n] = acc[i][j][a];
+        else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = acc[i][j][a];
       }
   }
 }
@@ -1529,6 +1569,24 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   y[i] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
 }
 
+// The split tail tiles of tile 13: y = the ranges' fp32 partials added in range order
+// (times the channel scale for per-channel W8).  blockIdx.y: tail tile, blockIdx.x:
+// its row, threadIdx.x: its column.
+template <bool kPerChannel>
+__global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __restrict__ part,
+                                                                const uint16_t* __restrict__ scales,
+                                                                uint16_t* __restrict__ y, int M, int N,
+                                                                int tail0, int S) {
+  const int mblocks = (M + DBM - 1) / DBM, lin = tail0 + (int)blockIdx.y;
+  const int m = (lin % mblocks) * DBM + (int)blockIdx.x, n = (lin / mblocks) * DBN + (int)threadIdx.x;
+  if (m >= M || n >= N) return;
+  const float* p = part + (size_t)blockIdx.y * S * DBM * DBN + blockIdx.x * DBN + threadIdx.x;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += p[(size_t)s * DBM * DBN];
+  const float sc = kPerChannel ? bf16_to_f32(scales[n]) : 1.f;
+  y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+}
+
 template <int FMT>
 wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, const uint16_t* x,
                         uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st) {
@@ -1572,21 +1630,45 @@ int gemm_dma_split(int tile, int64_t M, int64_t N) {
   return S;
 }
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+    return kDefaultCUs;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+int gemm_dma_tail(int64_t M, int64_t N, int* tail0) {
+  const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+  const int cus = device_cus();
+  *tail0 = (int)total;
+  const int64_t r = total % cus;
+  if (total <= cus || r == 0 || 2 * r > cus) return 1;  // no partial last round to spread
+  *tail0 = (int)(total - r);
+  return (int)std::min<int64_t>(kDmaTailMaxSplit, cus / r);
+}
+
 size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
+  if (tile == kDmaTailTile) {
+    int tail0 = 0;
+    const int S = gemm_dma_tail(M, N, &tail0);
+    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+    return S > 1 ? (size_t)S * (size_t)(total - tail0) * DBM * DBN * sizeof(float) : 0;
+  }
   const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : gemm_skinny_split(tile, M, N);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-size_t gemm_xh_offset(int64_t N, int64_t M, int S) {
-  const size_t part = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
-  return (part + 255) & ~(size_t)255;
-}
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
   const size_t need = gemm_workspace_bytes(N, M, tile);
   if (fmt == WQ_FMT_W8_PC || tile < 9 || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
-  const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : 1;
-  return gemm_xh_offset(N, M, S) + (size_t)M * (size_t)K * 2;
+  return round256(need) + (size_t)M * (size_t)K * 2;
 }
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
@@ -1618,22 +1700,35 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const bool pc = w->fmt == WQ_FMT_W8_PC;
   if (dma_tile && (pc || tile >= 9) && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-    const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
-    int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : 1;
-    if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
-    S = std::min<int>(S, K / (DBK * (pc ? 1 : 2)));  // at least one step (group) per range
+    const int kcap = K / (DBK * (pc ? 1 : 2));  // at least one step (group) per K range
+    int S = 1, tail0 = (int)total, tailS = 1;
+    if (tile == kDmaTailTile) {
+      tailS = std::min(gemm_dma_tail(M, N, &tail0), kcap);
+      if (tailS <= 1 || !ws || ws_bytes < gemm_workspace_bytes(N, M, tile)) {
+        tailS = 1;
+        tail0 = (int)total;
+      }
+    } else if (tile >= kDmaSplitTile0) {
+      S = gemm_dma_split(tile, M, N);
+      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
+      S = std::min(S, kcap);
+    }
+    const int64_t ntail = total - tail0;
+    const unsigned blocks = (unsigned)(8 * ((tail0 + 7) / 8) + 8 * ((tailS * ntail + 7) / 8));
     const dim3 grid(blocks, (unsigned)S);
     float* part = (float*)ws;
+    const size_t part_bytes = tailS > 1 ? (size_t)tailS * ntail * DBM * DBN * sizeof(float)
+                                        : (S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
     if (pc) {
       if (tile == 3)
-        gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+        gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
       else if (tile == 4)
-        gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+        gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
       else
-        gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N);
+        gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
     } else {
       // x in fp16 after the partials when the workspace has room for it
-      const size_t xh_off = gemm_xh_offset(N, M, S);
+      const size_t xh_off = round256(part_bytes);
       uint16_t* xh = nullptr;
       if (ws && ws_bytes >= xh_off + (size_t)M * K * 2 && ((uintptr_t)ws + xh_off) % 16 == 0) {
         xh = (uint16_t*)((uint8_t*)ws + xh_off);
@@ -1644,14 +1739,18 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       }
       if (w->fmt == WQ_FMT_W4_G128) {
         if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4, true><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N);
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4, true>
+              <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, tail0, tailS);
         else
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N);
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4>
+              <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, tail0, tailS);
       } else {
         if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4, true><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N);
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4, true>
+              <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, tail0, tailS);
         else
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N);
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4>
+              <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, tail0, tailS);
       }
     }
     WQ_HIP_CHECK(hipGetLastError());
@@ -1661,6 +1760,14 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
         gemm_splitk_reduce_kernel<true><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
       else
         gemm_splitk_reduce_kernel<false><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      WQ_HIP_CHECK(hipGetLastError());
+    }
+    if (tailS > 1) {
+      const dim3 rg(DBM, (unsigned)ntail);
+      if (pc)
+        gemm_tail_reduce_kernel<true><<<rg, DBN, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+      else
+        gemm_tail_reduce_kernel<false><<<rg, DBN, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;

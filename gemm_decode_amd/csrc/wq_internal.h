@@ -93,13 +93,21 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N);  // 0 when the tile is no
 constexpr int kDmaSplitTile0 = 10, kDmaSplitTileLast = 12;
 constexpr int64_t kDmaSplitMaxBytes = int64_t(256) << 20;
 int gemm_dma_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a split one
+// GEMM tile kDmaTailTile is tile 9 with the tiles of a partial last round (fewer than
+// half the CUs' worth) split over K into up to kDmaTailMaxSplit ranges, so that round
+// spreads over the idle CUs; gemm_dma_tail returns that split (1: nothing to split)
+// and sets *tail0 to the number of tiles that stay whole.
+constexpr int kDmaTailTile = 13, kDmaTailMaxSplit = 4;
+int gemm_dma_tail(int64_t M, int64_t N, int* tail0);
+// Compute units of the current device (kDefaultCUs, MI355X's count, if it cannot be queried).
+constexpr int kDefaultCUs = 256;
+int device_cus();
 // Workspace bytes a GEMM tile needs at this M (fp32 split-K partials; 0 for most tiles).
 size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile);
 // Bytes with which a tile takes its fastest path: for the group-128 LDS-DMA tiles
-// (9..12) also x converted to fp16 once per call (M x K x 2 bytes after the partials,
-// at gemm_xh_offset); without that room the tile converts x in LDS.
+// (9..13) also x converted to fp16 once per call (M x K x 2 bytes after the partials,
+// at a 256-byte boundary); without that room the tile converts x in LDS.
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile);
-size_t gemm_xh_offset(int64_t N, int64_t M, int S);
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       void* ws, size_t ws_bytes, hipStream_t s);
 

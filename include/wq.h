@@ -151,9 +151,10 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * ranges of a cross-workgroup K split -- 32 * M * N * 4 bytes for M < 8 (GEMV); for
  * M >= 8 the largest split * M * N * 4 of the split GEMM tiles: the skinny tiles (M <=
  * 128; split <= 16, split * M <= 1024, at most 2048 workgroups) and the split-K
- * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB); 0 when no
- * split applies (a grid that already fills the CUs).  For the group-128 formats the
- * LDS-DMA tiles 9..12 also use M * K * 2 bytes after the partials (at a 256-byte
+ * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB) -- or the
+ * partials of tile 13's split last round (sized for the current device's CU count, 256
+ * when none is visible); 0 when no split applies.  For the group-128 formats the
+ * LDS-DMA tiles 9..13 also use M * K * 2 bytes after the partials (at a 256-byte
  * boundary) for x converted to fp16 once per call; given less, they convert x inside
  * every workgroup instead (same results, slower), so that part is never required.
  * The contents are scratch: no initialisation is needed and nothing is kept between
@@ -232,18 +233,24 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
  *   4  as 3 with 1 x 4 waves;
  *   9  as 3 with 8 waves (2 x 4, two per SIMD); for group-128 the fp16 LDS-DMA tile
- *      above (tiles 3 and 4 for group-128, and 3, 4, 9-12 for other shapes: tile 1);
+ *      above (tiles 3 and 4 for group-128, and 3, 4, 9-13 for other shapes: tile 1);
  *   10..12  tile 9 with split-K 2, 4, 8 (ranges of whole groups for group-128; fp32
  *      partials in the workspace, added in range order), capped so that the grid
  *      stays within 512 workgroups and the partials within 256 MiB (needs that
  *      workspace, else WQ_ERR_WORKSPACE; with tile 0 and too small a workspace the
  *      split drops to 1);
+ *   13  tile 9 with the tiles of a partial last round split over K: when the tile
+ *      count exceeds the CU count C by r <= C/2 (864 = 3 x 256 + 96 at M = 2048, N =
+ *      27648), the last r tiles run as min(4, C / r) K ranges each, writing a 256 x 256
+ *      fp32 block per range to the workspace (r x ranges x 256 KiB; needs it, else
+ *      WQ_ERR_WORKSPACE; with tile 0 and too small a workspace it runs as tile 9), and a
+ *      second kernel adds them in range order; other shapes: tile 9;
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
- * to run for a given tile. */
-#define WQ_GEMM_TILES 12
+ * to run for a given tile, device and workspace size. */
+#define WQ_GEMM_TILES 13
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -272,7 +279,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 12
+#define WQ_TUNE_LAT_SLOTS 13
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

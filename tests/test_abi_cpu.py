@@ -185,7 +185,7 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
     dsa = _desc(wqlib, fmt=1, s=0x2002)
     assert L.wq_gemv(C.byref(dsa), x, 1, y, 1, None, 0, None) == 3          # tiled scales misaligned
-    assert L.wq_gemm(C.byref(d), x, 16, y, 13, None, 0, None) == 1          # bad tile
+    assert L.wq_gemm(C.byref(d), x, 16, y, 14, None, 0, None) == 1          # bad tile
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
     assert L.wq_pack(None, C.byref(dc), None) == 1
@@ -202,11 +202,14 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 8 * 129 * 1024 * 4
     big = _desc(wqlib, K=5120, N=27648)
     assert L.wq_workspace_size(C.byref(big), 512, C.byref(n)) == 0 and n.value == 2 * 512 * 27648 * 4
-    assert L.wq_workspace_size(C.byref(big), 2048, C.byref(n)) == 0 and n.value == 0   # 864 tiles: no split
-    assert L.wq_workspace_size(C.byref(big), 1024, C.byref(n)) == 0 and n.value == 0   # 432 tiles, x2 > 512
+    # 864 tiles = 3 rounds of 256 CUs + 96: tile 13 splits those 96 over K in 2 (a
+    # 256 x 256 fp32 block per range; sized for 256 CUs when no device is visible)
+    tail = 2 * 96 * 256 * 256 * 4
+    assert L.wq_workspace_size(C.byref(big), 2048, C.byref(n)) == 0 and n.value == tail
+    assert L.wq_workspace_size(C.byref(big), 1024, C.byref(n)) == 0 and n.value == 0   # 432 tiles: 176 left over
     # group-128: the LDS-DMA tiles also take x in fp16 (M x K x 2) after the partials
     big4 = _desc(wqlib, fmt=2, K=5120, N=27648)
-    assert L.wq_workspace_size(C.byref(big4), 2048, C.byref(n)) == 0 and n.value == 2048 * 5120 * 2
+    assert L.wq_workspace_size(C.byref(big4), 2048, C.byref(n)) == 0 and n.value == tail + 2048 * 5120 * 2
     assert L.wq_workspace_size(C.byref(big4), 512, C.byref(n)) == 0 and \
         n.value == 2 * 512 * 27648 * 4 + 512 * 5120 * 2
 

@@ -397,6 +397,32 @@ def test_dispatch_boundary_m7_m8(wq):
             assert_parity(_run_gemm(wq, g, x)[:, rows], y_ref, "gemm M=7")
 
 
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_gemm_tail_round_split(wq, fmt):
+    """Tile 13: 2 x 140 tiles of 256 x 256 (ragged in M and N) leave 24 tiles for a
+    last round on a 256-CU device, which are split over K into 4 fp32 partials (their
+    own block per range) and added by a second kernel; compared with the oracle everywhere,
+    also with huge weights in a tail tile (group-128: the exact fallback writes those
+    partials); the default tile without a workspace runs it as tile 9."""
+    K, N, M = 1024, 35800, 300
+    W = synth.weight(107, K, N, synth.uses_outliers(fmt))
+    if fmt != "w8pc":
+        W[35000:35008] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)
+    g, _ = quantize_on_gpu(wq, W, fmt)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    total = 2 * 140
+    if total > cus and 2 * (total % cus) <= cus:   # 256 CUs: 24 tiles left, split 4
+        r = total % cus
+        assert wq.wq_workspace_size(g, M) >= min(4, cus // r) * r * 256 * 256 * 4
+    x = synth.activation(107, K, M)
+    y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
+    # tile 0 picks 13 here; without a workspace it runs as tile 9, tile 13 itself refuses
+    for tile, with_ws in ((13, True), (0, True), (0, False), (9, True)):
+        assert_parity(_run_gemm(wq, g, x, tile, with_ws), y_ref, f"{fmt} tile={tile} ws={with_ws}")
+    with pytest.raises(wq.WqError):
+        _run_gemm(wq, g, x, 13, with_ws=False)
+
+
 def test_no_writes_outside_y_and_workspace(wq):
     """Canary bytes around y and the workspace stay untouched (ragged N tile,
     split-K)."""
