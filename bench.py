@@ -235,7 +235,7 @@ def profile_pass(steps: int = 10, replays: int = 2):
     log(f"profile pass: {replays} replays x {steps} steps x {len(pools)} GEMV launches")
 
 
-PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 9), ("w4g128", 5120, 27648, 2048, 9)]
+PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 13), ("w4g128", 5120, 27648, 2048, 13)]
 
 
 def profile_prefill(calls: int = 10):
@@ -503,7 +503,31 @@ def run_detail(wq, torch, args) -> dict:
     out["prefill_gemm"] = {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
                            for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
                            for M in (8, 64, 512, 2048)}
+    out["reference_bf16_gemm"] = reference_bf16_gemm(torch)
     return out
+
+
+def reference_bf16_gemm(torch, M: int = 2048, K: int = 5120, N: int = 27648) -> dict:
+    """Context, not this library: the vendor BLAS (torch.mm -> hipBLASLt) on a plain
+    bf16 x bf16 product of the prefill shape, timed like the detail lines (graph replay
+    over 4 distinct B matrices), as the matrix-core rate a library GEMM reaches on this
+    device at this shape."""
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    bs = [torch.randn(K, N, device="cuda", dtype=torch.bfloat16) for _ in range(4)]
+    i = [0]
+
+    def fn():
+        torch.mm(a, bs[i[0]])
+        i[0] = (i[0] + 1) % len(bs)
+
+    per = time_graph(torch, fn, 8) / 8
+    tf = 2.0 * M * K * N / (per / 1e3) / 1e12
+    log(f"reference torch.mm bf16 M={M} K={K} N={N}: {per * 1e3:.1f} us {tf:.1f} TF/s")
+    del a, bs
+    torch.cuda.empty_cache()
+    return {"what": "torch.mm bf16 (hipBLASLt), not this library", "M": M, "K": K, "N": N,
+            "us": round(per * 1e3, 3), "TFLOP/s": round(tf, 2),
+            "pct_mfma": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)}
 
 
 if __name__ == "__main__":

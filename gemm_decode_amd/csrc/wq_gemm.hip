@@ -1570,21 +1570,39 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
 }
 
 // The split tail tiles of tile 13: y = the ranges' fp32 partials added in range order
-// (times the channel scale for per-channel W8).  blockIdx.y: tail tile, blockIdx.x:
-// its row, threadIdx.x: its column.
+// (times the channel scale for per-channel W8).  blockIdx.y: tail tile; a thread takes
+// 8 consecutive columns of one row (32 threads per row, 8 rows per block, blockIdx.x:
+// the row group).
 template <bool kPerChannel>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __restrict__ part,
                                                                 const uint16_t* __restrict__ scales,
                                                                 uint16_t* __restrict__ y, int M, int N,
                                                                 int tail0, int S) {
   const int mblocks = (M + DBM - 1) / DBM, lin = tail0 + (int)blockIdx.y;
-  const int m = (lin % mblocks) * DBM + (int)blockIdx.x, n = (lin / mblocks) * DBN + (int)threadIdx.x;
+  const int r = (int)blockIdx.x * 8 + (int)(threadIdx.x >> 5), c = 8 * (int)(threadIdx.x & 31);
+  const int m = (lin % mblocks) * DBM + r, n = (lin / mblocks) * DBN + c;
   if (m >= M || n >= N) return;
-  const float* p = part + (size_t)blockIdx.y * S * DBM * DBN + blockIdx.x * DBN + threadIdx.x;
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += p[(size_t)s * DBM * DBN];
-  const float sc = kPerChannel ? bf16_to_f32(scales[n]) : 1.f;
-  y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+  const float* p = part + (size_t)blockIdx.y * S * DBM * DBN + r * DBN + c;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(p + (size_t)s * DBM * DBN);
+    const float4 b = *reinterpret_cast<const float4*>(p + (size_t)s * DBM * DBN + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  uint16_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float sc = kPerChannel ? bf16_to_f32(scales[min(n + j, N - 1)]) : 1.f;
+    o[j] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v[j]));
+  }
+  uint16_t* yo = y + (size_t)m * N + n;
+  if (N % 8 == 0) {  // n + 8 <= N and 16-byte aligned
+    *reinterpret_cast<uint4*>(yo) = make_uint4(o[0] | (uint32_t)o[1] << 16, o[2] | (uint32_t)o[3] << 16,
+                                               o[4] | (uint32_t)o[5] << 16, o[6] | (uint32_t)o[7] << 16);
+  } else {
+    for (int j = 0; j < 8 && n + j < N; ++j) yo[j] = o[j];
+  }
 }
 
 template <int FMT>
@@ -1763,11 +1781,11 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       WQ_HIP_CHECK(hipGetLastError());
     }
     if (tailS > 1) {
-      const dim3 rg(DBM, (unsigned)ntail);
+      const dim3 rg(DBM / 8, (unsigned)ntail);
       if (pc)
-        gemm_tail_reduce_kernel<true><<<rg, DBN, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       else
-        gemm_tail_reduce_kernel<false><<<rg, DBN, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<false><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;
