@@ -12,6 +12,9 @@ What it computes (plain, slow, obviously correct; NumPy only):
 * ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
   chunked along N; sampled-column variants for full-size checks; the
   comparison statistics with the per-element tolerance.
+* ``topk``   -- the k best bf16 logits of a row and the token drawn from them
+  with a temperature and a caller-supplied uniform draw (the LM head + top-k
+  step of the tileInfer README's feature list; reading in its docstring).
 
 Passages followed:
 
@@ -35,3 +38,4 @@ from .quant import (  # noqa: F401
 from .linear import (  # noqa: F401
     compare, ref_linear, ref_linear_columns, token_count, use_gemv,
 )
+from .topk import ref_topk_sample, sample_row, topk_row  # noqa: F401

@@ -16,6 +16,7 @@ import numpy as np
 
 import oracle.linear as OL
 import oracle.quant as OQ
+import oracle.topk as OT
 import synth
 from golden_io import num, read_fixture
 
@@ -365,6 +366,81 @@ def pin_dispatch():
     assert OL.use_gemv(1) and OL.use_gemv(7) and not OL.use_gemv(8) and not OL.use_gemv(2048)
 
 
+# ------------------------------------------------------------------- top-k, sampling
+def _bf16_num(b: int):
+    """A bf16 bit pattern as a Fraction, or None for NaN (an independent decoder)."""
+    e, m = (b >> 7) & 0xFF, b & 0x7F
+    if e == 0xFF:
+        return None if m else (Fraction(10) ** 40 if not b & 0x8000 else -Fraction(10) ** 40)
+    v = Fraction(m, 128) * Fraction(2) ** -126 if e == 0 else (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+    return -v if b & 0x8000 else v
+
+
+def pin_topk_golden():
+    """Hand-derived example (tests/golden/topk_worked.txt): order with ties, signed
+    zeros and a NaN; tokens drawn at temperatures 1, 0.5 and 0."""
+    head, blocks = read_fixture("topk_worked.txt")
+    bits = np.array([num(t) for t in blocks["logits"][0]], dtype=np.uint16)
+    for key in ("top5", "top8"):
+        want = [int(t) for t in head[key]]
+        idx, kb = OT.topk_row(bits, len(want))
+        assert idx.tolist() == want, (key, idx.tolist())
+        assert np.array_equal(kb, bits[want])
+    for k, T, u, tok in blocks["draws"]:
+        idx, kb = OT.topk_row(bits, int(k))
+        assert OT.sample_row(kb, idx, float(T), float(u)) == int(tok), (k, T, u, tok)
+
+
+def pin_topk_defining_property(seed=31, V=48):
+    """Brute force over pairs on a row with many ties (a small value set, both zeros,
+    a NaN, infinities): for every k the kept entries beat every dropped one, and each
+    kept entry beats the next, where a beats b iff a is a number and b is NaN, or
+    value(a) > value(b), or the values are equal and index(a) < index(b)."""
+    rng = np.random.default_rng(seed)
+    pool = [0x3F80, 0xBF80, 0x4000, 0x0000, 0x8000, 0x7FC0, 0x7F80, 0xFF80, 0x3F81]
+    bits = np.array([pool[i] for i in rng.integers(0, len(pool), V)], dtype=np.uint16)
+
+    def beats(a, b):
+        va, vb = _bf16_num(int(bits[a])), _bf16_num(int(bits[b]))
+        if va is None or vb is None:
+            return va is not None and vb is None or (va is None and vb is None and a < b)
+        return va > vb or (va == vb and a < b)
+
+    for k in range(1, V + 1):
+        idx, _ = OT.topk_row(bits, k)
+        kept = [int(i) for i in idx]
+        assert len(set(kept)) == k
+        dropped = set(range(V)) - set(kept)
+        assert all(beats(a, b) for a in kept for b in dropped), k
+        assert all(beats(kept[i], kept[i + 1]) for i in range(k - 1)), k
+
+
+def pin_topk_sampling_closed_forms():
+    """Equal logits give p = 1/k each, so u = j/k (exact) draws the (j+1)-th kept
+    token (the running sum must exceed u) and u = (j + 0.5)/k the (j+1)-th as well;
+    two logits d apart draw the first below 1/(1 + exp(-d/T)) and the second above;
+    T = 0 and k = 1 take the best token."""
+    bits = np.full(10, 0x4120, dtype=np.uint16)              # ten equal logits (10.0)
+    for k in (1, 2, 4, 8):
+        idx, kb = OT.topk_row(bits, k)
+        assert idx.tolist() == list(range(k))
+        for j in range(k):
+            # the running sum after i terms is i/k (exact for these k): the first to exceed
+            # j/k or (j + 1/2)/k is i = j + 1, the (j+1)-th kept token, index j
+            for u in (Fraction(j, k), Fraction(2 * j + 1, 2 * k)):
+                assert OT.sample_row(kb, idx, 1.0, float(u)) == j, (k, j, u)
+    row = np.array([0x4000, 0x4040, 0xC000], dtype=np.uint16)   # 2, 3, -2
+    idx, kb = OT.topk_row(row, 2)
+    assert idx.tolist() == [1, 0]
+    for T in (0.5, 1.0, 3.0):
+        p1 = 1.0 / (1.0 + math.exp(-1.0 / T))
+        assert OT.sample_row(kb, idx, T, p1 - 1e-9) == 1
+        assert OT.sample_row(kb, idx, T, min(p1 + 1e-9, 0.999999)) == 0
+        assert OT.sample_row(kb, idx, 0.0, 0.999) == 1
+    one, onek = OT.topk_row(row, 1)
+    assert OT.sample_row(onek, one, 1.0, 0.999) == 1
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
     pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
@@ -373,7 +449,8 @@ ALL_PINS = [
     lambda: pin_one_hot_random("w4g128"), pin_identity,
     lambda: pin_bruteforce("w8pc", 48), lambda: pin_bruteforce("w8g128", 128),
     lambda: pin_bruteforce("w4g128", 128), pin_library_factorisation, pin_invariants,
-    pin_compare, pin_dispatch,
+    pin_compare, pin_dispatch, pin_topk_golden, pin_topk_defining_property,
+    pin_topk_sampling_closed_forms,
 ]
 
 

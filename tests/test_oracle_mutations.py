@@ -4,8 +4,11 @@ index or a transposed operand slips through would not be a pin."""
 import numpy as np
 import pytest
 
+import math
+
 import oracle.linear as OL
 import oracle.quant as OQ
+import oracle.topk as OT
 import pins
 
 
@@ -130,9 +133,41 @@ def _mut_threshold(mp):
     mp.setattr(OL, "use_gemv", lambda M: M <= 8)
 
 
+def _mut_topk_ties_larger_index(mp):
+    mp.setattr(OT, "_rank_key", lambda v, i: (1, 0.0, -i) if math.isnan(v) else (0, -v, -i))
+
+
+def _mut_topk_ascending(mp):
+    mp.setattr(OT, "_rank_key", lambda v, i: (1, 0.0, i) if math.isnan(v) else (0, v, i))
+
+
+def _mut_topk_nan_first(mp):
+    mp.setattr(OT, "_rank_key", lambda v, i: (-1, 0.0, i) if math.isnan(v) else (0, -v, i))
+
+
+def _mut_topk_signed_zero(mp):
+    def key(v, i):
+        if math.isnan(v):
+            return (1, 0.0, i)
+        if v == 0 and math.copysign(1.0, v) < 0:
+            return (0, 1e-300, i)                       # -0 ranked below +0
+        return (0, -v, i)
+    mp.setattr(OT, "_rank_key", key)
+
+
+def _mut_sample_temperature_multiplies(mp):
+    mp.setattr(OT, "_weight", lambda v, v1, T: math.exp((v - v1) * T))
+
+
+def _mut_sample_at_or_above(mp):
+    mp.setattr(OT, "_reached", lambda run, u: run >= u)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
-             _mut_wrong_group_index, _mut_threshold]
+             _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
+             _mut_topk_ascending, _mut_topk_nan_first, _mut_topk_signed_zero,
+             _mut_sample_temperature_multiplies, _mut_sample_at_or_above]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
