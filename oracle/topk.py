@@ -16,7 +16,9 @@ module fixes the plainest reading, which the library follows as well:
   temperature T > 0 and a uniform draw u in [0, 1) supplied by the caller, the
   weights are p_i = exp((v_i - v_1) / T) / sum_j exp((v_j - v_1) / T) and the token
   is t_j for the smallest j whose running sum p_1 + ... + p_j exceeds u (the last
-  kept token if rounding leaves every sum at or below u); T = 0 takes t_1.
+  kept token if rounding leaves every sum at or below u); T = 0 takes t_1, and so
+  does a best logit that is not finite (+inf dominates; -inf or NaN everywhere
+  leaves nothing to weigh); a kept NaN logit behind a finite best one weighs 0.
 
 Arithmetic here is fp64 on the bf16 values (exactly representable).
 """
@@ -72,10 +74,11 @@ def sample_row(kept_bits, kept_idx, temperature: float, u: float) -> int:
     if not 0.0 <= u < 1.0:
         raise ValueError("u must lie in [0, 1)")
     idx = [int(i) for i in kept_idx]
-    if temperature == 0:
-        return idx[0]
     v = _values(kept_bits)
-    w = [_weight(float(v[i]), float(v[0]), temperature) for i in range(len(idx))]
+    if temperature == 0 or not math.isfinite(float(v[0])):
+        return idx[0]
+    w = [0.0 if math.isnan(float(v[i])) else _weight(float(v[i]), float(v[0]), temperature)
+         for i in range(len(idx))]
     total = math.fsum(w)
     run = 0.0
     for i, wi in enumerate(w):

@@ -439,6 +439,12 @@ def pin_topk_sampling_closed_forms():
         assert OT.sample_row(kb, idx, 0.0, 0.999) == 1
     one, onek = OT.topk_row(row, 1)
     assert OT.sample_row(onek, one, 1.0, 0.999) == 1
+    # a non-finite best logit draws it; a NaN behind a finite best weighs nothing;
+    # -inf weighs exp(-inf) = 0
+    for best in (0x7F80, 0xFF80, 0x7FC0):
+        assert OT.sample_row(np.array([best, 0x3F80], np.uint16), [5, 6], 1.0, 0.999) == 5
+    assert OT.sample_row(np.array([0x3F80, 0x7FC0], np.uint16), [5, 6], 1.0, 0.999) == 5
+    assert OT.sample_row(np.array([0x3F80, 0xFF80, 0x3F80], np.uint16), [5, 6, 7], 1.0, 0.6) == 7
 
 
 ALL_PINS = [
