@@ -503,8 +503,40 @@ def run_detail(wq, torch, args) -> dict:
     out["prefill_gemm"] = {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
                            for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
                            for M in (8, 64, 512, 2048)}
+    out["lm_head_topk"] = {f"{fmt}_{K}x{N}_M{M}": measure_lm_head_topk(wq, torch, 4, fmt, K, N, M)
+                           for fmt in ("w8g128", "w4g128") for K, N in [(5120, 151936)] for M in (1, 4)}
     out["reference_bf16_gemm"] = reference_bf16_gemm(torch)
     return out
+
+
+def measure_lm_head_topk(wq, torch, cfg, fmt, K, N, M, k: int = 50, temperature: float = 0.8) -> dict:
+    """The LM head + top-k sampling call against the LM head alone (both tuned, graph
+    replay over rotating weight copies): the cost the selection and the draw add."""
+    p = Pool(wq, torch, cfg, fmt, K, N, M)
+    tune(wq, p, 200, 200)
+    n = 2 * len(p.copies)
+    lin = time_graph(torch, lambda: p.call(wq), n) / n
+    ws = wq.workspace(wq.wq_lm_head_topk_workspace_size(p.copies[0], M, k))
+    u = torch.full((M,), 0.5, dtype=torch.float32, device="cuda")
+    vals = torch.empty((M, k), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+
+    def fn():
+        w = p.copies[p.i]
+        p.i = (p.i + 1) % len(p.copies)
+        wq.wq_lm_head_topk(w, p.x, k, temperature, u, vals, idx, tok, ws)
+
+    both = time_graph(torch, fn, n) / n
+    rec = {"k": k, "temperature": temperature, "us_linear": round(lin * 1e3, 3),
+           "us_linear_topk": round(both * 1e3, 3), "us_added": round((both - lin) * 1e3, 3),
+           "GB/s_linear_topk": round(p.bytes_per_call() / (both / 1e3) / 1e9, 1)}
+    log(f"lm head + top-k cfg{cfg} {fmt} K={K} N={N} M={M} k={k}: {rec['us_linear_topk']} us "
+        f"(layer alone {rec['us_linear']} us, +{rec['us_added']} us)")
+    p.free()
+    del p
+    torch.cuda.empty_cache()
+    return rec
 
 
 def reference_bf16_gemm(torch, M: int = 2048, K: int = 5120, N: int = 27648) -> dict:

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cinttypes>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -396,6 +397,64 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
   if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream);
   return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------ LM head + top-k
+namespace {
+struct TopkLayout {
+  size_t lin, logits_off, cand_off, total;
+};
+size_t round_up256(size_t b) { return (b + 255) & ~(size_t)255; }
+wq_status topk_layout(const wq_weight* w, int64_t M, int k, TopkLayout* L) {
+  if (!w) return fail(WQ_ERR_INVALID_ARG, "NULL weight");
+  wq_status st = check_shape(w->fmt, w->K, w->N);
+  if (st != WQ_OK) return st;
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (k < 1 || k > kTopkMaxK || k > w->N)
+    return fail(WQ_ERR_INVALID_ARG, "wq_lm_head_topk: k must lie in 1 .. min(64, N)");
+  if ((int64_t)topk_chunks(w->N) * k > kTopkMergeMax)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_lm_head_topk: ceil(N / 2048) * k must not exceed 8192");
+  if ((st = wq_workspace_size(w, M, &L->lin)) != WQ_OK) return st;
+  L->logits_off = round_up256(L->lin);
+  L->cand_off = round_up256(L->logits_off + (size_t)M * w->N * 2);
+  L->total = L->cand_off + (size_t)M * topk_chunks(w->N) * k * sizeof(uint64_t);
+  return WQ_OK;
+}
+}  // namespace
+
+wq_status wq_lm_head_topk_workspace_size(const wq_weight* w, int64_t M, int k, size_t* bytes) {
+  if (!bytes) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  TopkLayout L;
+  const wq_status st = topk_layout(w, M, k, &L);
+  if (st == WQ_OK) *bytes = L.total;
+  return st;
+}
+
+wq_status wq_lm_head_topk(const wq_weight* w, const void* x, int64_t M, int k, float temperature, const float* u,
+                          void* top_vals, int32_t* top_idx, int32_t* tokens, void* ws, size_t ws_bytes,
+                          void* stream) {
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  TopkLayout L;
+  if ((st = topk_layout(w, M, k, &L)) != WQ_OK) return st;
+  if (!x || !u || !top_vals || !top_idx || !tokens) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(WQ_ERR_INVALID_ARG, "wq_lm_head_topk: temperature must be finite and >= 0");
+  if (((uintptr_t)u | (uintptr_t)top_idx | (uintptr_t)tokens) % 4 || (uintptr_t)top_vals % 2)
+    return fail(WQ_ERR_ALIGNMENT, "wq_lm_head_topk: u, top_idx, tokens need 4-byte, top_vals 2-byte alignment");
+  if (!ws || ws_bytes < L.total)
+    return fail(WQ_ERR_WORKSPACE, "wq_lm_head_topk needs a workspace of " + std::to_string(L.total) + " bytes");
+  if ((uintptr_t)ws % 256)
+    return fail(WQ_ERR_ALIGNMENT, "wq_lm_head_topk: the workspace must be 256-byte aligned");
+  uint8_t* wsb = (uint8_t*)ws;
+  uint16_t* logits = (uint16_t*)(wsb + L.logits_off);
+  // the layer itself, confined to its own part of the workspace
+  void* lin_ws = L.lin ? ws : nullptr;
+  st = wq_dispatch_kind(M) == WQ_KIND_GEMV ? gemv_impl(w, x, M, logits, 0, 0, 0, lin_ws, L.lin, stream)
+                                          : gemm_impl(w, x, M, logits, 0, lin_ws, L.lin, stream);
+  if (st != WQ_OK) return st;
+  return launch_topk(logits, M, w->N, k, temperature, u, (uint64_t*)(wsb + L.cand_off), (uint16_t*)top_vals,
+                     top_idx, tokens, (hipStream_t)stream);
 }
 
 int wq_tune_pick(const double* lat, int n) {

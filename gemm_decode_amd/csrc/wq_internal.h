@@ -114,6 +114,14 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
 // Workspace bytes for a GEMV with the given split (fp32 partials of every slice).
 size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k);
 
+// LM head + top-k: chunks of 2048 logits per workgroup of the first kernel; the merge
+// kernel sorts up to kTopkMergeMax chunk candidates of a row in LDS.
+constexpr int kTopkMaxK = 64;
+constexpr int kTopkMergeMax = 8192;
+int topk_chunks(int64_t V);
+wq_status launch_topk(const uint16_t* logits, int64_t M, int64_t V, int k, float temperature, const float* u,
+                      uint64_t* cand, uint16_t* top_vals, int32_t* top_idx, int32_t* tokens, hipStream_t s);
+
 // Device tag "<arch>:<CUs>" of the current device; empty on failure.
 std::string current_device_tag();
 

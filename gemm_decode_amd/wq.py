@@ -20,6 +20,7 @@ __all__ = [
     "wq_abi_version", "wq_status_string", "wq_last_error", "wq_packed_sizes", "wq_dispatch_kind",
     "wq_gemv_max_waves", "wq_gemv_max_split",
     "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
+    "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -71,6 +72,9 @@ _SIGS = {
     "wq_gemv_ex": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
+    "wq_lm_head_topk": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_tune_pick": (C.c_int, [_P(C.c_double), C.c_int]),
     "wq_tune": (C.c_int, [_W, C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                           C.c_int, C.c_int, C.c_void_p, _P(C.c_int), _P(C.c_double)]),
@@ -245,6 +249,31 @@ def wq_linear(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tenso
     M, d = _xy(x, y, w), w.desc()
     _check(lib.wq_linear(C.byref(d), _ptr(x), M, _ptr(y), _ptr(ws),
                          0 if ws is None else ws.numel(), _stream(stream)), "wq_linear")
+
+
+# ------------------------------------------------------------ LM head + top-k
+def wq_lm_head_topk_workspace_size(w: PackedWeight, M: int, k: int) -> int:
+    d, n = w.desc(), C.c_size_t()
+    _check(lib.wq_lm_head_topk_workspace_size(C.byref(d), M, k, C.byref(n)), "wq_lm_head_topk_workspace_size")
+    return n.value
+
+
+def wq_lm_head_topk(w: PackedWeight, x: torch.Tensor, k: int, temperature: float, u: torch.Tensor,
+                    top_vals: torch.Tensor, top_idx: torch.Tensor, tokens: torch.Tensor,
+                    ws: torch.Tensor, stream=None) -> None:
+    """x bf16 [M][K]; u fp32 [M]; outputs top_vals bf16 [M][k], top_idx int32 [M][k],
+    tokens int32 [M] (all on the device)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    M = x.numel() // w.K
+    assert x.numel() == M * w.K
+    assert u.dtype == torch.float32 and u.numel() == M
+    assert top_vals.dtype == torch.bfloat16 and top_vals.numel() == M * k
+    assert top_idx.dtype == torch.int32 and top_idx.numel() == M * k
+    assert tokens.dtype == torch.int32 and tokens.numel() == M
+    d = w.desc()
+    _check(lib.wq_lm_head_topk(C.byref(d), _ptr(x), M, k, float(temperature), _ptr(u), _ptr(top_vals),
+                               _ptr(top_idx), _ptr(tokens), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(stream)), "wq_lm_head_topk")
 
 
 # ---------------------------------------------------------------------- tuner

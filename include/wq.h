@@ -259,6 +259,33 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- LM head + top-k */
+
+/* The LM head followed by top-k sampling in one call ("Fused LM Head + Top-k" and
+ * "Distributed Top-k Sampling" in the tileInfer README's feature list: the logits
+ * and the sampling in one step, and only the k best logits leave it).  The layer
+ * (wq_linear: the GEMV for M < 8) writes bf16 logits [M][N] into the workspace,
+ * where they stay; two more kernels select the k best of every row and draw one
+ * token from them.
+ *
+ * Order: larger logit first, equal values by smaller index, -0 == +0, NaN after
+ * every number.  Draw: with the kept logits v_1 >= ... >= v_k, weights
+ * exp((v_i - v_1) / temperature) in fp32, the token is the first kept one whose
+ * running weight exceeds u[m] times the total (the last kept one if none does);
+ * temperature 0, or a best logit that is not finite, takes the best; a NaN logit
+ * behind a finite best weighs 0.
+ *
+ * x: bf16 [M][K] (device); u: fp32 [M] (device), the caller's uniform draws in
+ * [0, 1); outputs (device): top_vals bf16 [M][k] (the logits' bits), top_idx int32
+ * [M][k], best first, and tokens int32 [M].  1 <= k <= min(64, N) and ceil(N / 2048)
+ * * k <= 8192 (else WQ_ERR_INVALID_ARG / WQ_ERR_UNSUPPORTED); temperature finite and
+ * >= 0; ws (256-byte aligned) of wq_lm_head_topk_workspace_size bytes, else
+ * WQ_ERR_WORKSPACE.  Results are bit-identical from run to run. */
+wq_status wq_lm_head_topk_workspace_size(const wq_weight* w, int64_t M, int k, size_t* bytes);
+wq_status wq_lm_head_topk(const wq_weight* w, const void* x, int64_t M, int k, float temperature,
+                          const float* u, void* top_vals, int32_t* top_idx, int32_t* tokens,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ tuner */
 
 /* Choose among measured candidates: the smallest latency wins and a tie goes to

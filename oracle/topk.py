@@ -33,7 +33,8 @@ from . import quant as _quant
 
 def _values(bits) -> np.ndarray:
     """bf16 bit patterns -> fp64 values, with NaN kept as NaN."""
-    return _quant.bf16_bits_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return _quant.bf16_bits_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
 
 
 def _rank_key(value: float, index: int):

@@ -214,6 +214,42 @@ def test_validation_rejects_before_any_device_work(wqlib):
         n.value == 2 * 512 * 27648 * 4 + 512 * 5120 * 2
 
 
+def test_lm_head_topk_validation_and_workspace(wqlib):
+    """The LM head + top-k entry point refuses bad arguments on the host, and its
+    workspace is the layer's, then the bf16 logits, then 8-byte candidates (k per
+    2048-logit chunk), each part 256-byte aligned."""
+    L = wqlib.lib
+    n = C.c_size_t()
+    d = _desc(wqlib, fmt=1, K=5120, N=151936)
+    lin = C.c_size_t()
+    assert L.wq_workspace_size(C.byref(d), 1, C.byref(lin)) == 0
+    r = lambda b: (b + 255) // 256 * 256
+    assert L.wq_lm_head_topk_workspace_size(C.byref(d), 1, 50, C.byref(n)) == 0
+    assert n.value == r(r(lin.value) + 151936 * 2) + 75 * 50 * 8
+    assert L.wq_lm_head_topk_workspace_size(C.byref(d), 1, 0, C.byref(n)) == 1       # k < 1
+    assert L.wq_lm_head_topk_workspace_size(C.byref(d), 1, 65, C.byref(n)) == 1      # k > 64
+    assert L.wq_lm_head_topk_workspace_size(C.byref(d), 0, 5, C.byref(n)) == 1       # M < 1
+    small = _desc(wqlib, fmt=0, K=64, N=40)
+    assert L.wq_lm_head_topk_workspace_size(C.byref(small), 1, 41, C.byref(n)) == 1  # k > N
+    wide = _desc(wqlib, fmt=0, K=64, N=300000)
+    assert L.wq_lm_head_topk_workspace_size(C.byref(wide), 1, 64, C.byref(n)) == 2   # 147 chunks x 64 > 8192
+    x, u = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    tv, ti, tk, ws = C.c_void_p(0x30000), C.c_void_p(0x40000), C.c_void_p(0x50000), C.c_void_p(0x100000)
+    big = 1 << 30
+    call = lambda T, **kw: L.wq_lm_head_topk(C.byref(kw.get("d", d)), kw.get("x", x), 1, kw.get("k", 8), T,
+                                             kw.get("u", u), tv, kw.get("ti", ti), tk, kw.get("ws", ws),
+                                             kw.get("wsb", big), None)
+    assert call(-1.0) == 1                                             # negative temperature
+    assert call(float("inf")) == 1 and call(float("nan")) == 1
+    assert call(1.0, u=None) == 1 and call(1.0, x=None) == 1
+    assert call(1.0, ti=C.c_void_p(0x40002)) == 3                      # int32 output misaligned
+    assert call(1.0, ws=C.c_void_p(0x100010)) == 3                     # workspace not 256-aligned
+    assert call(1.0, wsb=1024) == 4 and call(1.0, ws=None) == 4        # workspace too small / missing
+    assert call(1.0, k=0) == 1
+    canon = _desc(wqlib, fmt=1, layout=0, K=5120, N=151936)
+    assert call(1.0, d=canon) == 2                                     # not the gfx950 layout
+
+
 def test_binding_constants_match_the_header(wqlib):
     """The binding's copies of the header's array sizes and limits (a mismatch once let
     wq_tune write past the binding's latency buffer)."""
