@@ -256,6 +256,17 @@ def profile_prefill(calls: int = 10):
         torch.cuda.empty_cache()
 
 
+def profile_topk(calls: int = 10):
+    """Kernels for a rocprofv3 run of the LM head + top-k call: W8 and W4 group-128 LM
+    heads (5120, 151936) at M = 1, k = 50, tuned, `calls` calls on rotating weight
+    copies as one HIP graph replayed once."""
+    import torch
+    import gemm_decode_amd.wq as wq
+    for fmt in ("w8g128", "w4g128"):
+        rec = measure_lm_head_topk(wq, torch, 4, fmt, 5120, 151936, 1)
+        log(f"profile lm head + top-k {fmt}: {rec}")
+
+
 def _read_csv_rows(path):
     import csv
     with open(path) as f:
@@ -372,6 +383,8 @@ def main():
     ap.add_argument("--tune-iters", type=int, default=1000)
     ap.add_argument("--profile-pass", action="store_true",
                     help="launch the copy reference and the headline GEMVs for a rocprofv3 counter run")
+    ap.add_argument("--profile-topk", action="store_true",
+                    help="run the LM head + top-k profile workload (for rocprofv3) and exit")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="run the prefill GEMM profile workload (for rocprofv3) and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
@@ -401,6 +414,9 @@ def main():
         return
     if args.profile_prefill:
         profile_prefill()
+        return
+    if args.profile_topk:
+        profile_topk()
         return
     device_warmup(torch)
     log("warm-up done")

@@ -11,15 +11,15 @@
 //   topk_chunk_kernel         grid (ceil(V / 2048), M), 256 threads x 8 logits: the
 //                             chunk's k best (index ties by position) -> workspace;
 //   topk_merge_sample_kernel  grid M, 1024 threads x 8 candidates: the row's k best
-//                             of the chunk candidates (chunk order = index order, so
-//                             ties again go by position) and the drawn token.
+//                             of the chunk candidates (each carries its logit's
+//                             bits) and the drawn token.
 //
 // Selection, in two wave-level stages without block-wide searches: every wave keeps
-// the k best of its 512 entries (wave_select: a binary search over the rank with
-// ballot counts, then ballot prefix counts give each kept entry a slot), then wave 0
-// keeps the k best of the waves' lists and orders them (each kept key's place is its
-// count of better kept keys).  Keys are (rank << 32) | ~index, so equal ranks order
-// by index.
+// the k best of its 512 entries (wave_select: a search over the rank, three ballot
+// counts per step, then ballot prefix counts give each kept entry a slot), then wave 0
+// (through four waves first in the merge kernel) keeps the k best of the waves' lists
+// and orders them (each kept key's place is its count of better kept keys).  A key holds the rank, then the complemented index (so
+// equal ranks order by index), then the logit's own bits.
 //
 // Sampling (one wave, lane i holds the i-th best): weights exp((v_i - v_1) / T) in
 // fp32, an inclusive scan across the lanes, token = the first lane whose running sum
@@ -44,13 +44,16 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint64_t topk_key(uint32_t rank, uint32_t index) {
-  return ((uint64_t)rank << 32) | (uint64_t)(0xFFFFFFFFu - index);
+// Keys: rank (17 bits) | ~index (31 bits) | the logit's own bf16 bits (16): larger is
+// better, equal ranks order by index, and the bits travel with the entry.
+__device__ __forceinline__ uint64_t topk_key(uint32_t rank, uint32_t index, uint16_t bits) {
+  return ((uint64_t)rank << 47) | ((uint64_t)(0x7FFFFFFFu - index) << 16) | bits;
 }
-__device__ __forceinline__ uint32_t key_index(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
+__device__ __forceinline__ uint32_t key_rank(uint64_t key) { return (uint32_t)(key >> 47); }
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return 0x7FFFFFFFu - (uint32_t)((key >> 16) & 0x7FFFFFFFu); }
+__device__ __forceinline__ uint16_t key_bits(uint64_t key) { return (uint16_t)key; }
 
-// One wave keeps the k best of its 64 x E keys ((rank << 32) | ~index; rank 0 = empty
-// slot).  Entries of equal rank must lie in index order along the lane-major
+// One wave keeps the k best of its 64 x E keys (rank 0 = empty slot).  Entries of equal rank must lie in index order along the lane-major
 // positions lane * E + j; k <= the wave's nonempty entries, k <= 64.  Writes the kept
 // keys to dst[0 .. k) in no particular order.  Control flow is wave-uniform: a binary
 // search over the rank finds the k-th best rank T from ballot counts; the entries
@@ -60,14 +63,14 @@ template <int E>
 __device__ __forceinline__ uint32_t wave_count_ge(const uint64_t (&key)[E], uint32_t v) {
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < E; ++j) c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((uint32_t)(key[j] >> 32) >= v));
+  for (int j = 0; j < E; ++j) c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key_rank(key[j]) >= v));
   return c;
 }
 
 template <int E>
 __device__ void wave_select(const uint64_t (&key)[E], int k, uint64_t* dst) {
   // invariant: #(rank >= lo) >= k > #(rank >= hi); three thresholds per step (the
-  // counts are independent, so their ballot latencies overlap)
+  // counts are independent, so their latencies overlap), then halving for the rest
   uint32_t lo = 0, hi = 1u << 17;
   while (hi - lo >= 4) {
     const uint32_t q = (hi - lo) >> 2, t1 = lo + q, t2 = lo + 2 * q, t3 = lo + 3 * q;
@@ -93,7 +96,7 @@ __device__ void wave_select(const uint64_t (&key)[E], int k, uint64_t* dst) {
   uint32_t gt_below = 0, eq_below = 0, tg = 0;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const uint32_t r = (uint32_t)(key[j] >> 32);
+    const uint32_t r = key_rank(key[j]);
     const uint64_t mg = __builtin_amdgcn_ballot_w64(r > T), me = __builtin_amdgcn_ballot_w64(r == T);
     gt_below += lanes_below(mg);
     eq_below += lanes_below(me);
@@ -103,7 +106,7 @@ __device__ void wave_select(const uint64_t (&key)[E], int k, uint64_t* dst) {
   uint32_t og = gt_below, oe = eq_below;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const uint32_t r = (uint32_t)(key[j] >> 32);
+    const uint32_t r = key_rank(key[j]);
     if (r > T) {
       dst[og++] = key[j];
     } else if (r == T) {
@@ -129,20 +132,26 @@ __device__ __forceinline__ void wave_rank_sort(const uint64_t* src, int k, uint6
   if (lane < k) dst[pos] = own;
 }
 
-// Stage 2 of both kernels, wave 0: the k best of the NW per-wave lists stage[w][0 .. 64)
+// One wave: the k best (fewer if the lists hold fewer) of the NL lists lists[w][0 .. 64)
 // (empty slots 0), read lane-major so that list order (= index order for equal ranks)
-// is position order.
-template <int NW>
-__device__ void merge_wave_lists(const uint64_t (*stage)[64], int k, uint64_t* tmp, uint64_t* out) {
-  constexpr int E = NW;  // 64 x NW entries over 64 lanes
+// is position order; writes them to dst[0 .. kept) unordered and zeros the rest of
+// dst[0 .. 64); returns kept.
+template <int NL>
+__device__ int select_lists(const uint64_t (*lists)[64], int k, uint64_t* dst) {
+  constexpr int E = NL;  // 64 x NL entries over 64 lanes
   const int lane = threadIdx.x & 63;
-  const uint64_t* flat = &stage[0][0];
+  const uint64_t* flat = &lists[0][0];
   uint64_t key[E];
+  uint32_t nonempty = 0;
 #pragma unroll
-  for (int j = 0; j < E; ++j) key[j] = flat[lane * E + j];
-  if (lane >= k) tmp[lane] = 0ull;  // (the same wave fills [0, k) next)
-  wave_select<E>(key, k, tmp);
-  wave_rank_sort(tmp, k, out);
+  for (int j = 0; j < E; ++j) {
+    key[j] = flat[lane * E + j];
+    nonempty += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j] != 0ull));
+  }
+  const int kept = min(k, (int)nonempty);
+  if (lane >= kept) dst[lane] = 0ull;  // (the same wave fills [0, kept) next)
+  if (kept > 0) wave_select<E>(key, kept, dst);
+  return kept;
 }
 
 __global__ __launch_bounds__(256) void topk_chunk_kernel(const uint16_t* __restrict__ logits, int V, int k,
@@ -164,29 +173,29 @@ __global__ __launch_bounds__(256) void topk_chunk_kernel(const uint16_t* __restr
 #pragma unroll
   for (int j = 0; j < kTopkPer; ++j) {
     const int p = t * kTopkPer + j;
-    key[j] = p < n ? topk_key(topk_rank(b[j]), (uint32_t)(base + p)) : 0ull;
+    key[j] = p < n ? topk_key(topk_rank(b[j]), (uint32_t)(base + p), b[j]) : 0ull;
   }
   const int nw = min(max(n - wv * 64 * kTopkPer, 0), 64 * kTopkPer);  // this wave's entries
   const int kw = min(k, nw);
   if (kw > 0) wave_select<kTopkPer>(key, kw, stage[wv]);
   if (lane >= kw) stage[wv][lane] = 0ull;
   __syncthreads();
-  const int kk = min(k, n);
   if (wv == 0) {
-    merge_wave_lists<NW>(stage, kk, tmp, fin);
+    const int kk = select_lists<NW>(stage, k, tmp);   // = min(k, n)
+    wave_rank_sort(tmp, kk, fin);
     uint64_t* out = cand + ((size_t)m * P + c) * k;
     if (lane < k) out[lane] = lane < kk ? fin[lane] : 0ull;
   }
 }
 
-__global__ __launch_bounds__(1024) void topk_merge_sample_kernel(const uint16_t* __restrict__ logits, int V,
-                                                                 int k, int P, const uint64_t* __restrict__ cand,
+__global__ __launch_bounds__(1024) void topk_merge_sample_kernel(int k, int P, const uint64_t* __restrict__ cand,
                                                                  float temperature, const float* __restrict__ u,
                                                                  uint16_t* __restrict__ top_vals,
                                                                  int32_t* __restrict__ top_idx,
                                                                  int32_t* __restrict__ tokens) {
   constexpr int NW = 16;
   __shared__ uint64_t stage[NW][64];
+  __shared__ uint64_t part[4][64];
   __shared__ __attribute__((aligned(16))) uint64_t tmp[64];
   __shared__ uint64_t fin[64];
   const int m = blockIdx.x, t = threadIdx.x;
@@ -206,12 +215,17 @@ __global__ __launch_bounds__(1024) void topk_merge_sample_kernel(const uint16_t*
   if (kw > 0) wave_select<kTopkPer>(key, kw, stage[wv]);
   if (lane >= kw) stage[wv][lane] = 0ull;
   __syncthreads();
+  // 16 lists -> 4 (waves 0-3, four lists each) -> 1 (wave 0), then ordered
+  if (wv < 4) select_lists<4>(&stage[4 * wv], k, part[wv]);
+  __syncthreads();
   if (wv != 0) return;
-  merge_wave_lists<NW>(stage, k, tmp, fin);
+  select_lists<4>(part, k, tmp);
+  wave_rank_sort(tmp, k, fin);
   // wave 0: lane i holds the i-th best (k <= 64)
   const bool live = lane < k;
-  const uint32_t idx = live ? key_index(fin[lane]) : 0u;
-  const uint16_t bits = live ? logits[(size_t)m * V + idx] : (uint16_t)0;
+  const uint64_t best = live ? fin[lane] : 0ull;
+  const uint32_t idx = key_index(best);
+  const uint16_t bits = key_bits(best);
   if (live) {
     top_idx[(size_t)m * k + lane] = (int32_t)idx;
     top_vals[(size_t)m * k + lane] = bits;
@@ -244,8 +258,7 @@ wq_status launch_topk(const uint16_t* logits, int64_t M, int64_t V, int k, float
   const int P = topk_chunks(V);
   topk_chunk_kernel<<<dim3((unsigned)P, (unsigned)M), 256, 0, s>>>(logits, (int)V, k, cand);
   WQ_HIP_CHECK(hipGetLastError());
-  topk_merge_sample_kernel<<<(unsigned)M, 1024, 0, s>>>(logits, (int)V, k, P, cand, temperature, u, top_vals,
-                                                          top_idx, tokens);
+  topk_merge_sample_kernel<<<(unsigned)M, 1024, 0, s>>>(k, P, cand, temperature, u, top_vals, top_idx, tokens);
   WQ_HIP_CHECK(hipGetLastError());
   return WQ_OK;
 }
