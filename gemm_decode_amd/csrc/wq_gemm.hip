@@ -1255,31 +1255,36 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Per-channel int8: codes of three K steps live in registers (a static ring: the loop
+  // is unrolled by three), so while step ks is multiplied the loads of steps ks + 1 and
+  // ks + 2 are in flight.  Group-128 formats: one step ahead (the deeper ring costs
+  // their 4-token-block variants half their occupancy; measured slower for uint4).  x
+  // goes through the LDS double buffer one step ahead.
+  constexpr int kAhead = FMT == WQ_FMT_W8_PC ? 2 : 1;
+  uint4 c1[RT][CH], c2[RT][CH];
+  auto load_codes = [&](uint4 (*c)[CH], int ks) {
+    const int kc = min(ks, ks1 - 1);  // past the range: reload the last step (harmless)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) c[t][j] = load_stream16(code_ptr(t, j, kc));
+  };
   if (ks0 < ks1) {
     u32x4 xr[XJ];
     xload(xr, ks0);
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int j = 0; j < CH; ++j) cw[t][j] = load_stream16(code_ptr(t, j, ks0));
+    load_codes(cw, ks0);
+    if constexpr (kAhead == 2) load_codes(c1, ks0 + 1);
     xstore(xr, 0);
     __syncthreads();
   }
-  for (int ks = ks0; ks < ks1; ++ks) {
+  auto step = [&](uint4 (*cur)[CH], uint4 (*fut)[CH], int ks) {
     const int buf = (ks - ks0) & 1;
-    const bool more = ks + 1 < ks1;
-    // The next step (the last step reloads itself: harmless, and branch free), in
-    // flight during this one.
-    const int kn = more ? ks + 1 : ks;
+    const int kn = min(ks + 1, ks1 - 1);
     u32x4 xr[XJ];
-    uint4 cn[RT][CH];
     xload(xr, kn);
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int j = 0; j < CH; ++j) cn[t][j] = load_stream16(code_ptr(t, j, kn));
+    load_codes(fut, ks + kAhead);
     const uint8_t* xb = xs[buf];
-    transpose(cw);
+    transpose(cur);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       floatx4 part_acc[TB];
@@ -1288,8 +1293,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
       if constexpr (!kW4) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(cw[t][j]));
-          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(cw[t][j]));
+          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(cur[t][j]));
+          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(cur[t][j]));
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
             const uint8_t* xrow = xb + (16 * b + r16) * SK_XP + 128 * j + 32 * c4;
@@ -1303,7 +1308,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
         const int n = nrow[t];
         const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
         const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
-        const uint32_t wd[4] = {cw[t][0].x, cw[t][0].y, cw[t][0].z, cw[t][0].w};
+        const uint32_t wd[4] = {cur[t][0].x, cur[t][0].y, cur[t][0].z, cur[t][0].w};
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
           const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, w4_word_to_bf16(wd[s2], z));
@@ -1326,12 +1331,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
       }
     }
     xstore(xr, buf ^ 1);  // that buffer was last read before the previous barrier
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int j = 0; j < CH; ++j) cw[t][j] = cn[t][j];
     __syncthreads();
+  };
+  // ring: step ks multiplies the buffer loaded two steps earlier and loads ks + 2 into
+  // the one step ks - 1 has finished with
+  if constexpr (kAhead == 2) {
+    int ks = ks0;
+    for (; ks + 3 <= ks1; ks += 3) {
+      step(cw, c2, ks);
+      step(c1, cw, ks + 1);
+      step(c2, c1, ks + 2);
+    }
+    if (ks < ks1) step(cw, c2, ks);
+    if (ks + 1 < ks1) step(c1, cw, ks + 1);
+  } else {
+    for (int ks = ks0; ks < ks1; ++ks) {
+      step(cw, c1, ks);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) cw[t][j] = c1[t][j];
+    }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds D[token 4 c4 + q][weight row r16] of each 16 x 16 block
 #pragma unroll
