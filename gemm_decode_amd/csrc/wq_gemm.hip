@@ -1161,7 +1161,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 //     byte is used by two waves, so LDS would only add a round trip.  One 16-byte
 //     load per lane covers 16 rows x 64 k (W8) or 16 rows x 128 k (W4) of a tile;
 //   * the x slice of a K step (TB*16 tokens x 128 k, bf16) goes through LDS once per
-//     workgroup and feeds all four waves;
+//     workgroup and feeds all four waves (17 <= M; one token block takes the direct
+//     kernel below);
 //   * v_mfma_f32_16x16x32_bf16 with x as the A operand (16 tokens) and the exact
 //     bf16 codes as B (16 weight rows).  Lane group c (lanes 16c .. 16c+15) of MFMA s
 //     takes k = 16c + 8s + 0..7 (W8, per 64 k) or 32c + 8s + 0..7 (W4, per 128 k), so
@@ -1375,11 +1376,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
   }
 }
 
-// Skinny GEMM for M <= 32 (one or two token blocks): the x fragments are small enough
-// to come straight from memory (x is a few hundred KB and stays in L2), so every
-// wave streams on its own -- no LDS, no barrier -- with the next step's codes and x
-// in flight while the current step's MFMAs run.  Same operand mapping, K order and
-// epilogue as gemm_skinny_kernel.
+// Skinny GEMM for M <= 16 (one token block): the x fragments are small enough to come
+// straight from memory (x stays in L2), so every wave streams on its own -- no LDS
+// staging of x, no barrier -- with the next steps' codes and x in flight while the
+// current step's MFMAs run.  Same operand mapping, K order and epilogue as
+// gemm_skinny_kernel.  (With two token blocks each wave's x reads double and the LDS-
+// staged kernel wins.)
 template <int FMT, int TB>
 __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* __restrict__ qw,
                                                                   const uint16_t* __restrict__ scales,
@@ -1632,10 +1634,12 @@ wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs
                         uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st) {
   const dim3 grid((unsigned)((N + SK_ROWS - 1) / SK_ROWS), (unsigned)S);
   const int TB = (M + 15) / 16;
+  // one token block: the direct kernel; two: x through LDS as well (measured at M = 32:
+  // 39 us against 57 us for per-channel W8 at (5120, 27648), 53 against 74 for W4)
   if (TB <= 1)
     gemm_skinny_direct_kernel<FMT, 1><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
   else if (TB <= 2)
-    gemm_skinny_direct_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+    gemm_skinny_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
   else if (TB <= 4)
     gemm_skinny_kernel<FMT, 4><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
   else
