@@ -340,6 +340,14 @@ wq_status wq_pack(const float* w, const wq_weight* out, void* stream) {
   return launch_pack(w, out, (hipStream_t)stream);
 }
 
+wq_status wq_pack_bf16(const void* w, const wq_weight* out, void* stream) {
+  wq_status st = check_weight(out, WQ_LAYOUT_CANONICAL);
+  if (st != WQ_OK) return st;
+  if (!w) return fail(WQ_ERR_INVALID_ARG, "w must not be NULL");
+  if (!aligned(w, 8)) return fail(WQ_ERR_ALIGNMENT, "w (bf16) must be 8-byte aligned");
+  return launch_pack_bf16((const uint16_t*)w, out, (hipStream_t)stream);
+}
+
 static wq_status repack_common(const wq_weight* src, const wq_weight* dst, int from, int to,
                                void* stream) {
   wq_status st = check_weight(src, from);

@@ -41,6 +41,16 @@ __device__ __forceinline__ float group_min(float v) {
   return v;
 }
 
+// Four consecutive weights as fp32: fp32 input as is, bf16 input widened (exact).
+__device__ __forceinline__ float4 load_w4(const float* w, size_t off) {
+  return *reinterpret_cast<const float4*>(w + off);
+}
+__device__ __forceinline__ float4 load_w4(const uint16_t* w, size_t off) {
+  const uint2 v = *reinterpret_cast<const uint2*>(w + off);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ uint32_t w8_codes4(float4 w, float s) {
   // q = clamp(rint(w / s), -127, 127); s != 0 here.
   float c[4] = {w.x, w.y, w.z, w.w};
@@ -54,16 +64,17 @@ __device__ __forceinline__ uint32_t w8_codes4(float4 w, float s) {
 }
 
 // W8, one scale per output channel: one 256-thread block per row.
-__global__ __launch_bounds__(256) void pack_w8_pc_kernel(const float* __restrict__ w,
+template <typename T>
+__global__ __launch_bounds__(256) void pack_w8_pc_kernel(const T* __restrict__ w,
                                                            int8_t* __restrict__ q,
                                                            uint16_t* __restrict__ scales, int K) {
   const int n = blockIdx.x;
-  const float4* row = reinterpret_cast<const float4*>(w + (size_t)n * K);
+  const size_t row = (size_t)n * K;
   uint32_t* qrow = reinterpret_cast<uint32_t*>(q + (size_t)n * K);
   const int words = K / 4;
   float a = 0.f;
   for (int i = threadIdx.x; i < words; i += 256) {
-    float4 v = row[i];
+    float4 v = load_w4(w, row + 4 * (size_t)i);
     a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
   a = group_max<64>(a);
@@ -74,11 +85,12 @@ __global__ __launch_bounds__(256) void pack_w8_pc_kernel(const float* __restrict
   const uint16_t sb = f32_to_bf16_rne(a / 127.f);
   const float s = bf16_to_f32(sb);
   if (threadIdx.x == 0) scales[n] = sb;
-  for (int i = threadIdx.x; i < words; i += 256) qrow[i] = (s == 0.f) ? 0u : w8_codes4(row[i], s);
+  for (int i = threadIdx.x; i < words; i += 256) qrow[i] = (s == 0.f) ? 0u : w8_codes4(load_w4(w, row + 4 * (size_t)i), s);
 }
 
 // W8, group 128: 256 threads = 8 groups of 32 lanes, each lane 4 consecutive k.
-__global__ __launch_bounds__(256) void pack_w8_g128_kernel(const float* __restrict__ w,
+template <typename T>
+__global__ __launch_bounds__(256) void pack_w8_g128_kernel(const T* __restrict__ w,
                                                              int8_t* __restrict__ q,
                                                              uint16_t* __restrict__ scales,
                                                              int K, int N) {
@@ -89,7 +101,7 @@ __global__ __launch_bounds__(256) void pack_w8_g128_kernel(const float* __restri
   const int64_t gg = valid ? gid : 0;
   const int64_t n = gg / G, g = gg % G;
   const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
-  float4 v = *reinterpret_cast<const float4*>(w + off);
+  float4 v = load_w4(w, off);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   a = group_max<32>(a);
   const uint16_t sb = f32_to_bf16_rne(a / 127.f);
@@ -101,7 +113,8 @@ __global__ __launch_bounds__(256) void pack_w8_g128_kernel(const float* __restri
 
 // W4 asymmetric group 128, canonical layout: a block handles 8 rows x 1 group,
 // 32 lanes per row, 4 consecutive k per lane; the 8 zero-points form one word.
-__global__ __launch_bounds__(256) void pack_w4_g128_kernel(const float* __restrict__ w,
+template <typename T>
+__global__ __launch_bounds__(256) void pack_w4_g128_kernel(const T* __restrict__ w,
                                                              uint32_t* __restrict__ qw,
                                                              uint16_t* __restrict__ scales,
                                                              uint32_t* __restrict__ zeros, int K,
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(256) void pack_w4_g128_kernel(const float* __restri
   const int r = threadIdx.x >> 5, lane = threadIdx.x & 31;
   const int n = 8 * c8 + r;
   const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
-  float4 v = *reinterpret_cast<const float4*>(w + off);
+  float4 v = load_w4(w, off);
   float hi = group_max<32>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
   float lo = group_min<32>(fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
   const uint16_t sh = f32_to_f16_rne((hi - lo) / 15.f);
@@ -256,20 +269,21 @@ unsigned grid_for(size_t n, unsigned block) {
 
 }  // namespace
 
-wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s) {
+template <typename T>
+static wq_status launch_pack_t(const T* w, const wq_weight* out, hipStream_t s) {
   const int K = (int)out->K, N = (int)out->N;
   switch (out->fmt) {
     case WQ_FMT_W8_PC:
-      pack_w8_pc_kernel<<<N, 256, 0, s>>>(w, (int8_t*)out->qweight, (uint16_t*)out->scales, K);
+      pack_w8_pc_kernel<T><<<N, 256, 0, s>>>(w, (int8_t*)out->qweight, (uint16_t*)out->scales, K);
       break;
     case WQ_FMT_W8_G128: {
       const int64_t groups = (int64_t)N * (K / kGroup);
-      pack_w8_g128_kernel<<<(unsigned)((groups + 7) / 8), 256, 0, s>>>(
+      pack_w8_g128_kernel<T><<<(unsigned)((groups + 7) / 8), 256, 0, s>>>(
           w, (int8_t*)out->qweight, (uint16_t*)out->scales, K, N);
       break;
     }
     case WQ_FMT_W4_G128:
-      pack_w4_g128_kernel<<<dim3(N / 8, K / kGroup), 256, 0, s>>>(
+      pack_w4_g128_kernel<T><<<dim3(N / 8, K / kGroup), 256, 0, s>>>(
           w, (uint32_t*)out->qweight, (uint16_t*)out->scales, (uint32_t*)out->zeros, K, N);
       break;
     default:
@@ -277,6 +291,11 @@ wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s) {
   }
   WQ_HIP_CHECK(hipGetLastError());
   return WQ_OK;
+}
+
+wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s) { return launch_pack_t(w, out, s); }
+wq_status launch_pack_bf16(const uint16_t* w, const wq_weight* out, hipStream_t s) {
+  return launch_pack_t(w, out, s);
 }
 
 wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s) {

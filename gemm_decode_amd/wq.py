@@ -19,7 +19,7 @@ __all__ = [
     "FMT", "CANONICAL", "GFX950", "WqError", "PackedWeight", "lib",
     "wq_abi_version", "wq_status_string", "wq_last_error", "wq_packed_sizes", "wq_dispatch_kind",
     "wq_gemv_max_waves", "wq_gemv_max_split",
-    "wq_pack", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
+    "wq_pack", "wq_pack_bf16", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
@@ -65,6 +65,7 @@ _SIGS = {
     "wq_gemv_max_waves": (C.c_int, [C.c_int, C.c_int64, C.c_int]),
     "wq_gemv_max_split": (C.c_int, [C.c_int, C.c_int64]),
     "wq_pack": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
+    "wq_pack_bf16": (C.c_int, [C.c_void_p, _W, C.c_void_p]),
     "wq_repack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_unrepack": (C.c_int, [_W, _W, C.c_void_p]),
     "wq_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
@@ -183,6 +184,12 @@ def wq_pack(w: torch.Tensor, out: PackedWeight, stream=None) -> None:
     _check(lib.wq_pack(_ptr(w), C.byref(d), _stream(stream)), "wq_pack")
 
 
+def wq_pack_bf16(w: torch.Tensor, out: PackedWeight, stream=None) -> None:
+    assert w.dtype == torch.bfloat16 and w.is_contiguous() and tuple(w.shape) == (out.N, out.K)
+    d = out.desc()
+    _check(lib.wq_pack_bf16(_ptr(w), C.byref(d), _stream(stream)), "wq_pack_bf16")
+
+
 def wq_repack(src: PackedWeight, dst: PackedWeight, stream=None) -> None:
     a, b = src.desc(), dst.desc()
     _check(lib.wq_repack(C.byref(a), C.byref(b), _stream(stream)), "wq_repack")
@@ -194,10 +201,11 @@ def wq_unrepack(src: PackedWeight, dst: PackedWeight, stream=None) -> None:
 
 
 def quantize(w: torch.Tensor, fmt, stream=None, keep_canonical: bool = False):
-    """wq_pack into the canonical layout, then wq_repack into the gfx950 layout."""
+    """wq_pack (fp32 w) or wq_pack_bf16 (bf16 w) into the canonical layout, then
+    wq_repack into the gfx950 layout."""
     N, K = w.shape
     can = PackedWeight(fmt, CANONICAL, K, N, device=w.device)
-    wq_pack(w, can, stream)
+    (wq_pack_bf16 if w.dtype == torch.bfloat16 else wq_pack)(w, can, stream)
     g = PackedWeight(fmt, GFX950, K, N, device=w.device)
     wq_repack(can, g, stream)
     return (g, can) if keep_canonical else g

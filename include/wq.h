@@ -138,6 +138,12 @@ int wq_dispatch_kind(int64_t M);
  * The output is bit-exact and deterministic.  `w` must not alias the outputs. */
 wq_status wq_pack(const float* w, const wq_weight* out, void* stream);
 
+/* wq_pack for a bf16 weight w[N][K] (device, row-major, 8-byte aligned): each value
+ * widens exactly to fp32 and the recipe above runs on the widened weight, so the
+ * output is bit-identical to wq_pack of that fp32 copy (checkpoints stored in bf16
+ * need no fp32 staging buffer). */
+wq_status wq_pack_bf16(const void* w, const wq_weight* out, void* stream);
+
 /* CANONICAL -> GFX950 (wq_repack) and back (wq_unrepack); src and dst describe
  * distinct buffers of the same format and shape in the named layouts.  The two are
  * exact inverses on every valid packed weight. */

@@ -189,6 +189,9 @@ def test_validation_rejects_before_any_device_work(wqlib):
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
     assert L.wq_pack(None, C.byref(dc), None) == 1
+    assert L.wq_pack_bf16(None, C.byref(dc), None) == 1
+    assert L.wq_pack_bf16(C.c_void_p(0x10004), C.byref(dc), None) == 3       # bf16 w not 8-byte aligned
+    assert L.wq_pack_bf16(C.c_void_p(0x10008), C.byref(d), None) == 2        # out not canonical
     assert L.wq_repack(C.byref(d), C.byref(d), None) == 2                   # src not canonical
     assert L.wq_repack(C.byref(dc), C.byref(_desc(wqlib, q=0x1000)), None) == 1  # in place
     n = C.c_size_t()

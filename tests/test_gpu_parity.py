@@ -78,6 +78,24 @@ def _run_gemm(wq, g, x_bits, tile=0, with_ws=True):
 
 
 # ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+def test_pack_bf16_input_bitexact(wq, fmt):
+    """wq_pack_bf16: a bf16 weight packs exactly as the oracle packs its (exact) fp32
+    widening; ragged K groups and N rows across several blocks."""
+    K, N = 1280, 776
+    W = synth.weight(109, K, N, synth.uses_outliers(fmt))
+    Wb = OQ.bf16_rne_bits(W)                                   # the checkpoint's bf16 bits
+    Wf = OQ.bf16_bits_to_f32(Wb)                               # their exact widening
+    P = OQ.pack(fmt, Wf)
+    wt = torch.from_numpy(Wb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    g, can = wq.quantize(wt, fmt, keep_canonical=True)
+    got = canonical_to_host(can, fmt)
+    for key in ("qweight", "scales") + (("zeros",) if fmt == "w4g128" else ()):
+        assert np.array_equal(got[key].view(np.uint8), np.ascontiguousarray(P[key]).view(np.uint8)), key
+    x = synth.activation(109, K, 3)
+    assert_parity(_run_gemv(wq, g, x, 1), OL.ref_linear(x, P), f"{fmt} bf16-packed gemv")
+
+
 SMALL = [("w8pc", 1024, 1024), ("w8pc", 2320, 1000), ("w8g128", 1280, 1000), ("w4g128", 1280, 776),
          ("w8g128", 384, 264), ("w4g128", 384, 264), ("w8pc", 5200, 1000), ("w4g128", 9088, 264)]
 
