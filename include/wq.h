@@ -301,10 +301,11 @@ wq_status wq_lm_head_topk(const wq_weight* w, const void* x, int64_t M, int k, f
 int wq_tune_pick(const double* lat, int n);
 
 /* Time every candidate for (format, K, N, M) on the current device and store the
- * winner in the tuner cache: for M < 8 every (split_k, waves) pair with split_k in
- * the grid {1,2,4,8,16,32} (those the shape and workspace allow) and waves in
- * {1,2,4,8,16} plus the default (capped at wq_gemv_max_waves); for M >= 8 the GEMM
- * tiles.  Each candidate runs `warmup` untimed
+ * winner in the tuner cache: for M < 8 every (split_k, waves, rows) triple with
+ * split_k in the grid {1,2,4,8,16,32} (those the shape and workspace allow), waves in
+ * {1,2,3,4,6,8,12,16} plus the default (capped at wq_gemv_max_waves) and every rows
+ * setting; for M >= 8 the GEMM tiles.  The four fastest are then timed a second time
+ * and that timing decides among them.  Each candidate runs `warmup` untimed
  * and `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
  * weights (distinct buffers with the same format and shape) so that the weights
  * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k
