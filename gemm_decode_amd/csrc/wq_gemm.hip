@@ -442,8 +442,8 @@ struct DmaWork {
   size_t poff;        // partials of this range: part[poff + (m - pm0) * ppitch + n - pn0]
   int ppitch, pm0, pn0;
 };
-__device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, DmaWork& w) {
-  const int mblocks = (M + DBM - 1) / DBM, nblocks = (N + DBN - 1) / DBN, total = mblocks * nblocks;
+__device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, DmaWork& w, int tm = DBM) {
+  const int mblocks = (M + tm - 1) / tm, nblocks = (N + DBN - 1) / DBN, total = mblocks * nblocks;
   const int b = blockIdx.x, per_full = (tail0 + 7) / 8;
   if (b < 8 * per_full) {
     w.lin = (b & 7) * per_full + (b >> 3);
@@ -460,9 +460,9 @@ __device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, Dma
     w.lin = tail0 + lu / tailS;
     w.S = tailS;
     w.sp = lu % tailS;
-    w.poff = (size_t)lu * DBM * DBN;  // [tile - tail0][sp] blocks
+    w.poff = (size_t)lu * tm * DBN;  // [tile - tail0][sp] blocks
     w.ppitch = DBN;
-    w.pm0 = (w.lin % mblocks) * DBM;
+    w.pm0 = (w.lin % mblocks) * tm;
     w.pn0 = (w.lin / mblocks) * DBN;
   }
   return true;
@@ -472,27 +472,31 @@ __device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, Dma
 // row blocks and CB = 8 / WN column blocks of 32.  With 1 x 4 every code chunk is
 // converted by exactly one wave (half the conversion work of 2 x 2) at the price of
 // every wave reading the whole x tile from LDS.
-template <int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
+template <int WM, int WN, int TM>
+__device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
                                                                          uint16_t* __restrict__ y,
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
                                                                          int tailS) {
-  constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
-  constexpr int XI = 32 / NW, WI = 16 / NW;  // x and code DMA instructions per wave and step
+  // TM: rows of x per workgroup tile (256, or 64 for a few tokens, where the tile
+  // streams the same weights with a quarter of the x traffic and MFMA work)
+  constexpr int NW = WM * WN, RB = TM / 32 / WM, CB = 8 / WN;
+  constexpr int XI = TM / 8 / NW, WI = 16 / NW;  // x and code DMA instructions per wave and step
+  static_assert(XI >= 1 && RB >= 1, "tile shape");
   constexpr int kDmaPerStep = XI + WI;
   constexpr int KUNIT = 1;  // split-K granularity in steps
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGE];
+  constexpr int kDA = TM * DBK * 2, kStage = kDA + DB_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStage];
 
   DmaWork wk;
-  if (!dma_work(M, N, tail0, tailS, wk)) return;
-  const int mblocks = (M + DBM - 1) / DBM;
+  if (!dma_work(M, N, tail0, tailS, wk, TM)) return;
+  const int mblocks = (M + TM - 1) / TM;
   const int nb = wk.lin / mblocks, mb = wk.lin % mblocks;
-  const int n0 = nb * DBN, m0 = mb * DBM;
+  const int n0 = nb * DBN, m0 = mb * TM;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(x + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + DA_BYTES + (WI * wave + j) * 1024);
+    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + kDA + (WI * wave + j) * 1024);
   };
   // ---- fragment addresses (bytes within a stage); the swizzles depend only on l32.
   int aaddr[2][2], baddr[2];
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
       aaddr[P][s2] = (wm * 32 * RB + l32) * 128 + 16 * ((4 * P + 2 * lh + s2) ^ swz_x(l32));
-    baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
+    baddr[P] = kDA + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
   }
 
   bf16x8_t A0[2][RB], B0[2][CB];
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   // core never waits for a burst of VALU work.
   constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + CB;
   constexpr int kCvtPerPhase = 28 * CB;  // per 16 codes: 4 xor, 16 int -> f32, 8 packs
-  constexpr int kLead = 4;               // MFMAs that cover the LDS read latency
+  constexpr int kLead = kMfmaPerPhase > 4 ? 4 : 1;  // MFMAs that cover the LDS read latency
   constexpr int kv = (kCvtPerPhase + kMfmaPerPhase - kLead - 1) / (kMfmaPerPhase - kLead) + 1;
   auto phase_order = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase, 0);
@@ -666,6 +670,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   }
 }
 
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
+                                                                         const uint16_t* __restrict__ scales,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         uint16_t* __restrict__ y,
+                                                                         float* __restrict__ part, int M, int K,
+                                                                         int N, int tail0, int tailS) {
+  dma_w8pc_body<WM, WN, DBM>(qw, scales, x, y, part, M, K, N, tail0, tailS);
+}
+
+// 64-row tiles (capping the registers for two workgroups per CU spills: measured slower)
+__global__ __launch_bounds__(512, 1) void gemm_dma64_w8pc_kernel(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+                            const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part,
+                            int M, int K, int N, int tail0, int tailS) {
+  dma_w8pc_body<1, 8, 64>(qw, scales, x, y, part, M, K, N, tail0, tailS);
+}
+
 // ---------------------------------------------------------------------------------
 // Group-128 formats, large M: the same LDS-DMA pipeline with fp16 matrix products.
 //
@@ -705,20 +726,21 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(la), "v"(g) : "memory", "m0");
 }
 
-template <int FMT>
+template <int FMT, int TM = DBM>
 struct G128Dma {
   static constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  static constexpr int kXBytes = TM * DBK * 2;          // x rows of a stage
   static constexpr int kCodeRow = kW4 ? DBK / 2 : DBK;  // code bytes per row and step
   static constexpr int kCodeBytes = DBN * kCodeRow;
   static constexpr int kMetaBytes = DBN * 2 + (kW4 ? DBN / 2 : 0);
-  static constexpr int kStage = DA_BYTES + kCodeBytes + kMetaBytes;
+  static constexpr int kStage = kXBytes + kCodeBytes + kMetaBytes;
   static constexpr int kCodeInst = kCodeBytes / 1024;  // code DMA instructions per step
 };
 
 // Exact fallback for one workgroup tile (see above): each wave takes 32 x 32 blocks in
 // turn; per block and group, eight v_mfma_f32_32x32x16_bf16 on exact codes give the
 // group's fp32 partial, which the group scale adds into the block.
-template <int FMT>
+template <int FMT, int TM = DBM>
 __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                                 const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
                                 uint16_t* __restrict__ y, float* __restrict__ part, int M, int K, int N,
@@ -728,7 +750,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   const int G = K / kGroup;
   const int row_bytes = kW4 ? K / 2 : K;
-  for (int blk = wave; blk < (DBM / 32) * (DBN / 32); blk += NW) {
+  for (int blk = wave; blk < (TM / 32) * (DBN / 32); blk += NW) {
     const int bi = blk / (DBN / 32), bj = blk % (DBN / 32);
     const int m = min(m0 + 32 * bi + l32, M - 1), n = min(n0 + 32 * bj + l32, N - 1);
     const size_t mi = ((size_t)(n / kGemvTileRows) * G) * kGemvTileRows + n % kGemvTileRows;
@@ -794,7 +816,7 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__
 
 // XH: xd is x already in fp16 (x_to_f16_kernel); otherwise xd == x and the stages
 // are converted in LDS.  The exact fallback always reads the bf16 x.
-template <int FMT, int WM, int WN, bool XH = false>
+template <int FMT, int WM, int WN, bool XH = false, int TM = DBM>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
@@ -804,10 +826,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
                                                                          int tailS) {
-  using F = G128Dma<FMT>;
+  using F = G128Dma<FMT, TM>;
   constexpr bool kW4 = F::kW4;
-  constexpr int NW = WM * WN, RB = 8 / WM, CB = 8 / WN;
-  constexpr int XI = 32 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
+  constexpr int NW = WM * WN, RB = TM / 32 / WM, CB = 8 / WN;
+  constexpr int XI = TM / 8 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
+  constexpr int kDA = F::kXBytes;
+  static_assert(XI >= 1 && RB >= 1, "tile shape");
   constexpr int kDmaPerStep = XI + WI;
   constexpr int KUNIT = 2;  // split-K granularity in steps: one group
   static_assert(WI >= 1, "every wave takes part in the code DMA");
@@ -818,10 +842,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   __shared__ float wave_max[NW];
 
   DmaWork wk;
-  if (!dma_work(M, N, tail0, tailS, wk)) return;
-  const int mblocks = (M + DBM - 1) / DBM;
+  if (!dma_work(M, N, tail0, tailS, wk, TM)) return;
+  const int mblocks = (M + TM - 1) / TM;
   const int nb = wk.lin / mblocks, mb = wk.lin % mblocks;
-  const int n0 = nb * DBN, m0 = mb * DBM;
+  const int n0 = nb * DBN, m0 = mb * TM;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -872,13 +896,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(xd + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + DA_BYTES + (WI * wave + j) * 1024);
+    for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + kDA + (WI * wave + j) * 1024);
     const int g = k0 / kGroup;
     if (wave == 0 && lane < 32)
-      dma16(scales + ((size_t)mt * G + g) * kGemvTileRows + 8 * (lane & 1), st + DA_BYTES + F::kCodeBytes);
+      dma16(scales + ((size_t)mt * G + g) * kGemvTileRows + 8 * (lane & 1), st + kDA + F::kCodeBytes);
     if (kW4 && wave == 1 && lane < 32)
       dma4(zeros + ((size_t)mt * G + g) * (kGemvTileRows / 2) + 4 * (lane & 1),
-           st + DA_BYTES + F::kCodeBytes + DBN * 2);
+           st + kDA + F::kCodeBytes + DBN * 2);
   };
   // the x chunks this lane's own DMA brought into a stage, bf16 -> fp16 in place
   // (v_cvt_pk_f16_f32, nearest even: beyond fp16 range gives Inf)
@@ -899,9 +923,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     for (int s2 = 0; s2 < 2; ++s2)
       aaddr[P][s2] = (wm * 32 * RB + l32) * 128 + 16 * ((4 * P + 2 * lh + s2) ^ swz_x(l32));
     if constexpr (kW4)
-      baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 32 + 16 * (P ^ ((l32 >> 3) & 1)) + 8 * lh;
+      baddr[P] = kDA + (wn * 32 * CB + l32) * 32 + 16 * (P ^ ((l32 >> 3) & 1)) + 8 * lh;
     else
-      baddr[P] = DA_BYTES + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
+      baddr[P] = kDA + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
   }
 
   f16x8_t A0[2][RB], B0[2][CB];
@@ -913,10 +937,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const int n = wn * 32 * CB + j * 32 + l32;
-      const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + DA_BYTES + F::kCodeBytes + 2 * n);
+      const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + kDA + F::kCodeBytes + 2 * n);
       _Float16 sh;
       if constexpr (kW4) {
-        const uint8_t zb = st[DA_BYTES + F::kCodeBytes + DBN * 2 + (n >> 1)];
+        const uint8_t zb = st[kDA + F::kCodeBytes + DBN * 2 + (n >> 1)];
         const _Float16 z = (_Float16)(float)((zb >> (4 * (n & 1))) & 15u);
         sh = __builtin_bit_cast(_Float16, sb);
         mo0[j] = f16x2_t{-(_Float16)1024.f - z, -(_Float16)1024.f - z};
@@ -1032,7 +1056,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 
   constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + 3 * CB;
   constexpr int kCvtPerPhase = 30 * CB;  // per 16 codes: extraction, 8 packed adds, 8 packed multiplies
-  constexpr int kLead = 4;               // MFMAs that cover the LDS read latency
+  constexpr int kLead = kMfmaPerPhase > 4 ? 4 : 1;  // MFMAs that cover the LDS read latency
   constexpr int kv = (kCvtPerPhase + kMfmaPerPhase - kLead - 1) / (kMfmaPerPhase - kLead) + 1;
   auto phase_order = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase, 0);
@@ -1128,7 +1152,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   }
   constexpr float kCodeMax = kW4 ? 15.f : 127.f;  // largest |q - z| or |q|
   if (any || !(kCodeMax * ws <= 16.f)) {  // (NaN scales fail the comparison)
-    g128_tile_exact<FMT>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, S,
+    g128_tile_exact<FMT, TM>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, S,
                          wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
     return;
   }
@@ -1696,7 +1720,19 @@ int gemm_dma_tail(int64_t M, int64_t N, int* tail0) {
   return (int)std::min<int64_t>(kDmaTailMaxSplit, cus / r);
 }
 
+int gemm_dma64_split(int tile, int64_t M, int64_t N) {
+  if (tile < kDma64Tile0 || tile > kDma64TileLast) return 0;
+  const int64_t blocks = ((M + 63) / 64) * ((N + DBN - 1) / DBN);
+  int S = 1 << (tile - kDma64Tile0);
+  while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
+  return S;
+}
+
 size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
+  if (tile >= kDma64Tile0) {
+    const int S = gemm_dma64_split(tile, M, N);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  }
   if (tile == kDmaTailTile) {
     int tail0 = 0;
     const int S = gemm_dma_tail(M, N, &tail0);
@@ -1740,8 +1776,53 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   // the 4-wave layouts would spill its registers -- and tiles 3 and 4 take tile 1), and
   // 10..12: tile 9 with split-K 2, 4, 8 (fp32 partials in the workspace, added in
   // range order by a second kernel; split 1 when the workspace is too small)
-  const bool dma_tile = tile == 3 || tile == 4 || tile >= 9;
   const bool pc = w->fmt == WQ_FMT_W8_PC;
+  if (tile >= kDma64Tile0 && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
+    // 64-row LDS-DMA tiles, split-K 1 / 2 / 4 over gridDim.y
+    const int64_t total = ((M + 63) / 64) * ((N + DBN - 1) / DBN);
+    int S = gemm_dma64_split(tile, M, N);
+    if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
+    S = std::min(S, K / (DBK * (pc ? 1 : 2)));
+    const dim3 grid((unsigned)(8 * ((total + 7) / 8)), (unsigned)S);
+    float* part = (float*)ws;
+    if (pc) {
+      gemm_dma64_w8pc_kernel<<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
+    } else {
+      const size_t xh_off = round256(S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
+      uint16_t* xh = nullptr;
+      if (ws && ws_bytes >= xh_off + (size_t)M * K * 2 && ((uintptr_t)ws + xh_off) % 16 == 0) {
+        xh = (uint16_t*)((uint8_t*)ws + xh_off);
+        const int64_t n8 = M * K / 8;
+        x_to_f16_kernel<<<(unsigned)std::min<int64_t>((n8 + 255) / 256, 4096), 256, 0, s>>>((const uint4*)x,
+                                                                                          (uint4*)xh, n8);
+        WQ_HIP_CHECK(hipGetLastError());
+      }
+      const int t0 = (int)total;
+      if (w->fmt == WQ_FMT_W4_G128) {
+        if (xh)
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 1, 8, true, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1);
+        else
+          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 1, 8, false, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1);
+      } else {
+        if (xh)
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 1, 8, true, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1);
+        else
+          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 1, 8, false, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1);
+      }
+    }
+    WQ_HIP_CHECK(hipGetLastError());
+    if (S > 1) {
+      const int64_t MN = M * N;
+      if (pc)
+        gemm_splitk_reduce_kernel<true><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      else
+        gemm_splitk_reduce_kernel<false><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      WQ_HIP_CHECK(hipGetLastError());
+    }
+    return WQ_OK;
+  }
+  if (tile >= kDma64Tile0) tile = 1;  // shapes outside the LDS-DMA tiles
+  const bool dma_tile = tile == 3 || tile == 4 || tile >= 9;
   if (dma_tile && (pc || tile >= 9) && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
     const int kcap = K / (DBK * (pc ? 1 : 2));  // at least one step (group) per K range

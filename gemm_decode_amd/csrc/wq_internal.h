@@ -99,6 +99,11 @@ int gemm_dma_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a
 // spreads over the idle CUs; gemm_dma_tail returns that split (1: nothing to split)
 // and sets *tail0 to the number of tiles that stay whole.
 constexpr int kDmaTailTile = 13, kDmaTailMaxSplit = 4;
+// GEMM tiles kDma64Tile0 .. kDma64TileLast: the LDS-DMA pipeline with 64-row x tiles
+// (a few tokens: the weights stream as in tile 9 with a quarter of its x traffic and
+// MFMA work) and split-K 1, 2, 4, capped as the split LDS-DMA tiles.
+constexpr int kDma64Tile0 = 14, kDma64TileLast = 16;
+int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of them
 int gemm_dma_tail(int64_t M, int64_t N, int* tail0);
 // Compute units of the current device (kDefaultCUs, MI355X's count, if it cannot be queried).
 constexpr int kDefaultCUs = 256;

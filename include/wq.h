@@ -251,12 +251,16 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      fp32 block per range to the workspace (r x ranges x 256 KiB; needs it, else
  *      WQ_ERR_WORKSPACE; with tile 0 and too small a workspace it runs as tile 9), and a
  *      second kernel adds them in range order; other shapes: tile 9;
+ *   14..16  K % 64 == 0: the LDS-DMA pipeline of tile 9 with 64-row x tiles (1 x 8
+ *      waves; group-128 as tile 9), split-K 1, 2, 4 (partials as for 10..12, capped
+ *      so that the grid stays within 512 workgroups; 15 and 16 need that workspace,
+ *      else WQ_ERR_WORKSPACE); the default for 17..128 tokens; other shapes: tile 1;
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 13
+#define WQ_GEMM_TILES 16
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -313,7 +317,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 13
+#define WQ_TUNE_LAT_SLOTS 16
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

@@ -54,7 +54,7 @@ def _rows_options(wq, fmt, M):
 
 
 def _fp16_staged(fmt, tile):
-    """The group-128 formats' LDS-DMA GEMM (tile 9, and 10..12 with split-K) stages
+    """The group-128 formats' LDS-DMA GEMM (tile 9 and the tiles above it) stages
     fp16(dequant(W)): its exact selections return bf16(fp16(w)) rather than bf16(w)."""
     return fmt != "w8pc" and tile >= 9
 
@@ -316,7 +316,7 @@ def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
             xf[6, 900] = -3.0e5                 # beyond fp16: the first row block falls back
         x = OQ.bf16_rne_bits(xf.astype(np.float32))
         y_ref = OL.ref_linear(x, P)
-        for tile in (9, 11, 1):   # 11: the same with split-K 4 (fp32 partials, also on the exact path)
+        for tile in (9, 11, 15, 1):   # 11: split-K 4 (fp32 partials, also on the exact path); 15: 64-row tiles
             assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} {case} tile={tile}")
         # without a workspace tile 9 converts x to fp16 inside each workgroup: same bits
         assert np.array_equal(_run_gemm(wq, g, x, 9, with_ws=False), _run_gemm(wq, g, x, 9)), f"{fmt} {case}"
@@ -538,7 +538,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
     # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
-    split_tiles = list(range(5, 9)) + list(range(10, 13))  # the split-K tiles (skinny, LDS-DMA)
+    split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16]  # the split-K tiles (skinny, LDS-DMA)
     assert tile not in split_tiles, (tile, lat)
     assert all((v < 0) == (t in split_tiles) for t, v in enumerate(lat, start=1)), (tile, lat)
 
