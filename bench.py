@@ -239,11 +239,18 @@ PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 13), ("w4g128", 5120, 27648, 2048
 
 
 def profile_prefill(calls: int = 10):
-    """Kernels for a rocprofv3 run of the prefill GEMM: for each (fmt, K, N, M, tile) of
-    PREFILL_PROFILE, `calls` wq_linear calls on rotating weight copies with the GEMM
-    tile fixed, as one HIP graph replayed once."""
+    """Kernels for a rocprofv3 run of the prefill GEMM: the elementwise reference (the
+    FETCH_SIZE / WRITE_SIZE scale, as in profile_pass), then for each (fmt, K, N, M,
+    tile) of PREFILL_PROFILE `calls` wq_linear calls on rotating weight copies with the
+    GEMM tile fixed, as one HIP graph replayed once."""
     import torch
     import gemm_decode_amd.wq as wq
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.bitwise_not(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
     for fmt, K, N, M, tile in PREFILL_PROFILE:
         p = Pool(wq, torch, 5, fmt, K, N, M)
         wq.wq_tune_cache_set(fmt, K, N, M, wq.KIND_GEMM, tile)
@@ -288,7 +295,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, trace_dir: str | None, ou
 
     def split(rows, value):
         # the graph issues the shapes round-robin: launch j is shape j % 4
-        ref = [value(r) for r in rows if "elementwise" in r["Kernel_Name"]]
+        ref = [value(r) for r in rows if "bitwise_not" in r["Kernel_Name"]]
         gemv = [value(r) for r in rows if "gemv_kernel" in r["Kernel_Name"]]
         n = len(DECODE_SHAPES)
         return ref, [gemv[i::n] for i in range(n)]
@@ -334,6 +341,55 @@ def summarize_counters(fetch_dir: str, write_dir: str, trace_dir: str | None, ou
     json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
     with open(out_txt, "a") as f:
         f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_prefill_traffic(fetch_dir: str, write_dir: str, out_txt: str):
+    """Turn two rocprofv3 --pmc runs of --profile-prefill (FETCH_SIZE, then WRITE_SIZE,
+    KiB per dispatch) into HBM bytes per GEMM call against the algorithmic bytes
+    (weights + metadata + x + y once): the GEMM kernel, and with it the kernels the
+    call adds (the tail reduction, and x to fp16 for group-128).  Scaled by what the
+    counters read for the elementwise reference."""
+    import glob
+
+    def rows_of(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            out += [r for r in _read_csv_rows(f) if r["Counter_Name"] == counter]
+        return sorted(out, key=lambda r: int(r.get("Dispatch_Id", 0)))
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = rows_of(d, counter)
+        ref = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
+        if not ref:
+            raise SystemExit("reference kernel counters missing")
+        scale = COPY_BYTES / 1024.0 / float(np.median(ref)) * 1024.0  # bytes per counter unit
+        for r in rows:
+            name = r["Kernel_Name"]
+            if not any(k in name for k in ("gemm_dma", "tail_reduce", "x_to_f16")):
+                continue
+            # the per-channel kernels: the w8pc GEMM and tail_reduce<true>
+            pc = "w8pc_kernel" in name or "tail_reduce_kernel<true>" in name
+            kern = next(k for k in ("gemm_dma_w8pc_kernel", "gemm_dma_g128_kernel", "gemm_tail_reduce_kernel",
+                                    "x_to_f16_kernel") if k in name)
+            res.setdefault(("w8pc" if pc else "w4g128", kern, counter), []).append(float(r["Counter_Value"]) * scale)
+    lines = []
+    for fmt, K, N, M, tile in PREFILL_PROFILE:
+        alg = algorithmic_bytes(fmt, K, N, M)
+        main = "gemm_dma_w8pc_kernel" if fmt == "w8pc" else "gemm_dma_g128_kernel"
+        per_call = {}
+        for kern in (main, "gemm_tail_reduce_kernel", "x_to_f16_kernel"):
+            f = res.get((fmt, kern, "FETCH_SIZE"))
+            w = res.get((fmt, kern, "WRITE_SIZE"))
+            if f and w:
+                per_call[kern] = (float(np.median(f)), float(np.median(w)))
+        tot = sum(f + w for f, w in per_call.values())
+        parts = "; ".join(f"{k}: FETCH {f/1e6:.1f} MB + WRITE {w/1e6:.1f} MB" for k, (f, w) in per_call.items())
+        lines.append(f"{fmt} K={K} N={N} M={M} tile={tile}: {parts}; call total {tot/1e6:.1f} MB = "
+                     f"{tot/alg:.3f} x algorithmic {alg/1e6:.1f} MB")
+    with open(out_txt, "a") as fo:
+        fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -387,6 +443,8 @@ def main():
                     help="run the LM head + top-k profile workload (for rocprofv3) and exit")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="run the prefill GEMM profile workload (for rocprofv3) and exit")
+    ap.add_argument("--summarize-prefill-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_TXT"),
+                    help="turn two rocprofv3 --pmc runs of --profile-prefill into HBM bytes per GEMM call")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
                     help="turn rocprofv3 runs of --profile-pass into the traffic record and a summary")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
@@ -394,6 +452,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_prefill_traffic:
+        summarize_prefill_traffic(*args.summarize_prefill_traffic)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
