@@ -582,6 +582,9 @@ def run_detail(wq, torch, args) -> dict:
                            for M in (8, 64, 512, 2048)}
     out["lm_head_topk"] = {f"{fmt}_{K}x{N}_M{M}": measure_lm_head_topk(wq, torch, 4, fmt, K, N, M)
                            for fmt in ("w8g128", "w4g128") for K, N in [(5120, 151936)] for M in (1, 4)}
+    out["activation_permutation"] = {f"{fmt}_{K}x{N}_M{M}": measure_linear_perm(wq, torch, cfg, fmt, K, N, M)
+                                     for cfg, fmt, M in ((3, "w4g128", 1), (1, "w8pc", 1), (5, "w8pc", 2048))
+                                     for K, N in [(5120, 27648)]}
     out["reference_bf16_gemm"] = reference_bf16_gemm(torch)
     return out
 
@@ -609,6 +612,33 @@ def measure_lm_head_topk(wq, torch, cfg, fmt, K, N, M, k: int = 50, temperature:
            "us_linear_topk": round(both * 1e3, 3), "us_added": round((both - lin) * 1e3, 3),
            "GB/s_linear_topk": round(p.bytes_per_call() / (both / 1e3) / 1e9, 1)}
     log(f"lm head + top-k cfg{cfg} {fmt} K={K} N={N} M={M} k={k}: {rec['us_linear_topk']} us "
+        f"(layer alone {rec['us_linear']} us, +{rec['us_added']} us)")
+    p.free()
+    del p
+    torch.cuda.empty_cache()
+    return rec
+
+
+def measure_linear_perm(wq, torch, cfg, fmt, K, N, M) -> dict:
+    """The layer with the full-K activation permutation (gather + layer) against the
+    layer alone (both tuned, graph replay over rotating weight copies): the cost the
+    gather adds."""
+    p = Pool(wq, torch, cfg, fmt, K, N, M)
+    tune(wq, p, 200, 200)
+    n = 2 * len(p.copies)
+    lin = time_graph(torch, lambda: p.call(wq), n) / n
+    ws = wq.workspace(wq.wq_linear_perm_workspace_size(p.copies[0], M))
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(cfg)).to(torch.int32).to("cuda")
+
+    def fn():
+        w = p.copies[p.i]
+        p.i = (p.i + 1) % len(p.copies)
+        wq.wq_linear_perm(w, p.x, perm, p.y, ws)
+
+    both = time_graph(torch, fn, n) / n
+    rec = {"us_linear": round(lin * 1e3, 3), "us_linear_perm": round(both * 1e3, 3),
+           "us_added": round((both - lin) * 1e3, 3)}
+    log(f"activation permutation cfg{cfg} {fmt} K={K} N={N} M={M}: {rec['us_linear_perm']} us "
         f"(layer alone {rec['us_linear']} us, +{rec['us_added']} us)")
     p.free()
     del p

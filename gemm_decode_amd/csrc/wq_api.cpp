@@ -476,6 +476,49 @@ wq_status wq_lm_head_topk(const wq_weight* w, const void* x, int64_t M, int k, f
                      top_idx, tokens, (hipStream_t)stream);
 }
 
+// ------------------------------------------------- full-K activation permutation
+namespace {
+// workspace: [the layer's own workspace][x' bf16 [M][K]], x' 256-byte aligned
+wq_status perm_layout(const wq_weight* w, int64_t M, size_t* lin, size_t* xp_off, size_t* total) {
+  if (!w) return fail(WQ_ERR_INVALID_ARG, "NULL weight");
+  wq_status st = check_shape(w->fmt, w->K, w->N);
+  if (st != WQ_OK) return st;
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if ((st = wq_workspace_size(w, M, lin)) != WQ_OK) return st;
+  *xp_off = round_up256(*lin);
+  *total = *xp_off + (size_t)M * w->K * 2;
+  return WQ_OK;
+}
+}  // namespace
+
+wq_status wq_linear_perm_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
+  if (!bytes) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  size_t lin = 0, off = 0, total = 0;
+  const wq_status st = perm_layout(w, M, &lin, &off, &total);
+  if (st == WQ_OK) *bytes = total;
+  return st;
+}
+
+wq_status wq_linear_perm(const wq_weight* w, const void* x, const int32_t* perm, int64_t M, void* y, void* ws,
+                         size_t ws_bytes, void* stream) {
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  size_t lin = 0, off = 0, total = 0;
+  if ((st = perm_layout(w, M, &lin, &off, &total)) != WQ_OK) return st;
+  if (!x || !perm || !y) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  if ((uintptr_t)x % 2 || (uintptr_t)perm % 4 || (uintptr_t)y % 2)
+    return fail(WQ_ERR_ALIGNMENT, "wq_linear_perm: x and y need 2-byte, perm 4-byte alignment");
+  if (!ws || ws_bytes < total)
+    return fail(WQ_ERR_WORKSPACE, "wq_linear_perm needs a workspace of " + std::to_string(total) + " bytes");
+  if ((uintptr_t)ws % 256) return fail(WQ_ERR_ALIGNMENT, "wq_linear_perm: the workspace must be 256-byte aligned");
+  uint16_t* xp = (uint16_t*)((uint8_t*)ws + off);
+  if ((st = launch_perm_gather((const uint16_t*)x, perm, xp, M, w->K, (hipStream_t)stream)) != WQ_OK) return st;
+  // the layer on the gathered activations, confined to its own part of the workspace
+  void* lin_ws = lin ? ws : nullptr;
+  return wq_dispatch_kind(M) == WQ_KIND_GEMV ? gemv_impl(w, xp, M, y, 0, 0, 0, lin_ws, lin, stream)
+                                             : gemm_impl(w, xp, M, y, 0, lin_ws, lin, stream);
+}
+
 int wq_tune_pick(const double* lat, int n) {
   if (!lat || n < 1) return -1;
   int best = -1;

@@ -66,6 +66,10 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 // --- kernel launchers (implemented in the .hip files) ---
 wq_status launch_pack(const float* w, const wq_weight* out, hipStream_t s);
 wq_status launch_pack_bf16(const uint16_t* w, const wq_weight* out, hipStream_t s);
+// x'[m][j] = x[m][perm[j]] for m < M, j < K (K % 8 == 0, xp 16-byte aligned); an
+// index outside [0, K) reads as +0.
+wq_status launch_perm_gather(const uint16_t* x, const int32_t* perm, uint16_t* xp, int64_t M, int64_t K,
+                             hipStream_t s);
 wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s);
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
                       int waves, int rows, void* ws, hipStream_t s);

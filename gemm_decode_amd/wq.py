@@ -21,6 +21,7 @@ __all__ = [
     "wq_gemv_max_waves", "wq_gemv_max_split",
     "wq_pack", "wq_pack_bf16", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
+    "wq_linear_perm_workspace_size", "wq_linear_perm",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -74,6 +75,9 @@ _SIGS = {
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
+    "wq_linear_perm_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
+    "wq_linear_perm": (C.c_int, [_W, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t,
+                                 C.c_void_p]),
     "wq_lm_head_topk": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_tune_pick": (C.c_int, [_P(C.c_double), C.c_int]),
@@ -282,6 +286,23 @@ def wq_lm_head_topk(w: PackedWeight, x: torch.Tensor, k: int, temperature: float
     _check(lib.wq_lm_head_topk(C.byref(d), _ptr(x), M, k, float(temperature), _ptr(u), _ptr(top_vals),
                                _ptr(top_idx), _ptr(tokens), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream(stream)), "wq_lm_head_topk")
+
+
+def wq_linear_perm_workspace_size(w: PackedWeight, M: int) -> int:
+    d, n = w.desc(), C.c_size_t()
+    _check(lib.wq_linear_perm_workspace_size(C.byref(d), M, C.byref(n)), "wq_linear_perm_workspace_size")
+    return n.value
+
+
+def wq_linear_perm(w: PackedWeight, x: torch.Tensor, perm: torch.Tensor, y: torch.Tensor,
+                   ws: torch.Tensor, stream=None) -> None:
+    """x bf16 [M][K], perm int32 [K], y bf16 [M][N] (all on the device): y = x[:, perm]
+    times the stored weight."""
+    M = _xy(x, y, w)
+    assert perm.dtype == torch.int32 and perm.is_contiguous() and perm.numel() == w.K
+    d = w.desc()
+    _check(lib.wq_linear_perm(C.byref(d), _ptr(x), _ptr(perm), M, _ptr(y), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream)), "wq_linear_perm")
 
 
 # ---------------------------------------------------------------------- tuner

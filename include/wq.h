@@ -296,6 +296,27 @@ wq_status wq_lm_head_topk(const wq_weight* w, const void* x, int64_t M, int k, f
                           const float* u, void* top_vals, int32_t* top_idx, int32_t* tokens,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------- full-K activation permutation */
+
+/* The layer on activations gathered along K ("full-K activation permutation" in the
+ * Marlin register and launch scheduling benchmark page, "Validation and limits"; the
+ * same page counts activation-order index storage in its dense kernel): the weight
+ * is stored with its K columns in a permuted order, W'[n][j] = W[n][perm[j]] (pack
+ * W' with wq_pack, so its groups are contiguous along the stored order), and
+ *   y[m][n] = bf16( sum_j x[m][perm[j]] * dequant(W')[n][j] )  (= x . W^T).
+ * One kernel gathers x'[m][j] = x[m][perm[j]] into the workspace, then the layer runs
+ * as wq_linear on x' (same dispatch, tuned configurations and rounding: the result is
+ * bit-identical to wq_linear on x' given a workspace of wq_workspace_size bytes).
+ *
+ * x: bf16 [M][K] (device, 2-byte aligned); perm: int32 [K] (device, 4-byte aligned;
+ * read as given: an index outside [0, K) reads x as +0, a repeated index is a plain
+ * gather); y: bf16 [M][N] (device).  ws (256-byte aligned) of
+ * wq_linear_perm_workspace_size bytes (the layer's own workspace, then x'), else
+ * WQ_ERR_WORKSPACE.  The caller owns every buffer; nothing is allocated. */
+wq_status wq_linear_perm_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
+wq_status wq_linear_perm(const wq_weight* w, const void* x, const int32_t* perm, int64_t M, void* y,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ tuner */
 
 /* Choose among measured candidates: the smallest latency wins and a tie goes to

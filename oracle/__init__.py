@@ -11,7 +11,8 @@ What it computes (plain, slow, obviously correct; NumPy only):
   channel, W8 group-128, W4 asymmetric group-128), step by step.
 * ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
   chunked along N; sampled-column variants for full-size checks; the
-  comparison statistics with the per-element tolerance.
+  comparison statistics with the per-element tolerance; the full-K activation
+  permutation (x gathered along K before the product).
 * ``topk``   -- the k best bf16 logits of a row and the token drawn from them
   with a temperature and a caller-supplied uniform draw (the LM head + top-k
   step of the tileInfer README's feature list; reading in its docstring).
@@ -36,6 +37,6 @@ from .quant import (  # noqa: F401
     quantize_w4g128, quantize_w8, unpack_w4g128,
 )
 from .linear import (  # noqa: F401
-    compare, ref_linear, ref_linear_columns, token_count, use_gemv,
+    compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, token_count, use_gemv,
 )
 from .topk import ref_topk_sample, sample_row, topk_row  # noqa: F401

@@ -63,6 +63,30 @@ def ref_linear_columns(x_bits: np.ndarray, P: dict, cols) -> np.ndarray:
     return x @ Wd.T
 
 
+def gather_activations(x_bits: np.ndarray, perm) -> np.ndarray:
+    """x'[m, j] = x[m, perm[j]] (bf16 bits), an index outside [0, K) giving +0: the
+    full-K activation permutation that the Marlin register and launch scheduling
+    benchmark page lists among its validated cases ("Validation and limits").  The
+    stored weight then holds the columns in the same order, W'[n, j] = W[n, perm[j]],
+    so that x' . W'^T = x . W^T when perm is a permutation."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    x = x.reshape(-1, x.shape[-1])
+    K = x.shape[1]
+    perm = np.asarray(perm, dtype=np.int64).ravel()
+    if perm.size != K:
+        raise ValueError("perm must hold K indices")
+    out = np.zeros_like(x)
+    for j, i in enumerate(perm):
+        if 0 <= i < K:
+            out[:, j] = x[:, i]
+    return out
+
+
+def ref_linear_perm(x_bits: np.ndarray, P: dict, perm) -> np.ndarray:
+    """fp64 y = x' . dequant(W')^T with x' the activations gathered by perm."""
+    return ref_linear(gather_activations(x_bits, perm), P)
+
+
 def compare(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
     """Per-element check of bf16 results against the fp64 reference.
 

@@ -447,6 +447,42 @@ def pin_topk_sampling_closed_forms():
     assert OT.sample_row(np.array([0x3F80, 0xFF80, 0x3F80], np.uint16), [5, 6, 7], 1.0, 0.6) == 7
 
 
+# ------------------------------------------------- full-K activation permutation
+def pin_activation_permutation(seed=41, K=256, N=24, M=3):
+    """The gather x'[m, j] = x[m, perm[j]] against facts other than its own code:
+    (a) per-channel W8 codes do not depend on the column order (one scale per row),
+    so storing W[:, perm] and gathering x by the same perm reproduces the plain
+    layer to fp64 rounding -- a perm that is not its own inverse catches a gather in
+    the wrong direction; (b) a brute-force sum over exact rationals (codes and bf16
+    decoded by hand) of x[perm[j]] * W'[n, j], with one index out of range (+0) and
+    one repeated, on group-128 W4."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(K)
+    assert np.any(perm[perm] != np.arange(K))            # not an involution
+    W = synth.weight(seed, K, N)
+    x = synth.activation(seed, K, M)
+    y0 = OL.ref_linear(x, OQ.pack("w8pc", W))
+    y1 = OL.ref_linear_perm(x, OQ.pack("w8pc", np.ascontiguousarray(W[:, perm])), perm)
+    assert np.allclose(y1, y0, rtol=1e-12, atol=1e-12)
+    # (b) tiny brute force with an out-of-range and a repeated index
+    K2, N2 = 128, 8
+    W2 = synth.weight(seed + 1, K2, N2, outliers=True)
+    P2 = OQ.pack("w4g128", W2)
+    x2 = synth.activation(seed + 1, K2, 2)
+    p2 = rng.permutation(K2)
+    p2[5] = K2 + 3                                       # reads +0
+    p2[9] = p2[10]                                       # a plain gather repeats
+    y2 = OL.ref_linear_perm(x2, P2, p2)
+    for m in range(2):
+        xv = [_bf16_bits_value(int(b)) for b in x2[m]]
+        for n in range(N2):
+            terms = [(xv[int(p2[j])] if 0 <= p2[j] < K2 else Fraction(0)) * _exact_dequant(P2, n, j)
+                     for j in range(K2)]
+            exact = sum(terms)
+            bound = sum(abs(t) for t in terms) * Fraction(K2 + 2, 2 ** 53)
+            assert abs(Fraction(float(y2[m, n])) - exact) <= bound, (m, n)
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
     pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
@@ -456,7 +492,7 @@ ALL_PINS = [
     lambda: pin_bruteforce("w8pc", 48), lambda: pin_bruteforce("w8g128", 128),
     lambda: pin_bruteforce("w4g128", 128), pin_library_factorisation, pin_invariants,
     pin_compare, pin_dispatch, pin_topk_golden, pin_topk_defining_property,
-    pin_topk_sampling_closed_forms,
+    pin_topk_sampling_closed_forms, pin_activation_permutation,
 ]
 
 

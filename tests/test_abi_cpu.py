@@ -253,6 +253,32 @@ def test_lm_head_topk_validation_and_workspace(wqlib):
     assert call(1.0, d=canon) == 2                                     # not the gfx950 layout
 
 
+def test_linear_perm_validation_and_workspace(wqlib):
+    """The activation-permutation entry point refuses bad arguments on the host; its
+    workspace is the layer's own, then x' bf16 [M][K] from a 256-byte boundary."""
+    L = wqlib.lib
+    n, lin = C.c_size_t(), C.c_size_t()
+    r = lambda b: (b + 255) // 256 * 256
+    for fmt, M in ((0, 1), (2, 4), (1, 2048)):
+        d = _desc(wqlib, fmt=fmt, K=5120, N=27648)
+        assert L.wq_workspace_size(C.byref(d), M, C.byref(lin)) == 0
+        assert L.wq_linear_perm_workspace_size(C.byref(d), M, C.byref(n)) == 0
+        assert n.value == r(lin.value) + M * 5120 * 2
+    d = _desc(wqlib, fmt=0, K=5120, N=27648)
+    assert L.wq_linear_perm_workspace_size(C.byref(d), 0, C.byref(n)) == 1          # M < 1
+    x, perm, y, ws = C.c_void_p(0x10000), C.c_void_p(0x20000), C.c_void_p(0x30000), C.c_void_p(0x100000)
+    big = 1 << 30
+    call = lambda **kw: L.wq_linear_perm(C.byref(kw.get("d", d)), kw.get("x", x), kw.get("perm", perm),
+                                         kw.get("M", 1), kw.get("y", y), kw.get("ws", ws), kw.get("wsb", big), None)
+    assert call(perm=None) == 1 and call(x=None) == 1 and call(y=None) == 1
+    assert call(M=0) == 1
+    assert call(perm=C.c_void_p(0x20002)) == 3                          # int32 index misaligned
+    assert call(x=C.c_void_p(0x10001)) == 3
+    assert call(ws=C.c_void_p(0x100010)) == 3                           # workspace not 256-aligned
+    assert call(wsb=1024) == 4 and call(ws=None) == 4                   # workspace too small / missing
+    assert call(d=_desc(wqlib, fmt=0, layout=0, K=5120, N=27648)) == 2  # not the gfx950 layout
+
+
 def test_binding_constants_match_the_header(wqlib):
     """The binding's copies of the header's array sizes and limits (a mismatch once let
     wq_tune write past the binding's latency buffer)."""

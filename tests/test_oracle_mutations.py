@@ -163,11 +163,29 @@ def _mut_sample_at_or_above(mp):
     mp.setattr(OT, "_reached", lambda run, u: run >= u)
 
 
+def _mut_perm_inverse(mp):
+    orig = OL.gather_activations
+
+    def bad(x_bits, perm):                              # x'[perm[j]] = x[j]: the inverse gather
+        perm = np.asarray(perm)
+        inv = np.full(perm.size, perm.size, dtype=np.int64)
+        ok = (perm >= 0) & (perm < perm.size)
+        inv[perm[ok]] = np.nonzero(ok)[0]
+        return orig(x_bits, inv)
+    mp.setattr(OL, "gather_activations", bad)
+
+
+def _mut_perm_out_of_range_wraps(mp):
+    orig = OL.gather_activations
+    mp.setattr(OL, "gather_activations", lambda x_bits, perm: orig(x_bits, np.asarray(perm) % np.asarray(x_bits).shape[-1]))
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
              _mut_topk_ascending, _mut_topk_nan_first, _mut_topk_signed_zero,
-             _mut_sample_temperature_multiplies, _mut_sample_at_or_above]
+             _mut_sample_temperature_multiplies, _mut_sample_at_or_above, _mut_perm_inverse,
+             _mut_perm_out_of_range_wraps]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
