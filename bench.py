@@ -519,6 +519,9 @@ def main():
     del pools
     torch.cuda.empty_cache()
 
+    detail["streaming_ceiling"] = streaming_ceiling(torch)
+    detail["streaming_ceiling"]["headline_pct_of_read"] = round(
+        100 * value / detail["streaming_ceiling"]["read_GB/s"], 1)
     if not args.quick:
         detail.update(run_detail(wq, torch, args))
 
@@ -544,6 +547,43 @@ def main():
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
+
+
+def streaming_ceiling(torch, nbytes: int = 2 << 30, reps: int = 10) -> dict:
+    """Context for the GEMV's % of HBM: what plain vendor kernels stream on this device
+    in the same run -- a bf16 matrix-vector product over a 2 GiB matrix (read only,
+    torch.mv -> the vendor BLAS) and a 1 GiB elementwise copy (read + write), back to
+    back, HIP events around `reps` calls."""
+    K = 8192
+    a = torch.ones((nbytes // 2 // K, K), dtype=torch.bfloat16, device="cuda")
+    v = torch.ones(K, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(a.shape[0], dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        torch.mv(a, v, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mv(a, v, out=out)
+    e1.record()
+    e1.synchronize()
+    read = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, v, out
+    b = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    c = torch.empty_like(b)
+    for _ in range(2):
+        torch.bitwise_not(b, out=c)
+    e0.record()
+    for _ in range(reps):
+        torch.bitwise_not(b, out=c)
+    e1.record()
+    e1.synchronize()
+    copy = 2 * (nbytes // 2) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del b, c
+    torch.cuda.empty_cache()
+    log(f"streaming ceiling: read {read:.0f} GB/s (bf16 mv over 2 GiB), copy {copy:.0f} GB/s (1 GiB in + out)")
+    return {"read_GB/s": round(read, 1), "copy_GB/s": round(copy, 1),
+            "how": "torch.mv of a 2 GiB bf16 matrix [262144, 8192] (vendor BLAS); torch.bitwise_not "
+                   "1 GiB -> 1 GiB; HIP events over 10 back-to-back calls"}
 
 
 def run_detail(wq, torch, args) -> dict:
