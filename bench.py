@@ -86,8 +86,16 @@ class Pool:
         return algorithmic_bytes(self.fmt, self.K, self.N, self.M)
 
     def check(self, wq, torch, cols: int = 128) -> dict:
-        """Parity of copy 0 on sampled output channels against the oracle."""
+        """Parity of copy 0 on sampled output channels against the oracle, and every
+        copy's y bit-identical to copy 0's (a determinism check)."""
         import oracle
+        ys = []
+        for _ in range(len(self.copies)):
+            self.call(wq)
+            ys.append(self.y.clone())
+        torch.cuda.synchronize()
+        same = all(torch.equal(ys[0], t) for t in ys[1:])
+        del ys
         self.i = 0
         self.call(wq)
         torch.cuda.synchronize()
@@ -96,6 +104,7 @@ class Pool:
         P = oracle.pack(self.fmt, self.W[rows])
         y = self.y.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
         st = oracle.compare(y, oracle.ref_linear(self.x_bits, P))
+        st["copies_bit_identical"] = bool(same)
         self.i = 0
         return st
 
@@ -104,9 +113,10 @@ class Pool:
         self.W = None
 
 
-def time_graph(torch, fn, n_calls: int, reps: int = 3):
-    """Capture n_calls of fn() in one HIP graph; return the median replay time (ms)
-    measured with HIP events on the capturing stream."""
+def time_graph(torch, fn, n_calls: int, reps: int = 9, stats: dict | None = None):
+    """Capture n_calls of fn() in one HIP graph; after 2 warm-up replays return the
+    median of `reps` timed replays (ms), measured with HIP events on the capturing
+    stream (min and max go into `stats` when given)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -130,6 +140,8 @@ def time_graph(torch, fn, n_calls: int, reps: int = 3):
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
     del g
+    if stats is not None:
+        stats.update(min_ms=float(min(times)), max_ms=float(max(times)), reps=reps)
     return float(np.median(times))
 
 
@@ -490,7 +502,7 @@ def main():
         log(f"tuned w8pc K={p.K} N={p.N} M=1: split_k={tuned[(p.K, p.N)][0]} lat_us={tuned[(p.K, p.N)][1]}")
     parity = {f"{p.K}x{p.N}": p.check(wq, torch) for p in pools}
     for k, st in parity.items():
-        if st["fails"]:
+        if st["fails"] or not st["copies_bit_identical"]:
             raise SystemExit(f"parity failure on {k}: {st}")
 
     def step():
@@ -598,7 +610,9 @@ def run_detail(wq, torch, args) -> dict:
         if check:
             rec["parity"] = p.check(wq, torch)
         n = 2 * len(p.copies)
-        per = time_graph(torch, lambda: p.call(wq), n) / n
+        st = {}
+        per = time_graph(torch, lambda: p.call(wq), n, stats=st) / n
+        rec["us_min_max"] = [round(st["min_ms"] / n * 1e3, 3), round(st["max_ms"] / n * 1e3, 3)]
         gbs = p.bytes_per_call() / (per / 1e3) / 1e9
         tf = 2.0 * M * K * N / (per / 1e3) / 1e12
         rec.update({"us": round(per * 1e3, 3), "GB/s": round(gbs, 1),
