@@ -33,13 +33,9 @@ def wqlib():
 
 @pytest.fixture(autouse=True)
 def _name_the_gpu_case(request):
-    """Before each GPU test, record its id (flushed) so a run that ends the box
-    still names the case it was in."""
+    """Before each GPU test, print its id to stderr (flushed), so that a run which
+    ends abruptly still names the case it was in."""
     if request.node.get_closest_marker("gpu") is not None:
-        os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-        with open(os.path.join(ROOT, "gpurun_out", "current_case.txt"), "a") as f:
-            f.write(request.node.nodeid + "\n")
-            f.flush()
         sys.stderr.write(f"[gpu case] {request.node.nodeid}\n")
         sys.stderr.flush()
     yield
