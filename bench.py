@@ -275,6 +275,61 @@ def profile_prefill(calls: int = 10):
         torch.cuda.empty_cache()
 
 
+# (K, N) -> (split_k, waves, rows): the launches the tuner picks for the W4 decode shapes
+PROFILE_W4 = {(5120, 27648): (1, 3, 8), (13824, 5120): (1, 4, 4)}
+
+
+def profile_w4(calls: int = 10):
+    """Kernels for a rocprofv3 run of the W4 group-128 decode GEMV at M = 1: for each
+    (K, N) of PROFILE_W4 that launch (set in the tuning cache, so no tuner dispatches
+    enter the profile), `calls` wq_linear calls on rotating weight copies as one HIP
+    graph replayed once."""
+    import torch
+    import gemm_decode_amd.wq as wq
+    for (K, N), (sk, wv, rw) in PROFILE_W4.items():
+        p = Pool(wq, torch, 3, "w4g128", K, N, 1)
+        wq.wq_tune_cache_set("w4g128", K, N, 1, wq.KIND_GEMV, sk | (wv << 8) | (rw << 16))
+        v = wq.wq_tune_cache_get("w4g128", K, N, 1, wq.KIND_GEMV)
+        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1)
+        log(f"profile w4 K={K} N={N} M=1 (split, waves, rows) = ({v & 0xFF}, {(v >> 8) & 0xFF}, "
+            f"{v >> 16:#x}): {ms * 1e3 / calls:.2f} us per call (HIP events)")
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+
+
+def summarize_valu(pmc_dir: str, out_txt: str):
+    """Turn one rocprofv3 --pmc pass (SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VMEM_RD
+    SQ_WAVE_CYCLES SQ_WAIT_INST_ANY) of --profile-w4 into per-wave instruction counts and
+    the VALU issue time per SIMD (4 cycles per wave64 instruction, 1024 SIMDs)."""
+    import glob
+    from collections import defaultdict
+    rows = []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        rows += _read_csv_rows(f)
+    d = defaultdict(dict)
+    for r in rows:
+        if "gemv" in r["Kernel_Name"]:
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+            key = (name, int(r["Grid_Size"]), int(r["Dispatch_Id"]))
+            d[key][r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = defaultdict(list)
+    for (name, grid, _), c in d.items():
+        groups[(name, grid)].append(c)
+    lines = []
+    for (name, grid), cs in groups.items():
+        avg = {k: float(np.mean([c[k] for c in cs])) for k in cs[0]}
+        w = avg["SQ_WAVES"]
+        valu_us = avg["SQ_INSTS_VALU"] * 4 / 1024 / 2.4e3
+        lines.append(f"{name} grid={grid}: {len(cs)} dispatches, {w:.0f} waves; per wave {avg['SQ_INSTS_VALU'] / w:.0f} "
+                     f"VALU, {avg['SQ_INSTS_VMEM_RD'] / w:.1f} vector-memory reads, waiting to issue "
+                     f"{100 * avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.0f} % of wave cycles; VALU issue "
+                     f"per SIMD {valu_us:.2f} us at 2.4 GHz")
+    with open(out_txt, "a") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def profile_topk(calls: int = 10):
     """Kernels for a rocprofv3 run of the LM head + top-k call: W8 and W4 group-128 LM
     heads (5120, 151936) at M = 1, k = 50, tuned, `calls` calls on rotating weight
@@ -457,6 +512,9 @@ def main():
                     help="run the prefill GEMM profile workload (for rocprofv3) and exit")
     ap.add_argument("--summarize-prefill-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_TXT"),
                     help="turn two rocprofv3 --pmc runs of --profile-prefill into HBM bytes per GEMM call")
+    ap.add_argument("--profile-w4", action="store_true", help="kernels for rocprofv3: the W4 decode GEMV")
+    ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
+                    help="turn a rocprofv3 SQ counter pass of --profile-w4 into VALU figures")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
                     help="turn rocprofv3 runs of --profile-pass into the traffic record and a summary")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
@@ -464,6 +522,12 @@ def main():
     args = ap.parse_args()
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.profile_w4:
+        profile_w4()
+        return
+    if args.summarize_valu:
+        summarize_valu(*args.summarize_valu)
         return
     if args.summarize_prefill_traffic:
         summarize_prefill_traffic(*args.summarize_prefill_traffic)
