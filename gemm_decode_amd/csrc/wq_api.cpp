@@ -568,6 +568,49 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   WQ_HIP_CHECK(hipEventCreate(&e1));
   std::vector<double> lat(cand.size(), -1.0);
   int rot = 0;
+  // one call of candidate c on stream q, on the next weight copy
+  auto run_cand = [&](size_t c, hipStream_t q) -> wq_status {
+    const wq_weight* w = &copies[rot];
+    rot = (rot + 1) % n_copies;
+    return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, cand[c].rows, ws, ws_bytes, q)
+                : gemm_impl(w, x, M, y, cand[c].tile, ws, ws_bytes, q);
+  };
+  // Mean microseconds per call of candidate c as HIP graph replays: two rotations over
+  // the copies (at least 8 calls) captured on a stream of the tuner's own, 2 replays
+  // of warm-up, then replays covering about `iters` calls.  Leaves *us unchanged when
+  // the graph cannot be built (the back-to-back timing then stands).
+  auto time_cand_graph = [&](size_t c, double* us) -> wq_status {
+    if (*us < 0) return WQ_OK;
+    const int calls = std::max(8, 2 * n_copies);
+    const int reps = std::max(1, iters / calls);
+    hipStream_t cs = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    wq_status rs = WQ_OK;
+    float ms = 0.f;
+    WQ_HIP_CHECK(hipStreamSynchronize(hs));
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return WQ_OK;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed) == hipSuccess) {
+      for (int i = 0; i < calls && rs == WQ_OK; ++i) rs = run_cand(c, cs);
+      const hipError_t ec = hipStreamEndCapture(cs, &graph);
+      if (rs == WQ_OK && ec == hipSuccess && graph &&
+          hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess) {
+        bool ok = hipGraphLaunch(exec, cs) == hipSuccess && hipGraphLaunch(exec, cs) == hipSuccess &&
+                  hipEventRecord(e0, cs) == hipSuccess;
+        for (int r = 0; ok && r < reps; ++r) ok = hipGraphLaunch(exec, cs) == hipSuccess;
+        ok = ok && hipEventRecord(e1, cs) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+             hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        if (ok) *us = (double)ms * 1000.0 / ((double)reps * calls);
+        else rs = fail(WQ_ERR_HIP, "wq_tune: graph replay failed");
+      }
+    }
+    (void)hipStreamSynchronize(cs);
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    (void)hipGetLastError();  // a capture that could not be built leaves no sticky error
+    return rs == WQ_ERR_HIP ? rs : WQ_OK;
+  };
   // mean microseconds of candidate c over `iters` calls after `warmup` (negative: the
   // candidate cannot run with this workspace)
   auto time_cand = [&](size_t c, double* us) -> wq_status {
@@ -583,12 +626,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
           gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0)
         return WQ_OK;
     }
-    auto run = [&]() -> wq_status {
-      const wq_weight* w = &copies[rot];
-      rot = (rot + 1) % n_copies;
-      return gemv ? gemv_impl(w, x, M, y, cand[c].split, cand[c].waves, cand[c].rows, ws, ws_bytes, stream)
-                  : gemm_impl(w, x, M, y, cand[c].tile, ws, ws_bytes, stream);
-    };
+    auto run = [&]() -> wq_status { return run_cand(c, hs); };
     wq_status rs;
     for (int i = 0; i < warmup; ++i)
       if ((rs = run()) != WQ_OK) return rs;
@@ -605,8 +643,9 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
   for (size_t c = 0; c < cand.size(); ++c)
     if ((st = time_cand(c, &lat[c])) != WQ_OK) goto out;
   {
-    // Confirmation: the four fastest are timed once more and that second timing
-    // decides (a single pass favours whichever candidate happened to run fast).
+    // Confirmation: the four fastest are timed once more, as HIP graph replays (the way
+    // a decode step replays them), and that second timing decides (a single pass
+    // favours whichever candidate happened to run fast).
     std::vector<size_t> order;
     for (size_t c = 0; c < cand.size(); ++c)
       if (lat[c] >= 0) order.push_back(c);
@@ -614,7 +653,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
     if (order.size() > 4) order.resize(4);
     std::sort(order.begin(), order.end());  // re-time in candidate order
     for (const size_t c : order)
-      if ((st = time_cand(c, &lat[c])) != WQ_OK) goto out;
+      if ((st = time_cand_graph(c, &lat[c])) != WQ_OK) goto out;
   }
   {
     const int best = wq_tune_pick(lat.data(), (int)lat.size());

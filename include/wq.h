@@ -329,8 +329,11 @@ int wq_tune_pick(const double* lat, int n);
  * winner in the tuner cache: for M < 8 every (split_k, waves, rows) triple with
  * split_k in the grid {1,2,4,8,16,32} (those the shape and workspace allow), waves in
  * {1,2,3,4,6,8,12,16} plus the default (capped at wq_gemv_max_waves) and every rows
- * setting; for M >= 8 the GEMM tiles.  The four fastest are then timed a second time
- * and that timing decides among them.  Each candidate runs `warmup` untimed
+ * setting; for M >= 8 the GEMM tiles.  The four fastest are then timed a second time,
+ * as HIP graph replays of two rotations over the copies (at least 8 calls; captured
+ * on a stream the tuner creates and destroys; about `iters` calls timed after 2
+ * warm-up replays), and that timing decides among them (where a graph cannot be built
+ * the first timing stands).  Each candidate runs `warmup` untimed
  * and `iters` timed calls (the page uses 1000 + 1000), rotating over the n_copies
  * weights (distinct buffers with the same format and shape) so that the weights
  * do not stay cached.  x, y and ws are as for wq_linear.  Writes the chosen split_k
