@@ -680,11 +680,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
   dma_w8pc_body<WM, WN, DBM>(qw, scales, x, y, part, M, K, N, tail0, tailS);
 }
 
-// 64-row tiles (capping the registers for two workgroups per CU spills: measured slower)
+// 64- and 128-row tiles (capping the registers for two workgroups per CU spills:
+// measured slower)
+template <int TM>
 __global__ __launch_bounds__(512, 1) void gemm_dma64_w8pc_kernel(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                             const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part,
                             int M, int K, int N, int tail0, int tailS) {
-  dma_w8pc_body<1, 8, 64>(qw, scales, x, y, part, M, K, N, tail0, tailS);
+  dma_w8pc_body<1, 8, TM>(qw, scales, x, y, part, M, K, N, tail0, tailS);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1721,9 +1723,10 @@ int gemm_dma_tail(int64_t M, int64_t N, int* tail0) {
 }
 
 int gemm_dma64_split(int tile, int64_t M, int64_t N) {
-  if (tile < kDma64Tile0 || tile > kDma64TileLast) return 0;
-  const int64_t blocks = ((M + 63) / 64) * ((N + DBN - 1) / DBN);
-  int S = 1 << (tile - kDma64Tile0);
+  const int tm = gemm_dma_rows(tile);
+  if (tm == 0) return 0;
+  const int64_t blocks = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
+  int S = 1 << (tile - (tm == 64 ? kDma64Tile0 : kDma128Tile0));
   while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
   return S;
 }
@@ -1777,16 +1780,20 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   // 10..12: tile 9 with split-K 2, 4, 8 (fp32 partials in the workspace, added in
   // range order by a second kernel; split 1 when the workspace is too small)
   const bool pc = w->fmt == WQ_FMT_W8_PC;
-  if (tile >= kDma64Tile0 && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
-    // 64-row LDS-DMA tiles, split-K 1 / 2 / 4 over gridDim.y
-    const int64_t total = ((M + 63) / 64) * ((N + DBN - 1) / DBN);
+  const int tm = gemm_dma_rows(tile);
+  if (tm != 0 && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
+    // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 over gridDim.y
+    const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
     int S = gemm_dma64_split(tile, M, N);
     if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
     S = std::min(S, K / (DBK * (pc ? 1 : 2)));
     const dim3 grid((unsigned)(8 * ((total + 7) / 8)), (unsigned)S);
     float* part = (float*)ws;
     if (pc) {
-      gemm_dma64_w8pc_kernel<<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
+      if (tm == 64)
+        gemm_dma64_w8pc_kernel<64><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
+      else
+        gemm_dma64_w8pc_kernel<128><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
     } else {
       const size_t xh_off = round256(S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
       uint16_t* xh = nullptr;
@@ -1798,17 +1805,21 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
         WQ_HIP_CHECK(hipGetLastError());
       }
       const int t0 = (int)total;
+#define WQ_G128_ROWS(F, TMV)                                                                                  \
+  do {                                                                                                        \
+    if (xh)                                                                                                   \
+      gemm_dma_g128_kernel<F, 1, 8, true, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1); \
+    else                                                                                                      \
+      gemm_dma_g128_kernel<F, 1, 8, false, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1); \
+  } while (0)
       if (w->fmt == WQ_FMT_W4_G128) {
-        if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 1, 8, true, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1);
-        else
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 1, 8, false, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1);
+        if (tm == 64) WQ_G128_ROWS(WQ_FMT_W4_G128, 64);
+        else WQ_G128_ROWS(WQ_FMT_W4_G128, 128);
       } else {
-        if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 1, 8, true, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1);
-        else
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 1, 8, false, 64><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1);
+        if (tm == 64) WQ_G128_ROWS(WQ_FMT_W8_G128, 64);
+        else WQ_G128_ROWS(WQ_FMT_W8_G128, 128);
       }
+#undef WQ_G128_ROWS
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
@@ -1821,7 +1832,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     }
     return WQ_OK;
   }
-  if (tile >= kDma64Tile0) tile = 1;  // shapes outside the LDS-DMA tiles
+  if (tm != 0) tile = 1;  // shapes outside the LDS-DMA tiles
   const bool dma_tile = tile == 3 || tile == 4 || tile >= 9;
   if (dma_tile && (pc || tile >= 9) && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
     const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);

@@ -107,7 +107,14 @@ constexpr int kDmaTailTile = 13, kDmaTailMaxSplit = 4;
 // (a few tokens: the weights stream as in tile 9 with a quarter of its x traffic and
 // MFMA work) and split-K 1, 2, 4, capped as the split LDS-DMA tiles.
 constexpr int kDma64Tile0 = 14, kDma64TileLast = 16;
-int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of them
+// GEMM tiles kDma128Tile0 .. kDma128TileLast: the same with 128-row x tiles (mid M on
+// narrow N, where 256-row tiles leave most CUs idle), split-K 1, 2, 4.
+constexpr int kDma128Tile0 = 17, kDma128TileLast = 19;
+// rows per x tile of the row-tiled LDS-DMA tiles 14..19 (0 for other tiles)
+inline int gemm_dma_rows(int tile) {
+  return tile >= kDma64Tile0 && tile <= kDma64TileLast ? 64 : tile >= kDma128Tile0 && tile <= kDma128TileLast ? 128 : 0;
+}
+int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of 14..19
 int gemm_dma_tail(int64_t M, int64_t N, int* tail0);
 // Compute units of the current device (kDefaultCUs, MI355X's count, if it cannot be queried).
 constexpr int kDefaultCUs = 256;

@@ -36,8 +36,8 @@ FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2}
 FMT_NAME = {v: k for k, v in FMT.items()}
 CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1
-GEMM_TILES = 16
-TUNE_LAT_SLOTS = 16                      # WQ_TUNE_LAT_SLOTS: entries wq_tune writes to lat_us
+GEMM_TILES = 19
+TUNE_LAT_SLOTS = 19                      # WQ_TUNE_LAT_SLOTS: entries wq_tune writes to lat_us
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)

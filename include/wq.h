@@ -255,12 +255,15 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      waves; group-128 as tile 9), split-K 1, 2, 4 (partials as for 10..12, capped
  *      so that the grid stays within 512 workgroups; 15 and 16 need that workspace,
  *      else WQ_ERR_WORKSPACE); the default for 17..128 tokens; other shapes: tile 1;
+ *   17..19  as 14..16 with 128-row x tiles (mid M on narrow N, where the 256-row
+ *      tiles leave most compute units idle), split-K 1, 2, 4; 18 and 19 need the
+ *      workspace; the default for 129..256 tokens; other shapes: tile 1;
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
  *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 16
+#define WQ_GEMM_TILES 19
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -341,7 +344,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 16
+#define WQ_TUNE_LAT_SLOTS 19
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);
