@@ -92,7 +92,8 @@ def compare(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
 
     Returns max(err/tol), the number of failures and the relative RMS
     ||y - y_ref|| / ||y_ref|| (the statistic the Marlin benchmark page reports
-    for its fixed-input projection check).
+    for its fixed-input projection check).  Over a zero reference that ratio is
+    0 when y is zero as well and +inf otherwise.
     """
     y = _quant.bf16_bits_to_f32(y_bits).astype(np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
@@ -101,8 +102,12 @@ def compare(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
     err = np.abs(y - y_ref)
     tol = TOL_REL * np.maximum(1.0, np.abs(y_ref))
     ratio = err / tol
+    num = float(np.sqrt(np.sum((y - y_ref) ** 2)))
     denom = float(np.sqrt(np.sum(y_ref * y_ref)))
-    rel_rms = float(np.sqrt(np.sum((y - y_ref) ** 2)) / denom) if denom > 0 else float(np.sqrt(np.sum(y * y)))
+    if denom > 0:
+        rel_rms = num / denom
+    else:
+        rel_rms = 0.0 if num == 0 else float("inf")
     return dict(max_ratio=float(ratio.max()) if ratio.size else 0.0,
                 fails=int(np.count_nonzero(ratio > 1.0)),
                 rel_rms=rel_rms, n=int(ratio.size))

@@ -360,6 +360,25 @@ def pin_compare():
     assert st["fails"] == 2, st
 
 
+def pin_compare_rel_rms():
+    """The relative RMS ||y - y_ref||_2 / ||y_ref||_2 (the statistic of the Marlin
+    benchmark page's "Fixed-input projection check") on crafted values: y = (3, 4)
+    against y_ref = (6, 8) is half of a 3-4-5 triangle, so the ratio is 5 / 10 = 1/2
+    exactly, each error is 50 tolerances and both elements fail.  A zero reference
+    gives 0 for a zero result and +inf for any other (a relative error over a zero
+    denominator)."""
+    y = OQ.bf16_rne_bits(np.array([[3.0, 4.0]], dtype=np.float32))
+    st = OL.compare(y, np.array([[6.0, 8.0]]))
+    assert st["rel_rms"] == 0.5 and st["max_ratio"] == 50.0 and st["fails"] == 2, st
+    # a single element: |y - y_ref| / |y_ref| exactly
+    st = OL.compare(OQ.bf16_rne_bits(np.array([[1.5]], dtype=np.float32)), np.array([[-0.5]]))
+    assert st["rel_rms"] == 4.0, st
+    zero = np.zeros((2, 3))
+    assert OL.compare(OQ.bf16_rne_bits(zero.astype(np.float32)), zero)["rel_rms"] == 0.0
+    nz = OQ.bf16_rne_bits(np.array([[0.0, 0.25, 0.0], [0.0, 0.0, 0.0]], dtype=np.float32))
+    assert OL.compare(nz, zero)["rel_rms"] == float("inf")
+
+
 def pin_dispatch():
     """Token count numel/shape[-1]; fewer than 8 tokens -> GEMV."""
     assert OL.token_count((7, 5120)) == 7 and OL.token_count((2, 3, 64)) == 6
@@ -389,6 +408,22 @@ def pin_topk_golden():
     for k, T, u, tok in blocks["draws"]:
         idx, kb = OT.topk_row(bits, int(k))
         assert OT.sample_row(kb, idx, float(T), float(u)) == int(tok), (k, T, u, tok)
+
+
+def pin_topk_rows():
+    """Several rows in one call (tests/golden/topk_rows_worked.txt): each row keeps
+    its own k best and draws with its own u -- row 1 is row 0 reversed and row 2 row
+    0 rotated, so a draw that reused one row's u or one row's kept set for another
+    lands on a different token."""
+    head, blocks = read_fixture("topk_rows_worked.txt")
+    L = np.array([[num(t) for t in row] for row in blocks["logits"]], dtype=np.uint16)
+    k, T = int(head["k"][0]), float(head["T"][0])
+    u = np.array([float(t) for t in head["u"]])
+    idx, bits, tok = OT.ref_topk_sample(L, k, T, u)
+    want_idx = np.array([[int(t) for t in row] for row in blocks["kept"]])
+    assert np.array_equal(idx, want_idx), idx
+    assert np.array_equal(bits, np.take_along_axis(L, want_idx, axis=1))
+    assert tok.tolist() == [int(t) for t in head["tokens"]], tok
 
 
 def pin_topk_defining_property(seed=31, V=48):
@@ -491,7 +526,8 @@ ALL_PINS = [
     lambda: pin_one_hot_random("w4g128"), pin_identity,
     lambda: pin_bruteforce("w8pc", 48), lambda: pin_bruteforce("w8g128", 128),
     lambda: pin_bruteforce("w4g128", 128), pin_library_factorisation, pin_invariants,
-    pin_compare, pin_dispatch, pin_topk_golden, pin_topk_defining_property,
+    pin_compare, pin_compare_rel_rms, pin_dispatch, pin_topk_golden, pin_topk_rows,
+    pin_topk_defining_property,
     pin_topk_sampling_closed_forms, pin_activation_permutation,
 ]
 

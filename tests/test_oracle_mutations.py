@@ -180,12 +180,71 @@ def _mut_perm_out_of_range_wraps(mp):
     mp.setattr(OL, "gather_activations", lambda x_bits, perm: orig(x_bits, np.asarray(perm) % np.asarray(x_bits).shape[-1]))
 
 
+def _mut_rel_rms_over_result(mp):
+    orig = OL.compare
+
+    def bad(y_bits, y_ref):                             # divides by ||y|| instead of ||y_ref||
+        st = orig(y_bits, y_ref)
+        y = OQ.bf16_bits_to_f32(y_bits).astype(np.float64)
+        d = float(np.sqrt(np.sum(y * y)))
+        st["rel_rms"] = float(np.sqrt(np.sum((y - y_ref) ** 2))) / d if d > 0 else 0.0
+        return st
+    mp.setattr(OL, "compare", bad)
+
+
+def _mut_rel_rms_zero_reference_absolute(mp):
+    orig = OL.compare
+
+    def bad(y_bits, y_ref):                             # absolute RMS when the reference is 0
+        st = orig(y_bits, y_ref)
+        if not np.any(y_ref):
+            y = OQ.bf16_bits_to_f32(y_bits).astype(np.float64)
+            st["rel_rms"] = float(np.sqrt(np.mean(y * y)))
+        return st
+    mp.setattr(OL, "compare", bad)
+
+
+def _mut_topk_rows_first_u(mp):
+    orig = OT.sample_row
+    first = []
+
+    def bad(kept_bits, kept_idx, temperature, u):       # every row draws with row 0's u
+        if not first:
+            first.append(u)
+        return orig(kept_bits, kept_idx, temperature, first[0])
+    orig_ref = OT.ref_topk_sample
+
+    def ref(logit_bits, k, temperature, u):
+        first.clear()
+        return orig_ref(logit_bits, k, temperature, u)
+    mp.setattr(OT, "sample_row", bad)
+    mp.setattr(OT, "ref_topk_sample", ref)
+
+
+def _mut_topk_rows_shifted(mp):
+    def bad(logit_bits, k, temperature, u):             # row m draws from row m-1's kept set
+        L = np.asarray(logit_bits, dtype=np.uint16)
+        M = L.shape[0]
+        u = np.asarray(u, dtype=np.float64).ravel()
+        idx = np.zeros((M, k), dtype=np.int64)
+        bits = np.zeros((M, k), dtype=np.uint16)
+        tok = np.zeros(M, dtype=np.int64)
+        for m in range(M):
+            idx[m], bits[m] = OT.topk_row(L[m], k)
+        for m in range(M):
+            j = (m - 1) % M
+            tok[m] = OT.sample_row(bits[j], idx[j], temperature, float(u[m]))
+        return idx, bits, tok
+    mp.setattr(OT, "ref_topk_sample", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
              _mut_topk_ascending, _mut_topk_nan_first, _mut_topk_signed_zero,
              _mut_sample_temperature_multiplies, _mut_sample_at_or_above, _mut_perm_inverse,
-             _mut_perm_out_of_range_wraps]
+             _mut_perm_out_of_range_wraps, _mut_rel_rms_over_result,
+             _mut_rel_rms_zero_reference_absolute, _mut_topk_rows_first_u, _mut_topk_rows_shifted]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
