@@ -537,6 +537,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replays", type=int, default=7, help="timed graph replays of the headline (median)")
     ap.add_argument("--quick", action="store_true", help="headline only (no per-workload detail)")
+    ap.add_argument("--detail", default="", help="comma list of detail groups to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune-iters", type=int, default=1000)
     ap.add_argument("--profile-pass", action="store_true",
@@ -779,22 +780,29 @@ def run_detail(wq, torch, args) -> dict:
         torch.cuda.empty_cache()
         return rec
 
-    out["decode_w8pc_msweep"] = {f"{K}x{N}_M{M}": measure(2, "w8pc", K, N, M)
-                                 for K, N in DECODE_SHAPES for M in (2, 4, 7)}
-    out["decode_w4g128"] = {f"{K}x{N}_M{M}": measure(3, "w4g128", K, N, M)
-                            for K, N in [(5120, 27648), (13824, 5120)] for M in (1, 4)}
-    out["splitk_stress"] = {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
-                            for K, N in [(27648, 5120), (5120, 151936)]
-                            for fmt in ("w8pc", "w8g128", "w4g128")}
-    out["prefill_gemm"] = {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
-                           for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
-                           for M in (8, 64, 512, 2048)}
-    out["lm_head_topk"] = {f"{fmt}_{K}x{N}_M{M}": measure_lm_head_topk(wq, torch, 4, fmt, K, N, M)
-                           for fmt in ("w8g128", "w4g128") for K, N in [(5120, 151936)] for M in (1, 4)}
-    out["activation_permutation"] = {f"{fmt}_{K}x{N}_M{M}": measure_linear_perm(wq, torch, cfg, fmt, K, N, M)
-                                     for cfg, fmt, M in ((3, "w4g128", 1), (1, "w8pc", 1), (5, "w8pc", 2048))
-                                     for K, N in [(5120, 27648)]}
-    out["reference_bf16_gemm"] = reference_bf16_gemm(torch)
+    groups = {
+        "decode_w8pc_msweep": lambda: {f"{K}x{N}_M{M}": measure(2, "w8pc", K, N, M)
+                                       for K, N in DECODE_SHAPES for M in (2, 4, 7)},
+        "decode_w4g128": lambda: {f"{K}x{N}_M{M}": measure(3, "w4g128", K, N, M)
+                                  for K, N in [(5120, 27648), (13824, 5120)] for M in (1, 4)},
+        "splitk_stress": lambda: {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
+                                  for K, N in [(27648, 5120), (5120, 151936)]
+                                  for fmt in ("w8pc", "w8g128", "w4g128")},
+        "prefill_gemm": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
+                                 for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
+                                 for M in (8, 64, 512, 2048)},
+        "lm_head_topk": lambda: {f"{fmt}_{K}x{N}_M{M}": measure_lm_head_topk(wq, torch, 4, fmt, K, N, M)
+                                 for fmt in ("w8g128", "w4g128") for K, N in [(5120, 151936)] for M in (1, 4)},
+        "activation_permutation": lambda: {f"{fmt}_{K}x{N}_M{M}": measure_linear_perm(wq, torch, cfg, fmt, K, N, M)
+                                           for cfg, fmt, M in ((3, "w4g128", 1), (1, "w8pc", 1), (5, "w8pc", 2048))
+                                           for K, N in [(5120, 27648)]},
+        "reference_bf16_gemm": lambda: reference_bf16_gemm(torch),
+    }
+    want = list(groups) if not args.detail else args.detail.split(",")
+    for name in want:
+        if name not in groups:
+            raise SystemExit(f"unknown detail group {name!r}; choose from {', '.join(groups)}")
+        out[name] = groups[name]()
     return out
 
 

@@ -19,24 +19,20 @@
 //
 // In-register dequantisation, exact products with fp32 accumulation:
 //   * int8 (gfx950 layout stores u = q + 128): v_perm_b32 places two code bytes
-//     under the fp16 exponent byte 0x64, giving the fp16 pair (1024 + u_a,
-//     1024 + u_b) exactly in one instruction; x is converted to fp16 (exact for
-//     every bf16 value of magnitude 2^-17 .. 65280; smaller magnitudes round to
-//     the fp16 subnormal grid, an absolute change below 2^-25); v_dot2_f32_f16
-//     multiplies, and (1024 + 128) * sum(x) removes the offset.
+//     under the fp16 exponent byte 0x64, giving the fp16 pair (1024 + u_a, 1024 +
+//     u_b) exactly in one instruction, and one packed fp16 add of -1152 leaves the
+//     exact codes (q_a, q_b); x is converted to fp16; v_dot2_f32_f16 multiplies.
 //   * uint4 (nibbles interleaved by the gfx950 repack, pair i = (q_2i, q_2i+1) at
-//     bits 4i and 16 + 4i): word & 0x000F000F | 0x43004300 is the bf16 pair
-//     (128 + q_0, 128 + q_1) exactly, word & 0x00F000F0 | 0x54005400 the fp16 pair
-//     (64 + q_2, 64 + q_3) (the nibbles sit on the fp16 units place), and the same
-//     on word >> 8 for pairs 2 and 3; v_dot2_f32_bf16 with bf16 x and v_dot2_f32_f16
-//     with fp16 x, and (128 + z) * sum(x) resp. (64 + z) * sum(x) over each kind of
-//     pair per 32-element chunk removes offset and zero-point before the group scale.
-//   * Removing an offset cancels: the fp32 partials carry terms up to
-//     (1152 / |q|) resp. (143 / |q - z|) times larger than the product itself, and
-//     their rounding grows with |x|.  A slice in which some |x| >= 512 therefore
-//     takes the exact path (codes -> exact bf16 q or q - z, v_dot2_f32_bf16), which
-//     also covers magnitudes beyond fp16.  Below 512 the worst case of the offset
-//     paths stays under a third of the tolerance.
+//     bits 4i and 16 + 4i): word & 0x000F000F | 0x64006400 is the fp16 pair (1024 +
+//     q_0, 1024 + q_1), word & 0x00F000F0 | 0x54005400 the fp16 pair (64 + q_2, 64 +
+//     q_3) (the nibbles sit on the fp16 units place), and the same on word >> 8 for
+//     pairs 2 and 3; one packed fp16 add of -(1024 + z) resp. -(64 + z) leaves the
+//     exact q - z; v_dot2_f32_f16 against fp16 x.
+//   * Both are exact: every product x q (or x (q - z)) is exact in fp32, so each
+//     output carries only the rounding of an fp32 sum and the final bf16 rounding --
+//     provided x converts to fp16 exactly, which holds for 0 and 2^-17 <= |x| <=
+//     65280.  A slice with any other x takes the bf16 path (codes -> exact bf16 q or
+//     q - z, v_dot2_f32_bf16 against bf16 x).
 //   * Scales multiply fp32 partial sums (per row at the end for per-channel W8,
 //     per chunk for group-128), so codes are never rounded.
 //
@@ -79,6 +75,36 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
   auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
   return __builtin_bit_cast(uint32_t, h);
 }
+
+// fp16 pair + fp16 pair (v_pk_add_f16); exact whenever both sums are representable,
+// as for (offset + code) + (-offset).
+__device__ __forceinline__ uint32_t add_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) + __builtin_bit_cast(f16x2_t, b));
+}
+constexpr uint32_t kF16Minus1152 = 0xE480E480u;  // fp16 pair (-1152, -1152)
+// fp16 pair (-v, -v) of a small integer v (exact: v < 2048)
+__device__ __forceinline__ uint32_t f16x2_splat_neg(uint32_t v) {
+  const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-(float)v));
+  return h | (h << 16);
+}
+
+// Whether every bf16 value added converts to fp16 exactly: 0, or 2^-17 <= |x| <= 65280
+// (a bf16 value has 8 significant bits; fp16 holds them from its subnormal grid 2^-24
+// up to its largest finite value, and the next bf16 value after 65280 is 65536).  With
+// the sign cleared a bf16 bit pattern orders like its magnitude (Inf and NaN above
+// every number): a packed 16-bit running maximum, and a running minimum of the pattern
+// minus one (0 wraps to 0xFFFF, so zeros never count as small).
+struct F16Exact {
+  u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  __device__ __forceinline__ void add(uint32_t w) {
+    const u16x2_t a = __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, a);
+    mn = __builtin_elementwise_min(mn, a - u16x2_t{1, 1});
+  }
+  __device__ __forceinline__ bool ok() const {
+    return mx.x <= 0x477F && mx.y <= 0x477F && mn.x >= 0x36FF && mn.y >= 0x36FF;
+  }
+};
 
 // Cross-lane exchange partners.  xor 1 and 2 by DPP quad permutes, xor 4, 8 and 16
 // by ds_swizzle (bit-mask mode), xor 32 by ds_bpermute.
@@ -176,9 +202,6 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
   for (int r = 0; r < RR; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-  float xs_total[M];  // W8: sum of x over this lane's chunks (offset removal)
-#pragma unroll
-  for (int m = 0; m < M; ++m) xs_total[m] = 0.f;
 
   // Full slices of a full tile (every row a whole 1 KB, no row past N) take the fast
   // form: wave-uniform slice base + a 32-bit lane offset + r KB, so the loads need no
@@ -188,11 +211,11 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
   const int t_full = nr == R ? (int)(row_bytes / kSliceBytes) : 0;  // slices with whole 1 KB rows
   const uint32_t rlane = (uint32_t)(sub * RR) * kSliceBytes + lane * 16;
   const uint32_t xlane = (uint32_t)lane * F::kChunk * 2;  // byte offset of this lane's x chunk in a slice
-  // The uint4 nibble masks and the bf16 128.0 / fp16 64.0 pairs live in registers the
+  // The uint4 nibble masks and the fp16 1024.0 / 64.0 pairs live in registers the
   // compiler cannot see through, so each code pair is one v_and_or_b32 rather than a
   // separate and/or with two literal operands.
-  uint32_t nib_mask = 0x000F000Fu, bf16_128 = 0x43004300u, nib_mask_hi = 0x00F000F0u, f16_64 = 0x54005400u;
-  if constexpr (kW4) asm volatile("" : "+v"(nib_mask), "+v"(bf16_128), "+v"(nib_mask_hi), "+v"(f16_64));
+  uint32_t nib_mask = 0x000F000Fu, f16_1024 = 0x64006400u, nib_mask_hi = 0x00F000F0u, f16_64 = 0x54005400u;
+  if constexpr (kW4) asm volatile("" : "+v"(nib_mask), "+v"(f16_1024), "+v"(nib_mask_hi), "+v"(f16_64));
 
   // The arithmetic of one slice, given its codes (RR rows) and x chunk.
   auto slice_math = [&](const uint4* cw, const uint32_t (*xb)[F::kXWords], int kk) {
@@ -231,41 +254,32 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     };
     auto zero_of = [&](int r) -> uint32_t { return ((r < 8 ? zw : zw_hi) >> (4 * (r & 7))) & 0xFu; };
 
-    // any |x| >= 512 in this slice?  With the sign cleared, a bf16 bit pattern orders
-    // like its magnitude, and 512 is 0x4400 (Inf and NaN lie above): a packed 16-bit
-    // running maximum over the slice's x words, then one comparison per half.
-    u16x2_t mx = {0, 0};
+    // Does every x of the slice convert to fp16 exactly (see F16Exact)?  Otherwise the
+    // whole wave takes the bf16 path for this slice.
+    F16Exact fx;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int i = 0; i < F::kXWords; ++i)
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xb[m][i] & 0x7FFF7FFFu));
-    const bool big = mx.x >= 0x4400 || mx.y >= 0x4400;
-    const bool exact_path = __builtin_amdgcn_ballot_w64(big) != 0;
+      for (int i = 0; i < F::kXWords; ++i) fx.add(xb[m][i]);
+    const bool exact_path = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
 
     if constexpr (!kW4) {
-      // ---- int8
+      // ---- int8: fp16 (1024 + u) by v_perm_b32, minus 1152 by one packed fp16 add: the
+      // exact code q, against fp16 x
       if (!exact_path) {
         uint32_t xh[M][8];
-        float xs[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float t = 0.f;
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
-            t = dot2_f16(xh[m][i], 0x3C003C00u, t);  // x . (1, 1)
-          }
-          xs[m] = t;
-        }
+          for (int i = 0; i < 8; ++i) xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
           const uint32_t d[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
           uint32_t hp[8];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            hp[2 * j] = __builtin_amdgcn_perm(0x64646464u, d[j], 0x04010400u);
-            hp[2 * j + 1] = __builtin_amdgcn_perm(0x64646464u, d[j], 0x04030402u);
+            hp[2 * j] = add_f16x2(__builtin_amdgcn_perm(0x64646464u, d[j], 0x04010400u), kF16Minus1152);
+            hp[2 * j + 1] = add_f16x2(__builtin_amdgcn_perm(0x64646464u, d[j], 0x04030402u), kF16Minus1152);
           }
           if constexpr (FMT == WQ_FMT_W8_PC) {
 #pragma unroll
@@ -279,16 +293,12 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
               float t = 0.f;
 #pragma unroll
               for (int i = 0; i < 8; ++i) t = dot2_f16(hp[i], xh[m][i], t);
-              acc[r][m] = fmaf(sc, fmaf(-1152.f, xs[m], t), acc[r][m]);
+              acc[r][m] = fmaf(sc, t, acc[r][m]);
             }
           }
         }
-        if constexpr (FMT == WQ_FMT_W8_PC) {
-#pragma unroll
-          for (int m = 0; m < M; ++m) xs_total[m] += xs[m];
-        }
       } else {
-        // exact bf16 path: signed code -> fp32 -> bf16 pairs
+        // bf16 path: signed code -> fp32 -> bf16 pairs, against bf16 x
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
           const uint32_t d[4] = {cw[r].x ^ 0x80808080u, cw[r].y ^ 0x80808080u, cw[r].z ^ 0x80808080u,
@@ -310,33 +320,21 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
         }
       }
     } else if (!exact_path) {
-      // ---- uint4 group-128, offset path.  Of each word's four nibble pairs, those at bits
-      // (0, 16) and, after one shift by 8, (8, 24) go under the bf16 128.0 pattern (bf16
-      // 128 + q, against bf16 x); those at (4, 20) and (12, 28) under the fp16 64.0
-      // pattern, which gives fp16 64 + q with no shift (against x converted to fp16).
-      // Both feed one fp32 sum per token, from which (128 + z) X_lo + (64 + z) X_hi is
-      // removed (X: the sums of x over the two kinds of positions).
-      uint32_t xh[M][8];  // fp16 x of the pairs at the (4, 20) and (12, 28) positions
-      float xs_lo[M], xs_hi[M];
+      // ---- uint4 group-128.  Of each word's four nibble pairs, those at bits (0, 16) and,
+      // after one shift by 8, (8, 24) go under the fp16 1024.0 pattern (1024 + q), those
+      // at (4, 20) and (12, 28) under the fp16 64.0 pattern (64 + q: the nibble sits on
+      // the units place); one packed fp16 add of -(1024 + z) resp. -(64 + z) leaves the
+      // exact q - z, against fp16 x.
+      uint32_t xh[M][16];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float tl = 0.f, th = 0.f;
+      for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          xh[m][2 * wi] = bf16x2_to_f16x2(xb[m][4 * wi + 1]);
-          xh[m][2 * wi + 1] = bf16x2_to_f16x2(xb[m][4 * wi + 3]);
-          tl = dot2_bf16(xb[m][4 * wi], 0x3F803F80u, tl);  // x . (1, 1)
-          tl = dot2_bf16(xb[m][4 * wi + 2], 0x3F803F80u, tl);
-          th = dot2_f16(xh[m][2 * wi], 0x3C003C00u, th);
-          th = dot2_f16(xh[m][2 * wi + 1], 0x3C003C00u, th);
-        }
-        xs_lo[m] = tl;
-        xs_hi[m] = th;
-      }
+        for (int i = 0; i < 16; ++i) xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
 #pragma unroll
       for (int r = 0; r < RR; ++r) {
         const float sc = f16_to_f32(scale_of(r));
-        const float z = (float)zero_of(r);
+        const uint32_t z = zero_of(r);
+        const uint32_t off_a = f16x2_splat_neg(1024u + z), off_b = f16x2_splat_neg(64u + z);
         const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
         float t[M];
 #pragma unroll
@@ -344,19 +342,20 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
           const uint32_t w = words[wi], w8 = w >> 8;
-          const uint32_t p0 = (w & nib_mask) | bf16_128, p1 = (w & nib_mask_hi) | f16_64;
-          const uint32_t p2 = (w8 & nib_mask) | bf16_128, p3 = (w8 & nib_mask_hi) | f16_64;
+          const uint32_t p0 = add_f16x2((w & nib_mask) | f16_1024, off_a);
+          const uint32_t p1 = add_f16x2((w & nib_mask_hi) | f16_64, off_b);
+          const uint32_t p2 = add_f16x2((w8 & nib_mask) | f16_1024, off_a);
+          const uint32_t p3 = add_f16x2((w8 & nib_mask_hi) | f16_64, off_b);
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            t[m] = dot2_bf16(p0, xb[m][4 * wi], t[m]);
-            t[m] = dot2_f16(p1, xh[m][2 * wi], t[m]);
-            t[m] = dot2_bf16(p2, xb[m][4 * wi + 2], t[m]);
-            t[m] = dot2_f16(p3, xh[m][2 * wi + 1], t[m]);
+            t[m] = dot2_f16(p0, xh[m][4 * wi], t[m]);
+            t[m] = dot2_f16(p1, xh[m][4 * wi + 1], t[m]);
+            t[m] = dot2_f16(p2, xh[m][4 * wi + 2], t[m]);
+            t[m] = dot2_f16(p3, xh[m][4 * wi + 3], t[m]);
           }
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-          acc[r][m] = fmaf(sc, fmaf(-(128.f + z), xs_lo[m], fmaf(-(64.f + z), xs_hi[m], t[m])), acc[r][m]);
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, t[m], acc[r][m]);
       }
     } else {
       // ---- uint4 group-128, exact path: bf16(q - z) pairs
@@ -465,13 +464,6 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     }
     slice_math(cw, xb, kk);
   }
-  if constexpr (FMT == WQ_FMT_W8_PC) {
-#pragma unroll
-    for (int r = 0; r < RR; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(-1152.f, xs_total[m], acc[r][m]);
-  }
-
   // ---- wave reduce-scatter: afterwards lane l holds row (l % RR), all M tokens
   rs_level<1, RR, M>(acc, lane & 1);
   if constexpr (RR >= 4) rs_level<2, RR / 2, M>(acc, lane & 2);
@@ -548,19 +540,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // / 16)) -- and x at the same k; instruction s (0..3) of a unit contracts k = 32 (l /
 // 16) + 8 s + 0..7 in A and B alike.
 //
-// Codes become exact small numbers: int8 (stored u = q + 128) by v_perm_b32 under the
-// fp16 exponent byte 0x64 (fp16 1024 + u, as in the dot2 path) against x converted
-// to fp16; uint4 in one v_and_or_b32 per pair: the pairs at bits (0, 16) and, after a
-// shift by 8, (8, 24) under the bf16 128.0 pattern give bf16 (128 + q) against bf16
-// x, the pairs at bits (4, 20) and (12, 28) under the fp16 64.0 pattern give fp16 (64
-// + q) (their low nibble bits stay clear) against fp16 x.  The offsets leave the
-// products as sums of x times constants, taken out with matrix products of the same A
-// against constant B: int8 per-channel accumulates x sums over all of K and removes
-// 1152 sum(x) at the end; group-128 starts each group's accumulator at -(offset + z)
-// times the group's x sums, scales it by the group scale and adds it up.  The
-// offsets equal those of the dot2 path, so the same |x| < 512 condition bounds the
-// cancellation; a unit whose x has some |x| >= 512 takes exact bf16 codes (q or q - z)
-// against bf16 x.  A ragged last unit (int8 with K % 128 != 0) masks the lanes past K.
+// Codes become exact fp16 values as in the dot2 path: int8 (stored u = q + 128) by
+// v_perm_b32 under the fp16 exponent byte 0x64 (1024 + u) and one packed fp16 add of
+// -1152; uint4 pairs at bits (0, 16) and, after a shift by 8, (8, 24) under the fp16
+// 1024.0 pattern, pairs at (4, 20) and (12, 28) under the fp16 64.0 pattern, then one
+// packed fp16 add of -(1024 + z) resp. -(64 + z): the exact q - z.  x is converted to
+// fp16, so every product is exact and accumulates in fp32; a unit with an x that
+// does not convert to fp16 exactly (see F16Exact) takes exact bf16 codes (q or q - z)
+// against bf16 x.  Group-128 scales each group's partial and adds it up.  A ragged
+// last unit (int8 with K % 128 != 0) masks the lanes past K.
 constexpr int kMmaMaxWaves = 8;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -622,15 +610,12 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
   const uint8_t* xb8 = reinterpret_cast<const uint8_t*>(x);
   const uint32_t xrow = min(ln, (uint32_t)M - 1u) * (uint32_t)K * 2u;  // byte offset of this lane's token
   const uint32_t zshift = 4 * (ln & 1);
-  uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_b = 0x43004300u, mag_h = 0x54005400u;
-  if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_b), "+v"(mag_h));
-  const u32x4_t one_b = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const u32x4_t one_h = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_a = 0x64006400u, mag_h = 0x54005400u;
+  if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_a), "+v"(mag_h));
 
-  f32x4_t acc[NB];  // group-128: scaled sums; per-channel: raw sums incl. offsets
+  f32x4_t acc[NB];  // group-128: scaled sums; per-channel: raw sums of x q
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t xs_all = {0.f, 0.f, 0.f, 0.f};  // per-channel: x sums of the offset units
 
   // One unit's operands (32-bit fields only, so that the set stays in registers).
   struct Set {
@@ -683,16 +668,16 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
   };
   auto compute = [&](const Set& st) {
     const uint4 xv[4] = {st.xv[0], st.xv[1], st.xv[2], st.xv[3]};
-    // any |x| >= 512 among the unit's x (see the dot2 path)
-    u16x2_t mx = {0, 0};
+    // does every x of the unit convert to fp16 exactly (see the dot2 path)?
+    F16Exact fx;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xv[j].x & 0x7FFF7FFFu));
-      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xv[j].y & 0x7FFF7FFFu));
-      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xv[j].z & 0x7FFF7FFFu));
-      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, xv[j].w & 0x7FFF7FFFu));
+      fx.add(xv[j].x);
+      fx.add(xv[j].y);
+      fx.add(xv[j].z);
+      fx.add(xv[j].w);
     }
-    const bool exact = __builtin_amdgcn_ballot_w64(mx.x >= 0x4400 || mx.y >= 0x4400) != 0;
+    const bool exact = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
     // group-128: the unit's contribution d[t] to each tile, times the group scale
     auto fold1 = [&](int t, const f32x4_t& d) {
       const float sc = kW4 ? f16_to_f32((uint16_t)st.sv[t]) : bf16_to_f32((uint16_t)st.sv[t]);
@@ -705,49 +690,41 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     };
     if (!exact) {
       if constexpr (kW4) {
-        const u32x4_t a_lo0 = {xv[0].x, xv[0].z, xv[1].x, xv[1].z};
-        const u32x4_t a_lo1 = {xv[2].x, xv[2].z, xv[3].x, xv[3].z};
+        const u32x4_t a_lo0 = {bf16x2_to_f16x2(xv[0].x), bf16x2_to_f16x2(xv[0].z), bf16x2_to_f16x2(xv[1].x),
+                               bf16x2_to_f16x2(xv[1].z)};
+        const u32x4_t a_lo1 = {bf16x2_to_f16x2(xv[2].x), bf16x2_to_f16x2(xv[2].z), bf16x2_to_f16x2(xv[3].x),
+                               bf16x2_to_f16x2(xv[3].z)};
         const u32x4_t a_hi0 = {bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
                                bf16x2_to_f16x2(xv[1].w)};
         const u32x4_t a_hi1 = {bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
                                bf16x2_to_f16x2(xv[3].w)};
-        // group sums of x over the bf16 and the fp16 halves (every column alike)
-        f32x4_t xs_lo = {0.f, 0.f, 0.f, 0.f}, xs_hi = {0.f, 0.f, 0.f, 0.f};
-        xs_lo = mma_bf16(a_lo0, one_b, xs_lo);
-        xs_hi = mma_f16(a_hi0, one_h, xs_hi);
-        xs_lo = mma_bf16(a_lo1, one_b, xs_lo);
-        xs_hi = mma_f16(a_hi1, one_h, xs_hi);
-        u32x4_t b[4][NB];  // the four B operands of each tile
+        u32x4_t b[4][NB];  // the four B operands of each tile: exact fp16 q - z
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
+          const uint32_t z = (st.zb[t] >> zshift) & 15u;
+          const uint32_t off_a = f16x2_splat_neg(1024u + z), off_b = f16x2_splat_neg(64u + z);
           uint32_t lo[4], lo8[4], hi[4], hi8[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t w = st.c[t][0][q], w8 = w >> 8;
-            lo[q] = (w & m_lo) | mag_b;
-            hi[q] = (w & m_hi) | mag_h;
-            lo8[q] = (w8 & m_lo) | mag_b;
-            hi8[q] = (w8 & m_hi) | mag_h;
+            lo[q] = add_f16x2((w & m_lo) | mag_a, off_a);
+            hi[q] = add_f16x2((w & m_hi) | mag_h, off_b);
+            lo8[q] = add_f16x2((w8 & m_lo) | mag_a, off_a);
+            hi8[q] = add_f16x2((w8 & m_hi) | mag_h, off_b);
           }
           b[0][t] = u32x4_t{lo[0], lo8[0], lo[1], lo8[1]};
           b[1][t] = u32x4_t{lo[2], lo8[2], lo[3], lo8[3]};
           b[2][t] = u32x4_t{hi[0], hi8[0], hi[1], hi8[1]};
           b[3][t] = u32x4_t{hi[2], hi8[2], hi[3], hi8[3]};
         }
-        // each tile's accumulator starts at -(128 + z) X_lo - (64 + z) X_hi
         f32x4_t d[NB];
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const float z = (float)((st.zb[t] >> zshift) & 15u);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            d[t][i] = i < MI ? fmaf(-(128.f + z), xs_lo[i], -(64.f + z) * xs_hi[i]) : 0.f;
-        }
+        for (int t = 0; t < NB; ++t) d[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         // the four products, tiles interleaved so that no instruction waits for the previous
 #pragma unroll
-        for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo0, b[0][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_lo0, b[0][t], d[t]);
 #pragma unroll
-        for (int t = 0; t < NB; ++t) d[t] = mma_bf16(a_lo1, b[1][t], d[t]);
+        for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_lo1, b[1][t], d[t]);
 #pragma unroll
         for (int t = 0; t < NB; ++t) d[t] = mma_f16(a_hi0, b[2][t], d[t]);
 #pragma unroll
@@ -759,27 +736,20 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
         for (int j = 0; j < 4; ++j)
           a[j] = u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
                          bf16x2_to_f16x2(xv[j].w)};
-        f32x4_t xs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xs = mma_f16(a[j], one_h, xs);
         f32x4_t d[NB];
         if constexpr (kGrouped) {
 #pragma unroll
-          for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) d[t][i] = i < MI ? -1152.f * xs[i] : 0.f;
-        } else {
-          xs_all += xs;
+          for (int t = 0; t < NB; ++t) d[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int t = 0; t < NB; ++t) {
             const uint32_t w0 = st.c[t][j >> 1][2 * (j & 1)], w1 = st.c[t][j >> 1][2 * (j & 1) + 1];
-            const u32x4_t b = {__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u),
-                               __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u),
-                               __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u),
-                               __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)};
+            const u32x4_t b = {add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), kF16Minus1152)};
             if constexpr (kGrouped) d[t] = mma_f16(a[j], b, d[t]);
             else acc[t] = mma_f16(a[j], b, acc[t]);
           }
@@ -829,13 +799,6 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     load(st, u);
     compute(st);
   }
-  if constexpr (!kGrouped) {
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-      for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(-1152.f, xs_all[i], acc[t][i]);
-  }
-
   // the waves' partial sums meet in LDS and are added in wave order
 #pragma unroll
   for (int t = 0; t < NB; ++t)

@@ -345,19 +345,19 @@ def test_zero_and_power_of_two_scaling(wq, fmt):
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_gemv_with_large_and_tiny_activations(wq, fmt):
-    """Slices holding some |x| >= 512 take the exact code path of the GEMV (beyond
-    fp16 too); values just below the switch, at the fp16 limit and in the fp16
-    subnormal range stay well within tolerance."""
+    """Slices holding an x that fp16 cannot hold exactly (|x| > 65280, or 0 < |x| <
+    2^-17) take the bf16 path of the GEMV; values at the edges of the fp16-exact range
+    stay on the fp16 path.  Every case within tolerance of the oracle."""
     K, N = 8192, 264
     W = synth.weight(104, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
     P = OQ.pack(fmt, W)
     xf = OQ.bf16_bits_to_f32(synth.activation(104, K, 4)).copy()
-    xf[0, 17] = 3.0e5           # exact path, beyond fp16
-    xf[1, 2100] = -65280.0      # exact path, largest bf16 magnitude fp16 holds
-    xf[2, 3000] = 1.0e-6        # fp16 subnormal range (int8 offset path)
-    xf[2, 3001] = -3.0e-8
-    xf[3, 4100] = 510.0         # just below the switch: offset path
+    xf[0, 17] = 3.0e5           # bf16 path, beyond fp16
+    xf[1, 2100] = -65280.0      # fp16 path: the largest bf16 magnitude fp16 holds
+    xf[2, 3000] = 2.0 ** -17    # fp16 path: the smallest magnitude fp16 holds exactly
+    xf[2, 3001] = -3.0e-8       # bf16 path: below 2^-17
+    xf[3, 4100] = 510.0
     xf[3, 6000] = -500.0
     x = OQ.bf16_rne_bits(xf.astype(np.float32))
     y_ref = OL.ref_linear(x, P)
