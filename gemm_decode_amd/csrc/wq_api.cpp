@@ -160,21 +160,22 @@ int default_tile(const wq_weight* w, int64_t M) {
       ++t;
     return t;
   }
-  // fewer 256 x 256 tiles than half the CUs: the smallest split-K that gives at least
-  // that many workgroups (measured on MI355X: at M = 512, N = 5120 split 4 beats 8, and
-  // 160 tiles run best unsplit)
-  const int64_t blocks = ((M + 255) / 256) * ((w->N + 255) / 256);
+  // fewer tiles (256 x 256 for per-channel W8, 128 x 256 for group-128) than half the
+  // CUs: the smallest split-K that gives at least that many workgroups (measured on
+  // MI355X: at M = 512, N = 5120 split 4 beats 8, and 160 tiles run best unsplit)
+  const int64_t tm = gemm_big_dma_rows(w->fmt);
+  const int64_t blocks = ((M + tm - 1) / tm) * ((w->N + 255) / 256);
   if (blocks >= 128) {
     // a partial last round of tiles that would leave at least half the CUs idle: tile 13
     // spreads it over K (it needs a workspace; without one it runs as tile 9)
     int tail0 = 0;
-    return gemm_dma_tail(M, w->N, &tail0) > 1 ? kDmaTailTile : kDefaultTile;
+    return gemm_dma_tail(w->fmt, M, w->N, &tail0) > 1 ? kDmaTailTile : kDefaultTile;
   }
   int t = kDmaSplitTile0;
-  while (t < kDmaSplitTileLast && blocks * gemm_dma_split(t, M, w->N) < 128 &&
-         gemm_dma_split(t + 1, M, w->N) > gemm_dma_split(t, M, w->N))
+  while (t < kDmaSplitTileLast && blocks * gemm_dma_split(w->fmt, t, M, w->N) < 128 &&
+         gemm_dma_split(w->fmt, t + 1, M, w->N) > gemm_dma_split(w->fmt, t, M, w->N))
     ++t;
-  return gemm_dma_split(t, M, w->N) > 1 ? t : kDefaultTile;
+  return gemm_dma_split(w->fmt, t, M, w->N) > 1 ? t : kDefaultTile;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {
@@ -222,9 +223,9 @@ wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int t
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
   const int t = tile == 0 ? resolve_tile(w, M) : tile;
-  if (tile != 0 && gemm_workspace_bytes(w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->N, M, t)))
+  if (tile != 0 && gemm_workspace_bytes(w->fmt, w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, w->N, M, t)))
     return fail(WQ_ERR_WORKSPACE, "wq_gemm: tile " + std::to_string(t) + " needs a workspace of " +
-                                      std::to_string(gemm_workspace_bytes(w->N, M, t)) + " bytes");
+                                      std::to_string(gemm_workspace_bytes(w->fmt, w->N, M, t)) + " bytes");
   return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream);
 }
 
@@ -630,7 +631,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       if (s > split_units(&copies[0])) return WQ_OK;
       if (s > 1 && (!ws || ws_bytes < gemv_workspace_bytes(copies[0].N, M, s))) return WQ_OK;
     } else {
-      const size_t need = gemm_workspace_bytes(copies[0].N, M, cand[c].tile);
+      const size_t need = gemm_workspace_bytes(copies[0].fmt, copies[0].N, M, cand[c].tile);
       if (need > 0 && (!ws || ws_bytes < need)) return WQ_OK;
       if (cand[c].tile >= kSkinnyTile0 && cand[c].tile <= kSkinnyTileLast &&
           gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0)

@@ -690,29 +690,32 @@ __global__ __launch_bounds__(512, 1) void gemm_dma64_w8pc_kernel(const uint8_t* 
 }
 
 // ---------------------------------------------------------------------------------
-// Group-128 formats, large M: the same LDS-DMA pipeline with fp16 matrix products.
+// Group-128 formats: the same LDS-DMA pipeline with fp16 matrix products of exact
+// factors.
 //
-// A group scale cannot stay outside the products the way a per-channel scale does,
-// and bf16 cannot hold s (q - z) exactly (rounding every weight to bf16 costs up to
-// 0.9 of the tolerance at K = 5120, growing with sqrt(K)); fp16 rounds it 8x finer.
-// So the B fragments are fp16(s (q - z)) -- codes under an fp16 exponent pattern
-// (v_perm_b32 for int8: 1024 + u; v_and_or_b32 for uint4: 1024 + q from bits 0..3 of
-// a half, 64 + q from bits 4..7), the offset and zero-point removed exactly by one
-// packed fp16 add, then one packed fp16 multiply by s -- and x is converted to fp16 in
-// LDS, once per step and workgroup: every lane converts the 16-byte chunks its own DMA
-// brought, right after waiting for them, so the step's one barrier also covers the
-// conversion (bf16 -> fp16 is exact for |x| in [2^-14, 65504]; smaller magnitudes keep
-// an absolute error below 2^-24).  v_mfma_f32_32x32x16_f16 accumulates in fp32.
+// A group scale cannot stay outside the products the way a per-channel scale does, and
+// neither bf16 nor fp16 holds s (q - z) exactly (rounding every weight to bf16 costs up
+// to 0.9 of the tolerance at K = 5120, growing with sqrt(K); fp16 rounds 8x finer but
+// its worst case still exceeds the tolerance wherever products cancel).  So the B
+// fragments are the exact codes -- under an fp16 exponent pattern (v_perm_b32 for int8:
+// 1024 + u; v_and_or_b32 for uint4: 1024 + q from bits 0..3 of a half, 64 + q from bits
+// 4..7), the offset and zero-point removed exactly by one packed fp16 add -- against x
+// in fp16, and a second accumulator set takes each group's partial sums, which are added
+// into the first times the group's scale (fp32) when the group ends.  Every product is
+// exact, so an output carries only fp32 summation and the final bf16 rounding.  The
+// second set is why these tiles are 128 x 256 (eight waves of 128 x 32, or 64 x 32 for
+// the 64-row tiles): at 256 x 256 the two sets exceed the registers of two waves per SIMD.
 //
-// The fp16 rounding of each weight adds an error of up to 2^-11 |x w| per term, small
-// against the tolerance while the weights are of LLM size, but not for large weights
-// whose products cancel.  So a workgroup recomputes its tile on an exact path (bf16
-// codes q or q - z, fp32 partial per group times the scale, operands straight from
-// memory: slow, and only for such inputs) when a dequantised weight of its groups can
-// exceed 16 in magnitude (|s| times the largest |q - z| or |q|; N(0, 0.02^2) weights
-// with 1 % x8 outliers stay near 1), and when an accumulator ends non-finite: beyond
-// 65504 x and s (q - z) round to Inf (nearest-even conversion and multiply).  Large
-// activations are not bounded this way (tracking max |x| per step cost 7 %).
+// x reaches the matrix cores in fp16: converted once per call by x_to_f16_rows_kernel
+// when the workspace has room -- each row scaled by a power of two so that all of it
+// converts exactly, the scale taken back out in the epilogue -- otherwise in LDS,
+// unscaled, once per step and workgroup (every lane converts the 16-byte chunks its own
+// DMA brought, right after waiting for them, so the step's one barrier also covers the
+// conversion).  A value fp16 cannot hold exactly (unscaled: other than 0 or 2^-17 <= |x|
+// <= 65280) converts to NaN, so that the tile's accumulators end non-finite and the
+// workgroup recomputes its tile on the exact path (bf16 codes q or q - z against bf16 x,
+// fp32 partial per group times the scale, operands straight from memory: slow, and only
+// for such inputs).
 //
 // A stage also holds the step's group metadata (the 256 rows' scales and, for uint4,
 // zero-points), brought by one more LDS-DMA of waves 0 and 1.  uint4 codes take 32
@@ -795,35 +798,92 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
   }
 }
 
-// Eight bf16 values -> fp16 (v_cvt_pk_f16_f32: nearest even, Inf beyond the fp16 range).
+// Eight bf16 values -> fp16, each exactly, or NaN where fp16 cannot hold the value
+// exactly (0 < |x| < 2^-17, |x| > 65280, Inf, NaN): a NaN makes the tile's accumulators
+// non-finite, which sends the tile down the exact path, so the fp16 operands are
+// always the activations themselves.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_exact(uint32_t w) {
+  const float2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+  uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  if (lo != 0 && (lo < 0x3700u || lo > 0x477Fu)) o = (o & 0xFFFF0000u) | 0x7E00u;
+  if (hi != 0 && (hi < 0x3700u || hi > 0x477Fu)) o = (o & 0x0000FFFFu) | 0x7E000000u;
+  return o;
+}
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
+  return make_uint4(bf16x2_to_f16x2_exact(v.x), bf16x2_to_f16x2_exact(v.y), bf16x2_to_f16x2_exact(v.z),
+                    bf16x2_to_f16x2_exact(v.w));
+}
+
+// x converted to fp16 once per call for the group-128 LDS-DMA tiles when the workspace
+// has room, one workgroup per row, each row scaled by a power of two 2^e_m chosen from
+// its largest and smallest nonzero magnitude so that every value converts exactly: the
+// largest lands below 2^15, and the row is exact when its smallest nonzero value then
+// lands at 2^-17 or above (a spread of up to 2^31 between them; activations drawn from
+// N(0, 1) hold values near 1e-6, which unscaled fp16 cannot hold).  xinv[m] = 2^-e_m
+// takes the scale back out of the fp32 results, exactly.  A row that cannot be held
+// (a wider spread, a bf16 subnormal, Inf or NaN) is written as NaN, so that its tiles
+// recompute on the exact path.  Otherwise every workgroup converts the x chunks of each
+// stage it loads (no scaling: tiles whose x fp16 cannot hold fall back).
+__global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                                            float* __restrict__ xinv, int K) {
+  __shared__ uint32_t red_mx[4], red_mn[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K);
+  uint4* xo = reinterpret_cast<uint4*>(xh + (size_t)m * K);
+  const int n8 = K / 8;
+  uint32_t mx = 0, mn = 0xFFFFu;  // largest |x| bits, smallest nonzero |x| bits
+  for (int i = tid; i < n8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float2_t f = {__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xFFFF0000u)};
-    o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = w[q] & 0x7FFFu, hi = (w[q] >> 16) & 0x7FFFu;
+      mx = max(mx, max(lo, hi));
+      mn = min(mn, min(lo ? lo : 0xFFFFu, hi ? hi : 0xFFFFu));
+    }
   }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  for (int d = 32; d >= 1; d >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d));
+  }
+  if (lane == 0) {
+    red_mx[wave] = mx;
+    red_mn[wave] = mn;
+  }
+  __syncthreads();
+  mx = max(max(red_mx[0], red_mx[1]), max(red_mx[2], red_mx[3]));
+  mn = min(min(red_mn[0], red_mn[1]), min(red_mn[2], red_mn[3]));
+  // biased bf16 exponents; the scale puts the largest value below 2^15 (e capped so
+  // that 2^-e stays a normal fp32 number)
+  const int emax = (int)(mx >> 7), emin = (int)(mn >> 7);
+  const int e = mx == 0 ? 0 : min(141 - emax, 100);
+  const bool ok = mx == 0 || (emax < 255 && emax + e <= 141 && (mn == 0xFFFFu || (emin >= 1 && emin + e >= 110)));
+  const float sc = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);  // 2^e, -113 <= e <= 100
+  for (int i = tid; i < n8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float2_t f = {__uint_as_float(w[q] << 16) * sc, __uint_as_float(w[q] & 0xFFFF0000u) * sc};
+      o[q] = ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t)) : 0x7E007E00u;
+    }
+    xo[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (tid == 0) xinv[m] = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);  // 2^-e
 }
 
-// x converted to fp16 once per call, for the group-128 LDS-DMA tile when the workspace
-// has room: otherwise every workgroup converts the x chunks of each stage it loads, so
-// an x tile is converted once per 256-column block of the output.
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ xh,
-                                                       int64_t n8) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
-    xh[i] = bf16x8_to_f16x8(x[i]);
-}
-
-// XH: xd is x already in fp16 (x_to_f16_kernel); otherwise xd == x and the stages
-// are converted in LDS.  The exact fallback always reads the bf16 x.
+// XH: xd is x already in fp16, row m scaled by 1 / xinv[m] (x_to_f16_rows_kernel);
+// otherwise xd == x and the stages are converted in LDS.  The exact fallback always
+// reads the bf16 x.
 template <int FMT, int WM, int WN, bool XH = false, int TM = DBM>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
                                                                          const uint16_t* __restrict__ x,
                                                                          const uint16_t* __restrict__ xd,
+                                                                         const float* __restrict__ xinv,
                                                                          uint16_t* __restrict__ y,
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
@@ -837,11 +897,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   constexpr int kDmaPerStep = XI + WI;
   constexpr int KUNIT = 2;  // split-K granularity in steps: one group
   static_assert(WI >= 1, "every wave takes part in the code DMA");
+  static_assert(NW == 8, "eight waves: each holds one 16-k half of a slice at a time");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[F::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[F::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[F::kStage];
   __shared__ int wave_flag[NW];
-  __shared__ float wave_max[NW];
 
   DmaWork wk;
   if (!dma_work(M, N, tail0, tailS, wk, TM)) return;
@@ -908,7 +968,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   };
   // the x chunks this lane's own DMA brought into a stage, bf16 -> fp16 in place
   // (v_cvt_pk_f16_f32, nearest even: beyond fp16 range gives Inf)
-  // (nothing to do when x arrives as fp16: XH, converted by x_to_f16_kernel)
+  // (nothing to do when x arrives as fp16: XH, converted by x_to_f16_rows_kernel)
   auto convert = [&](uint8_t* st) {
     if constexpr (XH) return;
 #pragma unroll
@@ -930,72 +990,34 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       baddr[P] = kDA + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
   }
 
-  f16x8_t A0[2][RB], B0[2][CB];
-  f16x8_t A1[NW == 4 ? 2 : 1][RB], B1[NW == 4 ? 2 : 1][CB];
-  // the step's group metadata for this lane's CB columns, as fp16 pairs: the scale,
-  // and minus the code offset plus zero-point (uint4: 1024 + z and 64 + z; int8: 1152)
-  f16x2_t msc[CB], mo0[CB], mo1[CB];
+  // the step's group metadata for this lane's CB columns: the scale in fp32 (exact),
+  // and minus the code offset plus zero-point as fp16 pairs (uint4: 1024 + z and 64 + z;
+  // int8: 1152)
+  float msc[CB];
+  f16x2_t mo0[CB], mo1[CB];
   auto meta_read = [&](const uint8_t* st) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const int n = wn * 32 * CB + j * 32 + l32;
       const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + kDA + F::kCodeBytes + 2 * n);
-      _Float16 sh;
       if constexpr (kW4) {
         const uint8_t zb = st[kDA + F::kCodeBytes + DBN * 2 + (n >> 1)];
         const _Float16 z = (_Float16)(float)((zb >> (4 * (n & 1))) & 15u);
-        sh = __builtin_bit_cast(_Float16, sb);
+        msc[j] = f16_to_f32(sb);
         mo0[j] = f16x2_t{-(_Float16)1024.f - z, -(_Float16)1024.f - z};
         mo1[j] = f16x2_t{-(_Float16)64.f - z, -(_Float16)64.f - z};
       } else {
-        sh = (_Float16)bf16_to_f32(sb);
+        msc[j] = bf16_to_f32(sb);
         mo0[j] = f16x2_t{(_Float16)-1152.f, (_Float16)-1152.f};
       }
-      msc[j] = f16x2_t{sh, sh};
     }
   };
   uint32_t nib_lo = 0x000F000Fu, nib_hi = 0x00F000F0u, mag_1024 = 0x64006400u, mag_64 = 0x54005400u;
   if constexpr (kW4) asm volatile("" : "+v"(nib_lo), "+v"(nib_hi), "+s"(mag_1024), "+s"(mag_64));
-  // fp16 pair (offset + q) -> fp16 pair s (q - z): exact add, one rounding multiply
-  auto deq = [&](uint32_t h, f16x2_t off, f16x2_t sc) -> uint32_t {
-    return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, h) + off) * sc);
+  // fp16 pair (offset + q) -> fp16 pair (q - z), or q for int8: one exact add
+  auto deq = [&](uint32_t h, f16x2_t off) -> uint32_t {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h) + off);
   };
-  auto fread = [&](const uint8_t* st, int P, f16x8_t (*A)[RB], f16x8_t (*B)[CB]) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        A[s2][i] = *reinterpret_cast<const f16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
-    if (P == 0) meta_read(st);
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      if constexpr (kW4) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(st + baddr[P] + j * 32 * 32);
-        const uint32_t wd[2] = {raw.x, raw.y};
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const uint32_t w = wd[s2], w8 = w >> 8;
-          const uint4 o = make_uint4(deq((w & nib_lo) | mag_1024, mo0[j], msc[j]),
-                                     deq((w & nib_hi) | mag_64, mo1[j], msc[j]),
-                                     deq((w8 & nib_lo) | mag_1024, mo0[j], msc[j]),
-                                     deq((w8 & nib_hi) | mag_64, mo1[j], msc[j]));
-          B[s2][j] = __builtin_bit_cast(f16x8_t, o);
-        }
-      } else {
-        const uint4 raw = *reinterpret_cast<const uint4*>(st + baddr[P] + j * 32 * 64);
-        const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[2 * q] = deq(__builtin_amdgcn_perm(0x64646464u, d[q], 0x04010400u), mo0[j], msc[j]);
-          o[2 * q + 1] = deq(__builtin_amdgcn_perm(0x64646464u, d[q], 0x04030402u), mo0[j], msc[j]);
-        }
-        B[0][j] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        B[1][j] = __builtin_bit_cast(f16x8_t, make_uint4(o[4], o[5], o[6], o[7]));
-      }
-    }
-  };
-
   // One half s2 of a slice (eight waves: the registers hold one half at a time): the A
   // fragments of MFMA s2 and the B fragments they meet.
   auto fread_half = [&](const uint8_t* st, int P, int s2, f16x8_t* A, f16x8_t* B) {
@@ -1006,44 +1028,51 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     for (int j = 0; j < CB; ++j) {
       if constexpr (kW4) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(st + baddr[P] + j * 32 * 32 + 4 * s2), w8 = w >> 8;
-        const uint4 o = make_uint4(deq((w & nib_lo) | mag_1024, mo0[j], msc[j]),
-                                   deq((w & nib_hi) | mag_64, mo1[j], msc[j]),
-                                   deq((w8 & nib_lo) | mag_1024, mo0[j], msc[j]),
-                                   deq((w8 & nib_hi) | mag_64, mo1[j], msc[j]));
+        const uint4 o = make_uint4(deq((w & nib_lo) | mag_1024, mo0[j]),
+                                   deq((w & nib_hi) | mag_64, mo1[j]),
+                                   deq((w8 & nib_lo) | mag_1024, mo0[j]),
+                                   deq((w8 & nib_hi) | mag_64, mo1[j]));
         B[j] = __builtin_bit_cast(f16x8_t, o);
       } else {
         const uint2 raw = *reinterpret_cast<const uint2*>(st + baddr[P] + j * 32 * 64 + 8 * s2);
-        const uint4 o = make_uint4(deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04010400u), mo0[j], msc[j]),
-                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04030402u), mo0[j], msc[j]),
-                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04010400u), mo0[j], msc[j]),
-                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04030402u), mo0[j], msc[j]));
+        const uint4 o = make_uint4(deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04010400u), mo0[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.x, 0x04030402u), mo0[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04010400u), mo0[j]),
+                                   deq(__builtin_amdgcn_perm(0x64646464u, raw.y, 0x04030402u), mo0[j]));
         B[j] = __builtin_bit_cast(f16x8_t, o);
       }
     }
   };
 
-  floatx16 acc[RB][CB];
+  // acc: the scaled sum over the groups so far; grp: the current group's partial sums
+  // of exact products, added into acc times the group scale when the group ends
+  floatx16 acc[RB][CB], grp[RB][CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) acc[i][j][a] = 0.f;
+      for (int a = 0; a < 16; ++a) {
+        acc[i][j][a] = 0.f;
+        grp[i][j][a] = 0.f;
+      }
   auto mma_half = [&](const f16x8_t* A, const f16x8_t* B) {
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
       for (int j = 0; j < CB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+        grp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], grp[i][j], 0, 0, 0);
   };
-  auto mma = [&](f16x8_t (*A)[RB], f16x8_t (*B)[CB]) {
+  auto fold = [&]() {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+      for (int j = 0; j < CB; ++j)
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+        for (int a = 0; a < 16; ++a) {
+          acc[i][j][a] = fmaf(msc[j], grp[i][j][a], acc[i][j][a]);
+          grp[i][j][a] = 0.f;
+        }
   };
   // This wave's DMA of the step after the current one is complete (only the newest
   // step's kDmaPerStep may still be in flight; waves 0 and 1 issue one more, so they
@@ -1056,51 +1085,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  constexpr int kMfmaPerPhase = 2 * RB * CB, kReadsPerPhase = 2 * RB + 3 * CB;
-  constexpr int kCvtPerPhase = 30 * CB;  // per 16 codes: extraction, 8 packed adds, 8 packed multiplies
-  constexpr int kLead = kMfmaPerPhase > 4 ? 4 : 1;  // MFMAs that cover the LDS read latency
-  constexpr int kv = (kCvtPerPhase + kMfmaPerPhase - kLead - 1) / (kMfmaPerPhase - kLead) + 1;
-  auto phase_order = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerPhase, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
-#pragma unroll
-    for (int i = kLead; i < kMfmaPerPhase; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kv, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
   dma(st0, 0);
   dma(st1, 1);
   dma(st2, 2);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerStep) : "memory");
   convert(st0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  constexpr bool kPipelined = NW == 4;
-  if constexpr (kPipelined) fread(st0, 0, A0, B0);
+  // one step: both 32-k slices, a half (16 k) at a time (the registers hold one half);
+  // a group is two steps (the range starts on a group), so odd steps end one
   auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
-    if constexpr (kPipelined) {
-      fread(cur, 1, A1, B1);
-      mma(A0, B0);
-      phase_order();
-      step_barrier(nxt);
-      dma(cur, t + 3);  // every wave is done with this stage
-      __builtin_amdgcn_sched_barrier(0);
-      fread(nxt, 0, A0, B0);
-      mma(A1, B1);
-      phase_order();
-    } else {
-      f16x8_t Ah[RB], Bh[CB];
+    f16x8_t Ah[RB], Bh[CB];
 #pragma unroll
-      for (int P = 0; P < 2; ++P)
+    for (int P = 0; P < 2; ++P)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          fread_half(cur, P, s2, Ah, Bh);
-          mma_half(Ah, Bh);
-        }
-      step_barrier(nxt);
-      dma(cur, t + 3);
-    }
+      for (int s2 = 0; s2 < 2; ++s2) {
+        fread_half(cur, P, s2, Ah, Bh);
+        mma_half(Ah, Bh);
+      }
+    if (t & 1) fold();
+    step_barrier(nxt);
+    dma(cur, t + 3);
   };
   const int KS3 = KS - KS % 3;
   for (int t = 0; t < KS3; t += 3) {
@@ -1112,48 +1116,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   if (KS % 3 == 2) step(st1, st2, KS3 + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- a dequantised weight of more than 16 in magnitude, or a non-finite
-  // accumulator, sends the tile down the exact path
-  bool big = false;
+  // ---- a non-finite accumulator (an x that fp16 cannot hold exactly arrives as NaN,
+  // and beyond fp16's range products overflow) sends the tile down the exact path
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) big |= !__builtin_isfinite(acc[i][j][a]);
-  // max |s| of the tile's columns over this range's groups, from the tiled metadata
-  // (per tile a contiguous run of 32 bytes per group)
-  float smax;
-  {
-    const int gb = kb / KUNIT, ng = KS / KUNIT;
-    u16x2_t sm16 = {0, 0};
-    for (int c = threadIdx.x; c < 16 * 2 * ng; c += 64 * NW) {
-      const int tt = min(n0 / kGemvTileRows + c / (2 * ng), T - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(scales + ((size_t)tt * G + gb) * kGemvTileRows +
-                                                      8 * (c % (2 * ng)));
-      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
-      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
-      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
-      sm16 = __builtin_elementwise_max(sm16, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
-    }
-    smax = kW4 ? fmaxf(f16_to_f32(sm16.x), f16_to_f32(sm16.y)) : fmaxf(bf16_to_f32(sm16.x), bf16_to_f32(sm16.y));
-  }
-  for (int d = 1; d < 64; d <<= 1) smax = fmaxf(smax, __shfl_xor(smax, d));
-  const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
-  if (lane == 0) {
-    wave_flag[wave] = wave_big ? 1 : 0;
-    wave_max[wave] = smax;
-  }
+      for (int a = 0; a < 16; ++a) bad |= !__builtin_isfinite(acc[i][j][a]);
+  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if (lane == 0) wave_flag[wave] = wave_bad ? 1 : 0;
   __syncthreads();
   int any = 0;
-  float ws = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    any |= wave_flag[w];
-    ws = fmaxf(ws, wave_max[w]);
-  }
-  constexpr float kCodeMax = kW4 ? 15.f : 127.f;  // largest |q - z| or |q|
-  if (any || !(kCodeMax * ws <= 16.f)) {  // (NaN scales fail the comparison)
+  for (int w = 0; w < NW; ++w) any |= wave_flag[w];
+  if (any) {
     g128_tile_exact<FMT, TM>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, S,
                          wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
     return;
@@ -1170,8 +1148,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
-        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][a]);
-        else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = acc[i][j][a];
+        const float v = XH ? acc[i][j][a] * xinv[m] : acc[i][j][a];  // the row's scale back out (exact)
+        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = v;
       }
   }
 }
@@ -1623,20 +1602,20 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
 // (times the channel scale for per-channel W8).  blockIdx.y: tail tile; a thread takes
 // 8 consecutive columns of one row (32 threads per row, 8 rows per block, blockIdx.x:
 // the row group).
-template <bool kPerChannel>
+template <bool kPerChannel, int TM>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __restrict__ part,
                                                                 const uint16_t* __restrict__ scales,
                                                                 uint16_t* __restrict__ y, int M, int N,
                                                                 int tail0, int S) {
-  const int mblocks = (M + DBM - 1) / DBM, lin = tail0 + (int)blockIdx.y;
+  const int mblocks = (M + TM - 1) / TM, lin = tail0 + (int)blockIdx.y;
   const int r = (int)blockIdx.x * 8 + (int)(threadIdx.x >> 5), c = 8 * (int)(threadIdx.x & 31);
-  const int m = (lin % mblocks) * DBM + r, n = (lin / mblocks) * DBN + c;
+  const int m = (lin % mblocks) * TM + r, n = (lin / mblocks) * DBN + c;
   if (m >= M || n >= N) return;
-  const float* p = part + (size_t)blockIdx.y * S * DBM * DBN + r * DBN + c;
+  const float* p = part + (size_t)blockIdx.y * S * TM * DBN + r * DBN + c;
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(p + (size_t)s * DBM * DBN);
-    const float4 b = *reinterpret_cast<const float4*>(p + (size_t)s * DBM * DBN + 4);
+    const float4 a = *reinterpret_cast<const float4*>(p + (size_t)s * TM * DBN);
+    const float4 b = *reinterpret_cast<const float4*>(p + (size_t)s * TM * DBN + 4);
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
   }
@@ -1691,9 +1670,10 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N) {
   return S;
 }
 
-int gemm_dma_split(int tile, int64_t M, int64_t N) {
+int gemm_dma_split(int fmt, int tile, int64_t M, int64_t N) {
   if (tile < kDmaSplitTile0 || tile > kDmaSplitTileLast) return 0;
-  const int64_t blocks = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+  const int64_t tm = gemm_big_dma_rows(fmt);
+  const int64_t blocks = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
   int S = 2 << (tile - kDmaSplitTile0);
   // about two workgroups per CU at most, and a bounded workspace
   while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
@@ -1712,8 +1692,9 @@ int device_cus() {
   return c;
 }
 
-int gemm_dma_tail(int64_t M, int64_t N, int* tail0) {
-  const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+int gemm_dma_tail(int fmt, int64_t M, int64_t N, int* tail0) {
+  const int64_t tm = gemm_big_dma_rows(fmt);
+  const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
   const int cus = device_cus();
   *tail0 = (int)total;
   const int64_t r = total % cus;
@@ -1731,27 +1712,41 @@ int gemm_dma64_split(int tile, int64_t M, int64_t N) {
   return S;
 }
 
-size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile) {
+size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile) {
   if (tile >= kDma64Tile0) {
     const int S = gemm_dma64_split(tile, M, N);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
   }
   if (tile == kDmaTailTile) {
     int tail0 = 0;
-    const int S = gemm_dma_tail(M, N, &tail0);
-    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-    return S > 1 ? (size_t)S * (size_t)(total - tail0) * DBM * DBN * sizeof(float) : 0;
+    const int S = gemm_dma_tail(fmt, M, N, &tail0);
+    const int64_t tm = gemm_big_dma_rows(fmt);
+    const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
+    return S > 1 ? (size_t)S * (size_t)(total - tail0) * tm * DBN * sizeof(float) : 0;
   }
-  const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(tile, M, N) : gemm_skinny_split(tile, M, N);
+  const int S = tile >= kDmaSplitTile0 ? gemm_dma_split(fmt, tile, M, N) : gemm_skinny_split(tile, M, N);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
-  const size_t need = gemm_workspace_bytes(N, M, tile);
+  const size_t need = gemm_workspace_bytes(fmt, N, M, tile);
   if (fmt == WQ_FMT_W8_PC || tile < 9 || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
-  return round256(need) + (size_t)M * (size_t)K * 2;
+  return round256(round256(need) + (size_t)M * (size_t)K * 2) + (size_t)M * sizeof(float);
+}
+
+// The fp16 copy of x (rows scaled) and the row scales' inverses after part_bytes of
+// partials, when the workspace has room for both: launches x_to_f16_rows_kernel and sets
+// *xh and *xinv, else leaves them NULL (the tiles then convert x in LDS).
+static hipError_t x_to_f16_rows(const uint16_t* x, int64_t M, int K, void* ws, size_t ws_bytes, size_t part_bytes,
+                                uint16_t** xh, float** xinv, hipStream_t s) {
+  const size_t xh_off = round256(part_bytes), xi_off = round256(xh_off + (size_t)M * K * 2);
+  if (!ws || ws_bytes < xi_off + (size_t)M * sizeof(float) || ((uintptr_t)ws + xh_off) % 16 != 0) return hipSuccess;
+  *xh = (uint16_t*)((uint8_t*)ws + xh_off);
+  *xinv = (float*)((uint8_t*)ws + xi_off);
+  x_to_f16_rows_kernel<<<(unsigned)M, 256, 0, s>>>(x, *xh, *xinv, K);
+  return hipGetLastError();
 }
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
@@ -1764,7 +1759,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   if (tile >= kSkinnyTile0 && tile <= kSkinnyTileLast) {
     int S = gemm_skinny_split(tile, M, N);
     if (S > 0 && K % SK_STEP == 0 && (int64_t)M * K < (int64_t(1) << 31)) {
-      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;  // no room for partials
+      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;  // no room for partials
       float* part = (float*)ws;
       switch (w->fmt) {
         case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
@@ -1785,7 +1780,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 over gridDim.y
     const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
     int S = gemm_dma64_split(tile, M, N);
-    if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
+    if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;
     S = std::min(S, K / (DBK * (pc ? 1 : 2)));
     const dim3 grid((unsigned)(8 * ((total + 7) / 8)), (unsigned)S);
     float* part = (float*)ws;
@@ -1795,22 +1790,17 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       else
         gemm_dma64_w8pc_kernel<128><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
     } else {
-      const size_t xh_off = round256(S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
       uint16_t* xh = nullptr;
-      if (ws && ws_bytes >= xh_off + (size_t)M * K * 2 && ((uintptr_t)ws + xh_off) % 16 == 0) {
-        xh = (uint16_t*)((uint8_t*)ws + xh_off);
-        const int64_t n8 = M * K / 8;
-        x_to_f16_kernel<<<(unsigned)std::min<int64_t>((n8 + 255) / 256, 4096), 256, 0, s>>>((const uint4*)x,
-                                                                                          (uint4*)xh, n8);
-        WQ_HIP_CHECK(hipGetLastError());
-      }
+      float* xinv = nullptr;
+      WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh,
+                                 &xinv, s));
       const int t0 = (int)total;
 #define WQ_G128_ROWS(F, TMV)                                                                                  \
   do {                                                                                                        \
     if (xh)                                                                                                   \
-      gemm_dma_g128_kernel<F, 1, 8, true, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, t0, 1); \
+      gemm_dma_g128_kernel<F, 1, 8, true, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, t0, 1); \
     else                                                                                                      \
-      gemm_dma_g128_kernel<F, 1, 8, false, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, t0, 1); \
+      gemm_dma_g128_kernel<F, 1, 8, false, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, (int)M, K, N, t0, 1); \
   } while (0)
       if (w->fmt == WQ_FMT_W4_G128) {
         if (tm == 64) WQ_G128_ROWS(WQ_FMT_W4_G128, 64);
@@ -1835,25 +1825,28 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   if (tm != 0) tile = 1;  // shapes outside the LDS-DMA tiles
   const bool dma_tile = tile == 3 || tile == 4 || tile >= 9;
   if (dma_tile && (pc || tile >= 9) && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
-    const int64_t total = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+    // per-channel W8: 256 x 256 tiles; group-128: 128 x 256 tiles (the exact kernel's
+    // second accumulator set)
+    const int btm = gemm_big_dma_rows(w->fmt);
+    const int64_t total = ((M + btm - 1) / btm) * ((N + DBN - 1) / DBN);
     const int kcap = K / (DBK * (pc ? 1 : 2));  // at least one step (group) per K range
     int S = 1, tail0 = (int)total, tailS = 1;
     if (tile == kDmaTailTile) {
-      tailS = std::min(gemm_dma_tail(M, N, &tail0), kcap);
-      if (tailS <= 1 || !ws || ws_bytes < gemm_workspace_bytes(N, M, tile)) {
+      tailS = std::min(gemm_dma_tail(w->fmt, M, N, &tail0), kcap);
+      if (tailS <= 1 || !ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile)) {
         tailS = 1;
         tail0 = (int)total;
       }
     } else if (tile >= kDmaSplitTile0) {
-      S = gemm_dma_split(tile, M, N);
-      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(N, M, tile))) S = 1;
+      S = gemm_dma_split(w->fmt, tile, M, N);
+      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;
       S = std::min(S, kcap);
     }
     const int64_t ntail = total - tail0;
     const unsigned blocks = (unsigned)(8 * ((tail0 + 7) / 8) + 8 * ((tailS * ntail + 7) / 8));
     const dim3 grid(blocks, (unsigned)S);
     float* part = (float*)ws;
-    const size_t part_bytes = tailS > 1 ? (size_t)tailS * ntail * DBM * DBN * sizeof(float)
+    const size_t part_bytes = tailS > 1 ? (size_t)tailS * ntail * btm * DBN * sizeof(float)
                                         : (S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
     if (pc) {
       if (tile == 3)
@@ -1863,31 +1856,22 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       else
         gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
     } else {
-      // x in fp16 after the partials when the workspace has room for it
-      const size_t xh_off = round256(part_bytes);
+      // x in fp16 (rows scaled) after the partials when the workspace has room for it
       uint16_t* xh = nullptr;
-      if (ws && ws_bytes >= xh_off + (size_t)M * K * 2 && ((uintptr_t)ws + xh_off) % 16 == 0) {
-        xh = (uint16_t*)((uint8_t*)ws + xh_off);
-        const int64_t n8 = M * K / 8;
-        const unsigned cb = (unsigned)std::min<int64_t>((n8 + 255) / 256, 4096);
-        x_to_f16_kernel<<<cb, 256, 0, s>>>((const uint4*)x, (uint4*)xh, n8);
-        WQ_HIP_CHECK(hipGetLastError());
-      }
-      if (w->fmt == WQ_FMT_W4_G128) {
-        if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4, true>
-              <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, tail0, tailS);
-        else
-          gemm_dma_g128_kernel<WQ_FMT_W4_G128, 2, 4>
-              <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, tail0, tailS);
-      } else {
-        if (xh)
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4, true>
-              <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, y, part, (int)M, K, N, tail0, tailS);
-        else
-          gemm_dma_g128_kernel<WQ_FMT_W8_G128, 2, 4>
-              <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, y, part, (int)M, K, N, tail0, tailS);
-      }
+      float* xinv = nullptr;
+      WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, part_bytes, &xh, &xinv, s));
+#define WQ_G128_BIG(F)                                                                                 \
+  do {                                                                                                 \
+    if (xh)                                                                                            \
+      gemm_dma_g128_kernel<F, 1, 8, true, 128>                                                         \
+          <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS);         \
+    else                                                                                               \
+      gemm_dma_g128_kernel<F, 1, 8, false, 128>                                                        \
+          <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, (int)M, K, N, tail0, tailS);       \
+  } while (0)
+      if (w->fmt == WQ_FMT_W4_G128) WQ_G128_BIG(WQ_FMT_W4_G128);
+      else WQ_G128_BIG(WQ_FMT_W8_G128);
+#undef WQ_G128_BIG
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
@@ -1899,11 +1883,11 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       WQ_HIP_CHECK(hipGetLastError());
     }
     if (tailS > 1) {
-      const dim3 rg(DBM / 8, (unsigned)ntail);
+      const dim3 rg((unsigned)(btm / 8), (unsigned)ntail);
       if (pc)
-        gemm_tail_reduce_kernel<true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<true, 256><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       else
-        gemm_tail_reduce_kernel<false><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<false, 128><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;

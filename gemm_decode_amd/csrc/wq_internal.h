@@ -97,7 +97,7 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N);  // 0 when the tile is no
 // within two workgroups per CU and the fp32 partials within kDmaSplitMaxBytes.
 constexpr int kDmaSplitTile0 = 10, kDmaSplitTileLast = 12;
 constexpr int64_t kDmaSplitMaxBytes = int64_t(256) << 20;
-int gemm_dma_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not a split one
+int gemm_dma_split(int fmt, int tile, int64_t M, int64_t N);  // 0 when the tile is not a split one
 // GEMM tile kDmaTailTile is tile 9 with the tiles of a partial last round (fewer than
 // half the CUs' worth) split over K into up to kDmaTailMaxSplit ranges, so that round
 // spreads over the idle CUs; gemm_dma_tail returns that split (1: nothing to split)
@@ -114,13 +114,18 @@ constexpr int kDma128Tile0 = 17, kDma128TileLast = 19;
 inline int gemm_dma_rows(int tile) {
   return tile >= kDma64Tile0 && tile <= kDma64TileLast ? 64 : tile >= kDma128Tile0 && tile <= kDma128TileLast ? 128 : 0;
 }
+// rows per x tile of the LDS-DMA tiles 3, 4 and 9..13: 256 for per-channel W8; 128 for
+// the group-128 formats, whose exact kernel keeps a second accumulator set (each group's
+// partial sums, added into the first times the group scale) that a 256-row tile has no
+// registers for
+inline int gemm_big_dma_rows(int fmt) { return fmt == WQ_FMT_W8_PC ? 256 : 128; }
 int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of 14..19
-int gemm_dma_tail(int64_t M, int64_t N, int* tail0);
+int gemm_dma_tail(int fmt, int64_t M, int64_t N, int* tail0);
 // Compute units of the current device (kDefaultCUs, MI355X's count, if it cannot be queried).
 constexpr int kDefaultCUs = 256;
 int device_cus();
 // Workspace bytes a GEMM tile needs at this M (fp32 split-K partials; 0 for most tiles).
-size_t gemm_workspace_bytes(int64_t N, int64_t M, int tile);
+size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile);
 // Bytes with which a tile takes its fastest path: for the group-128 LDS-DMA tiles
 // (9..13) also x converted to fp16 once per call (M x K x 2 bytes after the partials,
 // at a 256-byte boundary); without that room the tile converts x in LDS.

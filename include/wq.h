@@ -160,9 +160,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB) -- or the
  * partials of tile 13's split last round (sized for the current device's CU count, 256
  * when none is visible); 0 when no split applies.  For the group-128 formats the
- * LDS-DMA tiles 9..13 also use M * K * 2 bytes after the partials (at a 256-byte
- * boundary) for x converted to fp16 once per call; given less, they convert x inside
- * every workgroup instead (same results, slower), so that part is never required.
+ * LDS-DMA tiles 9..19 also use M * K * 2 bytes after the partials (at a 256-byte
+ * boundary) for x converted to fp16 once per call (each row scaled by a power of two
+ * so that it converts exactly), then M * 4 bytes (at a 256-byte boundary) for the row
+ * scales; given less, they convert x inside every workgroup instead, unscaled (same
+ * results; slower, and much slower where x holds values fp16 cannot hold exactly, such
+ * as magnitudes below 2^-17), so that part is never required.
  * The contents are scratch: no initialisation is needed and nothing is kept between
  * calls.  Calls that share a workspace must not run concurrently. */
 wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes);
@@ -224,22 +227,24 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
 
 /* Prefill GEMM, M >= 1 (used by wq_linear for M >= 8; smaller M are accepted so
  * the two paths can be compared), the tileInfer README's dequantize-to-bf16 GEMM
- * ("Key Optimizations"): codes are converted to exact bf16 values (q, or q - z) and
- * multiplied by bf16 x on the matrix cores with fp32 accumulation; the per-channel
- * scale is applied to the finished fp32 sum, group-128 scales to each group's fp32
- * partial -- except tile 9 for the group-128 formats, which stages the dequantised
- * weight rounded once to fp16, fp16(s (q - z)), against x converted to fp16 (a
- * workgroup whose x or dequantised weights leave the fp16 range, or whose dequantised
- * weights can exceed 16 in magnitude, recomputes its tile the exact way).  w must be
- * in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
+ * ("Key Optimizations"): every tile multiplies exact code values (q, or q - z) by x on
+ * the matrix cores with fp32 accumulation; the per-channel scale is applied to the
+ * finished fp32 sum, group scales to each group's fp32 partial sum, so an output carries
+ * only fp32 summation and the final bf16 rounding.  The group-128 LDS-DMA tiles (9..19)
+ * multiply fp16 code values by fp16 copies of x: with the workspace's room for x (see
+ * wq_workspace_size) each row is scaled by a power of two so that it converts exactly;
+ * a workgroup whose x fp16 still cannot hold exactly recomputes its tile with bf16 codes
+ * against bf16 x.  w must be in the GFX950 layout; x: bf16 [M][K], y: bf16 [M][N].
  *
  * tile: 0 = the tuned tile (a default by M and format when untuned), else
  *   1  256 x 256 workgroup tile (256 x 128 for group-128), 4 waves, LDS-staged;
  *   2  128 x 128 tile, 4 waves of 64 x 64;
  *   3  per-channel W8, K % 64 == 0: 256 x 256 tile fed by LDS-DMA, 2 x 2 waves;
  *   4  as 3 with 1 x 4 waves;
- *   9  as 3 with 8 waves (2 x 4, two per SIMD); for group-128 the fp16 LDS-DMA tile
- *      above (tiles 3 and 4 for group-128, and 3, 4, 9-13 for other shapes: tile 1);
+ *   9  as 3 with 8 waves (2 x 4, two per SIMD); for group-128 the LDS-DMA tile with
+ *      fp16 code values and a 128 x 256 workgroup tile (eight waves of 128 x 32: the
+ *      group partial sums need a second accumulator set) (tiles 3 and 4 for group-128,
+ *      and 3, 4, 9-13 for other shapes: tile 1);
  *   10..12  tile 9 with split-K 2, 4, 8 (ranges of whole groups for group-128; fp32
  *      partials in the workspace, added in range order), capped so that the grid
  *      stays within 512 workgroups and the partials within 256 MiB (needs that
@@ -247,10 +252,11 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      split drops to 1);
  *   13  tile 9 with the tiles of a partial last round split over K: when the tile
  *      count exceeds the CU count C by r <= C/2 (864 = 3 x 256 + 96 at M = 2048, N =
- *      27648), the last r tiles run as min(4, C / r) K ranges each, writing a 256 x 256
- *      fp32 block per range to the workspace (r x ranges x 256 KiB; needs it, else
- *      WQ_ERR_WORKSPACE; with tile 0 and too small a workspace it runs as tile 9), and a
- *      second kernel adds them in range order; other shapes: tile 9;
+ *      27648 for per-channel W8), the last r tiles run as min(4, C / r) K ranges each,
+ *      writing an fp32 block of the tile's size per range to the workspace (r x ranges x
+ *      256 KiB, 128 KiB for group-128; needs it, else WQ_ERR_WORKSPACE; with tile 0 and
+ *      too small a workspace it runs as tile 9), and a second kernel adds them in range
+ *      order; other shapes: tile 9;
  *   14..16  K % 64 == 0: the LDS-DMA pipeline of tile 9 with 64-row x tiles (1 x 8
  *      waves; group-128 as tile 9), split-K 1, 2, 4 (partials as for 10..12, capped
  *      so that the grid stays within 512 workgroups; 15 and 16 need that workspace,

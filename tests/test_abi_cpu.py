@@ -210,11 +210,17 @@ def test_validation_rejects_before_any_device_work(wqlib):
     tail = 2 * 96 * 256 * 256 * 4
     assert L.wq_workspace_size(C.byref(big), 2048, C.byref(n)) == 0 and n.value == tail
     assert L.wq_workspace_size(C.byref(big), 1024, C.byref(n)) == 0 and n.value == 0   # 432 tiles: 176 left over
-    # group-128: the LDS-DMA tiles also take x in fp16 (M x K x 2) after the partials
+    # group-128: 128 x 256 tiles (the exact kernel's second accumulator set), and x in
+    # fp16 (M x K x 2) after the partials, then the M row scales (fp32).  M = 2048: 1728 tiles, a last round of 192
+    # (more than half the CUs: not split); M = 512: 432 tiles, no split either
     big4 = _desc(wqlib, fmt=2, K=5120, N=27648)
-    assert L.wq_workspace_size(C.byref(big4), 2048, C.byref(n)) == 0 and n.value == tail + 2048 * 5120 * 2
-    assert L.wq_workspace_size(C.byref(big4), 512, C.byref(n)) == 0 and \
-        n.value == 2 * 512 * 27648 * 4 + 512 * 5120 * 2
+    assert L.wq_workspace_size(C.byref(big4), 2048, C.byref(n)) == 0 and n.value == 2048 * 5120 * 2 + 2048 * 4
+    assert L.wq_workspace_size(C.byref(big4), 512, C.byref(n)) == 0 and n.value == 512 * 5120 * 2 + 512 * 4
+    # 16 x 17 = 272 tiles of 128 x 256: 16 left over, split over K in 4 (a 128 x 256
+    # fp32 block per range)
+    tail4 = _desc(wqlib, fmt=2, K=5120, N=17 * 256)
+    assert L.wq_workspace_size(C.byref(tail4), 2048, C.byref(n)) == 0 and \
+        n.value == 4 * 16 * 128 * 256 * 4 + 2048 * 5120 * 2 + 2048 * 4
 
 
 def test_lm_head_topk_validation_and_workspace(wqlib):
@@ -291,3 +297,4 @@ def test_binding_constants_match_the_header(wqlib):
     assert int(re.search(r"#define WQ_GEMV_PREFETCH (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_PREFETCH
     assert int(re.search(r"#define WQ_GEMV_MFMA (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_MFMA
     assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))
+

@@ -103,3 +103,37 @@ def test_tiny_activations_gemv(wq, fmt):
     assert np.median(np.abs(y_ref)) > 0.3
     for cfg, y in _run_all_gemv(wq, g, x, fmt):
         assert_parity(y, y_ref, f"{fmt} tiny-x gemv {cfg}")
+
+
+def _gemm_tiles(wq, fmt, K, M):
+    return list(range(1, wq.GEMM_TILES + 1))
+
+
+def _run_gemm_tile(wq, g, x_bits, tile):
+    M = x_bits.shape[0]
+    y = torch.empty((M, g.N), dtype=torch.bfloat16, device=DEV)
+    wq.wq_gemm(g, to_dev_bf16(x_bits), y, tile=tile, ws=wq.workspace(wq.wq_workspace_size(g, M)))
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("M", [8, 40, 300])
+def test_cancelling_large_activations_gemm(wq, fmt, M):
+    W, x = _cancelling_case(fmt, N=264, M=M)
+    g, _ = quantize_on_gpu(wq, W, fmt)
+    y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
+    assert np.max(np.abs(y_ref)) == 0.0
+    for tile in _gemm_tiles(wq, fmt, x.shape[1], M):
+        y = _run_gemm_tile(wq, g, x, tile)
+        assert_parity(y, y_ref, f"{fmt} cancelling gemm M={M} tile={tile}")
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("M", [8, 40, 300])
+def test_tiny_activations_gemm(wq, fmt, M):
+    W, x = _tiny_case(fmt, M=M)
+    g, _ = quantize_on_gpu(wq, W, fmt)
+    y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
+    for tile in _gemm_tiles(wq, fmt, x.shape[1], M):
+        assert_parity(_run_gemm_tile(wq, g, x, tile), y_ref, f"{fmt} tiny-x gemm M={M} tile={tile}")

@@ -53,16 +53,9 @@ def _rows_options(wq, fmt, M):
     return out
 
 
-def _fp16_staged(fmt, tile):
-    """The group-128 formats' LDS-DMA GEMM (tile 9 and the tiles above it) stages
-    fp16(dequant(W)): its exact selections return bf16(fp16(w)) rather than bf16(w)."""
-    return fmt != "w8pc" and tile >= 9
-
-
 def _selected(fmt, tile, w):
-    """bf16 bits a path returns when x selects the dequantised weights w exactly."""
-    if _fp16_staged(fmt, tile):
-        w = np.asarray(w, dtype=np.float64).astype(np.float16).astype(np.float32)
+    """bf16 bits a path returns when x selects the dequantised weights w exactly: every
+    path multiplies exact codes and scales fp32 sums, so bf16(w) on every tile."""
     return OQ.bf16_rne_bits(np.ascontiguousarray(w, dtype=np.float32))
 
 
@@ -259,8 +252,8 @@ def test_edge_shapes_every_path(wq, fmt, K, N):
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_one_hot_is_exact(wq, fmt):
     """x = e_k: every path returns bf16(dequant(W)[n, k]) bit-exactly (one exact
-    nonzero term in every fp32 sum), for every split, every waves count and both
-    GEMM tiles.  K spans several (and a ragged) K slices."""
+    nonzero term in every fp32 sum), for every split, every waves count and every
+    GEMM tile.  K spans several (and a ragged) K slices."""
     K, N = 9216, 264
     W = synth.weight(94, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
@@ -296,13 +289,13 @@ def test_identity_is_exact(wq, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["w8g128", "w4g128"])
-def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
-    """The fp16 LDS-DMA GEMM of the group-128 formats recomputes a workgroup's tile
-    exactly when its x leaves the fp16 range (|x| > 65504) or its dequantised weights
-    can exceed 16 in magnitude (huge weights whose fp16 rounding would break the
-    tolerance where their products cancel); other workgroups stay on the fp16 path,
-    and |x| up to 65504 is exact in fp16."""
-    K, N, M = 1024, 520, 300   # two 256-row blocks of x, three 256-column blocks
+def test_gemm_fp16_activations_fall_back_to_exact(wq, fmt):
+    """The group-128 LDS-DMA GEMM multiplies fp16 copies of x: a workgroup whose x holds
+    a value fp16 cannot hold exactly (|x| > 65280, or 0 < |x| < 2^-17) recomputes its
+    tile on the exact bf16 path; other workgroups stay on the fp16 path, and 40000 (fp16
+    holds it) stays there too.  Huge weights (scales beyond fp16's range of products)
+    change nothing: codes stay exact and scales multiply fp32 sums."""
+    K, N, M = 1024, 520, 300   # three 128-row blocks of x, three 256-column blocks
     W = synth.weight(105, K, N, synth.uses_outliers(fmt))
     W[300:308] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)  # huge weights in one 8-row block
     g, can = quantize_on_gpu(wq, W, fmt)
@@ -310,13 +303,15 @@ def test_gemm_fp16_staging_falls_back_to_exact(wq, fmt):
     sc = np.abs(P["scales"].astype(np.float32) if fmt == "w4g128" else OQ.bf16_bits_to_f32(P["scales"]))
     assert sc.max() > (4096 if fmt == "w4g128" else 512) and np.isfinite(sc).all()
     xf = OQ.bf16_bits_to_f32(synth.activation(105, K, M)).copy()
-    for case in ("plain", "big-x"):
+    for case in ("plain", "big-x", "tiny-x"):
         if case == "big-x":
-            xf[5, 17] = 40000.0                 # fp16 holds it: first row block stays on fp16
+            xf[5, 17] = 40000.0                 # fp16 holds it: the first row block stays on fp16
             xf[6, 900] = -3.0e5                 # beyond fp16: the first row block falls back
+        if case == "tiny-x":
+            xf[200, 33] = 3.0e-7                # below 2^-17: the second row block falls back
         x = OQ.bf16_rne_bits(xf.astype(np.float32))
         y_ref = OL.ref_linear(x, P)
-        for tile in (9, 11, 15, 1):   # 11: split-K 4 (fp32 partials, also on the exact path); 15: 64-row tiles
+        for tile in (9, 11, 13, 15, 18, 1):   # 11: split-K (fp32 partials, also on the exact path); 15, 18: 64- and 128-row tiles
             assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} {case} tile={tile}")
         # without a workspace tile 9 converts x to fp16 inside each workgroup: same bits
         assert np.array_equal(_run_gemm(wq, g, x, 9, with_ws=False), _run_gemm(wq, g, x, 9)), f"{fmt} {case}"
@@ -417,23 +412,29 @@ def test_dispatch_boundary_m7_m8(wq):
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_gemm_tail_round_split(wq, fmt):
-    """Tile 13: 2 x 140 tiles of 256 x 256 (ragged in M and N) leave 24 tiles for a
-    last round on a 256-CU device, which are split over K into 4 fp32 partials (their
-    own block per range) and added by a second kernel; compared with the oracle everywhere,
-    also with huge weights in a tail tile (group-128: the exact fallback writes those
-    partials); the default tile without a workspace runs it as tile 9."""
+    """Tile 13: the tiles (256 x 256 for per-channel W8: 2 x 140; 128 x 256 for
+    group-128: 3 x 94), ragged in M and N, leave 24 resp. 26 tiles for a last round on a
+    256-CU device, which are split over K into 4 fp32 partials (their own block per
+    range) and added by a second kernel; compared with the oracle everywhere, also with
+    huge weights in a tail tile and an activation below fp16's exact range in the last
+    row block (group-128: its tiles, tail tiles among them, fall back to the exact path,
+    which writes those partials); the default tile without a workspace runs it as tile
+    9."""
     K, M = 1024, 300
-    N = 35800 if fmt == "w4g128" else 35803   # odd N: the reduction's per-element stores
+    tm, nb = (256, 140) if fmt == "w8pc" else (128, 94)
+    N = 256 * nb - (40 if fmt == "w4g128" else 37)     # odd N: the reduction's per-element stores
     W = synth.weight(107, K, N, synth.uses_outliers(fmt))
     if fmt != "w8pc":
-        W[35000:35008] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)
+        W[N - 800:N - 792] *= np.float32(1.5e5 if fmt == "w4g128" else 2.0e6)
     g, _ = quantize_on_gpu(wq, W, fmt)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    total = 2 * 140
-    if total > cus and 2 * (total % cus) <= cus:   # 256 CUs: 24 tiles left, split 4
+    total = -(-M // tm) * nb
+    if total > cus and 2 * (total % cus) <= cus:   # 256 CUs: 24 / 26 tiles left, split 4
         r = total % cus
-        assert wq.wq_workspace_size(g, M) >= min(4, cus // r) * r * 256 * 256 * 4
-    x = synth.activation(107, K, M)
+        assert wq.wq_workspace_size(g, M) >= min(4, cus // r) * r * tm * 256 * 4
+    xf = OQ.bf16_bits_to_f32(synth.activation(107, K, M)).copy()
+    xf[290, 100] = 3.0e-7
+    x = OQ.bf16_rne_bits(xf.astype(np.float32))
     y_ref = OL.ref_linear(x, OQ.pack(fmt, W))
     # tile 0 picks 13 here; without a workspace it runs as tile 9, tile 13 itself refuses
     for tile, with_ws in ((13, True), (0, True), (0, False), (9, True)):
