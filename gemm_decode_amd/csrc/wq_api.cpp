@@ -429,6 +429,64 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
   return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------- the layer without allocation
+namespace {
+// Scratch of wq_linear_static: one copy per device, held from the library's load to
+// the end of the process.  In host code `scratch` names a host-side stand-in of the
+// symbol, never the device memory: kernels get the per-device address that
+// hipGetSymbolAddress returns for it (static_scratch below), nothing else.
+__device__ __align__(256) uint8_t scratch[WQ_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+// Device address of this device's scratch (looked up once per device, with that device
+// current), or NULL with the error text set.
+void* static_scratch(wq_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) return it->second;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    *st = e != hipSuccess ? hip_fail(e, "hipGetSymbolAddress(scratch)")
+                          : fail(WQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    return nullptr;
+  }
+  g_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+}  // namespace
+
+wq_status wq_linear_static(const wq_weight* w, const void* x, int64_t M, void* y, void* stream) {
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  // the workspace the configuration wq_linear would run needs (its split-K partials)
+  size_t need = 0;
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) {
+    int split = 1, waves = 0, rows = 0;
+    resolve_gemv(w, M, &split, &waves, &rows);
+    need = gemv_workspace_bytes(w->N, M, split);
+  } else {
+    need = gemm_workspace_bytes(w->fmt, w->N, M, resolve_tile(w, M));
+  }
+  if (need > (size_t)WQ_STATIC_SCRATCH_BYTES)
+    return fail(WQ_ERR_WORKSPACE, "wq_linear_static: this shape's configuration needs " + std::to_string(need) +
+                                      " bytes of partial sums, more than the " +
+                                      std::to_string((size_t)WQ_STATIC_SCRATCH_BYTES) +
+                                      "-byte static scratch; call wq_linear with a workspace");
+  void* ws = static_scratch(&st);
+  if (!ws) return st;
+  return wq_linear(w, x, M, y, ws, (size_t)WQ_STATIC_SCRATCH_BYTES, stream);
+}
+
 // ------------------------------------------------------------ LM head + top-k
 namespace {
 struct TopkLayout {

@@ -21,7 +21,7 @@ __all__ = [
     "wq_gemv_max_waves", "wq_gemv_max_split",
     "wq_pack", "wq_pack_bf16", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
-    "wq_linear_perm_workspace_size", "wq_linear_perm",
+    "wq_linear_perm_workspace_size", "wq_linear_perm", "wq_linear_static", "STATIC_SCRATCH_BYTES",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -43,6 +43,7 @@ WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)
 GEMV_PREFETCH = 0x100                    # WQ_GEMV_PREFETCH: rows flag, slice prefetch
 GEMV_MFMA = 0x200                        # WQ_GEMV_MFMA: rows flag: the matrix-core GEMV (rows = 16 NB)
+STATIC_SCRATCH_BYTES = 64 << 20          # WQ_STATIC_SCRATCH_BYTES: the scratch of wq_linear_static
 
 
 def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:
@@ -74,6 +75,7 @@ _SIGS = {
     "wq_gemv_ex": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_linear_static": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
     "wq_linear_perm_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
     "wq_linear_perm": (C.c_int, [_W, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t,
@@ -261,6 +263,12 @@ def wq_linear(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tenso
     M, d = _xy(x, y, w), w.desc()
     _check(lib.wq_linear(C.byref(d), _ptr(x), M, _ptr(y), _ptr(ws),
                          0 if ws is None else ws.numel(), _stream(stream)), "wq_linear")
+
+
+def wq_linear_static(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """wq_linear with the library's static scratch instead of a workspace (no allocation)."""
+    M, d = _xy(x, y, w), w.desc()
+    _check(lib.wq_linear_static(C.byref(d), _ptr(x), M, _ptr(y), _stream(stream)), "wq_linear_static")
 
 
 # ------------------------------------------------------------ LM head + top-k

@@ -15,8 +15,10 @@
  *   - Pointers named in a wq_weight, x, y and ws are DEVICE pointers (memory from
  *     hipMalloc or a PyTorch HIP tensor); size_t/int64_t out-parameters and the
  *     path strings are HOST pointers.
- *   - The caller owns every buffer.  The library never allocates device memory,
- *     never frees anything it was given and keeps no pointer after a call returns.
+ *   - The caller owns every buffer.  The library never allocates device memory
+ *     (its only device memory of its own is the static scratch of wq_linear_static,
+ *     which comes with the loaded code), never frees anything it was given and keeps
+ *     no pointer after a call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
  *     enqueued asynchronously on it; wq_gemv, wq_gemm and wq_linear neither
  *     synchronize nor read device memory on the host, so they may be captured
@@ -277,6 +279,26 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
  * the tuned tile (see wq_dispatch_kind). */
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------- the layer without allocation */
+
+/* wq_linear for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The split-K partials (and, where it fits, the fp16 copy of x of the
+ * group-128 GEMM tiles) go to a static scratch array of WQ_STATIC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends; the call itself
+ * allocates and frees nothing.  The configuration is the one wq_linear runs (tuned, or
+ * the default), so the result is bit-identical to wq_linear given a workspace of
+ * wq_workspace_size bytes.  A shape whose configuration needs more partial-sum space
+ * than the scratch holds returns WQ_ERR_WORKSPACE (nothing is written); use wq_linear
+ * with a workspace there.  The scratch keeps whatever the last call left (no call
+ * needs it cleared).  Every call on one device shares that device's scratch, so calls
+ * that may overlap on one device (different streams, or threads without ordering) race
+ * and must not be issued; calls ordered on one stream are safe.  x, y and the weight as
+ * for wq_linear.  The first call on a device looks the scratch address up (no device
+ * work, no allocation). */
+#define WQ_STATIC_SCRATCH_BYTES (64u << 20)
+wq_status wq_linear_static(const wq_weight* w, const void* x, int64_t M, void* y, void* stream);
 
 /* ------------------------------------------------------- LM head + top-k */
 

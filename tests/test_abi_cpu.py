@@ -297,4 +297,6 @@ def test_binding_constants_match_the_header(wqlib):
     assert int(re.search(r"#define WQ_GEMV_PREFETCH (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_PREFETCH
     assert int(re.search(r"#define WQ_GEMV_MFMA (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_MFMA
     assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))
+    m = re.search(r"#define WQ_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == wq.STATIC_SCRATCH_BYTES
 
