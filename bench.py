@@ -118,10 +118,20 @@ class Pool:
         self.W = None
 
 
-def time_graph(torch, fn, n_calls: int, reps: int = 9, stats: dict | None = None):
-    """Capture n_calls of fn() in one HIP graph; after 2 warm-up replays return the
-    median of `reps` timed replays (ms), measured with HIP events on the capturing
-    stream (min and max go into `stats` when given)."""
+SETTLE_S = 1.0   # untimed replays before a timed measurement (see time_graph)
+
+
+def time_graph(torch, fn, n_calls: int, reps: int = 9, stats: dict | None = None, settle_s: float | None = None):
+    """Capture n_calls of fn() in one HIP graph; after 2 warm-up replays and `settle_s`
+    seconds of untimed replays return the median of `reps` timed replays (ms), measured
+    with HIP events on the capturing stream (min and max go into `stats` when given).
+
+    The settle phase is there because MI355X's memory-side clocks rise under sustained
+    memory-bound load: the W8 (5120, 27648) M = 1 GEMV measured 26.9 us from cold, 23.6 us
+    after 45 s of GEMV load and 27.9 us again after 20 s idle (45 s of compute-bound
+    matmuls left it at 26.4 us), so a short timing right after setup sees the idle clocks,
+    not the steady state of a serving loop."""
+    settle_s = SETTLE_S if settle_s is None else settle_s
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -136,6 +146,11 @@ def time_graph(torch, fn, n_calls: int, reps: int = 9, stats: dict | None = None
         g.replay()
         g.replay()
         torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                g.replay()
+            torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -239,9 +254,25 @@ def traffic_entry(kernel_src_sha: str):
 
 # Launch configuration of the headline GEMV per shape (split_k, waves, rows) used by
 # the counter pass, so the profiled kernels are the ones the tuner picks on MI355X.
-PROFILE_CONFIG = {(5120, 27648): (1, 8, 4), (13824, 5120): (1, 4, 4), (5120, 7168): (1, 1, 4),
+PROFILE_CONFIG = {(5120, 27648): (1, 3, 4 | 0x100), (13824, 5120): (1, 12, 4), (5120, 7168): (1, 1, 4 | 0x100),
                   (6144, 5120): (1, 6, 4)}
 COPY_BYTES = 1 << 30
+
+
+def streaming_settle(torch, seconds: float = 5.0):
+    """Untimed memory-bound work (a 1 GiB elementwise kernel, a few dispatches a
+    millisecond) so that the memory-side clocks reach their steady state before a
+    profiled workload, without adding thousands of the profiled kernel's dispatches to
+    the trace (see time_graph)."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            torch.bitwise_not(a, out=b)
+        torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def profile_pass(steps: int = 10, replays: int = 2):
@@ -275,10 +306,17 @@ def profile_pass(steps: int = 10, replays: int = 2):
         with torch.cuda.graph(g, stream=s):
             for _ in range(steps):
                 step()
+        torch.cuda.synchronize()
+        streaming_settle(torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
         for _ in range(replays):
             g.replay()
+        e1.record(s)
         torch.cuda.synchronize()
-    log(f"profile pass: {replays} replays x {steps} steps x {len(pools)} GEMV launches")
+    us = e0.elapsed_time(e1) * 1e3 / (replays * steps)
+    log(f"profile pass: {replays} replays x {steps} steps x {len(pools)} GEMV launches: {us:.2f} us per step "
+        f"(HIP events), {sum(p.bytes_per_call() for p in pools) / us / 1e3:.0f} GB/s")
 
 
 PREFILL_PROFILE = [("w8pc", 5120, 27648, 2048, 13), ("w4g128", 5120, 27648, 2048, 13)]
@@ -300,7 +338,8 @@ def profile_prefill(calls: int = 10):
     for fmt, K, N, M, tile in PREFILL_PROFILE:
         p = Pool(wq, torch, 5, fmt, K, N, M)
         wq.wq_tune_cache_set(fmt, K, N, M, wq.KIND_GEMM, tile)
-        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1)
+        streaming_settle(torch, 3.0)
+        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1, settle_s=0.0)
         us = ms * 1e3 / calls
         log(f"profile prefill {fmt} K={K} N={N} M={M} tile={tile}: {us:.1f} us per call "
             f"(HIP events), {2.0 * M * K * N / us / 1e6:.1f} TFLOP/s")
@@ -310,7 +349,7 @@ def profile_prefill(calls: int = 10):
 
 
 # (K, N) -> (split_k, waves, rows): the launches the tuner picks for the W4 decode shapes
-PROFILE_W4 = {(5120, 27648): (1, 3, 8), (13824, 5120): (1, 4, 4)}
+PROFILE_W4 = {(5120, 27648): (1, 4, 16 | 0x200), (13824, 5120): (1, 4, 4)}
 
 
 def profile_w4(calls: int = 10):
@@ -324,7 +363,8 @@ def profile_w4(calls: int = 10):
         p = Pool(wq, torch, 3, "w4g128", K, N, 1)
         wq.wq_tune_cache_set("w4g128", K, N, 1, wq.KIND_GEMV, sk | (wv << 8) | (rw << 16))
         v = wq.wq_tune_cache_get("w4g128", K, N, 1, wq.KIND_GEMV)
-        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1)
+        streaming_settle(torch, 3.0)
+        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1, settle_s=0.0)
         log(f"profile w4 K={K} N={N} M=1 (split, waves, rows) = ({v & 0xFF}, {(v >> 8) & 0xFF}, "
             f"{v >> 16:#x}): {ms * 1e3 / calls:.2f} us per call (HIP events)")
         p.free()
@@ -536,6 +576,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replays", type=int, default=7, help="timed graph replays of the headline (median)")
+    ap.add_argument("--settle", type=float, default=8.0,
+                    help="seconds of untimed headline replays before timing (steady-state clocks)")
     ap.add_argument("--quick", action="store_true", help="headline only (no per-workload detail)")
     ap.add_argument("--detail", default="", help="comma list of detail groups to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -614,7 +656,7 @@ def main():
         step()
     torch.cuda.synchronize()
     head_stats = {}
-    ms = time_graph(torch, step, args.steps, reps=args.replays, stats=head_stats)
+    ms = time_graph(torch, step, args.steps, reps=args.replays, stats=head_stats, settle_s=args.settle)
     ms_per_step = ms / args.steps
     value = bytes_step / (ms_per_step / 1e3) / 1e9
     log(f"headline: {ms_per_step * 1e3:.2f} us/step (median of {args.replays} replays of {args.steps} steps; "
@@ -659,7 +701,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(bytes_step / 4),
                      "avg_launch_us": round(ms_per_step * 1e3 / 4, 3),
                      "timing": f"HIP events on the launching stream, median of {args.replays} graph replays "
-                               f"of {launches} launches"},
+                               f"of {launches} launches, after {args.settle:g} s of untimed replays"},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
         "targets": compact_targets(detail, value, ms_per_step),
     }

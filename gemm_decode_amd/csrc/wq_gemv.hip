@@ -571,10 +571,20 @@ __device__ __forceinline__ void i8_word_to_bf16(uint32_t d, uint32_t& lo, uint32
   hi = pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24));
 }
 
-template <int FMT, int M, int NB>
+// LX (x in LDS): the workgroup first converts its K range of x to fp16 in LDS (M x 128 k
+// per unit, uint4 operands in their lo / hi order) with one flag per unit that is set
+// when some x of the unit does not convert exactly; the waves then read their A
+// operands from LDS instead of converting and checking x for every unit, and load the
+// next unit's codes while multiplying the current one.  Chosen by the launcher when the
+// fp16 x fits kLxMaxBytes.
+constexpr int kLxMaxBytes = 64 * 1024;
+inline int lx_bytes(int M, int units) { return M * units * 256 + ((units + 15) & ~15); }
+
+template <int FMT, int M, int NB, bool LX>
 __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part, int K, int N) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lx_mem[];
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
   constexpr int MI = M < 4 ? M : 4;             // accumulator rows a lane keeps (token 4 (l / 16) + i, i < MI)
   constexpr int kUnitBytes = kW4 ? 64 : 128;    // code bytes per row and 128-k unit
@@ -616,12 +626,32 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
   f32x4_t acc[NB];  // group-128: scaled sums; per-channel: raw sums of x q
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nu = u1 - u0;                      // LX: units of this workgroup's K range
+  uint8_t* lx_flag = lx_mem + M * nu * 256;    // LX: per unit, 1 if some x is not fp16-exact
+
 
   // One unit's operands (32-bit fields only, so that the set stays in registers).
   struct Set {
     u32x4_t c[NB][CL];
     uint4 xv[4];
     uint32_t sv[NB], zb[NB];
+  };
+  // this lane's 32 x values of unit u (token min(l % 16, M - 1)); zero past K
+  auto load_x = [&](uint4 (&xv)[4], int u) {
+    const uint32_t k0 = 128u * (uint32_t)u + 32u * lk;
+    if (kW4 || 128 * (u + 1) <= K) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * k0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = k0 + 8u * j;
+        const bool ok = k + 8u <= (uint32_t)K;
+        const uint4 v = *reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * (ok ? k : 0u)));
+        xv[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
   };
   auto load = [&](Set& st, int u) {
     const uint32_t sl = (uint32_t)u / kUnitsPerSlice, ui = (uint32_t)u % kUnitsPerSlice;
@@ -635,9 +665,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
           st.c[t][c] = __builtin_bit_cast(
               u32x4_t, load_stream16(tbase[t] + nr1k[t] * sl +
                                      (__umul24(rsel[t], wsl) + kUnitBytes * ui + (kW4 ? 16u : 32u) * lk + 16u * c)));
-      const uint4* xp = reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * k0));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.xv[j] = xp[j];
+      if constexpr (!LX) load_x(st.xv, u);
     } else {
       // the ragged last unit: chunks past K load any in-bounds chunk, their x is zero
 #pragma unroll
@@ -649,13 +677,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
           st.c[t][c] = __builtin_bit_cast(u32x4_t, load_stream16(tbase[t] + nr1k[t] * sl +
                                                                  (__umul24(rsel[t], wsl) + off)));
         }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t k = k0 + 8u * j;
-        const bool ok = k + 8u <= (uint32_t)K;
-        const uint4 v = *reinterpret_cast<const uint4*>(xb8 + (xrow + 2u * (ok ? k : 0u)));
-        st.xv[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-      }
+      if constexpr (!LX) load_x(st.xv, u);
     }
     if constexpr (kGrouped) {
       const uint32_t soff = 32u * (uint32_t)u + 2u * ln, zoff = 8u * (uint32_t)u + (ln >> 1);
@@ -666,18 +688,71 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
       }
     }
   };
-  auto compute = [&](const Set& st) {
-    const uint4 xv[4] = {st.xv[0], st.xv[1], st.xv[2], st.xv[3]};
-    // does every x of the unit convert to fp16 exactly (see the dot2 path)?
-    F16Exact fx;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      fx.add(xv[j].x);
-      fx.add(xv[j].y);
-      fx.add(xv[j].z);
-      fx.add(xv[j].w);
+  // LX: the first unit's code loads go out first, so that their latency overlaps the
+  // conversion of x into LDS
+  const int first = u0 + wu;
+  const int n_my = first < u1 ? (u1 - first + W - 1) / W : 0;
+  Set sa, sb;
+  if constexpr (LX) {
+    if (n_my > 0) load(sa, first);
+  }
+  if constexpr (LX) {
+    for (int i = threadIdx.x; i < nu; i += blockDim.x) lx_flag[i] = 0;
+    __syncthreads();
+    // chunk c: token m, unit uu, 8 values j of the unit (k = 128 (u0 + uu) + 8 j)
+    for (int c = threadIdx.x; c < M * nu * 16; c += blockDim.x) {
+      const int m = c / (nu * 16), r = c - m * nu * 16, uu = r >> 4, j = r & 15;
+      const int k = 128 * (u0 + uu) + 8 * j;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k + 8 <= K) v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + k);
+      F16Exact fx;
+      fx.add(v.x);
+      fx.add(v.y);
+      fx.add(v.z);
+      fx.add(v.w);
+      if (!fx.ok()) lx_flag[uu] = 1;
+      const uint32_t h0 = bf16x2_to_f16x2(v.x), h1 = bf16x2_to_f16x2(v.y), h2 = bf16x2_to_f16x2(v.z),
+                     h3 = bf16x2_to_f16x2(v.w);
+      uint8_t* dst = lx_mem + (size_t)(m * nu + uu) * 256;
+      if constexpr (kW4) {
+        // word i of a 32-k block (pair k = 2i, 2i + 1) sits at i / 2 (i even: the pairs
+        // the 1024.0 pattern meets) or 8 + (i - 1) / 2 (odd: the 64.0 pattern's)
+        uint32_t* blk = reinterpret_cast<uint32_t*>(dst + 64 * (j >> 2));
+        const int jp = j & 3;
+        *reinterpret_cast<uint2*>(blk + 2 * jp) = make_uint2(h0, h2);
+        *reinterpret_cast<uint2*>(blk + 8 + 2 * jp) = make_uint2(h1, h3);
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * j) = make_uint4(h0, h1, h2, h3);
+      }
     }
-    const bool exact = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
+    __syncthreads();
+  }
+
+  auto compute = [&](const Set& st, int u) {
+    uint4 xv[4];
+    bool exact;
+    const u32x4_t* xa = nullptr;  // LX: this lane's four fp16 A operands in LDS
+    if constexpr (LX) {
+      exact = __builtin_amdgcn_readfirstlane(lx_flag[u - u0]) != 0;
+      xa = reinterpret_cast<const u32x4_t*>(lx_mem + (size_t)(min(ln, (uint32_t)M - 1u) * nu + (u - u0)) * 256 +
+                                            64 * lk);
+      if (exact) load_x(xv, u);
+    } else {
+      xv[0] = st.xv[0];
+      xv[1] = st.xv[1];
+      xv[2] = st.xv[2];
+      xv[3] = st.xv[3];
+      // does every x of the unit convert to fp16 exactly (see the dot2 path)?
+      F16Exact fx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fx.add(xv[j].x);
+        fx.add(xv[j].y);
+        fx.add(xv[j].z);
+        fx.add(xv[j].w);
+      }
+      exact = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
+    }
     // group-128: the unit's contribution d[t] to each tile, times the group scale
     auto fold1 = [&](int t, const f32x4_t& d) {
       const float sc = kW4 ? f16_to_f32((uint16_t)st.sv[t]) : bf16_to_f32((uint16_t)st.sv[t]);
@@ -690,19 +765,28 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     };
     if (!exact) {
       if constexpr (kW4) {
-        const u32x4_t a_lo0 = {bf16x2_to_f16x2(xv[0].x), bf16x2_to_f16x2(xv[0].z), bf16x2_to_f16x2(xv[1].x),
-                               bf16x2_to_f16x2(xv[1].z)};
-        const u32x4_t a_lo1 = {bf16x2_to_f16x2(xv[2].x), bf16x2_to_f16x2(xv[2].z), bf16x2_to_f16x2(xv[3].x),
-                               bf16x2_to_f16x2(xv[3].z)};
-        const u32x4_t a_hi0 = {bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
-                               bf16x2_to_f16x2(xv[1].w)};
-        const u32x4_t a_hi1 = {bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
-                               bf16x2_to_f16x2(xv[3].w)};
+        u32x4_t a_lo0, a_lo1, a_hi0, a_hi1;
+        if constexpr (LX) {
+          a_lo0 = xa[0];
+          a_lo1 = xa[1];
+          a_hi0 = xa[2];
+          a_hi1 = xa[3];
+        } else {
+          a_lo0 = u32x4_t{bf16x2_to_f16x2(xv[0].x), bf16x2_to_f16x2(xv[0].z), bf16x2_to_f16x2(xv[1].x),
+                          bf16x2_to_f16x2(xv[1].z)};
+          a_lo1 = u32x4_t{bf16x2_to_f16x2(xv[2].x), bf16x2_to_f16x2(xv[2].z), bf16x2_to_f16x2(xv[3].x),
+                          bf16x2_to_f16x2(xv[3].z)};
+          a_hi0 = u32x4_t{bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
+                          bf16x2_to_f16x2(xv[1].w)};
+          a_hi1 = u32x4_t{bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
+                          bf16x2_to_f16x2(xv[3].w)};
+        }
         u32x4_t b[4][NB];  // the four B operands of each tile: exact fp16 q - z
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           const uint32_t z = (st.zb[t] >> zshift) & 15u;
-          const uint32_t off_a = f16x2_splat_neg(1024u + z), off_b = f16x2_splat_neg(64u + z);
+          // fp16 pairs -(1024 + z) = 0xE400 + z and -(64 + z) = 0xD400 + 16 z
+          const uint32_t off_a = 0xE400E400u + z * 0x10001u, off_b = 0xD400D400u + z * 0x100010u;
           uint32_t lo[4], lo8[4], hi[4], hi8[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -734,8 +818,9 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
         u32x4_t a[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          a[j] = u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
-                         bf16x2_to_f16x2(xv[j].w)};
+          a[j] = LX ? xa[j]
+                    : u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
+                              bf16x2_to_f16x2(xv[j].w)};
         f32x4_t d[NB];
         if constexpr (kGrouped) {
 #pragma unroll
@@ -791,13 +876,37 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     }
   };
 
-  // A wave's units u0 + wave, + W, ...  (Loading the next unit's operands during the
-  // current one's products measured slower on MI355X: the second operand set halves
-  // the resident waves.)
-  for (int u = u0 + wu; u < u1; u += W) {
-    Set st;
-    load(st, u);
-    compute(st);
+  // A wave's units u0 + wave, + W, ...  Without LX each unit loads and multiplies in
+  // turn (a second operand set, x included, halves the resident waves: measured slower
+  // on MI355X).  With LX the set holds codes and metadata only, and the next unit's
+  // loads go out before the current unit's products (unconditionally inside the paired
+  // loop, so that waiting for one set never drains the other).
+  if constexpr (!LX) {
+    for (int u = u0 + wu; u < u1; u += W) {
+      Set st;
+      load(st, u);
+      compute(st, u);
+    }
+  } else {
+    // two operand sets: the next unit's loads go out before the current unit's
+    // products (unconditionally inside the paired loop, so that waiting for one set
+    // never drains the other); the first unit's loads went out before the x prologue
+    if (n_my > 0) {
+      int u = first, i = 0;
+      for (; i + 2 < n_my; i += 2, u += 2 * W) {
+        load(sb, u + W);
+        compute(sa, u);
+        load(sa, u + 2 * W);
+        compute(sb, u + W);
+      }
+      if (i + 1 < n_my) {
+        load(sb, u + W);
+        compute(sa, u);
+        compute(sb, u + W);
+      } else {
+        compute(sa, u);
+      }
+    }
   }
   // the waves' partial sums meet in LDS and are added in wave order
 #pragma unroll
@@ -818,13 +927,25 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
   }
 }
 
+template <int FMT, int M, int NB>
+void launch_mma_nb(dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
+                   const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+  // x in LDS when the largest split range's fp16 x fits (ranges differ by one unit at most)
+  const int U = (K + kGroup - 1) / kGroup, S = (int)grid.y;
+  const int lx = lx_bytes(M, (U + S - 1) / S);
+  if (lx <= kLxMaxBytes)
+    gemv_mma_kernel<FMT, M, NB, true><<<grid, block, lx, st>>>(qw, sc, zs, x, y, part, K, N);
+  else
+    gemv_mma_kernel<FMT, M, NB, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+}
+
 template <int FMT, int M>
 void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
                 const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
   switch (nb) {
-    case 1: gemv_mma_kernel<FMT, M, 1><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    case 2: gemv_mma_kernel<FMT, M, 2><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
-    default: gemv_mma_kernel<FMT, M, 4><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N); break;
+    case 1: launch_mma_nb<FMT, M, 1>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 2: launch_mma_nb<FMT, M, 2>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    default: launch_mma_nb<FMT, M, 4>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
   }
 }
 
