@@ -16,6 +16,9 @@ What it computes (plain, slow, obviously correct; NumPy only):
 * ``topk``   -- the k best bf16 logits of a row and the token drawn from them
   with a temperature and a caller-supplied uniform draw (the LM head + top-k
   step of the tileInfer README's feature list; reading in its docstring).
+* ``moe``    -- the grouped (mixture-of-experts) layer, each expert applied to its
+  own rows, and the SiLU-gated product of a fused gate/up projection (reading in
+  its docstring).
 
 Passages followed:
 
@@ -40,3 +43,6 @@ from .linear import (  # noqa: F401
     compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, token_count, use_gemv,
 )
 from .topk import ref_topk_sample, sample_row, topk_row  # noqa: F401
+from .moe import (  # noqa: F401
+    check_offsets, ref_linear_silu_mul, ref_moe_linear, ref_moe_silu_mul, silu, silu_mul,
+)

@@ -107,3 +107,15 @@ CONFIGS = {
 def uses_outliers(fmt: str) -> bool:
     """W4 workloads carry the 1% x8 outliers; W8 workloads are plain Gaussian."""
     return fmt == "w4g128"
+
+
+def moe_offsets(seed: int, T: int, E: int, empty=()) -> np.ndarray:
+    """Row offsets [E + 1] of T token rows grouped by E experts: a seeded random split
+    (each row's expert drawn uniformly, counted per expert), the experts listed in
+    `empty` left without rows.  Only the counts are drawn; the rows of x stay in the
+    order the caller lays them out."""
+    rng = np.random.default_rng([seed, T, E, 7])
+    live = np.array([e for e in range(E) if e not in set(empty)], dtype=np.int64)
+    pick = live[rng.integers(0, live.size, T)] if live.size else np.zeros(0, dtype=np.int64)
+    counts = np.bincount(pick, minlength=E)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)

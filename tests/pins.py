@@ -15,6 +15,7 @@ from fractions import Fraction
 import numpy as np
 
 import oracle.linear as OL
+import oracle.moe as OM
 import oracle.quant as OQ
 import oracle.topk as OT
 import synth
@@ -518,6 +519,50 @@ def pin_activation_permutation(seed=41, K=256, N=24, M=3):
             assert abs(Fraction(float(y2[m, n])) - exact) <= bound, (m, n)
 
 
+# ------------------------------------------------------ grouped layer, SiLU gate
+def pin_silu_closed_forms():
+    """silu(v) = v sigmoid(v): sigmoid(ln 3) = 3/4 exactly, so silu(+-ln 3) = (3/4) ln 3
+    and -(1/4) ln 3; silu(0) = 0; silu(v) - silu(-v) = v (sigmoid(v) + sigmoid(-v) = 1);
+    far tails: silu(50) = 50 in fp64 and silu(-800) = -0.0 (exp overflows, no NaN); the
+    gated product silu(g) * u of [g | u] at g = ln 3, u = 4 is 3 ln 3."""
+    l3 = math.log(3.0)
+    v = OM.silu(np.array([0.0, l3, -l3, 50.0, -800.0]))
+    assert v[0] == 0.0
+    assert abs(v[1] - 0.75 * l3) <= 4e-16 * l3 and abs(v[2] + 0.25 * l3) <= 4e-16 * l3, v
+    assert v[3] == 50.0 and v[4] == 0.0 and math.copysign(1.0, v[4]) < 0
+    xs = np.linspace(-12.0, 12.0, 97)
+    assert np.allclose(OM.silu(xs) - OM.silu(-xs), xs, rtol=1e-14, atol=1e-14)
+    h = OM.silu_mul(np.array([[l3, -l3, 4.0, 2.0]]))
+    assert abs(h[0, 0] - 3.0 * l3) <= 1e-15 * 3 * l3 and abs(h[0, 1] + 0.5 * l3) <= 1e-15, h
+
+
+def pin_moe_grouping(seed=51, K=256, N=24):
+    """Each row meets its own expert's weight: experts with distinct weights, one-hot
+    rows x[t] = e_{k_t}, so y[t, n] must be expert e(t)'s exactly dequantised weight at
+    (n, k_t) (decoded by hand from the packed bytes, independently of the oracle's
+    dequantiser); an empty expert between two others; one expert over all rows is the
+    dense layer; offsets that do not rise from 0 to T are refused."""
+    E, T = 4, 9
+    off = np.array([0, 3, 3, 7, 9])                       # expert 1 has no rows
+    for fmt in ("w8pc", "w4g128"):
+        Ps = [OQ.pack(fmt, synth.weight(seed + e, K, N, fmt == "w4g128")) for e in range(E)]
+        ks = [(7 * t + 3) % K for t in range(T)]
+        x = synth.one_hot_activation(K, ks)
+        y = OM.ref_moe_linear(x, off, Ps)
+        for t in range(T):
+            e = int(np.searchsorted(off, t, side="right")) - 1
+            for n in range(N):
+                assert Fraction(float(y[t, n])) == _exact_dequant(Ps[e], n, ks[t]), (fmt, t, n)
+        xr = synth.activation(seed, K, T)
+        assert np.array_equal(OM.ref_moe_linear(xr, [0, T], Ps[:1]), OL.ref_linear(xr, Ps[0]))
+    for bad in ([1, 3, 9], [0, 5, 3, 9], [0, 3, 8]):
+        try:
+            OM.check_offsets(bad, T)
+        except ValueError:
+            continue
+        raise AssertionError(f"offsets {bad} accepted")
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
     pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
@@ -528,7 +573,7 @@ ALL_PINS = [
     lambda: pin_bruteforce("w4g128", 128), pin_library_factorisation, pin_invariants,
     pin_compare, pin_compare_rel_rms, pin_dispatch, pin_topk_golden, pin_topk_rows,
     pin_topk_defining_property,
-    pin_topk_sampling_closed_forms, pin_activation_permutation,
+    pin_topk_sampling_closed_forms, pin_activation_permutation, pin_silu_closed_forms, pin_moe_grouping,
 ]
 
 

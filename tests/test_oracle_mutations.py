@@ -7,6 +7,7 @@ import pytest
 import math
 
 import oracle.linear as OL
+import oracle.moe as OM
 import oracle.quant as OQ
 import oracle.topk as OT
 import pins
@@ -238,13 +239,44 @@ def _mut_topk_rows_shifted(mp):
     mp.setattr(OT, "ref_topk_sample", bad)
 
 
+def _mut_silu_sign(mp):
+    mp.setattr(OM, "silu", lambda v: np.asarray(v, dtype=np.float64) / (1.0 + np.exp(np.asarray(v, dtype=np.float64))))
+
+
+def _mut_silu_mul_swapped(mp):
+    def bad(y):                                          # silu of the up half times the gate half
+        y = np.asarray(y, dtype=np.float64)
+        i = y.shape[-1] // 2
+        return OM.silu(y[..., i:]) * y[..., :i]
+    mp.setattr(OM, "silu_mul", bad)
+
+
+def _mut_moe_rows_shifted(mp):
+    orig = OM.ref_moe_linear
+
+    def bad(x_bits, offsets, packed):                    # expert e takes the rows one further on
+        off = np.asarray(offsets).copy()
+        off[1:-1] = np.minimum(off[1:-1] + 1, off[-1])
+        return orig(x_bits, off, packed)
+    mp.setattr(OM, "ref_moe_linear", bad)
+
+
+def _mut_moe_expert_index(mp):
+    orig = OM.ref_moe_linear
+
+    def bad(x_bits, offsets, packed):                    # rows of expert e meet expert e - 1
+        return orig(x_bits, offsets, [packed[(e - 1) % len(packed)] for e in range(len(packed))])
+    mp.setattr(OM, "ref_moe_linear", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
              _mut_topk_ascending, _mut_topk_nan_first, _mut_topk_signed_zero,
              _mut_sample_temperature_multiplies, _mut_sample_at_or_above, _mut_perm_inverse,
              _mut_perm_out_of_range_wraps, _mut_rel_rms_over_result,
-             _mut_rel_rms_zero_reference_absolute, _mut_topk_rows_first_u, _mut_topk_rows_shifted]
+             _mut_rel_rms_zero_reference_absolute, _mut_topk_rows_first_u, _mut_topk_rows_shifted,
+             _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
