@@ -839,6 +839,8 @@ def run_detail(wq, torch, args) -> dict:
                                            for cfg, fmt, M in ((3, "w4g128", 1), (1, "w8pc", 1), (5, "w8pc", 2048))
                                            for K, N in [(5120, 27648)]},
         "reference_bf16_gemm": lambda: reference_bf16_gemm(torch),
+        "moe": lambda: {f"{fmt}_E{E}_{K}x{N}_T{T}{'_silu' if gated else ''}": measure_moe(wq, torch, fmt, E, K, N, T, gated)
+                        for fmt, E, K, N, T, gated in MOE_ROWS},
     }
     want = list(groups) if not args.detail else args.detail.split(",")
     for name in want:
@@ -846,6 +848,56 @@ def run_detail(wq, torch, args) -> dict:
             raise SystemExit(f"unknown detail group {name!r}; choose from {', '.join(groups)}")
         out[name] = groups[name]()
     return out
+
+
+# MoE rows: 8 experts of a fused gate/up projection (K = 2048, N = 2 x 5632, SiLU-gated) and
+# of a down projection (K = 5632, N = 2048), one token routed to two experts (T = 2 rows)
+# and 16 tokens to two experts each (T = 32 rows, seeded counts)
+MOE_ROWS = [("w4g128", 8, 2048, 11264, 2, True), ("w4g128", 8, 2048, 11264, 32, True),
+            ("w8pc", 8, 5632, 2048, 2, False), ("w4g128", 8, 5632, 2048, 2, False)]
+
+
+def measure_moe(wq, torch, fmt, E, K, N, T, gated) -> dict:
+    """The grouped layer over E stacked experts (graph replay over rotating copies of the
+    stacked weight), checked against the oracle on every output; GB/s counts the packed
+    bytes of the experts that hold rows, x and y once."""
+    import oracle
+    import synth
+    Ws = [synth.weight(60 + e, K, N, synth.uses_outliers(fmt)) for e in range(E)]
+    base = wq.quantize_experts([torch.from_numpy(W).to("cuda") for W in Ws], fmt)
+    per = sum(wq.wq_packed_sizes(fmt, wq.GFX950, K, N))
+    copies = [base] + [base.clone() for _ in range(max(1, int(np.ceil(ROTATE_BYTES / (per * E)))) - 1)]
+    off = synth.moe_offsets(61, T, E) if T > 2 else np.array([0] + [1] * 3 + [2] * (E - 3), dtype=np.int32)
+    xb = synth.activation(62, K, T)
+    x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    od = torch.from_numpy(off.astype(np.int32)).to("cuda")
+    width = N // 2 if gated else N
+    y = torch.empty((T, width), dtype=torch.bfloat16, device="cuda")
+    epi = wq.EPILOGUE_SILU_MUL if gated else wq.EPILOGUE_NONE
+    i = [0]
+
+    def fn():
+        wq.wq_moe_linear(copies[i[0]], x, od, y, epi)
+        i[0] = (i[0] + 1) % len(copies)
+
+    fn()
+    torch.cuda.synchronize()
+    Ps = [oracle.pack(fmt, W) for W in Ws]
+    ref = oracle.ref_moe_silu_mul(xb, off, Ps) if gated else oracle.ref_moe_linear(xb, off, Ps)
+    st = oracle.compare(y.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    if st["fails"]:
+        raise SystemExit(f"moe parity failure {fmt} E={E} K={K} N={N} T={T}: {st}")
+    n = 2 * len(copies)
+    us = time_graph(torch, fn, n) / n * 1e3
+    active = int(np.count_nonzero(np.diff(off)))
+    alg = active * per + 2 * T * K + 2 * T * width
+    rec = {"us": round(us, 3), "GB/s": round(alg / us / 1e3, 1), "pct_hbm": round(100 * alg / us / 1e3 / HBM_PEAK_GBS, 1),
+           "experts_with_rows": active, "parity": st}
+    log(f"moe {fmt} E={E} K={K} N={N} T={T} gated={gated}: {rec['us']} us, {rec['GB/s']} GB/s over "
+        f"{active} experts with rows")
+    del copies, base
+    torch.cuda.empty_cache()
+    return rec
 
 
 def measure_lm_head_topk(wq, torch, cfg, fmt, K, N, M, k: int = 50, temperature: float = 0.8) -> dict:

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cinttypes>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -485,6 +486,30 @@ wq_status wq_linear_static(const wq_weight* w, const void* x, int64_t M, void* y
   void* ws = static_scratch(&st);
   if (!ws) return st;
   return wq_linear(w, x, M, y, ws, (size_t)WQ_STATIC_SCRATCH_BYTES, stream);
+}
+
+// ------------------------------------------------------- grouped (MoE) layer
+wq_status wq_moe_linear(const wq_weight* w, int E, const void* x, const int32_t* offsets, int64_t T, void* y,
+                        int epilogue, void* stream) {
+  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  if (st != WQ_OK) return st;
+  if (E < 1 || E > 65535) return fail(WQ_ERR_INVALID_ARG, "wq_moe_linear: E must lie in 1 .. 65535");
+  if (T < 0 || T > INT32_MAX) return fail(WQ_ERR_INVALID_ARG, "wq_moe_linear: T must lie in 0 .. 2^31 - 1");
+  if (epilogue != WQ_EPILOGUE_NONE && epilogue != WQ_EPILOGUE_SILU_MUL)
+    return fail(WQ_ERR_INVALID_ARG, "wq_moe_linear: unknown epilogue");
+  if (!x || !y || !offsets) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned(x, 16) || !aligned(y, 2) || !aligned(offsets, 4))
+    return fail(WQ_ERR_ALIGNMENT, "wq_moe_linear: x needs 16-byte, y 2-byte and offsets 4-byte alignment");
+  if (w->K % kGroup != 0 || w->N % 16 != 0 || (epilogue == WQ_EPILOGUE_SILU_MUL && w->N % 32 != 0))
+    return fail(WQ_ERR_UNSUPPORTED,
+                "wq_moe_linear: needs K % 128 == 0 and N % 16 == 0 (N % 32 == 0 with the gated epilogue)");
+  if (T * w->K >= (int64_t(1) << 31) || T * w->N >= (int64_t(1) << 31))
+    return fail(WQ_ERR_UNSUPPORTED, "wq_moe_linear: T * K and T * N must stay below 2^31");
+  if (T == 0) return WQ_OK;
+  size_t qb = 0, sb = 0, zb = 0;
+  if ((st = wq_packed_sizes(w->fmt, WQ_LAYOUT_GFX950, w->K, w->N, &qb, &sb, &zb)) != WQ_OK) return st;
+  return launch_moe(w, E, (const uint16_t*)x, offsets, T, (uint16_t*)y, epilogue == WQ_EPILOGUE_SILU_MUL, qb, sb,
+                    zb, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------ LM head + top-k

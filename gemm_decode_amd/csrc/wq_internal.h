@@ -144,6 +144,10 @@ int topk_chunks(int64_t V);
 wq_status launch_topk(const uint16_t* logits, int64_t M, int64_t V, int k, float temperature, const float* u,
                       uint64_t* cand, uint16_t* top_vals, int32_t* top_idx, int32_t* tokens, hipStream_t s);
 
+// Grouped (mixture-of-experts) layer: E experts stacked with the given byte strides.
+wq_status launch_moe(const wq_weight* w, int E, const uint16_t* x, const int32_t* offsets, int64_t T, uint16_t* y,
+                     bool gated, size_t qw_stride, size_t sc_stride, size_t zs_stride, hipStream_t s);
+
 // Device tag "<arch>:<CUs>" of the current device; empty on failure.
 std::string current_device_tag();
 

@@ -22,6 +22,7 @@ __all__ = [
     "wq_pack", "wq_pack_bf16", "wq_repack", "wq_unrepack", "wq_workspace_size", "wq_gemv", "wq_gemv_ex", "wq_gemm", "wq_linear",
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
     "wq_linear_perm_workspace_size", "wq_linear_perm", "wq_linear_static", "STATIC_SCRATCH_BYTES",
+    "wq_moe_linear", "quantize_experts", "EPILOGUE_NONE", "EPILOGUE_SILU_MUL",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -44,6 +45,7 @@ ROWS_GRID = (4, 8, 16)
 GEMV_PREFETCH = 0x100                    # WQ_GEMV_PREFETCH: rows flag, slice prefetch
 GEMV_MFMA = 0x200                        # WQ_GEMV_MFMA: rows flag: the matrix-core GEMV (rows = 16 NB)
 STATIC_SCRATCH_BYTES = 64 << 20          # WQ_STATIC_SCRATCH_BYTES: the scratch of wq_linear_static
+EPILOGUE_NONE, EPILOGUE_SILU_MUL = 0, 1  # WQ_EPILOGUE_*: epilogues of wq_moe_linear
 
 
 def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:
@@ -76,6 +78,7 @@ _SIGS = {
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear_static": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "wq_moe_linear": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]),
     "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
     "wq_linear_perm_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
     "wq_linear_perm": (C.c_int, [_W, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t,
@@ -158,12 +161,22 @@ class PackedWeight:
     """Device buffers of one packed weight (owned by torch tensors) plus its
     descriptor.  ``qweight``/``scales``/``zeros`` are flat uint8 tensors."""
 
-    def __init__(self, fmt, layout: int, K: int, N: int, device="cuda"):
-        self.fmt, self.layout, self.K, self.N = _fmt(fmt), layout, K, N
+    def __init__(self, fmt, layout: int, K: int, N: int, device="cuda", experts: int = 1):
+        self.fmt, self.layout, self.K, self.N, self.experts = _fmt(fmt), layout, K, N, experts
         qb, sb, zb = wq_packed_sizes(self.fmt, layout, K, N)
-        self.qweight = torch.empty(qb, dtype=torch.uint8, device=device)
-        self.scales = torch.empty(sb, dtype=torch.uint8, device=device)
-        self.zeros = torch.empty(zb, dtype=torch.uint8, device=device) if zb else None
+        self.qweight = torch.empty(qb * experts, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb * experts, dtype=torch.uint8, device=device)
+        self.zeros = torch.empty(zb * experts, dtype=torch.uint8, device=device) if zb else None
+
+    def expert(self, e: int) -> "PackedWeight":
+        """A view of expert e of a stacked weight (its own qweight / scales / zeros)."""
+        qb, sb, zb = wq_packed_sizes(self.fmt, self.layout, self.K, self.N)
+        v = PackedWeight.__new__(PackedWeight)
+        v.fmt, v.layout, v.K, v.N, v.experts = self.fmt, self.layout, self.K, self.N, 1
+        v.qweight = self.qweight[e * qb:(e + 1) * qb]
+        v.scales = self.scales[e * sb:(e + 1) * sb]
+        v.zeros = None if self.zeros is None else self.zeros[e * zb:(e + 1) * zb]
+        return v
 
     @property
     def fmt_name(self) -> str:
@@ -178,7 +191,7 @@ class PackedWeight:
 
     def clone(self) -> "PackedWeight":
         c = PackedWeight.__new__(PackedWeight)
-        c.fmt, c.layout, c.K, c.N = self.fmt, self.layout, self.K, self.N
+        c.fmt, c.layout, c.K, c.N, c.experts = self.fmt, self.layout, self.K, self.N, self.experts
         c.qweight, c.scales = self.qweight.clone(), self.scales.clone()
         c.zeros = None if self.zeros is None else self.zeros.clone()
         return c
@@ -215,6 +228,18 @@ def quantize(w: torch.Tensor, fmt, stream=None, keep_canonical: bool = False):
     g = PackedWeight(fmt, GFX950, K, N, device=w.device)
     wq_repack(can, g, stream)
     return (g, can) if keep_canonical else g
+
+
+def quantize_experts(ws, fmt, stream=None) -> PackedWeight:
+    """Pack E weights of one shape (a sequence of [N][K] fp32 or bf16 tensors) into one
+    stacked gfx950 weight for wq_moe_linear: expert e is wq_pack + wq_repack of ws[e]."""
+    N, K = ws[0].shape
+    out = PackedWeight(fmt, GFX950, K, N, device=ws[0].device, experts=len(ws))
+    for e, w in enumerate(ws):
+        can = PackedWeight(fmt, CANONICAL, K, N, device=w.device)
+        (wq_pack_bf16 if w.dtype == torch.bfloat16 else wq_pack)(w, can, stream)
+        wq_repack(can, out.expert(e), stream)
+    return out
 
 
 # ---------------------------------------------------------------- the linear
@@ -269,6 +294,20 @@ def wq_linear_static(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, stream=N
     """wq_linear with the library's static scratch instead of a workspace (no allocation)."""
     M, d = _xy(x, y, w), w.desc()
     _check(lib.wq_linear_static(C.byref(d), _ptr(x), M, _ptr(y), _stream(stream)), "wq_linear_static")
+
+
+def wq_moe_linear(w: PackedWeight, x: torch.Tensor, offsets: torch.Tensor, y: torch.Tensor,
+                  epilogue: int = EPILOGUE_NONE, stream=None) -> None:
+    """x bf16 [T][K] grouped by expert, offsets int32 [E + 1] (device), y bf16 [T][N] (or
+    [T][N / 2] with the gated epilogue); w a stacked weight of E experts."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and y.dtype == torch.bfloat16 and y.is_contiguous()
+    assert offsets.dtype == torch.int32 and offsets.is_contiguous() and offsets.numel() == w.experts + 1
+    T = x.numel() // w.K
+    assert x.numel() == T * w.K
+    assert y.numel() == T * (w.N // 2 if epilogue == EPILOGUE_SILU_MUL else w.N)
+    d = w.desc()
+    _check(lib.wq_moe_linear(C.byref(d), w.experts, _ptr(x), _ptr(offsets), T, _ptr(y), epilogue,
+                             _stream(stream)), "wq_moe_linear")
 
 
 # ------------------------------------------------------------ LM head + top-k

@@ -280,6 +280,41 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- grouped (MoE) layer */
+
+/* The grouped weight-only linear of a mixture-of-experts layer (the shared MoE kernel the
+ * Marlin register and launch scheduling benchmark page validates beside its dense one,
+ * "Validation and limits"; one WnA16 kernel for every format, SGLang quantization-stack
+ * review, Figure 4 comments), optionally with the SiLU gate fused into its epilogue
+ * (tileInfer README, "Key Optimizations", fused SiLU gate).
+ *
+ * E experts of one format and shape (K, N), each packed in the GFX950 layout, are stored
+ * one after another: w->qweight, w->scales and w->zeros point to E consecutive packed
+ * experts of wq_packed_sizes(fmt, WQ_LAYOUT_GFX950, K, N) bytes each (w describes one
+ * expert).  The T rows of x (bf16 [T][K], device, 16-byte aligned) are grouped by expert:
+ * expert e owns rows offsets[e] .. offsets[e + 1] - 1, offsets int32 [E + 1] on the
+ * device (a routing computed on the device needs no copy to the host; values are
+ * clamped into [0, T] and a range that would run backwards is empty, so malformed
+ * offsets cannot make the kernel read or write outside x and y).
+ *   epilogue WQ_EPILOGUE_NONE:     y bf16 [T][N], y[t] = bf16(x[t] . dequant(W_e)^T);
+ *   epilogue WQ_EPILOGUE_SILU_MUL: N = 2 I (the expert's gate rows, then its up rows),
+ *     y bf16 [T][I], y[t][j] = bf16(silu(g) * u) with g, u the fp32 sums of gate row j
+ *     and up row j, silu(v) = v / (1 + exp(-v)) (g and u never leave the kernel).
+ * With E = 1 and offsets {0, T} this is the dense layer (gated or not).  Rows outside
+ * every expert's range are not written.
+ *
+ * Arithmetic as wq_gemv's matrix-core path: exact code values against fp16 x (exact bf16
+ * codes against bf16 x where fp16 cannot hold an x exactly), fp32 accumulation, group
+ * scales on each group's partial sum, per-channel scales on the finished sum.  An expert
+ * is read once per block of 16 of its rows, so the call suits decode-sized batches per
+ * expert.  Needs K % 128 == 0, N % 16 == 0 (N % 32 == 0 gated), T * K and T * N below
+ * 2^31 (else WQ_ERR_UNSUPPORTED), 1 <= E <= 65535.  Allocates nothing, needs no
+ * workspace, graph-capturable. */
+#define WQ_EPILOGUE_NONE 0
+#define WQ_EPILOGUE_SILU_MUL 1
+wq_status wq_moe_linear(const wq_weight* w, int E, const void* x, const int32_t* offsets, int64_t T, void* y,
+                        int epilogue, void* stream);
+
 /* ------------------------------------------- the layer without allocation */
 
 /* wq_linear for callers that cannot allocate device memory or pass a workspace:

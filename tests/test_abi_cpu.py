@@ -297,6 +297,26 @@ def test_binding_constants_match_the_header(wqlib):
     assert int(re.search(r"#define WQ_GEMV_PREFETCH (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_PREFETCH
     assert int(re.search(r"#define WQ_GEMV_MFMA (0x[0-9a-fA-F]+)", hdr).group(1), 16) == wq.GEMV_MFMA
     assert wq.TUNE_LAT_SLOTS >= max(wq.GEMM_TILES, len(wq.SPLIT_GRID))
+    assert int(defs["WQ_EPILOGUE_NONE"]) == wq.EPILOGUE_NONE and int(defs["WQ_EPILOGUE_SILU_MUL"]) == wq.EPILOGUE_SILU_MUL
     m = re.search(r"#define WQ_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
     assert m and int(m.group(1)) << int(m.group(2)) == wq.STATIC_SCRATCH_BYTES
 
+
+
+def test_moe_linear_host_validation(wqlib):
+    """wq_moe_linear refuses bad arguments on the host, before any device work."""
+    L = wqlib.lib
+    p = C.c_void_p(1 << 20)
+    d = wqlib.WqWeightC(wqlib.FMT["w4g128"], wqlib.GFX950, 1024, 96, 1 << 20, 1 << 20, 1 << 20)
+    assert L.wq_moe_linear(C.byref(d), 0, p, p, 8, p, 0, None) == 1                 # E = 0
+    assert L.wq_moe_linear(C.byref(d), 4, p, p, -1, p, 0, None) == 1                # T < 0
+    assert L.wq_moe_linear(C.byref(d), 4, p, p, 8, p, 7, None) == 1                 # unknown epilogue
+    assert L.wq_moe_linear(C.byref(d), 4, None, p, 8, p, 0, None) == 1              # NULL x
+    assert L.wq_moe_linear(C.byref(d), 4, C.c_void_p((1 << 20) + 8), p, 8, p, 0, None) == 3   # x misaligned
+    d80 = wqlib.WqWeightC(wqlib.FMT["w4g128"], wqlib.GFX950, 1024, 80, 1 << 20, 1 << 20, 1 << 20)
+    assert L.wq_moe_linear(C.byref(d80), 4, p, p, 8, p, 1, None) == 2               # gated: N % 32
+    d2 = wqlib.WqWeightC(wqlib.FMT["w8pc"], wqlib.GFX950, 1040, 64, 1 << 20, 1 << 20, 0)
+    assert L.wq_moe_linear(C.byref(d2), 4, p, p, 8, p, 0, None) == 2                # K % 128
+    d3 = wqlib.WqWeightC(wqlib.FMT["w8pc"], wqlib.CANONICAL, 1024, 64, 1 << 20, 1 << 20, 0)
+    assert L.wq_moe_linear(C.byref(d3), 4, p, p, 8, p, 0, None) == 2                # layout
+    assert L.wq_moe_linear(C.byref(d2), 4, p, p, 0, p, 0, None) != 0                # (K % 128 first)
