@@ -127,8 +127,9 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
   *rows = 0;
 }
 
-// Untuned GEMM tile: up to 16 tokens the skinny kernel, with the smallest split-K that
-// gives about two workgroups per CU; 17..128 tokens the 64-row LDS-DMA tiles (14..16);
+// Untuned GEMM tile: up to 16 tokens the matrix-core GEMV tiles (uint4, and int8 on the
+// smaller shapes) or the skinny kernel, with the smallest split-K that gives about two
+// workgroups per CU; 17..128 tokens the 64-row LDS-DMA tiles (14..16);
 // above that the 8-wave LDS-DMA kernel
 // (tile 9) for every format, split over K (tiles 10..12) when its tiles would not
 // occupy half the CUs, or with its partial last round split over K (tile 13).
@@ -152,6 +153,14 @@ int default_tile(const wq_weight* w, int64_t M) {
            gemm_dma64_split(t + 1, M, w->N) > gemm_dma64_split(t, M, w->N))
       ++t;
     return t;
+  }
+  if (M <= kMmaTokens) {
+    // measured on MI355X at M = 8..16: uint4 (5120, 27648) 23.6 us with 64 rows per
+    // workgroup against 42.6 us for the best skinny tile, (13824, 5120) 19.0 us with 32
+    // against 30.8 us; int8 (5120, 7168) 12.5 us against 13.8 us up to 12 tokens, while
+    // the skinny kernel stays ahead for int8 on wide N or long K
+    if (w->fmt == WQ_FMT_W4_G128) return w->N >= 16384 ? kMmaTile0 + 2 : kMmaTile0 + 1;
+    if (w->N < 16384 && w->K < 8192 && M <= 12) return kMmaTile0 + 1;
   }
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
@@ -719,6 +728,8 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       if (cand[c].tile >= kSkinnyTile0 && cand[c].tile <= kSkinnyTileLast &&
           gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0)
         return WQ_OK;
+      if (cand[c].tile >= kMmaTile0 && gemm_mma_split(cand[c].tile, M, copies[0].K) == 0)
+        return WQ_OK;  // more tokens than the matrix-core GEMV kernel takes
     }
     auto run = [&]() -> wq_status { return run_cand(c, hs); };
     wq_status rs;

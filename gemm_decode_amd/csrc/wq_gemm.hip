@@ -1712,7 +1712,16 @@ int gemm_dma64_split(int tile, int64_t M, int64_t N) {
   return S;
 }
 
+int gemm_mma_split(int tile, int64_t M, int64_t K) {
+  if (tile < kMmaTile0 || tile > kMmaTileLast || M > kMmaTokens) return 0;
+  return tile == kMmaTileLast && (K + kGroup - 1) / kGroup >= 2 ? 2 : 1;
+}
+
 size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile) {
+  if (tile >= kMmaTile0) {
+    const int S = gemm_mma_split(tile, M, 0x7FFFFFFF);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  }
   if (tile >= kDma64Tile0) {
     const int S = gemm_dma64_split(tile, M, N);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
@@ -1732,7 +1741,8 @@ static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
   const size_t need = gemm_workspace_bytes(fmt, N, M, tile);
-  if (fmt == WQ_FMT_W8_PC || tile < 9 || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
+  if (fmt == WQ_FMT_W8_PC || tile < 9 || tile >= kMmaTile0 || K % DBK != 0 || M * K >= (int64_t(1) << 31))
+    return need;
   return round256(round256(need) + (size_t)M * (size_t)K * 2) + (size_t)M * sizeof(float);
 }
 
@@ -1756,6 +1766,17 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
+  if (tile >= kMmaTile0 && tile <= kMmaTileLast) {
+    // 8..16 tokens: the matrix-core GEMV kernel (one 16-token A operand)
+    int S = gemm_mma_split(tile, M, K);
+    if (S > 0) {
+      if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;  // no room for partials
+      const int nb = tile == kMmaTile0 + 1 ? 2 : tile == kMmaTile0 + 2 ? 4 : 1;
+      const int rows = (16 * nb) | kGemvMfma;
+      return launch_gemv(w, x, (int)M, y, S, gemv_default_waves(K, N, w->fmt, (int)M, S, rows), rows, ws, s);
+    }
+    tile = K % DBK == 0 ? kDma64Tile0 : 2;  // more tokens than one A operand holds
+  }
   if (tile >= kSkinnyTile0 && tile <= kSkinnyTileLast) {
     int S = gemm_skinny_split(tile, M, N);
     if (S > 0 && K % SK_STEP == 0 && (int64_t)M * K < (int64_t(1) << 31)) {

@@ -580,13 +580,17 @@ __device__ __forceinline__ void i8_word_to_bf16(uint32_t d, uint32_t& lo, uint32
 constexpr int kLxMaxBytes = 64 * 1024;
 inline int lx_bytes(int M, int units) { return M * units * 256 + ((units + 15) & ~15); }
 
+// M: the tokens (1..7), or kMmaTokens for a token count Mt of 8..kMmaTokens chosen at run
+// time (the GEMM's few-token tiles): the A operand holds 16 tokens, so a lane's x row is
+// its own token and the cost barely depends on M.
 template <int FMT, int M, int NB, bool LX>
 __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part, int K, int N) {
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part, int K, int N, int Mt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lx_mem[];
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
   constexpr int MI = M < 4 ? M : 4;             // accumulator rows a lane keeps (token 4 (l / 16) + i, i < MI)
+  const int Mr = M <= kGemvMaxM ? M : Mt;       // tokens
   constexpr int kUnitBytes = kW4 ? 64 : 128;    // code bytes per row and 128-k unit
   constexpr int kUnitsPerSlice = kSliceBytes / kUnitBytes;
   constexpr int CL = kW4 ? 1 : 2;               // 16-byte code loads per lane, tile and unit
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     rsel[t] = min(ln, (uint32_t)nr - 1u);
   }
   const uint8_t* xb8 = reinterpret_cast<const uint8_t*>(x);
-  const uint32_t xrow = min(ln, (uint32_t)M - 1u) * (uint32_t)K * 2u;  // byte offset of this lane's token
+  const uint32_t xrow = min(ln, (uint32_t)Mr - 1u) * (uint32_t)K * 2u;  // byte offset of this lane's token
   const uint32_t zshift = 4 * (ln & 1);
   uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_a = 0x64006400u, mag_h = 0x54005400u;
   if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_a), "+v"(mag_h));
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nu = u1 - u0;                      // LX: units of this workgroup's K range
-  uint8_t* lx_flag = lx_mem + M * nu * 256;    // LX: per unit, 1 if some x is not fp16-exact
+  uint8_t* lx_flag = lx_mem + Mr * nu * 256;   // LX: per unit, 1 if some x is not fp16-exact
 
 
   // One unit's operands (32-bit fields only, so that the set stays in registers).
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     for (int i = threadIdx.x; i < nu; i += blockDim.x) lx_flag[i] = 0;
     __syncthreads();
     // chunk c: token m, unit uu, 8 values j of the unit (k = 128 (u0 + uu) + 8 j)
-    for (int c = threadIdx.x; c < M * nu * 16; c += blockDim.x) {
+    for (int c = threadIdx.x; c < Mr * nu * 16; c += blockDim.x) {
       const int m = c / (nu * 16), r = c - m * nu * 16, uu = r >> 4, j = r & 15;
       const int k = 128 * (u0 + uu) + 8 * j;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     const u32x4_t* xa = nullptr;  // LX: this lane's four fp16 A operands in LDS
     if constexpr (LX) {
       exact = __builtin_amdgcn_readfirstlane(lx_flag[u - u0]) != 0;
-      xa = reinterpret_cast<const u32x4_t*>(lx_mem + (size_t)(min(ln, (uint32_t)M - 1u) * nu + (u - u0)) * 256 +
+      xa = reinterpret_cast<const u32x4_t*>(lx_mem + (size_t)(min(ln, (uint32_t)Mr - 1u) * nu + (u - u0)) * 256 +
                                             64 * lk);
       if (exact) load_x(xv, u);
     } else {
@@ -914,38 +918,38 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = 4 * (int)lk + i;
-      if (m < M) red[wave][t][m][ln] = acc[t][i];
+      if (m < Mr) red[wave][t][m][ln] = acc[t][i];
     }
   __syncthreads();
-  for (int o = threadIdx.x; o < NB * M * 16; o += blockDim.x) {
-    const int t = o / (M * 16), m = (o / 16) % M, n = 16 * (tile0 + t) + (o & 15);
+  for (int o = threadIdx.x; o < NB * Mr * 16; o += blockDim.x) {
+    const int t = o / (Mr * 16), m = (o / 16) % Mr, n = 16 * (tile0 + t) + (o & 15);
     if (tile0 + t >= T16 || n >= N) continue;
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[w][t][m][o & 15];
     if (S == 1) y[(size_t)m * N + n] = f32_to_bf16(kGrouped ? v : bf16_to_f32(scales[n]) * v);
-    else part[((size_t)s * M + m) * N + n] = v;
+    else part[((size_t)s * Mr + m) * N + n] = v;
   }
 }
 
 template <int FMT, int M, int NB>
 void launch_mma_nb(dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-                   const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+                   const uint16_t* x, uint16_t* y, float* part, int K, int N, int Mt, hipStream_t st) {
   // x in LDS when the largest split range's fp16 x fits (ranges differ by one unit at most)
   const int U = (K + kGroup - 1) / kGroup, S = (int)grid.y;
-  const int lx = lx_bytes(M, (U + S - 1) / S);
+  const int lx = lx_bytes(Mt, (U + S - 1) / S);
   if (lx <= kLxMaxBytes)
-    gemv_mma_kernel<FMT, M, NB, true><<<grid, block, lx, st>>>(qw, sc, zs, x, y, part, K, N);
+    gemv_mma_kernel<FMT, M, NB, true><<<grid, block, lx, st>>>(qw, sc, zs, x, y, part, K, N, Mt);
   else
-    gemv_mma_kernel<FMT, M, NB, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+    gemv_mma_kernel<FMT, M, NB, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, Mt);
 }
 
 template <int FMT, int M>
 void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-                const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+                const uint16_t* x, uint16_t* y, float* part, int K, int N, int Mt, hipStream_t st) {
   switch (nb) {
-    case 1: launch_mma_nb<FMT, M, 1>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 2: launch_mma_nb<FMT, M, 2>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    default: launch_mma_nb<FMT, M, 4>(grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 1: launch_mma_nb<FMT, M, 1>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
+    case 2: launch_mma_nb<FMT, M, 2>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
+    default: launch_mma_nb<FMT, M, 4>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
   }
 }
 
@@ -990,14 +994,17 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
     dim3 grid((unsigned)((row_tiles(N) + nb - 1) / nb), split_k);
     dim3 block(64 * waves);
     switch (M) {
-      case 1: launch_mma<FMT, 1>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 2: launch_mma<FMT, 2>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 3: launch_mma<FMT, 3>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 4: launch_mma<FMT, 4>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 5: launch_mma<FMT, 5>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 6: launch_mma<FMT, 6>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      case 7: launch_mma<FMT, 7>(nb, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-      default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
+      case 1: launch_mma<FMT, 1>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 1, st); break;
+      case 2: launch_mma<FMT, 2>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 2, st); break;
+      case 3: launch_mma<FMT, 3>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 3, st); break;
+      case 4: launch_mma<FMT, 4>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 4, st); break;
+      case 5: launch_mma<FMT, 5>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 5, st); break;
+      case 6: launch_mma<FMT, 6>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 6, st); break;
+      case 7: launch_mma<FMT, 7>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 7, st); break;
+      default:
+        if (M > kMmaTokens) return fail(WQ_ERR_INVALID_ARG, "matrix-core GEMV: M must be in 1..16");
+        launch_mma<FMT, kMmaTokens>(nb, grid, block, qw, sc, zs, x, y, part, K, N, M, st);
+        break;
     }
   } else {
   dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
@@ -1033,7 +1040,7 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
 int gemv_max_waves(int fmt, int M, int rows) {
   if (rows & kGemvMfma) {
     const int rr = rows & ~kGemvMfma;
-    if (M < 1 || M > kGemvMaxM) return 0;
+    if (M < 1 || M > kMmaTokens) return 0;
     return (rr == 16 || rr == 32 || rr == 64) ? kMmaMaxWaves : 0;
   }
   const int rr = rows & ~kGemvPrefetch;

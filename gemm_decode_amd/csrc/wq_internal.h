@@ -13,6 +13,7 @@ namespace wq {
 constexpr int kGroup = 128;        // group size along K for the group-128 formats
 constexpr int kMaxSplit = 32;      // largest split_k of the tuning grid
 constexpr int kGemvMaxM = 7;       // tokens < 8 take the GEMV
+constexpr int kMmaTokens = 16;     // tokens the matrix-core GEMV kernel takes (the GEMM's few-token tiles)
 constexpr int kGemvTileRows = 16;    // output rows per GEMV workgroup tile (and per
                                      // gfx950 metadata tile of the group-128 formats)
 constexpr int kGemvMaxWaves = 16;    // waves per GEMV workgroup (intra-workgroup K split)
@@ -110,6 +111,14 @@ constexpr int kDma64Tile0 = 14, kDma64TileLast = 16;
 // GEMM tiles kDma128Tile0 .. kDma128TileLast: the same with 128-row x tiles (mid M on
 // narrow N, where 256-row tiles leave most CUs idle), split-K 1, 2, 4.
 constexpr int kDma128Tile0 = 17, kDma128TileLast = 19;
+// GEMM tiles kMmaTile0 .. kMmaTileLast: the matrix-core GEMV kernel for 8 ..
+// kMmaTokens tokens (its A operand holds 16 tokens, so it streams the weights as at one
+// token): 16 NB output rows per workgroup with NB = 1, 2, 4 (tiles 20, 21, 22) and NB = 1
+// with split-K 2 (tile 23; fp32 partials in the workspace, split 1 without room for
+// them).  More tokens take tile 14 (tile 2 when K % 64 != 0).
+constexpr int kMmaTile0 = 20, kMmaTileLast = 23;
+// split-K of a tile kMmaTile0 .. kMmaTileLast at M tokens (0: not such a tile, or M too large)
+int gemm_mma_split(int tile, int64_t M, int64_t K);
 // rows per x tile of the row-tiled LDS-DMA tiles 14..19 (0 for other tiles)
 inline int gemm_dma_rows(int tile) {
   return tile >= kDma64Tile0 && tile <= kDma64TileLast ? 64 : tile >= kDma128Tile0 && tile <= kDma128TileLast ? 128 : 0;

@@ -5,10 +5,10 @@
 // offsets[e] .. offsets[e + 1] - 1 (offsets on the device, so a routing computed there
 // needs no copy to the host).  One launch covers every expert:
 //
-//   grid (tile pairs, E), 4 waves: a workgroup takes expert blockIdx.y and two 16-row
+//   grid (tile pairs, E), 8 waves: a workgroup takes expert blockIdx.y and two 16-row
 //   weight tiles -- tiles 2 b and 2 b + 1, or, for the gated epilogue, gate tile b and
 //   the matching up tile b + I / 16 (N = 2 I: gate rows, then up rows) -- and walks the
-//   expert's rows in blocks of 16 tokens (the A rows of v_mfma_f32_16x16x32), its four
+//   expert's rows in blocks of 16 tokens (the A rows of v_mfma_f32_16x16x32), its
 //   waves interleaving over 128-k units; an expert without rows leaves at once.
 //
 // The arithmetic is the matrix-core decode GEMV's: codes become exact fp16 values (int8
@@ -38,7 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMoeWaves = 4;
+constexpr int kMoeWaves = 8;
 constexpr int kMoeTokens = 16;  // tokens per block (A rows of one matrix instruction)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -88,8 +88,9 @@ __device__ __forceinline__ void i8_word_to_bf16(uint32_t d, uint32_t& lo, uint32
   hi = pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24));
 }
 
-// grid (pairs, E); block 64 * kMoeWaves.  K % 128 == 0, N % 16 == 0 (and, gated, (N / 2) %
-// 16 == 0), checked on the host.  Offsets are clamped into [0, T] before use.
+// grid (pairs, E); block 64 W, W <= kMoeWaves, with W * 2 KiB of dynamic LDS for the
+// waves' sums.  K % 128 == 0, N % 16 == 0 (and, gated, (N / 2) % 16 == 0), checked on the
+// host.  Offsets are clamped into [0, T] before use.
 template <int FMT, bool GATED>
 __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __restrict__ qw0,
                                                             const uint16_t* __restrict__ sc0,
@@ -102,14 +103,14 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __re
   constexpr int kUnitBytes = kW4 ? 64 : 128;  // code bytes per row and 128-k unit
   constexpr int kUnitsPerSlice = kSliceBytes / kUnitBytes;
   constexpr int CL = kW4 ? 1 : 2;             // 16-byte code loads per lane, tile and unit
-  __shared__ float red[kMoeWaves][2][kMoeTokens][16];
+  extern __shared__ float red[];  // [W][2][kMoeTokens][16]
 
   const int e = blockIdx.y;
   const int t0 = min(max(offsets[e], 0), T);
   const int t1 = min(max(offsets[e + 1], t0), T);
   if (t1 <= t0) return;  // the whole workgroup leaves together
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ln = lane & 15, lk = lane >> 4;
   const int T16 = N / 16, G = K / kGroup, U = K / kGroup;
@@ -136,33 +137,44 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __re
   uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_a = 0x64006400u, mag_h = 0x54005400u;
   if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_a), "+v"(mag_h));
 
+  // one unit's operands: both tiles' codes, their group scales and zero bytes, and this
+  // lane's 32 x values
+  struct Set {
+    u32x4_t c[2][CL];
+    uint4 xv[4];
+    uint32_t sv[2], zb[2];
+  };
   for (int tb = t0; tb < t1; tb += kMoeTokens) {
     const int MT = min(kMoeTokens, t1 - tb);
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (size_t)(tb + min((int)ln, MT - 1)) * K);
     f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int u = wu; u < U; u += kMoeWaves) {
+    auto load = [&](Set& st, int u) {
       const uint32_t sl = (uint32_t)u / kUnitsPerSlice, ui = (uint32_t)u % kUnitsPerSlice;
       const uint32_t wsl = min((uint32_t)kSliceBytes, row_bytes - (uint32_t)kSliceBytes * sl);
-      u32x4_t c[2][CL];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int j = 0; j < CL; ++j)
-          c[t][j] = __builtin_bit_cast(
+          st.c[t][j] = __builtin_bit_cast(
               u32x4_t, load_stream16(tbase[t] + (size_t)16 * kSliceBytes * sl +
                                      (ln * wsl + kUnitBytes * ui + (kW4 ? 16u : 32u) * lk + 16u * j)));
-      uint32_t sv[2] = {0u, 0u}, zb[2] = {0u, 0u};
+      st.sv[0] = st.sv[1] = st.zb[0] = st.zb[1] = 0u;
       if constexpr (kGrouped) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          sv[t] = sbase[t][16 * u + ln];
-          if constexpr (kW4) zb[t] = zbase[t][8 * u + (ln >> 1)];
+          st.sv[t] = sbase[t][16 * u + ln];
+          if constexpr (kW4) st.zb[t] = zbase[t][8 * u + (ln >> 1)];
         }
       }
-      uint4 xv[4];
       const uint4* xp = reinterpret_cast<const uint4*>(xrow + 2u * (128u * (uint32_t)u + 32u * lk));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+      for (int j = 0; j < 4; ++j) st.xv[j] = xp[j];
+    };
+    auto compute = [&](const Set& st) {
+      const u32x4_t(&c)[2][CL] = st.c;
+      const uint32_t* sv = st.sv;
+      const uint32_t* zb = st.zb;
+      const uint4* xv = st.xv;
       F16Exact fx;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -260,21 +272,28 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __re
           acc[t] += d[t];
         }
       }
+    };
+    // units wu, wu + W, ...: each loads and multiplies in turn (a second operand set in
+    // flight doubles the registers and halves the resident waves: measured slower on
+    // MI355X, like 4 or 16 waves per workgroup)
+    for (int u = wu; u < U; u += W) {
+      Set st;
+      load(st, u);
+      compute(st);
     }
     // lane l holds D[token 4 (l / 16) + i][row l % 16] of both tiles
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][t][4 * lk + i][ln] = acc[t][i];
+      for (int i = 0; i < 4; ++i) red[((wave * 2 + t) * kMoeTokens + 4 * lk + i) * 16 + ln] = acc[t][i];
     __syncthreads();
     for (int o = threadIdx.x; o < (GATED ? 1 : 2) * kMoeTokens * 16; o += blockDim.x) {
       const int t = o / (kMoeTokens * 16), m = (o / 16) % kMoeTokens, r = o & 15;
       if (m >= MT) continue;
       float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMoeWaves; ++w) {
-        v0 += red[w][t][m][r];
-        if (GATED) v1 += red[w][1][m][r];
+      for (int w = 0; w < W; ++w) {
+        v0 += red[((w * 2 + t) * kMoeTokens + m) * 16 + r];
+        if (GATED) v1 += red[((w * 2 + 1) * kMoeTokens + m) * 16 + r];
       }
       const int n0 = 16 * tt[t] + r;
       if constexpr (GATED) {
@@ -296,10 +315,14 @@ template <int FMT>
 void launch_fmt(bool gated, dim3 grid, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, size_t qs,
                 size_t ss, size_t zst, const uint16_t* x, const int32_t* off, uint16_t* y, int T, int K, int N,
                 hipStream_t st) {
+  // eight waves (measured on MI355X against 4, 16 and about three units per wave, with
+  // and without a second operand set: 10-30 % faster at one or two tokens per expert)
+  const int W = kMoeWaves;
+  const size_t lds = (size_t)W * 2 * kMoeTokens * 16 * sizeof(float);
   if (gated)
-    moe_kernel<FMT, true><<<grid, 64 * kMoeWaves, 0, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
+    moe_kernel<FMT, true><<<grid, 64 * W, lds, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
   else
-    moe_kernel<FMT, false><<<grid, 64 * kMoeWaves, 0, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
+    moe_kernel<FMT, false><<<grid, 64 * W, lds, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
 }
 
 }  // namespace

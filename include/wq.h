@@ -268,10 +268,15 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      workspace; the default for 129..256 tokens; other shapes: tile 1;
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
- *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2.
+ *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2;
+ *   20..22  M <= 16: the matrix-core GEMV (WQ_GEMV_MFMA) with 16, 32 or 64 rows per
+ *      workgroup: its A operand holds 16 tokens, so 8..16 tokens stream the weights
+ *      at about the cost of one; 23: as 20 with split-K 2 (needs 2 * M * N * 4 bytes
+ *      of workspace, else WQ_ERR_WORKSPACE; with tile 0 and too small a workspace the
+ *      split drops to 1); M > 16: tile 14 (tile 2 when K % 64 != 0).
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 19
+#define WQ_GEMM_TILES 23
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -407,7 +412,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 19
+#define WQ_TUNE_LAT_SLOTS 23
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

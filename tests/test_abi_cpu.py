@@ -185,7 +185,7 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_gemv(C.byref(d4), x, 1, y, 1, None, 0, None) == 1           # W4 without zeros
     dsa = _desc(wqlib, fmt=1, s=0x2002)
     assert L.wq_gemv(C.byref(dsa), x, 1, y, 1, None, 0, None) == 3          # tiled scales misaligned
-    assert L.wq_gemm(C.byref(d), x, 16, y, 20, None, 0, None) == 1          # bad tile
+    assert L.wq_gemm(C.byref(d), x, 16, y, wqlib.GEMM_TILES + 1, None, 0, None) == 1  # bad tile
     d8 = _desc(wqlib, fmt=1, K=64)
     assert L.wq_gemv(C.byref(d8), x, 1, y, 1, None, 0, None) == 2           # g128 with K=64
     assert L.wq_pack(None, C.byref(dc), None) == 1

@@ -222,11 +222,12 @@ EDGE = [("w8pc", 16, 8), ("w4g128", 128, 8), ("w8g128", 128, 24), ("w8pc", 64, 1
 def test_edge_shapes_every_path(wq, fmt, K, N):
     """Boundary shapes on every path: minimum K and N, a short last 16-row tile, a lone
     row in it, a ragged 1 KB slice, DMA K steps that leave 1 or 2 steps after the
-    three-step loop, and M at the edges of the 16-, 32-, 128- and 256-row tiles."""
+    three-step loop, and M at the edges of the 16-, 32-, 128- and 256-row tiles (13: a
+    16-token A operand that is partly filled)."""
     W = synth.weight(96, K, N, synth.uses_outliers(fmt))
     g, can = quantize_on_gpu(wq, W, fmt)
     P = OQ.pack(fmt, W)
-    for M in (1, 5, 7, 8, 16, 17, 33, 64, 128, 129, 257):
+    for M in (1, 5, 7, 8, 13, 16, 17, 33, 64, 128, 129, 257):
         x = synth.activation(96, K, M)
         y_ref = OL.ref_linear(x, P)
         if M < 8:
@@ -535,13 +536,24 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     yg = torch.empty((64, N), dtype=torch.bfloat16, device=DEV)
     wsg = wq.workspace(wq.wq_workspace_size(g, 64))
     tile, lat = wq.wq_tune(copies, xg, yg, wsg, warmup=2, iters=3)
-    assert 1 <= tile <= wq.GEMM_TILES and all(v > 0 for v in lat), (tile, lat)
+    # every tile runs at M = 64 but the matrix-core GEMV tiles (at most 16 tokens): not run
+    assert 1 <= tile <= wq.GEMM_TILES and tile not in wq.MMA_TILES, (tile, lat)
+    assert all((v > 0) == (t not in wq.MMA_TILES) for t, v in enumerate(lat, 1)), lat
     assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
     # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
     split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16, 18, 19]  # the split-K tiles (skinny, LDS-DMA)
     assert tile not in split_tiles, (tile, lat)
-    assert all((v < 0) == (t in split_tiles) for t, v in enumerate(lat, start=1)), (tile, lat)
+    skipped = set(split_tiles) | set(wq.MMA_TILES)
+    assert all((v < 0) == (t in skipped) for t, v in enumerate(lat, start=1)), (tile, lat)
+    # at 12 tokens the matrix-core GEMV tiles run (tile 23, split-K 2, only with a workspace)
+    x12 = to_dev_bf16(synth.activation(102, K, 12))
+    y12 = torch.empty((12, N), dtype=torch.bfloat16, device=DEV)
+    ws12 = wq.workspace(wq.wq_workspace_size(g, 12))
+    tile, lat = wq.wq_tune(copies, x12, y12, ws12, warmup=2, iters=3)
+    assert all(lat[t - 1] > 0 for t in wq.MMA_TILES), lat
+    tile, lat = wq.wq_tune(copies, x12, y12, None, warmup=2, iters=3)
+    assert lat[22] < 0 and all(lat[t - 1] > 0 for t in (20, 21, 22)), lat
 
 
 def test_error_paths_on_device(wq):
