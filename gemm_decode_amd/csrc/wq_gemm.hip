@@ -1181,51 +1181,11 @@ constexpr int SK_XP = SK_STEP * 2 + 16;  // LDS pitch of one token's x slice, by
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// A compile-time pass selector: the fp16 pass (x from the row-scaled fp16 copy, exact
-// fp16 code values) or the exact bf16 pass.
-template <bool B>
-struct PassTag {
-  static constexpr bool value = B;
-};
-
-// fp16 pairs of exact code values: int8 bytes (0, 1) / (2, 3) of a word (stored u = q +
-// 128) by v_perm_b32 under the fp16 exponent byte 0x64 (1024 + u) and one packed add of
-// -1152; uint4 nibble pairs under the 1024.0 / 64.0 patterns and one packed add of
-// -(1024 + z) / -(64 + z).
-__device__ __forceinline__ uint32_t sk_add_f16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) + __builtin_bit_cast(f16x2_t, b));
-}
-__device__ __forceinline__ u32x4 sk_i8x8_to_f16(uint32_t w0, uint32_t w1) {
-  constexpr uint32_t kM1152 = 0xE480E480u;  // fp16 pair (-1152, -1152)
-  return u32x4{sk_add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), kM1152),
-               sk_add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), kM1152),
-               sk_add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), kM1152),
-               sk_add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), kM1152)};
-}
-// one gfx950 W4 word (nibbles q0 q2 q4 q6 q1 q3 q5 q7) -> q0 - z .. q7 - z in fp16 (the
-// order of w4_word_to_bf16); off_a / off_b: the fp16 pairs -(1024 + z) and -(64 + z)
-__device__ __forceinline__ u32x4 sk_w4_to_f16(uint32_t w, uint32_t off_a, uint32_t off_b) {
-  const uint32_t w8 = w >> 8;
-  return u32x4{sk_add_f16x2((w & 0x000F000Fu) | 0x64006400u, off_a), sk_add_f16x2((w & 0x00F000F0u) | 0x54005400u, off_b),
-               sk_add_f16x2((w8 & 0x000F000Fu) | 0x64006400u, off_a), sk_add_f16x2((w8 & 0x00F000F0u) | 0x54005400u, off_b)};
-}
-__device__ __forceinline__ floatx4 sk_mma(bool f16, u32x4 a, u32x4 b, floatx4 c) {
-  return f16 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0)
-             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// XH: xh holds x in fp16, row m scaled by 1 / xinv[m] (x_to_f16_rows_kernel; a row it
-// cannot hold exactly is NaN).  The kernel then runs its fp16 pass (exact fp16 code
-// values against xh); a workgroup whose sums come out non-finite runs again on exact
-// bf16 codes against bf16 x, so its results are the bf16 pass's.  Without XH only the
-// bf16 pass runs.
-template <int FMT, int TB, bool XH>
+template <int FMT, int TB>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restrict__ qw,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint8_t* __restrict__ zeros,
                                                            const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ xh,
-                                                           const float* __restrict__ xinv,
                                                            uint16_t* __restrict__ y, float* __restrict__ part,
                                                            int M, int K, int N, int S) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
@@ -1247,14 +1207,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 #pragma unroll
   for (int t = 0; t < RT; ++t) nrow[t] = min(n0 + wave * 32 + t * 16 + r16, N - 1);
 
-  // x staging: chunk c = tid + 256 j is token c / 16, elements 8 (c % 16) .. + 7 (bf16 x,
-  // or its fp16 copy on the fp16 pass)
-  auto xload = [&](const uint16_t* xsrc, u32x4* xr, int ks) {
+  // x staging: chunk c = tid + 256 j is token c / 16, bf16 elements 8 (c % 16) .. + 7.
+  auto xload = [&](u32x4* xr, int ks) {
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
       const int c = tid + 256 * j;
       const int m = min(c >> 4, M - 1);  // tokens past M feed only outputs never stored
-      xr[j] = *reinterpret_cast<const u32x4*>(xsrc + (size_t)m * K + ks * SK_STEP + (c & 15) * 8);
+      xr[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + ks * SK_STEP + (c & 15) * 8);
     }
   };
   auto xstore = [&](const u32x4* xr, int buf) {
@@ -1264,6 +1223,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
       *reinterpret_cast<u32x4*>(&xs[buf][(c >> 4) * SK_XP + (c & 15) * 16]) = xr[j];
     }
   };
+  uint4 cw[RT][CH];
   // W4: lane l loads row l % 16, chunk l / 16 (the fragment layout).  W8: lane l loads
   // row l / 8 + 8 j, chunk l % 8 -- whole 128-byte lines per instruction -- and the
   // chunks reach the fragment layout through the wave's own LDS area (transpose()).
@@ -1296,148 +1256,110 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
   };
 
   floatx4 acc[RT][TB];
-  // One pass over the K range.  Per-channel int8: codes of three K steps live in
-  // registers (a static ring: the loop is unrolled by three), so while step ks is
-  // multiplied the loads of steps ks + 1 and ks + 2 are in flight.  Group-128 formats:
-  // one step ahead (the deeper ring costs their 4-token-block variants half their
-  // occupancy; measured slower for uint4).  x goes through the LDS double buffer one step
-  // ahead.
-  auto run = [&](auto pass) {
-    constexpr bool F16 = decltype(pass)::value;
-    const uint16_t* xsrc = F16 ? xh : x;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Per-channel int8: codes of three K steps live in registers (a static ring: the loop
+  // is unrolled by three), so while step ks is multiplied the loads of steps ks + 1 and
+  // ks + 2 are in flight.  Group-128 formats: one step ahead (the deeper ring costs
+  // their 4-token-block variants half their occupancy; measured slower for uint4).  x
+  // goes through the LDS double buffer one step ahead.
+  constexpr int kAhead = FMT == WQ_FMT_W8_PC ? 2 : 1;
+  uint4 c1[RT][CH], c2[RT][CH];
+  auto load_codes = [&](uint4 (*c)[CH], int ks) {
+    const int kc = min(ks, ks1 - 1);  // past the range: reload the last step (harmless)
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kAhead = FMT == WQ_FMT_W8_PC ? 2 : 1;
-    uint4 cw[RT][CH], c1[RT][CH], c2[RT][CH];
-    auto load_codes = [&](uint4 (*c)[CH], int ks) {
-      const int kc = min(ks, ks1 - 1);  // past the range: reload the last step (harmless)
+      for (int j = 0; j < CH; ++j) c[t][j] = load_stream16(code_ptr(t, j, kc));
+  };
+  if (ks0 < ks1) {
+    u32x4 xr[XJ];
+    xload(xr, ks0);
+    load_codes(cw, ks0);
+    if constexpr (kAhead == 2) load_codes(c1, ks0 + 1);
+    xstore(xr, 0);
+    __syncthreads();
+  }
+  auto step = [&](uint4 (*cur)[CH], uint4 (*fut)[CH], int ks) {
+    const int buf = (ks - ks0) & 1;
+    const int kn = min(ks + 1, ks1 - 1);
+    u32x4 xr[XJ];
+    xload(xr, kn);
+    load_codes(fut, ks + kAhead);
+    const uint8_t* xb = xs[buf];
+    transpose(cur);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      floatx4 part_acc[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) part_acc[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
+      if constexpr (!kW4) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(cur[t][j]));
+          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(cur[t][j]));
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            const uint8_t* xrow = xb + (16 * b + r16) * SK_XP + 128 * j + 32 * c4;
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(xrow);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(xrow + 16);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, part_acc[b], 0, 0, 0);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1, part_acc[b], 0, 0, 0);
+          }
+        }
+      } else {
+        const int n = nrow[t];
+        const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
+        const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
+        const uint32_t wd[4] = {cur[t][0].x, cur[t][0].y, cur[t][0].z, cur[t][0].w};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, w4_word_to_bf16(wd[s2], z));
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xb + (16 * b + r16) * SK_XP + 64 * c4 + 16 * s2);
+            part_acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wv, part_acc[b], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (kGrouped) {
+        const float sc = gscale(nrow[t], ks);
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, part_acc[b][q], acc[t][b][q]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[t][b] = part_acc[b];
+      }
+    }
+    xstore(xr, buf ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
+  };
+  // ring: step ks multiplies the buffer loaded two steps earlier and loads ks + 2 into
+  // the one step ks - 1 has finished with
+  if constexpr (kAhead == 2) {
+    int ks = ks0;
+    for (; ks + 3 <= ks1; ks += 3) {
+      step(cw, c2, ks);
+      step(c1, cw, ks + 1);
+      step(c2, c1, ks + 2);
+    }
+    if (ks < ks1) step(cw, c2, ks);
+    if (ks + 1 < ks1) step(c1, cw, ks + 1);
+  } else {
+    for (int ks = ks0; ks < ks1; ++ks) {
+      step(cw, c1, ks);
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int j = 0; j < CH; ++j) c[t][j] = load_stream16(code_ptr(t, j, kc));
-    };
-    if (ks0 < ks1) {
-      u32x4 xr[XJ];
-      xload(xsrc, xr, ks0);
-      load_codes(cw, ks0);
-      if constexpr (kAhead == 2) load_codes(c1, ks0 + 1);
-      xstore(xr, 0);
-      __syncthreads();
+        for (int j = 0; j < CH; ++j) cw[t][j] = c1[t][j];
     }
-    auto step = [&](uint4 (*cur)[CH], uint4 (*fut)[CH], int ks) {
-      const int buf = (ks - ks0) & 1;
-      const int kn = min(ks + 1, ks1 - 1);
-      u32x4 xr[XJ];
-      xload(xsrc, xr, kn);
-      load_codes(fut, ks + kAhead);
-      const uint8_t* xb = xs[buf];
-      transpose(cur);
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        floatx4 part_acc[TB];
-#pragma unroll
-        for (int b = 0; b < TB; ++b) part_acc[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
-        if constexpr (!kW4) {
-#pragma unroll
-          for (int j = 0; j < CH; ++j) {
-            const uint4 cc = cur[t][j];
-            u32x4 w0, w1;
-            if constexpr (F16) {
-              w0 = sk_i8x8_to_f16(cc.x, cc.y);
-              w1 = sk_i8x8_to_f16(cc.z, cc.w);
-            } else {
-              const uint4 lo = i8x16_to_bf16_lo(cc), hi = i8x16_to_bf16_hi(cc);
-              w0 = u32x4{lo.x, lo.y, lo.z, lo.w};
-              w1 = u32x4{hi.x, hi.y, hi.z, hi.w};
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-              const uint8_t* xrow = xb + (16 * b + r16) * SK_XP + 128 * j + 32 * c4;
-              const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow);
-              const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16);
-              part_acc[b] = sk_mma(F16, a0, w0, part_acc[b]);
-              part_acc[b] = sk_mma(F16, a1, w1, part_acc[b]);
-            }
-          }
-        } else {
-          const int n = nrow[t];
-          const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
-          const uint32_t zi = (zb >> ((n & 1) * 4)) & 0xFu;
-          const float z = (float)zi;
-          const uint32_t off_a = 0xE400E400u + zi * 0x10001u, off_b = 0xD400D400u + zi * 0x100010u;
-          const uint32_t wd[4] = {cur[t][0].x, cur[t][0].y, cur[t][0].z, cur[t][0].w};
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) {
-            u32x4 wv;
-            if constexpr (F16) {
-              wv = sk_w4_to_f16(wd[s2], off_a, off_b);
-            } else {
-              const uint4 o = w4_word_to_bf16(wd[s2], z);
-              wv = u32x4{o.x, o.y, o.z, o.w};
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-              const u32x4 a = *reinterpret_cast<const u32x4*>(xb + (16 * b + r16) * SK_XP + 64 * c4 + 16 * s2);
-              part_acc[b] = sk_mma(F16, a, wv, part_acc[b]);
-            }
-          }
-        }
-        if constexpr (kGrouped) {
-          const float sc = gscale(nrow[t], ks);
-#pragma unroll
-          for (int b = 0; b < TB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, part_acc[b][q], acc[t][b][q]);
-        } else {
-#pragma unroll
-          for (int b = 0; b < TB; ++b) acc[t][b] = part_acc[b];
-        }
-      }
-      xstore(xr, buf ^ 1);  // that buffer was last read before the previous barrier
-      __syncthreads();
-    };
-    // ring: step ks multiplies the buffer loaded two steps earlier and loads ks + 2 into
-    // the one step ks - 1 has finished with
-    if constexpr (kAhead == 2) {
-      int ks = ks0;
-      for (; ks + 3 <= ks1; ks += 3) {
-        step(cw, c2, ks);
-        step(c1, cw, ks + 1);
-        step(c2, c1, ks + 2);
-      }
-      if (ks < ks1) step(cw, c2, ks);
-      if (ks + 1 < ks1) step(c1, cw, ks + 1);
-    } else {
-      for (int ks = ks0; ks < ks1; ++ks) {
-        step(cw, c1, ks);
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-          for (int j = 0; j < CH; ++j) cw[t][j] = c1[t][j];
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  bool scaled = false;  // the sums carry the row scales of the fp16 copy
-  if constexpr (XH) {
-    run(PassTag<true>{});
-    int bad = 0;
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bad |= !__builtin_isfinite(acc[t][b][q]);
-    scaled = true;
-    if (__syncthreads_or(bad)) {  // uniform over the workgroup
-      run(PassTag<false>{});
-      scaled = false;
-    }
-  } else {
-    run(PassTag<false>{});
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds D[token 4 c4 + q][weight row r16] of each 16 x 16 block
 #pragma unroll
@@ -1451,11 +1373,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
       for (int q = 0; q < 4; ++q) {
         const int m = 16 * b + 4 * c4 + q;
         if (m >= M) continue;
-        const float v = scaled ? acc[t][b][q] * xinv[m] : acc[t][b][q];  // the row's scale back out (exact)
         if (S == 1)
-          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
         else
-          part[((size_t)blockIdx.y * M + m) * N + n] = v;
+          part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
       }
   }
 }
@@ -1466,13 +1387,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 // current step's MFMAs run.  Same operand mapping, K order and epilogue as
 // gemm_skinny_kernel.  (With two token blocks each wave's x reads double and the LDS-
 // staged kernel wins.)
-template <int FMT, int TB, bool XH>
+template <int FMT, int TB>
 __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* __restrict__ qw,
                                                                   const uint16_t* __restrict__ scales,
                                                                   const uint8_t* __restrict__ zeros,
                                                                   const uint16_t* __restrict__ x,
-                                                                  const uint16_t* __restrict__ xh,
-                                                                  const float* __restrict__ xinv,
                                                                   uint16_t* __restrict__ y,
                                                                   float* __restrict__ part, int M, int K,
                                                                   int N, int S) {
@@ -1506,6 +1425,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
     tbase[t] = qw + (size_t)ti * kGemvTileRows * row_bytes;
     trow[t] = min(r16, tnr[t] - 1);
   }
+  const uint16_t* xrow[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) xrow[b] = x + (size_t)min(16 * b + r16, M - 1) * K;
   // k offset (elements) of x fragment i within a step: W8 i = 2 j + s -> 64 j + 16 c + 8 s;
   // W4 i = s -> 32 c + 8 s.
   auto xoff = [&](int i) { return kW4 ? 32 * c4 + 8 * i : 64 * (i >> 1) + 16 * c4 + 8 * (i & 1); };
@@ -1537,146 +1459,108 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
         }
     }
   };
+  auto load_x = [&](bf16x8_t (*dst)[NX], int ks) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int i = 0; i < NX; ++i) dst[b][i] = *reinterpret_cast<const bf16x8_t*>(xrow[b] + ks * SK_STEP + xoff(i));
+  };
   auto gscale = [&](int n, int g) -> float {
     const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
     return (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
   };
 
   floatx4 acc[RT][TB];
-  // One pass over the K range (bf16 x and codes, or the fp16 copy of x and fp16 codes).
-  auto run = [&](auto pass) {
-    constexpr bool F16 = decltype(pass)::value;
-    const uint16_t* xrow[TB];
 #pragma unroll
-    for (int b = 0; b < TB; ++b) xrow[b] = (F16 ? xh : x) + (size_t)min(16 * b + r16, M - 1) * K;
-    auto load_x = [&](u32x4 (*dst)[NX], int ks) {
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int b = 0; b < TB; ++b)
+    for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Three register sets with fixed roles, so no set is copied (a copy would wait for
+  // its loads): while set s is multiplied, the sets for the next two steps are in
+  // flight.
+  auto step = [&](const u32x4 (*ld)[CH], const bf16x8_t (*xf_)[NX], int ks) {
+    u32x4 cw_[RT][CH];
+    if constexpr (kW4) {
 #pragma unroll
-        for (int i = 0; i < NX; ++i) dst[b][i] = *reinterpret_cast<const u32x4*>(xrow[b] + ks * SK_STEP + xoff(i));
-    };
+      for (int t = 0; t < RT; ++t) cw_[t][0] = ld[t][0];
+    } else {
+      // row-major [row][128 bytes] (pitch kTrPitch) -> lane l gets row l % 16, chunk
+      // 4 j + l / 16.  One wave's own region: LDS keeps a wave's accesses in order.
+      uint8_t* tw = trs[wave];
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int b = 0; b < TB; ++b) acc[t][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // Three register sets with fixed roles, so no set is copied (a copy would wait for
-    // its loads): while set s is multiplied, the sets for the next two steps are in
-    // flight.
-    auto step = [&](const u32x4 (*ld)[CH], const u32x4 (*xf_)[NX], int ks) {
-      u32x4 cw_[RT][CH];
-      if constexpr (kW4) {
+        for (int i = 0; i < CH; ++i)
+          *reinterpret_cast<u32x4*>(tw + (t * 16 + (lane >> 3) + 8 * i) * kTrPitch + 16 * (lane & 7)) = ld[t][i];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) cw_[t][0] = ld[t][0];
-      } else {
-        // row-major [row][128 bytes] (pitch kTrPitch) -> lane l gets row l % 16, chunk
-        // 4 j + l / 16.  One wave's own region: LDS keeps a wave's accesses in order.
-        uint8_t* tw = trs[wave];
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int j = 0; j < CH; ++j)
+          cw_[t][j] = *reinterpret_cast<const u32x4*>(tw + (t * 16 + r16) * kTrPitch + 16 * (4 * j + c4));
+    }
 #pragma unroll
-          for (int i = 0; i < CH; ++i)
-            *reinterpret_cast<u32x4*>(tw + (t * 16 + (lane >> 3) + 8 * i) * kTrPitch + 16 * (lane & 7)) = ld[t][i];
+    for (int t = 0; t < RT; ++t) {
+      floatx4 pa[TB];
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+      for (int b = 0; b < TB; ++b) pa[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
+      if constexpr (!kW4) {
 #pragma unroll
-          for (int j = 0; j < CH; ++j)
-            cw_[t][j] = *reinterpret_cast<const u32x4*>(tw + (t * 16 + r16) * kTrPitch + 16 * (4 * j + c4));
-      }
+        for (int j = 0; j < CH; ++j) {
+          const uint4 c = make_uint4(cw_[t][j].x, cw_[t][j].y, cw_[t][j].z, cw_[t][j].w);
+          const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(c));
+          const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(c));
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        floatx4 pa[TB];
-#pragma unroll
-        for (int b = 0; b < TB; ++b) pa[b] = kGrouped ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[t][b];
-        if constexpr (!kW4) {
-#pragma unroll
-          for (int j = 0; j < CH; ++j) {
-            u32x4 w0, w1;
-            if constexpr (F16) {
-              w0 = sk_i8x8_to_f16(cw_[t][j].x, cw_[t][j].y);
-              w1 = sk_i8x8_to_f16(cw_[t][j].z, cw_[t][j].w);
-            } else {
-              const uint4 c = make_uint4(cw_[t][j].x, cw_[t][j].y, cw_[t][j].z, cw_[t][j].w);
-              const uint4 lo = i8x16_to_bf16_lo(c), hi = i8x16_to_bf16_hi(c);
-              w0 = u32x4{lo.x, lo.y, lo.z, lo.w};
-              w1 = u32x4{hi.x, hi.y, hi.z, hi.w};
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-              pa[b] = sk_mma(F16, xf_[b][2 * j], w0, pa[b]);
-              pa[b] = sk_mma(F16, xf_[b][2 * j + 1], w1, pa[b]);
-            }
-          }
-        } else {
-          const int n = nrow[t];
-          const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
-          const uint32_t zi = (zb >> ((n & 1) * 4)) & 0xFu;
-          const float z = (float)zi;
-          const uint32_t off_a = 0xE400E400u + zi * 0x10001u, off_b = 0xD400D400u + zi * 0x100010u;
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) {
-            u32x4 wv;
-            if constexpr (F16) {
-              wv = sk_w4_to_f16(cw_[t][0][s2], off_a, off_b);
-            } else {
-              const uint4 o = w4_word_to_bf16(cw_[t][0][s2], z);
-              wv = u32x4{o.x, o.y, o.z, o.w};
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) pa[b] = sk_mma(F16, xf_[b][s2], wv, pa[b]);
+          for (int b = 0; b < TB; ++b) {
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][2 * j], w0, pa[b], 0, 0, 0);
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][2 * j + 1], w1, pa[b], 0, 0, 0);
           }
         }
-        if constexpr (kGrouped) {
-          const float sc = gscale(nrow[t], ks);
+      } else {
+        const int n = nrow[t];
+        const uint8_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + ks) * kGemvTileRows + n % kGemvTileRows) / 2];
+        const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, w4_word_to_bf16(cw_[t][0][s2], z));
 #pragma unroll
           for (int b = 0; b < TB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, pa[b][q], acc[t][b][q]);
-        } else {
-#pragma unroll
-          for (int b = 0; b < TB; ++b) acc[t][b] = pa[b];
+            pa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf_[b][s2], wv, pa[b], 0, 0, 0);
         }
       }
-    };
-    u32x4 ca[RT][CH], cb[RT][CH], cc[RT][CH];
-    u32x4 xa[TB][NX], xb[TB][NX], xc[TB][NX];
-    auto last = [&](int k) { return min(k, ks1 - 1); };  // past the end: reload the last step
-    if (ks0 < ks1) {
-      load_codes(ca, ks0);
-      load_x(xa, ks0);
-      load_codes(cb, last(ks0 + 1));
-      load_x(xb, last(ks0 + 1));
-    }
-    for (int ks = ks0; ks < ks1; ks += 3) {
-      load_codes(cc, last(ks + 2));
-      load_x(xc, last(ks + 2));
-      step(ca, xa, ks);
-      if (ks + 1 >= ks1) break;
-      load_codes(ca, last(ks + 3));
-      load_x(xa, last(ks + 3));
-      step(cb, xb, ks + 1);
-      if (ks + 2 >= ks1) break;
-      load_codes(cb, last(ks + 4));
-      load_x(xb, last(ks + 4));
-      step(cc, xc, ks + 2);
+      if constexpr (kGrouped) {
+        const float sc = gscale(nrow[t], ks);
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(sc, pa[b][q], acc[t][b][q]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[t][b] = pa[b];
+      }
     }
   };
-  bool scaled = false;  // the sums carry the row scales of the fp16 copy
-  if constexpr (XH) {
-    run(PassTag<true>{});
-    int bad = 0;
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bad |= !__builtin_isfinite(acc[t][b][q]);
-    scaled = true;
-    if (__syncthreads_or(bad)) {  // uniform over the workgroup
-      run(PassTag<false>{});
-      scaled = false;
-    }
-  } else {
-    run(PassTag<false>{});
+  u32x4 ca[RT][CH], cb[RT][CH], cc[RT][CH];
+  bf16x8_t xa[TB][NX], xb[TB][NX], xc[TB][NX];
+  auto last = [&](int k) { return min(k, ks1 - 1); };  // past the end: reload the last step
+  if (ks0 < ks1) {
+    load_codes(ca, ks0);
+    load_x(xa, ks0);
+    load_codes(cb, last(ks0 + 1));
+    load_x(xb, last(ks0 + 1));
+  }
+  for (int ks = ks0; ks < ks1; ks += 3) {
+    load_codes(cc, last(ks + 2));
+    load_x(xc, last(ks + 2));
+    step(ca, xa, ks);
+    if (ks + 1 >= ks1) break;
+    load_codes(ca, last(ks + 3));
+    load_x(xa, last(ks + 3));
+    step(cb, xb, ks + 1);
+    if (ks + 2 >= ks1) break;
+    load_codes(cb, last(ks + 4));
+    load_x(xb, last(ks + 4));
+    step(cc, xc, ks + 2);
   }
 
 #pragma unroll
@@ -1690,11 +1574,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
       for (int q = 0; q < 4; ++q) {
         const int m = 16 * b + 4 * c4 + q;
         if (m >= M) continue;
-        const float v = scaled ? acc[t][b][q] * xinv[m] : acc[t][b][q];  // the row's scale back out (exact)
         if (S == 1)
-          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
         else
-          part[((size_t)blockIdx.y * M + m) * N + n] = v;
+          part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
       }
   }
 }
@@ -1753,22 +1636,19 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __re
 
 template <int FMT>
 wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, const uint16_t* x,
-                        const uint16_t* xh, const float* xinv, uint16_t* y, float* part, int M, int K, int N, int S,
-                        hipStream_t st) {
+                        uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st) {
   const dim3 grid((unsigned)((N + SK_ROWS - 1) / SK_ROWS), (unsigned)S);
   const int TB = (M + 15) / 16;
   // one token block: the direct kernel; two: x through LDS as well (measured at M = 32:
   // 39 us against 57 us for per-channel W8 at (5120, 27648), 53 against 74 for W4)
-#define WQ_SKINNY(KERNEL, TBV)                                                                        \
-  do {                                                                                               \
-    if (xh) KERNEL<FMT, TBV, true><<<grid, 256, 0, st>>>(qw, sc, zs, x, xh, xinv, y, part, M, K, N, S); \
-    else KERNEL<FMT, TBV, false><<<grid, 256, 0, st>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, S); \
-  } while (0)
-  if (TB <= 1) WQ_SKINNY(gemm_skinny_direct_kernel, 1);
-  else if (TB <= 2) WQ_SKINNY(gemm_skinny_kernel, 2);
-  else if (TB <= 4) WQ_SKINNY(gemm_skinny_kernel, 4);
-  else WQ_SKINNY(gemm_skinny_kernel, 8);
-#undef WQ_SKINNY
+  if (TB <= 1)
+    gemm_skinny_direct_kernel<FMT, 1><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else if (TB <= 2)
+    gemm_skinny_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else if (TB <= 4)
+    gemm_skinny_kernel<FMT, 4><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+  else
+    gemm_skinny_kernel<FMT, 8><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
   WQ_HIP_CHECK(hipGetLastError());
   if (S > 1) {
     const int64_t MN = (int64_t)M * N;
@@ -1861,10 +1741,8 @@ static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
   const size_t need = gemm_workspace_bytes(fmt, N, M, tile);
-  // the fp16 copy of x: the skinny tiles (every format) and the group-128 LDS-DMA tiles
-  const bool skinny = tile >= kSkinnyTile0 && tile <= kSkinnyTileLast && M <= kSkinnyMaxM && K % SK_STEP == 0;
-  const bool g128_dma = fmt != WQ_FMT_W8_PC && tile >= 9 && tile < kMmaTile0 && K % DBK == 0;
-  if (!(skinny || g128_dma) || M * K >= (int64_t(1) << 31)) return need;
+  if (fmt == WQ_FMT_W8_PC || tile < 9 || tile >= kMmaTile0 || K % DBK != 0 || M * K >= (int64_t(1) << 31))
+    return need;
   return round256(round256(need) + (size_t)M * (size_t)K * 2) + (size_t)M * sizeof(float);
 }
 
@@ -1904,16 +1782,10 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     if (S > 0 && K % SK_STEP == 0 && (int64_t)M * K < (int64_t(1) << 31)) {
       if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;  // no room for partials
       float* part = (float*)ws;
-      // x in fp16 (rows scaled) after the partials when the workspace has room for it
-      uint16_t* xh = nullptr;
-      float* xinv = nullptr;
-      WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh, &xinv, s));
       switch (w->fmt) {
-        case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, S, s);
-        case WQ_FMT_W8_G128:
-          return launch_skinny<WQ_FMT_W8_G128>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, S, s);
-        case WQ_FMT_W4_G128:
-          return launch_skinny<WQ_FMT_W4_G128>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W8_G128: return launch_skinny<WQ_FMT_W8_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W4_G128: return launch_skinny<WQ_FMT_W4_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
         default: return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");
       }
     }

@@ -161,13 +161,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * 128; split <= 16, split * M <= 1024, at most 2048 workgroups) and the split-K
  * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB) -- or the
  * partials of tile 13's split last round (sized for the current device's CU count, 256
- * when none is visible); 0 when no split applies.  The skinny tiles 5..8 (every
- * format, M <= 128) and, for the group-128 formats, the LDS-DMA tiles 9..19 also use M *
- * K * 2 bytes after the partials (at a 256-byte boundary) for x converted to fp16 once
- * per call (each row scaled by a power of two so that it converts exactly), then M * 4
- * bytes (at a 256-byte boundary) for the row scales; given less, the skinny tiles
- * multiply bf16 codes by bf16 x and the LDS-DMA tiles convert x inside every workgroup,
- * unscaled (slower, and much slower where x holds values fp16 cannot hold exactly, such
+ * when none is visible); 0 when no split applies.  For the group-128 formats the
+ * LDS-DMA tiles 9..19 also use M * K * 2 bytes after the partials (at a 256-byte
+ * boundary) for x converted to fp16 once per call (each row scaled by a power of two
+ * so that it converts exactly), then M * 4 bytes (at a 256-byte boundary) for the row
+ * scales; given less, they convert x inside every workgroup instead, unscaled (same
+ * results; slower, and much slower where x holds values fp16 cannot hold exactly, such
  * as magnitudes below 2^-17), so that part is never required.
  * The contents are scratch: no initialisation is needed and nothing is kept between
  * calls.  Calls that share a workspace must not run concurrently. */
@@ -269,10 +268,7 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      workspace; the default for 129..256 tokens; other shapes: tile 1;
  *   5..8  M <= 128, K % 128 == 0: the skinny kernel with split-K 2, 4, 8, 16 (capped
  *      as in wq_workspace_size; needs that workspace, else WQ_ERR_WORKSPACE; with
- *      tile 0 and too small a workspace the split drops to 1): fp16 code values against
- *      the fp16 copy of x when the workspace holds it, and a workgroup whose sums come
- *      out non-finite (a row the copy cannot hold) recomputes on bf16 codes against bf16
- *      x; other shapes: tile 2;
+ *      tile 0 and too small a workspace the split drops to 1); other shapes: tile 2;
  *   20..22  M <= 16: the matrix-core GEMV (WQ_GEMV_MFMA) with 16, 32 or 64 rows per
  *      workgroup: its A operand holds 16 tokens, so 8..16 tokens stream the weights
  *      at about the cost of one; 23: as 20 with split-K 2 (needs 2 * M * N * 4 bytes

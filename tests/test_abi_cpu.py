@@ -198,15 +198,10 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_workspace_size(C.byref(d), 1, C.byref(n)) == 0 and n.value == 32 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 7, C.byref(n)) == 0 and n.value == 32 * 7 * 1024 * 4
     # M >= 8: split-K partials -- the skinny GEMM (split <= 16, split * M <= 1024, M <= 128)
-    # and the LDS-DMA tile (split <= 8, at most 512 workgroups of 256 x 256, <= 256 MiB);
-    # up to 128 tokens the skinny tiles also take x in fp16 (M x K x 2 after the partials,
-    # at a 256-byte boundary) and the M row scales (fp32, at a 256-byte boundary)
-    def with_x(M, part, K=1024):
-        r256 = lambda b: (b + 255) // 256 * 256
-        return r256(r256(part) + M * K * 2) + M * 4
-    assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == with_x(8, 16 * 8 * 1024 * 4)
-    assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == with_x(64, 16 * 64 * 1024 * 4)
-    assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == with_x(128, 8 * 128 * 1024 * 4)
+    # and the LDS-DMA tile (split <= 8, at most 512 workgroups of 256 x 256, <= 256 MiB)
+    assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 16 * 8 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == 16 * 64 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 8 * 128 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 8 * 129 * 1024 * 4
     big = _desc(wqlib, K=5120, N=27648)
     assert L.wq_workspace_size(C.byref(big), 512, C.byref(n)) == 0 and n.value == 2 * 512 * 27648 * 4

@@ -319,35 +319,6 @@ def test_gemm_fp16_activations_fall_back_to_exact(wq, fmt):
 
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
-def test_skinny_fp16_pass_and_its_fallbacks(wq, fmt):
-    """The skinny tiles (5..8) multiply fp16 code values by an fp16 copy of x, each row
-    scaled by a power of two; a row the copy cannot hold (3e5 and 1e-7 together: a
-    spread beyond 2^31) sends its workgroups to the exact bf16 pass, while a tiny value
-    in an ordinary row is scaled up with its row and stays on the fp16 pass.  The tuned
-    tile without a workspace runs unsplit on the bf16 pass alone.  One (13), three (40)
-    and seven (100) 16-token blocks."""
-    K, N = 1024, 520
-    W = synth.weight(106, K, N, synth.uses_outliers(fmt))
-    g, can = quantize_on_gpu(wq, W, fmt)
-    P = OQ.pack(fmt, W)
-    for M in (13, 40, 100):
-        xf = OQ.bf16_bits_to_f32(synth.activation(106, K, M)).copy()
-        for case in ("plain", "wide-row", "tiny-x"):
-            if case == "wide-row":
-                xf[3, 10] = 3.0e5
-                xf[3, 11] = 1.0e-7
-            if case == "tiny-x":
-                xf[M - 1, 5] = 3.0e-7
-            x = OQ.bf16_rne_bits(xf.astype(np.float32))
-            y_ref = OL.ref_linear(x, P)
-            for tile in (5, 6, 7, 8):
-                assert_parity(_run_gemm(wq, g, x, tile), y_ref, f"{fmt} M={M} {case} tile={tile}")
-                wq.wq_tune_cache_set(fmt, K, N, M, wq.KIND_GEMM, tile)
-                assert_parity(_run_gemm(wq, g, x, 0, with_ws=False), y_ref,
-                              f"{fmt} M={M} {case} tile={tile} without a workspace")
-
-
-@pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_zero_and_power_of_two_scaling(wq, fmt):
     """x = 0 gives y = 0; x * 4 gives y * 4 bit-exactly.  The scaling invariant
     holds when no intermediate is subnormal, so x is kept at |x| >= 2^-8 (the int8
