@@ -348,6 +348,107 @@ def profile_prefill(calls: int = 10):
         torch.cuda.empty_cache()
 
 
+# Few-token GEMM rows for rocprofv3 (fmt, K, N, M, tile): the tiles the tuner picks on
+# MI355X at 8 and 64 tokens on the widest decode shape.
+FEWTOKEN_PROFILE = [("w4g128", 5120, 27648, 8, 22), ("w4g128", 5120, 27648, 64, 15),
+                    ("w8pc", 5120, 27648, 8, 5), ("w8pc", 5120, 27648, 64, 15)]
+
+
+def profile_fewtoken(calls: int = 10):
+    """Kernels for a rocprofv3 run of the few-token GEMM: the elementwise reference (the
+    FETCH_SIZE / WRITE_SIZE scale), then for each row of FEWTOKEN_PROFILE `calls`
+    wq_linear calls on rotating weight copies with the tile fixed, as one HIP graph
+    replayed once (after its 2 eager warm-up calls), between a small torch.neg and a
+    small torch.abs dispatch (the row's bounds for summarize_fewtoken)."""
+    import torch
+    import gemm_decode_amd.wq as wq
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.bitwise_not(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    mark = torch.zeros(64, device="cuda")
+    for fmt, K, N, M, tile in FEWTOKEN_PROFILE:
+        p = Pool(wq, torch, 5, fmt, K, N, M)
+        wq.wq_tune_cache_set(fmt, K, N, M, wq.KIND_GEMM, tile)
+        streaming_settle(torch, 2.0)
+        torch.neg(mark, out=mark)
+        torch.cuda.synchronize()
+        ms = time_graph(torch, lambda: p.call(wq), calls, reps=1, settle_s=0.0)
+        torch.abs(mark, out=mark)
+        torch.cuda.synchronize()
+        log(f"profile few-token {fmt} K={K} N={N} M={M} tile={tile}: {ms * 1e3 / calls:.1f} us per call (HIP events)")
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+
+
+def summarize_fewtoken(trace_dir: str, fetch_dir: str, write_dir: str, out_txt: str):
+    """Per row of FEWTOKEN_PROFILE (the dispatches between torch.neg separators): each
+    kernel's dispatch count, mean duration (kernel trace), and median FETCH_SIZE /
+    WRITE_SIZE per dispatch scaled by the elementwise reference; the call's bytes against
+    the algorithmic bytes."""
+    import glob
+
+    def stream(d, pattern):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            rows += _read_csv_rows(f)
+        return sorted(rows, key=lambda r: int(r.get("Dispatch_Id", 0)))
+
+    def short(name):
+        return name.replace("void ", "").replace("wq::(anonymous namespace)::", "").split("(")[0]
+
+    def by_row(rows):
+        out, cur = [], None
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "neg_kernel" in name:
+                cur = {}
+                out.append(cur)
+            elif "AbsFunctor" in name or "abs_kernel" in name:
+                cur = None
+            elif cur is not None:
+                cur.setdefault(short(name), []).append(r)
+        return out
+
+    trace = by_row(stream(trace_dir, "*kernel_trace.csv"))
+    if len(trace) != len(FEWTOKEN_PROFILE):
+        raise SystemExit(f"found {len(trace)} row separators in the trace (full kernel names needed: no -T)")
+    scale = {}
+    counters = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in stream(d, "*counter_collection.csv") if r["Counter_Name"] == counter]
+        ref = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
+        if not ref:
+            raise SystemExit("reference kernel counters missing")
+        scale[counter] = COPY_BYTES / float(np.median(ref))  # bytes per counter unit
+        counters[counter] = by_row(rows)
+    lines = []
+    for i, (fmt, K, N, M, tile) in enumerate(FEWTOKEN_PROFILE):
+        alg = algorithmic_bytes(fmt, K, N, M)
+        parts, tot_b, tot_t = [], 0.0, 0.0
+        for name, rs in trace[i].items():
+            if len(rs) < 10:  # not one of the call's kernels (the graph holds 10 calls)
+                continue
+            us = float(np.mean([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]))
+            fb = float(np.median([float(r["Counter_Value"]) for r in counters["FETCH_SIZE"][i].get(name, [])] or [0])) * scale["FETCH_SIZE"]
+            wb = float(np.median([float(r["Counter_Value"]) for r in counters["WRITE_SIZE"][i].get(name, [])] or [0])) * scale["WRITE_SIZE"]
+            parts.append(f"{name}: {len(rs)} dispatches, {us:.2f} us mean, FETCH {fb/1e6:.2f} MB + WRITE {wb/1e6:.2f} MB")
+            tot_b += fb + wb
+            tot_t += us
+        lines.append(f"{fmt} K={K} N={N} M={M} tile={tile}: " + "; ".join(parts) +
+                     f"; per call {tot_t:.2f} us of kernel time, {tot_b/1e6:.1f} MB = {tot_b/alg:.3f} x algorithmic "
+                     f"{alg/1e6:.1f} MB -> {alg/tot_t/1e3:.0f} GB/s ({alg/tot_t/1e3/HBM_PEAK_GBS*100:.1f} % of 8 TB/s)")
+    for f in ("wq_gemm.hip", "wq_gemv.hip"):
+        src = open(os.path.join(ROOT, "gemm_decode_amd", "csrc", f), "rb").read()
+        lines.append(f"kernel source: gemm_decode_amd/csrc/{f} sha256 {hashlib.sha256(src).hexdigest()}")
+    with open(out_txt, "a") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # (K, N) -> (split_k, waves, rows): the launches the tuner picks for the W4 decode shapes
 PROFILE_W4 = {(5120, 27648): (1, 4, 16 | 0x200), (13824, 5120): (1, 4, 4)}
 
@@ -511,16 +612,16 @@ def summarize_prefill_traffic(fetch_dir: str, write_dir: str, out_txt: str):
             if not any(k in name for k in ("gemm_dma", "tail_reduce", "x_to_f16")):
                 continue
             # the per-channel kernels: the w8pc GEMM and tail_reduce<true>
-            pc = "w8pc_kernel" in name or "tail_reduce_kernel<true>" in name
+            pc = "w8pc_kernel" in name or "tail_reduce_kernel<true" in name
             kern = next(k for k in ("gemm_dma_w8pc_kernel", "gemm_dma_g128_kernel", "gemm_tail_reduce_kernel",
-                                    "x_to_f16_kernel") if k in name)
+                                    "x_to_f16_rows_kernel") if k in name)
             res.setdefault(("w8pc" if pc else "w4g128", kern, counter), []).append(float(r["Counter_Value"]) * scale)
     lines = []
     for fmt, K, N, M, tile in PREFILL_PROFILE:
         alg = algorithmic_bytes(fmt, K, N, M)
         main = "gemm_dma_w8pc_kernel" if fmt == "w8pc" else "gemm_dma_g128_kernel"
         per_call = {}
-        for kern in (main, "gemm_tail_reduce_kernel", "x_to_f16_kernel"):
+        for kern in (main, "gemm_tail_reduce_kernel", "x_to_f16_rows_kernel"):
             f = res.get((fmt, kern, "FETCH_SIZE"))
             w = res.get((fmt, kern, "WRITE_SIZE"))
             if f and w:
@@ -529,6 +630,8 @@ def summarize_prefill_traffic(fetch_dir: str, write_dir: str, out_txt: str):
         parts = "; ".join(f"{k}: FETCH {f/1e6:.1f} MB + WRITE {w/1e6:.1f} MB" for k, (f, w) in per_call.items())
         lines.append(f"{fmt} K={K} N={N} M={M} tile={tile}: {parts}; call total {tot/1e6:.1f} MB = "
                      f"{tot/alg:.3f} x algorithmic {alg/1e6:.1f} MB")
+    src = open(os.path.join(ROOT, "gemm_decode_amd", "csrc", "wq_gemm.hip"), "rb").read()
+    lines.append(f"kernel source: gemm_decode_amd/csrc/wq_gemm.hip sha256 {hashlib.sha256(src).hexdigest()}")
     with open(out_txt, "a") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -591,6 +694,9 @@ def main():
     ap.add_argument("--summarize-prefill-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_TXT"),
                     help="turn two rocprofv3 --pmc runs of --profile-prefill into HBM bytes per GEMM call")
     ap.add_argument("--profile-w4", action="store_true", help="kernels for rocprofv3: the W4 decode GEMV")
+    ap.add_argument("--profile-fewtoken", action="store_true", help="kernels for rocprofv3: the few-token GEMM rows")
+    ap.add_argument("--summarize-fewtoken", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_TXT"),
+                    help="per-row kernel time and HBM bytes of a --profile-fewtoken run")
     ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_DIR", "OUT_TXT"),
                     help="turn a rocprofv3 SQ counter pass of --profile-w4 into VALU figures")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_TXT"),
@@ -604,11 +710,17 @@ def main():
     if args.profile_w4:
         profile_w4()
         return
+    if args.profile_fewtoken:
+        profile_fewtoken()
+        return
     if args.summarize_valu:
         summarize_valu(*args.summarize_valu)
         return
     if args.summarize_prefill_traffic:
         summarize_prefill_traffic(*args.summarize_prefill_traffic)
+        return
+    if args.summarize_fewtoken:
+        summarize_fewtoken(*args.summarize_fewtoken)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)

@@ -129,10 +129,10 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 
 // Untuned GEMM tile: up to 16 tokens the matrix-core GEMV tiles (uint4, and int8 on the
 // smaller shapes) or the skinny kernel, with the smallest split-K that gives about two
-// workgroups per CU; 17..128 tokens the 64-row LDS-DMA tiles (14..16);
-// above that the 8-wave LDS-DMA kernel
-// (tile 9) for every format, split over K (tiles 10..12) when its tiles would not
-// occupy half the CUs, or with its partial last round split over K (tile 13).
+// workgroups per CU; 17..128 tokens the 64-row LDS-DMA tiles (14..16); 129..256 the
+// 128-row ones (17..19); above that the 8-wave LDS-DMA kernel (tile 9) for every format,
+// split over K (tiles 10..12, 24) when its tiles are fewer than the CUs, or with its
+// partial last round split over K (tile 13).
 int default_tile(const wq_weight* w, int64_t M) {
   if (M > 16 && M <= kSkinnyMaxM && w->K % 64 == 0) {
     // 64-row LDS-DMA tiles: the smallest split-K that gives at least 200 workgroups
@@ -170,22 +170,32 @@ int default_tile(const wq_weight* w, int64_t M) {
       ++t;
     return t;
   }
-  // fewer tiles (256 x 256 for per-channel W8, 128 x 256 for group-128) than half the
-  // CUs: the smallest split-K that gives at least that many workgroups (measured on
-  // MI355X: at M = 512, N = 5120 split 4 beats 8, and 160 tiles run best unsplit)
+  // fewer tiles (256 x 256 for per-channel W8, 128 x 256 for group-128) than CUs: the
+  // split-K (2, 3, 4 or 8; tiles 10, 24, 11, 12) whose rounds of workgroups per unit of
+  // work are fewest, ties to the smaller split (measured on MI355X at N = 5120: 40 tiles
+  // run best split 4, 80 and 160 group-128 tiles split 3 -- 107 against 139 us and 207
+  // against 239 us for uint4 at M = 512 and 1024 -- and 80 per-channel tiles split 3)
   const int64_t tm = gemm_big_dma_rows(w->fmt);
   const int64_t blocks = ((M + tm - 1) / tm) * ((w->N + 255) / 256);
-  if (blocks >= 128) {
-    // a partial last round of tiles that would leave at least half the CUs idle: tile 13
-    // spreads it over K (it needs a workspace; without one it runs as tile 9)
-    int tail0 = 0;
-    return gemm_dma_tail(w->fmt, M, w->N, &tail0) > 1 ? kDmaTailTile : kDefaultTile;
+  const int64_t cus = device_cus();
+  if (blocks < cus) {
+    int best_t = kDefaultTile;
+    double best = 1.0;  // unsplit: one round
+    for (const int t : {kDmaSplitTile0, kDmaSplit3Tile, kDmaSplitTile0 + 1, kDmaSplitTileLast}) {
+      const int S = gemm_dma_split(w->fmt, t, M, w->N);
+      if (S <= 1) continue;
+      const double r = (double)((blocks * S + cus - 1) / cus) / S;
+      if (r < best - 1e-9) {
+        best = r;
+        best_t = t;
+      }
+    }
+    return best_t;
   }
-  int t = kDmaSplitTile0;
-  while (t < kDmaSplitTileLast && blocks * gemm_dma_split(w->fmt, t, M, w->N) < 128 &&
-         gemm_dma_split(w->fmt, t + 1, M, w->N) > gemm_dma_split(w->fmt, t, M, w->N))
-    ++t;
-  return gemm_dma_split(w->fmt, t, M, w->N) > 1 ? t : kDefaultTile;
+  // a partial last round of tiles that would leave at least half the CUs idle: tile 13
+  // spreads it over K (it needs a workspace; without one it runs as tile 9)
+  int tail0 = 0;
+  return gemm_dma_tail(w->fmt, M, w->N, &tail0) > 1 ? kDmaTailTile : kDefaultTile;
 }
 
 int resolve_tile(const wq_weight* w, int64_t M) {
@@ -728,7 +738,7 @@ wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* 
       if (cand[c].tile >= kSkinnyTile0 && cand[c].tile <= kSkinnyTileLast &&
           gemm_skinny_split(cand[c].tile, M, copies[0].N) == 0)
         return WQ_OK;
-      if (cand[c].tile >= kMmaTile0 && gemm_mma_split(cand[c].tile, M, copies[0].K) == 0)
+      if (cand[c].tile >= kMmaTile0 && cand[c].tile <= kMmaTileLast && gemm_mma_split(cand[c].tile, M, copies[0].K) == 0)
         return WQ_OK;  // more tokens than the matrix-core GEMV kernel takes
     }
     auto run = [&]() -> wq_status { return run_cand(c, hs); };

@@ -1671,10 +1671,10 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N) {
 }
 
 int gemm_dma_split(int fmt, int tile, int64_t M, int64_t N) {
-  if (tile < kDmaSplitTile0 || tile > kDmaSplitTileLast) return 0;
+  if ((tile < kDmaSplitTile0 || tile > kDmaSplitTileLast) && tile != kDmaSplit3Tile) return 0;
   const int64_t tm = gemm_big_dma_rows(fmt);
   const int64_t blocks = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
-  int S = 2 << (tile - kDmaSplitTile0);
+  int S = tile == kDmaSplit3Tile ? 3 : 2 << (tile - kDmaSplitTile0);
   // about two workgroups per CU at most, and a bounded workspace
   while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
   return S;
@@ -1718,11 +1718,11 @@ int gemm_mma_split(int tile, int64_t M, int64_t K) {
 }
 
 size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile) {
-  if (tile >= kMmaTile0) {
+  if (tile >= kMmaTile0 && tile <= kMmaTileLast) {
     const int S = gemm_mma_split(tile, M, 0x7FFFFFFF);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
   }
-  if (tile >= kDma64Tile0) {
+  if (tile >= kDma64Tile0 && tile <= kDma128TileLast) {
     const int S = gemm_dma64_split(tile, M, N);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
   }
@@ -1741,8 +1741,8 @@ static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
   const size_t need = gemm_workspace_bytes(fmt, N, M, tile);
-  if (fmt == WQ_FMT_W8_PC || tile < 9 || tile >= kMmaTile0 || K % DBK != 0 || M * K >= (int64_t(1) << 31))
-    return need;
+  const bool dma = tile >= 9 && (tile < kMmaTile0 || tile == kDmaSplit3Tile);
+  if (fmt == WQ_FMT_W8_PC || !dma || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
   return round256(round256(need) + (size_t)M * (size_t)K * 2) + (size_t)M * sizeof(float);
 }
 

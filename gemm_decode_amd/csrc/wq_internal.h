@@ -97,6 +97,9 @@ int gemm_skinny_split(int tile, int64_t M, int64_t N);  // 0 when the tile is no
 // 2, 4, 8 over K steps (whole groups for group-128), capped so that the grid stays
 // within two workgroups per CU and the fp32 partials within kDmaSplitMaxBytes.
 constexpr int kDmaSplitTile0 = 10, kDmaSplitTileLast = 12;
+// GEMM tile kDmaSplit3Tile: the same with split-K 3 (a single partial round of 128 ..
+// 170 tiles on 256 CUs becomes 1.5 .. 2 rounds of thirds instead of 2 .. 2.7 of halves).
+constexpr int kDmaSplit3Tile = 24;
 constexpr int64_t kDmaSplitMaxBytes = int64_t(256) << 20;
 int gemm_dma_split(int fmt, int tile, int64_t M, int64_t N);  // 0 when the tile is not a split one
 // GEMM tile kDmaTailTile is tile 9 with the tiles of a partial last round (fewer than

@@ -273,10 +273,13 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      workgroup: its A operand holds 16 tokens, so 8..16 tokens stream the weights
  *      at about the cost of one; 23: as 20 with split-K 2 (needs 2 * M * N * 4 bytes
  *      of workspace, else WQ_ERR_WORKSPACE; with tile 0 and too small a workspace the
- *      split drops to 1); M > 16: tile 14 (tile 2 when K % 64 != 0).
+ *      split drops to 1); M > 16: tile 14 (tile 2 when K % 64 != 0);
+ *   24  tile 9 with split-K 3 (capped and needing the workspace as 10..12): a single
+ *      partial round of tiles (160 per-channel tiles at M = 2048, N = 5120) becomes
+ *      work for more of the CUs.
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 23
+#define WQ_GEMM_TILES 24
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -412,7 +415,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 23
+#define WQ_TUNE_LAT_SLOTS 24
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

@@ -542,7 +542,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
     # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
-    split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16, 18, 19]  # the split-K tiles (skinny, LDS-DMA)
+    split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16, 18, 19, 24]  # the split-K tiles (skinny, LDS-DMA)
     assert tile not in split_tiles, (tile, lat)
     skipped = set(split_tiles) | set(wq.MMA_TILES)
     assert all((v < 0) == (t in skipped) for t, v in enumerate(lat, start=1)), (tile, lat)
