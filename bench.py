@@ -966,7 +966,8 @@ def run_detail(wq, torch, args) -> dict:
 # of a down projection (K = 5632, N = 2048), one token routed to two experts (T = 2 rows)
 # and 16 tokens to two experts each (T = 32 rows, seeded counts)
 MOE_ROWS = [("w4g128", 8, 2048, 11264, 2, True), ("w4g128", 8, 2048, 11264, 32, True),
-            ("w8pc", 8, 5632, 2048, 2, False), ("w4g128", 8, 5632, 2048, 2, False)]
+            ("w8pc", 8, 5632, 2048, 2, False), ("w4g128", 8, 5632, 2048, 2, False),
+            ("w4g128", 8, 2048, 11264, 2048, True), ("w8pc", 8, 5632, 2048, 2048, False)]
 
 
 def measure_moe(wq, torch, fmt, E, K, N, T, gated) -> dict:
@@ -1004,9 +1005,9 @@ def measure_moe(wq, torch, fmt, E, K, N, T, gated) -> dict:
     active = int(np.count_nonzero(np.diff(off)))
     alg = active * per + 2 * T * K + 2 * T * width
     rec = {"us": round(us, 3), "GB/s": round(alg / us / 1e3, 1), "pct_hbm": round(100 * alg / us / 1e3 / HBM_PEAK_GBS, 1),
-           "experts_with_rows": active, "parity": st}
+           "TFLOP/s": round(2.0 * T * K * N / us / 1e6, 1), "experts_with_rows": active, "parity": st}
     log(f"moe {fmt} E={E} K={K} N={N} T={T} gated={gated}: {rec['us']} us, {rec['GB/s']} GB/s over "
-        f"{active} experts with rows")
+        f"{active} experts with rows, {rec['TFLOP/s']} TFLOP/s")
     del copies, base
     torch.cuda.empty_cache()
     return rec

@@ -91,7 +91,7 @@ __device__ __forceinline__ void i8_word_to_bf16(uint32_t d, uint32_t& lo, uint32
 // grid (pairs, E); block 64 W, W <= kMoeWaves, with W * 2 KiB of dynamic LDS for the
 // waves' sums.  K % 128 == 0, N % 16 == 0 (and, gated, (N / 2) % 16 == 0), checked on the
 // host.  Offsets are clamped into [0, T] before use.
-template <int FMT, bool GATED>
+template <int FMT, bool GATED, int MB>
 __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __restrict__ qw0,
                                                             const uint16_t* __restrict__ sc0,
                                                             const uint8_t* __restrict__ zs0, size_t qw_stride,
@@ -137,192 +137,228 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_kernel(const uint8_t* __re
   uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_a = 0x64006400u, mag_h = 0x54005400u;
   if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_a), "+v"(mag_h));
 
-  // one unit's operands: both tiles' codes, their group scales and zero bytes, and this
-  // lane's 32 x values
+  // One unit's operands: both tiles' codes, their group scales and zero bytes.  The
+  // codes become the B operands once per unit and feed the MFMAs of every token block.
   struct Set {
     u32x4_t c[2][CL];
-    uint4 xv[4];
     uint32_t sv[2], zb[2];
   };
-  for (int tb = t0; tb < t1; tb += kMoeTokens) {
-    const int MT = min(kMoeTokens, t1 - tb);
-    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (size_t)(tb + min((int)ln, MT - 1)) * K);
-    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    auto load = [&](Set& st, int u) {
-      const uint32_t sl = (uint32_t)u / kUnitsPerSlice, ui = (uint32_t)u % kUnitsPerSlice;
-      const uint32_t wsl = min((uint32_t)kSliceBytes, row_bytes - (uint32_t)kSliceBytes * sl);
+  auto load = [&](Set& st, int u) {
+    const uint32_t sl = (uint32_t)u / kUnitsPerSlice, ui = (uint32_t)u % kUnitsPerSlice;
+    const uint32_t wsl = min((uint32_t)kSliceBytes, row_bytes - (uint32_t)kSliceBytes * sl);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < CL; ++j)
-          st.c[t][j] = __builtin_bit_cast(
-              u32x4_t, load_stream16(tbase[t] + (size_t)16 * kSliceBytes * sl +
-                                     (ln * wsl + kUnitBytes * ui + (kW4 ? 16u : 32u) * lk + 16u * j)));
-      st.sv[0] = st.sv[1] = st.zb[0] = st.zb[1] = 0u;
-      if constexpr (kGrouped) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          st.sv[t] = sbase[t][16 * u + ln];
-          if constexpr (kW4) st.zb[t] = zbase[t][8 * u + (ln >> 1)];
-        }
-      }
-      const uint4* xp = reinterpret_cast<const uint4*>(xrow + 2u * (128u * (uint32_t)u + 32u * lk));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.xv[j] = xp[j];
-    };
-    auto compute = [&](const Set& st) {
-      const u32x4_t(&c)[2][CL] = st.c;
-      const uint32_t* sv = st.sv;
-      const uint32_t* zb = st.zb;
-      const uint4* xv = st.xv;
-      F16Exact fx;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        fx.add(xv[j].x);
-        fx.add(xv[j].y);
-        fx.add(xv[j].z);
-        fx.add(xv[j].w);
-      }
-      const bool exact = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
-      f32x4_t d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (!exact) {
-        if constexpr (kW4) {
-          const u32x4_t a_lo0 = {bf16x2_to_f16x2(xv[0].x), bf16x2_to_f16x2(xv[0].z), bf16x2_to_f16x2(xv[1].x),
-                                 bf16x2_to_f16x2(xv[1].z)};
-          const u32x4_t a_lo1 = {bf16x2_to_f16x2(xv[2].x), bf16x2_to_f16x2(xv[2].z), bf16x2_to_f16x2(xv[3].x),
-                                 bf16x2_to_f16x2(xv[3].z)};
-          const u32x4_t a_hi0 = {bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
-                                 bf16x2_to_f16x2(xv[1].w)};
-          const u32x4_t a_hi1 = {bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
-                                 bf16x2_to_f16x2(xv[3].w)};
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint32_t z = (zb[t] >> zshift) & 15u;
-            // fp16 pairs -(1024 + z) = 0xE400 + z and -(64 + z) = 0xD400 + 16 z
-            const uint32_t off_a = 0xE400E400u + z * 0x10001u, off_b = 0xD400D400u + z * 0x100010u;
-            uint32_t lo[4], lo8[4], hi[4], hi8[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t w = c[t][0][q], w8 = w >> 8;
-              lo[q] = add_f16x2((w & m_lo) | mag_a, off_a);
-              hi[q] = add_f16x2((w & m_hi) | mag_h, off_b);
-              lo8[q] = add_f16x2((w8 & m_lo) | mag_a, off_a);
-              hi8[q] = add_f16x2((w8 & m_hi) | mag_h, off_b);
-            }
-            d[t] = mma_f16(a_lo0, u32x4_t{lo[0], lo8[0], lo[1], lo8[1]}, d[t]);
-            d[t] = mma_f16(a_lo1, u32x4_t{lo[2], lo8[2], lo[3], lo8[3]}, d[t]);
-            d[t] = mma_f16(a_hi0, u32x4_t{hi[0], hi8[0], hi[1], hi8[1]}, d[t]);
-            d[t] = mma_f16(a_hi1, u32x4_t{hi[2], hi8[2], hi[3], hi8[3]}, d[t]);
-          }
-        } else {
-          u32x4_t a[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            a[j] = u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
-                           bf16x2_to_f16x2(xv[j].w)};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const uint32_t w0 = c[t][j >> 1][2 * (j & 1)], w1 = c[t][j >> 1][2 * (j & 1) + 1];
-              const u32x4_t b = {add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), kF16Minus1152),
-                                 add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), kF16Minus1152),
-                                 add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), kF16Minus1152),
-                                 add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), kF16Minus1152)};
-              d[t] = mma_f16(a[j], b, d[t]);
-            }
-        }
-      } else {
-        // exact codes (q, or q - z) in bf16 against bf16 x
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          if constexpr (kW4) {
-            const float z = (float)((zb[t] >> zshift) & 15u);
-            auto ex = [&](uint32_t w, int i) {
-              return pack_bf16x2((float)((w >> (4 * i)) & 15u) - z, (float)((w >> (16 + 4 * i)) & 15u) - z);
-            };
-            const uint32_t w0 = c[t][0][0], w1 = c[t][0][1], w2 = c[t][0][2], w3 = c[t][0][3];
-            d[t] = mma_bf16(u32x4_t{xv[0].x, xv[0].z, xv[1].x, xv[1].z},
-                            u32x4_t{ex(w0, 0), ex(w0, 2), ex(w1, 0), ex(w1, 2)}, d[t]);
-            d[t] = mma_bf16(u32x4_t{xv[2].x, xv[2].z, xv[3].x, xv[3].z},
-                            u32x4_t{ex(w2, 0), ex(w2, 2), ex(w3, 0), ex(w3, 2)}, d[t]);
-            d[t] = mma_bf16(u32x4_t{xv[0].y, xv[0].w, xv[1].y, xv[1].w},
-                            u32x4_t{ex(w0, 1), ex(w0, 3), ex(w1, 1), ex(w1, 3)}, d[t]);
-            d[t] = mma_bf16(u32x4_t{xv[2].y, xv[2].w, xv[3].y, xv[3].w},
-                            u32x4_t{ex(w2, 1), ex(w2, 3), ex(w3, 1), ex(w3, 3)}, d[t]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              uint32_t b0, b1, b2, b3;
-              i8_word_to_bf16(c[t][j >> 1][2 * (j & 1)], b0, b1);
-              i8_word_to_bf16(c[t][j >> 1][2 * (j & 1) + 1], b2, b3);
-              d[t] = mma_bf16(u32x4_t{xv[j].x, xv[j].y, xv[j].z, xv[j].w}, u32x4_t{b0, b1, b2, b3}, d[t]);
-            }
-          }
-        }
-      }
-      // the unit's partial sums: times the group scale (group-128), or kept whole
+      for (int j = 0; j < CL; ++j)
+        st.c[t][j] = __builtin_bit_cast(
+            u32x4_t, load_stream16(tbase[t] + (size_t)16 * kSliceBytes * sl +
+                                   (ln * wsl + kUnitBytes * ui + (kW4 ? 16u : 32u) * lk + 16u * j)));
+    st.sv[0] = st.sv[1] = st.zb[0] = st.zb[1] = 0u;
+    if constexpr (kGrouped) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        if constexpr (kGrouped) {
-          const float s = kW4 ? f16_to_f32((uint16_t)sv[t]) : bf16_to_f32((uint16_t)sv[t]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s, d[t][i], acc[t][i]);
-        } else {
-          acc[t] += d[t];
-        }
+        st.sv[t] = sbase[t][16 * u + ln];
+        if constexpr (kW4) st.zb[t] = zbase[t][8 * u + (ln >> 1)];
       }
-    };
+    }
+  };
+
+  // token groups of MB blocks of 16 rows
+  for (int tb = t0; tb < t1; tb += kMoeTokens * MB) {
+    const int MT = min(kMoeTokens * MB, t1 - tb);
+    const uint8_t* xrow[MB];  // this lane's token in each block (rows past the group repeat its last)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+      xrow[b] = reinterpret_cast<const uint8_t*>(x + (size_t)(tb + min(16 * b + (int)ln, MT - 1)) * K);
+    f32x4_t acc[2][MB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
     // units wu, wu + W, ...: each loads and multiplies in turn (a second operand set in
     // flight doubles the registers and halves the resident waves: measured slower on
     // MI355X, like 4 or 16 waves per workgroup)
     for (int u = wu; u < U; u += W) {
       Set st;
       load(st, u);
-      compute(st);
-    }
-    // lane l holds D[token 4 (l / 16) + i][row l % 16] of both tiles
+      // the B operands of both tiles as exact fp16 code values (q, or q - z)
+      u32x4_t bo[2][4];
+      if constexpr (kW4) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t z = (st.zb[t] >> zshift) & 15u;
+          // fp16 pairs -(1024 + z) = 0xE400 + z and -(64 + z) = 0xD400 + 16 z
+          const uint32_t off_a = 0xE400E400u + z * 0x10001u, off_b = 0xD400D400u + z * 0x100010u;
+          uint32_t lo[4], lo8[4], hi[4], hi8[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[((wave * 2 + t) * kMoeTokens + 4 * lk + i) * 16 + ln] = acc[t][i];
-    __syncthreads();
-    for (int o = threadIdx.x; o < (GATED ? 1 : 2) * kMoeTokens * 16; o += blockDim.x) {
-      const int t = o / (kMoeTokens * 16), m = (o / 16) % kMoeTokens, r = o & 15;
-      if (m >= MT) continue;
-      float v0 = 0.f, v1 = 0.f;
-      for (int w = 0; w < W; ++w) {
-        v0 += red[((w * 2 + t) * kMoeTokens + m) * 16 + r];
-        if (GATED) v1 += red[((w * 2 + 1) * kMoeTokens + m) * 16 + r];
-      }
-      const int n0 = 16 * tt[t] + r;
-      if constexpr (GATED) {
-        const int n1 = 16 * tt[1] + r;
-        const float g = kGrouped ? v0 : bf16_to_f32(sc[n0]) * v0;
-        const float up = kGrouped ? v1 : bf16_to_f32(sc[n1]) * v1;
-        const float h = g / (1.f + expf(-g)) * up;
-        y[(size_t)(tb + m) * (N / 2) + n0] = f32_to_bf16(h);
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = st.c[t][0][q], w8 = w >> 8;
+            lo[q] = add_f16x2((w & m_lo) | mag_a, off_a);
+            hi[q] = add_f16x2((w & m_hi) | mag_h, off_b);
+            lo8[q] = add_f16x2((w8 & m_lo) | mag_a, off_a);
+            hi8[q] = add_f16x2((w8 & m_hi) | mag_h, off_b);
+          }
+          bo[t][0] = u32x4_t{lo[0], lo8[0], lo[1], lo8[1]};
+          bo[t][1] = u32x4_t{lo[2], lo8[2], lo[3], lo8[3]};
+          bo[t][2] = u32x4_t{hi[0], hi8[0], hi[1], hi8[1]};
+          bo[t][3] = u32x4_t{hi[2], hi8[2], hi[3], hi8[3]};
+        }
       } else {
-        if (t == 1 && !second) continue;
-        y[(size_t)(tb + m) * N + n0] = f32_to_bf16(kGrouped ? v0 : bf16_to_f32(sc[n0]) * v0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w0 = st.c[t][j >> 1][2 * (j & 1)], w1 = st.c[t][j >> 1][2 * (j & 1) + 1];
+            bo[t][j] = u32x4_t{add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), kF16Minus1152),
+                               add_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), kF16Minus1152)};
+          }
+      }
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        if (16 * b >= MT) break;  // wave-uniform: no token of this block
+        uint4 xv[4];
+        const uint4* xp = reinterpret_cast<const uint4*>(xrow[b] + 2u * (128u * (uint32_t)u + 32u * lk));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+        F16Exact fx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fx.add(xv[j].x);
+          fx.add(xv[j].y);
+          fx.add(xv[j].z);
+          fx.add(xv[j].w);
+        }
+        const bool exact = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
+        f32x4_t d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (!exact) {
+          // x in fp16 (exact here), the A operands in the order of the B operands
+          u32x4_t a[4];
+          if constexpr (kW4) {
+            a[0] = u32x4_t{bf16x2_to_f16x2(xv[0].x), bf16x2_to_f16x2(xv[0].z), bf16x2_to_f16x2(xv[1].x),
+                           bf16x2_to_f16x2(xv[1].z)};
+            a[1] = u32x4_t{bf16x2_to_f16x2(xv[2].x), bf16x2_to_f16x2(xv[2].z), bf16x2_to_f16x2(xv[3].x),
+                           bf16x2_to_f16x2(xv[3].z)};
+            a[2] = u32x4_t{bf16x2_to_f16x2(xv[0].y), bf16x2_to_f16x2(xv[0].w), bf16x2_to_f16x2(xv[1].y),
+                           bf16x2_to_f16x2(xv[1].w)};
+            a[3] = u32x4_t{bf16x2_to_f16x2(xv[2].y), bf16x2_to_f16x2(xv[2].w), bf16x2_to_f16x2(xv[3].y),
+                           bf16x2_to_f16x2(xv[3].w)};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a[j] = u32x4_t{bf16x2_to_f16x2(xv[j].x), bf16x2_to_f16x2(xv[j].y), bf16x2_to_f16x2(xv[j].z),
+                             bf16x2_to_f16x2(xv[j].w)};
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) d[t] = mma_f16(a[j], bo[t][j], d[t]);
+        } else {
+          // exact codes (q, or q - z) in bf16 against bf16 x
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (kW4) {
+              const float z = (float)((st.zb[t] >> zshift) & 15u);
+              auto ex = [&](uint32_t w, int i) {
+                return pack_bf16x2((float)((w >> (4 * i)) & 15u) - z, (float)((w >> (16 + 4 * i)) & 15u) - z);
+              };
+              const uint32_t w0 = st.c[t][0][0], w1 = st.c[t][0][1], w2 = st.c[t][0][2], w3 = st.c[t][0][3];
+              d[t] = mma_bf16(u32x4_t{xv[0].x, xv[0].z, xv[1].x, xv[1].z},
+                              u32x4_t{ex(w0, 0), ex(w0, 2), ex(w1, 0), ex(w1, 2)}, d[t]);
+              d[t] = mma_bf16(u32x4_t{xv[2].x, xv[2].z, xv[3].x, xv[3].z},
+                              u32x4_t{ex(w2, 0), ex(w2, 2), ex(w3, 0), ex(w3, 2)}, d[t]);
+              d[t] = mma_bf16(u32x4_t{xv[0].y, xv[0].w, xv[1].y, xv[1].w},
+                              u32x4_t{ex(w0, 1), ex(w0, 3), ex(w1, 1), ex(w1, 3)}, d[t]);
+              d[t] = mma_bf16(u32x4_t{xv[2].y, xv[2].w, xv[3].y, xv[3].w},
+                              u32x4_t{ex(w2, 1), ex(w2, 3), ex(w3, 1), ex(w3, 3)}, d[t]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                uint32_t b0, b1, b2, b3;
+                i8_word_to_bf16(st.c[t][j >> 1][2 * (j & 1)], b0, b1);
+                i8_word_to_bf16(st.c[t][j >> 1][2 * (j & 1) + 1], b2, b3);
+                d[t] = mma_bf16(u32x4_t{xv[j].x, xv[j].y, xv[j].z, xv[j].w}, u32x4_t{b0, b1, b2, b3}, d[t]);
+              }
+            }
+          }
+        }
+        // the unit's partial sums: times the group scale (group-128), or kept whole
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if constexpr (kGrouped) {
+            const float s = kW4 ? f16_to_f32((uint16_t)st.sv[t]) : bf16_to_f32((uint16_t)st.sv[t]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][b][i] = fmaf(s, d[t][i], acc[t][b][i]);
+          } else {
+            acc[t][b] += d[t];
+          }
+        }
       }
     }
-    __syncthreads();  // red is reused by the next token block
+    // the waves' sums meet in LDS, block by block; lane l holds D[token 4 (l / 16) + i][row
+    // l % 16] of both tiles
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int tbb = tb + 16 * b, MB16 = min(16, MT - 16 * b);
+      if (MB16 <= 0) break;  // uniform over the workgroup
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wave * 2 + t) * kMoeTokens + 4 * lk + i) * 16 + ln] = acc[t][b][i];
+      __syncthreads();
+      for (int o = threadIdx.x; o < (GATED ? 1 : 2) * kMoeTokens * 16; o += blockDim.x) {
+        const int t = o / (kMoeTokens * 16), m = (o / 16) % kMoeTokens, r = o & 15;
+        if (m >= MB16) continue;
+        float v0 = 0.f, v1 = 0.f;
+        for (int w = 0; w < W; ++w) {
+          v0 += red[((w * 2 + t) * kMoeTokens + m) * 16 + r];
+          if (GATED) v1 += red[((w * 2 + 1) * kMoeTokens + m) * 16 + r];
+        }
+        const int n0 = 16 * tt[t] + r;
+        if constexpr (GATED) {
+          const int n1 = 16 * tt[1] + r;
+          const float g = kGrouped ? v0 : bf16_to_f32(sc[n0]) * v0;
+          const float up = kGrouped ? v1 : bf16_to_f32(sc[n1]) * v1;
+          const float h = g / (1.f + expf(-g)) * up;
+          y[(size_t)(tbb + m) * (N / 2) + n0] = f32_to_bf16(h);
+        } else {
+          if (t == 1 && !second) continue;
+          y[(size_t)(tbb + m) * N + n0] = f32_to_bf16(kGrouped ? v0 : bf16_to_f32(sc[n0]) * v0);
+        }
+      }
+      __syncthreads();  // red is reused by the next block
+    }
   }
 }
 
 template <int FMT>
 void launch_fmt(bool gated, dim3 grid, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, size_t qs,
                 size_t ss, size_t zst, const uint16_t* x, const int32_t* off, uint16_t* y, int T, int K, int N,
-                hipStream_t st) {
+                int E, hipStream_t st) {
   // eight waves (measured on MI355X against 4, 16 and about three units per wave, with
   // and without a second operand set: 10-30 % faster at one or two tokens per expert)
   const int W = kMoeWaves;
   const size_t lds = (size_t)W * 2 * kMoeTokens * 16 * sizeof(float);
-  if (gated)
-    moe_kernel<FMT, true><<<grid, 64 * W, lds, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
-  else
-    moe_kernel<FMT, false><<<grid, 64 * W, lds, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N);
+  // token blocks per pass over the weights, by the rows an expert holds on average: each
+  // unit's codes then feed up to four 16-token blocks (the routing itself stays on the
+  // device, so the average is all the host knows)
+  const int64_t avg = (T + E - 1) / E;
+  const int mb = avg <= kMoeTokens ? 1 : avg <= 2 * kMoeTokens ? 2 : avg <= 6 * kMoeTokens ? 4 : 8;
+#define WQ_MOE(G, MBV) moe_kernel<FMT, G, MBV><<<grid, 64 * W, lds, st>>>(qw, sc, zs, qs, ss, zst, x, off, y, T, K, N)
+  if (gated) {
+    if (mb == 1) WQ_MOE(true, 1);
+    else if (mb == 2) WQ_MOE(true, 2);
+    else if (mb == 4) WQ_MOE(true, 4);
+    else WQ_MOE(true, 8);
+  } else {
+    if (mb == 1) WQ_MOE(false, 1);
+    else if (mb == 2) WQ_MOE(false, 2);
+    else if (mb == 4) WQ_MOE(false, 4);
+    else WQ_MOE(false, 8);
+  }
+#undef WQ_MOE
 }
 
 }  // namespace
@@ -337,15 +373,15 @@ wq_status launch_moe(const wq_weight* w, int E, const uint16_t* x, const int32_t
   switch (w->fmt) {
     case WQ_FMT_W8_PC:
       launch_fmt<WQ_FMT_W8_PC>(gated, grid, qw, sc, zs, qw_stride, sc_stride, zs_stride, x, offsets, y, (int)T,
-                               (int)w->K, (int)w->N, s);
+                               (int)w->K, (int)w->N, E, s);
       break;
     case WQ_FMT_W8_G128:
       launch_fmt<WQ_FMT_W8_G128>(gated, grid, qw, sc, zs, qw_stride, sc_stride, zs_stride, x, offsets, y, (int)T,
-                                 (int)w->K, (int)w->N, s);
+                                 (int)w->K, (int)w->N, E, s);
       break;
     case WQ_FMT_W4_G128:
       launch_fmt<WQ_FMT_W4_G128>(gated, grid, qw, sc, zs, qw_stride, sc_stride, zs_stride, x, offsets, y, (int)T,
-                                 (int)w->K, (int)w->N, s);
+                                 (int)w->K, (int)w->N, E, s);
       break;
     default:
       return fail(WQ_ERR_UNSUPPORTED, "wq_moe_linear: unknown format");

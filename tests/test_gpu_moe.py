@@ -51,6 +51,27 @@ def test_moe_against_oracle(wq, fmt, gated):
 
 
 @pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("T,off", [
+    (90, [0, 25, 25, 58, 90]),            # 22.5 rows per expert: two blocks per pass; 25 = a partial second block
+    (260, [0, 1, 113, 200, 260]),         # 65 per expert: four blocks per pass; 112 = 1 3/4 groups of 64, 87 with a lone last row
+    (420, [0, 130, 130, 300, 420]),       # 105 per expert: eight blocks per pass; 130 = a group of 128 and 2 rows
+])
+def test_moe_token_blocks_per_pass(wq, fmt, T, off):
+    """More rows per expert: each unit's codes feed two, four or eight 16-row blocks per pass
+    over the weights (chosen from the average rows per expert), with partly filled
+    blocks and groups, an empty expert and one with a single row; both epilogues; an
+    fp16-inexact x in one block."""
+    E, K, N = 4, 640, 64
+    g, Ps = _experts(wq, fmt, E, K, N, seed=144)
+    xf = OQ.bf16_bits_to_f32(synth.activation(144, K, T)).copy()
+    xf[T - 2, 300] = 1.0e-7                                      # one unit of one block on the exact path
+    x = OQ.bf16_rne_bits(xf.astype(np.float32))
+    for gated in (False, True):
+        ref = OM.ref_moe_silu_mul(x, off, Ps) if gated else OM.ref_moe_linear(x, off, Ps)
+        assert_parity(_run(wq, g, x, off, gated), ref, f"moe {fmt} T={T} gated={gated}")
+
+
+@pytest.mark.parametrize("fmt", OQ.FORMATS)
 def test_moe_activations_fp16_cannot_hold(wq, fmt):
     """Units with |x| > 65280 or 0 < |x| < 2^-17 take the exact bf16 path."""
     E, K, N, T = 3, 1024, 64, 20
