@@ -8,7 +8,8 @@ library in ``gemm_decode_amd/`` and imports nothing from it.
 What it computes (plain, slow, obviously correct; NumPy only):
 
 * ``quant``  -- the quantisers and the canonical packed layouts (W8 per output
-  channel, W8 group-128, W4 asymmetric group-128), step by step.
+  channel, W8 group-128, W4 asymmetric group-128 and per output channel), step by
+  step.
 * ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
   chunked along N; sampled-column variants for full-size checks; the
   comparison statistics with the per-element tolerance; the full-K activation
@@ -36,8 +37,8 @@ hand-derived worked examples (``tests/golden/``), closed-form error bounds,
 brute force on tiny inputs and reductions to NumPy library routines.
 """
 from .quant import (  # noqa: F401
-    FORMATS, GROUP, bf16_bits_to_f32, bf16_rne_bits, dequant, pack, packed_sizes,
-    quantize_w4g128, quantize_w8, unpack_w4g128,
+    FORMATS, GROUP, W4PC, bf16_bits_to_f32, bf16_rne_bits, dequant, pack, packed_sizes,
+    quantize_w4, quantize_w4g128, quantize_w8, unpack_w4g128, unpack_w4pc,
 )
 from .linear import (  # noqa: F401
     compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, token_count, use_gemv,

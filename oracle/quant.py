@@ -18,15 +18,18 @@ group-128 INT8 head of the Marlin benchmark page, "Full inference"):
      stored (rounded) scale
   layout: q int8 [N, K] row-major; s bf16 [N, K/G].
 
-W4 asymmetric, group 128 (INT4 + group 128 in the Marlin page's "Validation
-and limits"):
+W4 asymmetric, one scale and zero-point per group of G consecutive k (G = 128:
+INT4 + group 128; G = K: INT4 per output channel -- both in the Marlin page's
+"Validation and limits", which lists INT4 with per-channel and group scales):
   1. hi = max w, lo = min w over the group
   2. s = fp16((hi - lo) / 15)                       -- the stored scale
   3. if s == 0: z = 0, q = 0
      else z = clamp(rint(-lo / s), 0, 15); q = clamp(rint(w / s) + z, 0, 15)
   layout: qweight uint32 [N, K/8], bits 4j..4j+3 of word (n, c) hold q[n, 8c+j];
-          scales fp16 [N, K/128];
-          zeros uint32 [K/128, N/8], bits 4j..4j+3 of word (g, c) hold z[8c+j, g].
+          group 128:   scales fp16 [N, K/128];
+                       zeros uint32 [K/128, N/8], bits 4j..4j+3 of word (g, c) hold z[8c+j, g];
+          per channel: scales fp16 [N]; zeros uint32 [N/8], bits 4j..4j+3 of word c
+                       hold z[8c+j] (the group-128 layout with one group).
 
 Dequantisation is exact in fp32: W8 q*s, W4 (q - z)*s.
 """
@@ -36,6 +39,7 @@ import numpy as np
 
 GROUP = 128
 FORMATS = ("w8pc", "w8g128", "w4g128")
+W4PC = "w4pc"  # INT4 per output channel (tested on its own; FORMATS are the configs' formats)
 
 
 # ---------------------------------------------------------------- conversions
@@ -82,14 +86,15 @@ def quantize_w8(W: np.ndarray, G: int | None = None):
     return q.astype(np.int8).reshape(N, K), s_bits
 
 
-def quantize_w4g128(W: np.ndarray):
-    """Asymmetric uint4 quantisation, group 128 along K, fp16 scale and uint4 zero.
+def quantize_w4(W: np.ndarray, G: int | None = GROUP):
+    """Asymmetric uint4 quantisation, one fp16 scale and uint4 zero per group of G
+    along K (G=None: one group per output channel, G = K).
 
-    Returns unpacked (q uint8 [N, K] in 0..15, s fp16 [N, K/128], z uint8 [N, K/128]).
+    Returns unpacked (q uint8 [N, K] in 0..15, s fp16 [N, K/G], z uint8 [N, K/G]).
     """
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
-    Wg = _groups(W, GROUP)
+    Wg = _groups(W, K if G is None else G)
     hi = np.max(Wg, axis=2)                                # step 1
     lo = np.min(Wg, axis=2)
     s16 = ((hi - lo) / np.float32(15.0)).astype(np.float16)  # step 2
@@ -100,6 +105,11 @@ def quantize_w4g128(W: np.ndarray):
     z[nz] = np.clip(np.rint(-lo[nz] / s[nz]), 0, 15)
     q[nz] = np.clip(np.rint(Wg[nz] / s[nz][:, None]) + z[nz][:, None], 0, 15)
     return q.astype(np.uint8).reshape(N, K), s16, z.astype(np.uint8)
+
+
+def quantize_w4g128(W: np.ndarray):
+    """quantize_w4 with groups of 128 along K."""
+    return quantize_w4(W, GROUP)
 
 
 # -------------------------------------------------------------------- packing
@@ -141,6 +151,12 @@ def pack(fmt: str, W: np.ndarray) -> dict:
         q, s16, z = quantize_w4g128(W)
         return dict(fmt=fmt, K=K, N=N, qweight=_pack_nibbles_rows(q), scales=s16,
                     zeros=_pack_nibbles_rows(np.ascontiguousarray(z.T)))
+    if fmt == W4PC:
+        if N % 8 or K % 8:
+            raise ValueError("W4 needs N % 8 == 0 and K % 8 == 0 (8 codes or zeros per word)")
+        q, s16, z = quantize_w4(W, None)
+        return dict(fmt=fmt, K=K, N=N, qweight=_pack_nibbles_rows(q), scales=s16.reshape(N),
+                    zeros=_pack_nibbles_rows(np.ascontiguousarray(z.T)).reshape(N // 8))
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -148,6 +164,13 @@ def unpack_w4g128(P: dict):
     """Canonical W4 words -> (q [N, K] uint8, s fp16 [N, K/128], z [N, K/128] uint8)."""
     q = _unpack_nibbles_rows(P["qweight"])
     z = np.ascontiguousarray(_unpack_nibbles_rows(P["zeros"]).T)
+    return q, P["scales"], z
+
+
+def unpack_w4pc(P: dict):
+    """Canonical per-channel W4 words -> (q [N, K] uint8, s fp16 [N], z [N] uint8)."""
+    q = _unpack_nibbles_rows(P["qweight"])
+    z = _unpack_nibbles_rows(np.asarray(P["zeros"]).reshape(1, -1)).reshape(-1)
     return q, P["scales"], z
 
 
@@ -159,6 +182,8 @@ def packed_sizes(fmt: str, K: int, N: int):
         return K * N, 2 * N * (K // GROUP), 0
     if fmt == "w4g128":
         return K * N // 2, 2 * N * (K // GROUP), (K // GROUP) * (N // 8) * 4
+    if fmt == W4PC:
+        return K * N // 2, 2 * N, (N // 8) * 4
     raise ValueError(fmt)
 
 
@@ -182,4 +207,10 @@ def dequant(P: dict, rows=None) -> np.ndarray:
         n = q.shape[0]
         d = q.astype(np.float32).reshape(n, K // GROUP, GROUP) - z.astype(np.float32)[:, :, None]
         return (d * s16.astype(np.float32)[:, :, None]).reshape(n, K)
+    if fmt == W4PC:
+        q, s16, z = unpack_w4pc(dict(qweight=P["qweight"][sel], scales=P["scales"][sel], zeros=P["zeros"]))
+        if rows is not None:
+            z = z[np.asarray(rows)]
+        d = q.astype(np.float32) - z.astype(np.float32)[:, None]
+        return d * s16.astype(np.float32)[:, None]
     raise ValueError(fmt)

@@ -57,8 +57,15 @@ def _decode_w4_zero(P: dict, n: int, g: int) -> int:
     return (word >> (4 * (n % 8))) & 0xF
 
 
+def _decode_w4pc_zero(P: dict, n: int) -> int:
+    word = int(np.asarray(P["zeros"]).reshape(-1)[n // 8])
+    return (word >> (4 * (n % 8))) & 0xF
+
+
 def _exact_dequant(P: dict, n: int, k: int) -> Fraction:
     fmt = P["fmt"]
+    if fmt == "w4pc":
+        return (_decode_w4_codes(P, n, k) - _decode_w4pc_zero(P, n)) * _fp16_value(P["scales"][n])
     if fmt == "w8pc":
         return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n]))
     if fmt == "w8g128":
@@ -144,6 +151,55 @@ def pin_golden_w4g128():
     for k in range(0, W.shape[1], 7):
         assert Fraction(float(Wd[0, k])) == _exact_dequant(P, 0, k)
     assert not np.any(Wd[1:])
+
+
+def pin_golden_w4pc():
+    """The per-channel W4 quantiser and its canonical packing against the hand-derived
+    rows of tests/golden/w4pc_worked.txt: ties in both directions, an all-zero row, a
+    constant row, a clamped zero-point, clamped codes, an fp16-rounded scale, and an
+    odd zero-point where adding z before rounding would differ."""
+    head, blocks = read_fixture("w4pc_worked.txt")
+    W = np.array([[float(t) for t in r] for r in blocks["W"]], dtype=np.float32)
+    exp_q = [[int(t) for t in r] for r in blocks["q"]]
+    P = OQ.pack("w4pc", W)
+    N, K = W.shape
+    for n in range(N):
+        assert [_decode_w4_codes(P, n, k) for k in range(K)] == exp_q[n], f"q row {n}"
+    assert [int(w) for w in P["qweight"][:, 0]] == [num(t) for t in head["qweight_words"]]
+    assert [int(b) for b in np.asarray(P["scales"]).view(np.uint16)] == [num(t) for t in head["s_bits"]]
+    assert [_decode_w4pc_zero(P, n) for n in range(N)] == [int(t) for t in head["z"]]
+    assert int(np.asarray(P["zeros"]).reshape(-1)[0]) == num(head["zeros_word"][0])
+    Wd = OQ.dequant(P)
+    for n in range(N):
+        for k in range(K):
+            assert Fraction(float(Wd[n, k])) == _exact_dequant(P, n, k), (n, k)
+    assert not np.any(Wd[1]) and not np.any(Wd[2])
+
+
+def pin_w4pc_one_group_is_group128(seed=12, N=24):
+    """With K = 128 a per-channel group is exactly one group of 128: the two formats
+    store the same codes, scales and zero-points (laid out as their layouts say)."""
+    W = synth.weight(seed, 128, N, outliers=True)
+    Pc, Pg = OQ.pack("w4pc", W), OQ.pack("w4g128", W)
+    assert np.array_equal(Pc["qweight"], Pg["qweight"])
+    assert np.array_equal(np.asarray(Pc["scales"]).view(np.uint16), np.asarray(Pg["scales"]).view(np.uint16)[:, 0])
+    assert np.array_equal(np.asarray(Pc["zeros"]).reshape(-1), np.asarray(Pg["zeros"])[0])
+    assert np.array_equal(OQ.dequant(Pc), OQ.dequant(Pg))
+
+
+def pin_w4pc_roundtrip_bound(seed=13, N=32, K=1024):
+    """P2 for one group per row: unclamped codes within s/2 of w, clamped ones within
+    s/2 + (hi - lo) 2^-11; the scale comes from the whole row's range."""
+    W = synth.weight(seed, K, N, outliers=True)
+    P = OQ.pack("w4pc", W)
+    s = np.asarray(P["scales"]).astype(np.float64)
+    span = W.max(axis=1).astype(np.float64) - W.min(axis=1).astype(np.float64)
+    for n in range(N):
+        assert abs(float(s[n]) - span[n] / 15) <= span[n] / 15 * 2.0 ** -10, n
+        z = _decode_w4pc_zero(P, n)
+        for k in range(0, K, 7):
+            wd = (_decode_w4_codes(P, n, k) - z) * float(s[n])
+            assert abs(float(W[n, k]) - wd) <= s[n] / 2 + span[n] * 2.0 ** -11 + abs(float(W[n, k])) * 2.0 ** -22, (n, k)
 
 
 def pin_nibble_layout():
@@ -271,7 +327,7 @@ def pin_one_hot_golden():
 
 
 def pin_one_hot_random(fmt="w8g128", K=512, N=40):
-    W = synth.weight(11, K, N, outliers=fmt == "w4g128")
+    W = synth.weight(11, K, N, outliers=fmt.startswith("w4"))
     P = OQ.pack(fmt, W)
     ks = [0, 127, 128, 300, K - 1]
     y = OL.ref_linear(synth.one_hot_activation(K, ks), P)
@@ -294,7 +350,7 @@ def pin_bruteforce(fmt, K, N=11, M=3, seed=5):
     """P7: a triple loop over exact rationals (codes decoded by hand, bf16 x decoded
     by hand) agrees with the NumPy path to fp64 rounding; N is not a multiple of
     the chunk so a dropped tail shows."""
-    W = synth.weight(seed, K, N if fmt != "w4g128" else 16, outliers=fmt == "w4g128")
+    W = synth.weight(seed, K, N if not fmt.startswith("w4") else 16, outliers=fmt.startswith("w4"))
     N = W.shape[0]
     P = OQ.pack(fmt, W)
     x = synth.activation(seed, K, M)
@@ -574,6 +630,8 @@ ALL_PINS = [
     pin_compare, pin_compare_rel_rms, pin_dispatch, pin_topk_golden, pin_topk_rows,
     pin_topk_defining_property,
     pin_topk_sampling_closed_forms, pin_activation_permutation, pin_silu_closed_forms, pin_moe_grouping,
+    pin_golden_w4pc, pin_w4pc_one_group_is_group128, pin_w4pc_roundtrip_bound,
+    lambda: pin_bruteforce("w4pc", 64), lambda: pin_one_hot_random("w4pc"),
 ]
 
 

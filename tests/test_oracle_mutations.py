@@ -269,6 +269,38 @@ def _mut_moe_expert_index(mp):
     mp.setattr(OM, "ref_moe_linear", bad)
 
 
+def _mut_w4pc_groups_of_128(mp):
+    orig = OQ.quantize_w4
+
+    def bad(W, G=OQ.GROUP):                              # "per channel" quantised per 128 k
+        return orig(W, OQ.GROUP if G is None else G)
+    mp.setattr(OQ, "quantize_w4", bad)
+
+
+def _mut_w4pc_zeros_reversed(mp):
+    orig = OQ.pack
+
+    def bad(fmt, W):
+        P = orig(fmt, W)
+        if fmt == "w4pc":                                # the 8 zero-points of a word in reverse order
+            z = OQ._unpack_nibbles_rows(np.asarray(P["zeros"]).reshape(1, -1)).reshape(-1, 8)[:, ::-1]
+            P["zeros"] = OQ._pack_nibbles_rows(np.ascontiguousarray(z.reshape(1, -1))).reshape(-1)
+        return P
+    mp.setattr(OQ, "pack", bad)
+
+
+def _mut_w4pc_dequant_row0_zero(mp):
+    orig = OQ.dequant
+
+    def bad(P, rows=None):
+        if P["fmt"] != "w4pc":
+            return orig(P, rows)
+        q, s16, z = OQ.unpack_w4pc(P)                     # every row takes row 0's zero-point
+        d = (q.astype(np.float32) - np.float32(z[0])) * s16.astype(np.float32)[:, None]
+        return d if rows is None else d[np.asarray(rows)]
+    mp.setattr(OQ, "dequant", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
@@ -276,7 +308,8 @@ MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant
              _mut_sample_temperature_multiplies, _mut_sample_at_or_above, _mut_perm_inverse,
              _mut_perm_out_of_range_wraps, _mut_rel_rms_over_result,
              _mut_rel_rms_zero_reference_absolute, _mut_topk_rows_first_u, _mut_topk_rows_shifted,
-             _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index]
+             _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index,
+             _mut_w4pc_groups_of_128, _mut_w4pc_zeros_reversed, _mut_w4pc_dequant_row0_zero]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
