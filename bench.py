@@ -48,6 +48,8 @@ def algorithmic_bytes(fmt: str, K: int, N: int, M: int) -> int:
         w = K * N + 2 * N
     elif fmt == "w8g128":
         w = K * N + 2 * N * G
+    elif fmt == "w4pc":  # one scale and zero-point per row (the gfx950 layout repeats them per group)
+        w = K * N // 2 + 2 * N + (N // 8) * 4
     else:
         w = K * N // 2 + 2 * N * G + G * (N // 8) * 4
     return w + 2 * M * K + 2 * M * N
@@ -939,6 +941,9 @@ def run_detail(wq, torch, args) -> dict:
                                        for K, N in DECODE_SHAPES for M in (2, 4, 7)},
         "decode_w4g128": lambda: {f"{K}x{N}_M{M}": measure(3, "w4g128", K, N, M)
                                   for K, N in [(5120, 27648), (13824, 5120)] for M in (1, 4)},
+        # INT4 per output channel: the group-128 kernels on its repeated metadata
+        "w4_per_channel": lambda: {f"w4pc_{K}x{N}_M{M}": measure(3, "w4pc", K, N, M)
+                                   for K, N in [(5120, 27648)] for M in (1, 2048)},
         "splitk_stress": lambda: {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
                                   for K, N in [(27648, 5120), (5120, 151936)]
                                   for fmt in ("w8pc", "w8g128", "w4g128")},

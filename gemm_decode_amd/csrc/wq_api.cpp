@@ -204,10 +204,12 @@ int resolve_tile(const wq_weight* w, int64_t M) {
   return default_tile(w, M);
 }
 
-wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int split_k, int waves,
+wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int split_k, int waves,
                     int rows, void* ws, size_t ws_bytes, void* stream) {
-  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
+  const wq_weight cview = compute_view(*w0);
+  const wq_weight* w = &cview;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (M > kGemvMaxM) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   if (split_k < 0 || waves < 0 || waves > kGemvMaxWaves)
@@ -236,10 +238,12 @@ wq_status gemv_impl(const wq_weight* w, const void* x, int64_t M, void* y, int s
                      (hipStream_t)stream);
 }
 
-wq_status gemm_impl(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
+wq_status gemm_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int tile, void* ws,
                     size_t ws_bytes, void* stream) {
-  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
+  const wq_weight cview = compute_view(*w0);
+  const wq_weight* w = &cview;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
   const int t = tile == 0 ? resolve_tile(w, M) : tile;
@@ -278,12 +282,13 @@ std::string current_device_tag() {
 }
 
 wq_status check_shape(int fmt, int64_t K, int64_t N) {
-  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G128) return fail(WQ_ERR_UNSUPPORTED, "unknown format");
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "unknown format");
   if (K <= 0 || N <= 0) return fail(WQ_ERR_INVALID_ARG, "K and N must be positive");
   if (K > (1LL << 22) || N > (1LL << 30)) return fail(WQ_ERR_UNSUPPORTED, "K or N too large");
   if (K % 16) return fail(WQ_ERR_UNSUPPORTED, "K must be a multiple of 16");
-  if (fmt != WQ_FMT_W8_PC && K % kGroup) return fail(WQ_ERR_UNSUPPORTED, "group-128 formats need K % 128 == 0");
-  if (fmt == WQ_FMT_W4_G128 && N % 8) return fail(WQ_ERR_UNSUPPORTED, "W4 needs N % 8 == 0");
+  if (fmt != WQ_FMT_W8_PC && K % kGroup)
+    return fail(WQ_ERR_UNSUPPORTED, "group-128 formats and W4 per channel need K % 128 == 0");
+  if (is_w4(fmt) && N % 8) return fail(WQ_ERR_UNSUPPORTED, "W4 needs N % 8 == 0");
   return WQ_OK;
 }
 
@@ -296,13 +301,13 @@ wq_status check_weight(const wq_weight* w, int want_layout) {
                                         ? "compute kernels need the GFX950 layout (call wq_repack)"
                                         : "expected the CANONICAL layout");
   if (!w->qweight || !w->scales) return fail(WQ_ERR_INVALID_ARG, "qweight/scales must not be NULL");
-  if (w->fmt == WQ_FMT_W4_G128 && !w->zeros) return fail(WQ_ERR_INVALID_ARG, "W4 needs zeros");
+  if (is_w4(w->fmt) && !w->zeros) return fail(WQ_ERR_INVALID_ARG, "W4 needs zeros");
   if (!aligned(w->qweight, 16)) return fail(WQ_ERR_ALIGNMENT, "qweight must be 16-byte aligned");
   if (!aligned(w->scales, want_layout == WQ_LAYOUT_GFX950 && w->fmt != WQ_FMT_W8_PC ? 16 : 2))
     return fail(WQ_ERR_ALIGNMENT, "scales must be 2-byte aligned (16-byte for tiled gfx950 scales)");
-  if (w->fmt == WQ_FMT_W4_G128 && want_layout == WQ_LAYOUT_GFX950 && !aligned(w->zeros, 8))
+  if (is_w4(w->fmt) && want_layout == WQ_LAYOUT_GFX950 && !aligned(w->zeros, 8))
     return fail(WQ_ERR_ALIGNMENT, "gfx950 zeros must be 8-byte aligned");
-  if (w->fmt == WQ_FMT_W4_G128 && want_layout == WQ_LAYOUT_CANONICAL && !aligned(w->zeros, 4))
+  if (is_w4(w->fmt) && want_layout == WQ_LAYOUT_CANONICAL && !aligned(w->zeros, 4))
     return fail(WQ_ERR_ALIGNMENT, "canonical zeros must be 4-byte aligned");
   return WQ_OK;
 }
@@ -346,11 +351,15 @@ wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb,
       s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * G) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
       break;
     case WQ_FMT_W4_G128:
+    case WQ_FMT_W4_PC: {
+      // per channel: one group in the canonical layout, K/128 repeated ones in gfx950's
+      const int64_t Gc = fmt == WQ_FMT_W4_PC ? 1 : G;
       q = (size_t)(K * N / 2);
-      s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * G) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
-      z = layout == WQ_LAYOUT_CANONICAL ? (size_t)(G * (N / 8) * 4)
+      s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * Gc) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
+      z = layout == WQ_LAYOUT_CANONICAL ? (size_t)(Gc * (N / 8) * 4)
                                         : (size_t)(row_tiles(N) * G * (kGemvTileRows / 2));
       break;
+    }
   }
   if (qb) *qb = q;
   if (sb) *sb = s;
@@ -360,12 +369,12 @@ wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb,
 
 int wq_gemv_max_split(int fmt, int64_t K) {
   if (check_shape(fmt, K, 8) != WQ_OK) return -1;
-  return clamp_split(kMaxSplit, gemv_slices(K, fmt));
+  return clamp_split(kMaxSplit, gemv_slices(K, compute_fmt(fmt)));
 }
 
 int wq_gemv_max_waves(int fmt, int64_t M, int rows) {
-  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G128 || M < 1 || M > kGemvMaxM) return -1;
-  const int cap = gemv_max_waves(fmt, (int)M, rows);
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_PC || M < 1 || M > kGemvMaxM) return -1;
+  const int cap = gemv_max_waves(compute_fmt(fmt), (int)M, rows);
   return cap > 0 ? cap : -1;
 }
 
@@ -411,10 +420,12 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream) 
   return repack_common(src, dst, WQ_LAYOUT_GFX950, WQ_LAYOUT_CANONICAL, stream);
 }
 
-wq_status wq_workspace_size(const wq_weight* w, int64_t M, size_t* bytes) {
-  if (!w || !bytes) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
-  wq_status st = check_shape(w->fmt, w->K, w->N);
+wq_status wq_workspace_size(const wq_weight* w0, int64_t M, size_t* bytes) {
+  if (!w0 || !bytes) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
+  wq_status st = check_shape(w0->fmt, w0->K, w0->N);
   if (st != WQ_OK) return st;
+  const wq_weight cview = compute_view(*w0);
+  const wq_weight* w = &cview;
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
   if (M <= kGemvMaxM) {
     *bytes = gemv_workspace_bytes(w->N, M, kMaxSplit);
@@ -484,10 +495,12 @@ void* static_scratch(wq_status* st) {
 }
 }  // namespace
 
-wq_status wq_linear_static(const wq_weight* w, const void* x, int64_t M, void* y, void* stream) {
+wq_status wq_linear_static(const wq_weight* w0, const void* x, int64_t M, void* y, void* stream) {
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
-  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
+  const wq_weight cview = compute_view(*w0);
+  const wq_weight* w = &cview;
   // the workspace the configuration wq_linear would run needs (its split-K partials)
   size_t need = 0;
   if (wq_dispatch_kind(M) == WQ_KIND_GEMV) {
@@ -508,10 +521,12 @@ wq_status wq_linear_static(const wq_weight* w, const void* x, int64_t M, void* y
 }
 
 // ------------------------------------------------------- grouped (MoE) layer
-wq_status wq_moe_linear(const wq_weight* w, int E, const void* x, const int32_t* offsets, int64_t T, void* y,
+wq_status wq_moe_linear(const wq_weight* w0, int E, const void* x, const int32_t* offsets, int64_t T, void* y,
                         int epilogue, void* stream) {
-  wq_status st = check_weight(w, WQ_LAYOUT_GFX950);
+  wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
+  const wq_weight cview = compute_view(*w0);
+  const wq_weight* w = &cview;
   if (E < 1 || E > 65535) return fail(WQ_ERR_INVALID_ARG, "wq_moe_linear: E must lie in 1 .. 65535");
   if (T < 0 || T > INT32_MAX) return fail(WQ_ERR_INVALID_ARG, "wq_moe_linear: T must lie in 0 .. 2^31 - 1");
   if (epilogue != WQ_EPILOGUE_NONE && epilogue != WQ_EPILOGUE_SILU_MUL)
@@ -642,16 +657,19 @@ int wq_tune_pick(const double* lat, int n) {
   return best;
 }
 
-wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y, void* ws,
+wq_status wq_tune(const wq_weight* copies0, int n_copies, int64_t M, const void* x, void* y, void* ws,
                   size_t ws_bytes, int warmup, int iters, void* stream, int* chosen, double* lat_us) {
-  if (!copies || n_copies < 1 || !chosen || iters < 1 || warmup < 0)
+  if (!copies0 || n_copies < 1 || !chosen || iters < 1 || warmup < 0)
     return fail(WQ_ERR_INVALID_ARG, "wq_tune: bad arguments");
   wq_status st;
   for (int i = 0; i < n_copies; ++i) {
-    if ((st = check_weight(&copies[i], WQ_LAYOUT_GFX950)) != WQ_OK) return st;
-    if (copies[i].fmt != copies[0].fmt || copies[i].K != copies[0].K || copies[i].N != copies[0].N)
+    if ((st = check_weight(&copies0[i], WQ_LAYOUT_GFX950)) != WQ_OK) return st;
+    if (copies0[i].fmt != copies0[0].fmt || copies0[i].K != copies0[0].K || copies0[i].N != copies0[0].N)
       return fail(WQ_ERR_INVALID_ARG, "wq_tune: copies differ in format or shape");
   }
+  std::vector<wq_weight> views(copies0, copies0 + n_copies);  // as the compute kernels take them
+  for (wq_weight& v : views) v = compute_view(v);
+  const wq_weight* copies = views.data();
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   const bool gemv = wq_dispatch_kind(M) == WQ_KIND_GEMV;
   // GEMV candidates: every (split_k, waves) pair; GEMM candidates: the tiles
@@ -809,6 +827,7 @@ wq_status wq_tune_cache_set(const char* tag, int fmt, int64_t K, int64_t N, int6
                             int value) {
   wq_status st = check_shape(fmt, K, N);
   if (st != WQ_OK) return st;
+  fmt = compute_fmt(fmt);  // per-channel W4 runs (and is tuned) as group-128 W4
   if (M < 1 || (kind != WQ_KIND_GEMV && kind != WQ_KIND_GEMM))
     return fail(WQ_ERR_INVALID_ARG, "bad M or kind");
   if (kind == WQ_KIND_GEMV && !valid_gemv_value(value))
@@ -827,7 +846,7 @@ wq_status wq_tune_cache_get(const char* tag, int fmt, int64_t K, int64_t N, int6
   if (!value) return fail(WQ_ERR_INVALID_ARG, "value is NULL");
   const std::string t = resolve_tag(tag);
   if (t.empty()) return fail(WQ_ERR_NO_DEVICE, "no device tag");
-  if (!cache_lookup(t, fmt, K, N, M, kind, value)) return fail(WQ_ERR_INVALID_ARG, "no entry");
+  if (!cache_lookup(t, compute_fmt(fmt), K, N, M, kind, value)) return fail(WQ_ERR_INVALID_ARG, "no entry");
   return WQ_OK;
 }
 

@@ -31,6 +31,17 @@ wq_status hip_fail(hipError_t e, const char* what);
     if (e_ != hipSuccess) return ::wq::hip_fail(e_, #call);  \
   } while (0)
 
+// uint4 formats (group-128 and per output channel)
+inline bool is_w4(int fmt) { return fmt == WQ_FMT_W4_G128 || fmt == WQ_FMT_W4_PC; }
+// The compute kernels take per-channel W4 in the gfx950 layout as group-128 W4: that
+// layout repeats each row's scale and zero-point in every 128-k group.
+inline int compute_fmt(int fmt) { return fmt == WQ_FMT_W4_PC ? WQ_FMT_W4_G128 : fmt; }
+inline wq_weight compute_view(const wq_weight& w) {
+  wq_weight v = w;
+  v.fmt = (decltype(v.fmt))compute_fmt(v.fmt);
+  return v;
+}
+
 // Shape/format validation shared by every entry point (no device access).
 wq_status check_shape(int fmt, int64_t K, int64_t N);
 wq_status check_weight(const wq_weight* w, int want_layout);

@@ -157,6 +157,58 @@ __global__ __launch_bounds__(256) void pack_w4_g128_kernel(const T* __restrict__
   }
 }
 
+// W4 asymmetric per output channel, canonical layout: a block handles 8 rows, 32 lanes
+// per row, each lane 4 consecutive k of every 128 (one pass for the row's min and max,
+// a second for the codes); the 8 zero-points form one word.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_w4_pc_kernel(const T* __restrict__ w, uint32_t* __restrict__ qw,
+                                                           uint16_t* __restrict__ scales,
+                                                           uint32_t* __restrict__ zeros, int K) {
+  const int G = K / kGroup;
+  const int c8 = blockIdx.x;  // rows 8*c8 .. 8*c8+7
+  const int r = threadIdx.x >> 5, lane = threadIdx.x & 31;
+  const int n = 8 * c8 + r;
+  const size_t row = (size_t)n * K + 4 * lane;
+  float hi = -INFINITY, lo = INFINITY;
+  for (int g = 0; g < G; ++g) {
+    const float4 v = load_w4(w, row + (size_t)g * kGroup);
+    hi = fmaxf(hi, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    lo = fminf(lo, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+  }
+  hi = group_max<32>(hi);
+  lo = group_min<32>(lo);
+  const uint16_t sh = f32_to_f16_rne((hi - lo) / 15.f);
+  const float s = f16_to_f32(sh);
+  const uint32_t z = s != 0.f ? (uint32_t)fminf(fmaxf(rintf(-lo / s), 0.f), 15.f) : 0u;
+  for (int g = 0; g < G; ++g) {
+    uint32_t nib = 0;
+    if (s != 0.f) {
+      const float4 v = load_w4(w, row + (size_t)g * kGroup);
+      const float c[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float qq = fminf(fmaxf(rintf(c[j] / s) + (float)z, 0.f), 15.f);
+        nib |= ((uint32_t)qq) << (4 * j);
+      }
+    }
+    // lanes 2i and 2i+1 hold k = 8i..8i+3 and 8i+4..8i+7 of the same word
+    const uint32_t partner = (uint32_t)__shfl_xor((int)nib, 1, 32);
+    if ((lane & 1) == 0) qw[(size_t)n * (K / 8) + (size_t)g * 16 + (lane >> 1)] = nib | (partner << 16);
+  }
+  __shared__ uint32_t zs[8];
+  if (lane == 0) {
+    scales[n] = sh;
+    zs[r] = z;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= zs[j] << (4 * j);
+    zeros[c8] = word;
+  }
+}
+
 // Nibble position p of a gfx950 W4 word holds canonical nibble kPerm[p].
 __device__ __forceinline__ uint32_t nibbles_to_gfx950(uint32_t c) {
   uint32_t o = 0;
@@ -205,29 +257,31 @@ __global__ void codes_repack_kernel(const uint8_t* __restrict__ src, uint8_t* __
   }
 }
 
-// Group scales: canonical [N][G]  <->  gfx950 tiles [N16][G][16] (16 rows of one
-// group side by side; rows past N hold 0).
+// Group scales: canonical [N][Gc]  <->  gfx950 tiles [N16][G][16] (16 rows of one
+// group side by side; rows past N hold 0).  Gc = G, or 1 for per-channel W4, whose one
+// scale per row fills every group of the tiles (and is read back from group 0).
 __global__ void scales_tile_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                   int N, int G, int to_tiled) {
-  const size_t total = to_tiled ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * G;
+                                   int N, int G, int Gc, int to_tiled) {
+  const size_t total = to_tiled ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * Gc;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
     if (to_tiled) {
       const size_t t = i / ((size_t)G * kGemvTileRows), rem = i % ((size_t)G * kGemvTileRows);
       const int g = (int)(rem / kGemvTileRows), j = (int)(rem % kGemvTileRows);
       const size_t n = t * kGemvTileRows + j;
-      dst[i] = n < (size_t)N ? src[n * G + g] : (uint16_t)0;
+      dst[i] = n < (size_t)N ? src[n * Gc + (Gc == 1 ? 0 : g)] : (uint16_t)0;
     } else {
-      const size_t n = i / G, g = i % G;
+      const size_t n = i / Gc, g = i % Gc;
       dst[i] = src[((n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
     }
   }
 }
 
-// canonical zeros uint32 [G][N/8]  ->  gfx950 zeros uint8 [N16][G][8], byte (t,g,h)
-// holding z[16t+2h][g] (bits 0..3) and z[16t+2h+1][g] (bits 4..7)
+// canonical zeros uint32 [Gc][N/8]  ->  gfx950 zeros uint8 [N16][G][8], byte (t,g,h)
+// holding z[16t+2h][g] (bits 0..3) and z[16t+2h+1][g] (bits 4..7); Gc = G, or 1 for
+// per-channel W4 (its one zero-point per row in every group)
 __global__ void w4_zeros_to_gfx950_kernel(const uint32_t* __restrict__ zc, uint8_t* __restrict__ zt,
-                                          int G, int N) {
+                                          int G, int Gc, int N) {
   const size_t total = (size_t)row_tiles(N) * G * (kGemvTileRows / 2);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -237,16 +291,16 @@ __global__ void w4_zeros_to_gfx950_kernel(const uint32_t* __restrict__ zc, uint8
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const size_t n = t * kGemvTileRows + 2 * h + e;
-      if (n < (size_t)N) b |= ((zc[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu) << (4 * e);
+      if (n < (size_t)N) b |= ((zc[(size_t)(Gc == 1 ? 0 : g) * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu) << (4 * e);
     }
     zt[i] = (uint8_t)b;
   }
 }
 
-// gfx950 zeros uint8 [N16][G][8]  ->  canonical zeros uint32 [G][N/8]
+// gfx950 zeros uint8 [N16][G][8]  ->  canonical zeros uint32 [Gc][N/8] (groups 0 .. Gc - 1)
 __global__ void w4_zeros_from_gfx950_kernel(const uint8_t* __restrict__ zt, uint32_t* __restrict__ zc,
-                                            int G, int N) {
-  const size_t total = (size_t)G * (N / 8);
+                                            int G, int Gc, int N) {
+  const size_t total = (size_t)Gc * (N / 8);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
     const int g = (int)(i / (N / 8)), c = (int)(i % (N / 8));
@@ -286,6 +340,10 @@ static wq_status launch_pack_t(const T* w, const wq_weight* out, hipStream_t s) 
       pack_w4_g128_kernel<T><<<dim3(N / 8, K / kGroup), 256, 0, s>>>(
           w, (uint32_t*)out->qweight, (uint16_t*)out->scales, (uint32_t*)out->zeros, K, N);
       break;
+    case WQ_FMT_W4_PC:
+      pack_w4_pc_kernel<T><<<N / 8, 256, 0, s>>>(w, (uint32_t*)out->qweight, (uint16_t*)out->scales,
+                                                (uint32_t*)out->zeros, K);
+      break;
     default:
       return fail(WQ_ERR_UNSUPPORTED, "wq_pack: unknown format");
   }
@@ -303,10 +361,11 @@ wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx9
   wq_status st = wq_packed_sizes(src->fmt, WQ_LAYOUT_CANONICAL, src->K, src->N, &qb, &sb, &zb);
   if (st != WQ_OK) return st;
   const int G = (int)(src->K / kGroup), N = (int)src->N;
+  const int Gc = src->fmt == WQ_FMT_W4_PC ? 1 : G;  // canonical groups per row
   const int64_t row_bytes = (int64_t)(qb / (size_t)N);
   const size_t chunks = qb / 16;
   // codes
-  if (src->fmt == WQ_FMT_W4_G128) {
+  if (is_w4(src->fmt)) {
     codes_repack_kernel<true><<<grid_for(chunks, 256), 256, 0, s>>>(
         (const uint8_t*)src->qweight, (uint8_t*)dst->qweight, N, row_bytes, to_gfx950);
   } else {
@@ -318,19 +377,19 @@ wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx9
   if (src->fmt == WQ_FMT_W8_PC) {
     WQ_HIP_CHECK(hipMemcpyAsync(dst->scales, src->scales, sb, hipMemcpyDeviceToDevice, s));
   } else {
-    const size_t n = to_gfx950 ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * G;
+    const size_t n = to_gfx950 ? (size_t)row_tiles(N) * G * kGemvTileRows : (size_t)N * Gc;
     scales_tile_kernel<<<grid_for(n, 256), 256, 0, s>>>((const uint16_t*)src->scales,
-                                                        (uint16_t*)dst->scales, N, G, to_gfx950);
+                                                        (uint16_t*)dst->scales, N, G, Gc, to_gfx950);
     WQ_HIP_CHECK(hipGetLastError());
   }
   // zero-points
-  if (src->fmt == WQ_FMT_W4_G128) {
+  if (is_w4(src->fmt)) {
     if (to_gfx950) {
       w4_zeros_to_gfx950_kernel<<<grid_for((size_t)row_tiles(N) * G * 8, 256), 256, 0, s>>>(
-          (const uint32_t*)src->zeros, (uint8_t*)dst->zeros, G, N);
+          (const uint32_t*)src->zeros, (uint8_t*)dst->zeros, G, Gc, N);
     } else {
-      w4_zeros_from_gfx950_kernel<<<grid_for((size_t)G * (N / 8), 256), 256, 0, s>>>(
-          (const uint8_t*)src->zeros, (uint32_t*)dst->zeros, G, N);
+      w4_zeros_from_gfx950_kernel<<<grid_for((size_t)Gc * (N / 8), 256), 256, 0, s>>>(
+          (const uint8_t*)src->zeros, (uint32_t*)dst->zeros, G, Gc, N);
     }
     WQ_HIP_CHECK(hipGetLastError());
   }

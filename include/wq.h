@@ -55,7 +55,8 @@ typedef enum {
 typedef enum {
   WQ_FMT_W8_PC = 0,    /* int8, symmetric, one bf16 scale per output channel       */
   WQ_FMT_W8_G128 = 1,  /* int8, symmetric, one bf16 scale per 128 consecutive k     */
-  WQ_FMT_W4_G128 = 2   /* uint4, asymmetric, fp16 scale + uint4 zero per 128 k      */
+  WQ_FMT_W4_G128 = 2,  /* uint4, asymmetric, fp16 scale + uint4 zero per 128 k      */
+  WQ_FMT_W4_PC = 3     /* uint4, asymmetric, fp16 scale + uint4 zero per channel    */
 } wq_format;
 
 /* Memory layouts of a packed weight.
@@ -65,6 +66,7 @@ typedef enum {
  *   W4:  qweight uint32 [N][K/8], bits 4j..4j+3 of word (n,c) hold q[n][8c+j];
  *        scales fp16 [N][K/128];
  *        zeros uint32 [K/128][N/8], bits 4j..4j+3 of word (g,c) hold z[8c+j][g].
+ *   W4 per channel: as W4 with one group: scales fp16 [N]; zeros uint32 [N/8].
  *
  * WQ_LAYOUT_GFX950 (what the compute kernels read; written by wq_repack).  N16 =
  * ceil(N/16) tiles of 16 output rows; metadata entries for rows >= N are 0.
@@ -85,6 +87,11 @@ typedef enum {
  *        scales fp16 [N16][G][16] as for W8 group-128;
  *        zeros uint8 [N16][G][8], byte (t,g,h) holds z[16t+2h][g] in bits 0..3 and
  *        z[16t+2h+1][g] in bits 4..7.
+ *   W4 per channel: exactly the W4 group-128 layout (same sizes) with each row's one
+ *        scale and zero-point written into every one of its K/128 groups, so that the
+ *        group-128 kernels compute it unchanged (the group scales multiply equal
+ *        factors: the same products in another fp32 summation order); wq_unrepack
+ *        reads the first group back.
  */
 typedef enum { WQ_LAYOUT_CANONICAL = 0, WQ_LAYOUT_GFX950 = 1 } wq_layout;
 
@@ -114,8 +121,8 @@ const char* wq_status_string(int status);
 const char* wq_last_error(void);
 
 /* Bytes of qweight, scales and zeros for a format/layout/shape (host only, no
- * device access).  Shape rules: K > 0, N > 0, K % 16 == 0; group-128 formats need
- * K % 128 == 0; W4 needs N % 8 == 0.  zero_bytes is 0 for W8.  Any out-pointer
+ * device access).  Shape rules: K > 0, N > 0, K % 16 == 0; group-128 formats and W4
+ * per channel need K % 128 == 0; W4 needs N % 8 == 0.  zero_bytes is 0 for W8.  Any out-pointer
  * may be NULL. */
 wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qweight_bytes,
                           size_t* scale_bytes, size_t* zero_bytes);
@@ -134,7 +141,9 @@ int wq_dispatch_kind(int64_t M);
  *   W8 (group G = K for per-channel, 128 otherwise):
  *     a = max|w| over the group; s = bf16(a / 127);
  *     q = 0 if s == 0 else clamp(rint(w / s), -127, 127)   (divides by the stored s)
- *   W4 (group 128): hi = max w, lo = min w; s = fp16((hi - lo) / 15);
+ *   W4 (group 128, or one group per output channel for WQ_FMT_W4_PC: the INT4
+ *   per-channel case of the Marlin page's "Validation and limits"):
+ *     hi = max w, lo = min w over the group; s = fp16((hi - lo) / 15);
  *     s == 0 -> z = 0, q = 0; else z = clamp(rint(-lo / s), 0, 15),
  *     q = clamp(rint(w / s) + z, 0, 15).
  * The output is bit-exact and deterministic.  `w` must not alias the outputs. */

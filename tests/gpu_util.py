@@ -51,6 +51,9 @@ def canonical_to_host(can, fmt: str) -> dict:
         return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.int8).reshape(N, K),
                     scales=s.view(np.uint16).reshape(N, K // 128))
     z = can.zeros.cpu().numpy()
+    if fmt == "w4pc":
+        return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.uint32).reshape(N, K // 8),
+                    scales=s.view(np.float16).reshape(N), zeros=z.view(np.uint32).reshape(N // 8))
     return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.uint32).reshape(N, K // 8),
                 scales=s.view(np.float16).reshape(N, K // 128), zeros=z.view(np.uint32).reshape(K // 128, N // 8))
 

@@ -320,3 +320,26 @@ def test_moe_linear_host_validation(wqlib):
     d3 = wqlib.WqWeightC(wqlib.FMT["w8pc"], wqlib.CANONICAL, 1024, 64, 1 << 20, 1 << 20, 0)
     assert L.wq_moe_linear(C.byref(d3), 4, p, p, 8, p, 0, None) == 2                # layout
     assert L.wq_moe_linear(C.byref(d2), 4, p, p, 0, p, 0, None) != 0                # (K % 128 first)
+
+
+def test_w4_per_channel_host_side(wqlib):
+    """INT4 per channel (fmt 3): canonical sizes as the oracle's, the gfx950 layout the
+    size of group-128's (each row's scale and zero-point repeated per group), the shape
+    rules (K % 128, N % 8), zeros required, and the tuner cache shared with group-128 W4
+    (the same kernels run both)."""
+    for K, N in ((1024, 1024), (5120, 27648), (13824, 5120)):
+        assert wqlib.wq_packed_sizes("w4pc", wqlib.CANONICAL, K, N) == OQ.packed_sizes("w4pc", K, N)
+        assert wqlib.wq_packed_sizes("w4pc", wqlib.GFX950, K, N) == wqlib.wq_packed_sizes("w4g128", wqlib.GFX950, K, N)
+    for K, N in ((1040, 64), (1024, 60)):
+        with pytest.raises(wqlib.WqError) as e:
+            wqlib.wq_packed_sizes("w4pc", wqlib.CANONICAL, K, N)
+        assert e.value.status == 2
+    L = wqlib.lib
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    d = wqlib.WqWeightC(wqlib.FMT["w4pc"], wqlib.GFX950, 1024, 64, 0x1000, 0x2000, 0)
+    assert L.wq_gemv(C.byref(d), x, 1, y, 1, None, 0, None) == 1          # W4 without zeros
+    assert wqlib.wq_gemv_max_split("w4pc", 5120) == wqlib.wq_gemv_max_split("w4g128", 5120)
+    tag = "test-w4pc:0"
+    wqlib.wq_tune_cache_set("w4pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(2, 4, 8), tag)
+    assert wqlib.wq_tune_cache_get("w4g128", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
+    assert wqlib.wq_tune_cache_get("w4pc", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
