@@ -8,8 +8,8 @@ library in ``gemm_decode_amd/`` and imports nothing from it.
 What it computes (plain, slow, obviously correct; NumPy only):
 
 * ``quant``  -- the quantisers and the canonical packed layouts (W8 per output
-  channel, W8 group-128, W4 asymmetric group-128 and per output channel), step by
-  step.
+  channel and with groups of 32, 64 or 128; W4 asymmetric with groups of 32, 64 or
+  128 and per output channel), step by step.
 * ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
   chunked along N; sampled-column variants for full-size checks; the
   comparison statistics with the per-element tolerance; the full-K activation
@@ -28,7 +28,8 @@ Passages followed:
   activations; decode multiplies the dequantised weights in registers, prefill
   dequantises to bf16 on the fly before a GEMM.
 * "Marlin register and launch scheduling benchmark", "Validation and limits":
-  INT4 and INT8 weights with bf16 activations, per-channel and group-128 scales.
+  INT4 and INT8 weights with bf16 activations, per-channel scales and groups of
+  32, 64 and 128.
 * "Heuristic: Mit han lab Llm awq Kernel Selection Thresholds", code excerpt
   from awq/quantize/qmodule.py: the token count is numel(x) / x.shape[-1].
 
@@ -37,8 +38,8 @@ hand-derived worked examples (``tests/golden/``), closed-form error bounds,
 brute force on tiny inputs and reductions to NumPy library routines.
 """
 from .quant import (  # noqa: F401
-    FORMATS, GROUP, W4PC, bf16_bits_to_f32, bf16_rne_bits, dequant, pack, packed_sizes,
-    quantize_w4, quantize_w4g128, quantize_w8, unpack_w4g128, unpack_w4pc,
+    FORMATS, GROUP, GROUPED, SMALL_GROUPS, W4PC, bf16_bits_to_f32, bf16_rne_bits, dequant, pack,
+    packed_sizes, quantize_w4, quantize_w4g128, quantize_w8, unpack_w4g, unpack_w4g128, unpack_w4pc,
 )
 from .linear import (  # noqa: F401
     compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, token_count, use_gemv,

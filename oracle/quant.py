@@ -18,16 +18,21 @@ group-128 INT8 head of the Marlin benchmark page, "Full inference"):
      stored (rounded) scale
   layout: q int8 [N, K] row-major; s bf16 [N, K/G].
 
+W8 also takes groups of 32 and 64 (the same three steps with G = 32 or 64: the
+Marlin page's "Validation and limits" lists per-channel scales and groups of 32, 64
+and 128): layout q int8 [N, K] row-major; s bf16 [N, K/G].
+
 W4 asymmetric, one scale and zero-point per group of G consecutive k (G = 128:
-INT4 + group 128; G = K: INT4 per output channel -- both in the Marlin page's
-"Validation and limits", which lists INT4 with per-channel and group scales):
+INT4 + group 128; G = 32 or 64: the smaller groups of the same list; G = K: INT4
+per output channel -- all in the Marlin page's "Validation and limits", which lists
+INT4 with per-channel and group scales):
   1. hi = max w, lo = min w over the group
   2. s = fp16((hi - lo) / 15)                       -- the stored scale
   3. if s == 0: z = 0, q = 0
      else z = clamp(rint(-lo / s), 0, 15); q = clamp(rint(w / s) + z, 0, 15)
   layout: qweight uint32 [N, K/8], bits 4j..4j+3 of word (n, c) hold q[n, 8c+j];
-          group 128:   scales fp16 [N, K/128];
-                       zeros uint32 [K/128, N/8], bits 4j..4j+3 of word (g, c) hold z[8c+j, g];
+          group G (32, 64, 128): scales fp16 [N, K/G];
+                       zeros uint32 [K/G, N/8], bits 4j..4j+3 of word (g, c) hold z[8c+j, g];
           per channel: scales fp16 [N]; zeros uint32 [N/8], bits 4j..4j+3 of word c
                        hold z[8c+j] (the group-128 layout with one group).
 
@@ -40,6 +45,10 @@ import numpy as np
 GROUP = 128
 FORMATS = ("w8pc", "w8g128", "w4g128")
 W4PC = "w4pc"  # INT4 per output channel (tested on its own; FORMATS are the configs' formats)
+# every grouped format and its group size along K (the g32 / g64 variants are tested on
+# their own, like W4PC)
+GROUPED = {"w8g32": 32, "w8g64": 64, "w8g128": 128, "w4g32": 32, "w4g64": 64, "w4g128": 128}
+SMALL_GROUPS = ("w8g32", "w8g64", "w4g32", "w4g64")
 
 
 # ---------------------------------------------------------------- conversions
@@ -142,13 +151,13 @@ def pack(fmt: str, W: np.ndarray) -> dict:
     if fmt == "w8pc":
         q, s = quantize_w8(W, None)
         return dict(fmt=fmt, K=K, N=N, qweight=q, scales=s.reshape(N))
-    if fmt == "w8g128":
-        q, s = quantize_w8(W, GROUP)
+    if fmt.startswith("w8g") and fmt in GROUPED:
+        q, s = quantize_w8(W, GROUPED[fmt])
         return dict(fmt=fmt, K=K, N=N, qweight=q, scales=s)
-    if fmt == "w4g128":
+    if fmt.startswith("w4g") and fmt in GROUPED:
         if N % 8:
             raise ValueError("W4 needs N % 8 == 0 (zeros are packed 8 per word along N)")
-        q, s16, z = quantize_w4g128(W)
+        q, s16, z = quantize_w4g128(W) if fmt == "w4g128" else quantize_w4(W, GROUPED[fmt])
         return dict(fmt=fmt, K=K, N=N, qweight=_pack_nibbles_rows(q), scales=s16,
                     zeros=_pack_nibbles_rows(np.ascontiguousarray(z.T)))
     if fmt == W4PC:
@@ -160,11 +169,14 @@ def pack(fmt: str, W: np.ndarray) -> dict:
     raise ValueError(f"unknown format {fmt!r}")
 
 
-def unpack_w4g128(P: dict):
-    """Canonical W4 words -> (q [N, K] uint8, s fp16 [N, K/128], z [N, K/128] uint8)."""
+def unpack_w4g(P: dict):
+    """Canonical grouped W4 words -> (q [N, K] uint8, s fp16 [N, K/G], z [N, K/G] uint8)."""
     q = _unpack_nibbles_rows(P["qweight"])
     z = np.ascontiguousarray(_unpack_nibbles_rows(P["zeros"]).T)
     return q, P["scales"], z
+
+
+unpack_w4g128 = unpack_w4g
 
 
 def unpack_w4pc(P: dict):
@@ -178,10 +190,11 @@ def packed_sizes(fmt: str, K: int, N: int):
     """Bytes of (qweight, scales, zeros) in the canonical layout."""
     if fmt == "w8pc":
         return K * N, 2 * N, 0
-    if fmt == "w8g128":
-        return K * N, 2 * N * (K // GROUP), 0
-    if fmt == "w4g128":
-        return K * N // 2, 2 * N * (K // GROUP), (K // GROUP) * (N // 8) * 4
+    if fmt.startswith("w8g") and fmt in GROUPED:
+        return K * N, 2 * N * (K // GROUPED[fmt]), 0
+    if fmt.startswith("w4g") and fmt in GROUPED:
+        G = GROUPED[fmt]
+        return K * N // 2, 2 * N * (K // G), (K // G) * (N // 8) * 4
     if fmt == W4PC:
         return K * N // 2, 2 * N, (N // 8) * 4
     raise ValueError(fmt)
@@ -192,20 +205,19 @@ def dequant(P: dict, rows=None) -> np.ndarray:
     """Exact fp32 dequantised weight Wd[N, K] (or only the given output rows)."""
     fmt, K = P["fmt"], P["K"]
     sel = slice(None) if rows is None else np.asarray(rows)
-    if fmt in ("w8pc", "w8g128"):
+    if fmt == "w8pc" or (fmt.startswith("w8g") and fmt in GROUPED):
         q = P["qweight"][sel].astype(np.float32)
         s = bf16_bits_to_f32(P["scales"][sel])
         if fmt == "w8pc":
             return q * s[:, None]
-        n = q.shape[0]
-        return (q.reshape(n, K // GROUP, GROUP) * s[:, :, None]).reshape(n, K)
-    if fmt == "w4g128":
-        q, s16, z = unpack_w4g128(dict(qweight=P["qweight"][sel], scales=P["scales"][sel],
-                                       zeros=P["zeros"]))
+        n, G = q.shape[0], GROUPED[fmt]
+        return (q.reshape(n, K // G, G) * s[:, :, None]).reshape(n, K)
+    if fmt.startswith("w4g") and fmt in GROUPED:
+        q, s16, z = unpack_w4g(dict(qweight=P["qweight"][sel], scales=P["scales"][sel], zeros=P["zeros"]))
         if rows is not None:
             z = z[np.asarray(rows)]
-        n = q.shape[0]
-        d = q.astype(np.float32).reshape(n, K // GROUP, GROUP) - z.astype(np.float32)[:, :, None]
+        n, G = q.shape[0], GROUPED[fmt]
+        d = q.astype(np.float32).reshape(n, K // G, G) - z.astype(np.float32)[:, :, None]
         return (d * s16.astype(np.float32)[:, :, None]).reshape(n, K)
     if fmt == W4PC:
         q, s16, z = unpack_w4pc(dict(qweight=P["qweight"][sel], scales=P["scales"][sel], zeros=P["zeros"]))

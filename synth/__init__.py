@@ -106,7 +106,7 @@ CONFIGS = {
 
 def uses_outliers(fmt: str) -> bool:
     """W4 workloads carry the 1% x8 outliers; W8 workloads are plain Gaussian."""
-    return fmt in ("w4g128", "w4pc")
+    return fmt.startswith("w4")
 
 
 def moe_offsets(seed: int, T: int, E: int, empty=()) -> np.ndarray:

@@ -62,17 +62,23 @@ def _decode_w4pc_zero(P: dict, n: int) -> int:
     return (word >> (4 * (n % 8))) & 0xF
 
 
+def _group_of(fmt: str) -> int:
+    """Group size spelled in a grouped format's name (w8g32 -> 32, w4g128 -> 128)."""
+    return int(fmt[3:])
+
+
 def _exact_dequant(P: dict, n: int, k: int) -> Fraction:
     fmt = P["fmt"]
     if fmt == "w4pc":
         return (_decode_w4_codes(P, n, k) - _decode_w4pc_zero(P, n)) * _fp16_value(P["scales"][n])
     if fmt == "w8pc":
         return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n]))
-    if fmt == "w8g128":
-        return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n, k // 128]))
+    g = k // _group_of(fmt)
+    if fmt.startswith("w8g"):
+        return int(P["qweight"][n, k]) * _bf16_bits_value(int(P["scales"][n, g]))
     q = _decode_w4_codes(P, n, k)
-    z = _decode_w4_zero(P, n, k // 128)
-    return (q - z) * _fp16_value(P["scales"][n, k // 128])
+    z = _decode_w4_zero(P, n, g)
+    return (q - z) * _fp16_value(P["scales"][n, g])
 
 
 # ------------------------------------------------------------------ conversions
@@ -202,6 +208,75 @@ def pin_w4pc_roundtrip_bound(seed=13, N=32, K=1024):
             assert abs(float(W[n, k]) - wd) <= s[n] / 2 + span[n] * 2.0 ** -11 + abs(float(W[n, k])) * 2.0 ** -22, (n, k)
 
 
+def pin_golden_small_groups():
+    """Groups of 32 and 64 against tests/golden/small_groups_worked.txt: groups built
+    from the hand-derived per-channel rows, repeated, take those rows' codes, scales
+    and zero-points, group by group, in the canonical layout."""
+    head, _ = read_fixture("small_groups_worked.txt")
+    _, b4 = read_fixture("w4pc_worked.txt")
+    h4, _ = read_fixture("w4pc_worked.txt")
+    W4 = np.array([[float(t) for t in r] for r in b4["W"]], dtype=np.float32)
+    q4 = [[int(t) for t in r] for r in b4["q"]]
+    s4 = [num(t) for t in h4["s_bits"]]
+    z4 = [int(t) for t in h4["z"]]
+    _, b8 = read_fixture("w8pc_worked.txt")
+    W8 = np.array([[float(t) for t in r] for r in b8["W"]], dtype=np.float32)
+    q8 = [[int(float(t)) for t in r] for r in b8["q"]]
+    s8 = [num(r[0]) for r in b8["s_bits"]]
+    for G in (32, 64):
+        rep = G // 8
+        W = np.zeros((8, 2 * G), dtype=np.float32)
+        for n in range(8):
+            for g in range(2):
+                W[n, g * G:(g + 1) * G] = np.tile(W4[(n + g) % 8], rep)
+        P = OQ.pack(f"w4g{G}", W)
+        assert P["scales"].shape == (8, 2) and np.asarray(P["zeros"]).shape == (2, 1)
+        for n in range(8):
+            for g in range(2):
+                src = (n + g) % 8
+                assert int(np.asarray(P["scales"][n, g]).view(np.uint16)) == s4[src], (G, n, g)
+                assert _decode_w4_zero(P, n, g) == z4[src], (G, n, g)
+                assert [_decode_w4_codes(P, n, g * G + k) for k in range(G)] == q4[src] * rep, (G, n, g)
+        assert [int(w) for w in np.asarray(P["zeros"])[:, 0]] == [num(t) for t in head["w4_zeros_words"]]
+        assert int(P["qweight"][3, 0]) == num(head["w4_row3_word0"][0])
+        assert int(P["qweight"][3, G // 8]) == num(head["w4_row3_group1_word0"][0])
+        Wd = OQ.dequant(P)
+        for n in range(8):
+            for k in range(0, 2 * G, 3):
+                assert Fraction(float(Wd[n, k])) == _exact_dequant(P, n, k), (G, n, k)
+        W = np.zeros((3, 2 * G), dtype=np.float32)
+        for n in range(3):
+            for g in range(2):
+                W[n, g * G:(g + 1) * G] = np.tile(W8[(n + g) % 3], rep)
+        P = OQ.pack(f"w8g{G}", W)
+        for n in range(3):
+            for g in range(2):
+                assert int(P["scales"][n, g]) == s8[(n + g) % 3], (G, n, g)
+                assert [int(v) for v in P["qweight"][n, g * G:(g + 1) * G]] == q8[(n + g) % 3] * rep
+        assert [int(v) for v in P["scales"][0]] == [num(t) for t in head["w8_scales_row0"]]
+        assert [int(v) for v in P["scales"][2]] == [num(t) for t in head["w8_scales_row2"]]
+
+
+def pin_small_groups_are_per_channel_blocks(seed=14, N=24, K=256):
+    """A group of G columns is quantised as a per-channel row of its own: every block of
+    G columns of a grouped pack equals the per-channel pack of that block alone (codes,
+    scales and zero-points, bit for bit, each in its layout's place)."""
+    W = synth.weight(seed, K, N, outliers=True)
+    for G in (32, 64):
+        P8, P4 = OQ.pack(f"w8g{G}", W), OQ.pack(f"w4g{G}", W)
+        for b in range(K // G):
+            blk = np.ascontiguousarray(W[:, b * G:(b + 1) * G])
+            C8, C4 = OQ.pack("w8pc", blk), OQ.pack("w4pc", blk)
+            assert np.array_equal(P8["qweight"][:, b * G:(b + 1) * G], C8["qweight"]), (G, b)
+            assert np.array_equal(P8["scales"][:, b], C8["scales"]), (G, b)
+            assert np.array_equal(P4["qweight"][:, b * G // 8:(b + 1) * G // 8], C4["qweight"]), (G, b)
+            assert np.array_equal(np.asarray(P4["scales"]).view(np.uint16)[:, b],
+                                  np.asarray(C4["scales"]).view(np.uint16)), (G, b)
+            assert np.array_equal(np.asarray(P4["zeros"])[b], np.asarray(C4["zeros"]).reshape(-1)), (G, b)
+        assert OQ.packed_sizes(f"w4g{G}", K, N) == (P4["qweight"].nbytes, P4["scales"].nbytes, P4["zeros"].nbytes)
+        assert OQ.packed_sizes(f"w8g{G}", K, N)[:2] == (P8["qweight"].nbytes, P8["scales"].nbytes)
+
+
 def pin_nibble_layout():
     head, _ = read_fixture("nibble_layout.txt")
     K, N = 16, 8
@@ -246,17 +321,17 @@ def pin_w8_roundtrip_bound(seed=7, N=64, K=1024, G=None):
         assert abs(got - exact) <= exact * Fraction(1, 2 ** 8) * Fraction(1001, 1000)
 
 
-def pin_w4_roundtrip_bound(seed=8, N=64, K=1024):
+def pin_w4_roundtrip_bound(seed=8, N=64, K=1024, G=128):
     """P2: unclamped codes are within s/2 (+ slack); clamped ones within
     s/2 + (hi - lo) * 2^-11 (the fp16 rounding of the scale)."""
     W = synth.weight(seed, K, N, outliers=True)
-    q, s16, z = OQ.quantize_w4g128(W)
-    s = np.repeat(s16.astype(np.float64), 128, axis=1)
-    zf = np.repeat(z.astype(np.float64), 128, axis=1)
+    q, s16, z = OQ.quantize_w4g128(W) if G == 128 else OQ.quantize_w4(W, G)
+    s = np.repeat(s16.astype(np.float64), G, axis=1)
+    zf = np.repeat(z.astype(np.float64), G, axis=1)
     wd = (q.astype(np.float64) - zf) * s
     err = np.abs(W.astype(np.float64) - wd)
-    Wg = W.reshape(N, -1, 128).astype(np.float64)
-    rng_ = np.repeat(Wg.max(axis=2) - Wg.min(axis=2), 128, axis=1)
+    Wg = W.reshape(N, -1, G).astype(np.float64)
+    rng_ = np.repeat(Wg.max(axis=2) - Wg.min(axis=2), G, axis=1)
     assert np.all(err <= s / 2 + rng_ * 2.0 ** -11 + np.abs(W) * 2.0 ** -22)
     assert q.max() <= 15 and z.max() <= 15
 
@@ -329,7 +404,7 @@ def pin_one_hot_golden():
 def pin_one_hot_random(fmt="w8g128", K=512, N=40):
     W = synth.weight(11, K, N, outliers=fmt.startswith("w4"))
     P = OQ.pack(fmt, W)
-    ks = [0, 127, 128, 300, K - 1]
+    ks = [0, 31, 32, 63, 64, 127, 128, 300, K - 1]   # both sides of every group edge size
     y = OL.ref_linear(synth.one_hot_activation(K, ks), P)
     for m, k in enumerate(ks):
         for n in range(N):
@@ -632,6 +707,13 @@ ALL_PINS = [
     pin_topk_sampling_closed_forms, pin_activation_permutation, pin_silu_closed_forms, pin_moe_grouping,
     pin_golden_w4pc, pin_w4pc_one_group_is_group128, pin_w4pc_roundtrip_bound,
     lambda: pin_bruteforce("w4pc", 64), lambda: pin_one_hot_random("w4pc"),
+    pin_golden_small_groups, pin_small_groups_are_per_channel_blocks,
+    lambda: pin_w8_roundtrip_bound(G=32), lambda: pin_w4_roundtrip_bound(G=32),
+    lambda: pin_w4_roundtrip_bound(G=64),
+    lambda: pin_bruteforce("w8g32", 64), lambda: pin_bruteforce("w8g64", 128),
+    lambda: pin_bruteforce("w4g32", 96), lambda: pin_bruteforce("w4g64", 128),
+    lambda: pin_one_hot_random("w8g32"), lambda: pin_one_hot_random("w8g64"),
+    lambda: pin_one_hot_random("w4g32"), lambda: pin_one_hot_random("w4g64"),
 ]
 
 

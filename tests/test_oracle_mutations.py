@@ -301,6 +301,50 @@ def _mut_w4pc_dequant_row0_zero(mp):
     mp.setattr(OQ, "dequant", bad)
 
 
+def _mut_small_groups_quantised_per_128(mp):
+    orig = OQ.pack
+
+    def bad(fmt, W):                                     # the g32 / g64 formats quantised in 128s
+        if fmt in OQ.SMALL_GROUPS:
+            P = orig(fmt[:3] + "128", W)
+            P["fmt"] = fmt
+            G = OQ.GROUPED[fmt]
+            r = 128 // G                                  # ... with the scales spread to their shape
+            P["scales"] = np.repeat(P["scales"], r, axis=1)
+            if "zeros" in P:
+                P["zeros"] = np.repeat(P["zeros"], r, axis=0)
+            return P
+        return orig(fmt, W)
+    mp.setattr(OQ, "pack", bad)
+
+
+def _mut_small_group_zeros_not_transposed(mp):
+    orig = OQ.pack
+
+    def bad(fmt, W):
+        P = orig(fmt, W)
+        if fmt in ("w4g32", "w4g64"):                    # zero-points packed along K, not along N
+            q, s16, z = OQ.quantize_w4(W, OQ.GROUPED[fmt])
+            zp = np.zeros((z.shape[0], -(-z.shape[1] // 8) * 8), dtype=np.uint8)
+            zp[:, :z.shape[1]] = z                        # each row's groups in one run of words
+            P["zeros"] = np.resize(OQ._pack_nibbles_rows(zp).reshape(-1), np.asarray(P["zeros"]).shape)
+        return P
+    mp.setattr(OQ, "pack", bad)
+
+
+def _mut_small_group_dequant_tiles_scales(mp):
+    orig = OQ.dequant
+
+    def bad(P, rows=None):
+        if P["fmt"] not in OQ.SMALL_GROUPS or not P["fmt"].startswith("w8"):
+            return orig(P, rows)
+        q = P["qweight"].astype(np.float32)              # column k takes group k % (K/G), not k // G
+        s = OQ.bf16_bits_to_f32(P["scales"])
+        d = q * np.tile(s, (1, OQ.GROUPED[P["fmt"]]))
+        return d if rows is None else d[np.asarray(rows)]
+    mp.setattr(OQ, "dequant", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
@@ -309,7 +353,9 @@ MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant
              _mut_perm_out_of_range_wraps, _mut_rel_rms_over_result,
              _mut_rel_rms_zero_reference_absolute, _mut_topk_rows_first_u, _mut_topk_rows_shifted,
              _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index,
-             _mut_w4pc_groups_of_128, _mut_w4pc_zeros_reversed, _mut_w4pc_dequant_row0_zero]
+             _mut_w4pc_groups_of_128, _mut_w4pc_zeros_reversed, _mut_w4pc_dequant_row0_zero,
+             _mut_small_groups_quantised_per_128, _mut_small_group_zeros_not_transposed,
+             _mut_small_group_dequant_tiles_scales]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
