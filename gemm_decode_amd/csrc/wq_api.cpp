@@ -160,8 +160,10 @@ int default_tile(const wq_weight* w, int64_t M) {
     // against 30.8 us; int8 (5120, 7168) 12.5 us against 13.8 us up to 12 tokens, while
     // the skinny kernel stays ahead for int8 on wide N or long K
     if (w->fmt == WQ_FMT_W4_G128) return w->N >= 16384 ? kMmaTile0 + 2 : kMmaTile0 + 1;
+    if (small_group(w->fmt)) return kDma64Tile0;  // no matrix-core GEMV or skinny tile for them
     if (w->N < 16384 && w->K < 8192 && M <= 12) return kMmaTile0 + 1;
   }
+  if (M <= kSkinnyMaxM && small_group(w->fmt)) return kDma64Tile0;
   if (M <= kSkinnyMaxM) {
     const int64_t blocks = (w->N + 127) / 128;
     int t = kSkinnyTile0;
@@ -200,8 +202,8 @@ int default_tile(const wq_weight* w, int64_t M) {
 
 int resolve_tile(const wq_weight* w, int64_t M) {
   int v = 0;
-  if (cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMM, &v)) return v;
-  return default_tile(w, M);
+  if (!cache_lookup(current_device_tag(), w->fmt, w->K, w->N, M, WQ_KIND_GEMM, &v)) v = default_tile(w, M);
+  return small_group(w->fmt) ? small_group_tile(v) : v;
 }
 
 wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int split_k, int waves,
@@ -246,7 +248,7 @@ wq_status gemm_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int 
   const wq_weight* w = &cview;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
-  const int t = tile == 0 ? resolve_tile(w, M) : tile;
+  const int t = tile == 0 ? resolve_tile(w, M) : small_group(w->fmt) ? small_group_tile(tile) : tile;
   if (tile != 0 && gemm_workspace_bytes(w->fmt, w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, w->N, M, t)))
     return fail(WQ_ERR_WORKSPACE, "wq_gemm: tile " + std::to_string(t) + " needs a workspace of " +
                                       std::to_string(gemm_workspace_bytes(w->fmt, w->N, M, t)) + " bytes");
@@ -282,12 +284,12 @@ std::string current_device_tag() {
 }
 
 wq_status check_shape(int fmt, int64_t K, int64_t N) {
-  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "unknown format");
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G64) return fail(WQ_ERR_UNSUPPORTED, "unknown format");
   if (K <= 0 || N <= 0) return fail(WQ_ERR_INVALID_ARG, "K and N must be positive");
   if (K > (1LL << 22) || N > (1LL << 30)) return fail(WQ_ERR_UNSUPPORTED, "K or N too large");
   if (K % 16) return fail(WQ_ERR_UNSUPPORTED, "K must be a multiple of 16");
   if (fmt != WQ_FMT_W8_PC && K % kGroup)
-    return fail(WQ_ERR_UNSUPPORTED, "group-128 formats and W4 per channel need K % 128 == 0");
+    return fail(WQ_ERR_UNSUPPORTED, "grouped formats and W4 per channel need K % 128 == 0");
   if (is_w4(fmt) && N % 8) return fail(WQ_ERR_UNSUPPORTED, "W4 needs N % 8 == 0");
   return WQ_OK;
 }
@@ -342,14 +344,18 @@ wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qb,
   if (st != WQ_OK) return st;
   if (layout != WQ_LAYOUT_CANONICAL && layout != WQ_LAYOUT_GFX950)
     return fail(WQ_ERR_UNSUPPORTED, "unknown layout");
-  const int64_t G = K / kGroup;
+  const int64_t G = fmt == WQ_FMT_W8_PC ? 0 : K / meta_group(fmt);  // groups per row (gfx950 metadata)
   size_t q = 0, s = 0, z = 0;
   switch (fmt) {
     case WQ_FMT_W8_PC: q = (size_t)(K * N); s = (size_t)(2 * N); break;
+    case WQ_FMT_W8_G32:
+    case WQ_FMT_W8_G64:
     case WQ_FMT_W8_G128:
       q = (size_t)(K * N);
       s = layout == WQ_LAYOUT_CANONICAL ? (size_t)(2 * N * G) : (size_t)(2 * row_tiles(N) * G * kGemvTileRows);
       break;
+    case WQ_FMT_W4_G32:
+    case WQ_FMT_W4_G64:
     case WQ_FMT_W4_G128:
     case WQ_FMT_W4_PC: {
       // per channel: one group in the canonical layout, K/128 repeated ones in gfx950's
@@ -373,7 +379,7 @@ int wq_gemv_max_split(int fmt, int64_t K) {
 }
 
 int wq_gemv_max_waves(int fmt, int64_t M, int rows) {
-  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_PC || M < 1 || M > kGemvMaxM) return -1;
+  if (fmt < WQ_FMT_W8_PC || fmt > WQ_FMT_W4_G64 || M < 1 || M > kGemvMaxM) return -1;
   const int cap = gemv_max_waves(compute_fmt(fmt), (int)M, rows);
   return cap > 0 ? cap : -1;
 }
@@ -431,7 +437,9 @@ wq_status wq_workspace_size(const wq_weight* w0, int64_t M, size_t* bytes) {
     *bytes = gemv_workspace_bytes(w->N, M, kMaxSplit);
   } else {
     size_t b = 0;
-    for (int t = 1; t <= WQ_GEMM_TILES; ++t) b = std::max(b, gemm_workspace_full_bytes(w->fmt, w->K, w->N, M, t));
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t)
+      if (!small_group(w->fmt) || small_group_tile(t) == t)
+        b = std::max(b, gemm_workspace_full_bytes(w->fmt, w->K, w->N, M, t));
     *bytes = b;
   }
   return WQ_OK;
@@ -534,6 +542,8 @@ wq_status wq_moe_linear(const wq_weight* w0, int E, const void* x, const int32_t
   if (!x || !y || !offsets) return fail(WQ_ERR_INVALID_ARG, "NULL argument");
   if (!aligned(x, 16) || !aligned(y, 2) || !aligned(offsets, 4))
     return fail(WQ_ERR_ALIGNMENT, "wq_moe_linear: x needs 16-byte, y 2-byte and offsets 4-byte alignment");
+  if (small_group(w->fmt))
+    return fail(WQ_ERR_UNSUPPORTED, "wq_moe_linear: takes per-channel and group-128 formats");
   if (w->K % kGroup != 0 || w->N % 16 != 0 || (epilogue == WQ_EPILOGUE_SILU_MUL && w->N % 32 != 0))
     return fail(WQ_ERR_UNSUPPORTED,
                 "wq_moe_linear: needs K % 128 == 0 and N % 16 == 0 (N % 32 == 0 with the gated epilogue)");
@@ -691,7 +701,9 @@ wq_status wq_tune(const wq_weight* copies0, int n_copies, int64_t M, const void*
             cand.push_back({s, wv, rw, 0});
       }
   } else {
-    for (int t = 1; t <= WQ_GEMM_TILES; ++t) cand.push_back({0, 0, 0, t});
+    for (int t = 1; t <= WQ_GEMM_TILES; ++t)
+      if (!small_group(copies[0].fmt) || small_group_tile(t) == t)  // the others run as one of these
+        cand.push_back({0, 0, 0, t});
   }
   hipStream_t hs = (hipStream_t)stream;
   hipEvent_t e0, e1;

@@ -65,19 +65,20 @@ __device__ __forceinline__ uint4 w4_word_to_bf16(uint32_t w, float z) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// gshift: the grouped formats' group size is 2^gshift k (32, 64 or 128)
 template <int FMT>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ qw,
                                                      const uint16_t* __restrict__ scales,
                                                      const uint8_t* __restrict__ zeros,
                                                      const uint16_t* __restrict__ x,
-                                                     uint16_t* __restrict__ y, int M, int K, int N) {
+                                                     uint16_t* __restrict__ y, int M, int K, int N, int gshift) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDA];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int G = K / kGroup;
+  const int G = K >> gshift, gmask = (1 << gshift) - 1;
   constexpr bool kGrouped = FMT != WQ_FMT_W8_PC;
 
   // ---- global -> register staging
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
     } else {
       const int row = tid >> 1, col = (tid & 1) * 32;
       const int n = min(n0 + row, N - 1);
-      const int g = k0 / kGroup;
+      const int g = (k0 + col) >> gshift;  // this thread's 32 k lie in one group
       const uint32_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows) / 2];
       const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
       *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 0]) = w4_word_to_bf16(wb[0].x, z);
@@ -171,22 +172,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-    }
-    if constexpr (kGrouped) {
-      if (((k0 + BK) % kGroup) == 0) {
-        const int g = k0 / kGroup;
+      // the end of a group: its partial sums, times the group scale, into acc
+      if constexpr (kGrouped) {
+        if (((k0 + kk + 16) & gmask) == 0) {
+          const int g = (k0 + kk) >> gshift;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = min(n0 + wn * 64 + j * 32 + l32, N - 1);
-          const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
-          const float s = (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
+          for (int j = 0; j < 2; ++j) {
+            const int n = min(n0 + wn * 64 + j * 32 + l32, N - 1);
+            const uint16_t sb = scales[((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows];
+            const float s = (FMT == WQ_FMT_W8_G128) ? bf16_to_f32(sb) : f16_to_f32(sb);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int a = 0; a < 16; ++a) {
-              acc[i][j][a] = fmaf(s, tmp[i][j][a], acc[i][j][a]);
-              tmp[i][j][a] = 0.f;
-            }
+              for (int a = 0; a < 16; ++a) {
+                acc[i][j][a] = fmaf(s, tmp[i][j][a], acc[i][j][a]);
+                tmp[i][j][a] = 0.f;
+              }
+          }
         }
       }
     }
@@ -731,13 +733,16 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(la), "v"(g) : "memory", "m0");
 }
 
-template <int FMT, int TM = DBM>
+// GS: k per group (128, or 64 / 32 for the smaller groups: a step of DBK = 64 k then
+// holds kGPS = 1 or 2 whole groups, and its stage their metadata side by side)
+template <int FMT, int TM = DBM, int GS = kGroup>
 struct G128Dma {
   static constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
+  static constexpr int kGPS = GS >= DBK ? 1 : DBK / GS;  // groups whose metadata a stage holds
   static constexpr int kXBytes = TM * DBK * 2;          // x rows of a stage
   static constexpr int kCodeRow = kW4 ? DBK / 2 : DBK;  // code bytes per row and step
   static constexpr int kCodeBytes = DBN * kCodeRow;
-  static constexpr int kMetaBytes = DBN * 2 + (kW4 ? DBN / 2 : 0);
+  static constexpr int kMetaBytes = kGPS * (DBN * 2 + (kW4 ? DBN / 2 : 0));
   static constexpr int kStage = kXBytes + kCodeBytes + kMetaBytes;
   static constexpr int kCodeInst = kCodeBytes / 1024;  // code DMA instructions per step
 };
@@ -745,7 +750,8 @@ struct G128Dma {
 // Exact fallback for one workgroup tile (see above): each wave takes 32 x 32 blocks in
 // turn; per block and group, eight v_mfma_f32_32x32x16_bf16 on exact codes give the
 // group's fp32 partial, which the group scale adds into the block.
-template <int FMT, int TM = DBM>
+// (g0, g1: the K range in units of 128 k; the groups of GS k inside it, in order)
+template <int FMT, int TM = DBM, int GS = kGroup>
 __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                                 const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
                                 uint16_t* __restrict__ y, float* __restrict__ part, int M, int K, int N,
@@ -753,7 +759,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
                                 int pn0, int wave, int NW) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
-  const int G = K / kGroup;
+  const int G = K / GS;
   const int row_bytes = kW4 ? K / 2 : K;
   for (int blk = wave; blk < (TM / 32) * (DBN / 32); blk += NW) {
     const int bi = blk / (DBN / 32), bj = blk % (DBN / 32);
@@ -762,7 +768,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
     floatx16 acc;
 #pragma unroll
     for (int a = 0; a < 16; ++a) acc[a] = 0.f;
-    for (int g = g0; g < g1; ++g) {
+    for (int g = g0 * (kGroup / GS); g < g1 * (kGroup / GS); ++g) {
       const uint16_t sb = scales[mi + (size_t)g * kGemvTileRows];
       const float sc = kW4 ? f16_to_f32(sb) : bf16_to_f32(sb);
       float z = 0.f;
@@ -770,8 +776,8 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
       floatx16 tmp;
 #pragma unroll
       for (int a = 0; a < 16; ++a) tmp[a] = 0.f;
-      for (int kk = 0; kk < kGroup / 16; ++kk) {
-        const int k = g * kGroup + 16 * kk + 8 * lh;
+      for (int kk = 0; kk < GS / 16; ++kk) {
+        const int k = g * GS + 16 * kk + 8 * lh;
         const uint4 xa = *reinterpret_cast<const uint4*>(x + (size_t)m * K + k);
         uint4 wb;
         if constexpr (kW4) {
@@ -877,7 +883,7 @@ __global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __re
 // XH: xd is x already in fp16, row m scaled by 1 / xinv[m] (x_to_f16_rows_kernel);
 // otherwise xd == x and the stages are converted in LDS.  The exact fallback always
 // reads the bf16 x.
-template <int FMT, int WM, int WN, bool XH = false, int TM = DBM>
+template <int FMT, int WM, int WN, bool XH = false, int TM = DBM, int GS = kGroup>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
@@ -888,7 +894,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
                                                                          int tailS) {
-  using F = G128Dma<FMT, TM>;
+  using F = G128Dma<FMT, TM, GS>;
   constexpr bool kW4 = F::kW4;
   constexpr int NW = WM * WN, RB = TM / 32 / WM, CB = 8 / WN;
   constexpr int XI = TM / 8 / NW, WI = F::kCodeInst / NW;  // x and code DMA instructions per wave and step
@@ -917,7 +923,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   // the group-128 formats); with S > 1 it writes fp32 partials (see the epilogue)
   const int S = wk.S, sp = wk.sp, U = K / (DBK * KUNIT);
   const int kb = KUNIT * (int)((int64_t)sp * U / S), KS = KUNIT * (int)((int64_t)(sp + 1) * U / S) - kb;
-  const int G = K / kGroup;
+  const int G = K / GS;
   const int row_bytes = kW4 ? K / 2 : K;
 
   // ---- DMA sources.  x: instruction j covers stage rows 8q .. 8q + 7, q = XI wave + j.
@@ -951,20 +957,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     return qw + wt_base[j] + (size_t)wt_nr[j] * kSliceBytes * sl + wlane[j] * w + jb + wc;
   };
   // metadata: wave 0 brings the 16 tiles' scales of the step's group (2 lanes x 16
-  // bytes per tile), wave 1 the uint4 zero-points (2 lanes x 4 bytes per tile)
-  const int mt = min(n0 / kGemvTileRows + (lane >> 1), T - 1);
+  // bytes per tile; lanes 32.. the second group of a step of two), wave 1 the uint4
+  // zero-points (2 lanes x 4 bytes per tile)
+  const int mt = min(n0 / kGemvTileRows + ((lane & 31) >> 1), T - 1);
   auto dma = [&](uint8_t* st, int ks) {
     const int k0 = (kb + min(ks, KS - 1)) * DBK;
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(xd + xo[j] + k0, st + (XI * wave + j) * 1024);
 #pragma unroll
     for (int j = 0; j < WI; ++j) dma16(code_src(j, k0), st + kDA + (WI * wave + j) * 1024);
-    const int g = k0 / kGroup;
-    if (wave == 0 && lane < 32)
+    const int g = k0 / GS + (F::kGPS > 1 ? lane >> 5 : 0);
+    if (wave == 0 && lane < 32 * F::kGPS)
       dma16(scales + ((size_t)mt * G + g) * kGemvTileRows + 8 * (lane & 1), st + kDA + F::kCodeBytes);
-    if (kW4 && wave == 1 && lane < 32)
+    if (kW4 && wave == 1 && lane < 32 * F::kGPS)
       dma4(zeros + ((size_t)mt * G + g) * (kGemvTileRows / 2) + 4 * (lane & 1),
-           st + kDA + F::kCodeBytes + DBN * 2);
+           st + kDA + F::kCodeBytes + F::kGPS * DBN * 2);
   };
   // the x chunks this lane's own DMA brought into a stage, bf16 -> fp16 in place
   // (v_cvt_pk_f16_f32, nearest even: beyond fp16 range gives Inf)
@@ -995,13 +1002,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   // int8: 1152)
   float msc[CB];
   f16x2_t mo0[CB], mo1[CB];
-  auto meta_read = [&](const uint8_t* st) {
+  auto meta_read = [&](const uint8_t* st, int gi) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const int n = wn * 32 * CB + j * 32 + l32;
-      const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + kDA + F::kCodeBytes + 2 * n);
+      const uint16_t sb = *reinterpret_cast<const uint16_t*>(st + kDA + F::kCodeBytes + gi * DBN * 2 + 2 * n);
       if constexpr (kW4) {
-        const uint8_t zb = st[kDA + F::kCodeBytes + DBN * 2 + (n >> 1)];
+        const uint8_t zb = st[kDA + F::kCodeBytes + F::kGPS * DBN * 2 + gi * (DBN / 2) + (n >> 1)];
         const _Float16 z = (_Float16)(float)((zb >> (4 * (n & 1))) & 15u);
         msc[j] = f16_to_f32(sb);
         mo0[j] = f16x2_t{-(_Float16)1024.f - z, -(_Float16)1024.f - z};
@@ -1023,7 +1030,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   auto fread_half = [&](const uint8_t* st, int P, int s2, f16x8_t* A, f16x8_t* B) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) A[i] = *reinterpret_cast<const f16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
-    if (P == 0 && s2 == 0) meta_read(st);
+    // the group's metadata where a group starts: each step for 128 and 64 (a group-128
+    // step re-reads its group's), each 32-k slice P for 32
+    if (s2 == 0 && (P == 0 || F::kGPS > 1)) meta_read(st, F::kGPS > 1 ? P : 0);
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       if constexpr (kW4) {
@@ -1092,17 +1101,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
   convert(st0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // one step: both 32-k slices, a half (16 k) at a time (the registers hold one half);
-  // a group is two steps (the range starts on a group), so odd steps end one
+  // a group of 128 is two steps (the range starts on a group), so odd steps end one; a
+  // group of 64 ends with every step, one of 32 with every slice
   auto step = [&](uint8_t* cur, uint8_t* nxt, int t) {
     f16x8_t Ah[RB], Bh[CB];
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
+    for (int P = 0; P < 2; ++P) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         fread_half(cur, P, s2, Ah, Bh);
         mma_half(Ah, Bh);
       }
-    if (t & 1) fold();
+      if constexpr (GS == 32) fold();
+    }
+    if constexpr (GS == 64) fold();
+    if constexpr (GS == kGroup) {
+      if (t & 1) fold();
+    }
     step_barrier(nxt);
     dma(cur, t + 3);
   };
@@ -1132,8 +1147,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 #pragma unroll
   for (int w = 0; w < NW; ++w) any |= wave_flag[w];
   if (any) {
-    g128_tile_exact<FMT, TM>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT, S,
-                         wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
+    g128_tile_exact<FMT, TM, GS>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT,
+                                 S, wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
     return;
   }
   // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block;
@@ -1759,6 +1774,40 @@ static hipError_t x_to_f16_rows(const uint16_t* x, int64_t M, int K, void* ws, s
   return hipGetLastError();
 }
 
+// The grouped LDS-DMA kernel for a format family, x-tile height and group size, fed by
+// the fp16 copy of x when there is one (xh), else converting x itself.
+template <int F, int TMV, int GS>
+static void g_dma_launch(dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
+                         const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y, float* part, int M,
+                         int K, int N, int tail0, int tailS) {
+  if (xh)
+    gemm_dma_g128_kernel<F, 1, 8, true, TMV, GS>
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+  else
+    gemm_dma_g128_kernel<F, 1, 8, false, TMV, GS>
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS);
+}
+template <int F, int TMV>
+static void g_dma_launch_gs(int gs, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
+                            const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
+                            float* part, int M, int K, int N, int tail0, int tailS) {
+  if (gs == 32) g_dma_launch<F, TMV, 32>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+  else if (gs == 64) g_dma_launch<F, TMV, 64>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+  else g_dma_launch<F, TMV, kGroup>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+}
+static void g_dma_dispatch(int fmt, int tm, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
+                           const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
+                           float* part, int M, int K, int N, int tail0, int tailS) {
+  const int gs = meta_group(fmt);
+  if (family(fmt) == WQ_FMT_W4_G128) {
+    if (tm == 64) g_dma_launch_gs<WQ_FMT_W4_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+    else g_dma_launch_gs<WQ_FMT_W4_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+  } else {
+    if (tm == 64) g_dma_launch_gs<WQ_FMT_W8_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+    else g_dma_launch_gs<WQ_FMT_W8_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+  }
+}
+
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       void* ws, size_t ws_bytes, hipStream_t s) {
   const int K = (int)w->K, N = (int)w->N;
@@ -1766,6 +1815,8 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
+  if (w->fmt == WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: per-channel W4 runs through its compute view");
+  if (small_group(w->fmt)) tile = small_group_tile(tile);
   if (tile >= kMmaTile0 && tile <= kMmaTileLast) {
     // 8..16 tokens: the matrix-core GEMV kernel (one 16-token A operand)
     int S = gemm_mma_split(tile, M, K);
@@ -1815,22 +1866,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       float* xinv = nullptr;
       WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh,
                                  &xinv, s));
-      const int t0 = (int)total;
-#define WQ_G128_ROWS(F, TMV)                                                                                  \
-  do {                                                                                                        \
-    if (xh)                                                                                                   \
-      gemm_dma_g128_kernel<F, 1, 8, true, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, t0, 1); \
-    else                                                                                                      \
-      gemm_dma_g128_kernel<F, 1, 8, false, TMV><<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, (int)M, K, N, t0, 1); \
-  } while (0)
-      if (w->fmt == WQ_FMT_W4_G128) {
-        if (tm == 64) WQ_G128_ROWS(WQ_FMT_W4_G128, 64);
-        else WQ_G128_ROWS(WQ_FMT_W4_G128, 128);
-      } else {
-        if (tm == 64) WQ_G128_ROWS(WQ_FMT_W8_G128, 64);
-        else WQ_G128_ROWS(WQ_FMT_W8_G128, 128);
-      }
-#undef WQ_G128_ROWS
+      g_dma_dispatch(w->fmt, tm, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, (int)total, 1);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
@@ -1881,18 +1917,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       uint16_t* xh = nullptr;
       float* xinv = nullptr;
       WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, part_bytes, &xh, &xinv, s));
-#define WQ_G128_BIG(F)                                                                                 \
-  do {                                                                                                 \
-    if (xh)                                                                                            \
-      gemm_dma_g128_kernel<F, 1, 8, true, 128>                                                         \
-          <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS);         \
-    else                                                                                               \
-      gemm_dma_g128_kernel<F, 1, 8, false, 128>                                                        \
-          <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, (int)M, K, N, tail0, tailS);       \
-  } while (0)
-      if (w->fmt == WQ_FMT_W4_G128) WQ_G128_BIG(WQ_FMT_W4_G128);
-      else WQ_G128_BIG(WQ_FMT_W8_G128);
-#undef WQ_G128_BIG
+      g_dma_dispatch(w->fmt, 128, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
@@ -1914,7 +1939,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     return WQ_OK;
   }
   if (dma_tile) tile = 1;
-  if (tile == 1) {
+  if (tile == 1 && !small_group(w->fmt)) {  // (groups of 32 and 64 take tile 2's kernel)
     const int bn = w->fmt == WQ_FMT_W8_PC ? Big<WQ_FMT_W8_PC>::BN : Big<WQ_FMT_W8_G128>::BN;
     const int64_t total = ((M + BM2 - 1) / BM2) * ((N + bn - 1) / bn);
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
@@ -1935,15 +1960,16 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     return WQ_OK;
   }
   dim3 grid((N + BN - 1) / BN, (unsigned)((M + BM - 1) / BM));
-  switch (w->fmt) {
+  const int gshift = meta_group(w->fmt) == 32 ? 5 : meta_group(w->fmt) == 64 ? 6 : 7;
+  switch (family(w->fmt)) {
     case WQ_FMT_W8_PC:
-      gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+      gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     case WQ_FMT_W8_G128:
-      gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+      gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     case WQ_FMT_W4_G128:
-      gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+      gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     default:
       return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");

@@ -175,7 +175,7 @@ template <int FMT, int M, int RR, bool PF>
 __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    float* __restrict__ part, int K, int N) {
+    float* __restrict__ part, int K, int N, int gshift) {
   using F = Fmt<FMT>;
   constexpr int kSlice = 64 * F::kChunk;
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
   const int s = blockIdx.y, S = gridDim.y;
   const int T = (K + kSlice - 1) / kSlice;
   const int sl0 = (int)(((int64_t)s * T) / S), sl1 = (int)(((int64_t)(s + 1) * T) / S);
-  const int G = K / kGroup;
+  const int G = K >> gshift;  // groups per row: 2^gshift k each (32, 64 or 128; a lane's chunk lies in one)
   const size_t row_bytes = kW4 ? (size_t)K / 2 : (size_t)K;
   // tile base in the gfx950 code layout and its row count (the last tile may be short)
   const uint8_t* tile_base = qw + (size_t)tile * R * row_bytes;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
 
   // The arithmetic of one slice, given its codes (RR rows) and x chunk.
   auto slice_math = [&](const uint4* cw, const uint32_t (*xb)[F::kXWords], int kk) {
-    const int g = kk / kGroup;
+    const int g = kk >> gshift;
     uint32_t sw[RR / 2];  // RR 16-bit scales of this sub-tile's rows for group g
     uint32_t zw = 0;      // RR 4-bit zero-points
     if constexpr (FMT != WQ_FMT_W8_PC) {
@@ -623,7 +623,9 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
   }
   const uint8_t* xb8 = reinterpret_cast<const uint8_t*>(x);
   const uint32_t xrow = min(ln, (uint32_t)Mr - 1u) * (uint32_t)K * 2u;  // byte offset of this lane's token
-  const uint32_t zshift = 4 * (ln & 1);
+  // metadata of row ln within the 32-bit words that hold it: its fp16/bf16 scale is half
+  // ln & 1 of a word, its zero-point nibble ln & 7 of one
+  const uint32_t sshift = 16 * (ln & 1), zshift = 4 * (ln & 7);
   uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, mag_a = 0x64006400u, mag_h = 0x54005400u;
   if constexpr (kW4) asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(mag_a), "+v"(mag_h));
 
@@ -684,11 +686,13 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
       if constexpr (!LX) load_x(st.xv, u);
     }
     if constexpr (kGrouped) {
-      const uint32_t soff = 32u * (uint32_t)u + 2u * ln, zoff = 8u * (uint32_t)u + (ln >> 1);
+      // whole aligned words: a loaded byte or half would be re-extended where the loop
+      // carries it, and that wait would drain the next unit's loads as well
+      const uint32_t soff = 32u * (uint32_t)u + 4u * (ln >> 1), zoff = 8u * (uint32_t)u + 4u * (ln >> 3);
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
-        st.sv[t] = *reinterpret_cast<const uint16_t*>(sbase[t] + soff);
-        st.zb[t] = kW4 ? zbase[t][zoff] : 0u;
+        st.sv[t] = *reinterpret_cast<const uint32_t*>(sbase[t] + soff);
+        st.zb[t] = kW4 ? *reinterpret_cast<const uint32_t*>(zbase[t] + zoff) : 0u;
       }
     }
   };
@@ -759,7 +763,8 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     }
     // group-128: the unit's contribution d[t] to each tile, times the group scale
     auto fold1 = [&](int t, const f32x4_t& d) {
-      const float sc = kW4 ? f16_to_f32((uint16_t)st.sv[t]) : bf16_to_f32((uint16_t)st.sv[t]);
+      const uint16_t sh = (uint16_t)(st.sv[t] >> sshift);
+      const float sc = kW4 ? f16_to_f32(sh) : bf16_to_f32(sh);
 #pragma unroll
       for (int i = 0; i < MI; ++i) acc[t][i] = fmaf(sc, d[i], acc[t][i]);
     };
@@ -955,26 +960,26 @@ void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t
 
 template <int FMT, int M, int RR>
 void launch_rr(bool pf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-               const uint16_t* x, uint16_t* y, float* part, int K, int N, hipStream_t st) {
+               const uint16_t* x, uint16_t* y, float* part, int K, int N, int gshift, hipStream_t st) {
   if constexpr (prefetch_allowed(FMT, RR, M)) {
     if (pf) {
-      gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+      gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
       return;
     }
   }
-  gemv_kernel<FMT, M, RR, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N);
+  gemv_kernel<FMT, M, RR, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
 }
 
 // rows: 4, 8 or 16, optionally | kGemvPrefetch (checked by the caller)
 template <int FMT, int M>
 wq_status launch_m(int rows, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
                    const uint8_t* zs, const uint16_t* x, uint16_t* y, float* part, int K, int N,
-                   hipStream_t st) {
+                   int gshift, hipStream_t st) {
   const bool pf = (rows & kGemvPrefetch) != 0;
   switch (rows & ~kGemvPrefetch) {
-    case 4: launch_rr<FMT, M, 4>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 8: launch_rr<FMT, M, 8>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 16: launch_rr<FMT, M, 16>(pf, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 4: launch_rr<FMT, M, 4>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 8: launch_rr<FMT, M, 8>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 16: launch_rr<FMT, M, 16>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   }
   return WQ_OK;
@@ -984,6 +989,7 @@ template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
                      int waves, int rows, void* ws, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
+  const int gshift = meta_group(w->fmt) == 32 ? 5 : meta_group(w->fmt) == 64 ? 6 : 7;
   float* part = (float*)ws;
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
@@ -1010,13 +1016,13 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
   dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
   dim3 block(64 * waves);
   switch (M) {
-    case 1: r = launch_m<FMT, 1>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 2: r = launch_m<FMT, 2>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 3: r = launch_m<FMT, 3>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 4: r = launch_m<FMT, 4>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 5: r = launch_m<FMT, 5>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 6: r = launch_m<FMT, 6>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
-    case 7: r = launch_m<FMT, 7>(rows, grid, block, qw, sc, zs, x, y, part, K, N, st); break;
+    case 1: r = launch_m<FMT, 1>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 2: r = launch_m<FMT, 2>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 3: r = launch_m<FMT, 3>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 4: r = launch_m<FMT, 4>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 5: r = launch_m<FMT, 5>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 6: r = launch_m<FMT, 6>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 7: r = launch_m<FMT, 7>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   }
   }
@@ -1040,18 +1046,19 @@ size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k) {
 int gemv_max_waves(int fmt, int M, int rows) {
   if (rows & kGemvMfma) {
     const int rr = rows & ~kGemvMfma;
-    if (M < 1 || M > kMmaTokens) return 0;
+    if (M < 1 || M > kMmaTokens || small_group(fmt)) return 0;
     return (rr == 16 || rr == 32 || rr == 64) ? kMmaMaxWaves : 0;
   }
   const int rr = rows & ~kGemvPrefetch;
   const bool pf = (rows & kGemvPrefetch) != 0;
+  fmt = family(fmt);
   if (rr != 4 && rr != 8 && rr != 16) return 0;
   if (pf && !prefetch_allowed(fmt, rr, M)) return 0;
   return max_waves_r(fmt, rr, M, pf);
 }
 
 int64_t gemv_slices(int64_t K, int fmt) {
-  const int64_t slice = 64 * (fmt == WQ_FMT_W4_G128 ? 32 : 16);
+  const int64_t slice = 64 * (is_w4(fmt) ? 32 : 16);
   return (K + slice - 1) / slice;
 }
 
@@ -1060,9 +1067,9 @@ int gemv_default_rows(int64_t K, int64_t N, int fmt, int M) {
   // rows per wave share each x chunk (and its conversion) among more rows, which
   // pays when there are many row tiles or several tokens (measured on MI355X)
   (void)K;
-  if (fmt == WQ_FMT_W4_G128 && M >= 5) return 8;  // 16 rows x 5+ tokens of uint4 spill registers
+  if (is_w4(fmt) && M >= 5) return 8;  // 16 rows x 5+ tokens of uint4 spill registers
   if (M >= 4) return N >= 16384 ? 16 : 8;
-  if (fmt == WQ_FMT_W4_G128) return 8;
+  if (is_w4(fmt)) return 8;
   return N >= 16384 ? 8 : 4;
 }
 
@@ -1087,7 +1094,8 @@ wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y,
   if (waves < 1 || waves > cap)
     return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: at this M and rows a workgroup holds 1.." +
                                         std::to_string(cap) + " waves");
-  switch (w->fmt) {
+  if (w->fmt == WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: per-channel W4 runs through its compute view");
+  switch (family(w->fmt)) {
     case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, s);
     case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, s);
     case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, s);

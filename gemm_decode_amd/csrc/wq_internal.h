@@ -31,8 +31,28 @@ wq_status hip_fail(hipError_t e, const char* what);
     if (e_ != hipSuccess) return ::wq::hip_fail(e_, #call);  \
   } while (0)
 
-// uint4 formats (group-128 and per output channel)
-inline bool is_w4(int fmt) { return fmt == WQ_FMT_W4_G128 || fmt == WQ_FMT_W4_PC; }
+// uint4 formats (grouped and per output channel)
+inline bool is_w4(int fmt) {
+  return fmt == WQ_FMT_W4_G128 || fmt == WQ_FMT_W4_PC || fmt == WQ_FMT_W4_G32 || fmt == WQ_FMT_W4_G64;
+}
+// k per group of a format's gfx950 metadata (what the compute kernels fold by): 0 for
+// per-channel W8; per-channel W4 is laid out as group-128 (see compute_view)
+inline int meta_group(int fmt) {
+  switch (fmt) {
+    case WQ_FMT_W8_G32: case WQ_FMT_W4_G32: return 32;
+    case WQ_FMT_W8_G64: case WQ_FMT_W4_G64: return 64;
+    case WQ_FMT_W8_PC: return 0;
+    default: return kGroup;
+  }
+}
+// groups of 32 or 64 (the kernels that take them run one template per group size)
+inline bool small_group(int fmt) { const int g = meta_group(fmt); return g == 32 || g == 64; }
+// kernel family of a format: the group-128 kernels (templated on the group size where
+// they take groups of 32 and 64) serve every grouped format of their code width
+inline int family(int fmt) {
+  if (fmt == WQ_FMT_W8_PC) return WQ_FMT_W8_PC;
+  return is_w4(fmt) ? WQ_FMT_W4_G128 : WQ_FMT_W8_G128;
+}
 // The compute kernels take per-channel W4 in the gfx950 layout as group-128 W4: that
 // layout repeats each row's scale and zero-point in every 128-k group.
 inline int compute_fmt(int fmt) { return fmt == WQ_FMT_W4_PC ? WQ_FMT_W4_G128 : fmt; }
@@ -133,6 +153,15 @@ constexpr int kDma128Tile0 = 17, kDma128TileLast = 19;
 constexpr int kMmaTile0 = 20, kMmaTileLast = 23;
 // split-K of a tile kMmaTile0 .. kMmaTileLast at M tokens (0: not such a tile, or M too large)
 int gemm_mma_split(int tile, int64_t M, int64_t K);
+// The tile that runs for groups of 32 or 64: their kernels are tile 2's and the LDS-DMA
+// tiles' (9..19, 24); tiles 1, 3 and 4 run as tile 9, the skinny and matrix-core GEMV
+// tiles (5..8, 20..23) as tile 14.
+inline int small_group_tile(int tile) {
+  if (tile == 1 || tile == 3 || tile == 4) return 9;
+  if ((tile >= kSkinnyTile0 && tile <= kSkinnyTileLast) || (tile >= kMmaTile0 && tile <= kMmaTileLast))
+    return kDma64Tile0;
+  return tile;
+}
 // rows per x tile of the row-tiled LDS-DMA tiles 14..19 (0 for other tiles)
 inline int gemm_dma_rows(int tile) {
   return tile >= kDma64Tile0 && tile <= kDma64TileLast ? 64 : tile >= kDma128Tile0 && tile <= kDma128TileLast ? 128 : 0;

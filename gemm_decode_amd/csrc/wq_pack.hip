@@ -88,22 +88,24 @@ __global__ __launch_bounds__(256) void pack_w8_pc_kernel(const T* __restrict__ w
   for (int i = threadIdx.x; i < words; i += 256) qrow[i] = (s == 0.f) ? 0u : w8_codes4(load_w4(w, row + 4 * (size_t)i), s);
 }
 
-// W8, group 128: 256 threads = 8 groups of 32 lanes, each lane 4 consecutive k.
-template <typename T>
-__global__ __launch_bounds__(256) void pack_w8_g128_kernel(const T* __restrict__ w,
-                                                             int8_t* __restrict__ q,
-                                                             uint16_t* __restrict__ scales,
-                                                             int K, int N) {
-  const int G = K / kGroup;
-  const int64_t gid = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int lane = threadIdx.x & 31;
+// W8 with groups of GS (32, 64, 128) k: 256 threads = 256 / (GS / 4) groups of GS / 4
+// lanes, each lane 4 consecutive k.
+template <typename T, int GS>
+__global__ __launch_bounds__(256) void pack_w8_g_kernel(const T* __restrict__ w,
+                                                          int8_t* __restrict__ q,
+                                                          uint16_t* __restrict__ scales,
+                                                          int K, int N) {
+  constexpr int L = GS / 4;  // lanes per group
+  const int G = K / GS;
+  const int64_t gid = (int64_t)blockIdx.x * (256 / L) + (threadIdx.x / L);
+  const int lane = threadIdx.x % L;
   const bool valid = gid < (int64_t)N * G;
   const int64_t gg = valid ? gid : 0;
   const int64_t n = gg / G, g = gg % G;
-  const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
+  const size_t off = (size_t)n * K + (size_t)g * GS + 4 * lane;
   float4 v = load_w4(w, off);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = group_max<32>(a);
+  a = group_max<L>(a);
   const uint16_t sb = f32_to_bf16_rne(a / 127.f);
   const float s = bf16_to_f32(sb);
   if (!valid) return;
@@ -111,23 +113,25 @@ __global__ __launch_bounds__(256) void pack_w8_g128_kernel(const T* __restrict__
   *reinterpret_cast<uint32_t*>(q + off) = (s == 0.f) ? 0u : w8_codes4(v, s);
 }
 
-// W4 asymmetric group 128, canonical layout: a block handles 8 rows x 1 group,
-// 32 lanes per row, 4 consecutive k per lane; the 8 zero-points form one word.
-template <typename T>
-__global__ __launch_bounds__(256) void pack_w4_g128_kernel(const T* __restrict__ w,
+// W4 asymmetric with groups of GS (32, 64, 128) k, canonical layout: a block of 2 GS
+// threads handles 8 rows x 1 group, GS / 4 lanes per row, 4 consecutive k per lane; the
+// 8 zero-points form one word.
+template <typename T, int GS>
+__global__ __launch_bounds__(2 * GS) void pack_w4_g_kernel(const T* __restrict__ w,
                                                              uint32_t* __restrict__ qw,
                                                              uint16_t* __restrict__ scales,
                                                              uint32_t* __restrict__ zeros, int K,
                                                              int N) {
-  const int G = K / kGroup;
+  constexpr int L = GS / 4;  // lanes per row
+  const int G = K / GS;
   const int c8 = blockIdx.x;  // rows 8*c8 .. 8*c8+7
   const int g = blockIdx.y;
-  const int r = threadIdx.x >> 5, lane = threadIdx.x & 31;
+  const int r = threadIdx.x / L, lane = threadIdx.x % L;
   const int n = 8 * c8 + r;
-  const size_t off = (size_t)n * K + (size_t)g * kGroup + 4 * lane;
+  const size_t off = (size_t)n * K + (size_t)g * GS + 4 * lane;
   float4 v = load_w4(w, off);
-  float hi = group_max<32>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-  float lo = group_min<32>(fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+  float hi = group_max<L>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  float lo = group_min<L>(fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
   const uint16_t sh = f32_to_f16_rne((hi - lo) / 15.f);
   const float s = f16_to_f32(sh);
   uint32_t z = 0, nib = 0;
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(256) void pack_w4_g128_kernel(const T* __restrict__
     }
   }
   // lanes 2i and 2i+1 hold k = 8i..8i+3 and 8i+4..8i+7 of the same word
-  const uint32_t partner = (uint32_t)__shfl_xor((int)nib, 1, 32);
-  if ((lane & 1) == 0) qw[(size_t)n * (K / 8) + (size_t)g * 16 + (lane >> 1)] = nib | (partner << 16);
+  const uint32_t partner = (uint32_t)__shfl_xor((int)nib, 1, L);
+  if ((lane & 1) == 0) qw[(size_t)n * (K / 8) + (size_t)g * (GS / 8) + (lane >> 1)] = nib | (partner << 16);
   __shared__ uint32_t zs[8];
   if (lane == 0) {
     scales[(size_t)n * G + g] = sh;
@@ -330,16 +334,32 @@ static wq_status launch_pack_t(const T* w, const wq_weight* out, hipStream_t s) 
     case WQ_FMT_W8_PC:
       pack_w8_pc_kernel<T><<<N, 256, 0, s>>>(w, (int8_t*)out->qweight, (uint16_t*)out->scales, K);
       break;
+    case WQ_FMT_W8_G32:
+    case WQ_FMT_W8_G64:
     case WQ_FMT_W8_G128: {
-      const int64_t groups = (int64_t)N * (K / kGroup);
-      pack_w8_g128_kernel<T><<<(unsigned)((groups + 7) / 8), 256, 0, s>>>(
-          w, (int8_t*)out->qweight, (uint16_t*)out->scales, K, N);
+      const int gs = meta_group(out->fmt);
+      const int64_t groups = (int64_t)N * (K / gs), per_block = 256 / (gs / 4);
+      const unsigned blocks = (unsigned)((groups + per_block - 1) / per_block);
+      int8_t* q = (int8_t*)out->qweight;
+      uint16_t* sc = (uint16_t*)out->scales;
+      if (gs == 32) pack_w8_g_kernel<T, 32><<<blocks, 256, 0, s>>>(w, q, sc, K, N);
+      else if (gs == 64) pack_w8_g_kernel<T, 64><<<blocks, 256, 0, s>>>(w, q, sc, K, N);
+      else pack_w8_g_kernel<T, 128><<<blocks, 256, 0, s>>>(w, q, sc, K, N);
       break;
     }
-    case WQ_FMT_W4_G128:
-      pack_w4_g128_kernel<T><<<dim3(N / 8, K / kGroup), 256, 0, s>>>(
-          w, (uint32_t*)out->qweight, (uint16_t*)out->scales, (uint32_t*)out->zeros, K, N);
+    case WQ_FMT_W4_G32:
+    case WQ_FMT_W4_G64:
+    case WQ_FMT_W4_G128: {
+      const int gs = meta_group(out->fmt);
+      const dim3 grid(N / 8, K / gs);
+      uint32_t* q = (uint32_t*)out->qweight;
+      uint16_t* sc = (uint16_t*)out->scales;
+      uint32_t* z = (uint32_t*)out->zeros;
+      if (gs == 32) pack_w4_g_kernel<T, 32><<<grid, 64, 0, s>>>(w, q, sc, z, K, N);
+      else if (gs == 64) pack_w4_g_kernel<T, 64><<<grid, 128, 0, s>>>(w, q, sc, z, K, N);
+      else pack_w4_g_kernel<T, 128><<<grid, 256, 0, s>>>(w, q, sc, z, K, N);
       break;
+    }
     case WQ_FMT_W4_PC:
       pack_w4_pc_kernel<T><<<N / 8, 256, 0, s>>>(w, (uint32_t*)out->qweight, (uint16_t*)out->scales,
                                                 (uint32_t*)out->zeros, K);
@@ -360,7 +380,8 @@ wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx9
   size_t qb = 0, sb = 0, zb = 0;
   wq_status st = wq_packed_sizes(src->fmt, WQ_LAYOUT_CANONICAL, src->K, src->N, &qb, &sb, &zb);
   if (st != WQ_OK) return st;
-  const int G = (int)(src->K / kGroup), N = (int)src->N;
+  const int gs = meta_group(src->fmt);  // 0 for per-channel W8 (its scales are copied)
+  const int G = gs ? (int)(src->K / gs) : 0, N = (int)src->N;
   const int Gc = src->fmt == WQ_FMT_W4_PC ? 1 : G;  // canonical groups per row
   const int64_t row_bytes = (int64_t)(qb / (size_t)N);
   const size_t chunks = qb / 16;

@@ -33,7 +33,7 @@ if not os.path.exists(LIB_PATH):
                       "(or __graft_entry__.build()) first")
 lib = C.CDLL(LIB_PATH)
 
-FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2, "w4pc": 3}
+FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2, "w4pc": 3, "w8g32": 4, "w8g64": 5, "w4g32": 6, "w4g64": 7}
 FMT_NAME = {v: k for k, v in FMT.items()}
 CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1

@@ -56,16 +56,25 @@ typedef enum {
   WQ_FMT_W8_PC = 0,    /* int8, symmetric, one bf16 scale per output channel       */
   WQ_FMT_W8_G128 = 1,  /* int8, symmetric, one bf16 scale per 128 consecutive k     */
   WQ_FMT_W4_G128 = 2,  /* uint4, asymmetric, fp16 scale + uint4 zero per 128 k      */
-  WQ_FMT_W4_PC = 3     /* uint4, asymmetric, fp16 scale + uint4 zero per channel    */
+  WQ_FMT_W4_PC = 3,    /* uint4, asymmetric, fp16 scale + uint4 zero per channel    */
+  WQ_FMT_W8_G32 = 4,   /* int8 as W8_G128 with one bf16 scale per 32 consecutive k  */
+  WQ_FMT_W8_G64 = 5,   /* int8 as W8_G128 with one bf16 scale per 64 consecutive k  */
+  WQ_FMT_W4_G32 = 6,   /* uint4 as W4_G128 with a scale and zero per 32 k           */
+  WQ_FMT_W4_G64 = 7    /* uint4 as W4_G128 with a scale and zero per 64 k           */
 } wq_format;
+/* The grouped formats (W8_G32/G64/G128, W4_G32/G64/G128; Gs = 32, 64 or 128 k per
+ * group, G = K / Gs groups per row) share one layout, written below for Gs = 128.
+ * Every grouped and W4 format needs K % 128 == 0 (the kernels' K steps); W4 needs
+ * N % 8 == 0.  The Marlin page's "Validation and limits" lists per-channel scales and
+ * groups of 32, 64 and 128 for INT4 and INT8 weights. */
 
 /* Memory layouts of a packed weight.
  *
  * WQ_LAYOUT_CANONICAL (interchange; what wq_pack writes):
- *   W8:  qweight int8 [N][K] row-major; scales bf16 [N] (per channel) or [N][K/128].
+ *   W8:  qweight int8 [N][K] row-major; scales bf16 [N] (per channel) or [N][G].
  *   W4:  qweight uint32 [N][K/8], bits 4j..4j+3 of word (n,c) hold q[n][8c+j];
- *        scales fp16 [N][K/128];
- *        zeros uint32 [K/128][N/8], bits 4j..4j+3 of word (g,c) hold z[8c+j][g].
+ *        scales fp16 [N][G];
+ *        zeros uint32 [G][N/8], bits 4j..4j+3 of word (g,c) hold z[8c+j][g].
  *   W4 per channel: as W4 with one group: scales fp16 [N]; zeros uint32 [N/8].
  *
  * WQ_LAYOUT_GFX950 (what the compute kernels read; written by wq_repack).  N16 =
@@ -78,13 +87,13 @@ typedef enum {
  *   so the 16 rows x 1 KB that a GEMV wave reads for one K slice are contiguous.
  *   W8:  the code bytes hold u = q + 128 (the sign bit of q flipped), so that a
  *        byte placed under the fp16 exponent byte 0x64 reads 1024 + u exactly;
- *        scales bf16 [N] for per-channel; for group-128 bf16 [N16][G][16] with
- *        element (t,g,j) = s[16t+j][g] (G = K/128): the 16 rows of a tile side by side.
+ *        scales bf16 [N] for per-channel; for the grouped formats bf16 [N16][G][16]
+ *        with element (t,g,j) = s[16t+j][g]: the 16 rows of a tile side by side.
  *   W4:  each 32-bit word of codes holds the same 8 codes as the canonical word with
  *        the nibbles interleaved: bits 4p..4p+3 hold q[n][8c + (2p mod 8) + (p >= 4)],
  *        i.e. nibble order q0 q2 q4 q6 q1 q3 q5 q7, so that (word >> 4i) & 0x000F000F
  *        yields the consecutive pair (q[8c+2i], q[8c+2i+1]) in the two 16-bit halves;
- *        scales fp16 [N16][G][16] as for W8 group-128;
+ *        scales fp16 [N16][G][16] as for grouped W8;
  *        zeros uint8 [N16][G][8], byte (t,g,h) holds z[16t+2h][g] in bits 0..3 and
  *        z[16t+2h+1][g] in bits 4..7.
  *   W4 per channel: exactly the W4 group-128 layout (same sizes) with each row's one
@@ -121,7 +130,7 @@ const char* wq_status_string(int status);
 const char* wq_last_error(void);
 
 /* Bytes of qweight, scales and zeros for a format/layout/shape (host only, no
- * device access).  Shape rules: K > 0, N > 0, K % 16 == 0; group-128 formats and W4
+ * device access).  Shape rules: K > 0, N > 0, K % 16 == 0; the grouped formats and W4
  * per channel need K % 128 == 0; W4 needs N % 8 == 0.  zero_bytes is 0 for W8.  Any out-pointer
  * may be NULL. */
 wq_status wq_packed_sizes(int fmt, int layout, int64_t K, int64_t N, size_t* qweight_bytes,
@@ -138,11 +147,11 @@ int wq_dispatch_kind(int64_t M);
 /* Quantize an fp32 weight w[N][K] (device, row-major) into `out`, which must
  * describe CANONICAL-layout buffers of wq_packed_sizes bytes.  Recipe (IEEE fp32,
  * round to nearest even, correctly rounded division):
- *   W8 (group G = K for per-channel, 128 otherwise):
+ *   W8 (group G = K for per-channel, else the format's 32, 64 or 128):
  *     a = max|w| over the group; s = bf16(a / 127);
  *     q = 0 if s == 0 else clamp(rint(w / s), -127, 127)   (divides by the stored s)
- *   W4 (group 128, or one group per output channel for WQ_FMT_W4_PC: the INT4
- *   per-channel case of the Marlin page's "Validation and limits"):
+ *   W4 (groups of 32, 64 or 128, or one group per output channel for WQ_FMT_W4_PC:
+ *   the INT4 cases of the Marlin page's "Validation and limits"):
  *     hi = max w, lo = min w over the group; s = fp16((hi - lo) / 15);
  *     s == 0 -> z = 0, q = 0; else z = clamp(rint(-lo / s), 0, 15),
  *     q = clamp(rint(w / s) + z, 0, 15).
@@ -216,7 +225,9 @@ int wq_gemv_max_split(int fmt, int64_t K);
  * WQ_GEMV_MFMA with NB in {1, 2, 4} 16-row tiles per workgroup; its 1..8 waves
  * interleave over 128-k units of the workgroup's K range and multiply on
  * v_mfma_f32_16x16x32 (bf16 and fp16) with exact code values, so its cost barely
- * grows with M; the fp32 partial sums meet in LDS in wave order. */
+ * grows with M; the fp32 partial sums meet in LDS in wave order.  Offered for the
+ * per-channel and group-128 formats (a 16x16x32 instruction sums k of four 32-k
+ * blocks, which groups of 32 or 64 would scale differently). */
 #define WQ_GEMV_MFMA 0x200
 
 /* Largest waves per GEMV workgroup for a format, 1 <= M <= 7 and rows per wave (4, 8
@@ -286,6 +297,9 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *   24  tile 9 with split-K 3 (capped and needing the workspace as 10..12): a single
  *      partial round of tiles (160 per-channel tiles at M = 2048, N = 5120) becomes
  *      work for more of the CUs.
+ * Groups of 32 and 64 run tiles 2 and 9..19, 24 as described for group-128 (their
+ * kernels fold every group's partial sum in as a group-128 tile does); tiles 1, 3 and
+ * 4 run as tile 9, tiles 5..8 and 20..23 as tile 14. 
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
 #define WQ_GEMM_TILES 24
@@ -324,8 +338,9 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
  * codes against bf16 x where fp16 cannot hold an x exactly), fp32 accumulation, group
  * scales on each group's partial sum, per-channel scales on the finished sum.  An expert
  * is read once per block of 16 of its rows, so the call suits decode-sized batches per
- * expert.  Needs K % 128 == 0, N % 16 == 0 (N % 32 == 0 gated), T * K and T * N below
- * 2^31 (else WQ_ERR_UNSUPPORTED), 1 <= E <= 65535.  Allocates nothing, needs no
+ * expert.  Needs a per-channel or group-128 format (groups of 32 and 64: as the
+ * matrix-core GEMV, WQ_ERR_UNSUPPORTED), K % 128 == 0, N % 16 == 0 (N % 32 == 0 gated),
+ * T * K and T * N below 2^31 (else WQ_ERR_UNSUPPORTED), 1 <= E <= 65535.  Allocates nothing, needs no
  * workspace, graph-capturable. */
 #define WQ_EPILOGUE_NONE 0
 #define WQ_EPILOGUE_SILU_MUL 1

@@ -47,15 +47,17 @@ def canonical_to_host(can, fmt: str) -> dict:
     s = can.scales.cpu().numpy()
     if fmt == "w8pc":
         return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.int8).reshape(N, K), scales=s.view(np.uint16).reshape(N))
-    if fmt == "w8g128":
+    if fmt.startswith("w8g"):
+        G = K // int(fmt[3:])
         return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.int8).reshape(N, K),
-                    scales=s.view(np.uint16).reshape(N, K // 128))
+                    scales=s.view(np.uint16).reshape(N, G))
     z = can.zeros.cpu().numpy()
     if fmt == "w4pc":
         return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.uint32).reshape(N, K // 8),
                     scales=s.view(np.float16).reshape(N), zeros=z.view(np.uint32).reshape(N // 8))
+    G = K // int(fmt[3:])
     return dict(fmt=fmt, K=K, N=N, qweight=q.view(np.uint32).reshape(N, K // 8),
-                scales=s.view(np.float16).reshape(N, K // 128), zeros=z.view(np.uint32).reshape(K // 128, N // 8))
+                scales=s.view(np.float16).reshape(N, G), zeros=z.view(np.uint32).reshape(G, N // 8))
 
 
 def sample_rows(N: int, count: int = 64, seed: int = 0) -> np.ndarray:

@@ -50,7 +50,7 @@ def test_packed_sizes_match_the_oracle_layout(wqlib, fmt, K, N):
     ("w8g128", 1040, 64, 2),    # K % 128
     ("w4g128", 1024, 60, 2),    # N % 8
     ("w8pc", 0, 64, 1),
-    (7, 1024, 64, 2),           # unknown format
+    (8, 1024, 64, 2),           # unknown format
 ])
 def test_packed_sizes_rejects_bad_shapes(wqlib, fmt, K, N, status):
     with pytest.raises(wqlib.WqError) as e:
@@ -343,3 +343,41 @@ def test_w4_per_channel_host_side(wqlib):
     wqlib.wq_tune_cache_set("w4pc", 5120, 27648, 1, 0, wqlib.gemv_cache_value(2, 4, 8), tag)
     assert wqlib.wq_tune_cache_get("w4g128", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
     assert wqlib.wq_tune_cache_get("w4pc", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
+
+
+def test_small_groups_host_side(wqlib):
+    """Groups of 32 and 64 (fmts 4..7): canonical sizes as the oracle's, gfx950 sizes
+    with one 16-row metadata tile per group, the shape rules (K % 128, N % 8 for W4),
+    zeros required for W4, the matrix-core GEMV and the MoE layer refused, the
+    remaining GEMV launch options offered as for group-128, and tuner entries of their
+    own (not shared with group-128: the kernels fold by another group size)."""
+    for fmt in ("w8g32", "w8g64", "w4g32", "w4g64"):
+        gs = int(fmt[3:])
+        for K, N in ((1024, 1024), (5120, 27648), (13824, 5120), (256, 40)):
+            assert wqlib.wq_packed_sizes(fmt, wqlib.CANONICAL, K, N) == OQ.packed_sizes(fmt, K, N), (fmt, K, N)
+            q, s, z = wqlib.wq_packed_sizes(fmt, wqlib.GFX950, K, N)
+            n16 = -(-N // 16)
+            assert q == (K * N if fmt.startswith("w8") else K * N // 2)
+            assert s == 2 * n16 * 16 * (K // gs)
+            assert z == (8 * n16 * (K // gs) if fmt.startswith("w4") else 0)
+        with pytest.raises(wqlib.WqError) as e:
+            wqlib.wq_packed_sizes(fmt, wqlib.CANONICAL, 1024 + 64, 64)   # K % 128 != 0
+        assert e.value.status == 2
+        assert wqlib.wq_gemv_max_split(fmt, 5120) == wqlib.wq_gemv_max_split(fmt[:3] + "128", 5120)
+        for M in range(1, 8):
+            for rows in (4, 8, 16):
+                assert wqlib.wq_gemv_max_waves(fmt, M, rows) == wqlib.wq_gemv_max_waves(fmt[:3] + "128", M, rows)
+            for nb in (16, 32, 64):
+                assert wqlib.wq_gemv_max_waves(fmt, M, nb | wqlib.GEMV_MFMA) == -1
+    L = wqlib.lib
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    d = wqlib.WqWeightC(wqlib.FMT["w4g32"], wqlib.GFX950, 1024, 64, 0x1000, 0x2000, 0)
+    assert L.wq_gemv(C.byref(d), x, 1, y, 1, None, 0, None) == 1          # W4 without zeros
+    d = wqlib.WqWeightC(wqlib.FMT["w8g64"], wqlib.GFX950, 1024, 64, 0x1000, 0x2000, 0)
+    off = C.c_void_p(0x30000)
+    assert L.wq_moe_linear(C.byref(d), 1, x, off, 8, y, 0, None) == 2     # MoE: not for groups of 64
+    assert L.wq_gemv_ex(C.byref(d), x, 1, y, 1, 1, 16 | wqlib.GEMV_MFMA, None, 0, None) == 2
+    tag = "test-small-groups:0"
+    wqlib.wq_tune_cache_set("w4g32", 5120, 27648, 1, 0, wqlib.gemv_cache_value(2, 4, 8), tag)
+    assert wqlib.wq_tune_cache_get("w4g32", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
+    assert wqlib.wq_tune_cache_get("w4g128", 5120, 27648, 1, 0, tag) is None

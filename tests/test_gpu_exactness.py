@@ -3,7 +3,7 @@ leaves the scale to fp32 sums, so an output carries only the rounding of an fp32
 and the final bf16 rounding (reading A12 of the layer: codes stay exact).  Two kinds of
 input that an approximate path would fail, each against the oracle:
 
-* large activations whose products cancel: x = +-c over pairs of 128-groups holding
+* large activations whose products cancel: x = +-c over pairs of 128-k blocks holding
   the same codes, so the exact output is 0 while the partial sums are large -- any
   arithmetic that adds a code offset (x (offset + q) - offset sum(x)) or rounds the
   dequantised weight leaves errors far beyond the tolerance here;
@@ -70,7 +70,7 @@ def _cancelling_case(fmt, K=5120, N=40, M=3, c=256.0):
     return W, OQ.bf16_rne_bits(xf)
 
 
-@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("fmt", OQ.FORMATS + OQ.SMALL_GROUPS)
 def test_cancelling_large_activations_gemv(wq, fmt):
     W, x = _cancelling_case(fmt)
     g, _ = quantize_on_gpu(wq, W, fmt)
@@ -92,7 +92,7 @@ def _tiny_case(fmt, K=5120, N=264, M=4):
     return W, OQ.bf16_rne_bits(xf.astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("fmt", OQ.FORMATS + OQ.SMALL_GROUPS)
 def test_tiny_activations_gemv(wq, fmt):
     W, x = _tiny_case(fmt)
     g, _ = quantize_on_gpu(wq, W, fmt)
@@ -117,7 +117,7 @@ def _run_gemm_tile(wq, g, x_bits, tile):
     return bf16_bits(y)
 
 
-@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("fmt", OQ.FORMATS + OQ.SMALL_GROUPS)
 @pytest.mark.parametrize("M", [8, 40, 300])
 def test_cancelling_large_activations_gemm(wq, fmt, M):
     W, x = _cancelling_case(fmt, N=264, M=M)
@@ -129,7 +129,7 @@ def test_cancelling_large_activations_gemm(wq, fmt, M):
         assert_parity(y, y_ref, f"{fmt} cancelling gemm M={M} tile={tile}")
 
 
-@pytest.mark.parametrize("fmt", OQ.FORMATS)
+@pytest.mark.parametrize("fmt", OQ.FORMATS + OQ.SMALL_GROUPS)
 @pytest.mark.parametrize("M", [8, 40, 300])
 def test_tiny_activations_gemm(wq, fmt, M):
     W, x = _tiny_case(fmt, M=M)
