@@ -43,10 +43,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_w8pc_decode_traffic.json")
 
 def algorithmic_bytes(fmt: str, K: int, N: int, M: int) -> int:
     """Packed codes + scales (+ zeros) + x + y, each counted once."""
-    G = K // 128
+    G = K // (int(fmt[3:]) if fmt[2] == "g" else 128)  # groups per row of a grouped format
     if fmt == "w8pc":
         w = K * N + 2 * N
-    elif fmt == "w8g128":
+    elif fmt.startswith("w8g"):
         w = K * N + 2 * N * G
     elif fmt == "w4pc":  # one scale and zero-point per row (the gfx950 layout repeats them per group)
         w = K * N // 2 + 2 * N + (N // 8) * 4
@@ -944,6 +944,10 @@ def run_detail(wq, torch, args) -> dict:
         # INT4 per output channel: the group-128 kernels on its repeated metadata
         "w4_per_channel": lambda: {f"w4pc_{K}x{N}_M{M}": measure(3, "w4pc", K, N, M)
                                    for K, N in [(5120, 27648)] for M in (1, 2048)},
+        # groups of 32 and 64: the dot2 GEMV and the LDS-DMA GEMM folding by the group size
+        "small_groups": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(3 if fmt.startswith("w4") else 2, fmt, K, N, M)
+                                 for fmt in ("w8g32", "w8g64", "w4g32", "w4g64")
+                                 for K, N in [(5120, 27648)] for M in (1, 2048)},
         "splitk_stress": lambda: {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
                                   for K, N in [(27648, 5120), (5120, 151936)]
                                   for fmt in ("w8pc", "w8g128", "w4g128")},
