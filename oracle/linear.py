@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 The layer is the weight-only quantised linear of the tileInfer README (feature
 table, "INT8 Weight-Only Quantization"; "Key Optimizations"): bf16 activations
 times int8 (or int4, Marlin benchmark page, "Validation and limits") weights
-carrying scales.  Its plain definition, which every GPU kernel (GEMV, split-K,
+carrying scales; the same page's list also names FP16 activations, which carry
+x and y in fp16 over the same weights.  Its plain definition, which every GPU kernel (GEMV, split-K,
 GEMM) must reach up to fp32 summation order and the final bf16 rounding:
 
     y[m, n] = sum_k x[m, k] * Wd[n, k],   Wd = dequant(packed W)   (exact fp32)
@@ -38,13 +39,30 @@ def use_gemv(M: int) -> bool:
     return M < GEMV_MAX_TOKENS + 1
 
 
-def _x64(x_bits) -> np.ndarray:
+ACTIVATIONS = ("bf16", "f16")
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """fp16 bit patterns -> the values they denote (NumPy's IEEE binary16 decode, exact;
+    subnormals, infinities and NaNs included)."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _x64(x_bits, act: str = "bf16") -> np.ndarray:
+    """Activation bit patterns -> fp64 values: bf16 (the configs' activations) or fp16
+    (the FP16 activations of the Marlin page's "Validation and limits" list)."""
+    if act == "f16":
+        return f16_bits_to_f64(x_bits)
+    if act != "bf16":
+        raise ValueError(f"unknown activation type {act!r}")
     return _quant.bf16_bits_to_f32(x_bits).astype(np.float64)
 
 
-def ref_linear(x_bits: np.ndarray, P: dict, chunk: int = 4096) -> np.ndarray:
-    """fp64 y[M, N] for bf16 x[M, K] (uint16 bits) and a canonical packed weight."""
-    x = _x64(x_bits)
+def ref_linear(x_bits: np.ndarray, P: dict, chunk: int = 4096, act: str = "bf16") -> np.ndarray:
+    """fp64 y[M, N] for x[M, K] (uint16 bits of bf16, or of fp16 with act="f16") and a
+    canonical packed weight.  The weight formats do not depend on the activation type:
+    y is the same sum whichever 16-bit type carries x."""
+    x = _x64(x_bits, act)
     N = P["N"]
     y = np.empty((x.shape[0], N), dtype=np.float64)
     for n0 in range(0, N, chunk):
@@ -54,11 +72,11 @@ def ref_linear(x_bits: np.ndarray, P: dict, chunk: int = 4096) -> np.ndarray:
     return y
 
 
-def ref_linear_columns(x_bits: np.ndarray, P: dict, cols) -> np.ndarray:
+def ref_linear_columns(x_bits: np.ndarray, P: dict, cols, act: str = "bf16") -> np.ndarray:
     """fp64 y[:, cols] only: the oracle one output channel at a time, for
     sampled checks at sizes where the full product is too slow on the host."""
     cols = np.asarray(cols)
-    x = _x64(x_bits)
+    x = _x64(x_bits, act)
     Wd = _quant.dequant(P, cols).astype(np.float64)
     return x @ Wd.T
 
@@ -87,15 +105,16 @@ def ref_linear_perm(x_bits: np.ndarray, P: dict, perm) -> np.ndarray:
     return ref_linear(gather_activations(x_bits, perm), P)
 
 
-def compare(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
-    """Per-element check of bf16 results against the fp64 reference.
+def compare(y_bits: np.ndarray, y_ref: np.ndarray, act: str = "bf16") -> dict:
+    """Per-element check of bf16 results (fp16 with act="f16") against the fp64
+    reference.
 
     Returns max(err/tol), the number of failures and the relative RMS
     ||y - y_ref|| / ||y_ref|| (the statistic the Marlin benchmark page reports
     for its fixed-input projection check).  Over a zero reference that ratio is
     0 when y is zero as well and +inf otherwise.
     """
-    y = _quant.bf16_bits_to_f32(y_bits).astype(np.float64)
+    y = _x64(y_bits, act)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     if y.shape != y_ref.shape:
         raise ValueError(f"shape mismatch {y.shape} vs {y_ref.shape}")

@@ -74,6 +74,13 @@ def activation(cfg: int, K: int, M: int) -> np.ndarray:
     return _round_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
 
 
+def activation_f16(cfg: int, K: int, M: int) -> np.ndarray:
+    """Seeded fp16 activations x[M, K] as uint16 bit patterns: the same N(0, 1) fp32
+    draws as ``activation``, rounded to fp16 (nearest even) instead of bf16."""
+    rng = np.random.default_rng([cfg, K, M, 1])
+    return rng.standard_normal((M, K), dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def one_hot_activation(K: int, cols) -> np.ndarray:
     """bf16 bit patterns of x whose row m is the unit vector e_{cols[m]}."""
     cols = list(cols)

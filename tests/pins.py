@@ -694,6 +694,44 @@ def pin_moe_grouping(seed=51, K=256, N=24):
         raise AssertionError(f"offsets {bad} accepted")
 
 
+def pin_f16_activations(seed=61):
+    """FP16 activations: the fp16 decode against the pins' own hand-written decoder on
+    every finite bit pattern and on hand values; the layer on fp16 x -- one-hot rows
+    give the exact dequantised weight, random rows agree with a rational triple loop --
+    and the parity statistic reading fp16 results."""
+    b = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = ((b >> 10) & 0x1F) != 0x1F
+    dec = OL.f16_bits_to_f64(b[finite])
+    for i in range(0, int(finite.sum()), 97):
+        assert Fraction(float(dec[i])) == _fp16_value(np.array(b[finite][i], dtype=np.uint16).view(np.float16)), hex(b[finite][i])
+    hand = OL.f16_bits_to_f64(np.array([0x3C00, 0xC000, 0x7BFF, 0x0400, 0x0001, 0x3555], dtype=np.uint16))
+    assert [Fraction(float(v)) for v in hand] == [1, -2, 65504, Fraction(1, 2 ** 14), Fraction(1, 2 ** 24),
+                                                 Fraction(1365, 4096)]
+    for fmt, K in (("w4g128", 256), ("w8pc", 96), ("w8g32", 64)):
+        W = synth.weight(seed, K, 16, outliers=fmt.startswith("w4"))
+        P = OQ.pack(fmt, W)
+        ks = [0, 31, 32, K - 1]
+        x = np.zeros((len(ks), K), dtype=np.uint16)
+        for m, k in enumerate(ks):
+            x[m, k] = 0x3C00                                  # fp16 1.0
+        y = OL.ref_linear(x, P, act="f16")
+        for m, k in enumerate(ks):
+            for n in range(16):
+                assert Fraction(float(y[m, n])) == _exact_dequant(P, n, k), (fmt, k, n)
+        x = synth.activation_f16(seed, K, 3)
+        y = OL.ref_linear(x, P, chunk=5, act="f16")
+        for m in range(3):
+            xv = [_fp16_value(np.array(v, dtype=np.uint16).view(np.float16)) for v in x[m]]
+            for n in range(0, 16, 3):
+                exact = sum(xv[k] * _exact_dequant(P, n, k) for k in range(K))
+                scale = sum(abs(xv[k] * _exact_dequant(P, n, k)) for k in range(K))
+                assert abs(Fraction(float(y[m, n])) - exact) <= scale * Fraction(K + 2, 2 ** 53), (fmt, m, n)
+    st = OL.compare(np.array([0x3C01, 0x5640, 0x0000], dtype=np.uint16), np.array([1.0, 100.0, 0.0]), act="f16")
+    assert st["fails"] == 0 and abs(st["max_ratio"] - 2.0 ** -10 / 1e-2) < 1e-12, st
+    st = OL.compare(np.array([0x3C00], dtype=np.uint16), np.array([1.5]), act="f16")
+    assert st["fails"] == 1 and abs(st["max_ratio"] - 0.5 / 0.015) < 1e-9, st
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
     pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
@@ -714,6 +752,7 @@ ALL_PINS = [
     lambda: pin_bruteforce("w4g32", 96), lambda: pin_bruteforce("w4g64", 128),
     lambda: pin_one_hot_random("w8g32"), lambda: pin_one_hot_random("w8g64"),
     lambda: pin_one_hot_random("w4g32"), lambda: pin_one_hot_random("w4g64"),
+    pin_f16_activations,
 ]
 
 

@@ -345,6 +345,23 @@ def _mut_small_group_dequant_tiles_scales(mp):
     mp.setattr(OQ, "dequant", bad)
 
 
+def _mut_f16_read_as_bf16(mp):
+    orig = OL._x64
+
+    def bad(x_bits, act="bf16"):                         # fp16 activations decoded as bf16
+        return orig(x_bits, "bf16")
+    mp.setattr(OL, "_x64", bad)
+
+
+def _mut_f16_decode_drops_subnormals(mp):
+    orig = OL.f16_bits_to_f64
+
+    def bad(bits):                                       # fp16 subnormals flushed to zero
+        v = orig(bits)
+        return np.where(np.abs(v) < 2.0 ** -14, 0.0, v)
+    mp.setattr(OL, "f16_bits_to_f64", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
@@ -355,7 +372,7 @@ MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant
              _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index,
              _mut_w4pc_groups_of_128, _mut_w4pc_zeros_reversed, _mut_w4pc_dequant_row0_zero,
              _mut_small_groups_quantised_per_128, _mut_small_group_zeros_not_transposed,
-             _mut_small_group_dequant_tiles_scales]
+             _mut_small_group_dequant_tiles_scales, _mut_f16_read_as_bf16, _mut_f16_decode_drops_subnormals]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
