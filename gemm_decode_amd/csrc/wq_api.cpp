@@ -207,7 +207,9 @@ int resolve_tile(const wq_weight* w, int64_t M) {
 }
 
 wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int split_k, int waves,
-                    int rows, void* ws, size_t ws_bytes, void* stream) {
+                    int rows, void* ws, size_t ws_bytes, void* stream, int act = WQ_ACT_BF16) {
+  if (act != WQ_ACT_BF16 && act != WQ_ACT_F16) return fail(WQ_ERR_INVALID_ARG, "unknown activation type");
+  const bool xf = act == WQ_ACT_F16;
   wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
   const wq_weight cview = compute_view(*w0);
@@ -222,10 +224,14 @@ wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int 
                 "or 16, 32, 64 or 128 | WQ_GEMV_MFMA");
   if (rows & (kGemvPrefetch | kGemvMfma) && gemv_max_waves(w->fmt, (int)M, rows) == 0)
     return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: this rows flag is not offered at this format, M and rows");
+  if (xf && (rows & (kGemvPrefetch | kGemvMfma)))
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: fp16 activations take rows 4, 8 or 16 without flags");
   int split = split_k, wv = waves, rw = rows;
   if (split_k == 0) {
     int tw = 0, tr = 0;
     resolve_gemv(w, M, &split, &tw, &tr);
+    if (xf && (tr & kGemvMfma)) tw = tr = 0;  // (tuned for bf16 x:) the default dot2 launch
+    if (xf) tr &= ~kGemvPrefetch;             // the same launch without the prefetch set
     if (wv == 0) wv = tw;
     if (rw == 0) rw = tr;
     if (split > 1 && (!ws || ws_bytes < gemv_workspace_bytes(w->N, M, split))) {
@@ -237,22 +243,25 @@ wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int 
   if (rw == 0) rw = gemv_default_rows(w->K, w->N, w->fmt, (int)M);
   if (wv == 0) wv = gemv_default_waves(w->K, w->N, w->fmt, (int)M, split, rw);
   return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, wv, rw, ws,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, xf);
 }
 
 wq_status gemm_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int tile, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, void* stream, int act = WQ_ACT_BF16) {
+  if (act != WQ_ACT_BF16 && act != WQ_ACT_F16) return fail(WQ_ERR_INVALID_ARG, "unknown activation type");
+  const bool xf = act == WQ_ACT_F16;
   wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
   if (st != WQ_OK) return st;
   const wq_weight cview = compute_view(*w0);
   const wq_weight* w = &cview;
   if ((st = check_xy(x, y, M)) != WQ_OK) return st;
   if (tile < 0 || tile > WQ_GEMM_TILES) return fail(WQ_ERR_INVALID_ARG, "wq_gemm: bad tile id");
-  const int t = tile == 0 ? resolve_tile(w, M) : small_group(w->fmt) ? small_group_tile(tile) : tile;
+  int t = tile == 0 ? resolve_tile(w, M) : small_group(w->fmt) ? small_group_tile(tile) : tile;
+  if (xf) t = act_tile(w->fmt, t);
   if (tile != 0 && gemm_workspace_bytes(w->fmt, w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, w->N, M, t)))
     return fail(WQ_ERR_WORKSPACE, "wq_gemm: tile " + std::to_string(t) + " needs a workspace of " +
                                       std::to_string(gemm_workspace_bytes(w->fmt, w->N, M, t)) + " bytes");
-  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream);
+  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream, xf);
 }
 
 }  // namespace
@@ -466,6 +475,26 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
   if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
   if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream);
   return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream);
+}
+
+wq_status wq_linear_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream, act);
+  return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream, act);
+}
+
+wq_status wq_gemv_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int split_k, int waves,
+                      int rows, void* ws, size_t ws_bytes, void* stream) {
+  if (split_k < 0) return fail(WQ_ERR_INVALID_ARG, "wq_gemv_act: split_k must be 0 (tuned) or >= 1");
+  if (split_k == 0 && (waves != 0 || rows != 0))
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv_act: waves and rows need an explicit split_k");
+  return gemv_impl(w, x, M, y, split_k, waves, rows, ws, ws_bytes, stream, act);
+}
+
+wq_status wq_gemm_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int tile, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return gemm_impl(w, x, M, y, tile, ws, ws_bytes, stream, act);
 }
 
 // ------------------------------------------------- the layer without allocation

@@ -25,6 +25,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
@@ -38,35 +40,55 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+// two small integers (exact in both 16-bit types) as a pair of the operand type: bf16,
+// or fp16 for fp16 activations (XF)
+template <bool XF>
+__device__ __forceinline__ uint32_t pack_x2(float lo, float hi) {
+  if constexpr (XF) return __builtin_bit_cast(uint32_t, h16x2_t{(_Float16)lo, (_Float16)hi});
+  else return pack_bf16x2(lo, hi);
+}
+// an fp32 result as the output type (nearest even): bf16, or fp16 with XF
+template <bool XF>
+__device__ __forceinline__ uint16_t f32_to_out(float v) {
+  if constexpr (XF) return __builtin_bit_cast(uint16_t, (_Float16)v);
+  else return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
 
-// gfx950 int8 codes are u = q + 128; flipping the sign bit gives q.
+// gfx950 int8 codes are u = q + 128; flipping the sign bit gives q (as bf16, or fp16 with XF).
+template <bool XF = false>
 __device__ __forceinline__ uint4 i8x16_to_bf16_lo(uint4 v) {
   auto cvt = [](uint32_t d) -> uint2 {
     d ^= 0x80808080u;
-    return make_uint2(pack_bf16x2((float)(int8_t)(d & 0xFFu), (float)(int8_t)((d >> 8) & 0xFFu)),
-                      pack_bf16x2((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24)));
+    return make_uint2(pack_x2<XF>((float)(int8_t)(d & 0xFFu), (float)(int8_t)((d >> 8) & 0xFFu)),
+                      pack_x2<XF>((float)(int8_t)((d >> 16) & 0xFFu), (float)(int8_t)(d >> 24)));
   };
   uint2 a = cvt(v.x), b = cvt(v.y);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
+template <bool XF = false>
 __device__ __forceinline__ uint4 i8x16_to_bf16_hi(uint4 v) {
-  return i8x16_to_bf16_lo(make_uint4(v.z, v.w, 0, 0));
+  return i8x16_to_bf16_lo<XF>(make_uint4(v.z, v.w, 0, 0));
 }
 
-// One gfx950-layout W4 word (8 codes, nibbles q0 q2 q4 q6 q1 q3 q5 q7) -> 8 exact bf16 (q - z).
+// One gfx950-layout W4 word (8 codes, nibbles q0 q2 q4 q6 q1 q3 q5 q7) -> 8 exact bf16 (q - z)
+// (fp16 with XF).
+template <bool XF = false>
 __device__ __forceinline__ uint4 w4_word_to_bf16(uint32_t w, float z) {
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = (float)((w >> (4 * i)) & 0xFu) - z;
     const float hi = (float)((w >> (16 + 4 * i)) & 0xFu) - z;
-    o[i] = pack_bf16x2(lo, hi);
+    o[i] = pack_x2<XF>(lo, hi);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// gshift: the grouped formats' group size is 2^gshift k (32, 64 or 128)
-template <int FMT>
+// gshift: the grouped formats' group size is 2^gshift k (32, 64 or 128).  XF: x and y in
+// fp16 (fp16 activations): the codes go to LDS as fp16 and the products run on
+// v_mfma_f32_32x32x16_f16 (every code value and every fp16 x is exact in fp16, their
+// products in fp32).
+template <int FMT, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ qw,
                                                      const uint16_t* __restrict__ scales,
                                                      const uint8_t* __restrict__ zeros,
@@ -119,8 +141,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
       for (int j = 0; j < 2; ++j) {
         const int i = tid + 256 * j;
         const int row = i >> 2, col = (i & 3) * 16;
-        *reinterpret_cast<uint4*>(&Bs[row * LDA + col]) = i8x16_to_bf16_lo(wb[j]);
-        *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 8]) = i8x16_to_bf16_hi(wb[j]);
+        *reinterpret_cast<uint4*>(&Bs[row * LDA + col]) = i8x16_to_bf16_lo<XF>(wb[j]);
+        *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 8]) = i8x16_to_bf16_hi<XF>(wb[j]);
       }
     } else {
       const int row = tid >> 1, col = (tid & 1) * 32;
@@ -128,10 +150,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
       const int g = (k0 + col) >> gshift;  // this thread's 32 k lie in one group
       const uint32_t zb = zeros[(((size_t)(n / kGemvTileRows) * G + g) * kGemvTileRows + n % kGemvTileRows) / 2];
       const float z = (float)((zb >> ((n & 1) * 4)) & 0xFu);
-      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 0]) = w4_word_to_bf16(wb[0].x, z);
-      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 8]) = w4_word_to_bf16(wb[0].y, z);
-      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 16]) = w4_word_to_bf16(wb[0].z, z);
-      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 24]) = w4_word_to_bf16(wb[0].w, z);
+      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 0]) = w4_word_to_bf16<XF>(wb[0].x, z);
+      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 8]) = w4_word_to_bf16<XF>(wb[0].y, z);
+      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 16]) = w4_word_to_bf16<XF>(wb[0].z, z);
+      *reinterpret_cast<uint4*>(&Bs[row * LDA + col + 24]) = w4_word_to_bf16<XF>(wb[0].w, z);
     }
   };
 
@@ -163,14 +185,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
         const int row = wn * 64 + j * 32 + l32;
         bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[row * LDA + kk + 8 * lh]);
       }
+      auto mfma = [&](const bf16x8_t& a, const bf16x8_t& b, const floatx16& c) -> floatx16 {
+        if constexpr (XF)
+          return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h16x8_t, a), __builtin_bit_cast(h16x8_t, b),
+                                                        c, 0, 0, 0);
+        else
+          return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+      };
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if constexpr (kGrouped)
-            tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], tmp[i][j], 0, 0, 0);
+            tmp[i][j] = mfma(af[i], bfr[j], tmp[i][j]);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
         }
       // the end of a group: its partial sums, times the group scale, into acc
       if constexpr (kGrouped) {
@@ -205,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 64 + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(s * acc[i][j][a]));
+        if (m < M) y[(size_t)m * N + n] = f32_to_out<XF>(s * acc[i][j][a]);
       }
   }
 }
@@ -883,7 +912,9 @@ __global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __re
 // XH: xd is x already in fp16, row m scaled by 1 / xinv[m] (x_to_f16_rows_kernel);
 // otherwise xd == x and the stages are converted in LDS.  The exact fallback always
 // reads the bf16 x.
-template <int FMT, int WM, int WN, bool XH = false, int TM = DBM, int GS = kGroup>
+// XF: fp16 activations -- x arrives as fp16 (passed as xd, with XH), needs no row
+// scale, no exact fallback (fp16 x times exact fp16 codes is exact in fp32), and y is fp16.
+template <int FMT, int WM, int WN, bool XH = false, int TM = DBM, int GS = kGroup, bool XF = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint8_t* __restrict__ zeros,
@@ -1133,23 +1164,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
 
   // ---- a non-finite accumulator (an x that fp16 cannot hold exactly arrives as NaN,
   // and beyond fp16's range products overflow) sends the tile down the exact path
-  bool bad = false;
+  // (fp16 activations are the operands themselves: their results stand as computed)
+  if constexpr (!XF) {
+    bool bad = false;
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < CB; ++j)
+      for (int j = 0; j < CB; ++j)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) bad |= !__builtin_isfinite(acc[i][j][a]);
-  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  if (lane == 0) wave_flag[wave] = wave_bad ? 1 : 0;
-  __syncthreads();
-  int any = 0;
+        for (int a = 0; a < 16; ++a) bad |= !__builtin_isfinite(acc[i][j][a]);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) wave_flag[wave] = wave_bad ? 1 : 0;
+    __syncthreads();
+    int any = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) any |= wave_flag[w];
-  if (any) {
-    g128_tile_exact<FMT, TM, GS>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT,
-                                 S, wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
-    return;
+    for (int w = 0; w < NW; ++w) any |= wave_flag[w];
+    if (any) {
+      g128_tile_exact<FMT, TM, GS>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT,
+                                   S, wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
+      return;
+    }
   }
   // ---- epilogue: D[row = 8*(a/4) + 4*(lane/32) + a%4][col = lane%32] of each 32x32 block;
   // split-K ranges write fp32 partials
@@ -1163,8 +1197,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
-        const float v = XH ? acc[i][j][a] * xinv[m] : acc[i][j][a];  // the row's scale back out (exact)
-        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        const float v = XH && !XF ? acc[i][j][a] * xinv[m] : acc[i][j][a];  // the row's scale back out (exact)
+        if (S == 1) y[(size_t)m * N + n] = f32_to_out<XF>(v);
         else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = v;
       }
   }
@@ -1599,7 +1633,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
 
 // y[m][n] = bf16(s[n] * sum_s part[s][m][n]) (per channel) or bf16(sum_s part[s][m][n]),
 // the split ranges added in order.
-template <bool kPerChannel>
+template <bool kPerChannel, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ part,
                                                                   const uint16_t* __restrict__ scales,
                                                                   uint16_t* __restrict__ y, int M, int N,
@@ -1610,14 +1644,14 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   float v = 0.f;
   for (int s = 0; s < S; ++s) v += part[(int64_t)s * MN + i];
   const float sc = kPerChannel ? bf16_to_f32(scales[i % N]) : 1.f;
-  y[i] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v));
+  y[i] = f32_to_out<XF>(sc * v);
 }
 
 // The split tail tiles of tile 13: y = the ranges' fp32 partials added in range order
 // (times the channel scale for per-channel W8).  blockIdx.y: tail tile; a thread takes
 // 8 consecutive columns of one row (32 threads per row, 8 rows per block, blockIdx.x:
 // the row group).
-template <bool kPerChannel, int TM>
+template <bool kPerChannel, int TM, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __restrict__ part,
                                                                 const uint16_t* __restrict__ scales,
                                                                 uint16_t* __restrict__ y, int M, int N,
@@ -1638,7 +1672,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __re
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float sc = kPerChannel ? bf16_to_f32(scales[min(n + j, N - 1)]) : 1.f;
-    o[j] = __builtin_bit_cast(uint16_t, (__bf16)(sc * v[j]));
+    o[j] = f32_to_out<XF>(sc * v[j]);
   }
   uint16_t* yo = y + (size_t)m * N + n;
   if (N % 8 == 0) {  // n + 8 <= N and 16-byte aligned
@@ -1779,8 +1813,11 @@ static hipError_t x_to_f16_rows(const uint16_t* x, int64_t M, int K, void* ws, s
 template <int F, int TMV, int GS>
 static void g_dma_launch(dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
                          const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y, float* part, int M,
-                         int K, int N, int tail0, int tailS) {
-  if (xh)
+                         int K, int N, int tail0, int tailS, bool xf) {
+  if (xf)  // fp16 activations: x is the fp16 operand
+    gemm_dma_g128_kernel<F, 1, 8, true, TMV, GS, true>
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS);
+  else if (xh)
     gemm_dma_g128_kernel<F, 1, 8, true, TMV, GS>
         <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
   else
@@ -1790,33 +1827,48 @@ static void g_dma_launch(dim3 grid, hipStream_t s, const uint8_t* qw, const uint
 template <int F, int TMV>
 static void g_dma_launch_gs(int gs, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
                             const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
-                            float* part, int M, int K, int N, int tail0, int tailS) {
-  if (gs == 32) g_dma_launch<F, TMV, 32>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
-  else if (gs == 64) g_dma_launch<F, TMV, 64>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
-  else g_dma_launch<F, TMV, kGroup>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+                            float* part, int M, int K, int N, int tail0, int tailS, bool xf) {
+  if (gs == 32) g_dma_launch<F, TMV, 32>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+  else if (gs == 64) g_dma_launch<F, TMV, 64>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+  else g_dma_launch<F, TMV, kGroup>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
 }
 static void g_dma_dispatch(int fmt, int tm, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
                            const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
-                           float* part, int M, int K, int N, int tail0, int tailS) {
+                           float* part, int M, int K, int N, int tail0, int tailS, bool xf) {
   const int gs = meta_group(fmt);
   if (family(fmt) == WQ_FMT_W4_G128) {
-    if (tm == 64) g_dma_launch_gs<WQ_FMT_W4_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
-    else g_dma_launch_gs<WQ_FMT_W4_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+    if (tm == 64)
+      g_dma_launch_gs<WQ_FMT_W4_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+    else
+      g_dma_launch_gs<WQ_FMT_W4_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
   } else {
-    if (tm == 64) g_dma_launch_gs<WQ_FMT_W8_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
-    else g_dma_launch_gs<WQ_FMT_W8_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+    if (tm == 64)
+      g_dma_launch_gs<WQ_FMT_W8_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+    else
+      g_dma_launch_gs<WQ_FMT_W8_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
   }
+}
+// the split-K reduction of the GEMM tiles, with the output type of the call
+static void splitk_reduce(bool pc, bool xf, const float* part, const uint16_t* sc, uint16_t* y, int64_t M, int N,
+                          int S, hipStream_t s) {
+  const int64_t MN = M * N;
+  const unsigned blocks = (unsigned)((MN + 255) / 256);
+  if (pc && xf) gemm_splitk_reduce_kernel<true, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
+  else if (pc) gemm_splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
+  else if (xf) gemm_splitk_reduce_kernel<false, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
+  else gemm_splitk_reduce_kernel<false><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
 }
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
-                      void* ws, size_t ws_bytes, hipStream_t s) {
+                      void* ws, size_t ws_bytes, hipStream_t s, bool xf) {
   const int K = (int)w->K, N = (int)w->N;
   if (M > 65535LL * BM) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: M too large");
   const uint8_t* qw = (const uint8_t*)w->qweight;
   const uint16_t* sc = (const uint16_t*)w->scales;
   const uint8_t* zs = (const uint8_t*)w->zeros;
   if (w->fmt == WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: per-channel W4 runs through its compute view");
-  if (small_group(w->fmt)) tile = small_group_tile(tile);
+  if (xf) tile = act_tile(w->fmt, tile);  // the kernels with an fp16-activation form
+  else if (small_group(w->fmt)) tile = small_group_tile(tile);
   if (tile >= kMmaTile0 && tile <= kMmaTileLast) {
     // 8..16 tokens: the matrix-core GEMV kernel (one 16-token A operand)
     int S = gemm_mma_split(tile, M, K);
@@ -1864,17 +1916,14 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     } else {
       uint16_t* xh = nullptr;
       float* xinv = nullptr;
-      WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh,
-                                 &xinv, s));
-      g_dma_dispatch(w->fmt, tm, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, (int)total, 1);
+      if (!xf)
+        WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh,
+                                   &xinv, s));
+      g_dma_dispatch(w->fmt, tm, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, (int)total, 1, xf);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
-      const int64_t MN = M * N;
-      if (pc)
-        gemm_splitk_reduce_kernel<true><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
-      else
-        gemm_splitk_reduce_kernel<false><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      splitk_reduce(pc, xf, part, sc, y, M, N, S, s);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;
@@ -1916,22 +1965,20 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       // x in fp16 (rows scaled) after the partials when the workspace has room for it
       uint16_t* xh = nullptr;
       float* xinv = nullptr;
-      WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, part_bytes, &xh, &xinv, s));
-      g_dma_dispatch(w->fmt, 128, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS);
+      if (!xf) WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, part_bytes, &xh, &xinv, s));
+      g_dma_dispatch(w->fmt, 128, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS, xf);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
-      const int64_t MN = M * N;
-      if (pc)
-        gemm_splitk_reduce_kernel<true><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
-      else
-        gemm_splitk_reduce_kernel<false><<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(part, sc, y, (int)M, N, S);
+      splitk_reduce(pc, xf, part, sc, y, M, N, S, s);
       WQ_HIP_CHECK(hipGetLastError());
     }
     if (tailS > 1) {
       const dim3 rg((unsigned)(btm / 8), (unsigned)ntail);
       if (pc)
         gemm_tail_reduce_kernel<true, 256><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+      else if (xf)
+        gemm_tail_reduce_kernel<false, 128, true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       else
         gemm_tail_reduce_kernel<false, 128><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
       WQ_HIP_CHECK(hipGetLastError());
@@ -1939,7 +1986,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     return WQ_OK;
   }
   if (dma_tile) tile = 1;
-  if (tile == 1 && !small_group(w->fmt)) {  // (groups of 32 and 64 take tile 2's kernel)
+  if (tile == 1 && !small_group(w->fmt) && !xf) {  // (groups of 32 and 64 and fp16 x take tile 2's kernel)
     const int bn = w->fmt == WQ_FMT_W8_PC ? Big<WQ_FMT_W8_PC>::BN : Big<WQ_FMT_W8_G128>::BN;
     const int64_t total = ((M + BM2 - 1) / BM2) * ((N + bn - 1) / bn);
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
@@ -1963,13 +2010,16 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const int gshift = meta_group(w->fmt) == 32 ? 5 : meta_group(w->fmt) == 64 ? 6 : 7;
   switch (family(w->fmt)) {
     case WQ_FMT_W8_PC:
-      gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W8_PC, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      else gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     case WQ_FMT_W8_G128:
-      gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W8_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      else gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     case WQ_FMT_W4_G128:
-      gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W4_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      else gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
       break;
     default:
       return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");

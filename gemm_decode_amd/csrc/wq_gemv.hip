@@ -70,6 +70,14 @@ __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builti
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: nearest even
 }
+__device__ __forceinline__ uint16_t f32_to_f16(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: nearest even
+}
+// an fp32 result as the output type: bf16, or fp16 for fp16 activations (XF)
+template <bool XF>
+__device__ __forceinline__ uint16_t f32_to_out(float v) {
+  return XF ? f32_to_f16(v) : f32_to_bf16(v);
+}
 // bf16 pair -> fp16 pair (exact in the range described above)
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
   auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
@@ -171,7 +179,9 @@ constexpr int max_waves_r(int fmt, int RR, int M, bool PF) {
 }
 
 // grid = (16-row tiles x sub-tiles of RR rows, split_k); block = 64 * W threads.
-template <int FMT, int M, int RR, bool PF>
+// XF: x and y in fp16 (fp16 activations): x is already the fp16 operand, so the
+// conversion and its exactness check drop out, and y is rounded to fp16.
+template <int FMT, int M, int RR, bool PF, bool XF = false>
 __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
@@ -255,13 +265,16 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     auto zero_of = [&](int r) -> uint32_t { return ((r < 8 ? zw : zw_hi) >> (4 * (r & 7))) & 0xFu; };
 
     // Does every x of the slice convert to fp16 exactly (see F16Exact)?  Otherwise the
-    // whole wave takes the bf16 path for this slice.
-    F16Exact fx;
+    // whole wave takes the bf16 path for this slice.  (fp16 x: it is the operand.)
+    bool exact_path = false;
+    if constexpr (!XF) {
+      F16Exact fx;
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+      for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int i = 0; i < F::kXWords; ++i) fx.add(xb[m][i]);
-    const bool exact_path = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
+        for (int i = 0; i < F::kXWords; ++i) fx.add(xb[m][i]);
+      exact_path = __builtin_amdgcn_ballot_w64(!fx.ok()) != 0;
+    }
 
     if constexpr (!kW4) {
       // ---- int8: fp16 (1024 + u) by v_perm_b32, minus 1152 by one packed fp16 add: the
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
+          for (int i = 0; i < 8; ++i) xh[m][i] = XF ? xb[m][i] : bf16x2_to_f16x2(xb[m][i]);
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
           const uint32_t d[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
 #pragma unroll
       for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xh[m][i] = bf16x2_to_f16x2(xb[m][i]);
+        for (int i = 0; i < 16; ++i) xh[m][i] = XF ? xb[m][i] : bf16x2_to_f16x2(xb[m][i]);
 #pragma unroll
       for (int r = 0; r < RR; ++r) {
         const float sc = f16_to_f32(scale_of(r));
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     if (S == 1) {
       const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
 #pragma unroll
-      for (int m = 0; m < M; ++m) y[(size_t)m * N + n] = f32_to_bf16(sc * v[m]);
+      for (int m = 0; m < M; ++m) y[(size_t)m * N + n] = f32_to_out<XF>(sc * v[m]);
     } else {
 #pragma unroll
       for (int m = 0; m < M; ++m) part[((size_t)s * M + m) * N + n] = v[m];
@@ -508,8 +521,8 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
   }
 }
 
-// y[m][n] = bf16(scale[n] * sum_s part[s][m][n]), ranges added in order.
-template <int FMT>
+// y[m][n] = bf16(scale[n] * sum_s part[s][m][n]) (fp16 with XF), ranges added in order.
+template <int FMT, bool XF = false>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ scales,
                                                               uint16_t* __restrict__ y, int M,
@@ -521,7 +534,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int s = 0; s < S; ++s) v += part[(int64_t)s * MN + i];
   const int n = (int)(i % N);
   const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
-  y[i] = f32_to_bf16(sc * v);
+  y[i] = f32_to_out<XF>(sc * v);
 }
 
 // ---------------------------------------------------------------------------------
@@ -959,8 +972,12 @@ void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t
 }
 
 template <int FMT, int M, int RR>
-void launch_rr(bool pf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
+void launch_rr(bool pf, bool xf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
                const uint16_t* x, uint16_t* y, float* part, int K, int N, int gshift, hipStream_t st) {
+  if (xf) {  // fp16 activations: no prefetch variant (the launcher checks)
+    gemv_kernel<FMT, M, RR, false, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
+    return;
+  }
   if constexpr (prefetch_allowed(FMT, RR, M)) {
     if (pf) {
       gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
@@ -972,14 +989,14 @@ void launch_rr(bool pf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t
 
 // rows: 4, 8 or 16, optionally | kGemvPrefetch (checked by the caller)
 template <int FMT, int M>
-wq_status launch_m(int rows, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
+wq_status launch_m(int rows, bool xf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
                    const uint8_t* zs, const uint16_t* x, uint16_t* y, float* part, int K, int N,
                    int gshift, hipStream_t st) {
   const bool pf = (rows & kGemvPrefetch) != 0;
   switch (rows & ~kGemvPrefetch) {
-    case 4: launch_rr<FMT, M, 4>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 8: launch_rr<FMT, M, 8>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 16: launch_rr<FMT, M, 16>(pf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 4: launch_rr<FMT, M, 4>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 8: launch_rr<FMT, M, 8>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 16: launch_rr<FMT, M, 16>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   }
   return WQ_OK;
@@ -987,8 +1004,10 @@ wq_status launch_m(int rows, dim3 grid, dim3 block, const uint8_t* qw, const uin
 
 template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                     int waves, int rows, void* ws, hipStream_t st) {
+                     int waves, int rows, void* ws, bool xf, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
+  if (xf && (rows & (kGemvMfma | kGemvPrefetch)))
+    return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: fp16 activations take the dot2 GEMV without prefetch");
   const int gshift = meta_group(w->fmt) == 32 ? 5 : meta_group(w->fmt) == 64 ? 6 : 7;
   float* part = (float*)ws;
   const uint8_t* qw = (const uint8_t*)w->qweight;
@@ -1016,13 +1035,13 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
   dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
   dim3 block(64 * waves);
   switch (M) {
-    case 1: r = launch_m<FMT, 1>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 2: r = launch_m<FMT, 2>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 3: r = launch_m<FMT, 3>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 4: r = launch_m<FMT, 4>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 5: r = launch_m<FMT, 5>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 6: r = launch_m<FMT, 6>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 7: r = launch_m<FMT, 7>(rows, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 1: r = launch_m<FMT, 1>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 2: r = launch_m<FMT, 2>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 3: r = launch_m<FMT, 3>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 4: r = launch_m<FMT, 4>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 5: r = launch_m<FMT, 5>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 6: r = launch_m<FMT, 6>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 7: r = launch_m<FMT, 7>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   }
   }
@@ -1030,7 +1049,8 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
   WQ_HIP_CHECK(hipGetLastError());
   if (split_k > 1) {
     const int64_t MN = (int64_t)M * N;
-    splitk_reduce_kernel<FMT><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k);
+    if (xf) splitk_reduce_kernel<FMT, true><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k);
+    else splitk_reduce_kernel<FMT><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k);
     WQ_HIP_CHECK(hipGetLastError());
   }
   return WQ_OK;
@@ -1088,7 +1108,7 @@ int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int ro
 }
 
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                      int waves, int rows, void* ws, hipStream_t s) {
+                      int waves, int rows, void* ws, hipStream_t s, bool xf) {
   const int cap = gemv_max_waves(w->fmt, M, rows);
   if (cap == 0) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   if (waves < 1 || waves > cap)
@@ -1096,9 +1116,9 @@ wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y,
                                         std::to_string(cap) + " waves");
   if (w->fmt == WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: per-channel W4 runs through its compute view");
   switch (family(w->fmt)) {
-    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, s);
-    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, s);
-    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, s);
+    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, xf, s);
+    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, xf, s);
+    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, xf, s);
   }
   return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: unknown format");
 }

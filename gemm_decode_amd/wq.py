@@ -23,6 +23,7 @@ __all__ = [
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
     "wq_linear_perm_workspace_size", "wq_linear_perm", "wq_linear_static", "STATIC_SCRATCH_BYTES",
     "wq_moe_linear", "quantize_experts", "EPILOGUE_NONE", "EPILOGUE_SILU_MUL",
+    "ACT", "wq_linear_act", "wq_gemv_act", "wq_gemm_act",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -47,6 +48,7 @@ GEMV_PREFETCH = 0x100                    # WQ_GEMV_PREFETCH: rows flag, slice pr
 GEMV_MFMA = 0x200                        # WQ_GEMV_MFMA: rows flag: the matrix-core GEMV (rows = 16 NB)
 STATIC_SCRATCH_BYTES = 64 << 20          # WQ_STATIC_SCRATCH_BYTES: the scratch of wq_linear_static
 EPILOGUE_NONE, EPILOGUE_SILU_MUL = 0, 1  # WQ_EPILOGUE_*: epilogues of wq_moe_linear
+ACT = {"bf16": 0, "f16": 1}              # WQ_ACT_*: activation types of the *_act entry points
 
 
 def gemv_cache_value(split_k: int, waves: int = 0, rows: int = 0) -> int:
@@ -79,6 +81,11 @@ _SIGS = {
     "wq_gemm": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "wq_linear_static": (C.c_int, [_W, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "wq_linear_act": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_gemv_act": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                              C.c_size_t, C.c_void_p]),
+    "wq_gemm_act": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t,
+                              C.c_void_p]),
     "wq_moe_linear": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]),
     "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
     "wq_linear_perm_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
@@ -255,8 +262,9 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def _xy(x: torch.Tensor, y: torch.Tensor, w: PackedWeight):
-    assert x.dtype == torch.bfloat16 and y.dtype == torch.bfloat16
+def _xy(x: torch.Tensor, y: torch.Tensor, w: PackedWeight, dtype=None):
+    dtype = torch.bfloat16 if dtype is None else dtype
+    assert x.dtype == dtype and y.dtype == dtype
     assert x.is_contiguous() and y.is_contiguous()
     M = x.numel() // w.K
     assert x.numel() == M * w.K and y.numel() == M * w.N, "x/y sizes do not match the weight"
@@ -289,6 +297,33 @@ def wq_linear(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tenso
     M, d = _xy(x, y, w), w.desc()
     _check(lib.wq_linear(C.byref(d), _ptr(x), M, _ptr(y), _ptr(ws),
                          0 if ws is None else ws.numel(), _stream(stream)), "wq_linear")
+
+
+def _act(x: torch.Tensor) -> int:
+    """Activation type of a bf16 or fp16 tensor."""
+    return ACT["f16"] if x.dtype == torch.float16 else ACT["bf16"]
+
+
+def wq_linear_act(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None = None,
+                  stream=None) -> None:
+    """wq_linear for bf16 or fp16 x and y (the activation type follows x)."""
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_linear_act(C.byref(d), _act(x), _ptr(x), M, _ptr(y), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(stream)), "wq_linear_act")
+
+
+def wq_gemv_act(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, split_k: int = 0, waves: int = 0,
+                rows: int = 0, ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_gemv_act(C.byref(d), _act(x), _ptr(x), M, _ptr(y), split_k, waves, rows, _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv_act")
+
+
+def wq_gemm_act(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0,
+                ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_gemm_act(C.byref(d), _act(x), _ptr(x), M, _ptr(y), tile, _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)), "wq_gemm_act")
 
 
 def wq_linear_static(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:

@@ -311,6 +311,36 @@ wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int til
 wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------- fp16 activations */
+
+/* Activation types of the *_act entry points: the 16-bit type of x and of y. */
+#define WQ_ACT_BF16 0
+#define WQ_ACT_F16 1
+
+/* The layer, the GEMV and the GEMM with x and y in the given activation type: the FP16
+ * and BF16 activations that the Marlin page's "Validation and limits" lists, over the
+ * same weight formats.  WQ_ACT_BF16 is wq_linear / wq_gemv_ex / wq_gemm.  With
+ * WQ_ACT_F16, x is fp16 [M][K] (16-byte aligned) and y fp16 [M][N]: every path
+ * multiplies fp16 x by exact fp16 code values (q, or q - z; the products are exact in
+ * fp32), accumulates in fp32, applies the scales to fp32 sums as for bf16 and rounds y
+ * to fp16 (nearest even; beyond 65504 to infinity).
+ *   - GEMV (M < 8): the dot2 launch options (rows 4, 8 or 16 without a flag; a flag:
+ *     WQ_ERR_UNSUPPORTED).  split_k 0 = the tuned launch of the bf16 layer with its
+ *     matrix-core option replaced by the default dot2 launch and its prefetch flag
+ *     dropped (waves and rows must then be 0); else as wq_gemv_ex.
+ *   - GEMM (M >= 8): per-channel W8 runs tile 2's kernel for every tile id; the grouped
+ *     formats run tile 2 and the LDS-DMA tiles 9..19 and 24 (x read as their fp16
+ *     operand: no conversion, no row scale, no fallback), tiles 1, 3, 4 as 9 and 5..8,
+ *     20..23 as 14.  The workspace is wq_workspace_size's.
+ * wq_moe_linear, wq_lm_head_topk, wq_linear_perm and wq_linear_static take bf16 only.
+ * Unknown act: WQ_ERR_INVALID_ARG. */
+wq_status wq_linear_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, void* ws,
+                        size_t ws_bytes, void* stream);
+wq_status wq_gemv_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int split_k, int waves,
+                      int rows, void* ws, size_t ws_bytes, void* stream);
+wq_status wq_gemm_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int tile, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------- grouped (MoE) layer */
 
 /* The grouped weight-only linear of a mixture-of-experts layer (the shared MoE kernel the

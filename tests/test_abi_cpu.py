@@ -381,3 +381,19 @@ def test_small_groups_host_side(wqlib):
     wqlib.wq_tune_cache_set("w4g32", 5120, 27648, 1, 0, wqlib.gemv_cache_value(2, 4, 8), tag)
     assert wqlib.wq_tune_cache_get("w4g32", 5120, 27648, 1, 0, tag) == wqlib.gemv_cache_value(2, 4, 8)
     assert wqlib.wq_tune_cache_get("w4g128", 5120, 27648, 1, 0, tag) is None
+
+
+def test_activation_type_validation(wqlib):
+    """The *_act entry points: an unknown activation type and, for fp16 x, the GEMV's
+    matrix-core and prefetch options are refused on the host."""
+    L = wqlib.lib
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    d = wqlib.WqWeightC(wqlib.FMT["w8pc"], wqlib.GFX950, 1024, 64, 0x1000, 0x2000, 0)
+    assert wqlib.ACT == {"bf16": 0, "f16": 1}
+    assert L.wq_linear_act(C.byref(d), 2, x, 1, y, None, 0, None) == 1
+    assert L.wq_gemv_act(C.byref(d), -1, x, 1, y, 1, 0, 0, None, 0, None) == 1
+    assert L.wq_gemm_act(C.byref(d), 7, x, 8, y, 2, None, 0, None) == 1
+    assert L.wq_gemv_act(C.byref(d), 1, x, 1, y, 1, 1, 16 | wqlib.GEMV_MFMA, None, 0, None) == 2
+    assert L.wq_gemv_act(C.byref(d), 1, x, 1, y, 1, 1, 4 | wqlib.GEMV_PREFETCH, None, 0, None) == 2
+    assert L.wq_gemv_act(C.byref(d), 1, x, 1, y, 0, 2, 0, None, 0, None) == 1    # waves without a split
+    assert L.wq_gemv_act(C.byref(d), 1, x, 8, y, 1, 0, 0, None, 0, None) == 1    # M > 7
