@@ -62,9 +62,10 @@ def log(*a):
 class Pool:
     """Rotation pool of identical packed copies of one seeded weight on the GPU."""
 
-    def __init__(self, wq, torch, cfg: int, fmt: str, K: int, N: int, M: int, min_copies: int = 2):
+    def __init__(self, wq, torch, cfg: int, fmt: str, K: int, N: int, M: int, min_copies: int = 2,
+                 act: str = "bf16"):
         import synth
-        self.fmt, self.K, self.N, self.M, self.cfg = fmt, K, N, M, cfg
+        self.fmt, self.K, self.N, self.M, self.cfg, self.act = fmt, K, N, M, cfg, act
         W = synth.weight(cfg, K, N, synth.uses_outliers(fmt))
         Wd = torch.from_numpy(W).to("cuda")
         base = wq.quantize(Wd, fmt)
@@ -72,17 +73,21 @@ class Pool:
         self.W = W
         n = max(min_copies, int(np.ceil(ROTATE_BYTES / base.nbytes())))
         self.copies = [base] + [base.clone() for _ in range(n - 1)]
-        xb = synth.activation(cfg, K, M)
+        xb = synth.activation_f16(cfg, K, M) if act == "f16" else synth.activation(cfg, K, M)
+        dt = torch.float16 if act == "f16" else torch.bfloat16
         self.x_bits = xb
-        self.x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16)
-        self.y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(dt)
+        self.y = torch.empty((M, N), dtype=dt, device="cuda")
         self.ws = wq.workspace(wq.wq_workspace_size(base, M))
         self.i = 0
 
     def call(self, wq):
         w = self.copies[self.i]
         self.i = (self.i + 1) % len(self.copies)
-        wq.wq_linear(w, self.x, self.y, ws=self.ws)
+        if self.act == "f16":
+            wq.wq_linear_act(w, self.x, self.y, ws=self.ws)
+        else:
+            wq.wq_linear(w, self.x, self.y, ws=self.ws)
 
     def bytes_per_call(self) -> int:
         return algorithmic_bytes(self.fmt, self.K, self.N, self.M)
@@ -109,7 +114,7 @@ class Pool:
             rows = (blocks[:, None] * 8 + np.arange(8)[None, :]).ravel()
         P = oracle.pack(self.fmt, self.W[rows])
         y = self.y.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
-        st = oracle.compare(y, oracle.ref_linear(self.x_bits, P))
+        st = oracle.compare(y, oracle.ref_linear(self.x_bits, P, act=self.act), act=self.act)
         st["channels_checked"] = int(len(rows))
         st["copies_bit_identical"] = bool(same)
         self.i = 0
@@ -176,7 +181,14 @@ def device_warmup(torch):
 
 
 def tune(wq, pool: Pool, warmup: int, iters: int):
-    chosen, lat = wq.wq_tune(pool.copies, pool.x, pool.y, pool.ws, warmup=warmup, iters=iters)
+    x, y = pool.x, pool.y
+    if pool.act == "f16":  # the tuner times bf16 calls; the fp16 layer takes its choice
+        import synth
+        import torch
+        xb = synth.activation(pool.cfg, pool.K, pool.M)
+        x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16)
+        y = torch.empty((pool.M, pool.N), dtype=torch.bfloat16, device="cuda")
+    chosen, lat = wq.wq_tune(pool.copies, x, y, pool.ws, warmup=warmup, iters=iters)
     return chosen, lat
 
 
@@ -914,8 +926,8 @@ def run_detail(wq, torch, args) -> dict:
     """Secondary workloads, each timed as graph replays over its rotation pool."""
     out = {}
 
-    def measure(cfg, fmt, K, N, M, tune_it=True, check=True):
-        p = Pool(wq, torch, cfg, fmt, K, N, M)
+    def measure(cfg, fmt, K, N, M, tune_it=True, check=True, act="bf16"):
+        p = Pool(wq, torch, cfg, fmt, K, N, M, act=act)
         rec = {}
         if tune_it:
             rec["tuned"], rec["tune_lat_us"] = tune(wq, p, 200, 200)
@@ -930,7 +942,8 @@ def run_detail(wq, torch, args) -> dict:
         rec.update({"us": round(per * 1e3, 3), "GB/s": round(gbs, 1),
                     "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1), "TFLOP/s": round(tf, 2),
                     "pct_mfma": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)})
-        log(f"cfg{cfg} {fmt} K={K} N={N} M={M}: {rec['us']} us {rec['GB/s']} GB/s {rec['TFLOP/s']} TF/s")
+        log(f"cfg{cfg} {fmt}{' f16 x' if act == 'f16' else ''} K={K} N={N} M={M}: {rec['us']} us {rec['GB/s']} GB/s "
+            f"{rec['TFLOP/s']} TF/s")
         p.free()
         del p
         torch.cuda.empty_cache()
@@ -948,6 +961,10 @@ def run_detail(wq, torch, args) -> dict:
         "small_groups": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(3 if fmt.startswith("w4") else 2, fmt, K, N, M)
                                  for fmt in ("w8g32", "w8g64", "w4g32", "w4g64")
                                  for K, N in [(5120, 27648)] for M in (1, 2048)},
+        # fp16 activations (tuned on bf16 x: the tuner times bf16 calls; the fp16 call takes its launch)
+        "f16_activations": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(2 if fmt == "w8pc" else 3, fmt, K, N, M,
+                                                                   act="f16")
+                                    for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648)] for M in (1, 2048)},
         "splitk_stress": lambda: {f"{fmt}_{K}x{N}": measure(4, fmt, K, N, 1)
                                   for K, N in [(27648, 5120), (5120, 151936)]
                                   for fmt in ("w8pc", "w8g128", "w4g128")},
