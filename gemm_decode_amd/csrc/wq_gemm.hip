@@ -1143,9 +1143,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
         fread_half(cur, P, s2, Ah, Bh);
         mma_half(Ah, Bh);
       }
-      if constexpr (GS == 32) fold();
+      if constexpr (GS == 32) {
+        if (KS > 0) fold();  // (always true: the branch keeps the fold in a block of its own)
+      }
     }
-    if constexpr (GS == 64) fold();
+    if constexpr (GS == 64) {
+      if (KS > 0) fold();
+    }
     if constexpr (GS == kGroup) {
       if (t & 1) fold();
     }
