@@ -207,7 +207,8 @@ int resolve_tile(const wq_weight* w, int64_t M) {
 }
 
 wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int split_k, int waves,
-                    int rows, void* ws, size_t ws_bytes, void* stream, int act = WQ_ACT_BF16) {
+                    int rows, void* ws, size_t ws_bytes, void* stream, int act = WQ_ACT_BF16,
+                    const void* res = nullptr) {
   if (act != WQ_ACT_BF16 && act != WQ_ACT_F16) return fail(WQ_ERR_INVALID_ARG, "unknown activation type");
   const bool xf = act == WQ_ACT_F16;
   wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
@@ -243,11 +244,11 @@ wq_status gemv_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int 
   if (rw == 0) rw = gemv_default_rows(w->K, w->N, w->fmt, (int)M);
   if (wv == 0) wv = gemv_default_waves(w->K, w->N, w->fmt, (int)M, split, rw);
   return launch_gemv(w, (const uint16_t*)x, (int)M, (uint16_t*)y, split, wv, rw, ws,
-                     (hipStream_t)stream, xf);
+                     (hipStream_t)stream, xf, (const uint16_t*)res);
 }
 
 wq_status gemm_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int tile, void* ws,
-                    size_t ws_bytes, void* stream, int act = WQ_ACT_BF16) {
+                    size_t ws_bytes, void* stream, int act = WQ_ACT_BF16, const void* res = nullptr) {
   if (act != WQ_ACT_BF16 && act != WQ_ACT_F16) return fail(WQ_ERR_INVALID_ARG, "unknown activation type");
   const bool xf = act == WQ_ACT_F16;
   wq_status st = check_weight(w0, WQ_LAYOUT_GFX950);
@@ -261,7 +262,8 @@ wq_status gemm_impl(const wq_weight* w0, const void* x, int64_t M, void* y, int 
   if (tile != 0 && gemm_workspace_bytes(w->fmt, w->N, M, t) > 0 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, w->N, M, t)))
     return fail(WQ_ERR_WORKSPACE, "wq_gemm: tile " + std::to_string(t) + " needs a workspace of " +
                                       std::to_string(gemm_workspace_bytes(w->fmt, w->N, M, t)) + " bytes");
-  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream, xf);
+  return launch_gemm(w, (const uint16_t*)x, M, (uint16_t*)y, t, ws, ws_bytes, (hipStream_t)stream, xf,
+                     (const uint16_t*)res);
 }
 
 }  // namespace
@@ -495,6 +497,40 @@ wq_status wq_gemv_act(const wq_weight* w, int act, const void* x, int64_t M, voi
 wq_status wq_gemm_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int tile, void* ws,
                       size_t ws_bytes, void* stream) {
   return gemm_impl(w, x, M, y, tile, ws, ws_bytes, stream, act);
+}
+
+wq_status wq_linear_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (M < 1) return fail(WQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (!r) return fail(WQ_ERR_INVALID_ARG, "wq_linear_residual: NULL residual");
+  if (!aligned(r, 2)) return fail(WQ_ERR_ALIGNMENT, "wq_linear_residual: the residual needs 2-byte alignment");
+  if (r != y && w && (const char*)r < (const char*)y + (size_t)M * w->N * 2 &&
+      (const char*)y < (const char*)r + (size_t)M * w->N * 2)
+    return fail(WQ_ERR_INVALID_ARG, "wq_linear_residual: the residual overlaps y without being y");
+  if (wq_dispatch_kind(M) == WQ_KIND_GEMV) return gemv_impl(w, x, M, y, 0, 0, 0, ws, ws_bytes, stream, act, r);
+  return gemm_impl(w, x, M, y, 0, ws, ws_bytes, stream, act, r);
+}
+
+wq_status wq_gemm_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y, int tile,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!r) return fail(WQ_ERR_INVALID_ARG, "wq_gemm_residual: NULL residual");
+  if (!aligned(r, 2)) return fail(WQ_ERR_ALIGNMENT, "wq_gemm_residual: the residual needs 2-byte alignment");
+  if (r != y && w && (const char*)r < (const char*)y + (size_t)M * w->N * 2 &&
+      (const char*)y < (const char*)r + (size_t)M * w->N * 2)
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemm_residual: the residual overlaps y without being y");
+  return gemm_impl(w, x, M, y, tile, ws, ws_bytes, stream, act, r);
+}
+
+wq_status wq_gemv_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y,
+                           int split_k, int waves, int rows, void* ws, size_t ws_bytes, void* stream) {
+  if (!r) return fail(WQ_ERR_INVALID_ARG, "wq_gemv_residual: NULL residual");
+  if (!aligned(r, 2)) return fail(WQ_ERR_ALIGNMENT, "wq_gemv_residual: the residual needs 2-byte alignment");
+  if (r != y && w && (const char*)r < (const char*)y + (size_t)M * w->N * 2 &&
+      (const char*)y < (const char*)r + (size_t)M * w->N * 2)
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv_residual: the residual overlaps y without being y");
+  if (split_k < 0 || (split_k == 0 && (waves != 0 || rows != 0)))
+    return fail(WQ_ERR_INVALID_ARG, "wq_gemv_residual: split_k 0 (tuned, with waves = rows = 0) or >= 1");
+  return gemv_impl(w, x, M, y, split_k, waves, rows, ws, ws_bytes, stream, act, r);
 }
 
 // ------------------------------------------------- the layer without allocation

@@ -53,6 +53,14 @@ __device__ __forceinline__ uint16_t f32_to_out(float v) {
   if constexpr (XF) return __builtin_bit_cast(uint16_t, (_Float16)v);
   else return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
+// the fp32 result plus element i of the residual (y's type, widened exactly) when there
+// is one, so that y is rounded once; the residual may be y itself (each element is read
+// by the thread that writes it, before the write)
+template <bool XF>
+__device__ __forceinline__ float with_res(float v, const uint16_t* res, size_t i) {
+  if (!res) return v;
+  return v + (XF ? f16_to_f32(res[i]) : bf16_to_f32(res[i]));
+}
 
 // gfx950 int8 codes are u = q + 128; flipping the sign bit gives q (as bf16, or fp16 with XF).
 template <bool XF = false>
@@ -93,7 +101,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
                                                      const uint16_t* __restrict__ scales,
                                                      const uint8_t* __restrict__ zeros,
                                                      const uint16_t* __restrict__ x,
-                                                     uint16_t* __restrict__ y, int M, int K, int N, int gshift) {
+                                                     uint16_t* y, int M, int K, int N, int gshift,
+                                                     const uint16_t* res) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDA];
 
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ q
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 64 + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
-        if (m < M) y[(size_t)m * N + n] = f32_to_out<XF>(s * acc[i][j][a]);
+        if (m < M) y[(size_t)m * N + n] = f32_to_out<XF>(with_res<XF>(s * acc[i][j][a], res, (size_t)m * N + n));
       }
   }
 }
@@ -269,7 +278,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const uint8_t* __restr
                                                            const uint16_t* __restrict__ scales,
                                                            const uint8_t* __restrict__ zeros,
                                                            const uint16_t* __restrict__ x,
-                                                           uint16_t* __restrict__ y, int M, int K, int N) {
+                                                           uint16_t* y, int M, int K, int N,
+                                                           const uint16_t* res) {
   using B_ = Big<FMT>;
   constexpr int JN = B_::JN, BN2 = B_::BN, STAGE2 = B_::STAGE;
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const uint8_t* __restr
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 128 + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+        if (m < M) y[(size_t)m * N + n] = f32_to_out<false>(with_res<false>(sc * acc[i][j][a], res, (size_t)m * N + n));
       }
   }
 }
@@ -507,10 +517,10 @@ template <int WM, int WN, int TM>
 __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
-                                                                         uint16_t* __restrict__ y,
+                                                                         uint16_t* y,
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
-                                                                         int tailS) {
+                                                                         int tailS, const uint16_t* res) {
   // TM: rows of x per workgroup tile (256, or 64 for a few tokens, where the tile
   // streams the same weights with a quarter of the x traffic and MFMA work)
   constexpr int NW = WM * WN, RB = TM / 32 / WM, CB = 8 / WN;
@@ -695,7 +705,7 @@ __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
-        if (S == 1) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[i][j][a]));
+        if (S == 1) y[(size_t)m * N + n] = f32_to_out<false>(with_res<false>(sc * acc[i][j][a], res, (size_t)m * N + n));
         else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = acc[i][j][a];
       }
   }
@@ -705,19 +715,20 @@ template <int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
-                                                                         uint16_t* __restrict__ y,
+                                                                         uint16_t* y,
                                                                          float* __restrict__ part, int M, int K,
-                                                                         int N, int tail0, int tailS) {
-  dma_w8pc_body<WM, WN, DBM>(qw, scales, x, y, part, M, K, N, tail0, tailS);
+                                                                         int N, int tail0, int tailS,
+                                                                         const uint16_t* res) {
+  dma_w8pc_body<WM, WN, DBM>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
 }
 
 // 64- and 128-row tiles (capping the registers for two workgroups per CU spills:
 // measured slower)
 template <int TM>
 __global__ __launch_bounds__(512, 1) void gemm_dma64_w8pc_kernel(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
-                            const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part,
-                            int M, int K, int N, int tail0, int tailS) {
-  dma_w8pc_body<1, 8, TM>(qw, scales, x, y, part, M, K, N, tail0, tailS);
+                            const uint16_t* __restrict__ x, uint16_t* y, float* __restrict__ part,
+                            int M, int K, int N, int tail0, int tailS, const uint16_t* res) {
+  dma_w8pc_body<1, 8, TM>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
 }
 
 // ---------------------------------------------------------------------------------
@@ -783,9 +794,9 @@ struct G128Dma {
 template <int FMT, int TM = DBM, int GS = kGroup>
 __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                                 const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x,
-                                uint16_t* __restrict__ y, float* __restrict__ part, int M, int K, int N,
+                                uint16_t* y, float* __restrict__ part, int M, int K, int N,
                                 int m0, int n0, int g0, int g1, int S, size_t poff, int ppitch, int pm0,
-                                int pn0, int wave, int NW) {
+                                int pn0, int wave, int NW, const uint16_t* res) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
   const int lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   const int G = K / GS;
@@ -827,7 +838,7 @@ __device__ void g128_tile_exact(const uint8_t* __restrict__ qw, const uint16_t* 
     for (int a = 0; a < 16; ++a) {
       const int mm = m0 + 32 * bi + 8 * (a >> 2) + 4 * lh + (a & 3);
       if (mm >= M) continue;
-      if (S == 1) y[(size_t)mm * N + nn] = __builtin_bit_cast(uint16_t, (__bf16)acc[a]);
+      if (S == 1) y[(size_t)mm * N + nn] = f32_to_out<false>(with_res<false>(acc[a], res, (size_t)mm * N + nn));
       else part[poff + (size_t)(mm - pm0) * ppitch + (nn - pn0)] = acc[a];
     }
   }
@@ -921,10 +932,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
                                                                          const uint16_t* __restrict__ x,
                                                                          const uint16_t* __restrict__ xd,
                                                                          const float* __restrict__ xinv,
-                                                                         uint16_t* __restrict__ y,
+                                                                         uint16_t* y,
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0,
-                                                                         int tailS) {
+                                                                         int tailS, const uint16_t* res) {
   using F = G128Dma<FMT, TM, GS>;
   constexpr bool kW4 = F::kW4;
   constexpr int NW = WM * WN, RB = TM / 32 / WM, CB = 8 / WN;
@@ -1185,7 +1196,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
     for (int w = 0; w < NW; ++w) any |= wave_flag[w];
     if (any) {
       g128_tile_exact<FMT, TM, GS>(qw, scales, zeros, x, y, part, M, K, N, m0, n0, kb / KUNIT, (kb + KS) / KUNIT,
-                                   S, wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW);
+                                   S, wk.poff, wk.ppitch, wk.pm0, wk.pn0, wave, NW, res);
       return;
     }
   }
@@ -1202,7 +1213,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_g128_kernel(const ui
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
         const float v = XH && !XF ? acc[i][j][a] * xinv[m] : acc[i][j][a];  // the row's scale back out (exact)
-        if (S == 1) y[(size_t)m * N + n] = f32_to_out<XF>(v);
+        if (S == 1) y[(size_t)m * N + n] = f32_to_out<XF>(with_res<XF>(v, res, (size_t)m * N + n));
         else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = v;
       }
   }
@@ -1239,8 +1250,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
                                                            const uint16_t* __restrict__ scales,
                                                            const uint8_t* __restrict__ zeros,
                                                            const uint16_t* __restrict__ x,
-                                                           uint16_t* __restrict__ y, float* __restrict__ part,
-                                                           int M, int K, int N, int S) {
+                                                           uint16_t* y, float* __restrict__ part,
+                                                           int M, int K, int N, int S, const uint16_t* res) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
   constexpr int RT = 2;                  // 16-row tiles per wave
   constexpr int CH = kW4 ? 1 : 2;        // 16-byte code chunks per lane, tile and step
@@ -1427,7 +1438,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
         const int m = 16 * b + 4 * c4 + q;
         if (m >= M) continue;
         if (S == 1)
-          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
+          y[(size_t)m * N + n] = f32_to_out<false>(with_res<false>(sc * acc[t][b][q], res, (size_t)m * N + n));
         else
           part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
       }
@@ -1445,9 +1456,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
                                                                   const uint16_t* __restrict__ scales,
                                                                   const uint8_t* __restrict__ zeros,
                                                                   const uint16_t* __restrict__ x,
-                                                                  uint16_t* __restrict__ y,
+                                                                  uint16_t* y,
                                                                   float* __restrict__ part, int M, int K,
-                                                                  int N, int S) {
+                                                                  int N, int S, const uint16_t* res) {
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
   constexpr int RT = 2;              // 16-row tiles per wave
   constexpr int CH = kW4 ? 1 : 2;    // 16-byte code chunks per lane, tile and step
@@ -1628,7 +1639,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
         const int m = 16 * b + 4 * c4 + q;
         if (m >= M) continue;
         if (S == 1)
-          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(sc * acc[t][b][q]));
+          y[(size_t)m * N + n] = f32_to_out<false>(with_res<false>(sc * acc[t][b][q], res, (size_t)m * N + n));
         else
           part[((size_t)blockIdx.y * M + m) * N + n] = acc[t][b][q];
       }
@@ -1640,15 +1651,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_direct_kernel(const uint8_t* 
 template <bool kPerChannel, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ part,
                                                                   const uint16_t* __restrict__ scales,
-                                                                  uint16_t* __restrict__ y, int M, int N,
-                                                                  int S) {
+                                                                  uint16_t* y, int M, int N,
+                                                                  int S, const uint16_t* res) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t MN = (int64_t)M * N;
   if (i >= MN) return;
   float v = 0.f;
   for (int s = 0; s < S; ++s) v += part[(int64_t)s * MN + i];
   const float sc = kPerChannel ? bf16_to_f32(scales[i % N]) : 1.f;
-  y[i] = f32_to_out<XF>(sc * v);
+  y[i] = f32_to_out<XF>(with_res<XF>(sc * v, res, (size_t)i));
 }
 
 // The split tail tiles of tile 13: y = the ranges' fp32 partials added in range order
@@ -1658,8 +1669,8 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
 template <bool kPerChannel, int TM, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __restrict__ part,
                                                                 const uint16_t* __restrict__ scales,
-                                                                uint16_t* __restrict__ y, int M, int N,
-                                                                int tail0, int S) {
+                                                                uint16_t* y, int M, int N,
+                                                                int tail0, int S, const uint16_t* res) {
   const int mblocks = (M + TM - 1) / TM, lin = tail0 + (int)blockIdx.y;
   const int r = (int)blockIdx.x * 8 + (int)(threadIdx.x >> 5), c = 8 * (int)(threadIdx.x & 31);
   const int m = (lin % mblocks) * TM + r, n = (lin / mblocks) * DBN + c;
@@ -1676,7 +1687,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __re
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float sc = kPerChannel ? bf16_to_f32(scales[min(n + j, N - 1)]) : 1.f;
-    o[j] = f32_to_out<XF>(sc * v[j]);
+    o[j] = f32_to_out<XF>(with_res<XF>(sc * v[j], res, (size_t)m * N + min(n + j, N - 1)));
   }
   uint16_t* yo = y + (size_t)m * N + n;
   if (N % 8 == 0) {  // n + 8 <= N and 16-byte aligned
@@ -1689,24 +1700,24 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float* __re
 
 template <int FMT>
 wq_status launch_skinny(const uint8_t* qw, const uint16_t* sc, const uint8_t* zs, const uint16_t* x,
-                        uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st) {
+                        uint16_t* y, float* part, int M, int K, int N, int S, hipStream_t st, const uint16_t* res) {
   const dim3 grid((unsigned)((N + SK_ROWS - 1) / SK_ROWS), (unsigned)S);
   const int TB = (M + 15) / 16;
   // one token block: the direct kernel; two: x through LDS as well (measured at M = 32:
   // 39 us against 57 us for per-channel W8 at (5120, 27648), 53 against 74 for W4)
   if (TB <= 1)
-    gemm_skinny_direct_kernel<FMT, 1><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+    gemm_skinny_direct_kernel<FMT, 1><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S, res);
   else if (TB <= 2)
-    gemm_skinny_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+    gemm_skinny_kernel<FMT, 2><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S, res);
   else if (TB <= 4)
-    gemm_skinny_kernel<FMT, 4><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+    gemm_skinny_kernel<FMT, 4><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S, res);
   else
-    gemm_skinny_kernel<FMT, 8><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S);
+    gemm_skinny_kernel<FMT, 8><<<grid, 256, 0, st>>>(qw, sc, zs, x, y, part, M, K, N, S, res);
   WQ_HIP_CHECK(hipGetLastError());
   if (S > 1) {
     const int64_t MN = (int64_t)M * N;
     gemm_splitk_reduce_kernel<FMT == WQ_FMT_W8_PC>
-        <<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, S);
+        <<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, S, res);
     WQ_HIP_CHECK(hipGetLastError());
   }
   return WQ_OK;
@@ -1817,54 +1828,54 @@ static hipError_t x_to_f16_rows(const uint16_t* x, int64_t M, int K, void* ws, s
 template <int F, int TMV, int GS>
 static void g_dma_launch(dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
                          const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y, float* part, int M,
-                         int K, int N, int tail0, int tailS, bool xf) {
+                         int K, int N, int tail0, int tailS, bool xf, const uint16_t* res) {
   if (xf)  // fp16 activations: x is the fp16 operand
     gemm_dma_g128_kernel<F, 1, 8, true, TMV, GS, true>
-        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS);
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS, res);
   else if (xh)
     gemm_dma_g128_kernel<F, 1, 8, true, TMV, GS>
-        <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS);
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, res);
   else
     gemm_dma_g128_kernel<F, 1, 8, false, TMV, GS>
-        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS);
+        <<<grid, 512, 0, s>>>(qw, sc, zs, x, x, nullptr, y, part, M, K, N, tail0, tailS, res);
 }
 template <int F, int TMV>
 static void g_dma_launch_gs(int gs, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
                             const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
-                            float* part, int M, int K, int N, int tail0, int tailS, bool xf) {
-  if (gs == 32) g_dma_launch<F, TMV, 32>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
-  else if (gs == 64) g_dma_launch<F, TMV, 64>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
-  else g_dma_launch<F, TMV, kGroup>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+                            float* part, int M, int K, int N, int tail0, int tailS, bool xf, const uint16_t* res) {
+  if (gs == 32) g_dma_launch<F, TMV, 32>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
+  else if (gs == 64) g_dma_launch<F, TMV, 64>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
+  else g_dma_launch<F, TMV, kGroup>(grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
 }
 static void g_dma_dispatch(int fmt, int tm, dim3 grid, hipStream_t s, const uint8_t* qw, const uint16_t* sc,
                            const uint8_t* zs, const uint16_t* x, const uint16_t* xh, const float* xinv, uint16_t* y,
-                           float* part, int M, int K, int N, int tail0, int tailS, bool xf) {
+                           float* part, int M, int K, int N, int tail0, int tailS, bool xf, const uint16_t* res) {
   const int gs = meta_group(fmt);
   if (family(fmt) == WQ_FMT_W4_G128) {
     if (tm == 64)
-      g_dma_launch_gs<WQ_FMT_W4_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+      g_dma_launch_gs<WQ_FMT_W4_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
     else
-      g_dma_launch_gs<WQ_FMT_W4_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+      g_dma_launch_gs<WQ_FMT_W4_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
   } else {
     if (tm == 64)
-      g_dma_launch_gs<WQ_FMT_W8_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+      g_dma_launch_gs<WQ_FMT_W8_G128, 64>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
     else
-      g_dma_launch_gs<WQ_FMT_W8_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf);
+      g_dma_launch_gs<WQ_FMT_W8_G128, 128>(gs, grid, s, qw, sc, zs, x, xh, xinv, y, part, M, K, N, tail0, tailS, xf, res);
   }
 }
 // the split-K reduction of the GEMM tiles, with the output type of the call
 static void splitk_reduce(bool pc, bool xf, const float* part, const uint16_t* sc, uint16_t* y, int64_t M, int N,
-                          int S, hipStream_t s) {
+                          int S, hipStream_t s, const uint16_t* res) {
   const int64_t MN = M * N;
   const unsigned blocks = (unsigned)((MN + 255) / 256);
-  if (pc && xf) gemm_splitk_reduce_kernel<true, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
-  else if (pc) gemm_splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
-  else if (xf) gemm_splitk_reduce_kernel<false, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
-  else gemm_splitk_reduce_kernel<false><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S);
+  if (pc && xf) gemm_splitk_reduce_kernel<true, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+  else if (pc) gemm_splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+  else if (xf) gemm_splitk_reduce_kernel<false, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+  else gemm_splitk_reduce_kernel<false><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
 }
 
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
-                      void* ws, size_t ws_bytes, hipStream_t s, bool xf) {
+                      void* ws, size_t ws_bytes, hipStream_t s, bool xf, const uint16_t* res) {
   const int K = (int)w->K, N = (int)w->N;
   if (M > 65535LL * BM) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: M too large");
   const uint8_t* qw = (const uint8_t*)w->qweight;
@@ -1880,7 +1891,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;  // no room for partials
       const int nb = tile == kMmaTile0 + 1 ? 2 : tile == kMmaTile0 + 2 ? 4 : 1;
       const int rows = (16 * nb) | kGemvMfma;
-      return launch_gemv(w, x, (int)M, y, S, gemv_default_waves(K, N, w->fmt, (int)M, S, rows), rows, ws, s);
+      return launch_gemv(w, x, (int)M, y, S, gemv_default_waves(K, N, w->fmt, (int)M, S, rows), rows, ws, s, false, res);
     }
     tile = K % DBK == 0 ? kDma64Tile0 : 2;  // more tokens than one A operand holds
   }
@@ -1890,9 +1901,9 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
       if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;  // no room for partials
       float* part = (float*)ws;
       switch (w->fmt) {
-        case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
-        case WQ_FMT_W8_G128: return launch_skinny<WQ_FMT_W8_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
-        case WQ_FMT_W4_G128: return launch_skinny<WQ_FMT_W4_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s);
+        case WQ_FMT_W8_PC: return launch_skinny<WQ_FMT_W8_PC>(qw, sc, zs, x, y, part, (int)M, K, N, S, s, res);
+        case WQ_FMT_W8_G128: return launch_skinny<WQ_FMT_W8_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s, res);
+        case WQ_FMT_W4_G128: return launch_skinny<WQ_FMT_W4_G128>(qw, sc, zs, x, y, part, (int)M, K, N, S, s, res);
         default: return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");
       }
     }
@@ -1914,20 +1925,20 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     float* part = (float*)ws;
     if (pc) {
       if (tm == 64)
-        gemm_dma64_w8pc_kernel<64><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
+        gemm_dma64_w8pc_kernel<64><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
       else
-        gemm_dma64_w8pc_kernel<128><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1);
+        gemm_dma64_w8pc_kernel<128><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
     } else {
       uint16_t* xh = nullptr;
       float* xinv = nullptr;
       if (!xf)
         WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, S > 1 ? (size_t)S * M * N * sizeof(float) : 0, &xh,
                                    &xinv, s));
-      g_dma_dispatch(w->fmt, tm, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, (int)total, 1, xf);
+      g_dma_dispatch(w->fmt, tm, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, (int)total, 1, xf, res);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
-      splitk_reduce(pc, xf, part, sc, y, M, N, S, s);
+      splitk_reduce(pc, xf, part, sc, y, M, N, S, s, res);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;
@@ -1960,31 +1971,31 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
                                         : (S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
     if (pc) {
       if (tile == 3)
-        gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
+        gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
       else if (tile == 4)
-        gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
+        gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
       else
-        gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS);
+        gemm_dma_w8pc_kernel<2, 4><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
     } else {
       // x in fp16 (rows scaled) after the partials when the workspace has room for it
       uint16_t* xh = nullptr;
       float* xinv = nullptr;
       if (!xf) WQ_HIP_CHECK(x_to_f16_rows(x, M, K, ws, ws_bytes, part_bytes, &xh, &xinv, s));
-      g_dma_dispatch(w->fmt, 128, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS, xf);
+      g_dma_dispatch(w->fmt, 128, grid, s, qw, sc, zs, x, xh, xinv, y, part, (int)M, K, N, tail0, tailS, xf, res);
     }
     WQ_HIP_CHECK(hipGetLastError());
     if (S > 1) {
-      splitk_reduce(pc, xf, part, sc, y, M, N, S, s);
+      splitk_reduce(pc, xf, part, sc, y, M, N, S, s, res);
       WQ_HIP_CHECK(hipGetLastError());
     }
     if (tailS > 1) {
       const dim3 rg((unsigned)(btm / 8), (unsigned)ntail);
       if (pc)
-        gemm_tail_reduce_kernel<true, 256><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<true, 256><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);
       else if (xf)
-        gemm_tail_reduce_kernel<false, 128, true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<false, 128, true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);
       else
-        gemm_tail_reduce_kernel<false, 128><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS);
+        gemm_tail_reduce_kernel<false, 128><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);
       WQ_HIP_CHECK(hipGetLastError());
     }
     return WQ_OK;
@@ -1996,13 +2007,13 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     const unsigned blocks = (unsigned)(8 * ((total + 7) / 8));
     switch (w->fmt) {
       case WQ_FMT_W8_PC:
-        gemm_big_kernel<WQ_FMT_W8_PC><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        gemm_big_kernel<WQ_FMT_W8_PC><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, res);
         break;
       case WQ_FMT_W8_G128:
-        gemm_big_kernel<WQ_FMT_W8_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        gemm_big_kernel<WQ_FMT_W8_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, res);
         break;
       case WQ_FMT_W4_G128:
-        gemm_big_kernel<WQ_FMT_W4_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N);
+        gemm_big_kernel<WQ_FMT_W4_G128><<<blocks, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, res);
         break;
       default:
         return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");
@@ -2014,16 +2025,16 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const int gshift = meta_group(w->fmt) == 32 ? 5 : meta_group(w->fmt) == 64 ? 6 : 7;
   switch (family(w->fmt)) {
     case WQ_FMT_W8_PC:
-      if (xf) gemm_kernel<WQ_FMT_W8_PC, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
-      else gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W8_PC, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
+      else gemm_kernel<WQ_FMT_W8_PC><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
       break;
     case WQ_FMT_W8_G128:
-      if (xf) gemm_kernel<WQ_FMT_W8_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
-      else gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W8_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
+      else gemm_kernel<WQ_FMT_W8_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
       break;
     case WQ_FMT_W4_G128:
-      if (xf) gemm_kernel<WQ_FMT_W4_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
-      else gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift);
+      if (xf) gemm_kernel<WQ_FMT_W4_G128, true><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
+      else gemm_kernel<WQ_FMT_W4_G128><<<grid, 256, 0, s>>>(qw, sc, zs, x, y, (int)M, K, N, gshift, res);
       break;
     default:
       return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: unknown format");

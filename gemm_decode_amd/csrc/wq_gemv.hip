@@ -78,6 +78,14 @@ template <bool XF>
 __device__ __forceinline__ uint16_t f32_to_out(float v) {
   return XF ? f32_to_f16(v) : f32_to_bf16(v);
 }
+// the fp32 result plus element i of the residual (the output type, widened exactly) when
+// there is one: the output is then rounded once.  The residual may be y itself: every
+// element is read by the thread that writes it, before it writes it.
+template <bool XF>
+__device__ __forceinline__ float with_res(float v, const uint16_t* res, size_t i) {
+  if (!res) return v;
+  return v + (XF ? f16_to_f32(res[i]) : bf16_to_f32(res[i]));
+}
 // bf16 pair -> fp16 pair (exact in the range described above)
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
   auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
@@ -184,8 +192,8 @@ constexpr int max_waves_r(int fmt, int RR, int M, bool PF) {
 template <int FMT, int M, int RR, bool PF, bool XF = false>
 __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    float* __restrict__ part, int K, int N, int gshift) {
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, uint16_t* y,
+    float* __restrict__ part, int K, int N, int gshift, const uint16_t* res) {
   using F = Fmt<FMT>;
   constexpr int kSlice = 64 * F::kChunk;
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128;
@@ -513,7 +521,8 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
     if (S == 1) {
       const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
 #pragma unroll
-      for (int m = 0; m < M; ++m) y[(size_t)m * N + n] = f32_to_out<XF>(sc * v[m]);
+      for (int m = 0; m < M; ++m)
+        y[(size_t)m * N + n] = f32_to_out<XF>(with_res<XF>(sc * v[m], res, (size_t)m * N + n));
     } else {
 #pragma unroll
       for (int m = 0; m < M; ++m) part[((size_t)s * M + m) * N + n] = v[m];
@@ -525,8 +534,8 @@ __global__ __launch_bounds__(64 * max_waves_r(FMT, RR, M, PF)) void gemv_kernel(
 template <int FMT, bool XF = false>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ scales,
-                                                              uint16_t* __restrict__ y, int M,
-                                                              int N, int S) {
+                                                              uint16_t* y, int M,
+                                                              int N, int S, const uint16_t* res) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t MN = (int64_t)M * N;
   if (i >= MN) return;
@@ -534,7 +543,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int s = 0; s < S; ++s) v += part[(int64_t)s * MN + i];
   const int n = (int)(i % N);
   const float sc = (FMT == WQ_FMT_W8_PC) ? bf16_to_f32(scales[n]) : 1.f;
-  y[i] = f32_to_out<XF>(sc * v);
+  y[i] = f32_to_out<XF>(with_res<XF>(sc * v, res, (size_t)i));
 }
 
 // ---------------------------------------------------------------------------------
@@ -599,7 +608,8 @@ inline int lx_bytes(int M, int units) { return M * units * 256 + ((units + 15) &
 template <int FMT, int M, int NB, bool LX>
 __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, float* __restrict__ part, int K, int N, int Mt) {
+    const uint16_t* __restrict__ x, uint16_t* y, float* __restrict__ part, int K, int N, int Mt,
+    const uint16_t* res) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lx_mem[];
   constexpr bool kW4 = FMT == WQ_FMT_W4_G128, kGrouped = FMT != WQ_FMT_W8_PC;
   constexpr int MI = M < 4 ? M : 4;             // accumulator rows a lane keeps (token 4 (l / 16) + i, i < MI)
@@ -944,59 +954,61 @@ __global__ __launch_bounds__(64 * kMmaMaxWaves) void gemv_mma_kernel(
     if (tile0 + t >= T16 || n >= N) continue;
     float v = 0.f;
     for (int w = 0; w < W; ++w) v += red[w][t][m][o & 15];
-    if (S == 1) y[(size_t)m * N + n] = f32_to_bf16(kGrouped ? v : bf16_to_f32(scales[n]) * v);
+    if (S == 1)
+      y[(size_t)m * N + n] = f32_to_bf16(with_res<false>(kGrouped ? v : bf16_to_f32(scales[n]) * v, res,
+                                                         (size_t)m * N + n));
     else part[((size_t)s * Mr + m) * N + n] = v;
   }
 }
 
 template <int FMT, int M, int NB>
 void launch_mma_nb(dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-                   const uint16_t* x, uint16_t* y, float* part, int K, int N, int Mt, hipStream_t st) {
+                   const uint16_t* x, uint16_t* y, const uint16_t* res, float* part, int K, int N, int Mt, hipStream_t st) {
   // x in LDS when the largest split range's fp16 x fits (ranges differ by one unit at most)
   const int U = (K + kGroup - 1) / kGroup, S = (int)grid.y;
   const int lx = lx_bytes(Mt, (U + S - 1) / S);
   if (lx <= kLxMaxBytes)
-    gemv_mma_kernel<FMT, M, NB, true><<<grid, block, lx, st>>>(qw, sc, zs, x, y, part, K, N, Mt);
+    gemv_mma_kernel<FMT, M, NB, true><<<grid, block, lx, st>>>(qw, sc, zs, x, y, part, K, N, Mt, res);
   else
-    gemv_mma_kernel<FMT, M, NB, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, Mt);
+    gemv_mma_kernel<FMT, M, NB, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, Mt, res);
 }
 
 template <int FMT, int M>
 void launch_mma(int nb, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-                const uint16_t* x, uint16_t* y, float* part, int K, int N, int Mt, hipStream_t st) {
+                const uint16_t* x, uint16_t* y, const uint16_t* res, float* part, int K, int N, int Mt, hipStream_t st) {
   switch (nb) {
-    case 1: launch_mma_nb<FMT, M, 1>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
-    case 2: launch_mma_nb<FMT, M, 2>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
-    default: launch_mma_nb<FMT, M, 4>(grid, block, qw, sc, zs, x, y, part, K, N, Mt, st); break;
+    case 1: launch_mma_nb<FMT, M, 1>(grid, block, qw, sc, zs, x, y, res, part, K, N, Mt, st); break;
+    case 2: launch_mma_nb<FMT, M, 2>(grid, block, qw, sc, zs, x, y, res, part, K, N, Mt, st); break;
+    default: launch_mma_nb<FMT, M, 4>(grid, block, qw, sc, zs, x, y, res, part, K, N, Mt, st); break;
   }
 }
 
 template <int FMT, int M, int RR>
 void launch_rr(bool pf, bool xf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc, const uint8_t* zs,
-               const uint16_t* x, uint16_t* y, float* part, int K, int N, int gshift, hipStream_t st) {
+               const uint16_t* x, uint16_t* y, const uint16_t* res, float* part, int K, int N, int gshift, hipStream_t st) {
   if (xf) {  // fp16 activations: no prefetch variant (the launcher checks)
-    gemv_kernel<FMT, M, RR, false, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
+    gemv_kernel<FMT, M, RR, false, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift, res);
     return;
   }
   if constexpr (prefetch_allowed(FMT, RR, M)) {
     if (pf) {
-      gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
+      gemv_kernel<FMT, M, RR, true><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift, res);
       return;
     }
   }
-  gemv_kernel<FMT, M, RR, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift);
+  gemv_kernel<FMT, M, RR, false><<<grid, block, 0, st>>>(qw, sc, zs, x, y, part, K, N, gshift, res);
 }
 
 // rows: 4, 8 or 16, optionally | kGemvPrefetch (checked by the caller)
 template <int FMT, int M>
 wq_status launch_m(int rows, bool xf, dim3 grid, dim3 block, const uint8_t* qw, const uint16_t* sc,
-                   const uint8_t* zs, const uint16_t* x, uint16_t* y, float* part, int K, int N,
+                   const uint8_t* zs, const uint16_t* x, uint16_t* y, const uint16_t* res, float* part, int K, int N,
                    int gshift, hipStream_t st) {
   const bool pf = (rows & kGemvPrefetch) != 0;
   switch (rows & ~kGemvPrefetch) {
-    case 4: launch_rr<FMT, M, 4>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 8: launch_rr<FMT, M, 8>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 16: launch_rr<FMT, M, 16>(pf, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 4: launch_rr<FMT, M, 4>(pf, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 8: launch_rr<FMT, M, 8>(pf, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 16: launch_rr<FMT, M, 16>(pf, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   }
   return WQ_OK;
@@ -1004,7 +1016,7 @@ wq_status launch_m(int rows, bool xf, dim3 grid, dim3 block, const uint8_t* qw, 
 
 template <int FMT>
 wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                     int waves, int rows, void* ws, bool xf, hipStream_t st) {
+                     int waves, int rows, void* ws, bool xf, const uint16_t* res, hipStream_t st) {
   const int K = (int)w->K, N = (int)w->N;
   if (xf && (rows & (kGemvMfma | kGemvPrefetch)))
     return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: fp16 activations take the dot2 GEMV without prefetch");
@@ -1019,29 +1031,29 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
     dim3 grid((unsigned)((row_tiles(N) + nb - 1) / nb), split_k);
     dim3 block(64 * waves);
     switch (M) {
-      case 1: launch_mma<FMT, 1>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 1, st); break;
-      case 2: launch_mma<FMT, 2>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 2, st); break;
-      case 3: launch_mma<FMT, 3>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 3, st); break;
-      case 4: launch_mma<FMT, 4>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 4, st); break;
-      case 5: launch_mma<FMT, 5>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 5, st); break;
-      case 6: launch_mma<FMT, 6>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 6, st); break;
-      case 7: launch_mma<FMT, 7>(nb, grid, block, qw, sc, zs, x, y, part, K, N, 7, st); break;
+      case 1: launch_mma<FMT, 1>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 1, st); break;
+      case 2: launch_mma<FMT, 2>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 2, st); break;
+      case 3: launch_mma<FMT, 3>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 3, st); break;
+      case 4: launch_mma<FMT, 4>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 4, st); break;
+      case 5: launch_mma<FMT, 5>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 5, st); break;
+      case 6: launch_mma<FMT, 6>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 6, st); break;
+      case 7: launch_mma<FMT, 7>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, 7, st); break;
       default:
         if (M > kMmaTokens) return fail(WQ_ERR_INVALID_ARG, "matrix-core GEMV: M must be in 1..16");
-        launch_mma<FMT, kMmaTokens>(nb, grid, block, qw, sc, zs, x, y, part, K, N, M, st);
+        launch_mma<FMT, kMmaTokens>(nb, grid, block, qw, sc, zs, x, y, res, part, K, N, M, st);
         break;
     }
   } else {
   dim3 grid((unsigned)(row_tiles(N) * (R / (rows & ~kGemvPrefetch))), split_k);
   dim3 block(64 * waves);
   switch (M) {
-    case 1: r = launch_m<FMT, 1>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 2: r = launch_m<FMT, 2>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 3: r = launch_m<FMT, 3>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 4: r = launch_m<FMT, 4>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 5: r = launch_m<FMT, 5>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 6: r = launch_m<FMT, 6>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
-    case 7: r = launch_m<FMT, 7>(rows, xf, grid, block, qw, sc, zs, x, y, part, K, N, gshift, st); break;
+    case 1: r = launch_m<FMT, 1>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 2: r = launch_m<FMT, 2>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 3: r = launch_m<FMT, 3>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 4: r = launch_m<FMT, 4>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 5: r = launch_m<FMT, 5>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 6: r = launch_m<FMT, 6>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
+    case 7: r = launch_m<FMT, 7>(rows, xf, grid, block, qw, sc, zs, x, y, res, part, K, N, gshift, st); break;
     default: return fail(WQ_ERR_INVALID_ARG, "wq_gemv: M must be in 1..7");
   }
   }
@@ -1049,8 +1061,8 @@ wq_status launch_fmt(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, 
   WQ_HIP_CHECK(hipGetLastError());
   if (split_k > 1) {
     const int64_t MN = (int64_t)M * N;
-    if (xf) splitk_reduce_kernel<FMT, true><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k);
-    else splitk_reduce_kernel<FMT><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k);
+    if (xf) splitk_reduce_kernel<FMT, true><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k, res);
+    else splitk_reduce_kernel<FMT><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, sc, y, M, N, split_k, res);
     WQ_HIP_CHECK(hipGetLastError());
   }
   return WQ_OK;
@@ -1108,7 +1120,7 @@ int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int ro
 }
 
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                      int waves, int rows, void* ws, hipStream_t s, bool xf) {
+                      int waves, int rows, void* ws, hipStream_t s, bool xf, const uint16_t* res) {
   const int cap = gemv_max_waves(w->fmt, M, rows);
   if (cap == 0) return fail(WQ_ERR_INVALID_ARG, "wq_gemv: rows per wave must be 4, 8 or 16");
   if (waves < 1 || waves > cap)
@@ -1116,9 +1128,9 @@ wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y,
                                         std::to_string(cap) + " waves");
   if (w->fmt == WQ_FMT_W4_PC) return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: per-channel W4 runs through its compute view");
   switch (family(w->fmt)) {
-    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, xf, s);
-    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, xf, s);
-    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, xf, s);
+    case WQ_FMT_W8_PC: return launch_fmt<WQ_FMT_W8_PC>(w, x, M, y, split_k, waves, rows, ws, xf, res, s);
+    case WQ_FMT_W8_G128: return launch_fmt<WQ_FMT_W8_G128>(w, x, M, y, split_k, waves, rows, ws, xf, res, s);
+    case WQ_FMT_W4_G128: return launch_fmt<WQ_FMT_W4_G128>(w, x, M, y, split_k, waves, rows, ws, xf, res, s);
   }
   return fail(WQ_ERR_UNSUPPORTED, "wq_gemv: unknown format");
 }

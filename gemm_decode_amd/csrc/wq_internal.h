@@ -104,8 +104,11 @@ wq_status launch_perm_gather(const uint16_t* x, const int32_t* perm, uint16_t* x
                              hipStream_t s);
 wq_status launch_repack(const wq_weight* src, const wq_weight* dst, bool to_gfx950, hipStream_t s);
 // xf: fp16 activations (x and y in fp16; the dot2 launch options without prefetch)
+// res: NULL, or a residual of y's type and shape added to the fp32 result before the one
+// rounding of y (it may be y itself)
 wq_status launch_gemv(const wq_weight* w, const uint16_t* x, int M, uint16_t* y, int split_k,
-                      int waves, int rows, void* ws, hipStream_t s, bool xf = false);
+                      int waves, int rows, void* ws, hipStream_t s, bool xf = false,
+                      const uint16_t* res = nullptr);
 // Rows per GEMV wave (4, 8 or 16) and waves per workgroup when none is tuned or given.
 int gemv_default_rows(int64_t K, int64_t N, int fmt, int M);
 int gemv_default_waves(int64_t K, int64_t N, int fmt, int M, int split_k, int rows);
@@ -186,7 +189,7 @@ size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int t
 // xf: fp16 activations (x and y in fp16): tile 2's kernel, and for the grouped formats the
 // LDS-DMA tiles, which read the fp16 x as their operand (act_tile gives what runs)
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
-                      void* ws, size_t ws_bytes, hipStream_t s, bool xf = false);
+                      void* ws, size_t ws_bytes, hipStream_t s, bool xf = false, const uint16_t* res = nullptr);
 // the GEMM tile that runs for fp16 activations: per-channel W8 takes tile 2's kernel for
 // every tile; the grouped formats map as small_group_tile does
 inline int act_tile(int fmt, int tile) { return fmt == WQ_FMT_W8_PC ? 2 : small_group_tile(tile); }

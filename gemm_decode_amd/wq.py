@@ -23,7 +23,8 @@ __all__ = [
     "wq_lm_head_topk_workspace_size", "wq_lm_head_topk",
     "wq_linear_perm_workspace_size", "wq_linear_perm", "wq_linear_static", "STATIC_SCRATCH_BYTES",
     "wq_moe_linear", "quantize_experts", "EPILOGUE_NONE", "EPILOGUE_SILU_MUL",
-    "ACT", "wq_linear_act", "wq_gemv_act", "wq_gemm_act",
+    "ACT", "wq_linear_act", "wq_gemv_act", "wq_gemm_act", "wq_linear_residual", "wq_gemv_residual",
+    "wq_gemm_residual",
     "wq_tune_pick", "wq_tune", "wq_tune_cache_set", "wq_tune_cache_get", "wq_tune_cache_clear",
     "wq_tune_cache_save", "wq_tune_cache_load", "quantize", "workspace",
 ]
@@ -86,6 +87,12 @@ _SIGS = {
                               C.c_size_t, C.c_void_p]),
     "wq_gemm_act": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t,
                               C.c_void_p]),
+    "wq_linear_residual": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_size_t, C.c_void_p]),
+    "wq_gemv_residual": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                   C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wq_gemm_residual": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
+                                   C.c_size_t, C.c_void_p]),
     "wq_moe_linear": (C.c_int, [_W, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]),
     "wq_lm_head_topk_workspace_size": (C.c_int, [_W, C.c_int64, C.c_int, _P(C.c_size_t)]),
     "wq_linear_perm_workspace_size": (C.c_int, [_W, C.c_int64, _P(C.c_size_t)]),
@@ -324,6 +331,33 @@ def wq_gemm_act(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, tile: int = 0
     M, d = _xy(x, y, w, x.dtype), w.desc()
     _check(lib.wq_gemm_act(C.byref(d), _act(x), _ptr(x), M, _ptr(y), tile, _ptr(ws),
                            0 if ws is None else ws.numel(), _stream(stream)), "wq_gemm_act")
+
+
+def _res(r: torch.Tensor, y: torch.Tensor):
+    assert r.dtype == y.dtype and r.is_contiguous() and r.numel() == y.numel(), "residual must match y"
+    return _ptr(r)
+
+
+def wq_linear_residual(w: PackedWeight, x: torch.Tensor, r: torch.Tensor, y: torch.Tensor,
+                       ws: torch.Tensor | None = None, stream=None) -> None:
+    """y = x . dequant(W)^T + r, rounded once (r may be y itself); bf16 or fp16 as x."""
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_linear_residual(C.byref(d), _act(x), _ptr(x), M, _res(r, y), _ptr(y), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)), "wq_linear_residual")
+
+
+def wq_gemv_residual(w: PackedWeight, x: torch.Tensor, r: torch.Tensor, y: torch.Tensor, split_k: int = 0,
+                     waves: int = 0, rows: int = 0, ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_gemv_residual(C.byref(d), _act(x), _ptr(x), M, _res(r, y), _ptr(y), split_k, waves, rows,
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "wq_gemv_residual")
+
+
+def wq_gemm_residual(w: PackedWeight, x: torch.Tensor, r: torch.Tensor, y: torch.Tensor, tile: int = 0,
+                     ws: torch.Tensor | None = None, stream=None) -> None:
+    M, d = _xy(x, y, w, x.dtype), w.desc()
+    _check(lib.wq_gemm_residual(C.byref(d), _act(x), _ptr(x), M, _res(r, y), _ptr(y), tile, _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)), "wq_gemm_residual")
 
 
 def wq_linear_static(w: PackedWeight, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:

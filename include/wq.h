@@ -341,6 +341,26 @@ wq_status wq_gemv_act(const wq_weight* w, int act, const void* x, int64_t M, voi
 wq_status wq_gemm_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, int tile, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- the residual epilogue */
+
+/* The layer with a residual added in its epilogue: y = round(x . dequant(W)^T + r), the
+ * residual r [M][N] (device, y's type: bf16, or fp16 with WQ_ACT_F16; 2-byte aligned)
+ * widened exactly and added to the fp32 result before the one rounding of y (the fused
+ * residual of the tileInfer README's "Key Optimizations": the layer's output joins the
+ * residual stream without a separate pass over y).  r may be y itself (y += x W^T, in
+ * place: every element is read by the thread that writes it, before it writes it); any
+ * other overlap of r and y is WQ_ERR_INVALID_ARG, as is a NULL r.  Every path, launch
+ * option and tile of wq_linear_act / wq_gemv_act / wq_gemm_act takes it (the residual is
+ * added where y is written: by the compute kernel, or by the split-K and tail
+ * reductions).  wq_gemv_residual and wq_gemm_residual take the launch explicitly as
+ * wq_gemv_act and wq_gemm_act do. */
+wq_status wq_linear_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y,
+                             void* ws, size_t ws_bytes, void* stream);
+wq_status wq_gemv_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y,
+                           int split_k, int waves, int rows, void* ws, size_t ws_bytes, void* stream);
+wq_status wq_gemm_residual(const wq_weight* w, int act, const void* x, int64_t M, const void* r, void* y, int tile,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------- grouped (MoE) layer */
 
 /* The grouped weight-only linear of a mixture-of-experts layer (the shared MoE kernel the

@@ -13,7 +13,8 @@ What it computes (plain, slow, obviously correct; NumPy only):
 * ``linear`` -- dequantise to fp32 (exact) and y = x . dequant(W)^T in fp64,
   chunked along N; sampled-column variants for full-size checks; the
   comparison statistics with the per-element tolerance; the full-K activation
-  permutation (x gathered along K before the product).
+  permutation (x gathered along K before the product); the layer with a residual
+  added to its output.
 * ``topk``   -- the k best bf16 logits of a row and the token drawn from them
   with a temperature and a caller-supplied uniform draw (the LM head + top-k
   step of the tileInfer README's feature list; reading in its docstring).
@@ -42,7 +43,8 @@ from .quant import (  # noqa: F401
     packed_sizes, quantize_w4, quantize_w4g128, quantize_w8, unpack_w4g, unpack_w4g128, unpack_w4pc,
 )
 from .linear import (  # noqa: F401
-    compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, token_count, use_gemv,
+    compare, gather_activations, ref_linear, ref_linear_columns, ref_linear_perm, ref_linear_residual, token_count,
+    use_gemv,
 )
 from .topk import ref_topk_sample, sample_row, topk_row  # noqa: F401
 from .moe import (  # noqa: F401

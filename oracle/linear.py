@@ -81,6 +81,15 @@ def ref_linear_columns(x_bits: np.ndarray, P: dict, cols, act: str = "bf16") -> 
     return x @ Wd.T
 
 
+def ref_linear_residual(x_bits: np.ndarray, P: dict, r_bits: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """fp64 y = x . dequant(W)^T + r: the layer with the residual of its output added before
+    the output is rounded (the fused residual of the tileInfer README's "Key
+    Optimizations"; r in the activation type, [M, N])."""
+    y = ref_linear(x_bits, P, act=act)
+    r = _x64(np.asarray(r_bits, dtype=np.uint16).reshape(y.shape), act)
+    return y + r
+
+
 def gather_activations(x_bits: np.ndarray, perm) -> np.ndarray:
     """x'[m, j] = x[m, perm[j]] (bf16 bits), an index outside [0, K) giving +0: the
     full-K activation permutation that the Marlin register and launch scheduling

@@ -732,6 +732,34 @@ def pin_f16_activations(seed=61):
     assert st["fails"] == 1 and abs(st["max_ratio"] - 0.5 / 0.015) < 1e-9, st
 
 
+def pin_residual(seed=62):
+    """The residual epilogue: r = 0 leaves the layer, x = 0 gives r exactly, and a one-hot
+    row gives the dequantised weight plus r (both exact rationals); in fp16 as in bf16."""
+    for fmt, K in (("w8pc", 96), ("w4g128", 128)):
+        W = synth.weight(seed, K, 16, outliers=fmt.startswith("w4"))
+        P = OQ.pack(fmt, W)
+        x = synth.activation(seed, K, 3)
+        zero = np.zeros((3, 16), dtype=np.uint16)
+        assert np.array_equal(OL.ref_linear_residual(x, P, zero), OL.ref_linear(x, P))
+        r = synth.activation(seed + 1, 16, 3)
+        y = OL.ref_linear_residual(np.zeros((3, K), dtype=np.uint16), P, r)
+        for m in range(3):
+            for n in range(16):
+                assert Fraction(float(y[m, n])) == _bf16_bits_value(int(r[m, n])), (fmt, m, n)
+        ks = [0, 5, K - 1]
+        y = OL.ref_linear_residual(synth.one_hot_activation(K, ks), P, r)
+        for m, k in enumerate(ks):
+            for n in range(16):
+                want = _exact_dequant(P, n, k) + _bf16_bits_value(int(r[m, n]))
+                assert Fraction(float(y[m, n])) == want, (fmt, k, n)
+        r16 = synth.activation_f16(seed + 1, 16, 3)
+        x16 = np.zeros((3, K), dtype=np.uint16)
+        y = OL.ref_linear_residual(x16, P, r16, act="f16")
+        for m in range(3):
+            for n in range(16):
+                assert Fraction(float(y[m, n])) == _fp16_value(np.array(r16[m, n], dtype=np.uint16).view(np.float16))
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_golden_w8pc, pin_golden_w4g128, pin_nibble_layout,
     pin_w8_roundtrip_bound, lambda: pin_w8_roundtrip_bound(G=128), pin_w4_roundtrip_bound,
@@ -752,7 +780,7 @@ ALL_PINS = [
     lambda: pin_bruteforce("w4g32", 96), lambda: pin_bruteforce("w4g64", 128),
     lambda: pin_one_hot_random("w8g32"), lambda: pin_one_hot_random("w8g64"),
     lambda: pin_one_hot_random("w4g32"), lambda: pin_one_hot_random("w4g64"),
-    pin_f16_activations,
+    pin_f16_activations, pin_residual,
 ]
 
 

@@ -397,3 +397,18 @@ def test_activation_type_validation(wqlib):
     assert L.wq_gemv_act(C.byref(d), 1, x, 1, y, 1, 1, 4 | wqlib.GEMV_PREFETCH, None, 0, None) == 2
     assert L.wq_gemv_act(C.byref(d), 1, x, 1, y, 0, 2, 0, None, 0, None) == 1    # waves without a split
     assert L.wq_gemv_act(C.byref(d), 1, x, 8, y, 1, 0, 0, None, 0, None) == 1    # M > 7
+
+
+def test_residual_validation(wqlib):
+    """The residual entry points refuse a NULL residual and a residual that overlaps y
+    without being y, on the host."""
+    L = wqlib.lib
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    d = wqlib.WqWeightC(wqlib.FMT["w8pc"], wqlib.GFX950, 1024, 64, 0x1000, 0x2000, 0)
+    assert L.wq_linear_residual(C.byref(d), 0, x, 1, None, y, None, 0, None) == 1
+    assert L.wq_linear_residual(C.byref(d), 0, x, 1, C.c_void_p(0x20002), y, None, 0, None) == 1
+    assert L.wq_linear_residual(C.byref(d), 0, x, 1, C.c_void_p(0x20001), y, None, 0, None) == 3
+    assert L.wq_gemm_residual(C.byref(d), 0, x, 8, C.c_void_p(0x1FFFE), y, 2, None, 0, None) == 1
+    assert L.wq_gemv_residual(C.byref(d), 0, x, 1, None, y, 1, 0, 0, None, 0, None) == 1
+    assert L.wq_gemv_residual(C.byref(d), 0, x, 1, y, y, 0, 2, 0, None, 0, None) == 1   # waves without split
+    assert L.wq_linear_residual(C.byref(d), 5, x, 1, y, y, None, 0, None) == 1          # unknown act

@@ -362,6 +362,25 @@ def _mut_f16_decode_drops_subnormals(mp):
     mp.setattr(OL, "f16_bits_to_f64", bad)
 
 
+def _mut_residual_subtracted(mp):
+    orig = OL.ref_linear
+
+    def bad(x_bits, P, r_bits, act="bf16"):              # the residual taken away instead of added
+        y = orig(x_bits, P, act=act)
+        return y - OL._x64(np.asarray(r_bits, dtype=np.uint16).reshape(y.shape), act)
+    mp.setattr(OL, "ref_linear_residual", bad)
+
+
+def _mut_residual_transposed(mp):
+    orig = OL.ref_linear
+
+    def bad(x_bits, P, r_bits, act="bf16"):              # r read as [N, M]
+        y = orig(x_bits, P, act=act)
+        r = np.asarray(r_bits, dtype=np.uint16).reshape(-1)
+        return y + OL._x64(r.reshape(y.shape[1], y.shape[0]).T, act)
+    mp.setattr(OL, "ref_linear_residual", bad)
+
+
 MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant_drops_zero,
              _mut_nibble_order, _mut_zeros_along_k, _mut_drop_tail_chunk, _mut_truncating_bf16,
              _mut_wrong_group_index, _mut_threshold, _mut_topk_ties_larger_index,
@@ -372,7 +391,8 @@ MUTATIONS = [_mut_round_half_away, _mut_fp32_scale, _mut_zero_sign, _mut_dequant
              _mut_silu_sign, _mut_silu_mul_swapped, _mut_moe_rows_shifted, _mut_moe_expert_index,
              _mut_w4pc_groups_of_128, _mut_w4pc_zeros_reversed, _mut_w4pc_dequant_row0_zero,
              _mut_small_groups_quantised_per_128, _mut_small_group_zeros_not_transposed,
-             _mut_small_group_dequant_tiles_scales, _mut_f16_read_as_bf16, _mut_f16_decode_drops_subnormals]
+             _mut_small_group_dequant_tiles_scales, _mut_f16_read_as_bf16, _mut_f16_decode_drops_subnormals,
+             _mut_residual_subtracted, _mut_residual_transposed]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
