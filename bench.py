@@ -268,7 +268,7 @@ def traffic_entry(kernel_src_sha: str):
 
 # Launch configuration of the headline GEMV per shape (split_k, waves, rows) used by
 # the counter pass, so the profiled kernels are the ones the tuner picks on MI355X.
-PROFILE_CONFIG = {(5120, 27648): (1, 3, 4 | 0x100), (13824, 5120): (1, 12, 4), (5120, 7168): (1, 1, 4 | 0x100),
+PROFILE_CONFIG = {(5120, 27648): (1, 3, 4 | 0x100), (13824, 5120): (1, 6, 4), (5120, 7168): (1, 1, 4 | 0x100),
                   (6144, 5120): (1, 6, 4)}
 COPY_BYTES = 1 << 30
 
@@ -365,7 +365,8 @@ def profile_prefill(calls: int = 10):
 # Few-token GEMM rows for rocprofv3 (fmt, K, N, M, tile): the tiles the tuner picks on
 # MI355X at 8 and 64 tokens on the widest decode shape.
 FEWTOKEN_PROFILE = [("w4g128", 5120, 27648, 8, 22), ("w4g128", 5120, 27648, 64, 15),
-                    ("w8pc", 5120, 27648, 8, 5), ("w8pc", 5120, 27648, 64, 15)]
+                    ("w8pc", 5120, 27648, 8, 5), ("w8pc", 5120, 27648, 64, 15),
+                    ("w4g128", 13824, 5120, 64, 25), ("w8pc", 13824, 5120, 64, 25)]
 
 
 def profile_fewtoken(calls: int = 10):
@@ -971,6 +972,10 @@ def run_detail(wq, torch, args) -> dict:
         "prefill_gemm": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M, tune_it=M >= 8)
                                  for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
                                  for M in (8, 64, 512, 2048)},
+        # between the matrix-core GEMV tiles (<= 16 tokens) and the MFMA-bound sizes
+        "mid_m_gemm": lambda: {f"{fmt}_{K}x{N}_M{M}": measure(5, fmt, K, N, M)
+                               for fmt in ("w8pc", "w4g128") for K, N in [(5120, 27648), (13824, 5120)]
+                               for M in (32, 128, 256)},
         "lm_head_topk": lambda: {f"{fmt}_{K}x{N}_M{M}": measure_lm_head_topk(wq, torch, 4, fmt, K, N, M)
                                  for fmt in ("w8g128", "w4g128") for K, N in [(5120, 151936)] for M in (1, 4)},
         "activation_permutation": lambda: {f"{fmt}_{K}x{N}_M{M}": measure_linear_perm(wq, torch, cfg, fmt, K, N, M)

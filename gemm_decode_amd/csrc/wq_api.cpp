@@ -135,14 +135,19 @@ void resolve_gemv(const wq_weight* w, int64_t M, int* split, int* waves, int* ro
 // partial last round split over K (tile 13).
 int default_tile(const wq_weight* w, int64_t M) {
   if (M > 16 && M <= kSkinnyMaxM && w->K % 64 == 0) {
-    // 64-row LDS-DMA tiles: the smallest split-K that gives at least 200 workgroups
-    // (measured on MI355X at M = 32..128: they beat the skinny kernel by 10-37 %)
+    // 64-row LDS-DMA tiles: the smallest split-K that gives at least 0.6 workgroups per
+    // CU (measured on MI355X at M = 32..128: they beat the skinny kernel by 10-37 %; at
+    // N = 5120 split 8 (160 workgroups) beats 16 (320: a second, partial round) -- int8
+    // at M = 64 31 against 41 us, uint4 45 against 58 us)
     const int64_t blocks = ((M + 63) / 64) * ((w->N + 255) / 256);
-    int t = kDma64Tile0;
-    while (t < kDma64TileLast && blocks * gemm_dma64_split(t, M, w->N) < 200 &&
-           gemm_dma64_split(t + 1, M, w->N) > gemm_dma64_split(t, M, w->N))
-      ++t;
-    return t;
+    const int64_t want = 3 * (int64_t)device_cus() / 5;
+    static constexpr int kSplits64[] = {kDma64Tile0, kDma64Tile0 + 1, kDma64TileLast, kDma64DeepTile0,
+                                        kDma64DeepTileLast};  // split-K 1, 2, 4, 8, 16
+    int i = 0;
+    while (i + 1 < 5 && blocks * gemm_dma64_split(kSplits64[i], M, w->N) < want &&
+           gemm_dma64_split(kSplits64[i + 1], M, w->N) > gemm_dma64_split(kSplits64[i], M, w->N))
+      ++i;
+    return kSplits64[i];
   }
   if (M > kSkinnyMaxM && M <= 2 * kSkinnyMaxM && w->K % 64 == 0) {
     // 128-row LDS-DMA tiles, the same rule (measured on MI355X at M = 256: 12 % faster

@@ -871,16 +871,20 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
 // (a wider spread, a bf16 subnormal, Inf or NaN) is written as NaN, so that its tiles
 // recompute on the exact path.  Otherwise every workgroup converts the x chunks of each
 // stage it loads (no scaling: tiles whose x fp16 cannot hold fall back).
-__global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
-                                                            float* __restrict__ xinv, int K) {
-  __shared__ uint32_t red_mx[4], red_mn[4];
+// One workgroup per row, up to 1024 threads: each thread keeps its first kXRowRegs 16-byte
+// chunks in registers between the two passes (rows up to 32768 k are read once, every
+// load issued before the first is used); longer rows read the rest again.
+constexpr int kXRowRegs = 4;
+__global__ __launch_bounds__(1024) void x_to_f16_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                                             float* __restrict__ xinv, int K) {
+  __shared__ uint32_t red_mx[16], red_mn[16];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = blockDim.x, NWv = T >> 6;
   const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K);
   uint4* xo = reinterpret_cast<uint4*>(xh + (size_t)m * K);
   const int n8 = K / 8;
   uint32_t mx = 0, mn = 0xFFFFu;  // largest |x| bits, smallest nonzero |x| bits
-  for (int i = tid; i < n8; i += 256) {
-    const uint4 v = xr[i];
+  auto scan = [&](const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -888,7 +892,16 @@ __global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __re
       mx = max(mx, max(lo, hi));
       mn = min(mn, min(lo ? lo : 0xFFFFu, hi ? hi : 0xFFFFu));
     }
+  };
+  uint4 keep[kXRowRegs];
+#pragma unroll
+  for (int j = 0; j < kXRowRegs; ++j) {
+    const int i = tid + j * T;
+    keep[j] = i < n8 ? xr[i] : make_uint4(0u, 0u, 0u, 0u);  // zeros change neither bound
   }
+#pragma unroll
+  for (int j = 0; j < kXRowRegs; ++j) scan(keep[j]);
+  for (int i = tid + kXRowRegs * T; i < n8; i += T) scan(xr[i]);
   for (int d = 32; d >= 1; d >>= 1) {
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, d));
@@ -898,16 +911,19 @@ __global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __re
     red_mn[wave] = mn;
   }
   __syncthreads();
-  mx = max(max(red_mx[0], red_mx[1]), max(red_mx[2], red_mx[3]));
-  mn = min(min(red_mn[0], red_mn[1]), min(red_mn[2], red_mn[3]));
+  mx = red_mx[0];
+  mn = red_mn[0];
+  for (int w = 1; w < NWv; ++w) {
+    mx = max(mx, red_mx[w]);
+    mn = min(mn, red_mn[w]);
+  }
   // biased bf16 exponents; the scale puts the largest value below 2^15 (e capped so
   // that 2^-e stays a normal fp32 number)
   const int emax = (int)(mx >> 7), emin = (int)(mn >> 7);
   const int e = mx == 0 ? 0 : min(141 - emax, 100);
   const bool ok = mx == 0 || (emax < 255 && emax + e <= 141 && (mn == 0xFFFFu || (emin >= 1 && emin + e >= 110)));
   const float sc = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);  // 2^e, -113 <= e <= 100
-  for (int i = tid; i < n8; i += 256) {
-    const uint4 v = xr[i];
+  auto conv = [&](const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
 #pragma unroll
@@ -915,8 +931,14 @@ __global__ __launch_bounds__(256) void x_to_f16_rows_kernel(const uint16_t* __re
       const float2_t f = {__uint_as_float(w[q] << 16) * sc, __uint_as_float(w[q] & 0xFFFF0000u) * sc};
       o[q] = ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t)) : 0x7E007E00u;
     }
-    xo[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
+#pragma unroll
+  for (int j = 0; j < kXRowRegs; ++j) {
+    const int i = tid + j * T;
+    if (i < n8) xo[i] = conv(keep[j]);
   }
+  for (int i = tid + kXRowRegs * T; i < n8; i += T) xo[i] = conv(xr[i]);
   if (tid == 0) xinv[m] = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);  // 2^-e
 }
 
@@ -1662,6 +1684,47 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   y[i] = f32_to_out<XF>(with_res<XF>(sc * v, res, (size_t)i));
 }
 
+// The same sum with four consecutive outputs per thread (M N % 4 == 0): 16-byte partial
+// loads, those of four ranges issued together; each output still adds its ranges in
+// order from 0, so the results are the scalar kernel's bit for bit.
+template <bool kPerChannel, bool XF = false>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce4_kernel(const float* __restrict__ part,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   uint16_t* y, int M, int N,
+                                                                   int S, const uint16_t* res) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // this thread's 4-output group
+  const int64_t MN = (int64_t)M * N, MN4 = MN / 4;
+  if (q >= MN4) return;
+  const float4* p4 = reinterpret_cast<const float4*>(part) + q;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    float4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = p4[(int64_t)(s + j) * MN4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[0] += a[j].x;
+      v[1] += a[j].y;
+      v[2] += a[j].z;
+      v[3] += a[j].w;
+    }
+  }
+  for (; s < S; ++s) {
+    const float4 a = p4[(int64_t)s * MN4];
+    v[0] += a.x;
+    v[1] += a.y;
+    v[2] += a.z;
+    v[3] += a.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = 4 * q + j;
+    const float sc = kPerChannel ? bf16_to_f32(scales[i % N]) : 1.f;
+    y[i] = f32_to_out<XF>(with_res<XF>(sc * v[j], res, (size_t)i));
+  }
+}
+
 // The split tail tiles of tile 13: y = the ranges' fp32 partials added in range order
 // (times the channel scale for per-channel W8).  blockIdx.y: tail tile; a thread takes
 // 8 consecutive columns of one row (32 threads per row, 8 rows per block, blockIdx.x:
@@ -1771,7 +1834,7 @@ int gemm_dma64_split(int tile, int64_t M, int64_t N) {
   const int tm = gemm_dma_rows(tile);
   if (tm == 0) return 0;
   const int64_t blocks = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
-  int S = 1 << (tile - (tm == 64 ? kDma64Tile0 : kDma128Tile0));
+  int S = tile >= kDma64DeepTile0 ? 8 << (tile - kDma64DeepTile0) : 1 << (tile - (tm == 64 ? kDma64Tile0 : kDma128Tile0));
   while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
   return S;
 }
@@ -1786,7 +1849,7 @@ size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile) {
     const int S = gemm_mma_split(tile, M, 0x7FFFFFFF);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
   }
-  if (tile >= kDma64Tile0 && tile <= kDma128TileLast) {
+  if (gemm_dma_rows(tile) != 0) {
     const int S = gemm_dma64_split(tile, M, N);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
   }
@@ -1805,7 +1868,7 @@ static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile) {
   const size_t need = gemm_workspace_bytes(fmt, N, M, tile);
-  const bool dma = tile >= 9 && (tile < kMmaTile0 || tile == kDmaSplit3Tile);
+  const bool dma = tile >= 9 && (tile < kMmaTile0 || tile >= kDmaSplit3Tile);
   if (fmt == WQ_FMT_W8_PC || !dma || K % DBK != 0 || M * K >= (int64_t(1) << 31)) return need;
   return round256(round256(need) + (size_t)M * (size_t)K * 2) + (size_t)M * sizeof(float);
 }
@@ -1819,7 +1882,9 @@ static hipError_t x_to_f16_rows(const uint16_t* x, int64_t M, int K, void* ws, s
   if (!ws || ws_bytes < xi_off + (size_t)M * sizeof(float) || ((uintptr_t)ws + xh_off) % 16 != 0) return hipSuccess;
   *xh = (uint16_t*)((uint8_t*)ws + xh_off);
   *xinv = (float*)((uint8_t*)ws + xi_off);
-  x_to_f16_rows_kernel<<<(unsigned)M, 256, 0, s>>>(x, *xh, *xinv, K);
+  // threads: a 16-byte chunk each (whole waves, at most 1024)
+  const int thr = (int)std::min<int64_t>(1024, std::max<int64_t>(64, ((K / 8 + 63) / 64) * 64));
+  x_to_f16_rows_kernel<<<(unsigned)M, thr, 0, s>>>(x, *xh, *xinv, K);
   return hipGetLastError();
 }
 
@@ -1867,6 +1932,14 @@ static void g_dma_dispatch(int fmt, int tm, dim3 grid, hipStream_t s, const uint
 static void splitk_reduce(bool pc, bool xf, const float* part, const uint16_t* sc, uint16_t* y, int64_t M, int N,
                           int S, hipStream_t s, const uint16_t* res) {
   const int64_t MN = M * N;
+  if (MN % 4 == 0) {  // four outputs per thread (the partials are 16-byte aligned: ws is 256-byte aligned)
+    const unsigned b4 = (unsigned)((MN / 4 + 255) / 256);
+    if (pc && xf) gemm_splitk_reduce4_kernel<true, true><<<b4, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+    else if (pc) gemm_splitk_reduce4_kernel<true><<<b4, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+    else if (xf) gemm_splitk_reduce4_kernel<false, true><<<b4, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+    else gemm_splitk_reduce4_kernel<false><<<b4, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
+    return;
+  }
   const unsigned blocks = (unsigned)((MN + 255) / 256);
   if (pc && xf) gemm_splitk_reduce_kernel<true, true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
   else if (pc) gemm_splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(part, sc, y, (int)M, N, S, res);
@@ -1916,7 +1989,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const bool pc = w->fmt == WQ_FMT_W8_PC;
   const int tm = gemm_dma_rows(tile);
   if (tm != 0 && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
-    // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 over gridDim.y
+    // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 (8 / 16 for 25 / 26) over gridDim.y
     const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
     int S = gemm_dma64_split(tile, M, N);
     if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;

@@ -177,10 +177,10 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * ranges of a cross-workgroup K split -- 32 * M * N * 4 bytes for M < 8 (GEMV); for
  * M >= 8 the largest split * M * N * 4 of the split GEMM tiles: the skinny tiles (M <=
  * 128; split <= 16, split * M <= 1024, at most 2048 workgroups) and the split-K
- * LDS-DMA tiles (split <= 8, at most 512 workgroups, at most 256 MiB) -- or the
+ * LDS-DMA tiles (split <= 16, at most 512 workgroups, at most 256 MiB) -- or the
  * partials of tile 13's split last round (sized for the current device's CU count, 256
  * when none is visible); 0 when no split applies.  For the group-128 formats the
- * LDS-DMA tiles 9..19 also use M * K * 2 bytes after the partials (at a 256-byte
+ * LDS-DMA tiles 9..19, 24..26 also use M * K * 2 bytes after the partials (at a 256-byte
  * boundary) for x converted to fp16 once per call (each row scaled by a power of two
  * so that it converts exactly), then M * 4 bytes (at a 256-byte boundary) for the row
  * scales; given less, they convert x inside every workgroup instead, unscaled (same
@@ -296,13 +296,17 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *      split drops to 1); M > 16: tile 14 (tile 2 when K % 64 != 0);
  *   24  tile 9 with split-K 3 (capped and needing the workspace as 10..12): a single
  *      partial round of tiles (160 per-channel tiles at M = 2048, N = 5120) becomes
- *      work for more of the CUs.
- * Groups of 32 and 64 run tiles 2 and 9..19, 24 as described for group-128 (their
+ *      work for more of the CUs;
+ *   25, 26  as 14..16 with split-K 8 and 16 (capped and needing the workspace as
+ *      15 and 16): narrow N at a few tokens (N = 5120 has 20 column tiles) spread over
+ *      more of the CUs; the default for 17..128 tokens where splits 1..4 leave fewer
+ *      than 200 workgroups; other shapes: tile 1.
+ * Groups of 32 and 64 run tiles 2 and 9..19, 24..26 as described for group-128 (their
  * kernels fold every group's partial sum in as a group-128 tile does); tiles 1, 3 and
  * 4 run as tile 9, tiles 5..8 and 20..23 as tile 14. 
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 24
+#define WQ_GEMM_TILES 26
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -489,7 +493,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 24
+#define WQ_TUNE_LAT_SLOTS 26
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

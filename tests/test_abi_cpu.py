@@ -198,11 +198,12 @@ def test_validation_rejects_before_any_device_work(wqlib):
     assert L.wq_workspace_size(C.byref(d), 1, C.byref(n)) == 0 and n.value == 32 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 7, C.byref(n)) == 0 and n.value == 32 * 7 * 1024 * 4
     # M >= 8: split-K partials -- the skinny GEMM (split <= 16, split * M <= 1024, M <= 128)
-    # and the LDS-DMA tile (split <= 8, at most 512 workgroups of 256 x 256, <= 256 MiB)
+    # and the LDS-DMA tiles (split <= 16 for the 64-row tiles, at most 512 workgroups,
+    # <= 256 MiB): 4 column tiles of 256 x 64-row tiles x 16 stays within 512 workgroups
     assert L.wq_workspace_size(C.byref(d), 8, C.byref(n)) == 0 and n.value == 16 * 8 * 1024 * 4
     assert L.wq_workspace_size(C.byref(d), 64, C.byref(n)) == 0 and n.value == 16 * 64 * 1024 * 4
-    assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 8 * 128 * 1024 * 4
-    assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 8 * 129 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 128, C.byref(n)) == 0 and n.value == 16 * 128 * 1024 * 4
+    assert L.wq_workspace_size(C.byref(d), 129, C.byref(n)) == 0 and n.value == 16 * 129 * 1024 * 4
     big = _desc(wqlib, K=5120, N=27648)
     assert L.wq_workspace_size(C.byref(big), 512, C.byref(n)) == 0 and n.value == 2 * 512 * 27648 * 4
     # 864 tiles = 3 rounds of 256 CUs + 96: tile 13 splits those 96 over K in 2 (a
