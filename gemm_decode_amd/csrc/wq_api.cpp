@@ -765,9 +765,16 @@ wq_status wq_tune(const wq_weight* copies0, int n_copies, int64_t M, const void*
         const int cap = gemv_max_waves(fmt, (int)M, rw);
         if (cap == 0) continue;  // flag not offered at this format and M
         const int dflt = gemv_default_waves(copies[0].K, copies[0].N, fmt, (int)M, s, rw);
-        // powers of two, 3 x powers of two, and the default
+        // K pieces a workgroup's waves share (1 KB slices, or 128-k units for the
+        // matrix-core kernel): a count that is the fewest waves giving each wave at most
+        // ceil(P / w) pieces spreads them evenly (P = 14: 5 and 7 waves)
+        const int64_t P = (rw & kGemvMfma) ? ((copies[0].K + kGroup - 1) / kGroup + s - 1) / s
+                                           : (gemv_slices(copies[0].K, fmt) + s - 1) / s;
+        auto balanced = [&](int wv) { return wv == 1 || (P + wv - 1) / wv < (P + wv - 2) / (wv - 1); };
+        // powers of two, 3 x powers of two, the balanced counts and the default
         for (int wv = 1; wv <= cap; ++wv)
-          if (((wv & (wv - 1)) == 0) || ((wv % 3 == 0) && (((wv / 3) & (wv / 3 - 1)) == 0)) || wv == dflt)
+          if (((wv & (wv - 1)) == 0) || ((wv % 3 == 0) && (((wv / 3) & (wv / 3 - 1)) == 0)) || balanced(wv) ||
+              wv == dflt)
             cand.push_back({s, wv, rw, 0});
       }
   } else {
