@@ -7,8 +7,10 @@ where it is unique: every kept entry matches the oracle's logit within tolerance
 beats every dropped entry up to twice the tolerance, and the order and the ties
 follow the stated rule on the kernel's own values.  Draws use a u in the middle of
 the oracle's widest probability interval, so that the token is decided away from
-any boundary; they are compared when the kept sets agree.  The same order is also
-checked exactly against the logits the layer itself returns (wq_linear)."""
+any boundary; they are compared when the kept sets agree, and on every row against the
+oracle's draw over the layer's own kept logits with the same u (unless u falls within
+1e-4 of one of that distribution's boundaries).  The same order is also checked
+exactly against the logits the layer itself returns (wq_linear)."""
 import numpy as np
 import pytest
 import torch
@@ -70,6 +72,17 @@ def _mid_u(bits_kept, T):
     return float((lo[j] + c[j]) / 2)
 
 
+def _near_boundary(bits_kept, T, u, margin=1e-4):
+    """Whether u lies within `margin` of a running-sum boundary of the draw over these
+    kept logits (fp64): there fp32 arithmetic may legitimately pick the neighbour."""
+    if T == 0:
+        return False
+    v = OQ.bf16_bits_to_f32(bits_kept).astype(np.float64)
+    p = np.exp((v - v[0]) / T)
+    c = np.cumsum(p / p.sum())
+    return bool(np.min(np.abs(c - u)) < margin)
+
+
 def _check_row(name, got_vals, got_idx, got_tok, y_ref_row, k, T, u, ref_idx, ref_tok):
     tol = OL.TOL_REL * np.maximum(1.0, np.abs(y_ref_row))
     assert len(set(got_idx.tolist())) == k, name
@@ -118,6 +131,10 @@ def test_topk_against_oracle(wq, fmt, K, V, M):
                 want = _order_of(own[m])[:k]
                 assert np.array_equal(idx[m], want), name
                 assert np.array_equal(vals[m], own[m][want]), name
+                # the token against the oracle's draw on those same kept logits, whether or
+                # not the kept set matches the oracle's own (u away from a boundary)
+                if not _near_boundary(own[m][want], T, u[m]):
+                    assert tok[m] == OT.sample_row(own[m][want], want, T, u[m]), name
                 if T == 0:
                     assert tok[m] == idx[m][0], name
 
@@ -201,6 +218,8 @@ def test_topk_full_lm_head(wq, cfg, fmt, K, V):
             assert np.array_equal(idx[m], want), name
             assert np.array_equal(vals[m], own[m][want]), name
             assert tok[m] in set(idx[m].tolist()), name
+            if not _near_boundary(own[m][want], T, u[m]):   # the oracle's draw on these kept logits
+                assert tok[m] == OT.sample_row(own[m][want], want, T, u[m]), name
             ref_kept = np.array([y_rows[m, pos[int(i)]] for i in idx[m]])
             tol_k = OL.TOL_REL * np.maximum(1.0, np.abs(ref_kept))
             gv = OQ.bf16_bits_to_f32(vals[m]).astype(np.float64)
