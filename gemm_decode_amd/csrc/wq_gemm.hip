@@ -18,6 +18,7 @@
 //     of every 128-element group.
 #include "wq_internal.h"
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 
 namespace wq {
@@ -513,7 +514,9 @@ __device__ __forceinline__ bool dma_work(int M, int N, int tail0, int tailS, Dma
 // row blocks and CB = 8 / WN column blocks of 32.  With 1 x 4 every code chunk is
 // converted by exactly one wave (half the conversion work of 2 x 2) at the price of
 // every wave reading the whole x tile from LDS.
-template <int WM, int WN, int TM>
+// XF: fp16 activations -- x arrives as fp16 (the same DMA), the codes become exact fp16
+// instead of bf16, the products run on v_mfma_f32_32x32x16_f16 and y is fp16.
+template <int WM, int WN, int TM, bool XF = false>
 __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
@@ -593,19 +596,33 @@ __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
     baddr[P] = kDA + (wn * 32 * CB + l32) * 64 + 16 * ((2 * P + lh) ^ swz_w(l32));
   }
 
-  bf16x8_t A0[2][RB], B0[2][CB];
-  bf16x8_t A1[NW == 4 ? 2 : 1][RB], B1[NW == 4 ? 2 : 1][CB];
-  auto fread = [&](const uint8_t* st, int P, bf16x8_t (*A)[RB], bf16x8_t (*B)[CB]) {
+  using frag_t = std::conditional_t<XF, h16x8_t, bf16x8_t>;  // eight 16-bit operands
+  frag_t A0[2][RB], B0[2][CB];
+  frag_t A1[NW == 4 ? 2 : 1][RB], B1[NW == 4 ? 2 : 1][CB];
+  auto fread = [&](const uint8_t* st, int P, frag_t (*A)[RB], frag_t (*B)[CB]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int i = 0; i < RB; ++i)
-        A[s2][i] = *reinterpret_cast<const bf16x8_t*>(st + aaddr[P][s2] + i * 32 * 128);
+        A[s2][i] = *reinterpret_cast<const frag_t*>(st + aaddr[P][s2] + i * 32 * 128);
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const uint4 raw = *reinterpret_cast<const uint4*>(st + baddr[P] + j * 32 * 64);
-      B[0][j] = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_lo(raw));
-      B[1][j] = __builtin_bit_cast(bf16x8_t, i8x16_to_bf16_hi(raw));
+      if constexpr (XF) {
+        // fp16 (1024 + u) pairs by v_perm_b32 under the exponent byte 0x64, minus 1152 by
+        // one packed add: the exact codes q = u - 128, in byte order
+        auto q2 = [](uint32_t w, uint32_t sel) {
+          return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h16x2_t, __builtin_amdgcn_perm(0x64646464u, w, sel)) +
+                                                  h16x2_t{(_Float16)-1152.f, (_Float16)-1152.f});
+        };
+        B[0][j] = __builtin_bit_cast(frag_t, make_uint4(q2(raw.x, 0x04010400u), q2(raw.x, 0x04030402u),
+                                                        q2(raw.y, 0x04010400u), q2(raw.y, 0x04030402u)));
+        B[1][j] = __builtin_bit_cast(frag_t, make_uint4(q2(raw.z, 0x04010400u), q2(raw.z, 0x04030402u),
+                                                        q2(raw.w, 0x04010400u), q2(raw.w, 0x04030402u)));
+      } else {
+        B[0][j] = __builtin_bit_cast(frag_t, i8x16_to_bf16_lo(raw));
+        B[1][j] = __builtin_bit_cast(frag_t, i8x16_to_bf16_hi(raw));
+      }
     }
   };
 
@@ -616,14 +633,16 @@ __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int a = 0; a < 16; ++a) acc[i][j][a] = 0.f;
-  auto mma = [&](bf16x8_t (*A)[RB], bf16x8_t (*B)[CB]) {
+  auto mma = [&](frag_t (*A)[RB], frag_t (*B)[CB]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < CB; ++j) {
+          if constexpr (XF) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+          else acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s2][i], B[s2][j], acc[i][j], 0, 0, 0);
+        }
   };
   // This wave's DMA of the step after the current one is complete (only the newest
   // step's kDmaPerStep may still be in flight) and every wave has finished reading
@@ -705,13 +724,13 @@ __device__ __forceinline__ void dma_w8pc_body(const uint8_t* __restrict__ qw,
       for (int a = 0; a < 16; ++a) {
         const int m = m0 + wm * 32 * RB + i * 32 + 8 * (a >> 2) + 4 * lh + (a & 3);
         if (m >= M) continue;
-        if (S == 1) y[(size_t)m * N + n] = f32_to_out<false>(with_res<false>(sc * acc[i][j][a], res, (size_t)m * N + n));
+        if (S == 1) y[(size_t)m * N + n] = f32_to_out<XF>(with_res<XF>(sc * acc[i][j][a], res, (size_t)m * N + n));
         else part[wk.poff + (size_t)(m - wk.pm0) * wk.ppitch + (n - wk.pn0)] = acc[i][j][a];
       }
   }
 }
 
-template <int WM, int WN>
+template <int WM, int WN, bool XF = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const uint8_t* __restrict__ qw,
                                                                          const uint16_t* __restrict__ scales,
                                                                          const uint16_t* __restrict__ x,
@@ -719,16 +738,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_w8pc_kernel(const ui
                                                                          float* __restrict__ part, int M, int K,
                                                                          int N, int tail0, int tailS,
                                                                          const uint16_t* res) {
-  dma_w8pc_body<WM, WN, DBM>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
+  dma_w8pc_body<WM, WN, DBM, XF>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
 }
 
 // 64- and 128-row tiles (capping the registers for two workgroups per CU spills:
 // measured slower)
-template <int TM>
+template <int TM, bool XF = false>
 __global__ __launch_bounds__(512, 1) void gemm_dma64_w8pc_kernel(const uint8_t* __restrict__ qw, const uint16_t* __restrict__ scales,
                             const uint16_t* __restrict__ x, uint16_t* y, float* __restrict__ part,
                             int M, int K, int N, int tail0, int tailS, const uint16_t* res) {
-  dma_w8pc_body<1, 8, TM>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
+  dma_w8pc_body<1, 8, TM, XF>(qw, scales, x, y, part, M, K, N, tail0, tailS, res);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1997,8 +2016,12 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     const dim3 grid((unsigned)(8 * ((total + 7) / 8)), (unsigned)S);
     float* part = (float*)ws;
     if (pc) {
-      if (tm == 64)
+      if (tm == 64 && xf)
+        gemm_dma64_w8pc_kernel<64, true><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
+      else if (tm == 64)
         gemm_dma64_w8pc_kernel<64><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
+      else if (xf)
+        gemm_dma64_w8pc_kernel<128, true><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
       else
         gemm_dma64_w8pc_kernel<128><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, (int)total, 1, res);
     } else {
@@ -2043,7 +2066,9 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     const size_t part_bytes = tailS > 1 ? (size_t)tailS * ntail * btm * DBN * sizeof(float)
                                         : (S > 1 ? (size_t)S * M * N * sizeof(float) : 0);
     if (pc) {
-      if (tile == 3)
+      if (xf)  // (tiles 3 and 4 run as 9 for fp16 activations)
+        gemm_dma_w8pc_kernel<2, 4, true><<<grid, 512, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
+      else if (tile == 3)
         gemm_dma_w8pc_kernel<2, 2><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
       else if (tile == 4)
         gemm_dma_w8pc_kernel<1, 4><<<grid, 256, 0, s>>>(qw, sc, x, y, part, (int)M, K, N, tail0, tailS, res);
@@ -2063,7 +2088,9 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
     }
     if (tailS > 1) {
       const dim3 rg((unsigned)(btm / 8), (unsigned)ntail);
-      if (pc)
+      if (pc && xf)
+        gemm_tail_reduce_kernel<true, 256, true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);
+      else if (pc)
         gemm_tail_reduce_kernel<true, 256><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);
       else if (xf)
         gemm_tail_reduce_kernel<false, 128, true><<<rg, 256, 0, s>>>(part, sc, y, (int)M, N, tail0, tailS, res);

@@ -196,9 +196,16 @@ size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int t
 // LDS-DMA tiles, which read the fp16 x as their operand (act_tile gives what runs)
 wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t* y, int tile,
                       void* ws, size_t ws_bytes, hipStream_t s, bool xf = false, const uint16_t* res = nullptr);
-// the GEMM tile that runs for fp16 activations: per-channel W8 takes tile 2's kernel for
-// every tile; the grouped formats map as small_group_tile does
-inline int act_tile(int fmt, int tile) { return fmt == WQ_FMT_W8_PC ? 2 : small_group_tile(tile); }
+// the GEMM tile that runs for fp16 activations: the LDS-DMA tiles have fp16 forms (tiles 3
+// and 4 run as 9); the skinny and matrix-core GEMV tiles run as tile 14, tile 1 as tile 2's
+// kernel; the grouped formats map as small_group_tile does
+inline int act_tile(int fmt, int tile) {
+  if (fmt != WQ_FMT_W8_PC) return small_group_tile(tile);
+  if (tile == 3 || tile == 4) return 9;
+  if ((tile >= kSkinnyTile0 && tile <= kSkinnyTileLast) || (tile >= kMmaTile0 && tile <= kMmaTileLast))
+    return kDma64Tile0;
+  return tile == 1 ? 2 : tile;
+}
 
 // Workspace bytes for a GEMV with the given split (fp32 partials of every slice).
 size_t gemv_workspace_bytes(int64_t N, int64_t M, int split_k);

@@ -332,10 +332,11 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
  *     WQ_ERR_UNSUPPORTED).  split_k 0 = the tuned launch of the bf16 layer with its
  *     matrix-core option replaced by the default dot2 launch and its prefetch flag
  *     dropped (waves and rows must then be 0); else as wq_gemv_ex.
- *   - GEMM (M >= 8): per-channel W8 runs tile 2's kernel for every tile id; the grouped
- *     formats run tile 2 and the LDS-DMA tiles 9..19 and 24 (x read as their fp16
- *     operand: no conversion, no row scale, no fallback), tiles 1, 3, 4 as 9 and 5..8,
- *     20..23 as 14.  The workspace is wq_workspace_size's.
+ *   - GEMM (M >= 8): per-channel W8 runs tile 2 and the LDS-DMA tiles 9..19 and 24..26
+ *     (exact fp16 codes, x as the fp16 operand of the DMA), tiles 3, 4 as 9, 1 as 2, and
+ *     5..8, 20..23 as 14; the grouped formats run tile 2 and the LDS-DMA tiles 9..19 and
+ *     24..26 (x read as their fp16 operand: no conversion, no row scale, no fallback),
+ *     tiles 1, 3, 4 as 9 and 5..8, 20..23 as 14.  The workspace is wq_workspace_size's.
  * wq_moe_linear, wq_lm_head_topk, wq_linear_perm and wq_linear_static take bf16 only.
  * Unknown act: WQ_ERR_INVALID_ARG. */
 wq_status wq_linear_act(const wq_weight* w, int act, const void* x, int64_t M, void* y, void* ws,
