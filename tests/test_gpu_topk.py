@@ -139,6 +139,31 @@ def test_topk_against_oracle(wq, fmt, K, V, M):
                     assert tok[m] == idx[m][0], name
 
 
+def test_topk_chunks_with_equal_tops(wq):
+    """Weight rows repeating every 2048 rows give every 2048-logit chunk the same values,
+    so each chunk's k best tie with every other chunk's and the merge must order equal
+    values across chunks by index (ten chunks at k = 64 and 7, five at k = 64).  Order
+    and token exactly as stated on the layer's own logits."""
+    K = 128
+    base = synth.weight(203, K, 2048) * np.float32(20.0)
+    for chunks, k in ((10, 64), (5, 64), (10, 7)):
+        V = 2048 * chunks
+        W = np.tile(base, (chunks, 1))
+        g, _ = quantize_on_gpu(wq, W, "w8pc")
+        x = synth.activation(203, K, 2)
+        own = _layer_logits(wq, g, x)
+        for T in (0.0, 1.0):
+            u = [0.31, 0.77]
+            vals, idx, tok = _run(wq, g, x, k, T, u)
+            for m in range(2):
+                name = f"equal tops chunks={chunks} k={k} T={T} m={m}"
+                want = _order_of(own[m])[:k]
+                assert np.array_equal(idx[m], want), name
+                assert np.array_equal(vals[m], own[m][want]), name
+                if not _near_boundary(own[m][want], T, u[m]):
+                    assert tok[m] == OT.sample_row(own[m][want], want, T, u[m]), name
+
+
 def test_topk_ties_signed_zeros_and_repeat(wq):
     """All-zero weights give logits that are all +0 or -0: every entry ties, so the k
     smallest indices are kept and any draw at T > 0 is uniform over them; the call is
