@@ -162,7 +162,7 @@ constexpr int kMmaTile0 = 20, kMmaTileLast = 23;
 // split-K of a tile kMmaTile0 .. kMmaTileLast at M tokens (0: not such a tile, or M too large)
 int gemm_mma_split(int tile, int64_t M, int64_t K);
 // The tile that runs for groups of 32 or 64: their kernels are tile 2's and the LDS-DMA
-// tiles' (9..19, 24); tiles 1, 3 and 4 run as tile 9, the skinny and matrix-core GEMV
+// tiles' (9..19, 24..26); tiles 1, 3 and 4 run as tile 9, the skinny and matrix-core GEMV
 // tiles (5..8, 20..23) as tile 14.
 inline int small_group_tile(int tile) {
   if (tile == 1 || tile == 3 || tile == 4) return 9;

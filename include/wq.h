@@ -252,7 +252,7 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * ("Key Optimizations"): every tile multiplies exact code values (q, or q - z) by x on
  * the matrix cores with fp32 accumulation; the per-channel scale is applied to the
  * finished fp32 sum, group scales to each group's fp32 partial sum, so an output carries
- * only fp32 summation and the final bf16 rounding.  The group-128 LDS-DMA tiles (9..19)
+ * only fp32 summation and the final bf16 rounding.  The group-128 LDS-DMA tiles (9..19, 24..26)
  * multiply fp16 code values by fp16 copies of x: with the workspace's room for x (see
  * wq_workspace_size) each row is scaled by a power of two so that it converts exactly;
  * a workgroup whose x fp16 still cannot hold exactly recomputes its tile with bf16 codes
