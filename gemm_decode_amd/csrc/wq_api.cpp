@@ -153,11 +153,13 @@ int default_tile(const wq_weight* w, int64_t M) {
     // 128-row LDS-DMA tiles, the same rule (measured on MI355X at M = 256: 12 % faster
     // than the 256-row tiles with or without split-K on the decode projection shapes)
     const int64_t blocks = ((M + 127) / 128) * ((w->N + 255) / 256);
-    int t = kDma128Tile0;
-    while (t < kDma128TileLast && blocks * gemm_dma64_split(t, M, w->N) < 200 &&
-           gemm_dma64_split(t + 1, M, w->N) > gemm_dma64_split(t, M, w->N))
-      ++t;
-    return t;
+    static constexpr int kSplits128[] = {kDma128Tile0, kDma128Tile0 + 1, kDma128TileLast, kDma128DeepTile0,
+                                         kDma128DeepTileLast};  // split-K 1, 2, 4, 8, 16
+    int i = 0;
+    while (i + 1 < 5 && blocks * gemm_dma64_split(kSplits128[i], M, w->N) < 200 &&
+           gemm_dma64_split(kSplits128[i + 1], M, w->N) > gemm_dma64_split(kSplits128[i], M, w->N))
+      ++i;
+    return kSplits128[i];
   }
   if (M <= kMmaTokens) {
     // measured on MI355X at M = 8..16: uint4 (5120, 27648) 23.6 us with 64 rows per

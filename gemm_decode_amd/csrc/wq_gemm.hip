@@ -1853,7 +1853,9 @@ int gemm_dma64_split(int tile, int64_t M, int64_t N) {
   const int tm = gemm_dma_rows(tile);
   if (tm == 0) return 0;
   const int64_t blocks = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
-  int S = tile >= kDma64DeepTile0 ? 8 << (tile - kDma64DeepTile0) : 1 << (tile - (tm == 64 ? kDma64Tile0 : kDma128Tile0));
+  int S = tile >= kDma128DeepTile0 ? 8 << (tile - kDma128DeepTile0)
+          : tile >= kDma64DeepTile0 ? 8 << (tile - kDma64DeepTile0)
+                                    : 1 << (tile - (tm == 64 ? kDma64Tile0 : kDma128Tile0));
   while (S > 1 && (blocks * S > 2 * 256 || (int64_t)S * M * N * (int64_t)sizeof(float) > kDmaSplitMaxBytes)) S >>= 1;
   return S;
 }
@@ -2011,7 +2013,7 @@ wq_status launch_gemm(const wq_weight* w, const uint16_t* x, int64_t M, uint16_t
   const bool pc = w->fmt == WQ_FMT_W8_PC;
   const int tm = gemm_dma_rows(tile);
   if (tm != 0 && K % DBK == 0 && M * K < (int64_t(1) << 31)) {
-    // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 (8 / 16 for 25 / 26) over gridDim.y
+    // 64- and 128-row LDS-DMA tiles, split-K 1 / 2 / 4 (8 / 16 for 25 / 26 and 27 / 28) over gridDim.y
     const int64_t total = ((M + tm - 1) / tm) * ((N + DBN - 1) / DBN);
     int S = gemm_dma64_split(tile, M, N);
     if (S > 1 && (!ws || ws_bytes < gemm_workspace_bytes(w->fmt, N, M, tile))) S = 1;

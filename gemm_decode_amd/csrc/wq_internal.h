@@ -150,6 +150,9 @@ constexpr int kDma64Tile0 = 14, kDma64TileLast = 16;
 // and 16, for narrow N (N = 5120 has 20 column tiles of 256: split 4 keeps 80
 // workgroups on 256 CUs, each holding only its own few DMA stages in flight).
 constexpr int kDma64DeepTile0 = 25, kDma64DeepTileLast = 26;
+// GEMM tiles kDma128DeepTile0 .. kDma128DeepTileLast: the 128-row tiles with split-K 8 and
+// 16 (narrow N at 129..256 tokens: N = 5120 has 20 column tiles).
+constexpr int kDma128DeepTile0 = 27, kDma128DeepTileLast = 28;
 // GEMM tiles kDma128Tile0 .. kDma128TileLast: the same with 128-row x tiles (mid M on
 // narrow N, where 256-row tiles leave most CUs idle), split-K 1, 2, 4.
 constexpr int kDma128Tile0 = 17, kDma128TileLast = 19;
@@ -162,7 +165,7 @@ constexpr int kMmaTile0 = 20, kMmaTileLast = 23;
 // split-K of a tile kMmaTile0 .. kMmaTileLast at M tokens (0: not such a tile, or M too large)
 int gemm_mma_split(int tile, int64_t M, int64_t K);
 // The tile that runs for groups of 32 or 64: their kernels are tile 2's and the LDS-DMA
-// tiles' (9..19, 24..26); tiles 1, 3 and 4 run as tile 9, the skinny and matrix-core GEMV
+// tiles' (9..19, 24..28); tiles 1, 3 and 4 run as tile 9, the skinny and matrix-core GEMV
 // tiles (5..8, 20..23) as tile 14.
 inline int small_group_tile(int tile) {
   if (tile == 1 || tile == 3 || tile == 4) return 9;
@@ -170,18 +173,20 @@ inline int small_group_tile(int tile) {
     return kDma64Tile0;
   return tile;
 }
-// rows per x tile of the row-tiled LDS-DMA tiles 14..19, 25, 26 (0 for other tiles)
+// rows per x tile of the row-tiled LDS-DMA tiles 14..19, 25..28 (0 for other tiles)
 inline int gemm_dma_rows(int tile) {
   if ((tile >= kDma64Tile0 && tile <= kDma64TileLast) || (tile >= kDma64DeepTile0 && tile <= kDma64DeepTileLast))
     return 64;
-  return tile >= kDma128Tile0 && tile <= kDma128TileLast ? 128 : 0;
+  if ((tile >= kDma128Tile0 && tile <= kDma128TileLast) || (tile >= kDma128DeepTile0 && tile <= kDma128DeepTileLast))
+    return 128;
+  return 0;
 }
 // rows per x tile of the LDS-DMA tiles 3, 4 and 9..13: 256 for per-channel W8; 128 for
 // the group-128 formats, whose exact kernel keeps a second accumulator set (each group's
 // partial sums, added into the first times the group scale) that a 256-row tile has no
 // registers for
 inline int gemm_big_dma_rows(int fmt) { return fmt == WQ_FMT_W8_PC ? 256 : 128; }
-int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of 14..19, 25, 26
+int gemm_dma64_split(int tile, int64_t M, int64_t N);  // 0 when the tile is not one of 14..19, 25..28
 int gemm_dma_tail(int fmt, int64_t M, int64_t N, int* tail0);
 // Compute units of the current device (kDefaultCUs, MI355X's count, if it cannot be queried).
 constexpr int kDefaultCUs = 256;
@@ -189,7 +194,7 @@ int device_cus();
 // Workspace bytes a GEMM tile needs at this M (fp32 split-K partials; 0 for most tiles).
 size_t gemm_workspace_bytes(int fmt, int64_t N, int64_t M, int tile);
 // Bytes with which a tile takes its fastest path: for the group-128 LDS-DMA tiles
-// (9..19, 24..26) also x converted to fp16 once per call (M x K x 2 bytes after the partials,
+// (9..19, 24..28) also x converted to fp16 once per call (M x K x 2 bytes after the partials,
 // at a 256-byte boundary); without that room the tile converts x in LDS.
 size_t gemm_workspace_full_bytes(int fmt, int64_t K, int64_t N, int64_t M, int tile);
 // xf: fp16 activations (x and y in fp16): tile 2's kernel, and for the grouped formats the

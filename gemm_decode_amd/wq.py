@@ -39,9 +39,9 @@ FMT = {"w8pc": 0, "w8g128": 1, "w4g128": 2, "w4pc": 3, "w8g32": 4, "w8g64": 5, "
 FMT_NAME = {v: k for k, v in FMT.items()}
 CANONICAL, GFX950 = 0, 1
 KIND_GEMV, KIND_GEMM = 0, 1
-GEMM_TILES = 26
+GEMM_TILES = 28
 MMA_TILES = range(20, 24)              # GEMM tiles of the matrix-core GEMV kernel (M <= 16)
-TUNE_LAT_SLOTS = 26                      # WQ_TUNE_LAT_SLOTS: entries wq_tune writes to lat_us
+TUNE_LAT_SLOTS = 28                      # WQ_TUNE_LAT_SLOTS: entries wq_tune writes to lat_us
 SPLIT_GRID = (1, 2, 4, 8, 16, 32)
 WAVES_GRID = (1, 2, 4, 8, 16)
 ROWS_GRID = (4, 8, 16)

@@ -180,7 +180,7 @@ wq_status wq_unrepack(const wq_weight* src, const wq_weight* dst, void* stream);
  * LDS-DMA tiles (split <= 16, at most 512 workgroups, at most 256 MiB) -- or the
  * partials of tile 13's split last round (sized for the current device's CU count, 256
  * when none is visible); 0 when no split applies.  For the group-128 formats the
- * LDS-DMA tiles 9..19, 24..26 also use M * K * 2 bytes after the partials (at a 256-byte
+ * LDS-DMA tiles 9..19, 24..28 also use M * K * 2 bytes after the partials (at a 256-byte
  * boundary) for x converted to fp16 once per call (each row scaled by a power of two
  * so that it converts exactly), then M * 4 bytes (at a 256-byte boundary) for the row
  * scales; given less, they convert x inside every workgroup instead, unscaled (same
@@ -252,7 +252,7 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  * ("Key Optimizations"): every tile multiplies exact code values (q, or q - z) by x on
  * the matrix cores with fp32 accumulation; the per-channel scale is applied to the
  * finished fp32 sum, group scales to each group's fp32 partial sum, so an output carries
- * only fp32 summation and the final bf16 rounding.  The group-128 LDS-DMA tiles (9..19, 24..26)
+ * only fp32 summation and the final bf16 rounding.  The group-128 LDS-DMA tiles (9..19, 24..28)
  * multiply fp16 code values by fp16 copies of x: with the workspace's room for x (see
  * wq_workspace_size) each row is scaled by a power of two so that it converts exactly;
  * a workgroup whose x fp16 still cannot hold exactly recomputes its tile with bf16 codes
@@ -300,13 +300,15 @@ wq_status wq_gemv_ex(const wq_weight* w, const void* x, int64_t M, void* y, int 
  *   25, 26  as 14..16 with split-K 8 and 16 (capped and needing the workspace as
  *      15 and 16): narrow N at a few tokens (N = 5120 has 20 column tiles) spread over
  *      more of the CUs; the default for 17..128 tokens where splits 1..4 leave fewer
- *      than 200 workgroups; other shapes: tile 1.
- * Groups of 32 and 64 run tiles 2 and 9..19, 24..26 as described for group-128 (their
+ *      than 200 workgroups; other shapes: tile 1;
+ *   27, 28  as 17..19 with split-K 8 and 16 (capped and needing the workspace as 18
+ *      and 19): narrow N at 129..256 tokens; other shapes: tile 1.
+ * Groups of 32 and 64 run tiles 2 and 9..19, 24..28 as described for group-128 (their
  * kernels fold every group's partial sum in as a group-128 tile does); tiles 1, 3 and
  * 4 run as tile 9, tiles 5..8 and 20..23 as tile 14. 
  * ws/ws_bytes may be NULL/0 for tiles 1-4 and 9.  Results are bit-identical from run
  * to run for a given tile, device and workspace size. */
-#define WQ_GEMM_TILES 26
+#define WQ_GEMM_TILES 28
 wq_status wq_gemm(const wq_weight* w, const void* x, int64_t M, void* y, int tile, void* ws,
                   size_t ws_bytes, void* stream);
 
@@ -332,10 +334,10 @@ wq_status wq_linear(const wq_weight* w, const void* x, int64_t M, void* y, void*
  *     WQ_ERR_UNSUPPORTED).  split_k 0 = the tuned launch of the bf16 layer with its
  *     matrix-core option replaced by the default dot2 launch and its prefetch flag
  *     dropped (waves and rows must then be 0); else as wq_gemv_ex.
- *   - GEMM (M >= 8): per-channel W8 runs tile 2 and the LDS-DMA tiles 9..19 and 24..26
+ *   - GEMM (M >= 8): per-channel W8 runs tile 2 and the LDS-DMA tiles 9..19 and 24..28
  *     (exact fp16 codes, x as the fp16 operand of the DMA), tiles 3, 4 as 9, 1 as 2, and
  *     5..8, 20..23 as 14; the grouped formats run tile 2 and the LDS-DMA tiles 9..19 and
- *     24..26 (x read as their fp16 operand: no conversion, no row scale, no fallback),
+ *     24..28 (x read as their fp16 operand: no conversion, no row scale, no fallback),
  *     tiles 1, 3, 4 as 9 and 5..8, 20..23 as 14.  The workspace is wq_workspace_size's.
  * wq_moe_linear, wq_lm_head_topk, wq_linear_perm and wq_linear_static take bf16 only.
  * Unknown act: WQ_ERR_INVALID_ARG. */
@@ -494,7 +496,7 @@ int wq_tune_pick(const double* lat, int n);
  * microseconds per call of each split_k (its best rows and waves, lat_us[0..5]) or
  * tile (lat_us[tile - 1]) into the WQ_TUNE_LAT_SLOTS entries of lat_us (host; -1
  * for candidates that could not run and for unused slots).  Synchronizes the stream. */
-#define WQ_TUNE_LAT_SLOTS 26
+#define WQ_TUNE_LAT_SLOTS 28
 wq_status wq_tune(const wq_weight* copies, int n_copies, int64_t M, const void* x, void* y,
                   void* ws, size_t ws_bytes, int warmup, int iters, void* stream, int* chosen,
                   double* lat_us);

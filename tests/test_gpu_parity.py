@@ -475,7 +475,7 @@ def test_no_writes_outside_y_and_workspace(wq):
     wsg[:pad] = 0xAB
     wsg[pad + ng:] = 0xCD
     ybig = torch.full((Mg * N + 2 * pad,), 321, dtype=torch.int16, device=DEV)
-    for tile in (9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 24, 25, 26):
+    for tile in (9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 24, 25, 26, 27, 28):
         wq.wq_gemm(g, to_dev_bf16(synth.activation(100, K, Mg)), ybig[pad:pad + Mg * N].view(torch.bfloat16),
                    tile=tile, ws=wsg[pad:pad + ng])
     torch.cuda.synchronize()
@@ -542,7 +542,7 @@ def test_tuner_runs_and_caches(wq, tmp_path):
     assert wq.wq_tune_cache_get("w8pc", K, N, 64, wq.KIND_GEMM) == tile
     # without a workspace the split-K tiles cannot run and are skipped
     tile, lat = wq.wq_tune(copies, xg, yg, None, warmup=2, iters=3)
-    split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16, 18, 19, 24, 25, 26]  # the split-K tiles (skinny, LDS-DMA)
+    split_tiles = list(range(5, 9)) + list(range(10, 13)) + [15, 16, 18, 19, 24, 25, 26, 27, 28]  # the split-K tiles (skinny, LDS-DMA)
     assert tile not in split_tiles, (tile, lat)
     skipped = set(split_tiles) | set(wq.MMA_TILES)
     assert all((v < 0) == (t in skipped) for t, v in enumerate(lat, start=1)), (tile, lat)
